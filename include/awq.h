@@ -1,0 +1,164 @@
+/*
+ * awq.h -- C ABI of the AWQ W4A16 g128 hot path for MI355X (gfx950).
+ *
+ * What the calls compute is set by these web pages (cited by title and
+ * section; no code is taken from them):
+ *   "AWQ: Activation-aware Weight Quantization for LLM Compression and
+ *    Acceleration" (llm-awq README): feature list (AWQ search, a 4-bit
+ *    linear layer, kernels for the context and decode stages), AWQ model zoo
+ *    table (INT4-g128 and INT3-g128), "Usage" (--w_bit 4 --q_group_size 128;
+ *    search, fake quantization, real INT4 quantization).
+ *   "transformers - AWQ": the quantization_config block (bits 4,
+ *    group_size 128, zero_point true, version "gemm").
+ *   "AWQ (Activation-Aware Weight Quantization) and how it differs from
+ *    GPTQ": "Applying AWQ with AutoAWQ" (saliency from activation magnitude
+ *    on calibration data), "Quantizing a model with AutoAWQ" (w_bit,
+ *    q_group_size, zero_point).
+ *   "LLM quantization's revolutionary breakthrough (VPTQ)", section 02.02
+ *    "AWQ": salient input channels are scaled up through an equivalent
+ *    transform; the scale comes from offline activation statistics.
+ *
+ * Conventions shared by every call
+ *   - Math: y = x . W^T.  W is fp16 [N][K] (output x input, row-major),
+ *     x is fp16 [M][K], y is fp16 [M][N].  Groups of group_size = 128
+ *     consecutive k share one fp16 scale D and one integer zero point z;
+ *     G = K / 128.  Q = 2^bits - 1.
+ *   - Pointers are DEVICE pointers (HBM) allocated by the caller, 16-byte
+ *     aligned, unless a comment says HOST.  The library never allocates or
+ *     frees and keeps nothing after a call returns; scratch memory comes only
+ *     from the caller's workspace.  Calls are asynchronous on `stream`
+ *     (a hipStream_t; NULL = the default stream); outputs are ready when the
+ *     stream is synchronized.  Calls on different streams are re-entrant.
+ *   - Arguments are validated on the host before anything is launched; on
+ *     any error nothing is launched and no output is touched.  No C++
+ *     exception crosses this interface.  Inputs must be finite (not checked).
+ *   - M == 0 or N == 0 is a valid empty call: it returns AWQ_OK and
+ *     launches nothing.
+ *
+ * Packed weight format, version 1 (chosen for gfx950 MFMA/VALU unpacking):
+ *   bits = 4: qweight is uint32 [N][K/8].  Word j of row n holds the codes
+ *     of k = 8j..8j+7.  Code 8j+2t is at bits 4t..4t+3 and code 8j+2t+1 at
+ *     bits 16+4t..19+4t (t = 0..3), so ((w >> 4t) & 0x000F000F) | 0x64006400
+ *     is the fp16 pair (1024 + q[8j+2t], 1024 + q[8j+2t+1]).
+ *   bits = 3: qweight is uint32 [N][3K/32].  Each run of 32 codes of a row
+ *     (k = 32c..32c+31) is a 96-bit little-endian bit stream, code i at
+ *     stream bits 3i..3i+2, stored as 3 consecutive words.
+ *   scales: fp16 [N][G], the group scale D.  zeros: fp16 [N][G], the integer
+ *     zero point z in 0..Q stored exactly.
+ *   Dequantized weight: w_hat[n][k] = (q[n][k] - z[n][g]) * D[n][g].
+ */
+#ifndef AWQ_MI355X_H
+#define AWQ_MI355X_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    AWQ_OK = 0,
+    AWQ_ERR_NULL = 1,         /* a required pointer is NULL                 */
+    AWQ_ERR_SHAPE = 2,        /* negative size, K == 0, K % group_size != 0 */
+    AWQ_ERR_UNSUPPORTED = 3,  /* bits, group_size, zero_point or M not supported */
+    AWQ_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned           */
+    AWQ_ERR_WORKSPACE = 5,    /* workspace smaller than required            */
+    AWQ_ERR_HIP = 6           /* a HIP launch or runtime call failed        */
+} awq_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* awq_status_str(int status);
+
+/* Version of the packed weight format described above (1). */
+int awq_pack_format_version(void);
+
+/* uint32 words per packed row: K/8 for bits 4, 3K/32 for bits 3
+ * (0 for unsupported bits). */
+size_t awq_packed_words_per_row(int K, int bits);
+
+/*
+ * awq_quantize_pack -- round-to-nearest group quantization of W*diag(s),
+ * then packing ("Usage" step 3 of the llm-awq README: real INT4 weights;
+ * "Quantizing a model with AutoAWQ": w_bit, q_group_size, zero_point).
+ *
+ *   W        fp16 [N][K]   weights, row-major (nn.Linear layout)
+ *   s        fp32 [K]      per-input-channel scale, or NULL for s == 1
+ *   qweight  uint32 [N][words_per_row]  out, format above
+ *   scales   fp16 [N][G]   out, D = largest fp16 <= max(hi - lo, 1e-5) / Q
+ *   zeros    fp16 [N][G]   out, z = clamp(rint(-lo / D), 0, Q)
+ * with, per (n, g), v = fp32(W) * s, lo = min(0, min v), hi = max(0, max v),
+ * and q = clamp(rint(v / D) + z, 0, Q); all fp32 IEEE, round-half-even,
+ * correctly rounded division.
+ * bits in {3, 4}; group_size must be 128; zero_point must be 1.
+ */
+int awq_quantize_pack(const void* W, const float* s, int N, int K, int bits,
+                      int group_size, int zero_point, void* qweight,
+                      void* scales, void* zeros, void* stream);
+
+/*
+ * awq_scale_activations -- the activation side of the equivalent transform
+ * (section 02.02 "AWQ" of the VPTQ blog): x_out[m][k] = fp16_rne(fp32(x[m][k]) / s[k]).
+ *   x      fp16 [M][K] in;  s fp32 [K] in;  x_out fp16 [M][K] out (may equal x).
+ */
+int awq_scale_activations(const void* x, const float* s, void* x_out, int M,
+                          int K, void* stream);
+
+/*
+ * awq_search_workspace_bytes -- device workspace needed by awq_search_scale
+ * for T calibration tokens, an N x K layer and n_alpha grid points.
+ */
+size_t awq_search_workspace_bytes(int T, int N, int K, int n_alpha);
+
+/*
+ * awq_search_scale -- the AWQ scale search ("Usage" step 1, --run_awq, of
+ * the llm-awq README; scale from offline activation statistics, section
+ * 02.02 of the VPTQ blog; saliency from activation magnitude, "Applying AWQ
+ * with AutoAWQ").
+ *   s_x[k]   = mean_t |X_cal[t][k]|                         (exact fp64 sum)
+ *   s_i[k]   = fp32(pow(max(s_x[k], 1e-4), alphas[i]))        (fp64 pow)
+ *   L_i      = mean_{t,n} (sum_k X_cal[t][k] (W[n][k] - w_hat_i[n][k] / s_i[k]))^2
+ *              with w_hat_i the dequantized weights of awq_quantize_pack(W, s_i)
+ *   best     = smallest i with L_i == min L
+ *   W        fp16 [N][K] in;  X_cal fp16 [T][K] in, 1 <= T <= 8192
+ *   alphas   HOST fp32 [n_alpha], 1 <= n_alpha <= 64
+ *   s_out    fp32 [K] out: s_best
+ *   loss_out fp32 [n_alpha] out, or NULL
+ *   best_out int32 [1] out (device), or NULL
+ *   workspace / workspace_bytes: device scratch of at least
+ *            awq_search_workspace_bytes(T, N, K, n_alpha) bytes.
+ * The loss GEMM runs on fp16 MFMA with fp32 accumulation, so L_i carries a
+ * relative error of order 1e-4 and near-ties may pick a neighbouring alpha.
+ */
+int awq_search_scale(const void* W, const void* X_cal, int T, int N, int K,
+                     const float* alphas, int n_alpha, int bits, int group_size,
+                     int zero_point, float* s_out, float* loss_out, int* best_out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * awq_gemv -- decode-stage W4A16 (or W3A16) product for small batches (the
+ * decode kernel of the llm-awq README feature list):
+ *   y[m][n] = sum_g D[n][g] * sum_{k in g} x[m][k] * (q[n][k] - z[n][g])
+ *   x fp16 [M][K] in; qweight, scales, zeros as produced by
+ *   awq_quantize_pack; y fp16 [M][N] out (round to nearest from fp32).
+ *   1 <= M <= 16; bits in {3, 4}; group_size 128.
+ */
+int awq_gemv(const void* x, const void* qweight, const void* scales,
+             const void* zeros, void* y, int M, int N, int K, int bits,
+             int group_size, void* stream);
+
+/*
+ * awq_gemm -- context-stage (prefill) W4A16 product, same formula as
+ * awq_gemv for any M >= 1 (the context kernel of the llm-awq README
+ * feature list; version "gemm" in the transformers quantization_config).
+ * Dequantized fp16 tiles feed fp16 MFMA with fp32 accumulation.
+ *   bits must be 4; group_size 128.
+ */
+int awq_gemm(const void* x, const void* qweight, const void* scales,
+             const void* zeros, void* y, int M, int N, int K, int bits,
+             int group_size, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AWQ_MI355X_H */

@@ -1,0 +1,10 @@
+"""CPU oracle for the AWQ W4A16 hot path -- test infrastructure only.
+
+Importable by the tests, by ``__graft_entry__.smoke`` and by the
+``cpu_baseline`` leg of ``bench.py``; never by the product package.
+"""
+from .awq_oracle import *  # noqa: F401,F403
+from .awq_oracle import (act_stat, candidate_scale, quantize, quantize_values, dequantize, pack,
+                         unpack, unpack_fast, matmul, matmul_rows, output_mse,
+                         search_scale, scale_activations, f16_round_down,
+                         awq_quantize_layer, levels, packed_words_per_row)

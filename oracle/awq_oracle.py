@@ -1,0 +1,349 @@
+"""CPU oracle for the AWQ W4A16 g128 hot path -- TEST INFRASTRUCTURE ONLY.
+
+This module is the slow, plain, obviously-correct definition that the HIP
+library is checked against.  Only the test suite, the smoke check in
+``__graft_entry__`` and the ``cpu_baseline`` leg of ``bench.py`` may import
+it.  The product path (``weight_only_quantization_pack_amd``) never imports
+it, and it imports nothing from the product: the two share no arithmetic.
+
+Sources (web pages, cited by title and section):
+  [P1] "AWQ: Activation-aware Weight Quantization for LLM Compression and
+       Acceleration" (llm-awq README, Chinese translation) -- feature list,
+       "AWQ model zoo" table (INT4-g128 / INT3-g128), "Usage" (search, fake
+       and real quantization with --w_bit 4 --q_group_size 128).
+  [P3] "transformers - AWQ" -- the quantization_config block
+       (bits 4, group_size 128, zero_point true, version "gemm").
+  [P4] "AWQ (Activation-Aware Weight Quantization) and how it differs from
+       GPTQ" -- "Applying AWQ with AutoAWQ" (salient weights are found from
+       the magnitude of the matching activations on calibration data) and
+       "Quantizing a model with AutoAWQ" (w_bit, q_group_size, zero_point).
+  [P5] "LLM quantization's revolutionary breakthrough (VPTQ)" -- section
+       02.02 "AWQ": scale salient input channels up through a
+       mathematically equivalent transform; the scale comes from offline
+       activation statistics; no backprop or reconstruction.
+
+The pages give the mechanism in words only.  The operational recipe taken
+here: s = s_x ** alpha with s_x the per-input-channel mean |activation|,
+alpha chosen from a grid by the smallest output MSE of the layer,
+round-to-nearest group quantization of W*diag(s) with an fp16 group scale and
+an integer zero point, bits 4 (or 3), group 128.  Every point the pages leave
+open is a stated reading (listed in the design notes of the repository and
+repeated at the function that takes it).
+
+Precision.  Where a float decides an integer (the codes, the zero point, the
+stored fp16 scale) the oracle works in IEEE fp32 with correctly rounded
+division and round-half-even, which is also the kernel's precision.  Every
+other quantity (statistics, dequantized weights, matmul, loss) is fp64.
+
+Parity status: every function here is pinned by tests/test_oracle_*.py
+against brute force, closed forms, invariants or the textbook definition.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Parameters named as on the pages ([P4] quant_config, [P3] quantization_config).
+GROUP_SIZE = 128
+SUPPORTED_BITS = (3, 4)
+SPAN_FLOOR = np.float32(1e-5)      # reading: (hi - lo) floored before /Q
+STAT_FLOOR = 1e-4                  # reading: s_x floored before the power
+
+PACK_FORMAT_VERSION = 1
+
+
+def levels(bits: int) -> int:
+    """Q = 2**bits - 1, the largest code."""
+    if bits not in SUPPORTED_BITS:
+        raise ValueError(f"bits must be 3 or 4, got {bits}")
+    return (1 << bits) - 1
+
+
+# ---------------------------------------------------------------------------
+# fp16 helpers
+# ---------------------------------------------------------------------------
+def f16_round_down(v32) -> np.ndarray:
+    """Largest fp16 value <= v for positive finite fp32 v.
+
+    Reading: the stored group scale is rounded toward -inf (not to nearest),
+    so that the group's extreme values still reach codes 0 and Q and a second
+    quantize of the dequantized weights reproduces the same codes.
+    """
+    v32 = np.asarray(v32, dtype=np.float32)
+    h = v32.astype(np.float16)                      # round to nearest even
+    went_up = h.astype(np.float32) > v32
+    lower = np.nextafter(h, np.float16(-np.inf))
+    return np.where(went_up, lower, h).astype(np.float16)
+
+
+# ---------------------------------------------------------------------------
+# a1 / a2: activation statistics and candidate scales
+# ---------------------------------------------------------------------------
+def act_stat(X_cal: np.ndarray) -> np.ndarray:
+    """s_x[k] = mean over calibration tokens of |X_cal[t, k]|  (fp32 result).
+
+    [P4] "Applying AWQ with AutoAWQ": salient weights are identified by the
+    magnitude of their activations on calibration data; [P5] 02.02: the scale
+    comes from offline activation statistics.  Reading: the statistic is the
+    mean absolute value per input channel, summed in fp64 (exact for fp16
+    inputs and T < 8192), divided by T in fp64, rounded once to fp32.
+    """
+    X = np.asarray(X_cal)
+    if X.dtype != np.float16 or X.ndim != 2:
+        raise ValueError("X_cal must be a 2-D float16 array [T][K]")
+    T = X.shape[0]
+    total = np.abs(X.astype(np.float64)).sum(axis=0)
+    return (total / np.float64(T)).astype(np.float32)
+
+
+def candidate_scale(s_x: np.ndarray, alpha: float) -> np.ndarray:
+    """s[k] = max(s_x[k], 1e-4) ** alpha, evaluated in fp64, rounded to fp32.
+
+    [P5] 02.02: salient channels are scaled up; the exponent form
+    s = s_x ** alpha and the floor 1e-4 are the readings taken.  alpha = 0
+    gives s == 1 exactly (plain round-to-nearest).
+    """
+    s64 = np.maximum(np.asarray(s_x, dtype=np.float64), STAT_FLOOR)
+    return np.power(s64, np.float64(alpha)).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# a3: group quantization
+# ---------------------------------------------------------------------------
+def quantize(W: np.ndarray, s: np.ndarray | None = None, bits: int = 4,
+             group_size: int = GROUP_SIZE):
+    """Round-to-nearest asymmetric group quantization of W * diag(s).
+
+    [P4] "Quantizing a model with AutoAWQ": q_group_size weights share one
+    scale and one zero point, zero_point=True means asymmetric; [P1] "Usage":
+    --w_bit 4 --q_group_size 128.  v = W[n, k] * s[k] is one fp32 multiply
+    (s = None means s == 1); the groups of v are then quantized by
+    ``quantize_values``.
+    Returns (q uint8 [N][K], scales fp16 [N][G], zeros fp16 [N][G]).
+    """
+    W = np.asarray(W)
+    if W.dtype != np.float16 or W.ndim != 2:
+        raise ValueError("W must be a 2-D float16 array [N][K]")
+    K = W.shape[1]
+    v = W.astype(np.float32)
+    if s is not None:
+        s32 = np.asarray(s, dtype=np.float32)
+        if s32.shape != (K,):
+            raise ValueError("s must have shape [K]")
+        v = v * s32[None, :]                        # one fp32 multiply
+    return quantize_values(v, bits, group_size)
+
+
+def quantize_values(v: np.ndarray, bits: int = 4, group_size: int = GROUP_SIZE):
+    """Group quantizer on already-scaled fp32 values v [N][K].
+
+    Per (row n, group g of 128 consecutive k), all in IEEE fp32:
+        lo  = min(0, min v),  hi = max(0, max v)
+        D32 = max(hi - lo, 1e-5) / Q ;  Dh = largest fp16 <= D32 ;  D = Dh
+        z   = clamp(rint(-lo / D), 0, Q)
+        q   = clamp(rint(v / D) + z, 0, Q)
+    rint rounds half to even.  Readings: the range is widened to contain 0;
+    the span floor 1e-5 keeps an all-zero group finite; Dh is rounded down;
+    the code is computed with the stored fp16 scale.
+    """
+    Q = levels(bits)
+    v = np.asarray(v)
+    if v.dtype != np.float32 or v.ndim != 2:
+        raise ValueError("v must be a 2-D float32 array [N][K]")
+    N, K = v.shape
+    if group_size != GROUP_SIZE or K % group_size != 0:
+        raise ValueError("K must be a multiple of the group size 128")
+    G = K // group_size
+    g = v.reshape(N, G, group_size)
+
+    lo = np.minimum(g.min(axis=2), np.float32(0.0))
+    hi = np.maximum(g.max(axis=2), np.float32(0.0))
+    span = np.maximum(hi - lo, SPAN_FLOOR)
+    delta16 = f16_round_down(span / np.float32(Q))
+    delta = delta16.astype(np.float32)
+
+    z = np.clip(np.rint(-lo / delta), 0, Q).astype(np.int32)
+    code = np.rint(g / delta[:, :, None]) + z[:, :, None].astype(np.float32)
+    q = np.clip(code, 0, Q).astype(np.uint8)
+    return q.reshape(N, K), delta16, z.astype(np.float16)
+
+
+def dequantize(q: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
+               group_size: int = GROUP_SIZE) -> np.ndarray:
+    """w_hat[n, k] = (q[n, k] - z[n, g]) * D[n, g] in fp64 (exact).
+
+    This is the "fake quantization" weight of [P1] "Usage" step 2.
+    """
+    N, K = q.shape
+    G = K // group_size
+    qq = q.astype(np.float64).reshape(N, G, group_size)
+    zz = zeros.astype(np.float64)[:, :, None]
+    dd = scales.astype(np.float64)[:, :, None]
+    return ((qq - zz) * dd).reshape(N, K)
+
+
+# ---------------------------------------------------------------------------
+# a6: packing (format version 1, chosen for gfx950)
+# ---------------------------------------------------------------------------
+def pack(q: np.ndarray, bits: int) -> np.ndarray:
+    """Pack codes q uint8 [N][K] into uint32 words, row by row.
+
+    bits=4: word j of row n holds codes k = 8j..8j+7.  Code 8j+2t sits at
+    bits 4t..4t+3 and code 8j+2t+1 at bits 16+4t..19+4t (t = 0..3), so that
+    (word >> 4t) & 0x000F000F holds the pair (q[8j+2t], q[8j+2t+1]) in its
+    two 16-bit halves.  Result shape [N][K/8].
+    bits=3: each run of 32 codes k = 32c..32c+31 is a 96-bit little-endian
+    bit stream (code i at stream bits 3i..3i+2) stored as 3 words.  Result
+    shape [N][3K/32].
+    """
+    q = np.asarray(q, dtype=np.uint8)
+    N, K = q.shape
+    Q = levels(bits)
+    if q.max(initial=0) > Q:
+        raise ValueError("code out of range")
+    if bits == 4:
+        c = q.reshape(N, K // 8, 8).astype(np.uint32)
+        word = np.zeros((N, K // 8), dtype=np.uint32)
+        for t in range(4):
+            word |= c[:, :, 2 * t] << np.uint32(4 * t)
+            word |= c[:, :, 2 * t + 1] << np.uint32(16 + 4 * t)
+        return word
+    c = q.reshape(N, K // 32, 32).astype(np.uint32)
+    out = np.zeros((N, K // 32, 3), dtype=np.uint32)
+    for i in range(32):
+        for b in range(3):
+            pos = 3 * i + b
+            bit = (c[:, :, i] >> np.uint32(b)) & np.uint32(1)
+            out[:, :, pos // 32] |= bit << np.uint32(pos % 32)
+    return out.reshape(N, 3 * (K // 32))
+
+
+def unpack(words: np.ndarray, bits: int, K: int) -> np.ndarray:
+    """Inverse of ``pack``: read every code back bit by bit."""
+    words = np.asarray(words, dtype=np.uint32)
+    N = words.shape[0]
+    q = np.zeros((N, K), dtype=np.uint8)
+    for k in range(K):
+        for b in range(bits):
+            if bits == 4:
+                j, r = divmod(k, 8)
+                pos = 4 * (r // 2) + 16 * (r % 2) + b
+                w = words[:, j]
+            else:
+                c, i = divmod(k, 32)
+                p = 3 * i + b
+                w = words[:, 3 * c + p // 32]
+                pos = p % 32
+            q[:, k] |= (((w >> np.uint32(pos)) & np.uint32(1)) << np.uint32(b)).astype(np.uint8)
+    return q
+
+
+def packed_words_per_row(K: int, bits: int) -> int:
+    return K // 8 if bits == 4 else 3 * (K // 32)
+
+
+# ---------------------------------------------------------------------------
+# a7: activation-side half of the equivalent transform
+# ---------------------------------------------------------------------------
+def scale_activations(x: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """x'[m, k] = fp16_rne(fp32(x[m, k]) / s[k]).
+
+    [P5] 02.02: (x / s) . (s w) = x . w; the weights carry s inside the
+    quantizer, the activations are divided by it.
+    """
+    x32 = np.asarray(x, dtype=np.float16).astype(np.float32)
+    return (x32 / np.asarray(s, dtype=np.float32)[None, :]).astype(np.float16)
+
+
+# ---------------------------------------------------------------------------
+# a8 / a9 / a10: the W4A16 (W3A16) matmul
+# ---------------------------------------------------------------------------
+def matmul(x: np.ndarray, qweight: np.ndarray, scales: np.ndarray,
+           zeros: np.ndarray, bits: int, K: int) -> np.ndarray:
+    """y[m, n] = sum_k x[m, k] * w_hat[n, k], fp64, from the packed weights.
+
+    [P1] feature list: the 4-bit linear layer and its context (GEMM) and
+    decode (GEMV) kernels compute this one product.
+    """
+    q = unpack_fast(qweight, bits, K)
+    w_hat = dequantize(q, scales, zeros)
+    return np.asarray(x, dtype=np.float16).astype(np.float64) @ w_hat.T
+
+
+def unpack_fast(words: np.ndarray, bits: int, K: int) -> np.ndarray:
+    """Vectorised inverse of ``pack`` (same format; checked against ``unpack``)."""
+    words = np.asarray(words, dtype=np.uint32)
+    N = words.shape[0]
+    if bits == 4:
+        w = words.reshape(N, K // 8, 1)
+        r = np.arange(8, dtype=np.uint32)
+        shift = 4 * (r // 2) + 16 * (r % 2)
+        return ((w >> shift[None, None, :]) & np.uint32(15)).astype(np.uint8).reshape(N, K)
+    w = words.reshape(N, K // 32, 3).astype(np.uint64)
+    stream_lo = w[:, :, 0] | (w[:, :, 1] << np.uint64(32))      # bits 0..63
+    stream_hi = w[:, :, 2]                                       # bits 64..95
+    q = np.zeros((N, K // 32, 32), dtype=np.uint8)
+    for i in range(32):
+        p = 3 * i
+        if p + 3 <= 64:
+            val = (stream_lo >> np.uint64(p)) & np.uint64(7)
+        elif p >= 64:
+            val = (stream_hi >> np.uint64(p - 64)) & np.uint64(7)
+        else:   # code straddles bit 64
+            nlo = 64 - p
+            val = (stream_lo >> np.uint64(p)) | ((stream_hi << np.uint64(nlo)) & np.uint64(7))
+        q[:, :, i] = val.astype(np.uint8)
+    return q.reshape(N, K)
+
+
+def matmul_rows(x: np.ndarray, qweight: np.ndarray, scales: np.ndarray,
+                zeros: np.ndarray, bits: int, K: int, rows) -> np.ndarray:
+    """Output columns y[:, rows] only (for sampled checks at full size)."""
+    rows = np.asarray(rows)
+    return matmul(x, qweight[rows], scales[rows], zeros[rows], bits, K)
+
+
+# ---------------------------------------------------------------------------
+# a4 / a5: output-MSE loss and the alpha grid search
+# ---------------------------------------------------------------------------
+def output_mse(X_cal: np.ndarray, W: np.ndarray, w_hat: np.ndarray,
+               s: np.ndarray) -> float:
+    """L = mean over (t, n) of (sum_k X[t,k] (W[n,k] - w_hat[n,k] / s[k]))^2.
+
+    The layer's own fp16 output X.W^T against the output of the deployed
+    pair (X / s).(w_hat)^T, in exact arithmetic; fp64.  Reading: the MSE is
+    of this single linear layer, averaged over calibration tokens and output
+    channels.
+    """
+    X = np.asarray(X_cal, dtype=np.float16).astype(np.float64)
+    D = np.asarray(W, dtype=np.float16).astype(np.float64) - w_hat / np.asarray(s, np.float32).astype(np.float64)[None, :]
+    E = X @ D.T
+    return float(np.mean(E * E))
+
+
+def search_scale(W: np.ndarray, X_cal: np.ndarray, alphas, bits: int = 4,
+                 group_size: int = GROUP_SIZE):
+    """Grid search of alpha minimising the layer's output MSE.
+
+    [P1] "Usage" step 1 (--run_awq: search and save the per-channel scales),
+    [P5] 02.02 (scale from offline activation statistics, no backprop).
+    For each alpha_i: s_i = candidate_scale(s_x, alpha_i), quantize W with
+    s_i, L_i = output_mse.  The smallest i attaining min L_i is chosen.
+    Returns (s_best fp32 [K], losses fp64 [n_alpha], best index).
+    """
+    s_x = act_stat(X_cal)
+    losses = []
+    for a in alphas:
+        s = candidate_scale(s_x, a)
+        q, d, z = quantize(W, s, bits, group_size)
+        losses.append(output_mse(X_cal, W, dequantize(q, d, z, group_size), s))
+    losses = np.asarray(losses, dtype=np.float64)
+    best = int(np.argmin(losses))                   # first minimum
+    return candidate_scale(s_x, alphas[best]), losses, best
+
+
+def awq_quantize_layer(W: np.ndarray, X_cal: np.ndarray, alphas, bits: int = 4):
+    """Whole offline pass: search, then quantize and pack with the chosen s."""
+    s, losses, best = search_scale(W, X_cal, alphas, bits)
+    q, d, z = quantize(W, s, bits)
+    return {"s": s, "losses": losses, "best": best,
+            "qweight": pack(q, bits), "scales": d, "zeros": z, "q": q}

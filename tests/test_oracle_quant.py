@@ -1,0 +1,223 @@
+"""Pins for the oracle's quantizer (fp16 scale rounding, codes, zero point).
+
+Each check comes from outside the oracle's own formula: brute force over
+the fp16 table and over integer codes, hand-derived closed forms, and
+invariants that any correct round-to-nearest group quantizer satisfies.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from weight_only_quantization_pack_amd import workloads as WL
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+# every positive finite fp16 value, ascending (brute-force table)
+_ALL_F16 = np.arange(0x0001, 0x7C00, dtype=np.uint16).view(np.float16)
+_ALL_F16_AS32 = _ALL_F16.astype(np.float32)
+
+
+def _brute_round_down(v32):
+    i = np.searchsorted(_ALL_F16_AS32, v32, side="right") - 1
+    return _ALL_F16[i]
+
+
+def test_f16_round_down_brute_force():
+    rng = np.random.default_rng(7)
+    samples = [
+        np.exp(rng.uniform(np.log(6e-8), np.log(65000), 200_000)).astype(np.float32),
+        _ALL_F16_AS32,                                          # exact fp16 values
+        np.nextafter(_ALL_F16_AS32, np.float32(np.inf)),        # just above
+        np.nextafter(_ALL_F16_AS32[1:], np.float32(0)),         # just below
+    ]
+    # midpoints between neighbours (where round-to-nearest goes either way)
+    mids = ((_ALL_F16_AS32[:-1].astype(np.float64) + _ALL_F16_AS32[1:]) / 2).astype(np.float32)
+    samples.append(mids)
+    v = np.concatenate(samples)
+    got = O.f16_round_down(v)
+    want = _brute_round_down(v)
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+    assert np.all(got.astype(np.float32) <= v)
+
+
+def _nearest_even(val):
+    """Integer nearest to the float val; an exact half goes to the even one."""
+    lo = int(np.floor(val))
+    d_lo, d_hi = val - lo, (lo + 1) - val
+    if d_lo < d_hi:
+        return lo
+    if d_hi < d_lo:
+        return lo + 1
+    return lo if lo % 2 == 0 else lo + 1
+
+
+def _brute_codes(v32, delta16, z, Q):
+    """q = clamp(j + z) with j the integer nearest to fp32(v / D), ties to even."""
+    d = delta16.astype(np.float32)
+    a = (v32 / d).astype(np.float64)              # the fp32 quotient, exactly
+    return np.array([min(max(_nearest_even(x) + int(z), 0), Q) for x in a], dtype=np.int64)
+
+
+def _brute_group(v_group, bits):
+    """Scale and zero of one group by brute force over the fp16 table."""
+    Q = (1 << bits) - 1
+    lo = min(np.float32(0), v_group.min())
+    hi = max(np.float32(0), v_group.max())
+    span = max(np.float32(hi - lo), np.float32(1e-5))
+    d32 = np.float32(span / np.float32(Q))
+    dh = _brute_round_down(np.array([d32], np.float32))[0]
+    a = np.float64(np.float32(-lo / np.float32(dh)))
+    return dh, min(max(_nearest_even(a), 0), Q)
+
+
+def _crafted_tiles(bits):
+    """4x128 tiles: random, ties, all positive, all negative, all zero, outlier."""
+    rng = np.random.default_rng(11 + bits)
+    tiles = []
+    tiles.append((rng.standard_normal((4, 128)) * 0.02).astype(np.float32))
+    # exact .5 ties on the grid D = 2^-6 around a zero of 3: values (j + 1/2) * 2^-6
+    t = ((rng.integers(-3, 3, (4, 128)) + 0.5) * 2.0 ** -6).astype(np.float32)
+    t[:, 0] = -3 * 2.0 ** -6
+    t[:, 1] = (2 ** bits - 4) * 2.0 ** -6
+    tiles.append(t)
+    tiles.append(np.abs(rng.standard_normal((4, 128)) * 0.02).astype(np.float32) + np.float32(0.01))
+    tiles.append(-np.abs(rng.standard_normal((4, 128)) * 0.02).astype(np.float32) - np.float32(0.01))
+    tiles.append(np.zeros((4, 128), np.float32))
+    o = (rng.standard_normal((4, 128)) * 0.02).astype(np.float32)
+    o[:, 17] *= 20
+    tiles.append(o)
+    return tiles
+
+
+@pytest.mark.parametrize("bits", [4, 3])
+def test_codes_scale_zero_brute_force_on_4x128_tiles(bits):
+    Q = (1 << bits) - 1
+    for tile in _crafted_tiles(bits):
+        q, d, z = O.quantize_values(tile, bits)
+        for n in range(4):
+            dh, zz = _brute_group(tile[n], bits)
+            assert d[n, 0].view(np.uint16) == dh.view(np.uint16)
+            assert int(z[n, 0]) == zz
+            want = _brute_codes(tile[n], d[n, 0], zz, Q)
+            assert np.array_equal(q[n].astype(np.int64), want)
+        assert q.max() <= Q
+
+
+@pytest.mark.parametrize("bits", [4, 3])
+def test_closed_form_group(bits):
+    g = json.load(open(os.path.join(GOLDEN, "closed_form_groups.json")))[f"int{bits}"]
+    i = np.arange(128) % g["period"]
+    v = ((i - g["offset"]) * 2.0 ** g["step_exp"]).astype(np.float32)[None, :]
+    q, d, z = O.quantize_values(v, bits)
+    assert np.array_equal(q[0], i.astype(np.uint8))
+    assert int(d[0, 0].view(np.uint16)) == g["scale_f16_bits"]
+    assert float(z[0, 0]) == g["zero"]
+    words = O.pack(q, bits)[0]
+    n = len(g["words"])
+    assert [int(w) for w in words[:n]] == g["words"]
+
+
+def test_zero_group_and_one_sided_groups():
+    v = np.zeros((1, 128), np.float32)
+    q, d, z = O.quantize_values(v, 4)
+    assert np.all(q == 0) and float(z[0, 0]) == 0.0
+    assert d[0, 0].view(np.uint16) == _brute_round_down(np.float32(1e-5) / np.float32(15)).view(np.uint16)
+    assert np.all(O.dequantize(q, d, z) == 0.0)
+    pos = np.linspace(0.01, 0.05, 128, dtype=np.float32)[None, :]
+    q, d, z = O.quantize_values(pos, 4)
+    assert float(z[0, 0]) == 0.0 and q.max() == 15          # lo widened to 0
+    q, d, z = O.quantize_values(-pos, 4)
+    assert float(z[0, 0]) == 15.0 and q.min() == 0          # hi widened to 0: code 15 is 0.0
+    assert q.max() == 15 + int(np.rint(np.float32(-0.01) / d[0, 0].astype(np.float32)))
+
+
+def _outlier_groups(bits, n_rows=1280):
+    rng = np.random.default_rng(100 + bits)
+    W = (rng.standard_normal((n_rows, 256)) * 0.02).astype(np.float32)
+    W[:, rng.choice(256, 4, replace=False)] *= 20
+    s = rng.lognormal(0, 1, 256).astype(np.float32)
+    return W.astype(np.float16), s
+
+
+@pytest.mark.parametrize("bits", [4, 3])
+def test_requantize_is_idempotent(bits):
+    W, s = _outlier_groups(bits)
+    q, d, z = O.quantize(W, s, bits)
+    w_hat = O.dequantize(q, d, z)
+    assert np.array_equal(w_hat.astype(np.float32).astype(np.float64), w_hat)   # exact in fp32
+    q2, d2, z2 = O.quantize_values(w_hat.astype(np.float32), bits)
+    assert np.array_equal(q, q2)
+    assert np.array_equal(d.view(np.uint16), d2.view(np.uint16))
+    assert np.array_equal(z, z2)
+
+
+@pytest.mark.parametrize("bits", [4, 3])
+def test_alpha_zero_is_plain_rtn(bits):
+    wl = WL.workload(1)
+    W, X = wl.weights(), wl.calibration()
+    s0 = O.candidate_scale(O.act_stat(X), 0.0)
+    assert np.all(s0 == np.float32(1.0))
+    a = O.quantize(W, s0, bits)
+    b = O.quantize(W, None, bits)
+    for x, y in zip(a, b):
+        assert x.tobytes() == y.tobytes()
+
+
+@pytest.mark.parametrize("p", [-3, 2])
+def test_power_of_two_equivariance(p):
+    W, s = _outlier_groups(4, 64)
+    v = W.astype(np.float32) * s[None, :]
+    q1, d1, z1 = O.quantize_values(v, 4)
+    q2, d2, z2 = O.quantize_values(v * np.float32(2.0 ** p), 4)
+    assert np.array_equal(q1, q2) and np.array_equal(z1, z2)
+    assert np.array_equal(d1.astype(np.float64) * 2.0 ** p, d2.astype(np.float64))
+
+
+def test_permutation_within_group():
+    W, s = _outlier_groups(4, 64)
+    v = W.astype(np.float32) * s[None, :]
+    perm = np.random.default_rng(3).permutation(128)
+    vp = v.reshape(64, 2, 128)[:, :, perm].reshape(64, 256)
+    q1, d1, z1 = O.quantize_values(v, 4)
+    q2, d2, z2 = O.quantize_values(vp, 4)
+    assert np.array_equal(d1.view(np.uint16), d2.view(np.uint16)) and np.array_equal(z1, z2)
+    assert np.array_equal(q1.reshape(64, 2, 128)[:, :, perm].reshape(64, 256), q2)
+
+
+@pytest.mark.parametrize("bits", [4, 3])
+def test_round_to_nearest_error_bound(bits):
+    W, s = _outlier_groups(bits)
+    v = (W.astype(np.float32) * s[None, :])
+    q, d, z = O.quantize_values(v, bits)
+    w_hat = O.dequantize(q, d, z)
+    Q = (1 << bits) - 1
+    dd = np.repeat(d.astype(np.float64), 128, axis=1)
+    zz = np.repeat(z.astype(np.float64), 128, axis=1)
+    err = np.abs(v.astype(np.float64) - w_hat)
+    unclamped = (np.rint(v.astype(np.float64) / dd) + zz >= 0) & (np.rint(v.astype(np.float64) / dd) + zz <= Q)
+    assert np.all(err[unclamped] <= 0.5 * dd[unclamped] * (1 + 2.0 ** -20))
+    assert np.all(err <= 0.52 * dd)
+
+
+def test_scale_is_per_input_channel():
+    """s multiplies columns (input channels k), never rows."""
+    W = WL.random_weights(3, 256, seed=5)
+    s = np.ones(256, np.float32)
+    s[130] = 4.0                                     # only group 1 changes
+    a, b = O.quantize(W, None, 4), O.quantize(W, s, 4)
+    assert np.array_equal(a[0][:, :128], b[0][:, :128])
+    assert not np.array_equal(a[1][:, 1], b[1][:, 1])
+    assert np.array_equal(a[1][:, 0], b[1][:, 0])
+
+
+def test_page_configs_are_the_defaults():
+    cfg = json.load(open(os.path.join(GOLDEN, "page_configs.json")))
+    assert cfg["autoawq_quant_config"]["w_bit"] in O.SUPPORTED_BITS
+    assert cfg["autoawq_quant_config"]["q_group_size"] == O.GROUP_SIZE
+    assert cfg["transformers_quantization_config"]["group_size"] == O.GROUP_SIZE
+    assert cfg["transformers_quantization_config"]["zero_point"] is True
+    for bits, gs in cfg["model_zoo_configs"]["configs"]:
+        assert bits in O.SUPPORTED_BITS and gs == O.GROUP_SIZE

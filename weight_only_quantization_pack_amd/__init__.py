@@ -1,0 +1,14 @@
+"""AWQ W4A16 g128 hot path for MI355X (gfx950).
+
+The compute lives in the HIP library ``libawq.so`` (C ABI declared in
+``include/awq.h``); this package is a thin ctypes binding over it plus the
+seeded synthetic workloads.  The library is loaded on first use and a
+missing build raises immediately: there is no CPU fallback.
+"""
+from .binding import (AwqError, quantize_pack, search_scale, search_workspace_bytes,  # noqa: F401
+                      gemv, gemm, scale_activations, library_path, load_library,
+                      pack_format_version, packed_words_per_row)
+
+__all__ = ["AwqError", "quantize_pack", "search_scale", "search_workspace_bytes",
+           "gemv", "gemm", "scale_activations", "library_path", "load_library",
+           "pack_format_version", "packed_words_per_row"]

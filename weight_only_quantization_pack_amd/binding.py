@@ -1,0 +1,218 @@
+"""ctypes binding of libawq.so (C ABI in include/awq.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  Tensors are torch tensors on the GPU; the binding checks dtype,
+device, shape and contiguity, allocates outputs with torch and passes raw
+device pointers and the current HIP stream.  A missing library raises
+``AwqError`` on first use; there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libawq.so"
+
+_c_void_p = ctypes.c_void_p
+_c_int = ctypes.c_int
+_c_size_t = ctypes.c_size_t
+
+# (name, restype, argtypes) for every exported symbol of include/awq.h
+SIGNATURES = [
+    ("awq_status_str", ctypes.c_char_p, [_c_int]),
+    ("awq_pack_format_version", _c_int, []),
+    ("awq_packed_words_per_row", _c_size_t, [_c_int, _c_int]),
+    ("awq_quantize_pack", _c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                   _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    ("awq_scale_activations", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_void_p]),
+    ("awq_search_workspace_bytes", _c_size_t, [_c_int, _c_int, _c_int, _c_int]),
+    ("awq_search_scale", _c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_int,
+                                  _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p,
+                                  _c_void_p, _c_size_t, _c_void_p]),
+    ("awq_gemv", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
+                          _c_int, _c_int, _c_int, _c_void_p]),
+    ("awq_gemm", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
+                          _c_int, _c_int, _c_int, _c_void_p]),
+]
+
+STATUS = {0: "AWQ_OK", 1: "AWQ_ERR_NULL", 2: "AWQ_ERR_SHAPE", 3: "AWQ_ERR_UNSUPPORTED",
+          4: "AWQ_ERR_ALIGN", 5: "AWQ_ERR_WORKSPACE", 6: "AWQ_ERR_HIP"}
+
+GROUP_SIZE = 128
+
+
+class AwqError(RuntimeError):
+    """A non-zero status from the library, or the library is missing."""
+
+    def __init__(self, msg, status=None):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.environ.get("AWQ_MI355X_LIB", os.path.join(_HERE, "lib", LIB_NAME))
+
+
+def load_library():
+    """Load libawq.so once; raise AwqError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise AwqError(f"HIP library not built: {path} is missing "
+                       "(run __graft_entry__.build() or python -m "
+                       "weight_only_quantization_pack_amd.build)")
+    lib = ctypes.CDLL(path)
+    for name, res, args in SIGNATURES:
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        name = STATUS.get(status, str(status))
+        raise AwqError(f"{what} failed: {name}", status)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need(t, dtype, shape, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def pack_format_version() -> int:
+    return int(load_library().awq_pack_format_version())
+
+
+def packed_words_per_row(K: int, bits: int) -> int:
+    return int(load_library().awq_packed_words_per_row(K, bits))
+
+
+def quantize_pack(W, s=None, bits: int = 4, group_size: int = GROUP_SIZE,
+                  zero_point: bool = True, out=None):
+    """Quantize fp16 W [N][K] (times s [K] if given) and pack.
+
+    Returns (qweight int32 [N][words], scales fp16 [N][G], zeros fp16 [N][G]).
+    """
+    torch = _torch()
+    lib = load_library()
+    N, K = W.shape
+    _need(W, torch.float16, (N, K), "W")
+    if s is not None:
+        _need(s, torch.float32, (K,), "s")
+    G = K // group_size if group_size > 0 else 0
+    if out is None:
+        words = int(lib.awq_packed_words_per_row(K, bits))
+        qweight = torch.empty((N, words), dtype=torch.int32, device=W.device)
+        scales = torch.empty((N, G), dtype=torch.float16, device=W.device)
+        zeros = torch.empty((N, G), dtype=torch.float16, device=W.device)
+    else:
+        qweight, scales, zeros = out
+    st = lib.awq_quantize_pack(_ptr(W), _ptr(s), N, K, bits, group_size, int(zero_point),
+                               _ptr(qweight), _ptr(scales), _ptr(zeros), _stream_ptr(W))
+    _check(st, "awq_quantize_pack")
+    return qweight, scales, zeros
+
+
+def scale_activations(x, s, out=None):
+    """x' = fp16(x / s) per input channel."""
+    torch = _torch()
+    lib = load_library()
+    M, K = x.shape
+    _need(x, torch.float16, (M, K), "x")
+    _need(s, torch.float32, (K,), "s")
+    if out is None:
+        out = torch.empty_like(x)
+    st = lib.awq_scale_activations(_ptr(x), _ptr(s), _ptr(out), M, K, _stream_ptr(x))
+    _check(st, "awq_scale_activations")
+    return out
+
+
+def search_workspace_bytes(T: int, N: int, K: int, n_alpha: int) -> int:
+    return int(load_library().awq_search_workspace_bytes(T, N, K, n_alpha))
+
+
+def search_scale(W, X_cal, alphas, bits: int = 4, group_size: int = GROUP_SIZE,
+                 zero_point: bool = True, workspace=None):
+    """AWQ alpha-grid search.  Returns (s fp32 [K], loss fp32 [n_alpha], best int32 [1])."""
+    torch = _torch()
+    lib = load_library()
+    N, K = W.shape
+    T = X_cal.shape[0]
+    _need(W, torch.float16, (N, K), "W")
+    _need(X_cal, torch.float16, (T, K), "X_cal")
+    a = (ctypes.c_float * len(alphas))(*[float(v) for v in alphas])
+    n_alpha = len(alphas)
+    need = int(lib.awq_search_workspace_bytes(T, N, K, n_alpha))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=W.device)
+    s_out = torch.empty(K, dtype=torch.float32, device=W.device)
+    loss = torch.empty(max(n_alpha, 1), dtype=torch.float32, device=W.device)
+    best = torch.empty(1, dtype=torch.int32, device=W.device)
+    st = lib.awq_search_scale(_ptr(W), _ptr(X_cal), T, N, K, ctypes.cast(a, _c_void_p), n_alpha,
+                              bits, group_size, int(zero_point), _ptr(s_out), _ptr(loss),
+                              _ptr(best), _ptr(workspace), workspace.numel(), _stream_ptr(W))
+    _check(st, "awq_search_scale")
+    return s_out, loss[:n_alpha], best
+
+
+def _matmul(fn_name, x, qweight, scales, zeros, N, bits, group_size, out):
+    torch = _torch()
+    lib = load_library()
+    M, K = x.shape
+    _need(x, torch.float16, (M, K), "x")
+    words = int(lib.awq_packed_words_per_row(K, bits))
+    _need(qweight, torch.int32, (N, words), "qweight")
+    G = K // group_size if group_size > 0 else 0
+    _need(scales, torch.float16, (N, G), "scales")
+    _need(zeros, torch.float16, (N, G), "zeros")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, torch.float16, (M, N), "out")
+    st = getattr(lib, fn_name)(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(out),
+                               M, N, K, bits, group_size, _stream_ptr(x))
+    _check(st, fn_name)
+    return out
+
+
+def gemv(x, qweight, scales, zeros, N=None, bits: int = 4, group_size: int = GROUP_SIZE, out=None):
+    """Decode product y = x . w_hat^T for 1 <= M <= 16."""
+    N = qweight.shape[0] if N is None else N
+    return _matmul("awq_gemv", x, qweight, scales, zeros, N, bits, group_size, out)
+
+
+def gemm(x, qweight, scales, zeros, N=None, bits: int = 4, group_size: int = GROUP_SIZE, out=None):
+    """Prefill product y = x . w_hat^T for any M >= 1 (bits 4)."""
+    N = qweight.shape[0] if N is None else N
+    return _matmul("awq_gemm", x, qweight, scales, zeros, N, bits, group_size, out)
