@@ -1,0 +1,313 @@
+#!/usr/bin/env python3
+"""Benchmark of the AWQ W4A16 g128 hot path on one MI355X.
+
+Headline (value): decode GEMV throughput at M = 1 on the Llama-7B layer
+shapes, in algorithmic GB/s.  One step = the seven linears of one Llama-7B
+decoder layer at decode (q, k, v, o: 4096x4096; gate, up: 4096->11008;
+down: 11008->4096), each one awq_gemv launch on packed int4 g128 weights.
+Weights rotate over enough replicas (>= 768 MB, three times the 256 MB
+Infinity Cache) that every step reads them from HBM.  The step's launches
+are captured once in a HIP graph and replayed, so host launch overhead is
+not timed.  Timing: HIP events on the launch stream around exactly --steps
+steps, after --warmup untimed steps.
+
+Second half of the metric (gemm): prefill GEMM TFLOP/s at M = 2048 on the
+Mistral-7B shapes (4096x14336, 14336x4096, 4096x6144).  Also reported:
+the offline path (alpha search on the 4096x4096 layer with 512 calibration
+tokens and 20 grid points; quantize+pack) and the CPU oracle timed on a
+bounded sample of the same decode step.
+
+Algorithmic bytes per GEMV launch: N*K/2 (int4 codes) + 4*N*K/128 (fp16
+scale and zero per group) + 2*M*K (x) + 2*M*N (y).  Flops per GEMM launch:
+2*M*N*K.  Peaks: HBM 8 TB/s; dense fp16 MFMA 2.5 PFLOP/s.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+COLD_BYTES = 768 * 2 ** 20
+METRIC = "W4A16 g128 GEMV GB/s (% HBM peak) at M=1 + GEMM TFLOP/s at M=2048"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def gemv_bytes(M, N, K, bits=4):
+    return N * K * bits // 8 + 4 * N * (K // 128) + 2 * M * K + 2 * M * N
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--gemm-iters", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-offline", action="store_true")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path in this "
+              "build (a layer would be split by output rows, one shard per GPU, with no "
+              "exchange for the matmul itself). Use --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import weight_only_quantization_pack_amd as awq
+    from weight_only_quantization_pack_amd import workloads as WL
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    awq.load_library()
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(0)
+    stream = torch.cuda.Stream()          # default priority
+
+    # ------------------------------------------------------------------ decode GEMV
+    wl2 = WL.workload(2)
+    shape_index = {s: i for i, s in enumerate(wl2.shapes)}
+    layer = WL.LLAMA7B_LAYER
+    packed = {}
+    xs = {}
+    with torch.cuda.stream(stream):
+        for (K, N), i in shape_index.items():
+            W = torch.from_numpy(wl2.weights(i)).to(dev)
+            packed[(K, N)] = awq.quantize_pack(W, None, bits=4)
+            xs[K] = torch.from_numpy(wl2.activations(1, i)).to(dev)
+            del W
+    step_bytes = sum(gemv_bytes(1, N, K) for K, N in layer)
+    weight_bytes = sum(N * K // 2 + 4 * N * (K // 128) for K, N in layer)
+    R = max(2, math.ceil(COLD_BYTES / weight_bytes))
+    reps = [[tuple(t.clone() for t in packed[s]) for s in layer] for _ in range(R)]
+    ys = [torch.empty((1, N), dtype=torch.float16, device=dev) for _, N in layer]
+    torch.cuda.synchronize()
+    log(f"decode step: {len(layer)} GEMVs, {step_bytes / 1e6:.2f} MB algorithmic, "
+        f"{R} weight replicas ({R * weight_bytes / 2**20:.0f} MiB)")
+
+    def step(r):
+        for j, (K, N) in enumerate(layer):
+            qw, sc, ze = reps[r][j]
+            awq.gemv(xs[K], qw, sc, ze, N=N, bits=4, out=ys[j])
+
+    # one graph = R consecutive steps, each on its own replica
+    with torch.cuda.stream(stream):
+        for r in range(R):          # eager warm-up (also loads the code object)
+            step(r)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for r in range(R):
+            step(r)
+    torch.cuda.synchronize()
+
+    def replay(n_steps):
+        assert n_steps % R == 0
+        for _ in range(n_steps // R):
+            graph.replay()
+
+    warm = R * max(1, math.ceil(args.warmup / R))
+    steps = R * max(1, math.ceil(args.steps / R))
+    with torch.cuda.stream(stream):
+        replay(warm)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        e0.record(stream)
+        replay(steps)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / steps
+    gemv_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    avg_launch_us = ms_per_step * 1e3 / len(layer)
+    log(f"decode step {ms_per_step * 1e3:.2f} us  ->  {gemv_gbs:.1f} GB/s "
+        f"({100 * gemv_gbs / HBM_PEAK_GBS:.1f}% of HBM peak); avg launch {avg_launch_us:.2f} us")
+
+    # per-shape GEMV times (same graph technique, one shape per graph)
+    per_shape = {}
+    for (K, N) in wl2.shapes:
+        j = layer.index((K, N))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for r in range(R):
+                qw, sc, ze = reps[r][j]
+                awq.gemv(xs[K], qw, sc, ze, N=N, bits=4, out=ys[j])
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n_rep = max(1, 200 // R)
+            a.record(stream)
+            for _ in range(n_rep):
+                g.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / (n_rep * R)
+        gbs = gemv_bytes(1, N, K) / (us * 1e-6) / 1e9
+        per_shape[f"{K}x{N}"] = {"us": round(us, 3), "GBps": round(gbs, 1),
+                                 "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        log(f"  gemv K={K} N={N}: {us:.2f} us, {gbs:.1f} GB/s")
+        del g
+
+    # ------------------------------------------------------------------ prefill GEMM
+    wl4 = WL.workload(4)
+    M = 2048
+    gemm_res = {}
+    tot_flops, tot_ms = 0.0, 0.0
+    for i, (K, N) in enumerate(wl4.shapes):
+        with torch.cuda.stream(stream):
+            W = torch.from_numpy(wl4.weights(i)).to(dev)
+            qw, sc, ze = awq.quantize_pack(W, None, bits=4)
+            del W
+            x = torch.from_numpy(wl4.activations(M, i)).to(dev)
+            y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            for _ in range(3):
+                awq.gemm(x, qw, sc, ze, N=N, bits=4, out=y)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(args.gemm_iters):
+                awq.gemm(x, qw, sc, ze, N=N, bits=4, out=y)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / args.gemm_iters
+        flops = 2.0 * M * N * K
+        tf = flops / (ms * 1e-3) / 1e12
+        gemm_res[f"{K}x{N}"] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
+                                "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+        tot_flops += flops
+        tot_ms += ms
+        log(f"  gemm M={M} K={K} N={N}: {ms * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+        del qw, sc, ze, x, y
+    gemm_tflops = tot_flops / (tot_ms * 1e-3) / 1e12
+
+    # ------------------------------------------------------------------ offline path
+    offline = None
+    if not args.no_offline:
+        wl5 = WL.workload(5)
+        with torch.cuda.stream(stream):
+            W = torch.from_numpy(wl5.weights()).to(dev)
+            X = torch.from_numpy(wl5.calibration()).to(dev)
+            ws = torch.empty(awq.search_workspace_bytes(X.shape[0], W.shape[0], W.shape[1],
+                                                        len(wl5.alphas)), dtype=torch.uint8, device=dev)
+            for _ in range(2):
+                s, loss, best = awq.search_scale(W, X, wl5.alphas, bits=4, workspace=ws)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(5):
+                s, loss, best = awq.search_scale(W, X, wl5.alphas, bits=4, workspace=ws)
+            b.record(stream)
+            torch.cuda.synchronize()
+            search_ms = a.elapsed_time(b) / 5
+            a.record(stream)
+            for _ in range(20):
+                qp = awq.quantize_pack(W, s, bits=4)
+            b.record(stream)
+            torch.cuda.synchronize()
+            qp_us = a.elapsed_time(b) * 1e3 / 20
+        qp_bytes = W.numel() * 2 + W.shape[1] * 4 + W.numel() // 2 + 4 * W.numel() // 128
+        offline = {"search_4096x4096_T512_20alpha_ms": round(search_ms, 3),
+                   "search_loss_gemm_TFLOPs_incl_quant": round(
+                       20 * 2.0 * 512 * 4096 * 4096 / (search_ms * 1e-3) / 1e12, 1),
+                   "quantize_pack_4096x4096_us": round(qp_us, 2),
+                   "quantize_pack_GBps": round(qp_bytes / (qp_us * 1e-6) / 1e9, 1),
+                   "best_alpha": float(wl5.alphas[int(best.item())])}
+        log(f"offline: search {search_ms:.3f} ms, quantize_pack {qp_us:.1f} us")
+        del W, X, ws
+
+    # ------------------------------------------------------------------ CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(layer, wl2, shape_index, step_bytes)
+
+    out = {
+        "metric": METRIC,
+        "value": round(gemv_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 weights x fp16 activations, fp32 accumulate",
+        "data": "synthetic (seeded: W ~ N(0,0.02), x = lognormal(0,1.5) channel scale x N(0,1))",
+        "config": {"workload": "Llama-7B decoder-layer decode GEMV, M=1, int4 g128 asym",
+                   "shapes_KxN": [f"{K}x{N}" for K, N in layer], "M": 1, "bits": 4,
+                   "group_size": 128, "step_bytes": step_bytes, "cold_weight_replicas": R,
+                   "launch": "HIP graph replay"},
+        "roofline": {"bound": "hbm", "achieved": round(gemv_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gemv_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_gemv_int4<1>", "avg_launch_us": round(avg_launch_us, 3)},
+        "gemv_per_shape": per_shape,
+        "gemm": {"M": M, "TFLOPs": round(gemm_tflops, 1), "per_shape": gemm_res,
+                 "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1),
+                              "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                              "traffic": None, "kernel": "k_gemm<true,false>"}},
+        "offline": offline,
+        "cpu_baseline": cpu,
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "arch": getattr(props, "gcnArchName", "")},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(layer, wl2, shape_index, step_bytes):
+    """The oracle (not tuned) on one decode step of the layer, on the host cores."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()
+                            if d.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas_threads = 1
+    log("cpu baseline: oracle packing the layer (untimed) ...")
+    packs, xs = {}, {}
+    for (K, N), i in shape_index.items():
+        q, d, z = O.quantize(wl2.weights(i), None, 4)
+        packs[(K, N)] = (O.pack(q, 4), d, z)
+        xs[K] = wl2.activations(1, i)
+    times = []
+    t_budget = time.perf_counter()
+    while len(times) < 3 and (time.perf_counter() - t_budget) < 30:
+        t0 = time.perf_counter()
+        for K, N in layer:
+            qw, d, z = packs[(K, N)]
+            O.matmul(xs[K], qw, d, z, 4, K)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    log(f"cpu baseline: {t:.3f} s per decode step ({len(times)} reps)")
+    return {"value": round(step_bytes / t / 1e9, 3), "unit": "GB/s", "cores": blas_threads,
+            "kind": "oracle",
+            "sample": f"{len(times)} full decode steps of the Llama-7B layer (7 GEMVs, M=1) through "
+                      f"oracle.matmul: numpy unpack + fp64 dequantize (single-threaded) and fp64 "
+                      f"product (OpenBLAS, {blas_threads} threads); median {t:.3f} s per step; "
+                      f"host has {os.cpu_count()} logical CPUs"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

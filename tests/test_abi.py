@@ -1,0 +1,153 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+declared in include/awq.h, and rejects invalid arguments with the documented
+status before launching anything (so fake pointers are never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from weight_only_quantization_pack_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "awq.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS = 0, 1, 2, 3, 4, 5
+
+P = ctypes.c_void_p(0x10000)       # aligned fake device pointers (never used)
+P2 = ctypes.c_void_p(0x20000)
+P3 = ctypes.c_void_p(0x30000)
+P4 = ctypes.c_void_p(0x40000)
+P5 = ctypes.c_void_p(0x50000)
+MIS = ctypes.c_void_p(0x10008)     # 8-byte aligned only
+NUL = ctypes.c_void_p(0)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(awq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for must in ["awq_quantize_pack", "awq_search_scale", "awq_search_workspace_bytes",
+                 "awq_gemv", "awq_gemm", "awq_scale_activations", "awq_status_str"]:
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert sorted(n for n, _, _ in B.SIGNATURES) == header_functions()
+
+
+def test_status_strings(lib):
+    for code, name in B.STATUS.items():
+        assert lib.awq_status_str(code).decode() == name
+    assert lib.awq_status_str(99).decode() == "AWQ_ERR_UNKNOWN"
+
+
+def test_format_helpers(lib):
+    assert lib.awq_pack_format_version() == 1
+    assert lib.awq_packed_words_per_row(4096, 4) == 512
+    assert lib.awq_packed_words_per_row(4096, 3) == 384
+    assert lib.awq_packed_words_per_row(4096, 2) == 0
+    assert lib.awq_packed_words_per_row(0, 4) == 0
+
+
+def test_search_workspace_size(lib):
+    T, N, K, A = 512, 4096, 4096, 20
+    need = lib.awq_search_workspace_bytes(T, N, K, A)
+    assert need >= A * N * K * 2 + (A + 1) * K * 4
+    assert lib.awq_search_workspace_bytes(0, N, K, A) == 0
+    assert lib.awq_search_workspace_bytes(T, N, K, 0) == 0
+
+
+def qp(lib, W=P, s=NUL, N=256, K=512, bits=4, gs=128, zp=1, qw=P2, sc=P3, ze=P4):
+    return lib.awq_quantize_pack(W, s, N, K, bits, gs, zp, qw, sc, ze, NUL)
+
+
+def test_quantize_pack_validation(lib):
+    assert qp(lib, bits=2) == UNSUP
+    assert qp(lib, bits=8) == UNSUP
+    assert qp(lib, gs=64) == UNSUP
+    assert qp(lib, zp=0) == UNSUP
+    assert qp(lib, K=500) == SHAPE
+    assert qp(lib, K=0) == SHAPE
+    assert qp(lib, N=-1) == SHAPE
+    assert qp(lib, W=NUL) == NULL
+    assert qp(lib, qw=NUL) == NULL
+    assert qp(lib, W=MIS) == ALIGN
+    assert qp(lib, s=MIS) == ALIGN
+    assert qp(lib, W=NUL, qw=MIS) == NULL          # NULL reported before alignment
+    assert qp(lib, N=0, W=NUL) == OK               # empty call: nothing to do
+
+
+def mm(lib, fn, x=P, qw=P2, sc=P3, ze=P4, y=P5, M=1, N=256, K=512, bits=4, gs=128):
+    return getattr(lib, fn)(x, qw, sc, ze, y, M, N, K, bits, gs, NUL)
+
+
+@pytest.mark.parametrize("fn", ["awq_gemv", "awq_gemm"])
+def test_matmul_validation(lib, fn):
+    assert mm(lib, fn, bits=5) == UNSUP
+    assert mm(lib, fn, gs=32) == UNSUP
+    assert mm(lib, fn, K=129) == SHAPE
+    assert mm(lib, fn, N=-4) == SHAPE
+    assert mm(lib, fn, M=-1) == SHAPE
+    assert mm(lib, fn, y=NUL) == NULL
+    assert mm(lib, fn, sc=MIS) == ALIGN
+    assert mm(lib, fn, M=0, x=NUL) == OK
+    assert mm(lib, fn, N=0, x=NUL) == OK
+
+
+def test_gemv_and_gemm_specific_limits(lib):
+    assert mm(lib, "awq_gemv", M=17) == UNSUP
+    assert mm(lib, "awq_gemm", bits=3) == UNSUP
+    assert mm(lib, "awq_gemv", M=17, bits=3, x=NUL) == UNSUP
+
+
+def test_scale_activations_validation(lib):
+    assert lib.awq_scale_activations(P, P2, P3, 4, 100, NUL) == SHAPE
+    assert lib.awq_scale_activations(P, P2, P3, -1, 128, NUL) == SHAPE
+    assert lib.awq_scale_activations(P, NUL, P3, 4, 128, NUL) == NULL
+    assert lib.awq_scale_activations(P, P2, MIS, 4, 128, NUL) == ALIGN
+    assert lib.awq_scale_activations(NUL, NUL, NUL, 0, 128, NUL) == OK
+
+
+def search(lib, W=P, X=P2, T=64, N=256, K=512, alphas=(0.0, 0.5), bits=4, gs=128, zp=1,
+           s_out=P3, loss=NUL, best=NUL, ws=P4, ws_bytes=None):
+    a = (ctypes.c_float * max(len(alphas), 1))(*alphas)
+    n = len(alphas)
+    if ws_bytes is None:
+        ws_bytes = lib.awq_search_workspace_bytes(T, N, K, max(n, 1))
+    return lib.awq_search_scale(W, X, T, N, K, ctypes.cast(a, ctypes.c_void_p), n, bits, gs, zp,
+                                s_out, loss, best, ws, ws_bytes, NUL)
+
+
+def test_search_validation(lib):
+    assert search(lib, bits=2) == UNSUP
+    assert search(lib, zp=0) == UNSUP
+    assert search(lib, alphas=()) == UNSUP
+    assert search(lib, alphas=tuple([0.5] * 65)) == UNSUP
+    assert search(lib, T=8193) == UNSUP
+    assert search(lib, T=0) == SHAPE
+    assert search(lib, K=130) == SHAPE
+    assert search(lib, W=NUL) == NULL
+    assert search(lib, s_out=MIS) == ALIGN
+    assert search(lib, loss=MIS) == ALIGN
+    good = lib.awq_search_workspace_bytes(64, 256, 512, 2)
+    assert search(lib, ws_bytes=good - 1) == WS
+
+
+def test_binding_refuses_when_library_missing(monkeypatch, tmp_path):
+    monkeypatch.setenv("AWQ_MI355X_LIB", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(B.AwqError):
+        B.load_library()

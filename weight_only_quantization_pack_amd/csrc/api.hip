@@ -1,0 +1,137 @@
+// C ABI of libawq: argument validation on the host, then dispatch to the
+// kernel launchers.  Nothing here touches the GPU before every argument has
+// been checked, so invalid calls never launch and never write an output.
+#include "awq_internal.h"
+
+namespace {
+
+constexpr int kMaxGemvM = 16;
+constexpr int kMaxT = 8192;        // exact fp64 |x| sums need T < 2^13
+constexpr int kMaxAlpha = 64;
+
+int check_ptr(const void* p) {
+    if (p == nullptr) return AWQ_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(p) & 15u) return AWQ_ERR_ALIGN;
+    return AWQ_OK;
+}
+
+// First non-OK status of a list of required pointers; NULL errors are
+// reported before alignment errors.
+int check_ptrs(std::initializer_list<const void*> ps) {
+    for (const void* p : ps) if (p == nullptr) return AWQ_ERR_NULL;
+    for (const void* p : ps) if (check_ptr(p) != AWQ_OK) return AWQ_ERR_ALIGN;
+    return AWQ_OK;
+}
+
+int check_quant_params(int bits, int group_size, int zero_point) {
+    if (bits != 3 && bits != 4) return AWQ_ERR_UNSUPPORTED;
+    if (group_size != awq::kGroup) return AWQ_ERR_UNSUPPORTED;
+    if (zero_point != 1) return AWQ_ERR_UNSUPPORTED;
+    return AWQ_OK;
+}
+
+int check_nk(int N, int K) {
+    if (N < 0 || K <= 0) return AWQ_ERR_SHAPE;
+    if (K % awq::kGroup != 0) return AWQ_ERR_SHAPE;
+    return AWQ_OK;
+}
+
+int hip_status(int err) { return err == 0 ? AWQ_OK : AWQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* awq_status_str(int status) {
+    switch (status) {
+        case AWQ_OK: return "AWQ_OK";
+        case AWQ_ERR_NULL: return "AWQ_ERR_NULL";
+        case AWQ_ERR_SHAPE: return "AWQ_ERR_SHAPE";
+        case AWQ_ERR_UNSUPPORTED: return "AWQ_ERR_UNSUPPORTED";
+        case AWQ_ERR_ALIGN: return "AWQ_ERR_ALIGN";
+        case AWQ_ERR_WORKSPACE: return "AWQ_ERR_WORKSPACE";
+        case AWQ_ERR_HIP: return "AWQ_ERR_HIP";
+        default: return "AWQ_ERR_UNKNOWN";
+    }
+}
+
+int awq_pack_format_version(void) { return 1; }
+
+size_t awq_packed_words_per_row(int K, int bits) {
+    if (K <= 0) return 0;
+    if (bits == 4) return (size_t)K / 8;
+    if (bits == 3) return 3 * ((size_t)K / 32);
+    return 0;
+}
+
+int awq_quantize_pack(const void* W, const float* s, int N, int K, int bits, int group_size,
+                      int zero_point, void* qweight, void* scales, void* zeros, void* stream) {
+    int st = check_quant_params(bits, group_size, zero_point);
+    if (st) return st;
+    if ((st = check_nk(N, K))) return st;
+    if (N == 0) return AWQ_OK;
+    if ((st = check_ptrs({W, qweight, scales, zeros}))) return st;
+    if (s != nullptr && (st = check_ptr(s))) return st;
+    return hip_status(awq::launch_quantize_pack(W, s, N, K, bits, qweight, scales, zeros,
+                                                (hipStream_t)stream));
+}
+
+int awq_scale_activations(const void* x, const float* s, void* x_out, int M, int K, void* stream) {
+    if (M < 0 || K <= 0 || K % awq::kGroup != 0) return AWQ_ERR_SHAPE;
+    if (M == 0) return AWQ_OK;
+    int st = check_ptrs({x, s, x_out});
+    if (st) return st;
+    return hip_status(awq::launch_scale_activations(x, s, x_out, M, K, (hipStream_t)stream));
+}
+
+size_t awq_search_workspace_bytes(int T, int N, int K, int n_alpha) {
+    if (T <= 0 || N <= 0 || K <= 0 || n_alpha <= 0) return 0;
+    return awq::search_workspace_bytes(T, N, K, n_alpha);
+}
+
+int awq_search_scale(const void* W, const void* X_cal, int T, int N, int K, const float* alphas,
+                     int n_alpha, int bits, int group_size, int zero_point, float* s_out,
+                     float* loss_out, int* best_out, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    int st = check_quant_params(bits, group_size, zero_point);
+    if (st) return st;
+    if (n_alpha < 1 || n_alpha > kMaxAlpha) return AWQ_ERR_UNSUPPORTED;
+    if (T > kMaxT) return AWQ_ERR_UNSUPPORTED;
+    if (T <= 0 || N <= 0) return AWQ_ERR_SHAPE;
+    if ((st = check_nk(N, K))) return st;
+    if (alphas == nullptr) return AWQ_ERR_NULL;
+    if ((st = check_ptrs({W, X_cal, s_out, workspace}))) return st;
+    if (loss_out != nullptr && (st = check_ptr(loss_out))) return st;
+    if (best_out != nullptr && (st = check_ptr(best_out))) return st;
+    if (workspace_bytes < awq::search_workspace_bytes(T, N, K, n_alpha)) return AWQ_ERR_WORKSPACE;
+    return hip_status(awq::launch_search(W, X_cal, T, N, K, alphas, n_alpha, bits, s_out,
+                                         loss_out, best_out, workspace, (hipStream_t)stream));
+}
+
+int awq_gemv(const void* x, const void* qweight, const void* scales, const void* zeros, void* y,
+             int M, int N, int K, int bits, int group_size, void* stream) {
+    int st = check_quant_params(bits, group_size, 1);
+    if (st) return st;
+    if (M > kMaxGemvM) return AWQ_ERR_UNSUPPORTED;
+    if (M < 0) return AWQ_ERR_SHAPE;
+    if ((st = check_nk(N, K))) return st;
+    if (M == 0 || N == 0) return AWQ_OK;
+    if ((st = check_ptrs({x, qweight, scales, zeros, y}))) return st;
+    return hip_status(awq::launch_gemv(x, qweight, scales, zeros, y, M, N, K, bits,
+                                       (hipStream_t)stream));
+}
+
+int awq_gemm(const void* x, const void* qweight, const void* scales, const void* zeros, void* y,
+             int M, int N, int K, int bits, int group_size, void* stream) {
+    int st = check_quant_params(bits, group_size, 1);
+    if (st) return st;
+    if (bits != 4) return AWQ_ERR_UNSUPPORTED;
+    if (M < 0) return AWQ_ERR_SHAPE;
+    if ((st = check_nk(N, K))) return st;
+    if (M == 0 || N == 0) return AWQ_OK;
+    if ((st = check_ptrs({x, qweight, scales, zeros, y}))) return st;
+    return hip_status(awq::launch_gemm(x, qweight, scales, zeros, y, M, N, K,
+                                       (hipStream_t)stream));
+}
+
+}  // extern "C"

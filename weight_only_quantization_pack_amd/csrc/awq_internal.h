@@ -1,0 +1,88 @@
+// Internal declarations shared by the HIP sources of libawq (gfx950 only).
+//
+// The whole library is compiled with -ffp-contract=off: every fused
+// multiply-add in these sources is written out with __builtin_fmaf, so the
+// quantizer's fp32 arithmetic is exactly the IEEE sequence it states.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <initializer_list>
+
+#include "../../include/awq.h"
+
+namespace awq {
+
+constexpr int kGroup = 128;          // q_group_size
+constexpr int kWave = 64;            // CDNA wavefront width
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ uint16_t half_bits(_Float16 h) { return __builtin_bit_cast(uint16_t, h); }
+__device__ __forceinline__ _Float16 bits_half(uint16_t b) { return __builtin_bit_cast(_Float16, b); }
+
+// Largest fp16 value <= d, for positive finite d >= 2^-24: convert to nearest
+// (v_cvt_f16_f32, round-half-even, fp16 denormals kept) and step one fp16
+// down when that rounded up.  +inf from overflow steps down to 65504.
+__device__ __forceinline__ uint16_t f16_bits_round_down(float d) {
+    _Float16 h = (_Float16)d;
+    uint16_t b = half_bits(h);
+    if ((float)h > d) b = (uint16_t)(b - 1);
+    return b;
+}
+
+// Group parameters of one quantization group from its (already reduced)
+// minimum and maximum of v = w * s.  All IEEE fp32, correctly rounded
+// division, round-half-even rint.
+struct GroupParams {
+    float delta;       // D as fp32 (exactly the stored fp16 value)
+    float zero;        // integer zero point z, as fp32
+    uint16_t dbits;    // the stored fp16 scale
+};
+
+template <int Q>
+__device__ __forceinline__ GroupParams group_params(float vmin, float vmax) {
+    float lo = fminf(vmin, 0.0f);
+    float hi = fmaxf(vmax, 0.0f);
+    float span = fmaxf(hi - lo, 1e-5f);
+    float d32 = span / (float)Q;
+    GroupParams p;
+    p.dbits = f16_bits_round_down(d32);
+    p.delta = (float)bits_half(p.dbits);
+    float z = __builtin_rintf(-lo / p.delta);
+    p.zero = fminf(fmaxf(z, 0.0f), (float)Q);
+    return p;
+}
+
+template <int Q>
+__device__ __forceinline__ uint32_t quant_code(float v, const GroupParams& p) {
+    float c = __builtin_rintf(v / p.delta) + p.zero;
+    c = fminf(fmaxf(c, 0.0f), (float)Q);
+    return (uint32_t)c;
+}
+
+// ---------------------------------------------------------------------------
+// host-side launchers (each .hip file owns its kernels); they return 0 or a
+// hipError_t value.  Arguments have been validated by the C ABI layer.
+// ---------------------------------------------------------------------------
+int launch_quantize_pack(const void* W, const float* s, int N, int K, int bits,
+                         void* qweight, void* scales, void* zeros, hipStream_t st);
+int launch_scale_activations(const void* x, const float* s, void* x_out, int M, int K,
+                             hipStream_t st);
+int launch_gemv(const void* x, const void* qweight, const void* scales, const void* zeros,
+                void* y, int M, int N, int K, int bits, hipStream_t st);
+int launch_gemm(const void* x, const void* qweight, const void* scales, const void* zeros,
+                void* y, int M, int N, int K, hipStream_t st);
+size_t search_workspace_bytes(int T, int N, int K, int n_alpha);
+size_t loss_gemm_tiles(int T, int N);
+int launch_loss_gemm(const void* X, const void* D, int T, int N, int K, int n_batch,
+                     double* partials, hipStream_t st);
+int launch_search(const void* W, const void* X_cal, int T, int N, int K, const float* alphas,
+                  int n_alpha, int bits, float* s_out, float* loss_out, int* best_out,
+                  void* workspace, hipStream_t st);
+
+}  // namespace awq

@@ -1,0 +1,181 @@
+// AWQ scale search on the GPU (llm-awq README "Usage" step 1, --run_awq;
+// scale from offline activation statistics, section 02.02 "AWQ" of the VPTQ
+// blog; saliency from activation magnitude, "Applying AWQ with AutoAWQ").
+//
+//   1. s_x[k]   = mean_t |X_cal[t][k]|            exact fp64 sums
+//   2. s_i[k]   = fp32(pow(max(s_x[k], 1e-4), alpha_i))   fp64 pow
+//   3. D_i      = fp16(W - w_hat_i / s_i)         same quantizer as quantize_pack
+//   4. L_i      = sum over tiles of sum (X_cal . D_i^T)^2 / (T N)   MFMA GEMM
+//   5. best     = first i with the smallest L_i; s_out = s_best
+// All alphas are processed in one launch per stage (the D_i of every alpha
+// live side by side in the workspace), so the loss GEMM grid has
+// n_alpha x tiles workgroups.  The reductions run in a fixed order, so the
+// result does not depend on scheduling.
+#include "awq_internal.h"
+
+namespace awq {
+
+namespace {
+
+constexpr int kMaxAlpha = 64;
+struct AlphaGrid { float a[kMaxAlpha]; };
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+struct Layout {
+    size_t sx, sall, D, part, total;
+};
+
+Layout layout(int T, int N, int K, int n_alpha) {
+    Layout L;
+    size_t off = 0;
+    L.sx = off;   off += align256((size_t)K * sizeof(float));
+    L.sall = off; off += align256((size_t)n_alpha * K * sizeof(float));
+    L.D = off;    off += align256((size_t)n_alpha * N * K * sizeof(_Float16));
+    L.part = off; off += align256((size_t)n_alpha * loss_gemm_tiles(T, N) * sizeof(double));
+    L.total = off;
+    return L;
+}
+
+// Block: 64 columns x 4 row phases.  Sums of |fp16| in fp64 are exact for
+// T < 2^13, so the partial order cannot change the result.
+__global__ __launch_bounds__(256) void k_act_stat(const _Float16* __restrict__ X, int T, int K,
+                                                 float* __restrict__ s_x) {
+    const int kk = threadIdx.x & 63, ph = threadIdx.x >> 6;
+    const int k = blockIdx.x * 64 + kk;
+    double sum = 0.0;
+    if (k < K)
+        for (int t = ph; t < T; t += 4) sum += fabs((double)X[(size_t)t * K + k]);
+    __shared__ double part[4][64];
+    part[ph][kk] = sum;
+    __syncthreads();
+    if (ph == 0 && k < K) {
+        const double tot = ((part[0][kk] + part[1][kk]) + part[2][kk]) + part[3][kk];
+        s_x[k] = (float)(tot / (double)T);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_candidate_scales(const float* __restrict__ s_x, int K,
+                                                         AlphaGrid grid, int n_alpha,
+                                                         float* __restrict__ s_all) {
+    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (long long)n_alpha * K) return;
+    const int i = (int)(t / K), k = (int)(t % K);
+    const double base = fmax((double)s_x[k], 1e-4);
+    s_all[t] = (float)pow(base, (double)grid.a[i]);
+}
+
+// Quantization error of every alpha: one lane = 8 consecutive weights of one
+// row, 16 lanes = one group (same lane layout as the int4 quantize kernel;
+// the error does not depend on the packed format).
+template <int Q>
+__global__ __launch_bounds__(256) void k_quant_err(const uint4* __restrict__ W,
+                                                  const float* __restrict__ s_all, int K,
+                                                  long long n_chunks, uint4* __restrict__ D) {
+    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int alpha = blockIdx.y;
+    const bool active = t < n_chunks;
+    const float* s = s_all + (size_t)alpha * K;
+    const int k0 = active ? (int)(t % (K / 8)) * 8 : 0;
+    float w[8], v[8], sv[8];
+    if (active) {
+        const uint4 raw = W[t];
+        const _Float16* h = reinterpret_cast<const _Float16*>(&raw);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { w[i] = (float)h[i]; sv[i] = s[k0 + i]; v[i] = w[i] * sv[i]; }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { w[i] = 0.f; sv[i] = 1.f; v[i] = 0.f; }
+    }
+    float mn = v[0], mx = v[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) { mn = fminf(mn, v[i]); mx = fmaxf(mx, v[i]); }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, m, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, m, 16));
+    }
+    const GroupParams p = group_params<Q>(mn, mx);
+    uint4 out;
+    _Float16* o = reinterpret_cast<_Float16*>(&out);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float q = (float)quant_code<Q>(v[i], p);
+        const float w_hat = (q - p.zero) * p.delta;          // exact in fp32
+        o[i] = (_Float16)(w[i] - w_hat / sv[i]);
+    }
+    if (active) D[(size_t)alpha * (n_chunks) + t] = out;
+}
+
+// One workgroup: fixed-order fp64 sums of the loss partials, first argmin.
+__global__ __launch_bounds__(256) void k_select(const double* __restrict__ partials, int n_tiles,
+                                               int n_alpha, double inv_count,
+                                               const float* __restrict__ s_all, int K,
+                                               float* __restrict__ s_out,
+                                               float* __restrict__ loss_out,
+                                               int* __restrict__ best_out) {
+    __shared__ double loss[kMaxAlpha];
+    __shared__ int best_s;
+    const int tid = threadIdx.x;
+    if (tid < n_alpha) {
+        double s = 0.0;
+        for (int j = 0; j < n_tiles; ++j) s += partials[(size_t)tid * n_tiles + j];
+        loss[tid] = s * inv_count;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int b = 0;
+        for (int i = 1; i < n_alpha; ++i)
+            if (loss[i] < loss[b]) b = i;
+        best_s = b;
+        if (best_out) *best_out = b;
+    }
+    __syncthreads();
+    if (loss_out && tid < n_alpha) loss_out[tid] = (float)loss[tid];
+    const float* sb = s_all + (size_t)best_s * K;
+    for (int k = tid; k < K; k += blockDim.x) s_out[k] = sb[k];
+}
+
+}  // namespace
+
+size_t search_workspace_bytes(int T, int N, int K, int n_alpha) {
+    return layout(T, N, K, n_alpha).total;
+}
+
+int launch_search(const void* W, const void* X_cal, int T, int N, int K, const float* alphas,
+                  int n_alpha, int bits, float* s_out, float* loss_out, int* best_out,
+                  void* workspace, hipStream_t st) {
+    const Layout L = layout(T, N, K, n_alpha);
+    char* ws = static_cast<char*>(workspace);
+    float* s_x = reinterpret_cast<float*>(ws + L.sx);
+    float* s_all = reinterpret_cast<float*>(ws + L.sall);
+    _Float16* D = reinterpret_cast<_Float16*>(ws + L.D);
+    double* part = reinterpret_cast<double*>(ws + L.part);
+
+    AlphaGrid grid{};
+    for (int i = 0; i < n_alpha; ++i) grid.a[i] = alphas[i];
+
+    hipLaunchKernelGGL(k_act_stat, dim3((K + 63) / 64), dim3(256), 0, st,
+                       (const _Float16*)X_cal, T, K, s_x);
+    const long long nsk = (long long)n_alpha * K;
+    hipLaunchKernelGGL(k_candidate_scales, dim3((unsigned)((nsk + 255) / 256)), dim3(256), 0, st,
+                       s_x, K, grid, n_alpha, s_all);
+    const long long n_chunks = (long long)N * K / 8;
+    const dim3 qgrid((unsigned)((n_chunks + 255) / 256), n_alpha);
+    if (bits == 4)
+        hipLaunchKernelGGL(k_quant_err<15>, qgrid, dim3(256), 0, st, (const uint4*)W, s_all, K,
+                           n_chunks, (uint4*)D);
+    else
+        hipLaunchKernelGGL(k_quant_err<7>, qgrid, dim3(256), 0, st, (const uint4*)W, s_all, K,
+                           n_chunks, (uint4*)D);
+    int err = (int)hipGetLastError();
+    if (err) return err;
+    err = launch_loss_gemm(X_cal, D, T, N, K, n_alpha, part, st);
+    if (err) return err;
+    const int n_tiles = (int)loss_gemm_tiles(T, N);
+    hipLaunchKernelGGL(k_select, dim3(1), dim3(256), 0, st, part, n_tiles, n_alpha,
+                       1.0 / ((double)T * (double)N), s_all, K, s_out, loss_out, best_out);
+    return (int)hipGetLastError();
+}
+
+}  // namespace awq
