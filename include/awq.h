@@ -35,16 +35,25 @@
  *   - M == 0 or N == 0 is a valid empty call: it returns AWQ_OK and
  *     launches nothing.
  *
- * Packed weight format, version 1 (chosen for gfx950 MFMA/VALU unpacking):
- *   bits = 4: qweight is uint32 [N][K/8].  Word j of row n holds the codes
- *     of k = 8j..8j+7.  Code 8j+2t is at bits 4t..4t+3 and code 8j+2t+1 at
- *     bits 16+4t..19+4t (t = 0..3), so ((w >> 4t) & 0x000F000F) | 0x64006400
- *     is the fp16 pair (1024 + q[8j+2t], 1024 + q[8j+2t+1]).
- *   bits = 3: qweight is uint32 [N][3K/32].  Each run of 32 codes of a row
- *     (k = 32c..32c+31) is a 96-bit little-endian bit stream, code i at
- *     stream bits 3i..3i+2, stored as 3 consecutive words.
- *   scales: fp16 [N][G], the group scale D.  zeros: fp16 [N][G], the integer
- *     zero point z in 0..Q stored exactly.
+ * Packed weight format, version 2 (chosen for gfx950 MFMA operand loads):
+ *   Row words.  bits = 4: word j of row n holds the codes of k = 8j..8j+7;
+ *     code 8j+2t is at bits 4t..4t+3 and code 8j+2t+1 at bits 16+4t..19+4t
+ *     (t = 0..3), so ((w >> 4t) & 0x000F000F) | 0x64006400 is the fp16 pair
+ *     (1024 + q[8j+2t], 1024 + q[8j+2t+1]).  bits = 3: each run of 32 codes
+ *     k = 32c..32c+31 is a 96-bit little-endian bit stream (code i at stream
+ *     bits 3i..3i+2) held in 3 words.
+ *   Tiles.  Rows are taken 16 at a time (row block b = rows 16b..16b+15,
+ *     padded with zero rows past N).  Tile (b, g) holds group g (k = 128g ..
+ *     128g+127) of the 16 rows of block b as 64 lane slots; slot s = 16h + j
+ *     holds the row words of row 16b + j that cover k = 128g + 32h ..
+ *     128g + 32h + 31 (4 words for bits 4, 3 for bits 3).  qweight is the
+ *     array of tiles [ceil(N/16)][G][64][4 or 3] uint32: one tile is one
+ *     contiguous 1 KB (768 B for bits 3) wave load whose slots are the
+ *     v_mfma_f32_16x16x32_f16 operand layout.
+ *   scales, zeros: fp16 [ceil(N/16)][G][16], the same tiling: the group
+ *     scale D[n][g] and the integer zero point z[n][g] (0..Q, stored
+ *     exactly) of row n sit at [n / 16][g][n % 16]; padding rows hold 0.
+ *     One group's 16 scales are one 32-byte load next to their tile.
  *   Dequantized weight: w_hat[n][k] = (q[n][k] - z[n][g]) * D[n][g].
  */
 #ifndef AWQ_MI355X_H
@@ -69,12 +78,16 @@ typedef enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* awq_status_str(int status);
 
-/* Version of the packed weight format described above (1). */
+/* Version of the packed weight format described above (2). */
 int awq_pack_format_version(void);
 
 /* uint32 words per packed row: K/8 for bits 4, 3K/32 for bits 3
- * (0 for unsupported bits). */
+ * (0 for unsupported bits or K <= 0). */
 size_t awq_packed_words_per_row(int K, int bits);
+
+/* uint32 words of a whole packed matrix: 16 * ceil(N/16) * words_per_row
+ * (0 for invalid arguments). */
+size_t awq_packed_words(int N, int K, int bits);
 
 /*
  * awq_quantize_pack -- round-to-nearest group quantization of W*diag(s),
@@ -83,9 +96,10 @@ size_t awq_packed_words_per_row(int K, int bits);
  *
  *   W        fp16 [N][K]   weights, row-major (nn.Linear layout)
  *   s        fp32 [K]      per-input-channel scale, or NULL for s == 1
- *   qweight  uint32 [N][words_per_row]  out, format above
- *   scales   fp16 [N][G]   out, D = largest fp16 <= max(hi - lo, 1e-5) / Q
- *   zeros    fp16 [N][G]   out, z = clamp(rint(-lo / D), 0, Q)
+ *   qweight  uint32 [awq_packed_words(N, K, bits)]  out, format above
+ *            (padding rows of the last block are written as zeros)
+ *   scales   fp16 [ceil(N/16)][G][16]  out, D = largest fp16 <= max(hi - lo, 1e-5) / Q
+ *   zeros    fp16 [ceil(N/16)][G][16]  out, z = clamp(rint(-lo / D), 0, Q)
  * with, per (n, g), v = fp32(W) * s, lo = min(0, min v), hi = max(0, max v),
  * and q = clamp(rint(v / D) + z, 0, Q); all fp32 IEEE, round-half-even,
  * correctly rounded division.

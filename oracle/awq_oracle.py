@@ -48,7 +48,7 @@ SUPPORTED_BITS = (3, 4)
 SPAN_FLOOR = np.float32(1e-5)      # reading: (hi - lo) floored before /Q
 STAT_FLOOR = 1e-4                  # reading: s_x floored before the power
 
-PACK_FORMAT_VERSION = 1
+PACK_FORMAT_VERSION = 2
 
 
 def levels(bits: int) -> int:
@@ -182,18 +182,25 @@ def dequantize(q: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
 
 
 # ---------------------------------------------------------------------------
-# a6: packing (format version 1, chosen for gfx950)
+# a6: packing (format version 2, chosen for gfx950)
 # ---------------------------------------------------------------------------
-def pack(q: np.ndarray, bits: int) -> np.ndarray:
-    """Pack codes q uint8 [N][K] into uint32 words, row by row.
+ROW_BLOCK = 16          # rows of one packed tile
+QUARTER = 32            # codes of one lane slot in a tile
 
-    bits=4: word j of row n holds codes k = 8j..8j+7.  Code 8j+2t sits at
-    bits 4t..4t+3 and code 8j+2t+1 at bits 16+4t..19+4t (t = 0..3), so that
-    (word >> 4t) & 0x000F000F holds the pair (q[8j+2t], q[8j+2t+1]) in its
-    two 16-bit halves.  Result shape [N][K/8].
-    bits=3: each run of 32 codes k = 32c..32c+31 is a 96-bit little-endian
-    bit stream (code i at stream bits 3i..3i+2) stored as 3 words.  Result
-    shape [N][3K/32].
+
+def words_per_quarter(bits: int) -> int:
+    return 4 if bits == 4 else 3
+
+
+def pack_rows(q: np.ndarray, bits: int) -> np.ndarray:
+    """Bit-pack each row of codes q uint8 [N][K] into uint32 words [N][W].
+
+    bits=4 (W = K/8): word j of a row holds codes k = 8j..8j+7; code 8j+2t
+    is at bits 4t..4t+3 and code 8j+2t+1 at bits 16+4t..19+4t (t = 0..3),
+    so (word >> 4t) & 0x000F000F holds the pair (q[8j+2t], q[8j+2t+1]) in
+    its two 16-bit halves.
+    bits=3 (W = 3K/32): each run of 32 codes k = 32c..32c+31 is a 96-bit
+    little-endian bit stream (code i at stream bits 3i..3i+2) in 3 words.
     """
     q = np.asarray(q, dtype=np.uint8)
     N, K = q.shape
@@ -217,23 +224,76 @@ def pack(q: np.ndarray, bits: int) -> np.ndarray:
     return out.reshape(N, 3 * (K // 32))
 
 
-def unpack(words: np.ndarray, bits: int, K: int) -> np.ndarray:
-    """Inverse of ``pack``: read every code back bit by bit."""
+def pack(q: np.ndarray, bits: int) -> np.ndarray:
+    """Packed weights, format 2: tiles of 16 rows x one 128-code group.
+
+    The row words of ``pack_rows`` are regrouped so that the 16 rows of
+    block b and the group g form one contiguous tile of 64 lane slots:
+    slot s = 16h + j holds the words of row n = 16b + j that cover codes
+    k = 128g + 32h .. 128g + 32h + 31 (4 words for bits 4, 3 for bits 3).
+    Result shape [ceil(N/16)][G][64][4 or 3]; rows past N are zero.
+    Reading: the pages say only that the packing is chosen per platform
+    ("platform-aware weight packing"); this order makes one tile one
+    contiguous 1 KB load whose lane slots are the MFMA operand layout.
+    """
+    rows = pack_rows(q, bits)
+    N, K = np.asarray(q).shape
+    W = words_per_quarter(bits)
+    NB, G = -(-N // ROW_BLOCK), K // GROUP_SIZE
+    padded = np.zeros((NB * ROW_BLOCK, rows.shape[1]), dtype=np.uint32)
+    padded[:N] = rows
+    t = padded.reshape(NB, ROW_BLOCK, G, 4, W)          # [b][j][g][h][i]
+    return np.ascontiguousarray(t.transpose(0, 2, 3, 1, 4)).reshape(NB, G, 64, W)
+
+
+def tile_params(p: np.ndarray) -> np.ndarray:
+    """Scales or zeros [N][G] -> format-2 layout [ceil(N/16)][G][16] (zero padded).
+
+    Element (n, g) moves to [n // 16][g][n % 16]: the 16 rows of a row block
+    sit side by side for each group, next to the tile they scale.
+    """
+    p = np.asarray(p)
+    N, G = p.shape
+    NB = -(-N // ROW_BLOCK)
+    out = np.zeros((NB * ROW_BLOCK, G), dtype=p.dtype)
+    out[:N] = p
+    return np.ascontiguousarray(out.reshape(NB, ROW_BLOCK, G).transpose(0, 2, 1))
+
+
+def untile_params(t: np.ndarray, N: int) -> np.ndarray:
+    """Inverse of ``tile_params`` ([ceil(N/16)][G][16] -> [N][G])."""
+    t = np.asarray(t)
+    NB, G = t.shape[0], t.shape[1]
+    return np.ascontiguousarray(t.reshape(NB, G, ROW_BLOCK).transpose(0, 2, 1)).reshape(NB * ROW_BLOCK, G)[:N]
+
+
+def packed_words(N: int, K: int, bits: int) -> int:
+    """uint32 words of a packed weight matrix (rows padded to 16)."""
+    return -(-N // ROW_BLOCK) * ROW_BLOCK * packed_words_per_row(K, bits)
+
+
+def unpack(words: np.ndarray, bits: int, K: int, N: int | None = None) -> np.ndarray:
+    """Inverse of ``pack``: locate every code's bits one by one."""
+    W = words_per_quarter(bits)
     words = np.asarray(words, dtype=np.uint32)
-    N = words.shape[0]
+    NB = words.size // ((K // GROUP_SIZE) * 64 * W)
+    t = words.reshape(NB, K // GROUP_SIZE, 64, W)
+    N = NB * ROW_BLOCK if N is None else N
     q = np.zeros((N, K), dtype=np.uint8)
     for k in range(K):
+        g, r = divmod(k, GROUP_SIZE)
+        h, kk = divmod(r, QUARTER)                 # quarter and code within it
         for b in range(bits):
             if bits == 4:
-                j, r = divmod(k, 8)
-                pos = 4 * (r // 2) + 16 * (r % 2) + b
-                w = words[:, j]
+                i, e = divmod(kk, 8)
+                pos = 4 * (e // 2) + 16 * (e % 2) + b
             else:
-                c, i = divmod(k, 32)
-                p = 3 * i + b
-                w = words[:, 3 * c + p // 32]
-                pos = p % 32
-            q[:, k] |= (((w >> np.uint32(pos)) & np.uint32(1)) << np.uint32(b)).astype(np.uint8)
+                p = 3 * kk + b
+                i, pos = divmod(p, 32)
+            for n in range(N):
+                blk, j = divmod(n, ROW_BLOCK)
+                w = t[blk, g, 16 * h + j, i]
+                q[n, k] |= np.uint8(((int(w) >> pos) & 1) << b)
     return q
 
 
@@ -264,21 +324,31 @@ def matmul(x: np.ndarray, qweight: np.ndarray, scales: np.ndarray,
     [P1] feature list: the 4-bit linear layer and its context (GEMM) and
     decode (GEMV) kernels compute this one product.
     """
-    q = unpack_fast(qweight, bits, K)
+    N = np.asarray(scales).shape[0]
+    q = unpack_fast(qweight, bits, K, N)
     w_hat = dequantize(q, scales, zeros)
     return np.asarray(x, dtype=np.float16).astype(np.float64) @ w_hat.T
 
 
-def unpack_fast(words: np.ndarray, bits: int, K: int) -> np.ndarray:
+def tiles_to_rows(words: np.ndarray, bits: int, K: int) -> np.ndarray:
+    """Row words [ceil(N/16)*16][W] of a format-2 array (inverse regrouping)."""
+    W = words_per_quarter(bits)
+    t = np.asarray(words, dtype=np.uint32).reshape(-1, K // GROUP_SIZE, 4, ROW_BLOCK, W)
+    NB = t.shape[0]                                            # [b][g][h][j][i]
+    return np.ascontiguousarray(t.transpose(0, 3, 1, 2, 4)).reshape(NB * ROW_BLOCK, -1)
+
+
+def unpack_fast(words: np.ndarray, bits: int, K: int, N: int | None = None) -> np.ndarray:
     """Vectorised inverse of ``pack`` (same format; checked against ``unpack``)."""
-    words = np.asarray(words, dtype=np.uint32)
-    N = words.shape[0]
+    rows = tiles_to_rows(words, bits, K)
+    N = rows.shape[0] if N is None else N
+    rows = rows[:N]
     if bits == 4:
-        w = words.reshape(N, K // 8, 1)
+        w = rows.reshape(N, K // 8, 1)
         r = np.arange(8, dtype=np.uint32)
         shift = 4 * (r // 2) + 16 * (r % 2)
         return ((w >> shift[None, None, :]) & np.uint32(15)).astype(np.uint8).reshape(N, K)
-    w = words.reshape(N, K // 32, 3).astype(np.uint64)
+    w = rows.reshape(N, K // 32, 3).astype(np.uint64)
     stream_lo = w[:, :, 0] | (w[:, :, 1] << np.uint64(32))      # bits 0..63
     stream_hi = w[:, :, 2]                                       # bits 64..95
     q = np.zeros((N, K // 32, 32), dtype=np.uint8)
@@ -299,7 +369,14 @@ def matmul_rows(x: np.ndarray, qweight: np.ndarray, scales: np.ndarray,
                 zeros: np.ndarray, bits: int, K: int, rows) -> np.ndarray:
     """Output columns y[:, rows] only (for sampled checks at full size)."""
     rows = np.asarray(rows)
-    return matmul(x, qweight[rows], scales[rows], zeros[rows], bits, K)
+    W = words_per_quarter(bits)
+    t = np.asarray(qweight, dtype=np.uint32).reshape(-1, K // GROUP_SIZE, 4, ROW_BLOCK, W)
+    blk, j = rows // ROW_BLOCK, rows % ROW_BLOCK
+    sel = t[blk, :, :, j, :]                                   # [len(rows)][G][h][i]
+    q = unpack_fast(sel[:, :, :, None, :].repeat(ROW_BLOCK, axis=3), bits, K)
+    q = q.reshape(len(rows), ROW_BLOCK, K)[:, 0, :]
+    w_hat = dequantize(q, scales[rows], zeros[rows])
+    return np.asarray(x, dtype=np.float16).astype(np.float64) @ w_hat.T
 
 
 # ---------------------------------------------------------------------------

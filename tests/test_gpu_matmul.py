@@ -39,7 +39,8 @@ def workload_layer(w, shape_index, bits=4):
 
 def run(fn, x, qw, d, z, N, bits):
     import torch
-    y = getattr(awq, fn)(dev(x), dev(qw), dev(d), dev(z), N=N, bits=bits)
+    y = getattr(awq, fn)(dev(x), dev(qw.reshape(-1)), dev(O.tile_params(d)), dev(O.tile_params(z)),
+                         N=N, bits=bits)
     torch.cuda.synchronize()
     return host(y).astype(np.float64)
 
@@ -158,7 +159,7 @@ def test_no_write_past_output_and_repeatable(gpu, fn):
     x = WL.random_activations(M, K, seed=13)
     qw, d, z = packed(W, 4)
     y, raw, n = guarded_empty((M, N), torch.float16)
-    args = (dev(x), dev(qw), dev(d), dev(z))
+    args = (dev(x), dev(qw.reshape(-1)), dev(O.tile_params(d)), dev(O.tile_params(z)))
     announce(fn, "guarded", M, N, K)
     getattr(awq, fn)(*args, N=N, bits=4, out=y)
     first = host(y).copy()
@@ -173,5 +174,6 @@ def test_empty_calls(gpu, fn):
     import torch
     qw, d, z = packed(WL.random_weights(8, 128, seed=1), 4)
     x = torch.empty((0, 128), dtype=torch.float16, device="cuda:0")
-    y = getattr(awq, fn)(x, dev(qw), dev(d), dev(z), N=8, bits=4)
+    y = getattr(awq, fn)(x, dev(qw.reshape(-1)), dev(O.tile_params(d)), dev(O.tile_params(z)),
+                         N=8, bits=4)
     assert tuple(y.shape) == (0, 8)

@@ -18,11 +18,24 @@ def _check_rows(W, s, bits, rows=None):
     announce("quantize_pack", f"N={N} K={K} bits={bits} s={'yes' if s is not None else 'no'}")
     qw, sc, ze = awq.quantize_pack(dev(W), None if s is None else dev(s), bits=bits)
     torch.cuda.synchronize()
-    rows = np.arange(N) if rows is None else np.asarray(rows)
-    q, d, z = O.quantize(W[rows], s, bits)
-    assert np.array_equal(host(qw)[rows].view(np.uint32), O.pack(q, bits)), "packed codes differ"
-    assert np.array_equal(host(sc)[rows].view(np.uint16), d.view(np.uint16)), "scales differ"
-    assert np.array_equal(host(ze)[rows].view(np.uint16), z.view(np.uint16)), "zeros differ"
+    words = host(qw).view(np.uint32)
+    if rows is None:
+        q, d, z = O.quantize(W, s, bits)
+        assert np.array_equal(words, O.pack(q, bits).ravel()), "packed tiles differ"
+        rows = np.arange(N)
+    else:
+        rows = np.asarray(rows)
+        q, d, z = O.quantize(W[rows], s, bits)
+        assert words.size == O.packed_words(N, K, bits)
+        got_rows = O.tiles_to_rows(words, bits, K)
+        assert np.array_equal(got_rows[rows], O.pack_rows(q, bits)), "packed codes differ"
+        assert not got_rows[N:].any(), "padding rows not zero"
+    sc_h, ze_h = host(sc), host(ze)
+    assert sc_h.shape == ((N + 15) // 16, K // 128, 16)
+    assert not O.untile_params(sc_h, sc_h.shape[0] * 16)[N:].any(), "padding scales not zero"
+    sc_rows, ze_rows = O.untile_params(sc_h, N)[rows], O.untile_params(ze_h, N)[rows]
+    assert np.array_equal(sc_rows.view(np.uint16), d.view(np.uint16)), "scales differ"
+    assert np.array_equal(ze_rows.view(np.uint16), z.view(np.uint16)), "zeros differ"
 
 
 @pytest.mark.parametrize("bits", [4, 3])
@@ -79,9 +92,9 @@ def test_no_write_past_outputs_and_deterministic(gpu):
     W = WL.random_weights(37, 384, seed=3)
     Wd = dev(W)
     announce("quantize_pack guarded", "N=37 K=384")
-    qw, raw_q, nq = guarded_empty((37, 48), torch.int32)
-    sc, raw_s, ns = guarded_empty((37, 3), torch.float16)
-    ze, raw_z, nz = guarded_empty((37, 3), torch.float16)
+    qw, raw_q, nq = guarded_empty((O.packed_words(37, 384, 4),), torch.int32)
+    sc, raw_s, ns = guarded_empty((3, 3, 16), torch.float16)
+    ze, raw_z, nz = guarded_empty((3, 3, 16), torch.float16)
     awq.quantize_pack(Wd, None, 4, out=(qw, sc, ze))
     first = [host(t).copy() for t in (qw, sc, ze)]
     awq.quantize_pack(Wd, None, 4, out=(qw, sc, ze))

@@ -70,12 +70,12 @@ def test_workload5_full_offline_pass(gpu, bits):
     qw, sc, ze = awq.quantize_pack(dev(W), dev(s_g), bits=bits)
     q, d, z = O.quantize(W, s_g, bits)
     torch.cuda.synchronize()
-    assert np.array_equal(host(qw).view(np.uint32), O.pack(q, bits))
-    assert np.array_equal(host(sc).view(np.uint16), d.view(np.uint16))
-    assert np.array_equal(host(ze).view(np.uint16), z.view(np.uint16))
+    assert np.array_equal(host(qw).view(np.uint32), O.pack(q, bits).ravel())
+    assert np.array_equal(host(sc).view(np.uint16), O.tile_params(d).view(np.uint16))
+    assert np.array_equal(host(ze).view(np.uint16), O.tile_params(z).view(np.uint16))
     x = wl.eval_activations(1)
     xs = awq.scale_activations(dev(x), dev(s_g))
-    y = awq.gemv(xs, qw, sc, ze, bits=bits)
+    y = awq.gemv(xs, qw, sc, ze, N=W.shape[0], bits=bits)
     torch.cuda.synchronize()
     y_ref = O.matmul(O.scale_activations(x, s_g), O.pack(q, bits), d, z, bits, W.shape[1])
     assert rel_err(host(y), y_ref) <= TOL
@@ -96,12 +96,12 @@ def test_workload1_end_to_end(gpu):
     ulp = np.abs(s_g.view(np.int32).astype(np.int64) - s_ref.view(np.int32).astype(np.int64))
     assert ulp.max() <= 1
     q, d, z = O.quantize(W, s_g, 4)
-    assert np.array_equal(host(qw).view(np.uint32), O.pack(q, 4))
+    assert np.array_equal(host(qw).view(np.uint32), O.pack(q, 4).ravel())
     for M in wl.Ms:
         x = wl.activations(M)
         xs = awq.scale_activations(dev(x), s)
         y_ref = O.matmul(O.scale_activations(x, s_g), O.pack(q, 4), d, z, 4, W.shape[1])
         for fn in ("gemv", "gemm"):
-            y = getattr(awq, fn)(xs, qw, sc, ze, bits=4)
+            y = getattr(awq, fn)(xs, qw, sc, ze, N=W.shape[0], bits=4)
             torch.cuda.synchronize()
             assert rel_err(host(y), y_ref) <= TOL, fn

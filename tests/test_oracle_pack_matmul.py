@@ -8,13 +8,40 @@ from weight_only_quantization_pack_amd import workloads as WL
 
 def test_int4_literal_word():
     q = np.tile(np.arange(8, dtype=np.uint8), 16)[None, :]
-    assert int(O.pack(q, 4)[0, 0]) == 0x75316420
+    assert int(O.pack_rows(q, 4)[0, 0]) == 0x75316420
+    assert int(O.pack(q, 4)[0, 0, 0, 0]) == 0x75316420
+
+
+@pytest.mark.parametrize("bits", [4, 3])
+def test_tile_slot_is_row_and_quarter(bits):
+    """Format 2: slot s of a tile holds row s % 16 and quarter s // 16."""
+    Q = (1 << bits) - 1
+    rep = 0x11111111 if bits == 4 else None
+    # codes equal to the row index (mod Q+1): every word of slot s encodes row s % 16
+    q = (np.arange(16)[:, None] % (Q + 1) * np.ones((1, 256))).astype(np.uint8)
+    t = O.pack(q, bits)
+    assert t.shape == (1, 2, 64, 4 if bits == 4 else 3)
+    for s_ in range(64):
+        v = (s_ % 16) % (Q + 1)
+        if bits == 4:
+            assert all(int(w) == v * rep for w in t[0, 1, s_])
+        else:
+            stream = sum(v << (3 * i) for i in range(32))
+            assert [int(w) for w in t[0, 1, s_]] == [(stream >> (32 * d)) & 0xFFFFFFFF for d in range(3)]
+    # codes equal to the quarter index: slot s encodes quarter s // 16
+    q = ((np.arange(256) % 128) // 32 * np.ones((5, 1))).astype(np.uint8)
+    t = O.pack(q, bits)
+    for s_ in range(64):
+        if s_ % 16 >= 5:
+            assert not t[0, 0, s_].any()                 # padded rows are zero
+        elif bits == 4:
+            assert all(int(w) == (s_ // 16) * rep for w in t[0, 0, s_])
 
 
 def test_int3_stream_matches_big_integer():
     rng = np.random.default_rng(1)
     q = rng.integers(0, 8, (3, 256)).astype(np.uint8)
-    words = O.pack(q, 3)
+    words = O.pack_rows(q, 3)
     for n in range(3):
         for c in range(256 // 32):
             stream = 0
@@ -28,7 +55,7 @@ def test_int4_pairs_are_fp16_magic_operands():
     """(w >> 4t) & 0x000F000F | 0x64006400 is the fp16 pair (1024+q_2t, 1024+q_2t+1)."""
     rng = np.random.default_rng(2)
     q = rng.integers(0, 16, (4, 128)).astype(np.uint8)
-    words = O.pack(q, 4)
+    words = O.pack_rows(q, 4)
     for t in range(4):
         pair = ((words >> np.uint32(4 * t)) & np.uint32(0x000F000F)) | np.uint32(0x64006400)
         h = pair.view(np.float16).reshape(4, 16, 2).astype(np.float64) - 1024
@@ -41,9 +68,23 @@ def test_pack_unpack_round_trip(bits):
     rng = np.random.default_rng(3 + bits)
     q = rng.integers(0, 1 << bits, (5, 384)).astype(np.uint8)
     w = O.pack(q, bits)
-    assert w.shape == (5, O.packed_words_per_row(384, bits))
-    assert np.array_equal(O.unpack(w, bits, 384), q)
-    assert np.array_equal(O.unpack_fast(w, bits, 384), q)
+    assert w.size == O.packed_words(5, 384, bits) == 16 * O.packed_words_per_row(384, bits)
+    assert np.array_equal(O.unpack(w, bits, 384, 5), q)
+    assert np.array_equal(O.unpack_fast(w, bits, 384, 5), q)
+    assert not O.unpack(w, bits, 384)[5:].any()         # padding rows decode to 0
+
+
+def test_tiled_params_layout():
+    """Format 2 scales/zeros: element (n, g) at [n // 16][g][n % 16]; padding zero."""
+    N, G = 37, 3
+    p = (np.arange(N)[:, None] * 10 + np.arange(G)[None, :]).astype(np.float16)
+    t = O.tile_params(p)
+    assert t.shape == (3, G, 16)
+    for n in range(N):
+        for g in range(G):
+            assert t[n // 16, g, n % 16] == n * 10 + g
+    assert not t[2, :, 5:].any()
+    assert np.array_equal(O.untile_params(t, N), p)
 
 
 def test_pack_rejects_out_of_range_codes():
@@ -82,7 +123,7 @@ def test_matmul_against_loops(bits):
     y = O.matmul(x, words, d, z, bits, 128)
     # independent dequant from the per-bit unpack, then loops
     w_hat = np.zeros((3, 128))
-    qq = O.unpack(words, bits, 128)
+    qq = O.unpack(words, bits, 128, 3)
     for n in range(3):
         for k in range(128):
             w_hat[n, k] = (int(qq[n, k]) - float(z[n, 0])) * float(d[n, 0])
@@ -99,6 +140,17 @@ def test_matmul_one_hot_selects_a_column_of_w_hat():
         x[0, k] = 1.0
         y = O.matmul(x, words, d, z, 4, 256)
         assert np.array_equal(y[0], w_hat[:, k])
+
+
+def test_matmul_rows_matches_full_product():
+    W = WL.random_weights(37, 384, seed=25)
+    x = WL.random_activations(3, 384, seed=26)
+    for bits in (4, 3):
+        q, d, z = O.quantize(W, None, bits)
+        words = O.pack(q, bits)
+        rows = np.array([0, 15, 16, 36])
+        assert np.allclose(O.matmul_rows(x, words, d, z, bits, 384, rows),
+                           O.matmul(x, words, d, z, bits, 384)[:, rows], rtol=1e-15, atol=0)
 
 
 def test_matmul_all_ones_is_group_sum():

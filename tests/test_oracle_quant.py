@@ -115,7 +115,7 @@ def test_closed_form_group(bits):
     assert np.array_equal(q[0], i.astype(np.uint8))
     assert int(d[0, 0].view(np.uint16)) == g["scale_f16_bits"]
     assert float(z[0, 0]) == g["zero"]
-    words = O.pack(q, bits)[0]
+    words = O.pack_rows(q, bits)[0]
     n = len(g["words"])
     assert [int(w) for w in words[:n]] == g["words"]
 

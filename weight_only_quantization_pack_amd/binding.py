@@ -23,6 +23,7 @@ SIGNATURES = [
     ("awq_status_str", ctypes.c_char_p, [_c_int]),
     ("awq_pack_format_version", _c_int, []),
     ("awq_packed_words_per_row", _c_size_t, [_c_int, _c_int]),
+    ("awq_packed_words", _c_size_t, [_c_int, _c_int, _c_int]),
     ("awq_quantize_pack", _c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int,
                                    _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     ("awq_scale_activations", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_void_p]),
@@ -118,11 +119,17 @@ def packed_words_per_row(K: int, bits: int) -> int:
     return int(load_library().awq_packed_words_per_row(K, bits))
 
 
+def packed_words(N: int, K: int, bits: int) -> int:
+    """uint32 words of a packed N x K matrix (format 2: rows padded to 16)."""
+    return int(load_library().awq_packed_words(N, K, bits))
+
+
 def quantize_pack(W, s=None, bits: int = 4, group_size: int = GROUP_SIZE,
                   zero_point: bool = True, out=None):
     """Quantize fp16 W [N][K] (times s [K] if given) and pack.
 
-    Returns (qweight int32 [N][words], scales fp16 [N][G], zeros fp16 [N][G]).
+    Returns (qweight int32 [packed_words(N, K, bits)], scales fp16
+    [ceil(N/16)][G][16], zeros fp16 [ceil(N/16)][G][16]) in packed format 2.
     """
     torch = _torch()
     lib = load_library()
@@ -132,10 +139,11 @@ def quantize_pack(W, s=None, bits: int = 4, group_size: int = GROUP_SIZE,
         _need(s, torch.float32, (K,), "s")
     G = K // group_size if group_size > 0 else 0
     if out is None:
-        words = int(lib.awq_packed_words_per_row(K, bits))
-        qweight = torch.empty((N, words), dtype=torch.int32, device=W.device)
-        scales = torch.empty((N, G), dtype=torch.float16, device=W.device)
-        zeros = torch.empty((N, G), dtype=torch.float16, device=W.device)
+        words = int(lib.awq_packed_words(N, K, bits))
+        qweight = torch.empty((words,), dtype=torch.int32, device=W.device)
+        NB = (N + 15) // 16
+        scales = torch.empty((NB, G, 16), dtype=torch.float16, device=W.device)
+        zeros = torch.empty((NB, G, 16), dtype=torch.float16, device=W.device)
     else:
         qweight, scales, zeros = out
     st = lib.awq_quantize_pack(_ptr(W), _ptr(s), N, K, bits, group_size, int(zero_point),
@@ -191,11 +199,12 @@ def _matmul(fn_name, x, qweight, scales, zeros, N, bits, group_size, out):
     lib = load_library()
     M, K = x.shape
     _need(x, torch.float16, (M, K), "x")
-    words = int(lib.awq_packed_words_per_row(K, bits))
-    _need(qweight, torch.int32, (N, words), "qweight")
+    words = int(lib.awq_packed_words(N, K, bits))
+    _need(qweight, torch.int32, (words,), "qweight")
     G = K // group_size if group_size > 0 else 0
-    _need(scales, torch.float16, (N, G), "scales")
-    _need(zeros, torch.float16, (N, G), "zeros")
+    NB = (N + 15) // 16
+    _need(scales, torch.float16, (NB, G, 16), "scales")
+    _need(zeros, torch.float16, (NB, G, 16), "zeros")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=x.device)
     else:
@@ -206,13 +215,11 @@ def _matmul(fn_name, x, qweight, scales, zeros, N, bits, group_size, out):
     return out
 
 
-def gemv(x, qweight, scales, zeros, N=None, bits: int = 4, group_size: int = GROUP_SIZE, out=None):
-    """Decode product y = x . w_hat^T for 1 <= M <= 16."""
-    N = qweight.shape[0] if N is None else N
+def gemv(x, qweight, scales, zeros, N: int, bits: int = 4, group_size: int = GROUP_SIZE, out=None):
+    """Decode product y = x . w_hat^T for 1 <= M <= 16 rows of x; N output columns."""
     return _matmul("awq_gemv", x, qweight, scales, zeros, N, bits, group_size, out)
 
 
-def gemm(x, qweight, scales, zeros, N=None, bits: int = 4, group_size: int = GROUP_SIZE, out=None):
-    """Prefill product y = x . w_hat^T for any M >= 1 (bits 4)."""
-    N = qweight.shape[0] if N is None else N
+def gemm(x, qweight, scales, zeros, N: int, bits: int = 4, group_size: int = GROUP_SIZE, out=None):
+    """Prefill product y = x . w_hat^T for any M >= 1 rows of x (bits 4); N output columns."""
     return _matmul("awq_gemm", x, qweight, scales, zeros, N, bits, group_size, out)

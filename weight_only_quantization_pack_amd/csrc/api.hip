@@ -55,13 +55,18 @@ const char* awq_status_str(int status) {
     }
 }
 
-int awq_pack_format_version(void) { return 1; }
+int awq_pack_format_version(void) { return 2; }
 
 size_t awq_packed_words_per_row(int K, int bits) {
     if (K <= 0) return 0;
     if (bits == 4) return (size_t)K / 8;
     if (bits == 3) return 3 * ((size_t)K / 32);
     return 0;
+}
+
+size_t awq_packed_words(int N, int K, int bits) {
+    if (N < 0) return 0;
+    return 16 * (((size_t)N + 15) / 16) * awq_packed_words_per_row(K, bits);
 }
 
 int awq_quantize_pack(const void* W, const float* s, int N, int K, int bits, int group_size,

@@ -57,18 +57,21 @@ __global__ __launch_bounds__(256) void k_gemm(
                           : make_uint4(0, 0, 0, 0);
         }
         if constexpr (B_INT4) {
+            // format 2: tile (block, kt) is 64 slots of 16 B; slot s = 16h + j
+            // is row 16*block + j, codes 32h..32h+31 of the group
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const int id = tid + 256 * i, r = id >> 2, c = id & 3, n = n0 + r;
-                if (n < N) {
-                    rb[i] = *reinterpret_cast<const uint4*>(Bq + (size_t)n * (K / 8) + kt * 16 + c * 4);
-                    rs[i] = scales[(size_t)n * G + kt];
-                    rz[i] = zeros[(size_t)n * G + kt];
+                const int id = tid + 256 * i, rb16 = id >> 6, slot = id & 63;
+                const int blk = n0 / 16 + rb16;
+                if (16 * blk < N) {
+                    rb[i] = *reinterpret_cast<const uint4*>(Bq + ((size_t)blk * G + kt) * 256 + slot * 4);
                 } else {
                     rb[i] = make_uint4(0, 0, 0, 0);
-                    rs[i] = (_Float16)0.0f;
-                    rz[i] = (_Float16)0.0f;
                 }
+                // format-2 scales/zeros: [block][g][16], zero on padding rows
+                const size_t pidx = ((size_t)blk * G + kt) * 16 + (slot & 15);
+                rs[i] = 16 * blk < N ? scales[pidx] : (_Float16)0.0f;
+                rz[i] = 16 * blk < N ? zeros[pidx] : (_Float16)0.0f;
             }
         } else {
 #pragma unroll
@@ -89,7 +92,8 @@ __global__ __launch_bounds__(256) void k_gemm(
         if constexpr (B_INT4) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const int id = tid + 256 * i, r = id >> 2, c = id & 3;
+                const int id = tid + 256 * i, slot = id & 63;
+                const int r = 16 * (id >> 6) + (slot & 15), c = slot >> 4;
                 const _Float16 zb = (_Float16)1024.0f + rz[i];
                 const half2_t zz = {zb, zb};
                 const half2_t dd = {rs[i], rs[i]};

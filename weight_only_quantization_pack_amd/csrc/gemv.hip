@@ -2,177 +2,296 @@
 // (the decode kernel of the llm-awq README feature list):
 //   y[m][n] = sum_g D[n][g] * sum_{k in g} x[m][k] * (q[n][k] - z[n][g])
 //
-// Bandwidth-bound: every packed weight byte is read once from HBM.  One
-// wavefront owns one output row n at a time; its lanes stride over the row
-// in 16-byte chunks (32 int4 codes, all inside one group), so each wave load
-// instruction reads 1 KB of contiguous HBM.  Per chunk the codes are
-// unpacked in registers with the fp16 exponent trick (OR 0x6400 turns a
-// 4-bit code q into the fp16 value 1024 + q), the zero is removed exactly
-// in fp16 (1024 + q - (1024 + z) = q - z), the fp16 pairs are dotted with
-// x on v_dot2_f32_f16 into fp32, and the group scale is applied once per
-// chunk.  The row sum ends with a wavefront butterfly reduction.
+// HBM-bound: every packed weight byte is read once.  The product runs on
+// v_mfma_f32_16x16x32_f16 with the activations as the A operand (M rows,
+// zero-padded to 16) and the weights as the B operand, so the cost per
+// weight stays flat up to M = 16.
+//
+// Work split.  Packed format 2 stores tile (b, g) = 16 rows x group g as 64
+// lane slots of 16 bytes (slot s = 16h + j: row j, quarter h), contiguous
+// along g, with the 16 scales and zeros of the tile in [b][g][16] order.
+// A workgroup of WK waves owns one row block at a time and loops over row
+// blocks blockIdx.x, +gridDim.x, ... (the grid is sized to the machine).
+// Its waves take the groups round-robin, so each step of the workgroup reads
+// WK consecutive tiles and the block's slab is swept front to back.  Each
+// wave keeps its next U tiles (1 KB wave load each) and their 32-byte scale
+// and zero loads in flight while it computes on the current U; the rolling
+// prefetch runs on across row blocks.  x is staged in LDS once per
+// workgroup (or once per K-slice when M*K is large).
+//
+// Dequantization is exact: OR 0x6400 turns a 4-bit code q into the fp16
+// value 1024 + q and subtracting 1024 + z leaves q - z, so each group's
+// four MFMAs give sum_k x (q - z) with fp32 accumulation; the group scale
+// then multiplies the four accumulator lanes of that row (the accumulator
+// column of lane s is its own row j).  The waves' partial sums meet in LDS
+// and wave 0 adds them in a fixed order: the result is deterministic.
 #include "awq_internal.h"
 
 namespace awq {
 namespace {
 
+#ifndef AWQ_GEMV_WAVES
+#define AWQ_GEMV_WAVES 8
+#endif
+#ifndef AWQ_GEMV_UNROLL
+#define AWQ_GEMV_UNROLL 4
+#endif
+#ifndef AWQ_GEMV_XBUF
+#define AWQ_GEMV_XBUF 65536
+#endif
+constexpr int kGemvWaves = AWQ_GEMV_WAVES;    // waves per workgroup
+constexpr int kGemvUnroll = AWQ_GEMV_UNROLL;  // tiles per wave per load batch
+constexpr int kGemvXBuf = AWQ_GEMV_XBUF;      // LDS bytes for the staged x slice
+
 __device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 
-template <int MT>
-__global__ __launch_bounds__(256) void k_gemv_int4(
-    const _Float16* __restrict__ x, const uint32_t* __restrict__ qweight,
-    const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
-    _Float16* __restrict__ y, int M, int N, int K) {
-    const int lane = threadIdx.x & 63;
-    const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (n >= N) return;                              // the whole wave leaves
-    const int G = K / kGroup;
-    const int n_chunks = K / 32;
-    const uint4* qrow = reinterpret_cast<const uint4*>(qweight + (size_t)n * (K / 8));
-    const _Float16* srow = scales + (size_t)n * G;
-    const _Float16* zrow = zeros + (size_t)n * G;
-    float acc[MT];
+// fp16 operand (q - z) of 8 int4 codes in one packed word.
+__device__ __forceinline__ half8_t dequant_word_int4(uint32_t w, half2_t zz) {
+    half8_t b;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
-
-    for (int c = lane; c < n_chunks; c += kWave) {
-        const uint4 w = qrow[c];
-        const int g = c >> 2;
-        const float d = (float)srow[g];
-        const _Float16 zb = (_Float16)1024.0f + zrow[g];          // exact
-        const half2_t zz = {zb, zb};
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-        half2_t hq[16];                                          // pair p = k/2 in the chunk
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const uint32_t b = ((ws[i] >> (4 * t)) & 0x000F000Fu) | 0x64006400u;
-                hq[4 * i + t] = as_half2(b) - zz;
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            if (m < M) {
-                const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)m * K + 32 * c);
-                float p = 0.0f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint4 xv = xr[j];
-                    p = __builtin_amdgcn_fdot2(hq[4 * j + 0], as_half2(xv.x), p, false);
-                    p = __builtin_amdgcn_fdot2(hq[4 * j + 1], as_half2(xv.y), p, false);
-                    p = __builtin_amdgcn_fdot2(hq[4 * j + 2], as_half2(xv.z), p, false);
-                    p = __builtin_amdgcn_fdot2(hq[4 * j + 3], as_half2(xv.w), p, false);
-                }
-                acc[m] = __builtin_fmaf(d, p, acc[m]);
-            }
-        }
+    for (int t = 0; t < 4; ++t) {
+        const half2_t p = as_half2(((w >> (4 * t)) & 0x000F000Fu) | 0x64006400u) - zz;
+        b[2 * t] = p[0];
+        b[2 * t + 1] = p[1];
     }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) acc[m] += __shfl_xor(acc[m], off);
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-            if (m < M) y[(size_t)m * N + n] = (_Float16)acc[m];
-    }
+    return b;
 }
 
-// int3: a chunk is 32 codes = 3 words (96-bit little-endian stream).
-template <int MT>
-__global__ __launch_bounds__(256) void k_gemv_int3(
-    const _Float16* __restrict__ x, const uint32_t* __restrict__ qweight,
-    const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
-    _Float16* __restrict__ y, int M, int N, int K) {
-    const int lane = threadIdx.x & 63;
-    const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (n >= N) return;
-    const int G = K / kGroup;
-    const int n_chunks = K / 32;
-    const uint32_t* qrow = qweight + (size_t)n * (3 * (K / 32));
-    const _Float16* srow = scales + (size_t)n * G;
-    const _Float16* zrow = zeros + (size_t)n * G;
-    float acc[MT];
+// fp16 operand (q - z) of 8 int3 codes held in the low 24 bits of v.
+__device__ __forceinline__ half8_t dequant_24_int3(uint32_t v, half2_t zz) {
+    half8_t b;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
-
-    for (int c = lane; c < n_chunks; c += kWave) {
-        const uint64_t lo = (uint64_t)qrow[3 * c] | ((uint64_t)qrow[3 * c + 1] << 32);
-        const uint32_t hi = qrow[3 * c + 2];
-        const int g = c >> 2;
-        const float d = (float)srow[g];
-        const _Float16 zb = (_Float16)1024.0f + zrow[g];
-        const half2_t zz = {zb, zb};
-        half2_t hq[16];
-#pragma unroll
-        for (int p = 0; p < 16; ++p) {
-            uint32_t q2[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int pos = 3 * (2 * p + e);
-                uint32_t q;
-                if (pos + 3 <= 64) q = (uint32_t)(lo >> pos) & 7u;
-                else if (pos >= 64) q = (hi >> (pos - 64)) & 7u;
-                else q = ((uint32_t)(lo >> pos) | (hi << (64 - pos))) & 7u;
-                q2[e] = q;
-            }
-            hq[p] = as_half2((q2[0] | (q2[1] << 16)) | 0x64006400u) - zz;
-        }
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            if (m < M) {
-                const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)m * K + 32 * c);
-                float p = 0.0f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint4 xv = xr[j];
-                    p = __builtin_amdgcn_fdot2(hq[4 * j + 0], as_half2(xv.x), p, false);
-                    p = __builtin_amdgcn_fdot2(hq[4 * j + 1], as_half2(xv.y), p, false);
-                    p = __builtin_amdgcn_fdot2(hq[4 * j + 2], as_half2(xv.z), p, false);
-                    p = __builtin_amdgcn_fdot2(hq[4 * j + 3], as_half2(xv.w), p, false);
-                }
-                acc[m] = __builtin_fmaf(d, p, acc[m]);
-            }
-        }
+    for (int t = 0; t < 4; ++t) {
+        const uint32_t pair = ((v >> (6 * t)) & 7u) | (((v >> (6 * t + 3)) & 7u) << 16);
+        const half2_t p = as_half2(pair | 0x64006400u) - zz;
+        b[2 * t] = p[0];
+        b[2 * t + 1] = p[1];
     }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) acc[m] += __shfl_xor(acc[m], off);
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-            if (m < M) y[(size_t)m * N + n] = (_Float16)acc[m];
-    }
+    return b;
 }
 
-template <int MT>
-void launch_gemv_mt(const void* x, const void* qweight, const void* scales, const void* zeros,
-                    void* y, int M, int N, int K, int bits, hipStream_t st) {
-    const dim3 grid((N + 3) / 4), block(256);
-    if (bits == 4) {
-        hipLaunchKernelGGL(k_gemv_int4<MT>, grid, block, 0, st, (const _Float16*)x,
-                           (const uint32_t*)qweight, (const _Float16*)scales,
-                           (const _Float16*)zeros, (_Float16*)y, M, N, K);
+template <int WQ>
+struct Slot { uint32_t w[WQ]; };
+
+template <int WQ>
+__device__ __forceinline__ Slot<WQ> load_slot(const uint32_t* p) {
+    Slot<WQ> s;
+    if constexpr (WQ == 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(p);
+        s.w[0] = v.x; s.w[1] = v.y; s.w[2] = v.z; s.w[3] = v.w;
     } else {
-        hipLaunchKernelGGL(k_gemv_int3<MT>, grid, block, 0, st, (const _Float16*)x,
-                           (const uint32_t*)qweight, (const _Float16*)scales,
-                           (const _Float16*)zeros, (_Float16*)y, M, N, K);
+#pragma unroll
+        for (int i = 0; i < WQ; ++i) s.w[i] = p[i];
     }
+    return s;
+}
+
+struct Params { _Float16 d, z; };
+
+size_t gemv_lds_bytes(int M, int SG, int WK) {
+    return (((size_t)M * (SG * kGroup + 8) * 2 + 15) & ~(size_t)15) + 2 * (size_t)WK * 64 * 16;
+}
+
+template <int BITS, int WK, int U>
+__global__ __launch_bounds__(64 * WK) void k_gemv(
+    const _Float16* __restrict__ x, const uint32_t* __restrict__ qweight,
+    const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
+    _Float16* __restrict__ y, int M, int N, int K, int SG) {
+    constexpr int WQ = BITS == 4 ? 4 : 3;              // words per lane slot
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int G = K / kGroup;
+    const int NB = (N + 15) / 16;
+    const int XS = SG * kGroup + 8;                    // halves per staged x row
+    _Float16* xs = reinterpret_cast<_Float16*>(smem);
+    float4_t* red = reinterpret_cast<float4_t*>(smem + (((size_t)M * XS * 2 + 15) & ~(size_t)15));
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int j = lane & 15, h = lane >> 4;
+    const bool one_slice = SG >= G;
+    // this wave's groups of a block: g = wave + WK * i, i < nw
+    const int nw = wave < G ? (G - wave + WK - 1) / WK : 0;
+    // index bound of the slice holding batch index i: with several slices SG is
+    // a multiple of WK, so slice [s0, s0 + SG) holds i in [s0 / WK, (s0 + SG) / WK)
+    auto slice_end = [&](int i) { return one_slice ? nw : min(nw, (i * WK / SG + 1) * SG / WK); };
+
+    auto load = [&](int b, int i0, int cnt, Slot<WQ>* w, Params* p) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (u < cnt) {
+                const size_t t = (size_t)b * G + wave + WK * (i0 + u);   // tile index
+                w[u] = load_slot<WQ>(qweight + (t * 64 + lane) * WQ);
+                p[u].d = scales[t * 16 + j];
+                p[u].z = zeros[t * 16 + j];
+            }
+        }
+    };
+    auto stage_x = [&](int s0) {
+        const int sg = min(SG, G - s0);
+        const int c8 = sg * (kGroup / 8);                          // uint4 per staged row
+        for (int idx = tid; idx < M * c8; idx += 64 * WK) {
+            const int m = idx / c8, c = idx % c8;
+            *reinterpret_cast<uint4*>(xs + (size_t)m * XS + 8 * c) =
+                *reinterpret_cast<const uint4*>(x + (size_t)m * K + (size_t)s0 * kGroup + 8 * c);
+        }
+    };
+
+    int b = blockIdx.x;
+    Slot<WQ> cur[U];
+    Params pc[U];
+    int i_cur = 0, n_cur = min(U, slice_end(0));
+    if (b < NB) load(b, 0, n_cur, cur, pc);
+    if (one_slice) {
+        stage_x(0);
+        __syncthreads();
+    }
+    int buf = 0;
+    for (; b < NB; b += gridDim.x) {
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
+        int staged = -1;
+        while (true) {
+            if (!one_slice) {
+                // every wave walks the slices in step; stage the slice of the current batch
+                const int s_here = n_cur > 0 ? (wave + WK * i_cur) / SG * SG : -1;
+                // each wave stages every slice exactly once, in order, so all
+                // waves meet the same sequence of barriers
+                for (int s0 = staged < 0 ? 0 : staged + SG; s0 <= s_here && s0 < G; s0 += SG) {
+                    __syncthreads();
+                    stage_x(s0);
+                    __syncthreads();
+                    staged = s0;
+                }
+            }
+            if (n_cur <= 0) break;
+            // descriptor of the next batch (may be in the next slice or block)
+            int nb_b = b, nb_i = i_cur + n_cur;
+            int nb_n = nb_i < nw ? min(U, slice_end(nb_i) - nb_i) : 0;
+            if (nb_n <= 0) {
+                nb_b = b + gridDim.x;
+                nb_i = 0;
+                nb_n = nb_b < NB ? min(U, slice_end(0)) : 0;
+            }
+            Slot<WQ> nxt[U];
+            Params pn[U];
+            if (nb_n > 0) load(nb_b, nb_i, nb_n, nxt, pn);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (u >= n_cur) break;                                   // wave-uniform
+                const int g = wave + WK * (i_cur + u);
+                const int gl = one_slice ? g : g % SG;                   // group within the staged slice
+                const _Float16 zb = (_Float16)1024.0f + pc[u].z;
+                const half2_t zz = {zb, zb};
+                half8_t bop[4];
+                if constexpr (BITS == 4) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) bop[i] = dequant_word_int4(cur[u].w[i], zz);
+                } else {
+                    // 96-bit stream of 32 codes; operand i takes stream bits 24i..24i+23
+                    const uint32_t w0 = cur[u].w[0], w1 = cur[u].w[1], w2 = cur[u].w[2];
+                    bop[0] = dequant_24_int3(w0 & 0xFFFFFFu, zz);
+                    bop[1] = dequant_24_int3((w0 >> 24) | ((w1 & 0xFFFFu) << 8), zz);
+                    bop[2] = dequant_24_int3((w1 >> 16) | ((w2 & 0xFFu) << 16), zz);
+                    bop[3] = dequant_24_int3(w2 >> 8, zz);
+                }
+                float4_t accg = {0.f, 0.f, 0.f, 0.f};
+                // rows j >= M of the A operand are zero; their address is clamped to
+                // row 0 so that no LDS read leaves the staged rows
+                const _Float16* xa = xs + (size_t)(j < M ? j : 0) * XS + gl * kGroup + 32 * h;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const half8_t a = j < M ? *reinterpret_cast<const half8_t*>(xa + 8 * i)
+                                            : (half8_t){0, 0, 0, 0, 0, 0, 0, 0};
+                    accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bop[i], accg, 0, 0, 0);
+                }
+                const float d = (float)pc[u].d;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(d, accg[r], acc[r]);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) { cur[u] = nxt[u]; pc[u] = pn[u]; }
+            const bool next_block = nb_b != b;
+            i_cur = nb_i;
+            n_cur = nb_n;
+            if (next_block) break;
+        }
+        if (!one_slice) {
+            // waves whose groups ended early still pass every staging barrier
+            for (int s0 = staged < 0 ? 0 : staged + SG; s0 < G; s0 += SG) {
+                __syncthreads();
+                stage_x(s0);
+                __syncthreads();
+            }
+        }
+        red[(buf * WK + wave) * 64 + lane] = acc;
+        __syncthreads();
+        if (wave == 0) {
+            float4_t sum = red[(buf * WK) * 64 + lane];
+#pragma unroll
+            for (int w = 1; w < WK; ++w) {
+                const float4_t o = red[(buf * WK + w) * 64 + lane];
+                sum[0] += o[0]; sum[1] += o[1]; sum[2] += o[2]; sum[3] += o[3];
+            }
+            // accumulator layout: lane 16h + j holds rows m = 4h + r of column j
+            const int n = 16 * b + j;
+            if (n < N) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = 4 * h + r;
+                    if (m < M) y[(size_t)m * N + n] = (_Float16)sum[r];
+                }
+            }
+        }
+        buf ^= 1;
+    }
+}
+
+int num_cus() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            cus = v;
+        else
+            cus = 256;
+    }
+    return cus;
+}
+
+template <int BITS>
+int launch_bits(const void* x, const void* qweight, const void* scales, const void* zeros,
+                void* y, int M, int N, int K, hipStream_t st) {
+    const int G = K / kGroup;
+    const int NB = (N + 15) / 16;
+    int SG = kGemvXBuf / (M * kGroup * 2);
+    if (SG >= G) {
+        SG = G;                                        // x staged once
+    } else {
+        SG = max(kGemvWaves, SG / kGemvWaves * kGemvWaves);
+    }
+    const size_t lds = gemv_lds_bytes(M, SG, kGemvWaves);
+    auto kern = k_gemv<BITS, kGemvWaves, kGemvUnroll>;
+    if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return (int)e;
+    }
+    // persistent workgroups when x is staged once (as many as fit on a CU by
+    // LDS, at most 2 of 8 waves); one row block each otherwise
+    const int per_cu = max(1, min(2, (int)((160 * 1024) / lds)));
+    const int grid = SG == G ? min(NB, num_cus() * per_cu) : NB;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kGemvWaves), lds, st,
+                       (const _Float16*)x, (const uint32_t*)qweight, (const _Float16*)scales,
+                       (const _Float16*)zeros, (_Float16*)y, M, N, K, SG);
+    return (int)hipGetLastError();
 }
 
 }  // namespace
 
 int launch_gemv(const void* x, const void* qweight, const void* scales, const void* zeros,
                 void* y, int M, int N, int K, int bits, hipStream_t st) {
-    if (M <= 1) launch_gemv_mt<1>(x, qweight, scales, zeros, y, M, N, K, bits, st);
-    else if (M <= 4) launch_gemv_mt<4>(x, qweight, scales, zeros, y, M, N, K, bits, st);
-    else if (M <= 8) launch_gemv_mt<8>(x, qweight, scales, zeros, y, M, N, K, bits, st);
-    else launch_gemv_mt<16>(x, qweight, scales, zeros, y, M, N, K, bits, st);
-    return (int)hipGetLastError();
+    return bits == 4 ? launch_bits<4>(x, qweight, scales, zeros, y, M, N, K, st)
+                     : launch_bits<3>(x, qweight, scales, zeros, y, M, N, K, st);
 }
 
 }  // namespace awq
