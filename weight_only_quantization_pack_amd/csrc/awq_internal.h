@@ -35,6 +35,21 @@ __device__ __forceinline__ uint16_t f16_bits_round_down(float d) {
     return b;
 }
 
+// (x & mask) | bits in one VALU instruction.  The compiler otherwise often
+// emits a separate AND and OR for the int4 -> fp16 exponent trick.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t bits) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask), "v"(bits));
+    return r;
+}
+
+// The fp16 pair (1024 + q[2t], 1024 + q[2t+1]) of a packed int4 word: the two
+// codes sit at bits 4t..4t+3 and 16+4t..19+4t, and OR 0x6400 makes each the
+// low mantissa bits of an fp16 number with exponent 2^10.
+__device__ __forceinline__ uint32_t int4_pair_bits(uint32_t w, int t) {
+    return and_or(w >> (4 * t), 0x000F000Fu, 0x64006400u);
+}
+
 // Group parameters of one quantization group from its (already reduced)
 // minimum and maximum of v = w * s.  All IEEE fp32, correctly rounded
 // division, round-half-even rint.

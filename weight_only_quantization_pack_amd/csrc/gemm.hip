@@ -2,17 +2,30 @@
 // scale search, both on fp16 MFMA with fp32 accumulation.
 //
 // Y[m][n] = sum_k X[m][k] * B[n][k]   ("NT": both operands K-contiguous)
-//   W4A16: B = w_hat = (q - z) * D, dequantized tile by tile into LDS
-//          (context kernel of the llm-awq README feature list; version
-//          "gemm" of the transformers quantization_config).
-//   loss:  B = D_alpha = W - w_hat_alpha / s_alpha (fp16), and the epilogue
-//          sums Y^2 per tile instead of storing Y.
 //
-// Tiling: a 256-thread workgroup owns a 128x128 output tile and walks K in
-// steps of 128 (one quantization group, so each B row has one scale and one
-// zero per step).  The four waves form a 2x2 grid of 64x64 sub-tiles, each
-// 4x4 v_mfma_f32_16x16x32_f16 blocks.  Global loads of step k+1 are issued
-// into registers before the MFMAs of step k, then written to LDS.
+// W4A16 (k_gemm_w4; context kernel of the llm-awq README feature list,
+// version "gemm" of the transformers quantization_config).  B is the packed
+// format-2 weight: tile (b, g) = 16 rows x group g, lane slot s = 16h + j
+// holding row j's codes 32h..32h+31, which is exactly the B-operand layout
+// of v_mfma_f32_16x16x32_f16 for the four k32 steps of the group (step i
+// uses word i of every slot, physical k = 128g + 32h + 8i + e).  So each
+// wave loads its B tiles straight from HBM/L2 into registers (one 16-byte
+// load per tile per lane, prefetched a group ahead) and dequantizes them in
+// registers: OR 0x6400 gives 1024 + q in fp16, subtracting 1024 + z is
+// exact, one fp16 multiply by the group scale gives w_hat.  Only A (the
+// fp16 activations) goes through LDS: global_load_lds_dwordx4 writes each
+// 128 x 128 A tile straight to LDS (no register staging), double-buffered,
+// with the 16-byte chunks of a row XOR-swizzled by the row so that the
+// MFMA operand reads (8 rows per LDS phase) hit distinct banks.
+// A workgroup (4 waves) owns a 128 x 256 output tile; each wave a 128 x 64
+// strip (8 x 4 MFMA blocks, 128 fp32 accumulators per lane), so per k32 step
+// a wave reads 8 A fragments from LDS and dequantizes 4 B fragments for 32
+// MFMAs.  Tiles are mapped so that each XCD (workgroup id mod 8) walks a
+// contiguous run of row-major tiles and keeps its A rows in its L2.
+//
+// Loss GEMM (k_gemm_loss): B = D_alpha = W - w_hat_alpha / s_alpha (fp16,
+// row-major), 128 x 128 tiles through LDS, and the epilogue sums Y^2 per tile
+// instead of storing Y.
 #include "awq_internal.h"
 
 namespace awq {
@@ -25,7 +38,7 @@ __device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_c
 __device__ __forceinline__ uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
 
 template <bool B_INT4, bool SQSUM>
-__global__ __launch_bounds__(256) void k_gemm(
+__global__ __launch_bounds__(256) void k_gemm_lds(
     const _Float16* __restrict__ A, const void* __restrict__ Bv,
     const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
     _Float16* __restrict__ Y, double* __restrict__ partials, int M, int N, int K,
@@ -184,14 +197,169 @@ __global__ __launch_bounds__(256) void k_gemm(
     }
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void global_void_t;
+
+namespace w4 {
+constexpr int GM = 128, GN = 256, GK = 128;    // workgroup tile; GK = one group
+constexpr int ROW_BYTES = GK * 2;              // one A row of a K-step in LDS
+constexpr int ABUF = GM * ROW_BYTES;           // 32 KB per A buffer
+}  // namespace w4
+
+// fp16 B operand w_hat = (q - z) * D of the 8 int4 codes of one packed word
+__device__ __forceinline__ half8_t dequant_scaled(uint32_t w, half2_t zz, half2_t dd) {
+    half8_t b;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const half2_t p = (as_half2(int4_pair_bits(w, t)) - zz) * dd;
+        b[2 * t] = p[0];
+        b[2 * t + 1] = p[1];
+    }
+    return b;
+}
+
+__global__ __launch_bounds__(256, 2) void k_gemm_w4(
+    const _Float16* __restrict__ A, const uint32_t* __restrict__ qw,
+    const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
+    _Float16* __restrict__ Y, int M, int N, int K) {
+    using namespace w4;
+    __shared__ __attribute__((aligned(16))) unsigned char As[2 * ABUF];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int j = lane & 15, hq = lane >> 4;
+    const int G = K / kGroup;
+    const int NB = (N + 15) / 16;
+    const int nTn = (N + GN - 1) / GN, nTm = (M + GM - 1) / GM;
+    const int nT = nTn * nTm;
+
+    // XCD-aware order: workgroup t runs on XCD t % 8; give each XCD a
+    // contiguous run of row-major tiles so that its tiles share A rows
+    int t = blockIdx.x;
+    if (nT % 8 == 0) t = (t % 8) * (nT / 8) + t / 8;
+    const int m0 = (t / nTn) * GM, n0 = (t % nTn) * GN;
+
+    // A: 32 direct-to-LDS instructions per K-step (1 KB = 4 rows each), 8 per
+    // wave.  Lane l of instruction rg writes LDS chunk p = l & 15 of row
+    // r = 4 rg + (l >> 4), which holds the row's global chunk p ^ (r & 15):
+    // the 16 rows read by one LDS phase then sit on 16 different bank quads.
+    const _Float16* a_src[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int rg = wave * 8 + i;
+        const int r = 4 * rg + (lane >> 4);
+        const int kc = (lane & 15) ^ (r & 15);
+        const int grow = min(m0 + r, M - 1);          // rows past M: any valid row (never stored)
+        a_src[i] = A + (size_t)grow * K + 8 * kc;
+    }
+    auto issue_a = [&](int kt, int buf) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int rg = wave * 8 + i;
+            __builtin_amdgcn_global_load_lds((global_void_t*)(a_src[i] + (size_t)kt * GK),
+                                             (lds_void_t*)(As + buf * ABUF + rg * 1024), 16, 0, 0);
+        }
+    };
+
+    // B: this wave's four 16-row blocks of the 256-column tile
+    size_t tbase[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int blk = min(n0 / 16 + wave * 4 + c, NB - 1);   // blocks past N: never stored
+        tbase[c] = (size_t)blk * G;
+    }
+    uint4 bq[4], bq_next[4];
+    _Float16 bs[4], bz[4], bs_next[4], bz_next[4];
+    auto load_b = [&](int g, uint4* q, _Float16* sc, _Float16* ze) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const size_t tt = tbase[c] + g;
+            q[c] = *reinterpret_cast<const uint4*>(qw + (tt * 64 + lane) * 4);
+            sc[c] = scales[tt * 16 + j];
+            ze[c] = zeros[tt * 16 + j];
+        }
+    };
+
+    float4_t acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[i][c] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+    issue_a(0, 0);
+    load_b(0, bq, bs, bz);
+    for (int kt = 0; kt < G; ++kt) {
+        const int buf = kt & 1;
+        __builtin_amdgcn_s_waitcnt(0);                 // this wave's A(kt) landed in LDS
+        __syncthreads();                               // everyone's A(kt) landed; A(kt-1) reads done
+        if (kt + 1 < G) {
+            issue_a(kt + 1, buf ^ 1);
+            load_b(kt + 1, bq_next, bs_next, bz_next);
+        }
+        half2_t zz[4], dd[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const _Float16 zb = (_Float16)1024.0f + bz[c];
+            zz[c] = (half2_t){zb, zb};
+            dd[c] = (half2_t){bs[c], bs[c]};
+        }
+        const unsigned char* abuf = As + buf * ABUF;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            half8_t b[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t w = s == 0 ? bq[c].x : s == 1 ? bq[c].y : s == 2 ? bq[c].z : bq[c].w;
+                b[c] = dequant_scaled(w, zz[c], dd[c]);
+            }
+            const int kc = 4 * hq + s;                  // A chunk matching the B k-slots
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = 16 * i + j;
+                const half8_t a = *reinterpret_cast<const half8_t*>(
+                    abuf + r * ROW_BYTES + ((kc ^ (r & 15)) << 4));
+                // weights as the A operand, activations as B: the accumulator of
+                // lane 16 hq + j then holds output row m = 16 i + j and the four
+                // consecutive columns 16 c + 4 hq + r
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[c], a, acc[i][c], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) { bq[c] = bq_next[c]; bs[c] = bs_next[c]; bz[c] = bz_next[c]; }
+    }
+
+    // accumulator of lane 16 hq + j, block (i, c): row m = 16 i + j, columns
+    // 16 c + 4 hq + r (r = 0..3) -> one 8-byte store when all four are in range
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int m = m0 + 16 * i + j;
+        if (m >= M) continue;
+        _Float16* yrow = Y + (size_t)m * N;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int n = n0 + wave * 64 + 16 * c + 4 * hq;
+            const half2_t lo = {(_Float16)acc[i][c][0], (_Float16)acc[i][c][1]};
+            const half2_t hi = {(_Float16)acc[i][c][2], (_Float16)acc[i][c][3]};
+            if (n + 3 < N && ((N & 3) == 0)) {
+                *reinterpret_cast<uint2*>(yrow + n) = make_uint2(as_u32(lo), as_u32(hi));
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < N) yrow[n + r] = (_Float16)acc[i][c][r];
+            }
+        }
+    }
+}
+
 }  // namespace
 
 int launch_gemm(const void* x, const void* qweight, const void* scales, const void* zeros,
                 void* y, int M, int N, int K, hipStream_t st) {
-    const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM, 1), block(256);
-    hipLaunchKernelGGL((k_gemm<true, false>), grid, block, 0, st, (const _Float16*)x, qweight,
-                       (const _Float16*)scales, (const _Float16*)zeros, (_Float16*)y,
-                       (double*)nullptr, M, N, K, 0LL);
+    const int nT = ((N + w4::GN - 1) / w4::GN) * ((M + w4::GM - 1) / w4::GM);
+    hipLaunchKernelGGL(k_gemm_w4, dim3(nT), dim3(256), 0, st, (const _Float16*)x,
+                       (const uint32_t*)qweight, (const _Float16*)scales, (const _Float16*)zeros,
+                       (_Float16*)y, M, N, K);
     return (int)hipGetLastError();
 }
 
@@ -202,7 +370,7 @@ size_t loss_gemm_tiles(int T, int N) {
 int launch_loss_gemm(const void* X, const void* D, int T, int N, int K, int n_batch,
                      double* partials, hipStream_t st) {
     const dim3 grid((N + BN - 1) / BN, (T + BM - 1) / BM, n_batch), block(256);
-    hipLaunchKernelGGL((k_gemm<false, true>), grid, block, 0, st, (const _Float16*)X, D,
+    hipLaunchKernelGGL((k_gemm_lds<false, true>), grid, block, 0, st, (const _Float16*)X, D,
                        (const _Float16*)nullptr, (const _Float16*)nullptr, (_Float16*)nullptr,
                        partials, T, N, K, (long long)N * K);
     return (int)hipGetLastError();

@@ -50,7 +50,7 @@ __device__ __forceinline__ half8_t dequant_word_int4(uint32_t w, half2_t zz) {
     half8_t b;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        const half2_t p = as_half2(((w >> (4 * t)) & 0x000F000Fu) | 0x64006400u) - zz;
+        const half2_t p = as_half2(int4_pair_bits(w, t)) - zz;
         b[2 * t] = p[0];
         b[2 * t + 1] = p[1];
     }
@@ -63,7 +63,7 @@ __device__ __forceinline__ half8_t dequant_24_int3(uint32_t v, half2_t zz) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const uint32_t pair = ((v >> (6 * t)) & 7u) | (((v >> (6 * t + 3)) & 7u) << 16);
-        const half2_t p = as_half2(pair | 0x64006400u) - zz;
+        const half2_t p = as_half2(and_or(pair, 0x00070007u, 0x64006400u)) - zz;
         b[2 * t] = p[0];
         b[2 * t + 1] = p[1];
     }
