@@ -34,7 +34,7 @@ namespace {
 #define AWQ_GEMV_WAVES 8
 #endif
 #ifndef AWQ_GEMV_UNROLL
-#define AWQ_GEMV_UNROLL 4
+#define AWQ_GEMV_UNROLL 2
 #endif
 #ifndef AWQ_GEMV_XBUF
 #define AWQ_GEMV_XBUF 65536
@@ -245,6 +245,124 @@ __global__ __launch_bounds__(64 * WK) void k_gemv(
     }
 }
 
+// x staged once per workgroup (all of x fits in LDS): the common decode case.
+// Same tile walk as k_gemv without slices: pointers advance by constant
+// strides, A rows j >= M read row 0 (their outputs are rows >= M, never stored).
+// minimum waves per SIMD (HIP launch-bounds meaning): 4 keeps two 8-wave
+// workgroups resident per CU (<= 128 VGPRs)
+#ifndef AWQ_GEMV_MINBLK
+#define AWQ_GEMV_MINBLK 4
+#endif
+template <int BITS, int WK, int U>
+__global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
+    const _Float16* __restrict__ x, const uint32_t* __restrict__ qweight,
+    const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
+    _Float16* __restrict__ y, int M, int N, int K) {
+    constexpr int WQ = BITS == 4 ? 4 : 3;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int G = K / kGroup;
+    const int NB = (N + 15) / 16;
+    const int XS = K + 8;                              // halves per staged x row
+    _Float16* xs = reinterpret_cast<_Float16*>(smem);
+    float4_t* red = reinterpret_cast<float4_t*>(smem + (((size_t)M * XS * 2 + 15) & ~(size_t)15));
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int j = lane & 15, h = lane >> 4;
+    const int nw = wave < G ? (G - wave + WK - 1) / WK : 0;   // groups g = wave + WK i of a block
+    const size_t tstride = (size_t)WK * 64 * WQ;                // words between this wave's tiles
+    const _Float16* xa0 = xs + (size_t)(j < M ? j : 0) * XS + 32 * h;
+
+    auto load = [&](int b, int i, Slot<WQ>& w, Params& p) {
+        const size_t t = (size_t)b * G + wave + (size_t)WK * i;
+        w = load_slot<WQ>(qweight + (t * 64 + lane) * WQ);
+        p.d = scales[t * 16 + j];
+        p.z = zeros[t * 16 + j];
+    };
+
+    Slot<WQ> cur[U];
+    Params pc[U];
+    int b = blockIdx.x;
+    if (b < NB) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (u < nw) load(b, u, cur[u], pc[u]);
+    }
+    for (int idx = tid; idx < M * (K / 8); idx += 64 * WK) {
+        const int m = idx / (K / 8), c = idx % (K / 8);
+        *reinterpret_cast<uint4*>(xs + (size_t)m * XS + 8 * c) =
+            *reinterpret_cast<const uint4*>(x + (size_t)m * K + 8 * c);
+    }
+    __syncthreads();
+
+    int buf = 0;
+    for (; b < NB; b += gridDim.x) {
+        const int bn = b + gridDim.x;                  // next block of this workgroup
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int i0 = 0; i0 < nw; i0 += U) {
+            Slot<WQ> nxt[U];
+            Params pn[U];
+            if (i0 + U < nw) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (i0 + U + u < nw) load(b, i0 + U + u, nxt[u], pn[u]);
+            } else if (bn < NB) {                      // last batch: prefetch the next block
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (u < nw) load(bn, u, nxt[u], pn[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (i0 + u >= nw) break;               // wave-uniform
+                const int g = wave + WK * (i0 + u);
+                const _Float16 zb = (_Float16)1024.0f + pc[u].z;
+                const half2_t zz = {zb, zb};
+                half8_t bop[4];
+                if constexpr (BITS == 4) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) bop[i] = dequant_word_int4(cur[u].w[i], zz);
+                } else {
+                    const uint32_t w0 = cur[u].w[0], w1 = cur[u].w[1], w2 = cur[u].w[2];
+                    bop[0] = dequant_24_int3(w0 & 0xFFFFFFu, zz);
+                    bop[1] = dequant_24_int3((w0 >> 24) | ((w1 & 0xFFFFu) << 8), zz);
+                    bop[2] = dequant_24_int3((w1 >> 16) | ((w2 & 0xFFu) << 16), zz);
+                    bop[3] = dequant_24_int3(w2 >> 8, zz);
+                }
+                const _Float16* xa = xa0 + (size_t)g * kGroup;
+                float4_t accg = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        *reinterpret_cast<const half8_t*>(xa + 8 * i), bop[i], accg, 0, 0, 0);
+                const float d = (float)pc[u].d;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(d, accg[r], acc[r]);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) { cur[u] = nxt[u]; pc[u] = pn[u]; }
+        }
+        red[(buf * WK + wave) * 64 + lane] = acc;
+        __syncthreads();
+        if (wave == 0) {
+            float4_t sum = red[(buf * WK) * 64 + lane];
+#pragma unroll
+            for (int w = 1; w < WK; ++w) {
+                const float4_t o = red[(buf * WK + w) * 64 + lane];
+                sum[0] += o[0]; sum[1] += o[1]; sum[2] += o[2]; sum[3] += o[3];
+            }
+            const int n = 16 * b + j;
+            if (n < N) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = 4 * h + r;
+                    if (m < M) y[(size_t)m * N + n] = (_Float16)sum[r];
+                }
+            }
+        }
+        buf ^= 1;
+    }
+}
+
 int num_cus() {
     static int cus = 0;
     if (cus == 0) {
@@ -270,19 +388,28 @@ int launch_bits(const void* x, const void* qweight, const void* scales, const vo
         SG = max(kGemvWaves, SG / kGemvWaves * kGemvWaves);
     }
     const size_t lds = gemv_lds_bytes(M, SG, kGemvWaves);
+    auto kern1 = k_gemv_x1<BITS, kGemvWaves, kGemvUnroll>;
     auto kern = k_gemv<BITS, kGemvWaves, kGemvUnroll>;
     if (lds > 64 * 1024) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        const void* f = SG == G ? reinterpret_cast<const void*>(kern1) : reinterpret_cast<const void*>(kern);
+        const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return (int)e;
     }
     // persistent workgroups when x is staged once (as many as fit on a CU by
     // LDS, at most 2 of 8 waves); one row block each otherwise
+#ifndef AWQ_GEMV_PERSIST
+#define AWQ_GEMV_PERSIST 1
+#endif
     const int per_cu = max(1, min(2, (int)((160 * 1024) / lds)));
-    const int grid = SG == G ? min(NB, num_cus() * per_cu) : NB;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kGemvWaves), lds, st,
-                       (const _Float16*)x, (const uint32_t*)qweight, (const _Float16*)scales,
-                       (const _Float16*)zeros, (_Float16*)y, M, N, K, SG);
+    const int grid = (AWQ_GEMV_PERSIST && SG == G) ? min(NB, num_cus() * per_cu) : NB;
+    if (SG == G)
+        hipLaunchKernelGGL(kern1, dim3(grid), dim3(64 * kGemvWaves), lds, st,
+                           (const _Float16*)x, (const uint32_t*)qweight, (const _Float16*)scales,
+                           (const _Float16*)zeros, (_Float16*)y, M, N, K);
+    else
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kGemvWaves), lds, st,
+                           (const _Float16*)x, (const uint32_t*)qweight, (const _Float16*)scales,
+                           (const _Float16*)zeros, (_Float16*)y, M, N, K, SG);
     return (int)hipGetLastError();
 }
 
