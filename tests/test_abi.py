@@ -115,6 +115,7 @@ def test_gemv_and_gemm_specific_limits(lib):
     assert mm(lib, "awq_gemv", M=17) == UNSUP
     assert mm(lib, "awq_gemm", bits=3) == UNSUP
     assert mm(lib, "awq_gemv", M=17, bits=3, x=NUL) == UNSUP
+    assert mm(lib, "awq_gemm", M=1 << 20, K=4096) == SHAPE      # 32-bit offset limit
 
 
 def test_scale_activations_validation(lib):

@@ -133,6 +133,8 @@ int awq_gemm(const void* x, const void* qweight, const void* scales, const void*
     if (bits != 4) return AWQ_ERR_UNSUPPORTED;
     if (M < 0) return AWQ_ERR_SHAPE;
     if ((st = check_nk(N, K))) return st;
+    // the prefill kernel addresses x and the packed tiles with 32-bit offsets
+    if ((long long)M * K >= (1LL << 31) || (long long)N * K / 8 >= (1LL << 31)) return AWQ_ERR_SHAPE;
     if (M == 0 || N == 0) return AWQ_OK;
     if ((st = check_ptrs({x, qweight, scales, zeros, y}))) return st;
     return hip_status(awq::launch_gemm(x, qweight, scales, zeros, y, M, N, K,

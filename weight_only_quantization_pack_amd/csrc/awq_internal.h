@@ -50,6 +50,19 @@ __device__ __forceinline__ uint32_t int4_pair_bits(uint32_t w, int t) {
     return and_or(w >> (4 * t), 0x000F000Fu, 0x64006400u);
 }
 
+// The four fp16 pairs of a packed int4 word with one shift.  Pairs t = 0, 2
+// (code nibbles at bits 0..3 / 16..19 of w and of w >> 8) use exponent 2^10,
+// giving 1024 + q; pairs t = 1, 3 (nibbles at bits 4..7 / 20..23) are OR-ed
+// in place under 0x5400 = 64.0, whose mantissa step is 1/16, giving 64 + q.
+// Subtracting 1024 + z resp. 64 + z leaves q - z exactly in every lane.
+__device__ __forceinline__ void int4_word_pairs(uint32_t w, uint32_t p[4]) {
+    const uint32_t w8 = w >> 8;
+    p[0] = and_or(w, 0x000F000Fu, 0x64006400u);
+    p[1] = and_or(w, 0x00F000F0u, 0x54005400u);
+    p[2] = and_or(w8, 0x000F000Fu, 0x64006400u);
+    p[3] = and_or(w8, 0x00F000F0u, 0x54005400u);
+}
+
 // Group parameters of one quantization group from its (already reduced)
 // minimum and maximum of v = w * s.  All IEEE fp32, correctly rounded
 // division, round-half-even rint.

@@ -206,12 +206,15 @@ constexpr int ROW_BYTES = GK * 2;              // one A row of a K-step in LDS
 constexpr int ABUF = GM * ROW_BYTES;           // 32 KB per A buffer
 }  // namespace w4
 
-// fp16 B operand w_hat = (q - z) * D of the 8 int4 codes of one packed word
-__device__ __forceinline__ half8_t dequant_scaled(uint32_t w, half2_t zz, half2_t dd) {
+// fp16 B operand w_hat = (q - z) * D of the 8 int4 codes of one packed word;
+// zz = 1024 + z (even pairs), zz16 = 64 + z (odd pairs, see int4_word_pairs)
+__device__ __forceinline__ half8_t dequant_scaled(uint32_t w, half2_t zz, half2_t zz16, half2_t dd) {
+    uint32_t pr[4];
+    int4_word_pairs(w, pr);
     half8_t b;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        const half2_t p = (as_half2(int4_pair_bits(w, t)) - zz) * dd;
+        const half2_t p = (as_half2(pr[t]) - ((t & 1) ? zz16 : zz)) * dd;
         b[2 * t] = p[0];
         b[2 * t + 1] = p[1];
     }
@@ -225,7 +228,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(
     using namespace w4;
     __shared__ __attribute__((aligned(16))) unsigned char As[2 * ABUF];
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: SGPR math
     const int j = lane & 15, hq = lane >> 4;
     const int G = K / kGroup;
     const int NB = (N + 15) / 16;
@@ -242,40 +246,41 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(
     // wave.  Lane l of instruction rg writes LDS chunk p = l & 15 of row
     // r = 4 rg + (l >> 4), which holds the row's global chunk p ^ (r & 15):
     // the 16 rows read by one LDS phase then sit on 16 different bank quads.
-    const _Float16* a_src[8];
+    // 32-bit element offsets into A (the launcher guarantees M * K < 2^31)
+    uint32_t a_off[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int rg = wave * 8 + i;
         const int r = 4 * rg + (lane >> 4);
         const int kc = (lane & 15) ^ (r & 15);
         const int grow = min(m0 + r, M - 1);          // rows past M: any valid row (never stored)
-        a_src[i] = A + (size_t)grow * K + 8 * kc;
+        a_off[i] = (uint32_t)grow * (uint32_t)K + 8u * kc;
     }
     auto issue_a = [&](int kt, int buf) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int rg = wave * 8 + i;
-            __builtin_amdgcn_global_load_lds((global_void_t*)(a_src[i] + (size_t)kt * GK),
+            __builtin_amdgcn_global_load_lds((global_void_t*)(A + a_off[i] + (uint32_t)kt * GK),
                                              (lds_void_t*)(As + buf * ABUF + rg * 1024), 16, 0, 0);
         }
     };
 
     // B: this wave's four 16-row blocks of the 256-column tile
-    size_t tbase[4];
+    // tile index of this wave's four 16-row blocks at group 0 (N * K / 2048 < 2^31)
+    uint32_t tbase[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const int blk = min(n0 / 16 + wave * 4 + c, NB - 1);   // blocks past N: never stored
-        tbase[c] = (size_t)blk * G;
+        tbase[c] = (uint32_t)blk * (uint32_t)G;
     }
     uint4 bq[4], bq_next[4];
-    _Float16 bs[4], bz[4], bs_next[4], bz_next[4];
-    auto load_b = [&](int g, uint4* q, _Float16* sc, _Float16* ze) {
+    half2_t bp[4], bp_next[4];                          // (scale, zero) of each block's row j
+    auto load_b = [&](int g, uint4* q, half2_t* p) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const size_t tt = tbase[c] + g;
-            q[c] = *reinterpret_cast<const uint4*>(qw + (tt * 64 + lane) * 4);
-            sc[c] = scales[tt * 16 + j];
-            ze[c] = zeros[tt * 16 + j];
+            const uint32_t tt = tbase[c] + (uint32_t)g;
+            q[c] = *reinterpret_cast<const uint4*>(qw + (size_t)(tt * 256u + 4u * lane));
+            p[c] = (half2_t){scales[tt * 16u + j], zeros[tt * 16u + j]};
         }
     };
 
@@ -286,21 +291,23 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(
         for (int c = 0; c < 4; ++c) acc[i][c] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
     issue_a(0, 0);
-    load_b(0, bq, bs, bz);
+    load_b(0, bq, bp);
     for (int kt = 0; kt < G; ++kt) {
         const int buf = kt & 1;
         __builtin_amdgcn_s_waitcnt(0);                 // this wave's A(kt) landed in LDS
         __syncthreads();                               // everyone's A(kt) landed; A(kt-1) reads done
         if (kt + 1 < G) {
             issue_a(kt + 1, buf ^ 1);
-            load_b(kt + 1, bq_next, bs_next, bz_next);
+            load_b(kt + 1, bq_next, bp_next);
         }
-        half2_t zz[4], dd[4];
+        half2_t zz[4], zz16[4], dd[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const _Float16 zb = (_Float16)1024.0f + bz[c];
+            const _Float16 zb = (_Float16)1024.0f + bp[c][1];
+            const _Float16 zb16 = (_Float16)64.0f + bp[c][1];
             zz[c] = (half2_t){zb, zb};
-            dd[c] = (half2_t){bs[c], bs[c]};
+            zz16[c] = (half2_t){zb16, zb16};
+            dd[c] = (half2_t){bp[c][0], bp[c][0]};
         }
         const unsigned char* abuf = As + buf * ABUF;
 #pragma unroll
@@ -309,7 +316,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const uint32_t w = s == 0 ? bq[c].x : s == 1 ? bq[c].y : s == 2 ? bq[c].z : bq[c].w;
-                b[c] = dequant_scaled(w, zz[c], dd[c]);
+                b[c] = dequant_scaled(w, zz[c], zz16[c], dd[c]);
             }
             const int kc = 4 * hq + s;                  // A chunk matching the B k-slots
 #pragma unroll
@@ -324,9 +331,23 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(
                 for (int c = 0; c < 4; ++c)
                     acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b[c], a, acc[i][c], 0, 0, 0);
             }
+            // schedule hint: 4 LDS reads up front, then (4 MFMAs, 1 LDS read) x 4 so
+            // reads run ahead of their MFMAs, then the remaining 16 MFMAs each
+            // followed by up to 3 VALU ops (the next step's dequantization)
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+            }
         }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) { bq[c] = bq_next[c]; bs[c] = bs_next[c]; bz[c] = bz_next[c]; }
+        for (int c = 0; c < 4; ++c) { bq[c] = bq_next[c]; bp[c] = bp_next[c]; }
     }
 
     // accumulator of lane 16 hq + j, block (i, c): row m = 16 i + j, columns
@@ -356,6 +377,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(
 
 int launch_gemm(const void* x, const void* qweight, const void* scales, const void* zeros,
                 void* y, int M, int N, int K, hipStream_t st) {
+    // the kernel uses 32-bit element offsets into x and into the packed tiles
+    if ((unsigned long long)M * K >= (1ull << 31) || (unsigned long long)N * K / 8 >= (1ull << 31))
+        return (int)hipErrorInvalidValue;
     const int nT = ((N + w4::GN - 1) / w4::GN) * ((M + w4::GM - 1) / w4::GM);
     hipLaunchKernelGGL(k_gemm_w4, dim3(nT), dim3(256), 0, st, (const _Float16*)x,
                        (const uint32_t*)qweight, (const _Float16*)scales, (const _Float16*)zeros,

@@ -45,12 +45,15 @@ constexpr int kGemvXBuf = AWQ_GEMV_XBUF;      // LDS bytes for the staged x slic
 
 __device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 
-// fp16 operand (q - z) of 8 int4 codes in one packed word.
-__device__ __forceinline__ half8_t dequant_word_int4(uint32_t w, half2_t zz) {
+// fp16 operand (q - z) of 8 int4 codes in one packed word; zz = 1024 + z for
+// the even pairs, zz16 = 64 + z for the odd pairs (see int4_word_pairs).
+__device__ __forceinline__ half8_t dequant_word_int4(uint32_t w, half2_t zz, half2_t zz16) {
+    uint32_t pr[4];
+    int4_word_pairs(w, pr);
     half8_t b;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        const half2_t p = as_half2(int4_pair_bits(w, t)) - zz;
+        const half2_t p = as_half2(pr[t]) - ((t & 1) ? zz16 : zz);
         b[2 * t] = p[0];
         b[2 * t + 1] = p[1];
     }
@@ -180,11 +183,12 @@ __global__ __launch_bounds__(64 * WK) void k_gemv(
                 const int g = wave + WK * (i_cur + u);
                 const int gl = one_slice ? g : g % SG;                   // group within the staged slice
                 const _Float16 zb = (_Float16)1024.0f + pc[u].z;
-                const half2_t zz = {zb, zb};
+                const _Float16 zb16 = (_Float16)64.0f + pc[u].z;
+                const half2_t zz = {zb, zb}, zz16 = {zb16, zb16};
                 half8_t bop[4];
                 if constexpr (BITS == 4) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) bop[i] = dequant_word_int4(cur[u].w[i], zz);
+                    for (int i = 0; i < 4; ++i) bop[i] = dequant_word_int4(cur[u].w[i], zz, zz16);
                 } else {
                     // 96-bit stream of 32 codes; operand i takes stream bits 24i..24i+23
                     const uint32_t w0 = cur[u].w[0], w1 = cur[u].w[1], w2 = cur[u].w[2];
@@ -316,11 +320,12 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
                 if (i0 + u >= nw) break;               // wave-uniform
                 const int g = wave + WK * (i0 + u);
                 const _Float16 zb = (_Float16)1024.0f + pc[u].z;
-                const half2_t zz = {zb, zb};
+                const _Float16 zb16 = (_Float16)64.0f + pc[u].z;
+                const half2_t zz = {zb, zb}, zz16 = {zb16, zb16};
                 half8_t bop[4];
                 if constexpr (BITS == 4) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) bop[i] = dequant_word_int4(cur[u].w[i], zz);
+                    for (int i = 0; i < 4; ++i) bop[i] = dequant_word_int4(cur[u].w[i], zz, zz16);
                 } else {
                     const uint32_t w0 = cur[u].w[0], w1 = cur[u].w[1], w2 = cur[u].w[2];
                     bop[0] = dequant_24_int3(w0 & 0xFFFFFFu, zz);
