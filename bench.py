@@ -49,6 +49,28 @@ def gemv_bytes(M, N, K, bits=4):
     return N * K * bits // 8 + 4 * N * (K // 128) + 2 * M * K + 2 * M * N
 
 
+def gemv_traffic_per_launch():
+    """HBM bytes per decode GEMV launch from the committed rocprofv3 PMC runs.
+
+    profiles/gemv_llama7b_decode_traffic.json holds FETCH_SIZE + WRITE_SIZE,
+    scaled by a copy of known size, per launch of the decode step.  It is used
+    only while its recorded hash matches the current GEMV source; after any
+    change to the kernel the counters are stale and the traffic is null.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemv_llama7b_decode_traffic.json")
+    csrc = os.path.join(ROOT, "weight_only_quantization_pack_amd", "csrc")
+    try:
+        rec = json.load(open(path))
+        src = open(os.path.join(csrc, "gemv.hip"), "rb").read() + \
+            open(os.path.join(csrc, "awq_internal.h"), "rb").read()
+    except (OSError, ValueError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -57,6 +79,9 @@ def main(argv=None):
     ap.add_argument("--gemm-iters", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-offline", action="store_true")
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="short run for rocprofv3 --pmc: a 256 MiB device copy (known size, "
+                         "calibrates FETCH_SIZE/WRITE_SIZE) then one cold pass of the decode step")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -105,6 +130,22 @@ def main(argv=None):
         for j, (K, N) in enumerate(layer):
             qw, sc, ze = reps[r][j]
             awq.gemv(xs[K], qw, sc, ze, N=N, bits=4, out=ys[j])
+
+    if args.pmc_probe:
+        # calibration copy of known size, then each replica's decode step once
+        src = torch.empty(256 * 2**20, dtype=torch.uint8, device=dev).random_(0, 255)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for r in range(R):
+                step(r)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_probe": True, "copy_bytes": src.numel(), "step_bytes": step_bytes,
+                          "gemv_launch_bytes": {f"{K}x{N}": gemv_bytes(1, N, K) for K, N in layer}}))
+        return 0
 
     # one graph = R consecutive steps, each on its own replica
     with torch.cuda.stream(stream):
@@ -258,14 +299,16 @@ def main(argv=None):
                    "group_size": 128, "step_bytes": step_bytes, "cold_weight_replicas": R,
                    "launch": "HIP graph replay"},
         "roofline": {"bound": "hbm", "achieved": round(gemv_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gemv_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "k_gemv_int4<1>", "avg_launch_us": round(avg_launch_us, 3)},
+                     "unit": "GB/s", "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": gemv_traffic_per_launch(), "traffic_unit": "HBM bytes per launch",
+                     "algorithmic_bytes_per_launch": round(step_bytes / len(layer)),
+                     "kernel": "k_gemv_x1<4,8,2>", "avg_launch_us": round(avg_launch_us, 3)},
         "gemv_per_shape": per_shape,
         "gemm": {"M": M, "TFLOPs": round(gemm_tflops, 1), "per_shape": gemm_res,
                  "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1),
                               "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                              "traffic": None, "kernel": "k_gemm<true,false>"}},
+                              "traffic": None, "kernel": "k_gemm_w4"}},
         "offline": offline,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count,
