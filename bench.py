@@ -302,7 +302,7 @@ def main(argv=None):
                      "unit": "GB/s", "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
                      "traffic": gemv_traffic_per_launch(), "traffic_unit": "HBM bytes per launch",
                      "algorithmic_bytes_per_launch": round(step_bytes / len(layer)),
-                     "kernel": "k_gemv_x1<4,8,2>", "avg_launch_us": round(avg_launch_us, 3)},
+                     "kernel": "k_gemv_x1<4,8,U> (ring U=2 for K=4096, U=4 for K=11008)", "avg_launch_us": round(avg_launch_us, 3)},
         "gemv_per_shape": per_shape,
         "gemm": {"M": M, "TFLOPs": round(gemm_tflops, 1), "per_shape": gemm_res,
                  "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1),

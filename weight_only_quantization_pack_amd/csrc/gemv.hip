@@ -13,11 +13,12 @@
 // A workgroup of WK waves owns one row block at a time and loops over row
 // blocks blockIdx.x, +gridDim.x, ... (the grid is sized to the machine).
 // Its waves take the groups round-robin, so each step of the workgroup reads
-// WK consecutive tiles and the block's slab is swept front to back.  Each
-// wave keeps its next U tiles (1 KB wave load each) and their 32-byte scale
-// and zero loads in flight while it computes on the current U; the rolling
-// prefetch runs on across row blocks.  x is staged in LDS once per
-// workgroup (or once per K-slice when M*K is large).
+// WK consecutive tiles and the block's slab is swept front to back.  When x
+// fits in LDS (k_gemv_x1, the decode case) it is staged once per workgroup and
+// each wave streams its tiles (1 KB wave load each, plus the tile's scales and
+// zeros) through a ring of U register slots with a fixed-order load stream,
+// so U tiles stay in flight across row blocks.  Otherwise (k_gemv) x is
+// staged one K-slice at a time and each wave double-buffers U tiles.
 //
 // Dequantization is exact: OR 0x6400 turns a 4-bit code q into the fp16
 // value 1024 + q and subtracting 1024 + z leaves q - z, so each group's
@@ -42,6 +43,12 @@ namespace {
 constexpr int kGemvWaves = AWQ_GEMV_WAVES;    // waves per workgroup
 constexpr int kGemvUnroll = AWQ_GEMV_UNROLL;  // tiles per wave per load batch
 constexpr int kGemvXBuf = AWQ_GEMV_XBUF;      // LDS bytes for the staged x slice
+// tiles in flight per wave when x is staged once: 2 while a wave has at most 4
+// tiles per row block (a deeper ring only moves dequantization and MFMA work
+// behind the last byte to land), 4 for longer rows (measured on MI355X:
+// 4096x4096 4.9 us with 2 vs 5.1 with 4; 11008x4096 8.0 us with 4 vs 9.1)
+constexpr int kGemvRingShort = 2;
+constexpr int kGemvRingLong = 4;
 
 __device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 
@@ -250,13 +257,53 @@ __global__ __launch_bounds__(64 * WK) void k_gemv(
 }
 
 // x staged once per workgroup (all of x fits in LDS): the common decode case.
-// Same tile walk as k_gemv without slices: pointers advance by constant
-// strides, A rows j >= M read row 0 (their outputs are rows >= M, never stored).
+//
+// Each wave streams its tiles through a ring of U register slots: slot u holds
+// item i0 + u of the current block (items are the wave's groups g = wave + WK i,
+// padded per block to a multiple of U), and right after the item has been
+// consumed the slot is refilled with the item U places further on, which may
+// belong to the workgroup's next block.  The load stream is branch-free: items
+// past the wave's groups or past the last block are issued as buffer loads at an
+// out-of-range offset, which return zero without touching memory.  With a fixed
+// number of loads between a slot's fill and its use the compiler waits on
+// exactly that slot (vmcnt(3 (U - 1))), so U tiles stay in flight per wave
+// through the whole sweep, across row blocks and the reduction barrier.
 // minimum waves per SIMD (HIP launch-bounds meaning): 4 keeps two 8-wave
 // workgroups resident per CU (<= 128 VGPRs)
 #ifndef AWQ_GEMV_MINBLK
 #define AWQ_GEMV_MINBLK 4
 #endif
+
+constexpr uint32_t kBufferOutOfRange = 0x80000000u;   // > every buffer's size (< 2^31 bytes)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+    // raw buffer (stride 0): byte offsets, range-checked against `bytes`
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int WQ>
+__device__ __forceinline__ Slot<WQ> buffer_slot(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    Slot<WQ> s;
+    if constexpr (WQ == 4) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        s.w[0] = v[0]; s.w[1] = v[1]; s.w[2] = v[2]; s.w[3] = v[3];
+    } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+        s.w[0] = v[0]; s.w[1] = v[1]; s.w[2] = v[2];
+    }
+    return s;
+}
+
+// a tile's scale and zero as loaded: the aligned 32-bit word holding the
+// lane's entry (and its neighbour's), one register each, reduced to the lane's
+// half only when the tile is consumed -- narrowing or packing the values at
+// load time would make the compiler wait for the loads right away
+struct RawParams { uint32_t d, z; };
+
+__device__ __forceinline__ _Float16 low_half(uint32_t v) {
+    return __builtin_bit_cast(_Float16, (unsigned short)v);
+}
+
 template <int BITS, int WK, int U>
 __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qweight,
@@ -274,28 +321,57 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
     const int lane = tid & 63, wave = tid >> 6;
     const int j = lane & 15, h = lane >> 4;
     const int nw = wave < G ? (G - wave + WK - 1) / WK : 0;   // groups g = wave + WK i of a block
-    const size_t tstride = (size_t)WK * 64 * WQ;                // words between this wave's tiles
+    const int nwp = (nw + U - 1) / U * U;                       // ring items per block
     const _Float16* xa0 = xs + (size_t)(j < M ? j : 0) * XS + 32 * h;
+    const uint32_t psh = 16u * (uint32_t)(j & 1);              // the lane's half of a param word
 
-    auto load = [&](int b, int i, Slot<WQ>& w, Params& p) {
-        const size_t t = (size_t)b * G + wave + (size_t)WK * i;
-        w = load_slot<WQ>(qweight + (t * 64 + lane) * WQ);
-        p.d = scales[t * 16 + j];
-        p.z = zeros[t * 16 + j];
+    // the launcher guarantees every buffer is < 2^31 bytes
+    const uint32_t tiles = (uint32_t)NB * (uint32_t)G;
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(qweight, tiles * 64u * WQ * 4u);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scales, tiles * 32u);
+    const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(zeros, tiles * 32u);
+    auto load = [&](int b, int i, Slot<WQ>& w, RawParams& p) {
+        const bool ok = b < NB && i < nw;
+        const uint32_t t = (uint32_t)b * (uint32_t)G + (uint32_t)(wave + WK * i);
+        const uint32_t oq = ok ? (t * 64u + (uint32_t)lane) * (WQ * 4u) : kBufferOutOfRange;
+        const uint32_t op = ok ? (t * 16u + (uint32_t)(j & ~1)) * 2u : kBufferOutOfRange;
+        w = buffer_slot<WQ>(rq, oq);
+        p.d = __builtin_amdgcn_raw_buffer_load_b32(rs, op, 0, 0);
+        p.z = __builtin_amdgcn_raw_buffer_load_b32(rz, op, 0, 0);
     };
 
-    Slot<WQ> cur[U];
-    Params pc[U];
-    int b = blockIdx.x;
-    if (b < NB) {
+    // x first (16-byte chunks, XC per thread; chunks past M*K are out-of-range
+    // loads), then the ring in slot order: the x stores below wait for the x
+    // loads only, and the loads in flight on entry to the sweep are ordered as
+    // in the sweep itself, so the first tile is consumed as soon as it lands
+    constexpr int XC = kGemvXBuf / (64 * WK * 16);
+    const uint32_t xbytes = (uint32_t)M * (uint32_t)K * 2u;
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x, xbytes);
+    uint4 xv[XC];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (u < nw) load(b, u, cur[u], pc[u]);
+    for (int c = 0; c < XC; ++c) {
+        const uint32_t off = (uint32_t)(tid + 64 * WK * c) * 16u;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, off < xbytes ? off : kBufferOutOfRange, 0, 0);
+        xv[c] = make_uint4(v[0], v[1], v[2], v[3]);
     }
-    for (int idx = tid; idx < M * (K / 8); idx += 64 * WK) {
-        const int m = idx / (K / 8), c = idx % (K / 8);
-        *reinterpret_cast<uint4*>(xs + (size_t)m * XS + 8 * c) =
-            *reinterpret_cast<const uint4*>(x + (size_t)m * K + 8 * c);
+    Slot<WQ> ring[U];
+    RawParams pr[U];
+    int b = blockIdx.x;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        load(b, u, ring[u], pr[u]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < XC; ++c) {
+        // chunk of 8 halves; a chunk past M*K (zeros) lands in row 0's padding
+        // xs[K..K+7], which no read touches -- an unconditional store keeps the
+        // x load ahead of the ring loads
+        const int idx = tid + 64 * WK * c;
+        const int m = idx / (K / 8), col = idx % (K / 8);
+        const size_t at = idx < M * (K / 8) ? (size_t)m * XS + 8 * col : (size_t)K;
+        *reinterpret_cast<uint4*>(xs + at) = xv[c];
     }
     __syncthreads();
 
@@ -303,48 +379,41 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
     for (; b < NB; b += gridDim.x) {
         const int bn = b + gridDim.x;                  // next block of this workgroup
         float4_t acc = {0.f, 0.f, 0.f, 0.f};
-        for (int i0 = 0; i0 < nw; i0 += U) {
-            Slot<WQ> nxt[U];
-            Params pn[U];
-            if (i0 + U < nw) {
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    if (i0 + U + u < nw) load(b, i0 + U + u, nxt[u], pn[u]);
-            } else if (bn < NB) {                      // last batch: prefetch the next block
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    if (u < nw) load(bn, u, nxt[u], pn[u]);
-            }
+        for (int i0 = 0; i0 < nwp; i0 += U) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                if (i0 + u >= nw) break;               // wave-uniform
-                const int g = wave + WK * (i0 + u);
-                const _Float16 zb = (_Float16)1024.0f + pc[u].z;
-                const _Float16 zb16 = (_Float16)64.0f + pc[u].z;
-                const half2_t zz = {zb, zb}, zz16 = {zb16, zb16};
-                half8_t bop[4];
-                if constexpr (BITS == 4) {
+                const int i = i0 + u;
+                if (i < nw) {                          // wave-uniform; loads stay outside
+                    const _Float16 zh = low_half(pr[u].z >> psh);
+                    const _Float16 zb = (_Float16)1024.0f + zh;
+                    const _Float16 zb16 = (_Float16)64.0f + zh;
+                    const half2_t zz = {zb, zb}, zz16 = {zb16, zb16};
+                    half8_t bop[4];
+                    if constexpr (BITS == 4) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) bop[i] = dequant_word_int4(cur[u].w[i], zz, zz16);
-                } else {
-                    const uint32_t w0 = cur[u].w[0], w1 = cur[u].w[1], w2 = cur[u].w[2];
-                    bop[0] = dequant_24_int3(w0 & 0xFFFFFFu, zz);
-                    bop[1] = dequant_24_int3((w0 >> 24) | ((w1 & 0xFFFFu) << 8), zz);
-                    bop[2] = dequant_24_int3((w1 >> 16) | ((w2 & 0xFFu) << 16), zz);
-                    bop[3] = dequant_24_int3(w2 >> 8, zz);
+                        for (int q = 0; q < 4; ++q) bop[q] = dequant_word_int4(ring[u].w[q], zz, zz16);
+                    } else {
+                        const uint32_t w0 = ring[u].w[0], w1 = ring[u].w[1], w2 = ring[u].w[2];
+                        bop[0] = dequant_24_int3(w0 & 0xFFFFFFu, zz);
+                        bop[1] = dequant_24_int3((w0 >> 24) | ((w1 & 0xFFFFu) << 8), zz);
+                        bop[2] = dequant_24_int3((w1 >> 16) | ((w2 & 0xFFu) << 16), zz);
+                        bop[3] = dequant_24_int3(w2 >> 8, zz);
+                    }
+                    const _Float16* xa = xa0 + (size_t)(wave + WK * i) * kGroup;
+                    float4_t accg = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            *reinterpret_cast<const half8_t*>(xa + 8 * q), bop[q], accg, 0, 0, 0);
+                    const float d = (float)low_half(pr[u].d >> psh);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(d, accg[r], acc[r]);
                 }
-                const _Float16* xa = xa0 + (size_t)g * kGroup;
-                float4_t accg = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        *reinterpret_cast<const half8_t*>(xa + 8 * i), bop[i], accg, 0, 0, 0);
-                const float d = (float)pc[u].d;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(d, accg[r], acc[r]);
+                // refill the slot with the item U places on (this block or the next)
+                const int k = i + U;
+                const bool here = k < nwp;
+                load(here ? b : bn, here ? k : k - nwp, ring[u], pr[u]);
             }
-#pragma unroll
-            for (int u = 0; u < U; ++u) { cur[u] = nxt[u]; pc[u] = pn[u]; }
         }
         red[(buf * WK + wave) * 64 + lane] = acc;
         __syncthreads();
@@ -392,11 +461,16 @@ int launch_bits(const void* x, const void* qweight, const void* scales, const vo
     } else {
         SG = max(kGemvWaves, SG / kGemvWaves * kGemvWaves);
     }
+    // the ring kernel addresses its buffers with 32-bit offsets (< 2^31 bytes)
+    constexpr size_t WQ = BITS == 4 ? 4 : 3;
+    const size_t tiles = (size_t)NB * G;
+    const bool ring = SG == G && tiles * 64 * WQ * 4 < ((size_t)1 << 31);
     const size_t lds = gemv_lds_bytes(M, SG, kGemvWaves);
-    auto kern1 = k_gemv_x1<BITS, kGemvWaves, kGemvUnroll>;
+    auto kern1 = G <= 4 * kGemvWaves ? k_gemv_x1<BITS, kGemvWaves, kGemvRingShort>
+                                     : k_gemv_x1<BITS, kGemvWaves, kGemvRingLong>;
     auto kern = k_gemv<BITS, kGemvWaves, kGemvUnroll>;
     if (lds > 64 * 1024) {
-        const void* f = SG == G ? reinterpret_cast<const void*>(kern1) : reinterpret_cast<const void*>(kern);
+        const void* f = ring ? reinterpret_cast<const void*>(kern1) : reinterpret_cast<const void*>(kern);
         const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return (int)e;
     }
@@ -407,7 +481,7 @@ int launch_bits(const void* x, const void* qweight, const void* scales, const vo
 #endif
     const int per_cu = max(1, min(2, (int)((160 * 1024) / lds)));
     const int grid = (AWQ_GEMV_PERSIST && SG == G) ? min(NB, num_cus() * per_cu) : NB;
-    if (SG == G)
+    if (ring)
         hipLaunchKernelGGL(kern1, dim3(grid), dim3(64 * kGemvWaves), lds, st,
                            (const _Float16*)x, (const uint32_t*)qweight, (const _Float16*)scales,
                            (const _Float16*)zeros, (_Float16*)y, M, N, K);
