@@ -47,7 +47,10 @@ constexpr int kGemvXBuf = AWQ_GEMV_XBUF;      // LDS bytes for the staged x slic
 // tiles per row block (a deeper ring only moves dequantization and MFMA work
 // behind the last byte to land), 4 for longer rows (measured on MI355X:
 // 4096x4096 4.9 us with 2 vs 5.1 with 4; 11008x4096 8.0 us with 4 vs 9.1)
-constexpr int kGemvRingShort = 2;
+#ifndef AWQ_GEMV_RING_SHORT
+#define AWQ_GEMV_RING_SHORT 2
+#endif
+constexpr int kGemvRingShort = AWQ_GEMV_RING_SHORT;
 constexpr int kGemvRingLong = 4;
 
 __device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
@@ -304,7 +307,7 @@ __device__ __forceinline__ _Float16 low_half(uint32_t v) {
     return __builtin_bit_cast(_Float16, (unsigned short)v);
 }
 
-template <int BITS, int WK, int U>
+template <int BITS, int WK, int U, int XL>
 __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qweight,
     const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
@@ -340,19 +343,29 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
         p.z = __builtin_amdgcn_raw_buffer_load_b32(rz, op, 0, 0);
     };
 
-    // x first (16-byte chunks, XC per thread; chunks past M*K are out-of-range
-    // loads), then the ring in slot order: the x stores below wait for the x
-    // loads only, and the loads in flight on entry to the sweep are ordered as
-    // in the sweep itself, so the first tile is consumed as soon as it lands
-    constexpr int XC = kGemvXBuf / (64 * WK * 16);
-    const uint32_t xbytes = (uint32_t)M * (uint32_t)K * 2u;
-    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x, xbytes);
-    uint4 xv[XC];
+    // Each wave stages only the x columns of its own groups (the same groups in
+    // every block), so it waits for no other wave before its sweep.  Lanes
+    // 16p'..16p'+15 of load p carry the 256-byte (group, row) pair
+    // q = (lane >> 4) + 4p as 16-byte chunks; pairs past the wave's nw * M are
+    // out-of-range loads whose zeros land in row 0's padding xs[K..K+7], which
+    // no read touches.  x is loaded before the ring and the stores are
+    // unconditional, so they wait for the x loads alone, and the loads in
+    // flight on entry to the sweep are ordered as in the sweep itself.
+    const int pairs = nw * M;
+    const uint32_t mdiv = 65536u / (uint32_t)M + 1u;   // q / M = (q * mdiv) >> 16 for q < 2048, M <= 16
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+    uint4 xv[XL];
+    uint32_t xat[XL];
 #pragma unroll
-    for (int c = 0; c < XC; ++c) {
-        const uint32_t off = (uint32_t)(tid + 64 * WK * c) * 16u;
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, off < xbytes ? off : kBufferOutOfRange, 0, 0);
-        xv[c] = make_uint4(v[0], v[1], v[2], v[3]);
+    for (int p = 0; p < XL; ++p) {
+        const uint32_t q = (uint32_t)((lane >> 4) + 4 * p);
+        const uint32_t i = (q * mdiv) >> 16, m = q - i * (uint32_t)M;
+        const uint32_t col = (uint32_t)kGroup * (uint32_t)(wave + WK * (int)i) + 8u * (uint32_t)j;
+        const bool ok = (int)q < pairs;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+            rx, ok ? (m * (uint32_t)K + col) * 2u : kBufferOutOfRange, 0, 0);
+        xv[p] = make_uint4(v[0], v[1], v[2], v[3]);
+        xat[p] = ok ? m * (uint32_t)XS + col : (uint32_t)K;
     }
     Slot<WQ> ring[U];
     RawParams pr[U];
@@ -364,19 +377,14 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int c = 0; c < XC; ++c) {
-        // chunk of 8 halves; a chunk past M*K (zeros) lands in row 0's padding
-        // xs[K..K+7], which no read touches -- an unconditional store keeps the
-        // x load ahead of the ring loads
-        const int idx = tid + 64 * WK * c;
-        const int m = idx / (K / 8), col = idx % (K / 8);
-        const size_t at = idx < M * (K / 8) ? (size_t)m * XS + 8 * col : (size_t)K;
-        *reinterpret_cast<uint4*>(xs + at) = xv[c];
-    }
-    __syncthreads();
+    for (int p = 0; p < XL; ++p) *reinterpret_cast<uint4*>(xs + xat[p]) = xv[p];
+    // the wave's own LDS stores complete before its lanes read each other's chunks
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
+    // grid <= NB, so every workgroup has a first block; a loop without an entry
+    // test keeps the compiler from sinking the ring loads above into it
     int buf = 0;
-    for (; b < NB; b += gridDim.x) {
+    do {
         const int bn = b + gridDim.x;                  // next block of this workgroup
         float4_t acc = {0.f, 0.f, 0.f, 0.f};
         for (int i0 = 0; i0 < nwp; i0 += U) {
@@ -434,7 +442,8 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
             }
         }
         buf ^= 1;
-    }
+        b = bn;
+    } while (b < NB);
 }
 
 int num_cus() {
@@ -448,6 +457,24 @@ int num_cus() {
             cus = 256;
     }
     return cus;
+}
+
+// k_gemv_x1 instance: ring depth (short rows: 2, else 4) and the number of
+// 16-byte x loads per lane that stage a wave's (group, row) pairs (<= 12:
+// M * K <= 32768 gives at most 48 pairs per wave)
+using GemvX1Fn = void (*)(const _Float16*, const uint32_t*, const _Float16*, const _Float16*,
+                          _Float16*, int, int, int);
+template <int BITS, int U>
+GemvX1Fn pick_x1_loads(int xl) {
+    if (xl <= 1) return k_gemv_x1<BITS, kGemvWaves, U, 1>;
+    if (xl <= 2) return k_gemv_x1<BITS, kGemvWaves, U, 2>;
+    if (xl <= 4) return k_gemv_x1<BITS, kGemvWaves, U, 4>;
+    if (xl <= 8) return k_gemv_x1<BITS, kGemvWaves, U, 8>;
+    return k_gemv_x1<BITS, kGemvWaves, U, 12>;
+}
+template <int BITS>
+GemvX1Fn pick_x1(bool short_rows, int xl) {
+    return short_rows ? pick_x1_loads<BITS, kGemvRingShort>(xl) : pick_x1_loads<BITS, kGemvRingLong>(xl);
 }
 
 template <int BITS>
@@ -466,8 +493,8 @@ int launch_bits(const void* x, const void* qweight, const void* scales, const vo
     const size_t tiles = (size_t)NB * G;
     const bool ring = SG == G && tiles * 64 * WQ * 4 < ((size_t)1 << 31);
     const size_t lds = gemv_lds_bytes(M, SG, kGemvWaves);
-    auto kern1 = G <= 4 * kGemvWaves ? k_gemv_x1<BITS, kGemvWaves, kGemvRingShort>
-                                     : k_gemv_x1<BITS, kGemvWaves, kGemvRingLong>;
+    auto kern1 = pick_x1<BITS>(G <= 4 * kGemvWaves,
+                               ((G + kGemvWaves - 1) / kGemvWaves * M + 3) / 4);   // x loads per lane
     auto kern = k_gemv<BITS, kGemvWaves, kGemvUnroll>;
     if (lds > 64 * 1024) {
         const void* f = ring ? reinterpret_cast<const void*>(kern1) : reinterpret_cast<const void*>(kern);
