@@ -218,6 +218,7 @@ def main(argv=None):
         with torch.cuda.stream(stream):
             W = torch.from_numpy(wl4.weights(i)).to(dev)
             qw, sc, ze = awq.quantize_pack(W, None, bits=4)
+            Wt = W.t().contiguous()                    # [K][N]: dense fp16 reference operand
             del W
             x = torch.from_numpy(wl4.activations(M, i)).to(dev)
             y = torch.empty((M, N), dtype=torch.float16, device=dev)
@@ -233,12 +234,26 @@ def main(argv=None):
         ms = a.elapsed_time(b) / args.gemm_iters
         flops = 2.0 * M * N * K
         tf = flops / (ms * 1e-3) / 1e12
+        # context, not the metric: the same product with dense fp16 weights
+        # through torch.matmul (hipBLASLt), i.e. what the vendor library reaches
+        # on this GPU for this shape without any dequantization
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                ref = torch.matmul(x, Wt)
+            a.record(stream)
+            for _ in range(args.gemm_iters):
+                ref = torch.matmul(x, Wt)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ref_tf = flops / (a.elapsed_time(b) / args.gemm_iters * 1e-3) / 1e12
         gemm_res[f"{K}x{N}"] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
-                                "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+                                "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                                "dense_fp16_hipblaslt_TFLOPs": round(ref_tf, 1)}
         tot_flops += flops
         tot_ms += ms
-        log(f"  gemm M={M} K={K} N={N}: {ms * 1e3:.1f} us, {tf:.1f} TFLOP/s")
-        del qw, sc, ze, x, y
+        log(f"  gemm M={M} K={K} N={N}: {ms * 1e3:.1f} us, {tf:.1f} TFLOP/s "
+            f"(dense fp16 torch.matmul {ref_tf:.1f})")
+        del qw, sc, ze, x, y, Wt, ref
     gemm_tflops = tot_flops / (tot_ms * 1e-3) / 1e12
 
     # ------------------------------------------------------------------ offline path
@@ -308,7 +323,8 @@ def main(argv=None):
                  "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1),
                               "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                              "traffic": None, "kernel": "k_gemm_w4"}},
+                              "traffic": None,
+                              "kernel": "k_gemm_w4p<4> (<= 256 tiles: 14336x4096), k_gemm_w4 (more)"}},
         "offline": offline,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count,

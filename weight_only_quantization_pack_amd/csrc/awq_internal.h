@@ -101,6 +101,9 @@ int launch_quantize_pack(const void* W, const float* s, int N, int K, int bits,
                          void* qweight, void* scales, void* zeros, hipStream_t st);
 int launch_scale_activations(const void* x, const float* s, void* x_out, int M, int K,
                              hipStream_t st);
+// compute units of the current device
+int device_cu_count();
+
 int launch_gemv(const void* x, const void* qweight, const void* scales, const void* zeros,
                 void* y, int M, int N, int K, int bits, hipStream_t st);
 int launch_gemm(const void* x, const void* qweight, const void* scales, const void* zeros,

@@ -23,6 +23,13 @@
 // MFMAs.  Tiles are mapped so that each XCD (workgroup id mod 8) walks a
 // contiguous run of row-major tiles and keeps its A rows in its L2.
 //
+// Two schedules of that tile: k_gemm_w4 double-buffers A and B (one K-step
+// ahead) at two workgroups per CU; k_gemm_w4p keeps three K-steps in flight
+// (four 32 KB A buffers, four B register slots) at one workgroup per CU, with
+// the next k32 substep's A fragments and B operands prepared under the
+// current substep's MFMAs.  The launcher takes k_gemm_w4p while the tiles fit
+// on the CUs in one round and k_gemm_w4 otherwise.
+//
 // Loss GEMM (k_gemm_loss): B = D_alpha = W - w_hat_alpha / s_alpha (fp16,
 // row-major), 128 x 128 tiles through LDS, and the epilogue sums Y^2 per tile
 // instead of storing Y.
@@ -200,6 +207,10 @@ __global__ __launch_bounds__(256) void k_gemm_lds(
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void global_void_t;
 
+// s_waitcnt immediate (gfx9): wait until at most n vector-memory ops are
+// outstanding, no wait on lgkm/exp counters
+constexpr unsigned vmcnt_imm(unsigned n) { return (n & 15u) | ((n >> 4) << 14) | (7u << 4) | (15u << 8); }
+
 namespace w4 {
 constexpr int GM = 128, GN = 256, GK = 128;    // workgroup tile; GK = one group
 constexpr int ROW_BYTES = GK * 2;              // one A row of a K-step in LDS
@@ -373,6 +384,186 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(
     }
 }
 
+// S-stage pipeline: A tiles of K-steps kt+1 .. kt+S-1 are in flight to LDS
+// (S buffers of 32 KB) and the matching B tiles and parameters to registers
+// (S slots) while step kt is computed, so a K-step's MFMA work (128 per
+// wave) need not cover a full memory latency.  The K loop is unrolled by S so
+// that every register slot and LDS buffer index is static; steps past the
+// last group (the last round runs whole) re-load group G - 1 (valid
+// addresses, never consumed), which keeps the load stream the same every step: 20 loads per step and wave
+// (8 A direct-to-LDS, 4 B tiles, 4 scale words, 4 zero words).
+template <int S>
+__global__ __launch_bounds__(256, 1) void k_gemm_w4p(
+    const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
+    const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
+    _Float16* __restrict__ Y, int M, int N, int K) {
+    using namespace w4;
+    extern __shared__ __attribute__((aligned(16))) unsigned char As[];   // S x ABUF
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15, hq = lane >> 4;
+    const int G = K / kGroup;
+    const int NB = (N + 15) / 16;
+    const int nTn = (N + GN - 1) / GN, nTm = (M + GM - 1) / GM;
+    const int nT = nTn * nTm;
+    int t = blockIdx.x;
+    if (nT % 8 == 0) t = (t % 8) * (nT / 8) + t / 8;
+    const int m0 = (t / nTn) * GM, n0 = (t % nTn) * GN;
+
+    uint32_t a_off[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int rg = wave * 8 + i;
+        const int r = 4 * rg + (lane >> 4);
+        const int kc = (lane & 15) ^ (r & 15);
+        const int grow = min(m0 + r, M - 1);
+        a_off[i] = (uint32_t)grow * (uint32_t)K + 8u * kc;
+    }
+    uint32_t tbase[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int blk = min(n0 / 16 + wave * 4 + c, NB - 1);
+        tbase[c] = (uint32_t)blk * (uint32_t)G;
+    }
+    const uint32_t psh = 16u * (uint32_t)(j & 1);      // the lane's half of a parameter word
+
+    struct BStage { uint4 q[4]; uint32_t d[4], z[4]; };
+    // part p (0..3) of step kt's loads: A rows groups 2p, 2p + 1 (direct to LDS
+    // buffer `slot`), B tile p of this wave and its scale and zero words
+    auto issue_part = [&](int kt, int slot, BStage& bs, int p) {
+        const uint32_t g = (uint32_t)min(kt, G - 1);
+#pragma unroll
+        for (int i = 2 * p; i < 2 * p + 2; ++i) {
+            const int rg = wave * 8 + i;
+            __builtin_amdgcn_global_load_lds((global_void_t*)(x + a_off[i] + g * GK),
+                                             (lds_void_t*)(As + slot * ABUF + rg * 1024), 16, 0, 0);
+        }
+        const uint32_t tt = tbase[p] + g;
+        bs.q[p] = *reinterpret_cast<const uint4*>(qw + (size_t)(tt * 256u + 4u * lane));
+        bs.d[p] = *reinterpret_cast<const uint32_t*>(scales + tt * 16u + (uint32_t)(j & ~1));
+        bs.z[p] = *reinterpret_cast<const uint32_t*>(zeros + tt * 16u + (uint32_t)(j & ~1));
+    };
+    auto issue = [&](int kt, int slot, BStage& bs) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) issue_part(kt, slot, bs, p);
+    };
+
+    float4_t acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[i][c] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+    // One K-step: four k32 substeps of 32 MFMAs.  The A fragments (8 LDS reads)
+    // and B operands (4 dequantized words) of substep s + 1 are produced while
+    // the MFMAs of substep s run, so that neither LDS latency nor the
+    // dequantization sits between two MFMA groups.
+    auto compute = [&](const BStage& bs, const unsigned char* abuf) {
+        half2_t zz[4], zz16[4], dd[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const _Float16 z = __builtin_bit_cast(_Float16, (unsigned short)(bs.z[c] >> psh));
+            const _Float16 d = __builtin_bit_cast(_Float16, (unsigned short)(bs.d[c] >> psh));
+            const _Float16 zb = (_Float16)1024.0f + z, zb16 = (_Float16)64.0f + z;
+            zz[c] = (half2_t){zb, zb};
+            zz16[c] = (half2_t){zb16, zb16};
+            dd[c] = (half2_t){d, d};
+        }
+        auto read_a = [&](int s, half8_t* a) {
+            const int kc = 4 * hq + s;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r = 16 * i + j;
+                a[i] = *reinterpret_cast<const half8_t*>(abuf + r * ROW_BYTES + ((kc ^ (r & 15)) << 4));
+            }
+        };
+        auto dequant = [&](int s, half8_t* b) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t w = s == 0 ? bs.q[c].x : s == 1 ? bs.q[c].y : s == 2 ? bs.q[c].z : bs.q[c].w;
+                b[c] = dequant_scaled(w, zz[c], zz16[c], dd[c]);
+            }
+        };
+        half8_t a_cur[8], b_cur[4];
+        read_a(0, a_cur);
+        dequant(0, b_cur);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            half8_t a_nxt[8], b_nxt[4];
+            if (s < 3) {
+                read_a(s + 1, a_nxt);
+                dequant(s + 1, b_nxt);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b_cur[c], a_cur[i], acc[i][c], 0, 0, 0);
+            if (s < 3) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) a_cur[i] = a_nxt[i];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) b_cur[c] = b_nxt[c];
+            }
+        }
+    };
+
+    // the loads of every step are issued as one unit in the same order, in the
+    // prologue as in the loop, so that the compiler's per-register wait counts
+    // agree on loop entry and along the back edge
+    BStage bs[S];
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(s, s, bs[s]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // G >= 1; a loop without an entry test keeps the compiler from sinking the
+    // prologue's register loads behind one (out of the order above)
+    int kt0 = 0;
+    do {
+#pragma unroll
+        for (int st = 0; st < S; ++st) {
+            const int kt = kt0 + st;
+            // step kt has landed once at most the S - 2 later steps' loads are outstanding
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(20 * (S - 2)));
+            // every wave's A(kt) is in LDS and its reads of A(kt-1) are done.  A
+            // bare barrier: __syncthreads() is a release fence that would also
+            // drain the later steps' direct-to-LDS loads (vmcnt(0))
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            issue(kt + S - 1, (st + S - 1) % S, bs[(st + S - 1) % S]);
+            __builtin_amdgcn_sched_barrier(0);
+            // the last round may run past G: those steps keep the load stream
+            // (and so the compiler's wait counts) uniform but compute nothing
+            if (kt < G) compute(bs[st], As + st * ABUF);
+        }
+        kt0 += S;
+    } while (kt0 < G);
+
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int m = m0 + 16 * i + j;
+        if (m >= M) continue;
+        _Float16* yrow = Y + (size_t)m * N;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int n = n0 + wave * 64 + 16 * c + 4 * hq;
+            const half2_t lo = {(_Float16)acc[i][c][0], (_Float16)acc[i][c][1]};
+            const half2_t hi = {(_Float16)acc[i][c][2], (_Float16)acc[i][c][3]};
+            if (n + 3 < N && ((N & 3) == 0)) {
+                *reinterpret_cast<uint2*>(yrow + n) = make_uint2(as_u32(lo), as_u32(hi));
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (n + r < N) yrow[n + r] = (_Float16)acc[i][c][r];
+            }
+        }
+    }
+}
+
 }  // namespace
 
 int launch_gemm(const void* x, const void* qweight, const void* scales, const void* zeros,
@@ -381,9 +572,25 @@ int launch_gemm(const void* x, const void* qweight, const void* scales, const vo
     if ((unsigned long long)M * K >= (1ull << 31) || (unsigned long long)N * K / 8 >= (1ull << 31))
         return (int)hipErrorInvalidValue;
     const int nT = ((N + w4::GN - 1) / w4::GN) * ((M + w4::GM - 1) / w4::GM);
-    hipLaunchKernelGGL(k_gemm_w4, dim3(nT), dim3(256), 0, st, (const _Float16*)x,
-                       (const uint32_t*)qweight, (const _Float16*)scales, (const _Float16*)zeros,
-                       (_Float16*)y, M, N, K);
+    // Up to one tile per CU: the 4-stage pipelined kernel (one workgroup per
+    // CU).  More tiles: the double-buffered kernel at two workgroups per CU,
+    // whose 2 x CUs slots round the tile count better (MI355X, M = 2048:
+    // 14336x4096 (256 tiles) 974 vs 743 TFLOP/s; 4096x14336 (896 tiles) 764 vs
+    // 816; 4096x6144 (384 tiles) 739 vs 849).
+    if (nT <= device_cu_count()) {
+        constexpr int S = 4;
+        const size_t lds = (size_t)S * w4::ABUF;
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_w4p<S>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return (int)e;
+        hipLaunchKernelGGL(k_gemm_w4p<S>, dim3(nT), dim3(256), lds, st, (const _Float16*)x,
+                           (const uint32_t*)qweight, (const _Float16*)scales, (const _Float16*)zeros,
+                           (_Float16*)y, M, N, K);
+    } else {
+        hipLaunchKernelGGL(k_gemm_w4, dim3(nT), dim3(256), 0, st, (const _Float16*)x,
+                           (const uint32_t*)qweight, (const _Float16*)scales, (const _Float16*)zeros,
+                           (_Float16*)y, M, N, K);
+    }
     return (int)hipGetLastError();
 }
 

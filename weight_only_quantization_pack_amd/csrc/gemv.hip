@@ -43,6 +43,10 @@ namespace {
 constexpr int kGemvWaves = AWQ_GEMV_WAVES;    // waves per workgroup
 constexpr int kGemvUnroll = AWQ_GEMV_UNROLL;  // tiles per wave per load batch
 constexpr int kGemvXBuf = AWQ_GEMV_XBUF;      // LDS bytes for the staged x slice
+#ifndef AWQ_GEMV_CU_WAVES
+#define AWQ_GEMV_CU_WAVES 16
+#endif
+constexpr int kGemvCuWaves = AWQ_GEMV_CU_WAVES;  // resident waves per CU for persistent grids
 // tiles in flight per wave when x is staged once: 2 while a wave has at most 4
 // tiles per row block (a deeper ring only moves dequantization and MFMA work
 // behind the last byte to land), 4 for longer rows (measured on MI355X:
@@ -446,18 +450,6 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
     } while (b < NB);
 }
 
-int num_cus() {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            cus = v;
-        else
-            cus = 256;
-    }
-    return cus;
-}
 
 // k_gemv_x1 instance: ring depth (short rows: 2, else 4) and the number of
 // 16-byte x loads per lane that stage a wave's (group, row) pairs (<= 12:
@@ -502,12 +494,12 @@ int launch_bits(const void* x, const void* qweight, const void* scales, const vo
         if (e != hipSuccess) return (int)e;
     }
     // persistent workgroups when x is staged once (as many as fit on a CU by
-    // LDS, at most 2 of 8 waves); one row block each otherwise
+    // LDS, at most kGemvCuWaves waves); one row block each otherwise
 #ifndef AWQ_GEMV_PERSIST
 #define AWQ_GEMV_PERSIST 1
 #endif
-    const int per_cu = max(1, min(2, (int)((160 * 1024) / lds)));
-    const int grid = (AWQ_GEMV_PERSIST && SG == G) ? min(NB, num_cus() * per_cu) : NB;
+    const int per_cu = max(1, min(kGemvCuWaves / kGemvWaves, (int)((160 * 1024) / lds)));
+    const int grid = (AWQ_GEMV_PERSIST && SG == G) ? min(NB, device_cu_count() * per_cu) : NB;
     if (ring)
         hipLaunchKernelGGL(kern1, dim3(grid), dim3(64 * kGemvWaves), lds, st,
                            (const _Float16*)x, (const uint32_t*)qweight, (const _Float16*)scales,
@@ -520,6 +512,15 @@ int launch_bits(const void* x, const void* qweight, const void* scales, const vo
 }
 
 }  // namespace
+
+int device_cu_count() {
+    // per call (the runtime caches device attributes), for the current device
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+        return v;
+    return 256;
+}
 
 int launch_gemv(const void* x, const void* qweight, const void* scales, const void* zeros,
                 void* y, int M, int N, int K, int bits, hipStream_t st) {
