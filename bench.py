@@ -209,6 +209,59 @@ def main(argv=None):
         log(f"  gemv K={K} N={N}: {us:.2f} us, {gbs:.1f} GB/s")
         del g
 
+    del reps, packed
+    torch.cuda.empty_cache()
+
+    # --------------------------------------------- batched decode (context, not the metric)
+    # Llama-70B MLP shapes at M = 1, 4, 16 (awq_gemv) and 64 (awq_gemm): the
+    # bandwidth -> compute crossover, cold weights as above
+    wl3 = WL.workload(3)
+    batched = {}
+    for i, (K, N) in enumerate(wl3.shapes):
+        with torch.cuda.stream(stream):
+            W = torch.from_numpy(wl3.weights(i)).to(dev)
+            base = awq.quantize_pack(W, None, bits=4)
+            del W
+        wb = N * K // 2 + 4 * N * (K // 128)
+        R3 = max(2, math.ceil(COLD_BYTES / wb))
+        reps3 = [tuple(t.clone() for t in base) for _ in range(R3)]
+        del base
+        res = {}
+        for M in (1, 4, 16, 64):
+            fn = awq.gemv if M <= 16 else awq.gemm
+            x = torch.from_numpy(wl3.activations(M, i)).to(dev)
+            y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            with torch.cuda.stream(stream):
+                for r in range(R3):
+                    fn(x, *reps3[r], N=N, bits=4, out=y)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for r in range(R3):
+                    fn(x, *reps3[r], N=N, bits=4, out=y)
+            with torch.cuda.stream(stream):
+                for _ in range(2):
+                    g.replay()
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                n_rep = max(2, 100 // R3)
+                a.record(stream)
+                for _ in range(n_rep):
+                    g.replay()
+                b.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / (n_rep * R3)
+            gbs = gemv_bytes(M, N, K) / (us * 1e-6) / 1e9
+            res[f"M{M}"] = {"us": round(us, 2), "GBps": round(gbs, 1),
+                            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                            "TFLOPs": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 1),
+                            "entry": "awq_gemv" if M <= 16 else "awq_gemm"}
+            log(f"  batched decode K={K} N={N} M={M}: {us:.2f} us, {gbs:.1f} GB/s")
+            del g, x, y
+        batched[f"{K}x{N}"] = res
+        del reps3
+        torch.cuda.empty_cache()
+
     # ------------------------------------------------------------------ prefill GEMM
     wl4 = WL.workload(4)
     M = 2048
@@ -319,6 +372,7 @@ def main(argv=None):
                      "algorithmic_bytes_per_launch": round(step_bytes / len(layer)),
                      "kernel": "k_gemv_x1<4,8,U> (ring U=2 for K=4096, U=4 for K=11008)", "avg_launch_us": round(avg_launch_us, 3)},
         "gemv_per_shape": per_shape,
+        "batched_decode_llama70b_mlp": batched,
         "gemm": {"M": M, "TFLOPs": round(gemm_tflops, 1), "per_shape": gemm_res,
                  "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1),
                               "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",

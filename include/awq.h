@@ -154,7 +154,9 @@ int awq_search_scale(const void* W, const void* X_cal, int T, int N, int K,
  *   y[m][n] = sum_g D[n][g] * sum_{k in g} x[m][k] * (q[n][k] - z[n][g])
  *   x fp16 [M][K] in; qweight, scales, zeros as produced by
  *   awq_quantize_pack; y fp16 [M][N] out (round to nearest from fp32).
- *   1 <= M <= 16; bits in {3, 4}; group_size 128.
+ *   1 <= M <= 16; bits in {3, 4}; group_size 128.  The packed weight must
+ *   be < 2^31 bytes (16 * ceil(N/16) * K * bits / 8) and x < 2^31 bytes
+ *   (M * K * 2), else AWQ_ERR_SHAPE.
  */
 int awq_gemv(const void* x, const void* qweight, const void* scales,
              const void* zeros, void* y, int M, int N, int K, int bits,

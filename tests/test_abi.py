@@ -116,6 +116,10 @@ def test_gemv_and_gemm_specific_limits(lib):
     assert mm(lib, "awq_gemm", bits=3) == UNSUP
     assert mm(lib, "awq_gemv", M=17, bits=3, x=NUL) == UNSUP
     assert mm(lib, "awq_gemm", M=1 << 20, K=4096) == SHAPE      # 32-bit offset limit
+    # decode: packed weight >= 2^31 bytes (int4: N*K >= 2^32) or x >= 2^31 bytes
+    assert mm(lib, "awq_gemv", M=1, N=1 << 16, K=1 << 16) == SHAPE
+    assert mm(lib, "awq_gemv", M=1, N=1 << 16, K=(1 << 16) - 128, x=NUL) == NULL   # just below: passes
+    assert mm(lib, "awq_gemv", M=16, N=16, K=1 << 26) == SHAPE
 
 
 def test_scale_activations_validation(lib):

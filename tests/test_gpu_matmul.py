@@ -92,6 +92,16 @@ def test_gemv_workload3_sampled(gpu, M, shape_index):
           x=wl.activations(M, shape_index), rows=rows)
 
 
+@pytest.mark.parametrize("M", [5, 16])
+def test_gemv_sliced_two_blocks_per_workgroup(gpu, M):
+    """x too large to stage at once (K sliced) with 1019 row blocks over at most
+    512 persistent workgroups: each owns two blocks, some only one valid."""
+    N, K = 16300, 4096
+    rng = np.random.default_rng(M)
+    rows = np.concatenate([[0, 15, 16, N - 1], rng.choice(N, 60, replace=False)])
+    check("gemv", M, N, K, 4, seed=31 + M, rows=rows)
+
+
 # ----------------------------------------------------------------------------- GEMM
 @pytest.mark.parametrize("M", [1, 5, 64, 128, 130, 257])
 @pytest.mark.parametrize("N,K", [(512, 512), (37, 384), (200, 1152)])

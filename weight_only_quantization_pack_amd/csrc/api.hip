@@ -120,6 +120,10 @@ int awq_gemv(const void* x, const void* qweight, const void* scales, const void*
     if (M > kMaxGemvM) return AWQ_ERR_UNSUPPORTED;
     if (M < 0) return AWQ_ERR_SHAPE;
     if ((st = check_nk(N, K))) return st;
+    // the decode kernels address x and the packed tiles with 32-bit offsets
+    if ((long long)M * K * 2 >= (1LL << 31) ||
+        16LL * ((N + 15) / 16) * K / 8 * bits >= (1LL << 31))
+        return AWQ_ERR_SHAPE;
     if (M == 0 || N == 0) return AWQ_OK;
     if ((st = check_ptrs({x, qweight, scales, zeros, y}))) return st;
     return hip_status(awq::launch_gemv(x, qweight, scales, zeros, y, M, N, K, bits,

@@ -10,15 +10,16 @@
 // Work split.  Packed format 2 stores tile (b, g) = 16 rows x group g as 64
 // lane slots of 16 bytes (slot s = 16h + j: row j, quarter h), contiguous
 // along g, with the 16 scales and zeros of the tile in [b][g][16] order.
-// A workgroup of WK waves owns one row block at a time and loops over row
-// blocks blockIdx.x, +gridDim.x, ... (the grid is sized to the machine).
-// Its waves take the groups round-robin, so each step of the workgroup reads
-// WK consecutive tiles and the block's slab is swept front to back.  When x
-// fits in LDS (k_gemv_x1, the decode case) it is staged once per workgroup and
-// each wave streams its tiles (1 KB wave load each, plus the tile's scales and
-// zeros) through a ring of U register slots with a fixed-order load stream,
-// so U tiles stay in flight across row blocks.  Otherwise (k_gemv) x is
-// staged one K-slice at a time and each wave double-buffers U tiles.
+// Persistent workgroups of WK waves own row blocks blockIdx.x, +gridDim.x,
+// ... (the grid is sized to the machine).  Their waves take the groups
+// round-robin, so each step of a workgroup reads WK consecutive tiles and a
+// block's slab is swept front to back.  Each wave streams its tiles (1 KB
+// wave load each, plus the tile's scales and zeros) through a ring of U
+// register slots with a fixed-order load stream, so U tiles stay in flight,
+// and stages in LDS only the x columns of its own groups.  k_gemv_x1 (x fits
+// in LDS, the decode case) stages x once and walks its blocks one after the
+// other; k_gemv_xs (larger M * K) sweeps K in slices and keeps one
+// accumulator per owned block across the slices.
 //
 // Dequantization is exact: OR 0x6400 turns a 4-bit code q into the fp16
 // value 1024 + q and subtracting 1024 + z leaves q - z, so each group's
@@ -34,15 +35,11 @@ namespace {
 #ifndef AWQ_GEMV_WAVES
 #define AWQ_GEMV_WAVES 8
 #endif
-#ifndef AWQ_GEMV_UNROLL
-#define AWQ_GEMV_UNROLL 2
-#endif
 #ifndef AWQ_GEMV_XBUF
 #define AWQ_GEMV_XBUF 65536
 #endif
 constexpr int kGemvWaves = AWQ_GEMV_WAVES;    // waves per workgroup
-constexpr int kGemvUnroll = AWQ_GEMV_UNROLL;  // tiles per wave per load batch
-constexpr int kGemvXBuf = AWQ_GEMV_XBUF;      // LDS bytes for the staged x slice
+constexpr int kGemvXBuf = AWQ_GEMV_XBUF;      // LDS bytes for x staged once (k_gemv_x1)
 #ifndef AWQ_GEMV_CU_WAVES
 #define AWQ_GEMV_CU_WAVES 16
 #endif
@@ -105,164 +102,6 @@ __device__ __forceinline__ Slot<WQ> load_slot(const uint32_t* p) {
 
 struct Params { _Float16 d, z; };
 
-size_t gemv_lds_bytes(int M, int SG, int WK) {
-    return (((size_t)M * (SG * kGroup + 8) * 2 + 15) & ~(size_t)15) + 2 * (size_t)WK * 64 * 16;
-}
-
-template <int BITS, int WK, int U>
-__global__ __launch_bounds__(64 * WK) void k_gemv(
-    const _Float16* __restrict__ x, const uint32_t* __restrict__ qweight,
-    const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
-    _Float16* __restrict__ y, int M, int N, int K, int SG) {
-    constexpr int WQ = BITS == 4 ? 4 : 3;              // words per lane slot
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    const int G = K / kGroup;
-    const int NB = (N + 15) / 16;
-    const int XS = SG * kGroup + 8;                    // halves per staged x row
-    _Float16* xs = reinterpret_cast<_Float16*>(smem);
-    float4_t* red = reinterpret_cast<float4_t*>(smem + (((size_t)M * XS * 2 + 15) & ~(size_t)15));
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int j = lane & 15, h = lane >> 4;
-    const bool one_slice = SG >= G;
-    // this wave's groups of a block: g = wave + WK * i, i < nw
-    const int nw = wave < G ? (G - wave + WK - 1) / WK : 0;
-    // index bound of the slice holding batch index i: with several slices SG is
-    // a multiple of WK, so slice [s0, s0 + SG) holds i in [s0 / WK, (s0 + SG) / WK)
-    auto slice_end = [&](int i) { return one_slice ? nw : min(nw, (i * WK / SG + 1) * SG / WK); };
-
-    auto load = [&](int b, int i0, int cnt, Slot<WQ>* w, Params* p) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (u < cnt) {
-                const size_t t = (size_t)b * G + wave + WK * (i0 + u);   // tile index
-                w[u] = load_slot<WQ>(qweight + (t * 64 + lane) * WQ);
-                p[u].d = scales[t * 16 + j];
-                p[u].z = zeros[t * 16 + j];
-            }
-        }
-    };
-    auto stage_x = [&](int s0) {
-        const int sg = min(SG, G - s0);
-        const int c8 = sg * (kGroup / 8);                          // uint4 per staged row
-        for (int idx = tid; idx < M * c8; idx += 64 * WK) {
-            const int m = idx / c8, c = idx % c8;
-            *reinterpret_cast<uint4*>(xs + (size_t)m * XS + 8 * c) =
-                *reinterpret_cast<const uint4*>(x + (size_t)m * K + (size_t)s0 * kGroup + 8 * c);
-        }
-    };
-
-    int b = blockIdx.x;
-    Slot<WQ> cur[U];
-    Params pc[U];
-    int i_cur = 0, n_cur = min(U, slice_end(0));
-    if (b < NB) load(b, 0, n_cur, cur, pc);
-    if (one_slice) {
-        stage_x(0);
-        __syncthreads();
-    }
-    int buf = 0;
-    for (; b < NB; b += gridDim.x) {
-        float4_t acc = {0.f, 0.f, 0.f, 0.f};
-        int staged = -1;
-        while (true) {
-            if (!one_slice) {
-                // every wave walks the slices in step; stage the slice of the current batch
-                const int s_here = n_cur > 0 ? (wave + WK * i_cur) / SG * SG : -1;
-                // each wave stages every slice exactly once, in order, so all
-                // waves meet the same sequence of barriers
-                for (int s0 = staged < 0 ? 0 : staged + SG; s0 <= s_here && s0 < G; s0 += SG) {
-                    __syncthreads();
-                    stage_x(s0);
-                    __syncthreads();
-                    staged = s0;
-                }
-            }
-            if (n_cur <= 0) break;
-            // descriptor of the next batch (may be in the next slice or block)
-            int nb_b = b, nb_i = i_cur + n_cur;
-            int nb_n = nb_i < nw ? min(U, slice_end(nb_i) - nb_i) : 0;
-            if (nb_n <= 0) {
-                nb_b = b + gridDim.x;
-                nb_i = 0;
-                nb_n = nb_b < NB ? min(U, slice_end(0)) : 0;
-            }
-            Slot<WQ> nxt[U];
-            Params pn[U];
-            if (nb_n > 0) load(nb_b, nb_i, nb_n, nxt, pn);
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (u >= n_cur) break;                                   // wave-uniform
-                const int g = wave + WK * (i_cur + u);
-                const int gl = one_slice ? g : g % SG;                   // group within the staged slice
-                const _Float16 zb = (_Float16)1024.0f + pc[u].z;
-                const _Float16 zb16 = (_Float16)64.0f + pc[u].z;
-                const half2_t zz = {zb, zb}, zz16 = {zb16, zb16};
-                half8_t bop[4];
-                if constexpr (BITS == 4) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) bop[i] = dequant_word_int4(cur[u].w[i], zz, zz16);
-                } else {
-                    // 96-bit stream of 32 codes; operand i takes stream bits 24i..24i+23
-                    const uint32_t w0 = cur[u].w[0], w1 = cur[u].w[1], w2 = cur[u].w[2];
-                    bop[0] = dequant_24_int3(w0 & 0xFFFFFFu, zz);
-                    bop[1] = dequant_24_int3((w0 >> 24) | ((w1 & 0xFFFFu) << 8), zz);
-                    bop[2] = dequant_24_int3((w1 >> 16) | ((w2 & 0xFFu) << 16), zz);
-                    bop[3] = dequant_24_int3(w2 >> 8, zz);
-                }
-                float4_t accg = {0.f, 0.f, 0.f, 0.f};
-                // rows j >= M of the A operand are zero; their address is clamped to
-                // row 0 so that no LDS read leaves the staged rows
-                const _Float16* xa = xs + (size_t)(j < M ? j : 0) * XS + gl * kGroup + 32 * h;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const half8_t a = j < M ? *reinterpret_cast<const half8_t*>(xa + 8 * i)
-                                            : (half8_t){0, 0, 0, 0, 0, 0, 0, 0};
-                    accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bop[i], accg, 0, 0, 0);
-                }
-                const float d = (float)pc[u].d;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(d, accg[r], acc[r]);
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) { cur[u] = nxt[u]; pc[u] = pn[u]; }
-            const bool next_block = nb_b != b;
-            i_cur = nb_i;
-            n_cur = nb_n;
-            if (next_block) break;
-        }
-        if (!one_slice) {
-            // waves whose groups ended early still pass every staging barrier
-            for (int s0 = staged < 0 ? 0 : staged + SG; s0 < G; s0 += SG) {
-                __syncthreads();
-                stage_x(s0);
-                __syncthreads();
-            }
-        }
-        red[(buf * WK + wave) * 64 + lane] = acc;
-        __syncthreads();
-        if (wave == 0) {
-            float4_t sum = red[(buf * WK) * 64 + lane];
-#pragma unroll
-            for (int w = 1; w < WK; ++w) {
-                const float4_t o = red[(buf * WK + w) * 64 + lane];
-                sum[0] += o[0]; sum[1] += o[1]; sum[2] += o[2]; sum[3] += o[3];
-            }
-            // accumulator layout: lane 16h + j holds rows m = 4h + r of column j
-            const int n = 16 * b + j;
-            if (n < N) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = 4 * h + r;
-                    if (m < M) y[(size_t)m * N + n] = (_Float16)sum[r];
-                }
-            }
-        }
-        buf ^= 1;
-    }
-}
-
 // x staged once per workgroup (all of x fits in LDS): the common decode case.
 //
 // Each wave streams its tiles through a ring of U register slots: slot u holds
@@ -309,6 +148,39 @@ struct RawParams { uint32_t d, z; };
 
 __device__ __forceinline__ _Float16 low_half(uint32_t v) {
     return __builtin_bit_cast(_Float16, (unsigned short)v);
+}
+
+// acc += D * sum_k x[j][k] * (q[k] - z) over one tile: the four k32 MFMAs of
+// a group with x (rows j >= M read row 0) as the A operand from LDS at xa and
+// the slot's exact (q - z) as the B operand; the group scale multiplies the
+// accumulator lanes of the lane's row.
+template <int BITS, int WQ>
+__device__ __forceinline__ void accumulate_tile(const Slot<WQ>& w, const RawParams& p, const _Float16* xa,
+                                                uint32_t psh, float4_t& acc) {
+    const _Float16 zh = low_half(p.z >> psh);
+    const _Float16 zb = (_Float16)1024.0f + zh;
+    const _Float16 zb16 = (_Float16)64.0f + zh;
+    const half2_t zz = {zb, zb}, zz16 = {zb16, zb16};
+    half8_t bop[4];
+    if constexpr (BITS == 4) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bop[q] = dequant_word_int4(w.w[q], zz, zz16);
+    } else {
+        // 96-bit stream of 32 codes; operand q takes stream bits 24q..24q+23
+        const uint32_t w0 = w.w[0], w1 = w.w[1], w2 = w.w[2];
+        bop[0] = dequant_24_int3(w0 & 0xFFFFFFu, zz);
+        bop[1] = dequant_24_int3((w0 >> 24) | ((w1 & 0xFFFFu) << 8), zz);
+        bop[2] = dequant_24_int3((w1 >> 16) | ((w2 & 0xFFu) << 16), zz);
+        bop[3] = dequant_24_int3(w2 >> 8, zz);
+    }
+    float4_t accg = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const half8_t*>(xa + 8 * q), bop[q],
+                                                      accg, 0, 0, 0);
+    const float d = (float)low_half(p.d >> psh);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(d, accg[r], acc[r]);
 }
 
 template <int BITS, int WK, int U, int XL>
@@ -395,32 +267,8 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int i = i0 + u;
-                if (i < nw) {                          // wave-uniform; loads stay outside
-                    const _Float16 zh = low_half(pr[u].z >> psh);
-                    const _Float16 zb = (_Float16)1024.0f + zh;
-                    const _Float16 zb16 = (_Float16)64.0f + zh;
-                    const half2_t zz = {zb, zb}, zz16 = {zb16, zb16};
-                    half8_t bop[4];
-                    if constexpr (BITS == 4) {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) bop[q] = dequant_word_int4(ring[u].w[q], zz, zz16);
-                    } else {
-                        const uint32_t w0 = ring[u].w[0], w1 = ring[u].w[1], w2 = ring[u].w[2];
-                        bop[0] = dequant_24_int3(w0 & 0xFFFFFFu, zz);
-                        bop[1] = dequant_24_int3((w0 >> 24) | ((w1 & 0xFFFFu) << 8), zz);
-                        bop[2] = dequant_24_int3((w1 >> 16) | ((w2 & 0xFFu) << 16), zz);
-                        bop[3] = dequant_24_int3(w2 >> 8, zz);
-                    }
-                    const _Float16* xa = xa0 + (size_t)(wave + WK * i) * kGroup;
-                    float4_t accg = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            *reinterpret_cast<const half8_t*>(xa + 8 * q), bop[q], accg, 0, 0, 0);
-                    const float d = (float)low_half(pr[u].d >> psh);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(d, accg[r], acc[r]);
-                }
+                if (i < nw)                            // wave-uniform; loads stay outside
+                    accumulate_tile<BITS, WQ>(ring[u], pr[u], xa0 + (size_t)(wave + WK * i) * kGroup, psh, acc);
                 // refill the slot with the item U places on (this block or the next)
                 const int k = i + U;
                 const bool here = k < nwp;
@@ -451,11 +299,165 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
 }
 
 
+using GemvX1FnT = void (*)(const _Float16*, const uint32_t*, const _Float16*, const _Float16*,
+                           _Float16*, int, int, int);
+using GemvX1Fn = GemvX1FnT;
+
+// x too large for LDS at once (M rows, M * K > 32K halves): K is swept in
+// slices of SG = WK * U groups, x staged one slice at a time, each wave
+// staging only its own U groups' columns (no workgroup barrier).  A
+// persistent workgroup owns up to BMAX row blocks (blockIdx.x + k gridDim.x)
+// and keeps one accumulator per block across all slices, so every staged x
+// slice serves all of them.  Per slice and block each wave has exactly U
+// items, one ring round: the slice body is fully unrolled and its load
+// stream fixed (items past G or past the last block are out-of-range loads),
+// so the compiler's waits cover exactly one ring slot; the next slice's x is
+// loaded into registers during the current slice, ahead of its ring loads.
+// The waves' partial sums meet in LDS once per block at the end.
+template <int BITS, int WK, int U, int BMAX, int XL>
+__global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_xs(
+    const _Float16* __restrict__ x, const uint32_t* __restrict__ qweight,
+    const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
+    _Float16* __restrict__ y, int M, int N, int K) {
+    constexpr int WQ = BITS == 4 ? 4 : 3;
+    constexpr int SG = WK * U;                         // groups per slice
+    constexpr int XS = SG * kGroup + 8;                // halves per staged x row
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    _Float16* xs = reinterpret_cast<_Float16*>(smem);
+    float4_t* red = reinterpret_cast<float4_t*>(smem);   // after the sweep, over x
+    const int G = K / kGroup;
+    const int NB = (N + 15) / 16;
+    const int NS = (G + SG - 1) / SG;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int j = lane & 15, h = lane >> 4;
+    const _Float16* xa0 = xs + (size_t)(j < M ? j : 0) * XS + 32 * h;
+    const uint32_t psh = 16u * (uint32_t)(j & 1);
+
+    const uint32_t tiles = (uint32_t)NB * (uint32_t)G;
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(qweight, tiles * 64u * WQ * 4u);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scales, tiles * 32u);
+    const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(zeros, tiles * 32u);
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+
+    // item (s, k, u): block blockIdx.x + k gridDim.x, group s SG + wave + WK u
+    auto load = [&](int s, int k, int u, Slot<WQ>& w, RawParams& p) {
+        const int b = blockIdx.x + k * gridDim.x;
+        const int g = s * SG + wave + WK * u;
+        const bool ok = b < NB && g < G;
+        const uint32_t t = (uint32_t)b * (uint32_t)G + (uint32_t)g;
+        const uint32_t oq = ok ? (t * 64u + (uint32_t)lane) * (WQ * 4u) : kBufferOutOfRange;
+        const uint32_t op = ok ? (t * 16u + (uint32_t)(j & ~1)) * 2u : kBufferOutOfRange;
+        w = buffer_slot<WQ>(rq, oq);
+        p.d = __builtin_amdgcn_raw_buffer_load_b32(rs, op, 0, 0);
+        p.z = __builtin_amdgcn_raw_buffer_load_b32(rz, op, 0, 0);
+    };
+    // the wave's x of slice s: (group u, row m) pairs q = (lane >> 4) + 4p as
+    // 16-byte chunks; pairs past U * M land in row 0's padding xs[SG*128 ..]
+    const uint32_t mdiv = 65536u / (uint32_t)M + 1u;   // q / M = (q * mdiv) >> 16 for q < 2048, M <= 16
+    auto x_at = [&](int p) -> uint32_t {               // LDS position of chunk p (recomputed: registers)
+        const uint32_t q = (uint32_t)((lane >> 4) + 4 * p);
+        const uint32_t u = (q * mdiv) >> 16, m = q - u * (uint32_t)M;
+        const uint32_t col = (uint32_t)kGroup * (uint32_t)(wave + WK * (int)u) + 8u * (uint32_t)j;
+        return (int)q < U * M ? m * (uint32_t)XS + col : (uint32_t)(SG * kGroup);
+    };
+    auto load_x = [&](int s, uint4* xv) {
+#pragma unroll
+        for (int p = 0; p < XL; ++p) {
+            const uint32_t q = (uint32_t)((lane >> 4) + 4 * p);
+            const uint32_t u = (q * mdiv) >> 16, m = q - u * (uint32_t)M;
+            const int g = s * SG + wave + WK * (int)u;
+            const bool ok = (int)q < U * M && g < G;
+            const uint32_t off = (m * (uint32_t)K + (uint32_t)kGroup * (uint32_t)g + 8u * (uint32_t)j) * 2u;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? off : kBufferOutOfRange, 0, 0);
+            xv[p] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+    };
+
+    uint4 xv[XL];
+    Slot<WQ> ring[U];
+    RawParams pr[U];
+    load_x(0, xv);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        load(0, 0, u, ring[u], pr[u]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float4_t acc[BMAX];
+#pragma unroll
+    for (int k = 0; k < BMAX; ++k) acc[k] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+    // NS >= 1: no entry test, so the loads above stay where they are
+    int s = 0;
+    do {
+        // stage slice s (this wave's reads of slice s - 1 precede in program order)
+#pragma unroll
+        for (int p = 0; p < XL; ++p) *reinterpret_cast<uint4*>(xs + x_at(p)) = xv[p];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        load_x(s + 1, xv);
+#pragma unroll
+        for (int k = 0; k < BMAX; ++k) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int g = s * SG + wave + WK * u;
+                if (blockIdx.x + k * gridDim.x < NB && g < G)    // wave-uniform
+                    accumulate_tile<BITS, WQ>(ring[u], pr[u], xa0 + (size_t)(wave + WK * u) * kGroup, psh, acc[k]);
+                // refill: the same group of the next block, or of the first block in the next slice
+                if (k + 1 < BMAX)
+                    load(s, k + 1, u, ring[u], pr[u]);
+                else
+                    load(s + 1, 0, u, ring[u], pr[u]);
+            }
+        }
+        ++s;
+    } while (s < NS);
+
+    __syncthreads();                                   // every wave is done with x
+#pragma unroll
+    for (int k = 0; k < BMAX; ++k) {
+        const int buf = k & 1;
+        red[(buf * WK + wave) * 64 + lane] = acc[k];
+        __syncthreads();
+        const int b = blockIdx.x + k * gridDim.x;
+        if (wave == 0 && b < NB) {
+            float4_t sum = red[(buf * WK) * 64 + lane];
+#pragma unroll
+            for (int w = 1; w < WK; ++w) {
+                const float4_t o = red[(buf * WK + w) * 64 + lane];
+                sum[0] += o[0]; sum[1] += o[1]; sum[2] += o[2]; sum[3] += o[3];
+            }
+            const int n = 16 * b + j;
+            if (n < N) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = 4 * h + r;
+                    if (m < M) y[(size_t)m * N + n] = (_Float16)sum[r];
+                }
+            }
+        }
+    }
+}
+
+constexpr int kGemvSliceRing = 2;                      // U of k_gemv_xs: slices of 16 groups
+
+using GemvXsFn = GemvX1FnT;
+template <int BITS, int BMAX>
+GemvXsFn pick_xs_loads(int xl) {
+    if (xl <= 2) return k_gemv_xs<BITS, kGemvWaves, kGemvSliceRing, BMAX, 2>;
+    if (xl <= 4) return k_gemv_xs<BITS, kGemvWaves, kGemvSliceRing, BMAX, 4>;
+    return k_gemv_xs<BITS, kGemvWaves, kGemvSliceRing, BMAX, 8>;
+}
+template <int BITS>
+GemvXsFn pick_xs(int bmax, int xl) {
+    return bmax <= 1 ? pick_xs_loads<BITS, 1>(xl) : pick_xs_loads<BITS, 2>(xl);
+}
+
 // k_gemv_x1 instance: ring depth (short rows: 2, else 4) and the number of
 // 16-byte x loads per lane that stage a wave's (group, row) pairs (<= 12:
 // M * K <= 32768 gives at most 48 pairs per wave)
-using GemvX1Fn = void (*)(const _Float16*, const uint32_t*, const _Float16*, const _Float16*,
-                          _Float16*, int, int, int);
 template <int BITS, int U>
 GemvX1Fn pick_x1_loads(int xl) {
     if (xl <= 1) return k_gemv_x1<BITS, kGemvWaves, U, 1>;
@@ -474,40 +476,47 @@ int launch_bits(const void* x, const void* qweight, const void* scales, const vo
                 void* y, int M, int N, int K, hipStream_t st) {
     const int G = K / kGroup;
     const int NB = (N + 15) / 16;
-    int SG = kGemvXBuf / (M * kGroup * 2);
-    if (SG >= G) {
-        SG = G;                                        // x staged once
-    } else {
-        SG = max(kGemvWaves, SG / kGemvWaves * kGemvWaves);
-    }
-    // the ring kernel addresses its buffers with 32-bit offsets (< 2^31 bytes)
     constexpr size_t WQ = BITS == 4 ? 4 : 3;
-    const size_t tiles = (size_t)NB * G;
-    const bool ring = SG == G && tiles * 64 * WQ * 4 < ((size_t)1 << 31);
-    const size_t lds = gemv_lds_bytes(M, SG, kGemvWaves);
-    auto kern1 = pick_x1<BITS>(G <= 4 * kGemvWaves,
-                               ((G + kGemvWaves - 1) / kGemvWaves * M + 3) / 4);   // x loads per lane
-    auto kern = k_gemv<BITS, kGemvWaves, kGemvUnroll>;
-    if (lds > 64 * 1024) {
-        const void* f = ring ? reinterpret_cast<const void*>(kern1) : reinterpret_cast<const void*>(kern);
-        const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return (int)e;
-    }
-    // persistent workgroups when x is staged once (as many as fit on a CU by
-    // LDS, at most kGemvCuWaves waves); one row block each otherwise
-#ifndef AWQ_GEMV_PERSIST
-#define AWQ_GEMV_PERSIST 1
-#endif
-    const int per_cu = max(1, min(kGemvCuWaves / kGemvWaves, (int)((160 * 1024) / lds)));
-    const int grid = (AWQ_GEMV_PERSIST && SG == G) ? min(NB, device_cu_count() * per_cu) : NB;
-    if (ring)
-        hipLaunchKernelGGL(kern1, dim3(grid), dim3(64 * kGemvWaves), lds, st,
+    // the kernels address their buffers with 32-bit offsets (the API rejects
+    // larger matrices)
+    if ((size_t)NB * G * 64 * WQ * 4 >= ((size_t)1 << 31)) return (int)hipErrorInvalidValue;
+    const int cus = device_cu_count();
+    const size_t red = 2 * (size_t)kGemvWaves * 64 * 16;
+    const size_t x1_lds = (((size_t)M * (K + 8) * 2 + 15) & ~(size_t)15) + red;
+    if ((size_t)M * (K + 8) * 2 <= (size_t)kGemvXBuf) {
+        // x staged once; persistent workgroups (as many as fit on a CU by LDS,
+        // at most kGemvCuWaves waves)
+        auto kern = pick_x1<BITS>(G <= 4 * kGemvWaves,
+                                  ((G + kGemvWaves - 1) / kGemvWaves * M + 3) / 4);   // x loads per lane
+        if (x1_lds > 64 * 1024) {
+            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)x1_lds);
+            if (e != hipSuccess) return (int)e;
+        }
+        const int per_cu = max(1, min(kGemvCuWaves / kGemvWaves, (int)((160 * 1024) / x1_lds)));
+        const int grid = min(NB, cus * per_cu);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kGemvWaves), x1_lds, st,
                            (const _Float16*)x, (const uint32_t*)qweight, (const _Float16*)scales,
                            (const _Float16*)zeros, (_Float16*)y, M, N, K);
-    else
+    } else {
+        // K in slices of 16 groups; up to 2 row blocks per workgroup (4 per
+        // workgroup reads x half as often but spills at M = 16; measured on
+        // MI355X, 8192x28672 at M = 16: 39.5 us with 2, 41.8 us with 4)
+        constexpr int SG = kGemvWaves * kGemvSliceRing;
+        const size_t lds = max(((size_t)M * (SG * kGroup + 8) * 2 + 15) & ~(size_t)15, red);
+        const int per_cu = max(1, min(kGemvCuWaves / kGemvWaves, (int)((160 * 1024) / lds)));
+        const int grid = max(min(NB, cus * per_cu), (NB + 1) / 2);
+        const int bmax = (NB + grid - 1) / grid;
+        auto kern = pick_xs<BITS>(bmax, (kGemvSliceRing * M + 3) / 4);
+        if (lds > 64 * 1024) {
+            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return (int)e;
+        }
         hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kGemvWaves), lds, st,
                            (const _Float16*)x, (const uint32_t*)qweight, (const _Float16*)scales,
-                           (const _Float16*)zeros, (_Float16*)y, M, N, K, SG);
+                           (const _Float16*)zeros, (_Float16*)y, M, N, K);
+    }
     return (int)hipGetLastError();
 }
 
