@@ -98,12 +98,17 @@ size_t awq_packed_words(int N, int K, int bits);
  *   s        fp32 [K]      per-input-channel scale, or NULL for s == 1
  *   qweight  uint32 [awq_packed_words(N, K, bits)]  out, format above
  *            (padding rows of the last block are written as zeros)
- *   scales   fp16 [ceil(N/16)][G][16]  out, D = largest fp16 <= max(hi - lo, 1e-5) / Q
- *   zeros    fp16 [ceil(N/16)][G][16]  out, z = clamp(rint(-lo / D), 0, Q)
- * with, per (n, g), v = fp32(W) * s, lo = min(0, min v), hi = max(0, max v),
- * and q = clamp(rint(v / D) + z, 0, Q); all fp32 IEEE, round-half-even,
- * correctly rounded division.
- * bits in {3, 4}; group_size must be 128; zero_point must be 1.
+ *   scales   fp16 [ceil(N/16)][G][16]  out, D (below)
+ *   zeros    fp16 [ceil(N/16)][G][16]  out, z (below)
+ * with, per (n, g), v = fp32(W) * s and q = clamp(rint(v / D) + z, 0, Q),
+ * Q = 2^bits - 1:
+ *   zero_point = 1 (asymmetric): lo = min(0, min v), hi = max(0, max v),
+ *     D = largest fp16 <= max(hi - lo, 1e-5) / Q, z = clamp(rint(-lo / D), 0, Q)
+ *   zero_point = 0 (symmetric): D = largest fp16 <= max(max |v|, 1e-5) /
+ *     (2^(bits-1) - 1), z = 2^(bits-1) (codes z - 7..z + 7 for int4)
+ * all fp32 IEEE, round-half-even, correctly rounded division.  Either way
+ * w_hat = (q - z) * D, so awq_gemv and awq_gemm serve both.
+ * bits in {3, 4}; group_size must be 128; zero_point 0 or 1.
  */
 int awq_quantize_pack(const void* W, const float* s, int N, int K, int bits,
                       int group_size, int zero_point, void* qweight,
@@ -132,6 +137,7 @@ size_t awq_search_workspace_bytes(int T, int N, int K, int n_alpha);
  *   s_i[k]   = fp32(pow(max(s_x[k], 1e-4), alphas[i]))        (fp64 pow)
  *   L_i      = mean_{t,n} (sum_k X_cal[t][k] (W[n][k] - w_hat_i[n][k] / s_i[k]))^2
  *              with w_hat_i the dequantized weights of awq_quantize_pack(W, s_i)
+ *              (same bits and zero_point)
  *   best     = smallest i with L_i == min L
  *   W        fp16 [N][K] in;  X_cal fp16 [T][K] in, 1 <= T <= 8192
  *   alphas   HOST fp32 [n_alpha], 1 <= n_alpha <= 64

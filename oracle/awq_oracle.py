@@ -45,7 +45,7 @@ import numpy as np
 # Parameters named as on the pages ([P4] quant_config, [P3] quantization_config).
 GROUP_SIZE = 128
 SUPPORTED_BITS = (3, 4)
-SPAN_FLOOR = np.float32(1e-5)      # reading: (hi - lo) floored before /Q
+SPAN_FLOOR = np.float32(1e-5)      # reading: (hi - lo), or max |v|, floored before the divide
 STAT_FLOOR = 1e-4                  # reading: s_x floored before the power
 
 PACK_FORMAT_VERSION = 2
@@ -110,14 +110,14 @@ def candidate_scale(s_x: np.ndarray, alpha: float) -> np.ndarray:
 # a3: group quantization
 # ---------------------------------------------------------------------------
 def quantize(W: np.ndarray, s: np.ndarray | None = None, bits: int = 4,
-             group_size: int = GROUP_SIZE):
-    """Round-to-nearest asymmetric group quantization of W * diag(s).
+             group_size: int = GROUP_SIZE, zero_point: bool = True):
+    """Round-to-nearest group quantization of W * diag(s).
 
     [P4] "Quantizing a model with AutoAWQ": q_group_size weights share one
-    scale and one zero point, zero_point=True means asymmetric; [P1] "Usage":
-    --w_bit 4 --q_group_size 128.  v = W[n, k] * s[k] is one fp32 multiply
-    (s = None means s == 1); the groups of v are then quantized by
-    ``quantize_values``.
+    scale and one zero point; zero_point=True means asymmetric quantization,
+    False symmetric; [P1] "Usage": --w_bit 4 --q_group_size 128.
+    v = W[n, k] * s[k] is one fp32 multiply (s = None means s == 1); the
+    groups of v are then quantized by ``quantize_values``.
     Returns (q uint8 [N][K], scales fp16 [N][G], zeros fp16 [N][G]).
     """
     W = np.asarray(W)
@@ -130,20 +130,27 @@ def quantize(W: np.ndarray, s: np.ndarray | None = None, bits: int = 4,
         if s32.shape != (K,):
             raise ValueError("s must have shape [K]")
         v = v * s32[None, :]                        # one fp32 multiply
-    return quantize_values(v, bits, group_size)
+    return quantize_values(v, bits, group_size, zero_point)
 
 
-def quantize_values(v: np.ndarray, bits: int = 4, group_size: int = GROUP_SIZE):
+def quantize_values(v: np.ndarray, bits: int = 4, group_size: int = GROUP_SIZE,
+                    zero_point: bool = True):
     """Group quantizer on already-scaled fp32 values v [N][K].
 
-    Per (row n, group g of 128 consecutive k), all in IEEE fp32:
+    Per (row n, group g of 128 consecutive k), all in IEEE fp32, with
+    zero_point (asymmetric):
         lo  = min(0, min v),  hi = max(0, max v)
         D32 = max(hi - lo, 1e-5) / Q ;  Dh = largest fp16 <= D32 ;  D = Dh
         z   = clamp(rint(-lo / D), 0, Q)
+    without (symmetric, zero centred; Qs = 2**(bits-1) - 1):
+        D32 = max(max |v|, 1e-5) / Qs ;  Dh = largest fp16 <= D32 ;  D = Dh
+        z   = 2**(bits-1)       (a fixed offset, so the codes stay unsigned)
+    and in both cases
         q   = clamp(rint(v / D) + z, 0, Q)
-    rint rounds half to even.  Readings: the range is widened to contain 0;
-    the span floor 1e-5 keeps an all-zero group finite; Dh is rounded down;
-    the code is computed with the stored fp16 scale.
+    rint rounds half to even.  Readings: the asymmetric range is widened to
+    contain 0; the floor 1e-5 keeps an all-zero group finite; Dh is rounded
+    down; the code is computed with the stored fp16 scale; the symmetric
+    grid is the textbook one, codes -Qs..Qs around the offset.
     """
     Q = levels(bits)
     v = np.asarray(v)
@@ -155,13 +162,18 @@ def quantize_values(v: np.ndarray, bits: int = 4, group_size: int = GROUP_SIZE):
     G = K // group_size
     g = v.reshape(N, G, group_size)
 
-    lo = np.minimum(g.min(axis=2), np.float32(0.0))
-    hi = np.maximum(g.max(axis=2), np.float32(0.0))
-    span = np.maximum(hi - lo, SPAN_FLOOR)
-    delta16 = f16_round_down(span / np.float32(Q))
-    delta = delta16.astype(np.float32)
-
-    z = np.clip(np.rint(-lo / delta), 0, Q).astype(np.int32)
+    if zero_point:
+        lo = np.minimum(g.min(axis=2), np.float32(0.0))
+        hi = np.maximum(g.max(axis=2), np.float32(0.0))
+        span = np.maximum(hi - lo, SPAN_FLOOR)
+        delta16 = f16_round_down(span / np.float32(Q))
+        delta = delta16.astype(np.float32)
+        z = np.clip(np.rint(-lo / delta), 0, Q).astype(np.int32)
+    else:
+        amax = np.maximum(np.abs(g).max(axis=2), SPAN_FLOOR)
+        delta16 = f16_round_down(amax / np.float32(2 ** (bits - 1) - 1))
+        delta = delta16.astype(np.float32)
+        z = np.full(delta.shape, 2 ** (bits - 1), dtype=np.int32)
     code = np.rint(g / delta[:, :, None]) + z[:, :, None].astype(np.float32)
     q = np.clip(code, 0, Q).astype(np.uint8)
     return q.reshape(N, K), delta16, z.astype(np.float16)
@@ -398,7 +410,7 @@ def output_mse(X_cal: np.ndarray, W: np.ndarray, w_hat: np.ndarray,
 
 
 def search_scale(W: np.ndarray, X_cal: np.ndarray, alphas, bits: int = 4,
-                 group_size: int = GROUP_SIZE):
+                 group_size: int = GROUP_SIZE, zero_point: bool = True):
     """Grid search of alpha minimising the layer's output MSE.
 
     [P1] "Usage" step 1 (--run_awq: search and save the per-channel scales),
@@ -411,16 +423,17 @@ def search_scale(W: np.ndarray, X_cal: np.ndarray, alphas, bits: int = 4,
     losses = []
     for a in alphas:
         s = candidate_scale(s_x, a)
-        q, d, z = quantize(W, s, bits, group_size)
+        q, d, z = quantize(W, s, bits, group_size, zero_point)
         losses.append(output_mse(X_cal, W, dequantize(q, d, z, group_size), s))
     losses = np.asarray(losses, dtype=np.float64)
     best = int(np.argmin(losses))                   # first minimum
     return candidate_scale(s_x, alphas[best]), losses, best
 
 
-def awq_quantize_layer(W: np.ndarray, X_cal: np.ndarray, alphas, bits: int = 4):
+def awq_quantize_layer(W: np.ndarray, X_cal: np.ndarray, alphas, bits: int = 4,
+                       zero_point: bool = True):
     """Whole offline pass: search, then quantize and pack with the chosen s."""
-    s, losses, best = search_scale(W, X_cal, alphas, bits)
-    q, d, z = quantize(W, s, bits)
+    s, losses, best = search_scale(W, X_cal, alphas, bits, zero_point=zero_point)
+    q, d, z = quantize(W, s, bits, zero_point=zero_point)
     return {"s": s, "losses": losses, "best": best,
             "qweight": pack(q, bits), "scales": d, "zeros": z, "q": q}

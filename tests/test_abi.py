@@ -82,7 +82,8 @@ def test_quantize_pack_validation(lib):
     assert qp(lib, bits=2) == UNSUP
     assert qp(lib, bits=8) == UNSUP
     assert qp(lib, gs=64) == UNSUP
-    assert qp(lib, zp=0) == UNSUP
+    assert qp(lib, zp=2) == UNSUP
+    assert qp(lib, zp=0, W=NUL) == NULL            # zero_point 0 (symmetric) is supported
     assert qp(lib, K=500) == SHAPE
     assert qp(lib, K=0) == SHAPE
     assert qp(lib, N=-1) == SHAPE
@@ -142,7 +143,8 @@ def search(lib, W=P, X=P2, T=64, N=256, K=512, alphas=(0.0, 0.5), bits=4, gs=128
 
 def test_search_validation(lib):
     assert search(lib, bits=2) == UNSUP
-    assert search(lib, zp=0) == UNSUP
+    assert search(lib, zp=2) == UNSUP
+    assert search(lib, zp=0, W=NUL) == NULL
     assert search(lib, alphas=()) == UNSUP
     assert search(lib, alphas=tuple([0.5] * 65)) == UNSUP
     assert search(lib, T=8193) == UNSUP

@@ -11,21 +11,23 @@ from gpu_util import announce, dev, guarded_empty, host, sentinel_intact
 pytestmark = pytest.mark.gpu
 
 
-def _check_rows(W, s, bits, rows=None):
+def _check_rows(W, s, bits, rows=None, zero_point=True):
     """GPU quantize_pack of the whole W; oracle on `rows` (all if None)."""
     import torch
     N, K = W.shape
-    announce("quantize_pack", f"N={N} K={K} bits={bits} s={'yes' if s is not None else 'no'}")
-    qw, sc, ze = awq.quantize_pack(dev(W), None if s is None else dev(s), bits=bits)
+    announce("quantize_pack", f"N={N} K={K} bits={bits} s={'yes' if s is not None else 'no'} "
+                              f"zero_point={zero_point}")
+    qw, sc, ze = awq.quantize_pack(dev(W), None if s is None else dev(s), bits=bits,
+                                   zero_point=zero_point)
     torch.cuda.synchronize()
     words = host(qw).view(np.uint32)
     if rows is None:
-        q, d, z = O.quantize(W, s, bits)
+        q, d, z = O.quantize(W, s, bits, zero_point=zero_point)
         assert np.array_equal(words, O.pack(q, bits).ravel()), "packed tiles differ"
         rows = np.arange(N)
     else:
         rows = np.asarray(rows)
-        q, d, z = O.quantize(W[rows], s, bits)
+        q, d, z = O.quantize(W[rows], s, bits, zero_point=zero_point)
         assert words.size == O.packed_words(N, K, bits)
         got_rows = O.tiles_to_rows(words, bits, K)
         assert np.array_equal(got_rows[rows], O.pack_rows(q, bits)), "packed codes differ"
@@ -47,16 +49,18 @@ def test_workload1_with_awq_scale(gpu, bits):
     _check_rows(W, None, bits)
 
 
+@pytest.mark.parametrize("zero_point", [True, False])
 @pytest.mark.parametrize("bits", [4, 3])
 @pytest.mark.parametrize("N,K", [(1, 128), (3, 256), (37, 384), (129, 11008), (64, 4224)])
-def test_ragged_shapes(gpu, bits, N, K):
+def test_ragged_shapes(gpu, bits, N, K, zero_point):
     W = WL.random_weights(N, K, seed=N * 7 + K)
     s = np.random.default_rng(K).lognormal(0, 1.5, K).astype(np.float32)
-    _check_rows(W, s, bits)
+    _check_rows(W, s, bits, zero_point=zero_point)
 
 
+@pytest.mark.parametrize("zero_point", [True, False])
 @pytest.mark.parametrize("bits", [4, 3])
-def test_degenerate_groups(gpu, bits):
+def test_degenerate_groups(gpu, bits, zero_point):
     """All-zero rows (subnormal fp16 scale), one-sided groups, ties, huge outliers."""
     rng = np.random.default_rng(5)
     W = (rng.standard_normal((8, 512)) * 0.02).astype(np.float32)
@@ -67,8 +71,9 @@ def test_degenerate_groups(gpu, bits):
     W[4, ::37] *= 300                                # outliers
     W[5] = 1e-6                                      # fp16-subnormal weights
     W[6, :128] = 0.0                                 # one zero group among normal ones
-    _check_rows(W.astype(np.float16), None, bits)
-    _check_rows(W.astype(np.float16), rng.lognormal(0, 1, 512).astype(np.float32), bits)
+    _check_rows(W.astype(np.float16), None, bits, zero_point=zero_point)
+    _check_rows(W.astype(np.float16), rng.lognormal(0, 1, 512).astype(np.float32), bits,
+                zero_point=zero_point)
 
 
 @pytest.mark.parametrize("shape_index", [0, 1, 2])
@@ -85,6 +90,8 @@ def test_workload3_full_size_sampled_rows(gpu, shape_index, bits):
     rows = np.concatenate([[0, W.shape[0] - 1], rows])
     s = np.random.default_rng(9).lognormal(0, 1, W.shape[1]).astype(np.float32)
     _check_rows(W, s, bits, rows)
+    if bits == 4:
+        _check_rows(W, s, bits, rows, zero_point=False)
 
 
 def test_no_write_past_outputs_and_deterministic(gpu):

@@ -19,17 +19,17 @@ from gpu_util import TOL, announce, dev, host, rel_err
 pytestmark = pytest.mark.gpu
 
 
-def gpu_search(W, X, alphas, bits):
+def gpu_search(W, X, alphas, bits, zero_point=True):
     import torch
-    s, loss, best = awq.search_scale(dev(W), dev(X), alphas, bits=bits)
+    s, loss, best = awq.search_scale(dev(W), dev(X), alphas, bits=bits, zero_point=zero_point)
     torch.cuda.synchronize()
     return host(s), host(loss).astype(np.float64), int(host(best)[0])
 
 
-def check_search(W, X, alphas, bits):
-    announce("search_scale", W.shape, X.shape, len(alphas), bits)
-    s_g, loss_g, best_g = gpu_search(W, X, alphas, bits)
-    s_r, loss_r, best_r = O.search_scale(W, X, alphas, bits)
+def check_search(W, X, alphas, bits, zero_point=True):
+    announce("search_scale", W.shape, X.shape, len(alphas), bits, f"zero_point={zero_point}")
+    s_g, loss_g, best_g = gpu_search(W, X, alphas, bits, zero_point)
+    s_r, loss_r, best_r = O.search_scale(W, X, alphas, bits, zero_point=zero_point)
     assert np.allclose(loss_g, loss_r, rtol=1e-2, atol=0), (loss_g, loss_r)
     assert best_g == best_r or loss_r[best_g] <= (1 + 1e-3) * loss_r[best_r], (best_g, best_r)
     s_expect = O.candidate_scale(O.act_stat(X), alphas[best_g])
@@ -57,6 +57,30 @@ def test_ragged_search(gpu):
     W = WL.random_weights(77, 384, seed=4)
     X = WL.random_activations(100, 384, seed=5, sigma=1.5)
     check_search(W, X, [0.0, 0.3, 0.6, 0.9], 4)
+
+
+@pytest.mark.parametrize("bits", [4, 3])
+def test_symmetric_search_and_pass(gpu, bits):
+    """zero_point=False: search, then pack with the GPU's s; both matmuls on it."""
+    import torch
+    wl = WL.workload(1)
+    W, X = wl.weights(), wl.calibration()
+    s_g, _ = check_search(W, X, [i / 20 for i in range(20)], bits, zero_point=False)
+    qw, sc, ze = awq.quantize_pack(dev(W), dev(s_g), bits=bits, zero_point=False)
+    q, d, z = O.quantize(W, s_g, bits, zero_point=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(qw).view(np.uint32), O.pack(q, bits).ravel())
+    assert np.array_equal(host(sc).view(np.uint16), O.tile_params(d).view(np.uint16))
+    assert np.array_equal(host(ze).view(np.uint16), O.tile_params(z).view(np.uint16))
+    x = O.scale_activations(wl.activations(16), s_g)
+    y_ref = O.matmul(x, O.pack(q, bits), d, z, bits, W.shape[1])
+    ys = [("gemv", awq.gemv(dev(x), qw, sc, ze, N=W.shape[0], bits=bits))]
+    if bits == 4:
+        ys.append(("gemm", awq.gemm(dev(x), qw, sc, ze, N=W.shape[0], bits=bits)))
+    torch.cuda.synchronize()
+    for name, y in ys:
+        err = rel_err(host(y).astype(np.float64), y_ref)
+        assert err <= TOL, f"{name} on symmetric weights: rel err {err:.3e}"
 
 
 @pytest.mark.parametrize("bits", [4, 3])

@@ -72,17 +72,31 @@ struct GroupParams {
     uint16_t dbits;    // the stored fp16 scale
 };
 
-template <int Q>
+// Scale and zero point of a group from its min and max (fp32, IEEE).
+// zero_point (asymmetric): range widened to contain 0, D = largest fp16 <=
+// max(hi - lo, 1e-5) / Q, z = clamp(rint(-lo / D), 0, Q).  Symmetric
+// (zero_point false, "Quantizing a model with AutoAWQ"): D = largest fp16 <=
+// max(max |v|, 1e-5) / (2^(b-1) - 1) and the fixed z = 2^(b-1), so codes
+// rint(v / D) + z keep the same unsigned storage and (q - z) * D dequant.
+template <int Q, bool ZP>
 __device__ __forceinline__ GroupParams group_params(float vmin, float vmax) {
-    float lo = fminf(vmin, 0.0f);
-    float hi = fmaxf(vmax, 0.0f);
-    float span = fmaxf(hi - lo, 1e-5f);
-    float d32 = span / (float)Q;
     GroupParams p;
-    p.dbits = f16_bits_round_down(d32);
-    p.delta = (float)bits_half(p.dbits);
-    float z = __builtin_rintf(-lo / p.delta);
-    p.zero = fminf(fmaxf(z, 0.0f), (float)Q);
+    if constexpr (ZP) {
+        float lo = fminf(vmin, 0.0f);
+        float hi = fmaxf(vmax, 0.0f);
+        float span = fmaxf(hi - lo, 1e-5f);
+        float d32 = span / (float)Q;
+        p.dbits = f16_bits_round_down(d32);
+        p.delta = (float)bits_half(p.dbits);
+        float z = __builtin_rintf(-lo / p.delta);
+        p.zero = fminf(fmaxf(z, 0.0f), (float)Q);
+    } else {
+        const float amax = fmaxf(fmaxf(-vmin, vmax), 1e-5f);   // max |v|: negation is exact
+        const float d32 = amax / (float)((Q - 1) / 2);
+        p.dbits = f16_bits_round_down(d32);
+        p.delta = (float)bits_half(p.dbits);
+        p.zero = (float)((Q + 1) / 2);
+    }
     return p;
 }
 
@@ -97,7 +111,7 @@ __device__ __forceinline__ uint32_t quant_code(float v, const GroupParams& p) {
 // host-side launchers (each .hip file owns its kernels); they return 0 or a
 // hipError_t value.  Arguments have been validated by the C ABI layer.
 // ---------------------------------------------------------------------------
-int launch_quantize_pack(const void* W, const float* s, int N, int K, int bits,
+int launch_quantize_pack(const void* W, const float* s, int N, int K, int bits, int zero_point,
                          void* qweight, void* scales, void* zeros, hipStream_t st);
 int launch_scale_activations(const void* x, const float* s, void* x_out, int M, int K,
                              hipStream_t st);
@@ -113,7 +127,7 @@ size_t loss_gemm_tiles(int T, int N);
 int launch_loss_gemm(const void* X, const void* D, int T, int N, int K, int n_batch,
                      double* partials, hipStream_t st);
 int launch_search(const void* W, const void* X_cal, int T, int N, int K, const float* alphas,
-                  int n_alpha, int bits, float* s_out, float* loss_out, int* best_out,
-                  void* workspace, hipStream_t st);
+                  int n_alpha, int bits, int zero_point, float* s_out, float* loss_out,
+                  int* best_out, void* workspace, hipStream_t st);
 
 }  // namespace awq

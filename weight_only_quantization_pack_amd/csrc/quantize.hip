@@ -26,7 +26,7 @@ __device__ __forceinline__ void unpack8(const uint4& raw, float* f) {
 }
 
 // One wave per tile; BITS selects 4 words (int4) or 3 words (int3) per slot.
-template <int BITS>
+template <int BITS, bool ZP>
 __global__ __launch_bounds__(256) void k_quantize_pack(
     const _Float16* __restrict__ W, const float* __restrict__ s, int N, int K,
     long long n_tiles, uint32_t* __restrict__ qweight, uint16_t* __restrict__ scales,
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void k_quantize_pack(
     // the four quarters of row j sit in lanes j, j+16, j+32, j+48
     mn = fminf(mn, __shfl_xor(mn, 16)); mx = fmaxf(mx, __shfl_xor(mx, 16));
     mn = fminf(mn, __shfl_xor(mn, 32)); mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const GroupParams p = group_params<Q>(mn, mx);
+    const GroupParams p = group_params<Q, ZP>(mn, mx);
 
     uint32_t out[WQ];
     if constexpr (BITS == 4) {
@@ -131,18 +131,14 @@ __global__ __launch_bounds__(256) void k_scale_activations(
 
 }  // namespace
 
-int launch_quantize_pack(const void* W, const float* s, int N, int K, int bits, void* qweight,
-                         void* scales, void* zeros, hipStream_t st) {
+int launch_quantize_pack(const void* W, const float* s, int N, int K, int bits, int zero_point,
+                         void* qweight, void* scales, void* zeros, hipStream_t st) {
     const long long n_tiles = (long long)((N + 15) / 16) * (K / kGroup);
     const long long grid = (n_tiles + 3) / 4;
-    if (bits == 4)
-        hipLaunchKernelGGL(k_quantize_pack<4>, dim3((unsigned)grid), dim3(256), 0, st,
-                           (const _Float16*)W, s, N, K, n_tiles, (uint32_t*)qweight,
-                           (uint16_t*)scales, (uint16_t*)zeros);
-    else
-        hipLaunchKernelGGL(k_quantize_pack<3>, dim3((unsigned)grid), dim3(256), 0, st,
-                           (const _Float16*)W, s, N, K, n_tiles, (uint32_t*)qweight,
-                           (uint16_t*)scales, (uint16_t*)zeros);
+    auto kern = bits == 4 ? (zero_point ? k_quantize_pack<4, true> : k_quantize_pack<4, false>)
+                          : (zero_point ? k_quantize_pack<3, true> : k_quantize_pack<3, false>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const _Float16*)W, s, N, K,
+                       n_tiles, (uint32_t*)qweight, (uint16_t*)scales, (uint16_t*)zeros);
     return (int)hipGetLastError();
 }
 

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void k_candidate_scales(const float* __restric
 // Quantization error of every alpha: one lane = 8 consecutive weights of one
 // row, 16 lanes = one group (same lane layout as the int4 quantize kernel;
 // the error does not depend on the packed format).
-template <int Q>
+template <int Q, bool ZP>
 __global__ __launch_bounds__(256) void k_quant_err(const uint4* __restrict__ W,
                                                   const float* __restrict__ s_all, int K,
                                                   long long n_chunks, uint4* __restrict__ D) {
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(256) void k_quant_err(const uint4* __restrict__ W,
         mn = fminf(mn, __shfl_xor(mn, m, 16));
         mx = fmaxf(mx, __shfl_xor(mx, m, 16));
     }
-    const GroupParams p = group_params<Q>(mn, mx);
+    const GroupParams p = group_params<Q, ZP>(mn, mx);
     uint4 out;
     _Float16* o = reinterpret_cast<_Float16*>(&out);
 #pragma unroll
@@ -143,8 +143,8 @@ size_t search_workspace_bytes(int T, int N, int K, int n_alpha) {
 }
 
 int launch_search(const void* W, const void* X_cal, int T, int N, int K, const float* alphas,
-                  int n_alpha, int bits, float* s_out, float* loss_out, int* best_out,
-                  void* workspace, hipStream_t st) {
+                  int n_alpha, int bits, int zero_point, float* s_out, float* loss_out,
+                  int* best_out, void* workspace, hipStream_t st) {
     const Layout L = layout(T, N, K, n_alpha);
     char* ws = static_cast<char*>(workspace);
     float* s_x = reinterpret_cast<float*>(ws + L.sx);
@@ -162,12 +162,9 @@ int launch_search(const void* W, const void* X_cal, int T, int N, int K, const f
                        s_x, K, grid, n_alpha, s_all);
     const long long n_chunks = (long long)N * K / 8;
     const dim3 qgrid((unsigned)((n_chunks + 255) / 256), n_alpha);
-    if (bits == 4)
-        hipLaunchKernelGGL(k_quant_err<15>, qgrid, dim3(256), 0, st, (const uint4*)W, s_all, K,
-                           n_chunks, (uint4*)D);
-    else
-        hipLaunchKernelGGL(k_quant_err<7>, qgrid, dim3(256), 0, st, (const uint4*)W, s_all, K,
-                           n_chunks, (uint4*)D);
+    auto qerr = bits == 4 ? (zero_point ? k_quant_err<15, true> : k_quant_err<15, false>)
+                          : (zero_point ? k_quant_err<7, true> : k_quant_err<7, false>);
+    hipLaunchKernelGGL(qerr, qgrid, dim3(256), 0, st, (const uint4*)W, s_all, K, n_chunks, (uint4*)D);
     int err = (int)hipGetLastError();
     if (err) return err;
     err = launch_loss_gemm(X_cal, D, T, N, K, n_alpha, part, st);
