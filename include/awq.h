@@ -180,6 +180,32 @@ int awq_gemm(const void* x, const void* qweight, const void* scales,
              const void* zeros, void* y, int M, int N, int K, int bits,
              int group_size, void* stream);
 
+/*
+ * awq_gemm_splitk_workspace_bytes -- device workspace awq_gemm_splitk needs
+ * for an M x N x K product on the current device: 0 when the output tiles
+ * already occupy at least half the compute units (no split), else
+ * splits * M * N * 4 bytes of fp32 partial sums.  0 for invalid shapes.
+ */
+size_t awq_gemm_splitk_workspace_bytes(int M, int N, int K);
+
+/*
+ * awq_gemm_splitk -- the awq_gemm product for small M (few output tiles),
+ * with K split across workgroups: each split writes an fp32 partial tile to
+ * the workspace and a second kernel adds the splits in a fixed order and
+ * rounds to fp16 (deterministic).  The split count is chosen per shape and
+ * device (each split keeps >= 8 groups, at most 16 splits); with one split
+ * this is awq_gemm.  Same arguments and limits as awq_gemm, plus
+ *   workspace / workspace_bytes: device scratch of at least
+ *   awq_gemm_splitk_workspace_bytes(M, N, K) bytes (ignored, may be NULL,
+ *   when that is 0), 16-byte aligned; too small -> AWQ_ERR_WORKSPACE.
+ * Callers that need no workspace use awq_gemm.  (The split-K / stream-K
+ * prefill item of the decode/prefill split in "transformers - AWQ".)
+ */
+int awq_gemm_splitk(const void* x, const void* qweight, const void* scales,
+                    const void* zeros, void* y, int M, int N, int K, int bits,
+                    int group_size, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -123,6 +123,22 @@ def test_gemv_and_gemm_specific_limits(lib):
     assert mm(lib, "awq_gemv", M=16, N=16, K=1 << 26) == SHAPE
 
 
+def test_gemm_splitk_validation(lib):
+    # without a GPU the library assumes 256 compute units: 32 tiles of a
+    # 64 x 8192 output leave most idle, so K = 28672 (224 groups) is split 8 ways
+    need = lib.awq_gemm_splitk_workspace_bytes(64, 8192, 28672)
+    assert need == 8 * 64 * 8192 * 4
+    assert lib.awq_gemm_splitk_workspace_bytes(2048, 14336, 4096) == 0      # enough tiles
+    assert lib.awq_gemm_splitk_workspace_bytes(64, 8192, 1000) == 0         # invalid K
+    f = lib.awq_gemm_splitk
+    assert f(P, P2, P3, P4, P5, 64, 8192, 28672, 4, 128, P, need - 1, NUL) == WS
+    assert f(P, P2, P3, P4, P5, 64, 8192, 28672, 4, 128, NUL, need, NUL) == NULL
+    assert f(P, P2, P3, P4, P5, 64, 8192, 28672, 4, 128, MIS, need, NUL) == ALIGN
+    assert f(P, P2, P3, P4, P5, 64, 8192, 28672, 3, 128, P, need, NUL) == UNSUP
+    assert f(P, P2, P3, P4, P5, 64, 8192, 1000, 4, 128, P, need, NUL) == SHAPE
+    assert f(NUL, NUL, NUL, NUL, NUL, 0, 8192, 28672, 4, 128, NUL, 0, NUL) == OK   # empty
+
+
 def test_scale_activations_validation(lib):
     assert lib.awq_scale_activations(P, P2, P3, 4, 100, NUL) == SHAPE
     assert lib.awq_scale_activations(P, P2, P3, -1, 128, NUL) == SHAPE

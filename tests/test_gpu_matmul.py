@@ -109,6 +109,25 @@ def test_gemm_small(gpu, M, N, K):
     check("gemm", M, N, K, 4, seed=200 + M + N + K)
 
 
+@pytest.mark.parametrize("M,N,K", [(5, 302, 2048), (130, 200, 4736), (64, 1000, 8192)])
+def test_gemm_split_k(gpu, M, N, K):
+    """Few output tiles: K split over workgroups (fp32 partials + ordered sum).
+    (130, 200, 4736): 37 groups in splits of 10, 10, 10, 7; N = 302: the
+    scalar tails of the partial store and of the reduction."""
+    import torch
+    assert awq.gemm_splitk_workspace_bytes(M, N, K) > 0
+    qw, d, z = packed(WL.random_weights(N, K, seed=N + K), 4)
+    x = WL.random_activations(M, K, seed=M + 1, sigma=1.0)
+    announce("gemm split-K", f"M={M} N={N} K={K}")
+    y_ref = O.matmul(x, qw, d, z, 4, K)
+    args = (dev(x), dev(qw.reshape(-1)), dev(O.tile_params(d)), dev(O.tile_params(z)))
+    for split in (True, False):
+        y = awq.gemm(*args, N=N, bits=4, split_k=split)
+        torch.cuda.synchronize()
+        err = rel_err(host(y).astype(np.float64), y_ref)
+        assert err <= TOL, f"split_k={split}: rel err {err:.3e}"
+
+
 @pytest.mark.parametrize("shape_index", [0, 1, 2])
 @pytest.mark.parametrize("M", [512, 2048])
 def test_gemm_workload4_sampled(gpu, M, shape_index):

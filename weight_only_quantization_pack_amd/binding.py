@@ -35,6 +35,9 @@ SIGNATURES = [
                           _c_int, _c_int, _c_int, _c_void_p]),
     ("awq_gemm", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                           _c_int, _c_int, _c_int, _c_void_p]),
+    ("awq_gemm_splitk_workspace_bytes", _c_size_t, [_c_int, _c_int, _c_int]),
+    ("awq_gemm_splitk", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
+                                 _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_size_t, _c_void_p]),
 ]
 
 STATUS = {0: "AWQ_OK", 1: "AWQ_ERR_NULL", 2: "AWQ_ERR_SHAPE", 3: "AWQ_ERR_UNSUPPORTED",
@@ -194,7 +197,7 @@ def search_scale(W, X_cal, alphas, bits: int = 4, group_size: int = GROUP_SIZE,
     return s_out, loss[:n_alpha], best
 
 
-def _matmul(fn_name, x, qweight, scales, zeros, N, bits, group_size, out):
+def _matmul(fn_name, x, qweight, scales, zeros, N, bits, group_size, out, workspace=None):
     torch = _torch()
     lib = load_library()
     M, K = x.shape
@@ -209,8 +212,14 @@ def _matmul(fn_name, x, qweight, scales, zeros, N, bits, group_size, out):
         out = torch.empty((M, N), dtype=torch.float16, device=x.device)
     else:
         _need(out, torch.float16, (M, N), "out")
-    st = getattr(lib, fn_name)(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(out),
-                               M, N, K, bits, group_size, _stream_ptr(x))
+    if fn_name == "awq_gemm_splitk":
+        st = lib.awq_gemm_splitk(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(out),
+                                 M, N, K, bits, group_size, _ptr(workspace),
+                                 0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                 _stream_ptr(x))
+    else:
+        st = getattr(lib, fn_name)(_ptr(x), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(out),
+                                   M, N, K, bits, group_size, _stream_ptr(x))
     _check(st, fn_name)
     return out
 
@@ -220,6 +229,25 @@ def gemv(x, qweight, scales, zeros, N: int, bits: int = 4, group_size: int = GRO
     return _matmul("awq_gemv", x, qweight, scales, zeros, N, bits, group_size, out)
 
 
-def gemm(x, qweight, scales, zeros, N: int, bits: int = 4, group_size: int = GROUP_SIZE, out=None):
-    """Prefill product y = x . w_hat^T for any M >= 1 rows of x (bits 4); N output columns."""
+def gemm_splitk_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Workspace bytes awq_gemm_splitk needs for this shape (0: no split)."""
+    return int(load_library().awq_gemm_splitk_workspace_bytes(M, N, K))
+
+
+def gemm(x, qweight, scales, zeros, N: int, bits: int = 4, group_size: int = GROUP_SIZE, out=None,
+         split_k: bool = True, workspace=None):
+    """Prefill product y = x . w_hat^T for any M >= 1 rows of x (bits 4); N output columns.
+
+    With split_k (default) shapes with few output tiles run through
+    awq_gemm_splitk; its fp32 workspace is `workspace` (a device tensor of at
+    least gemm_splitk_workspace_bytes bytes) or allocated here.  split_k=False
+    always calls awq_gemm.
+    """
+    if split_k and bits == 4 and x.dim() == 2:
+        need = gemm_splitk_workspace_bytes(x.shape[0], N, x.shape[1])
+        if need > 0:
+            if workspace is None:
+                workspace = _torch().empty(need, dtype=_torch().uint8, device=x.device)
+            return _matmul("awq_gemm_splitk", x, qweight, scales, zeros, N, bits, group_size, out,
+                           workspace)
     return _matmul("awq_gemm", x, qweight, scales, zeros, N, bits, group_size, out)

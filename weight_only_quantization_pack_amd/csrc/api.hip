@@ -145,4 +145,30 @@ int awq_gemm(const void* x, const void* qweight, const void* scales, const void*
                                        (hipStream_t)stream));
 }
 
+size_t awq_gemm_splitk_workspace_bytes(int M, int N, int K) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % awq::kGroup != 0) return 0;
+    return awq::gemm_splitk_workspace_bytes(M, N, K);
+}
+
+int awq_gemm_splitk(const void* x, const void* qweight, const void* scales, const void* zeros,
+                    void* y, int M, int N, int K, int bits, int group_size, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    int st = check_quant_params(bits, group_size, 1);
+    if (st) return st;
+    if (bits != 4) return AWQ_ERR_UNSUPPORTED;
+    if (M < 0) return AWQ_ERR_SHAPE;
+    if ((st = check_nk(N, K))) return st;
+    if ((long long)M * K >= (1LL << 31) || (long long)N * K / 8 >= (1LL << 31)) return AWQ_ERR_SHAPE;
+    if (M == 0 || N == 0) return AWQ_OK;
+    if ((st = check_ptrs({x, qweight, scales, zeros, y}))) return st;
+    const size_t need = awq::gemm_splitk_workspace_bytes(M, N, K);
+    if (need > 0) {
+        if (workspace == nullptr) return AWQ_ERR_NULL;
+        if ((st = check_ptr(workspace))) return st;
+        if (workspace_bytes < need) return AWQ_ERR_WORKSPACE;
+    }
+    return hip_status(awq::launch_gemm_splitk(x, qweight, scales, zeros, y, M, N, K, workspace,
+                                              (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -392,11 +392,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(
 // last group (the last round runs whole) re-load group G - 1 (valid
 // addresses, never consumed), which keeps the load stream the same every step: 20 loads per step and wave
 // (8 A direct-to-LDS, 4 B tiles, 4 scale words, 4 zero words).
+//
+// Split K (part != nullptr): workgroup (tile, blockIdx.y) covers groups
+// [blockIdx.y * gsplit, +gsplit) and writes its fp32 partial tile to
+// part[blockIdx.y][M][N]; k_splitk_reduce adds the splits in order.
 template <int S>
 __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
     const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
-    _Float16* __restrict__ Y, int M, int N, int K) {
+    _Float16* __restrict__ Y, float* __restrict__ part, int M, int N, int K, int gsplit) {
     using namespace w4;
     extern __shared__ __attribute__((aligned(16))) unsigned char As[];   // S x ABUF
 
@@ -405,6 +409,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, hq = lane >> 4;
     const int G = K / kGroup;
+    const int g_begin = (int)blockIdx.y * gsplit;      // this workgroup's groups: [g_begin, g_begin + GS)
+    const int GS = min(G - g_begin, gsplit);
     const int NB = (N + 15) / 16;
     const int nTn = (N + GN - 1) / GN, nTm = (M + GM - 1) / GM;
     const int nT = nTn * nTm;
@@ -433,7 +439,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     // part p (0..3) of step kt's loads: A rows groups 2p, 2p + 1 (direct to LDS
     // buffer `slot`), B tile p of this wave and its scale and zero words
     auto issue_part = [&](int kt, int slot, BStage& bs, int p) {
-        const uint32_t g = (uint32_t)min(kt, G - 1);
+        const uint32_t g = (uint32_t)(g_begin + min(kt, GS - 1));
 #pragma unroll
         for (int i = 2 * p; i < 2 * p + 2; ++i) {
             const int rg = wave * 8 + i;
@@ -520,7 +526,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
         issue(s, s, bs[s]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // G >= 1; a loop without an entry test keeps the compiler from sinking the
+    // GS >= 1; a loop without an entry test keeps the compiler from sinking the
     // prologue's register loads behind one (out of the order above)
     int kt0 = 0;
     do {
@@ -538,11 +544,32 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
             __builtin_amdgcn_sched_barrier(0);
             // the last round may run past G: those steps keep the load stream
             // (and so the compiler's wait counts) uniform but compute nothing
-            if (kt < G) compute(bs[st], As + st * ABUF);
+            if (kt < GS) compute(bs[st], As + st * ABUF);
         }
         kt0 += S;
-    } while (kt0 < G);
+    } while (kt0 < GS);
 
+    if (part != nullptr) {
+        float* prow0 = part + (size_t)blockIdx.y * M * N;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int m = m0 + 16 * i + j;
+            if (m >= M) continue;
+            float* prow = prow0 + (size_t)m * N;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int n = n0 + wave * 64 + 16 * c + 4 * hq;
+                if (n + 3 < N && ((N & 3) == 0)) {
+                    *reinterpret_cast<float4_t*>(prow + n) = acc[i][c];
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N) prow[n + r] = acc[i][c][r];
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int m = m0 + 16 * i + j;
@@ -564,7 +591,82 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     }
 }
 
+// y[i] = fp16(sum over s = 0 .. splits-1 of part[s][i]), in that order.
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part,
+                                                       _Float16* __restrict__ y, long long mn,
+                                                       int splits) {
+    const long long i0 = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i0 >= mn) return;
+    if (i0 + 3 < mn && (mn & 3) == 0) {
+        float4_t acc = *reinterpret_cast<const float4_t*>(part + i0);
+        for (int s = 1; s < splits; ++s) {
+            const float4_t v = *reinterpret_cast<const float4_t*>(part + (size_t)s * mn + i0);
+            acc[0] += v[0]; acc[1] += v[1]; acc[2] += v[2]; acc[3] += v[3];
+        }
+        const half2_t lo = {(_Float16)acc[0], (_Float16)acc[1]};
+        const half2_t hi = {(_Float16)acc[2], (_Float16)acc[3]};
+        *reinterpret_cast<uint2*>(y + i0) = make_uint2(as_u32(lo), as_u32(hi));
+    } else {
+        for (long long i = i0; i < i0 + 4 && i < mn; ++i) {
+            float a = part[i];
+            for (int s = 1; s < splits; ++s) a += part[(size_t)s * mn + i];
+            y[i] = (_Float16)a;
+        }
+    }
+}
+
+constexpr int kGemmStages = 4;
+
+int launch_w4p(const void* x, const void* qweight, const void* scales, const void* zeros, void* y,
+               float* part, int M, int N, int K, int splits, int gsplit, hipStream_t st) {
+    const int nT = ((N + w4::GN - 1) / w4::GN) * ((M + w4::GM - 1) / w4::GM);
+    const size_t lds = (size_t)kGemmStages * w4::ABUF;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_w4p<kGemmStages>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return (int)e;
+    hipLaunchKernelGGL(k_gemm_w4p<kGemmStages>, dim3(nT, splits), dim3(256), lds, st, (const _Float16*)x,
+                       (const uint32_t*)qweight, (const _Float16*)scales, (const _Float16*)zeros,
+                       (_Float16*)y, part, M, N, K, gsplit);
+    return (int)hipGetLastError();
+}
+
 }  // namespace
+
+int gemm_splits(int M, int N, int K) {
+    // split K only while the tiles leave at least half the CUs idle; each
+    // split keeps >= 8 groups (two rounds of the 4-step pipeline), <= 16 splits
+    const int nT = ((N + w4::GN - 1) / w4::GN) * ((M + w4::GM - 1) / w4::GM);
+    const int cus = device_cu_count();
+    const int G = K / kGroup;
+    if (2 * nT > cus) return 1;
+    int s = min(min(cus / nT, G / 8), 16);
+    if (s < 2) return 1;
+    const int gsplit = (G + s - 1) / s;
+    return (G + gsplit - 1) / gsplit;                  // no empty split
+}
+
+size_t gemm_splitk_workspace_bytes(int M, int N, int K) {
+    const int s = gemm_splits(M, N, K);
+    return s > 1 ? (size_t)s * M * N * sizeof(float) : 0;
+}
+
+int launch_gemm_splitk(const void* x, const void* qweight, const void* scales, const void* zeros,
+                       void* y, int M, int N, int K, void* workspace, hipStream_t st) {
+    const int s = gemm_splits(M, N, K);
+    if (s <= 1) return launch_gemm(x, qweight, scales, zeros, y, M, N, K, st);
+    if ((unsigned long long)M * K >= (1ull << 31) || (unsigned long long)N * K / 8 >= (1ull << 31))
+        return (int)hipErrorInvalidValue;
+    const int G = K / kGroup;
+    const int gsplit = (G + s - 1) / s;
+    float* part = static_cast<float*>(workspace);
+    int err = launch_w4p(x, qweight, scales, zeros, y, part, M, N, K, s, gsplit, st);
+    if (err) return err;
+    const long long mn = (long long)M * N;
+    const long long blocks = (mn / 4 + 1 + 255) / 256;
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)blocks), dim3(256), 0, st, part, (_Float16*)y,
+                       mn, s);
+    return (int)hipGetLastError();
+}
 
 int launch_gemm(const void* x, const void* qweight, const void* scales, const void* zeros,
                 void* y, int M, int N, int K, hipStream_t st) {
@@ -578,14 +680,7 @@ int launch_gemm(const void* x, const void* qweight, const void* scales, const vo
     // 14336x4096 (256 tiles) 974 vs 743 TFLOP/s; 4096x14336 (896 tiles) 764 vs
     // 816; 4096x6144 (384 tiles) 739 vs 849).
     if (nT <= device_cu_count()) {
-        constexpr int S = 4;
-        const size_t lds = (size_t)S * w4::ABUF;
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_w4p<S>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return (int)e;
-        hipLaunchKernelGGL(k_gemm_w4p<S>, dim3(nT), dim3(256), lds, st, (const _Float16*)x,
-                           (const uint32_t*)qweight, (const _Float16*)scales, (const _Float16*)zeros,
-                           (_Float16*)y, M, N, K);
+        return launch_w4p(x, qweight, scales, zeros, y, nullptr, M, N, K, 1, K / kGroup, st);
     } else {
         hipLaunchKernelGGL(k_gemm_w4, dim3(nT), dim3(256), 0, st, (const _Float16*)x,
                            (const uint32_t*)qweight, (const _Float16*)scales, (const _Float16*)zeros,
