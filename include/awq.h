@@ -173,7 +173,7 @@ int awq_gemv(const void* x, const void* qweight, const void* scales,
  * awq_gemv for any M >= 1 (the context kernel of the llm-awq README
  * feature list; version "gemm" in the transformers quantization_config).
  * Dequantized fp16 tiles feed fp16 MFMA with fp32 accumulation.
- *   bits must be 4; group_size 128; M*K < 2^31 and N*K/8 < 2^31 (else
+ *   bits in {3, 4}; group_size 128; M*K < 2^31 and N*K/8 < 2^31 (else
  *   AWQ_ERR_SHAPE).
  */
 int awq_gemm(const void* x, const void* qweight, const void* scales,

@@ -114,7 +114,7 @@ def test_matmul_validation(lib, fn):
 
 def test_gemv_and_gemm_specific_limits(lib):
     assert mm(lib, "awq_gemv", M=17) == UNSUP
-    assert mm(lib, "awq_gemm", bits=3) == UNSUP
+    assert mm(lib, "awq_gemm", bits=3, x=NUL) == NULL             # int3 prefill is supported
     assert mm(lib, "awq_gemv", M=17, bits=3, x=NUL) == UNSUP
     assert mm(lib, "awq_gemm", M=1 << 20, K=4096) == SHAPE      # 32-bit offset limit
     # decode: packed weight >= 2^31 bytes (int4: N*K >= 2^32) or x >= 2^31 bytes
@@ -134,7 +134,7 @@ def test_gemm_splitk_validation(lib):
     assert f(P, P2, P3, P4, P5, 64, 8192, 28672, 4, 128, P, need - 1, NUL) == WS
     assert f(P, P2, P3, P4, P5, 64, 8192, 28672, 4, 128, NUL, need, NUL) == NULL
     assert f(P, P2, P3, P4, P5, 64, 8192, 28672, 4, 128, MIS, need, NUL) == ALIGN
-    assert f(P, P2, P3, P4, P5, 64, 8192, 28672, 3, 128, P, need, NUL) == UNSUP
+    assert f(P, P2, P3, P4, P5, 64, 8192, 28672, 2, 128, P, need, NUL) == UNSUP
     assert f(P, P2, P3, P4, P5, 64, 8192, 1000, 4, 128, P, need, NUL) == SHAPE
     assert f(NUL, NUL, NUL, NUL, NUL, 0, 8192, 28672, 4, 128, NUL, 0, NUL) == OK   # empty
 

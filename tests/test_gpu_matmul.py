@@ -103,26 +103,36 @@ def test_gemv_sliced_two_blocks_per_workgroup(gpu, M):
 
 
 # ----------------------------------------------------------------------------- GEMM
+@pytest.mark.parametrize("bits", [4, 3])
 @pytest.mark.parametrize("M", [1, 5, 64, 128, 130, 257])
 @pytest.mark.parametrize("N,K", [(512, 512), (37, 384), (200, 1152)])
-def test_gemm_small(gpu, M, N, K):
-    check("gemm", M, N, K, 4, seed=200 + M + N + K)
+def test_gemm_small(gpu, M, N, K, bits):
+    check("gemm", M, N, K, bits, seed=200 + M + N + K)
 
 
+@pytest.mark.parametrize("M", [256, 2048])
+def test_gemm_int3_many_tiles(gpu, M):
+    """int3 with more tiles than CUs (the pipelined kernel in rounds)."""
+    N, K = 4096, 1024
+    rows = np.random.default_rng(M).choice(N, 40, replace=False)
+    check("gemm", M, N, K, 3, seed=7, rows=np.concatenate([[0, N - 1], rows]))
+
+
+@pytest.mark.parametrize("bits", [4, 3])
 @pytest.mark.parametrize("M,N,K", [(5, 302, 2048), (130, 200, 4736), (64, 1000, 8192)])
-def test_gemm_split_k(gpu, M, N, K):
+def test_gemm_split_k(gpu, M, N, K, bits):
     """Few output tiles: K split over workgroups (fp32 partials + ordered sum).
     (130, 200, 4736): 37 groups in splits of 10, 10, 10, 7; N = 302: the
     scalar tails of the partial store and of the reduction."""
     import torch
     assert awq.gemm_splitk_workspace_bytes(M, N, K) > 0
-    qw, d, z = packed(WL.random_weights(N, K, seed=N + K), 4)
+    qw, d, z = packed(WL.random_weights(N, K, seed=N + K), bits)
     x = WL.random_activations(M, K, seed=M + 1, sigma=1.0)
-    announce("gemm split-K", f"M={M} N={N} K={K}")
-    y_ref = O.matmul(x, qw, d, z, 4, K)
+    announce("gemm split-K", f"M={M} N={N} K={K} bits={bits}")
+    y_ref = O.matmul(x, qw, d, z, bits, K)
     args = (dev(x), dev(qw.reshape(-1)), dev(O.tile_params(d)), dev(O.tile_params(z)))
     for split in (True, False):
-        y = awq.gemm(*args, N=N, bits=4, split_k=split)
+        y = awq.gemm(*args, N=N, bits=bits, split_k=split)
         torch.cuda.synchronize()
         err = rel_err(host(y).astype(np.float64), y_ref)
         assert err <= TOL, f"split_k={split}: rel err {err:.3e}"
@@ -149,7 +159,7 @@ def test_gemm_workload3_m64_sampled(gpu, shape_index):
 
 
 # ----------------------------------------------------------------------------- exact cases
-@pytest.mark.parametrize("fn,bits", [("gemv", 4), ("gemv", 3), ("gemm", 4)])
+@pytest.mark.parametrize("fn,bits", [("gemv", 4), ("gemv", 3), ("gemm", 4), ("gemm", 3)])
 def test_one_hot_rows_are_exact(gpu, fn, bits):
     """x = e_k picks column k of w_hat; with D = 2^-4 every value is an exact fp16."""
     K, N = 256, 48
@@ -182,10 +192,11 @@ def test_gemv_equals_gemm_at_m1(gpu):
     assert rel_err(a, b) <= TOL
 
 
-@pytest.mark.parametrize("fn", ["gemv", "gemm"])
-def test_no_write_past_output_and_repeatable(gpu, fn):
+@pytest.mark.parametrize("fn,K", [("gemv", 384), ("gemm", 384), ("gemm", 2048)])
+def test_no_write_past_output_and_repeatable(gpu, fn, K):
+    """K = 2048 with 3 rows: the GEMM splits K (fp32 partials + reduction)."""
     import torch
-    M, N, K = (3, 37, 384)
+    M, N = 3, 37
     W = WL.random_weights(N, K, seed=12)
     x = WL.random_activations(M, K, seed=13)
     qw, d, z = packed(W, 4)

@@ -236,14 +236,14 @@ def gemm_splitk_workspace_bytes(M: int, N: int, K: int) -> int:
 
 def gemm(x, qweight, scales, zeros, N: int, bits: int = 4, group_size: int = GROUP_SIZE, out=None,
          split_k: bool = True, workspace=None):
-    """Prefill product y = x . w_hat^T for any M >= 1 rows of x (bits 4); N output columns.
+    """Prefill product y = x . w_hat^T for any M >= 1 rows of x (bits 4 or 3); N output columns.
 
     With split_k (default) shapes with few output tiles run through
     awq_gemm_splitk; its fp32 workspace is `workspace` (a device tensor of at
     least gemm_splitk_workspace_bytes bytes) or allocated here.  split_k=False
     always calls awq_gemm.
     """
-    if split_k and bits == 4 and x.dim() == 2:
+    if split_k and x.dim() == 2:
         need = gemm_splitk_workspace_bytes(x.shape[0], N, x.shape[1])
         if need > 0:
             if workspace is None:

@@ -134,14 +134,13 @@ int awq_gemm(const void* x, const void* qweight, const void* scales, const void*
              int M, int N, int K, int bits, int group_size, void* stream) {
     int st = check_quant_params(bits, group_size, 1);
     if (st) return st;
-    if (bits != 4) return AWQ_ERR_UNSUPPORTED;
     if (M < 0) return AWQ_ERR_SHAPE;
     if ((st = check_nk(N, K))) return st;
     // the prefill kernel addresses x and the packed tiles with 32-bit offsets
     if ((long long)M * K >= (1LL << 31) || (long long)N * K / 8 >= (1LL << 31)) return AWQ_ERR_SHAPE;
     if (M == 0 || N == 0) return AWQ_OK;
     if ((st = check_ptrs({x, qweight, scales, zeros, y}))) return st;
-    return hip_status(awq::launch_gemm(x, qweight, scales, zeros, y, M, N, K,
+    return hip_status(awq::launch_gemm(x, qweight, scales, zeros, y, M, N, K, bits,
                                        (hipStream_t)stream));
 }
 
@@ -155,7 +154,6 @@ int awq_gemm_splitk(const void* x, const void* qweight, const void* scales, cons
                     size_t workspace_bytes, void* stream) {
     int st = check_quant_params(bits, group_size, 1);
     if (st) return st;
-    if (bits != 4) return AWQ_ERR_UNSUPPORTED;
     if (M < 0) return AWQ_ERR_SHAPE;
     if ((st = check_nk(N, K))) return st;
     if ((long long)M * K >= (1LL << 31) || (long long)N * K / 8 >= (1LL << 31)) return AWQ_ERR_SHAPE;
@@ -167,8 +165,8 @@ int awq_gemm_splitk(const void* x, const void* qweight, const void* scales, cons
         if ((st = check_ptr(workspace))) return st;
         if (workspace_bytes < need) return AWQ_ERR_WORKSPACE;
     }
-    return hip_status(awq::launch_gemm_splitk(x, qweight, scales, zeros, y, M, N, K, workspace,
-                                              (hipStream_t)stream));
+    return hip_status(awq::launch_gemm_splitk(x, qweight, scales, zeros, y, M, N, K, bits,
+                                              workspace, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -121,13 +121,13 @@ int device_cu_count();
 int launch_gemv(const void* x, const void* qweight, const void* scales, const void* zeros,
                 void* y, int M, int N, int K, int bits, hipStream_t st);
 int launch_gemm(const void* x, const void* qweight, const void* scales, const void* zeros,
-                void* y, int M, int N, int K, hipStream_t st);
+                void* y, int M, int N, int K, int bits, hipStream_t st);
 // split-K prefill: number of K splits for this shape on the current device
 // (1: no split, no workspace) and the fp32 partial workspace it needs
 int gemm_splits(int M, int N, int K);
 size_t gemm_splitk_workspace_bytes(int M, int N, int K);
 int launch_gemm_splitk(const void* x, const void* qweight, const void* scales, const void* zeros,
-                       void* y, int M, int N, int K, void* workspace, hipStream_t st);
+                       void* y, int M, int N, int K, int bits, void* workspace, hipStream_t st);
 size_t search_workspace_bytes(int T, int N, int K, int n_alpha);
 size_t loss_gemm_tiles(int T, int N);
 int launch_loss_gemm(const void* X, const void* D, int T, int N, int K, int n_batch,

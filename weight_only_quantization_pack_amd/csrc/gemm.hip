@@ -232,6 +232,20 @@ __device__ __forceinline__ half8_t dequant_scaled(uint32_t w, half2_t zz, half2_
     return b;
 }
 
+// fp16 B operand w_hat = (q - z) * D of 8 int3 codes held in the low 24 bits
+// of v (code e at bits 3e..3e+2); zz = 1024 + z
+__device__ __forceinline__ half8_t dequant_scaled_int3(uint32_t v, half2_t zz, half2_t dd) {
+    half8_t b;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const uint32_t pair = ((v >> (6 * t)) & 7u) | (((v >> (6 * t + 3)) & 7u) << 16);
+        const half2_t p = (as_half2(pair | 0x64006400u) - zz) * dd;
+        b[2 * t] = p[0];
+        b[2 * t + 1] = p[1];
+    }
+    return b;
+}
+
 __global__ __launch_bounds__(256, 2) void k_gemm_w4(
     const _Float16* __restrict__ A, const uint32_t* __restrict__ qw,
     const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
@@ -396,7 +410,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(
 // Split K (part != nullptr): workgroup (tile, blockIdx.y) covers groups
 // [blockIdx.y * gsplit, +gsplit) and writes its fp32 partial tile to
 // part[blockIdx.y][M][N]; k_splitk_reduce adds the splits in order.
-template <int S>
+template <int BITS, int S>
 __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
     const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
@@ -435,7 +449,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     }
     const uint32_t psh = 16u * (uint32_t)(j & 1);      // the lane's half of a parameter word
 
-    struct BStage { uint4 q[4]; uint32_t d[4], z[4]; };
+    constexpr int WQ = BITS == 4 ? 4 : 3;              // words per lane slot
+    struct BStage { uint32_t q[4][WQ]; uint32_t d[4], z[4]; };
     // part p (0..3) of step kt's loads: A rows groups 2p, 2p + 1 (direct to LDS
     // buffer `slot`), B tile p of this wave and its scale and zero words
     auto issue_part = [&](int kt, int slot, BStage& bs, int p) {
@@ -447,7 +462,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
                                              (lds_void_t*)(As + slot * ABUF + rg * 1024), 16, 0, 0);
         }
         const uint32_t tt = tbase[p] + g;
-        bs.q[p] = *reinterpret_cast<const uint4*>(qw + (size_t)(tt * 256u + 4u * lane));
+        // one dwordx4 (int4) or dwordx3 (int3) load: 20 loads per step either way
+        if constexpr (BITS == 4) {
+            const uint4 v = *reinterpret_cast<const uint4*>(qw + (size_t)(tt * 256u + 4u * lane));
+            bs.q[p][0] = v.x; bs.q[p][1] = v.y; bs.q[p][2] = v.z; bs.q[p][3] = v.w;
+        } else {
+            const uint3 v = *reinterpret_cast<const uint3*>(qw + (size_t)(tt * 192u + 3u * lane));
+            bs.q[p][0] = v.x; bs.q[p][1] = v.y; bs.q[p][2] = v.z;
+        }
         bs.d[p] = *reinterpret_cast<const uint32_t*>(scales + tt * 16u + (uint32_t)(j & ~1));
         bs.z[p] = *reinterpret_cast<const uint32_t*>(zeros + tt * 16u + (uint32_t)(j & ~1));
     };
@@ -488,8 +510,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
         auto dequant = [&](int s, half8_t* b) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const uint32_t w = s == 0 ? bs.q[c].x : s == 1 ? bs.q[c].y : s == 2 ? bs.q[c].z : bs.q[c].w;
-                b[c] = dequant_scaled(w, zz[c], zz16[c], dd[c]);
+                if constexpr (BITS == 4) {
+                    b[c] = dequant_scaled(bs.q[c][s], zz[c], zz16[c], dd[c]);
+                } else {
+                    // 96-bit stream of 32 codes; substep s takes bits 24s..24s+23
+                    const uint32_t* w = bs.q[c];
+                    const uint32_t v = s == 0 ? (w[0] & 0xFFFFFFu)
+                                     : s == 1 ? ((w[0] >> 24) | ((w[1] & 0xFFFFu) << 8))
+                                     : s == 2 ? ((w[1] >> 16) | ((w[2] & 0xFFu) << 16))
+                                              : (w[2] >> 8);
+                    b[c] = dequant_scaled_int3(v, zz[c], dd[c]);
+                }
             }
         };
         half8_t a_cur[8], b_cur[4];
@@ -618,13 +649,14 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 constexpr int kGemmStages = 4;
 
 int launch_w4p(const void* x, const void* qweight, const void* scales, const void* zeros, void* y,
-               float* part, int M, int N, int K, int splits, int gsplit, hipStream_t st) {
+               float* part, int M, int N, int K, int bits, int splits, int gsplit, hipStream_t st) {
     const int nT = ((N + w4::GN - 1) / w4::GN) * ((M + w4::GM - 1) / w4::GM);
     const size_t lds = (size_t)kGemmStages * w4::ABUF;
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_w4p<kGemmStages>),
+    auto kern = bits == 4 ? k_gemm_w4p<4, kGemmStages> : k_gemm_w4p<3, kGemmStages>;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return (int)e;
-    hipLaunchKernelGGL(k_gemm_w4p<kGemmStages>, dim3(nT, splits), dim3(256), lds, st, (const _Float16*)x,
+    hipLaunchKernelGGL(kern, dim3(nT, splits), dim3(256), lds, st, (const _Float16*)x,
                        (const uint32_t*)qweight, (const _Float16*)scales, (const _Float16*)zeros,
                        (_Float16*)y, part, M, N, K, gsplit);
     return (int)hipGetLastError();
@@ -651,15 +683,15 @@ size_t gemm_splitk_workspace_bytes(int M, int N, int K) {
 }
 
 int launch_gemm_splitk(const void* x, const void* qweight, const void* scales, const void* zeros,
-                       void* y, int M, int N, int K, void* workspace, hipStream_t st) {
+                       void* y, int M, int N, int K, int bits, void* workspace, hipStream_t st) {
     const int s = gemm_splits(M, N, K);
-    if (s <= 1) return launch_gemm(x, qweight, scales, zeros, y, M, N, K, st);
+    if (s <= 1) return launch_gemm(x, qweight, scales, zeros, y, M, N, K, bits, st);
     if ((unsigned long long)M * K >= (1ull << 31) || (unsigned long long)N * K / 8 >= (1ull << 31))
         return (int)hipErrorInvalidValue;
     const int G = K / kGroup;
     const int gsplit = (G + s - 1) / s;
     float* part = static_cast<float*>(workspace);
-    int err = launch_w4p(x, qweight, scales, zeros, y, part, M, N, K, s, gsplit, st);
+    int err = launch_w4p(x, qweight, scales, zeros, y, part, M, N, K, bits, s, gsplit, st);
     if (err) return err;
     const long long mn = (long long)M * N;
     const long long blocks = (mn / 4 + 1 + 255) / 256;
@@ -669,7 +701,7 @@ int launch_gemm_splitk(const void* x, const void* qweight, const void* scales, c
 }
 
 int launch_gemm(const void* x, const void* qweight, const void* scales, const void* zeros,
-                void* y, int M, int N, int K, hipStream_t st) {
+                void* y, int M, int N, int K, int bits, hipStream_t st) {
     // the kernel uses 32-bit element offsets into x and into the packed tiles
     if ((unsigned long long)M * K >= (1ull << 31) || (unsigned long long)N * K / 8 >= (1ull << 31))
         return (int)hipErrorInvalidValue;
@@ -679,8 +711,9 @@ int launch_gemm(const void* x, const void* qweight, const void* scales, const vo
     // whose 2 x CUs slots round the tile count better (MI355X, M = 2048:
     // 14336x4096 (256 tiles) 974 vs 743 TFLOP/s; 4096x14336 (896 tiles) 764 vs
     // 816; 4096x6144 (384 tiles) 739 vs 849).
-    if (nT <= device_cu_count()) {
-        return launch_w4p(x, qweight, scales, zeros, y, nullptr, M, N, K, 1, K / kGroup, st);
+    // int3 has the pipelined kernel only
+    if (bits == 3 || nT <= device_cu_count()) {
+        return launch_w4p(x, qweight, scales, zeros, y, nullptr, M, N, K, bits, 1, K / kGroup, st);
     } else {
         hipLaunchKernelGGL(k_gemm_w4, dim3(nT), dim3(256), 0, st, (const _Float16*)x,
                            (const uint32_t*)qweight, (const _Float16*)scales, (const _Float16*)zeros,
