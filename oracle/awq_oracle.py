@@ -43,7 +43,8 @@ from __future__ import annotations
 import numpy as np
 
 # Parameters named as on the pages ([P4] quant_config, [P3] quantization_config).
-GROUP_SIZE = 128
+GROUP_SIZE = 128                   # default group; also the K width of a packed tile
+SUPPORTED_GROUP_SIZES = (64, 128)  # [P4] "Quantizing a model with AutoAWQ": typical 64, 128
 SUPPORTED_BITS = (3, 4)
 SPAN_FLOOR = np.float32(1e-5)      # reading: (hi - lo), or max |v|, floored before the divide
 STAT_FLOOR = 1e-4                  # reading: s_x floored before the power
@@ -137,8 +138,8 @@ def quantize_values(v: np.ndarray, bits: int = 4, group_size: int = GROUP_SIZE,
                     zero_point: bool = True):
     """Group quantizer on already-scaled fp32 values v [N][K].
 
-    Per (row n, group g of 128 consecutive k), all in IEEE fp32, with
-    zero_point (asymmetric):
+    Per (row n, group g of group_size (128 or 64) consecutive k), all in
+    IEEE fp32, with zero_point (asymmetric):
         lo  = min(0, min v),  hi = max(0, max v)
         D32 = max(hi - lo, 1e-5) / Q ;  Dh = largest fp16 <= D32 ;  D = Dh
         z   = clamp(rint(-lo / D), 0, Q)
@@ -157,8 +158,8 @@ def quantize_values(v: np.ndarray, bits: int = 4, group_size: int = GROUP_SIZE,
     if v.dtype != np.float32 or v.ndim != 2:
         raise ValueError("v must be a 2-D float32 array [N][K]")
     N, K = v.shape
-    if group_size != GROUP_SIZE or K % group_size != 0:
-        raise ValueError("K must be a multiple of the group size 128")
+    if group_size not in SUPPORTED_GROUP_SIZES or K % group_size != 0:
+        raise ValueError("group_size must be 64 or 128 and divide K")
     G = K // group_size
     g = v.reshape(N, G, group_size)
 
@@ -237,7 +238,8 @@ def pack_rows(q: np.ndarray, bits: int) -> np.ndarray:
 
 
 def pack(q: np.ndarray, bits: int) -> np.ndarray:
-    """Packed weights, format 2: tiles of 16 rows x one 128-code group.
+    """Packed weights, format 2: tiles of 16 rows x 128 codes (one 128-group or
+    two 64-groups; the codes' layout does not depend on the group size).
 
     The row words of ``pack_rows`` are regrouped so that the 16 rows of
     block b and the group g form one contiguous tile of 64 lane slots:
@@ -336,9 +338,9 @@ def matmul(x: np.ndarray, qweight: np.ndarray, scales: np.ndarray,
     [P1] feature list: the 4-bit linear layer and its context (GEMM) and
     decode (GEMV) kernels compute this one product.
     """
-    N = np.asarray(scales).shape[0]
+    N, G = np.asarray(scales).shape
     q = unpack_fast(qweight, bits, K, N)
-    w_hat = dequantize(q, scales, zeros)
+    w_hat = dequantize(q, scales, zeros, K // G)        # group size from the [N][G] parameters
     return np.asarray(x, dtype=np.float16).astype(np.float64) @ w_hat.T
 
 
@@ -387,7 +389,7 @@ def matmul_rows(x: np.ndarray, qweight: np.ndarray, scales: np.ndarray,
     sel = t[blk, :, :, j, :]                                   # [len(rows)][G][h][i]
     q = unpack_fast(sel[:, :, :, None, :].repeat(ROW_BLOCK, axis=3), bits, K)
     q = q.reshape(len(rows), ROW_BLOCK, K)[:, 0, :]
-    w_hat = dequantize(q, scales[rows], zeros[rows])
+    w_hat = dequantize(q, scales[rows], zeros[rows], K // np.asarray(scales).shape[1])
     return np.asarray(x, dtype=np.float16).astype(np.float64) @ w_hat.T
 
 
@@ -431,9 +433,9 @@ def search_scale(W: np.ndarray, X_cal: np.ndarray, alphas, bits: int = 4,
 
 
 def awq_quantize_layer(W: np.ndarray, X_cal: np.ndarray, alphas, bits: int = 4,
-                       zero_point: bool = True):
+                       zero_point: bool = True, group_size: int = GROUP_SIZE):
     """Whole offline pass: search, then quantize and pack with the chosen s."""
-    s, losses, best = search_scale(W, X_cal, alphas, bits, zero_point=zero_point)
-    q, d, z = quantize(W, s, bits, zero_point=zero_point)
+    s, losses, best = search_scale(W, X_cal, alphas, bits, group_size, zero_point)
+    q, d, z = quantize(W, s, bits, group_size, zero_point)
     return {"s": s, "losses": losses, "best": best,
             "qweight": pack(q, bits), "scales": d, "zeros": z, "q": q}
