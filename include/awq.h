@@ -1,5 +1,6 @@
 /*
- * awq.h -- C ABI of the AWQ W4A16 g128 hot path for MI355X (gfx950).
+ * awq.h -- C ABI of the AWQ W4A16 g128 hot path for MI355X (gfx950)
+ * (also W3A16, and 64-wide groups).
  *
  * What the calls compute is set by these web pages (cited by title and
  * section; no code is taken from them):
@@ -21,8 +22,10 @@
  * Conventions shared by every call
  *   - Math: y = x . W^T.  W is fp16 [N][K] (output x input, row-major),
  *     x is fp16 [M][K], y is fp16 [M][N].  Groups of group_size = 128
- *     consecutive k share one fp16 scale D and one integer zero point z;
- *     G = K / 128.  Q = 2^bits - 1.
+ *     (or 64: "Quantizing a model with AutoAWQ" gives 64 and 128 as typical
+ *     q_group_size values) consecutive k share one fp16 scale D and one
+ *     integer zero point z; G = K / group_size.  Q = 2^bits - 1.  K must be
+ *     a multiple of 128 for either group size (a packed tile spans 128 k).
  *   - Pointers are DEVICE pointers (HBM) allocated by the caller, 16-byte
  *     aligned, unless a comment says HOST.  The library never allocates or
  *     frees and keeps nothing after a call returns; scratch memory comes only
@@ -43,17 +46,19 @@
  *     k = 32c..32c+31 is a 96-bit little-endian bit stream (code i at stream
  *     bits 3i..3i+2) held in 3 words.
  *   Tiles.  Rows are taken 16 at a time (row block b = rows 16b..16b+15,
- *     padded with zero rows past N).  Tile (b, g) holds group g (k = 128g ..
- *     128g+127) of the 16 rows of block b as 64 lane slots; slot s = 16h + j
- *     holds the row words of row 16b + j that cover k = 128g + 32h ..
- *     128g + 32h + 31 (4 words for bits 4, 3 for bits 3).  qweight is the
- *     array of tiles [ceil(N/16)][G][64][4 or 3] uint32: one tile is one
+ *     padded with zero rows past N).  Tile (b, t) holds k = 128t .. 128t+127
+ *     of the 16 rows of block b as 64 lane slots; slot s = 16h + j holds the
+ *     row words of row 16b + j that cover k = 128t + 32h .. 128t + 32h + 31
+ *     (4 words for bits 4, 3 for bits 3).  The codes' layout does not depend
+ *     on the group size.  qweight is the array of tiles
+ *     [ceil(N/16)][K/128][64][4 or 3] uint32: one tile is one
  *     contiguous 1 KB (768 B for bits 3) wave load whose slots are the
  *     v_mfma_f32_16x16x32_f16 operand layout.
  *   scales, zeros: fp16 [ceil(N/16)][G][16], the same tiling: the group
  *     scale D[n][g] and the integer zero point z[n][g] (0..Q, stored
  *     exactly) of row n sit at [n / 16][g][n % 16]; padding rows hold 0.
- *     One group's 16 scales are one 32-byte load next to their tile.
+ *     One group's 16 scales are one 32-byte load next to their tile (with
+ *     64-wide groups a tile's two groups are g = 2t, 2t + 1).
  *   Dequantized weight: w_hat[n][k] = (q[n][k] - z[n][g]) * D[n][g].
  */
 #ifndef AWQ_MI355X_H
@@ -108,7 +113,7 @@ size_t awq_packed_words(int N, int K, int bits);
  *     (2^(bits-1) - 1), z = 2^(bits-1) (codes z - 7..z + 7 for int4)
  * all fp32 IEEE, round-half-even, correctly rounded division.  Either way
  * w_hat = (q - z) * D, so awq_gemv and awq_gemm serve both.
- * bits in {3, 4}; group_size must be 128; zero_point 0 or 1.
+ * bits in {3, 4}; group_size 128 or 64; zero_point 0 or 1.
  */
 int awq_quantize_pack(const void* W, const float* s, int N, int K, int bits,
                       int group_size, int zero_point, void* qweight,
@@ -160,7 +165,10 @@ int awq_search_scale(const void* W, const void* X_cal, int T, int N, int K,
  *   y[m][n] = sum_g D[n][g] * sum_{k in g} x[m][k] * (q[n][k] - z[n][g])
  *   x fp16 [M][K] in; qweight, scales, zeros as produced by
  *   awq_quantize_pack; y fp16 [M][N] out (round to nearest from fp32).
- *   1 <= M <= 16; bits in {3, 4}; group_size 128.  The packed weight must
+ *   1 <= M <= 16; bits in {3, 4}; group_size 128 or 64 (as packed).  With
+ *   64-wide groups each weight is dequantized to fp16 (q - z) * D before the
+ *   product (one rounding); with 128 the group sums are scaled in fp32.
+ *   The packed weight must
  *   be < 2^31 bytes (16 * ceil(N/16) * K * bits / 8) and x < 2^31 bytes
  *   (M * K * 2), else AWQ_ERR_SHAPE.
  */
@@ -173,7 +181,7 @@ int awq_gemv(const void* x, const void* qweight, const void* scales,
  * awq_gemv for any M >= 1 (the context kernel of the llm-awq README
  * feature list; version "gemm" in the transformers quantization_config).
  * Dequantized fp16 tiles feed fp16 MFMA with fp32 accumulation.
- *   bits in {3, 4}; group_size 128; M*K < 2^31 and N*K/8 < 2^31 (else
+ *   bits in {3, 4}; group_size 128 or 64; M*K < 2^31 and N*K/8 < 2^31 (else
  *   AWQ_ERR_SHAPE).
  */
 int awq_gemm(const void* x, const void* qweight, const void* scales,

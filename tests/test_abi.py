@@ -81,7 +81,8 @@ def qp(lib, W=P, s=NUL, N=256, K=512, bits=4, gs=128, zp=1, qw=P2, sc=P3, ze=P4)
 def test_quantize_pack_validation(lib):
     assert qp(lib, bits=2) == UNSUP
     assert qp(lib, bits=8) == UNSUP
-    assert qp(lib, gs=64) == UNSUP
+    assert qp(lib, gs=32) == UNSUP
+    assert qp(lib, gs=64, W=NUL) == NULL            # 64-wide groups are supported
     assert qp(lib, zp=2) == UNSUP
     assert qp(lib, zp=0, W=NUL) == NULL            # zero_point 0 (symmetric) is supported
     assert qp(lib, K=500) == SHAPE
@@ -103,6 +104,7 @@ def mm(lib, fn, x=P, qw=P2, sc=P3, ze=P4, y=P5, M=1, N=256, K=512, bits=4, gs=12
 def test_matmul_validation(lib, fn):
     assert mm(lib, fn, bits=5) == UNSUP
     assert mm(lib, fn, gs=32) == UNSUP
+    assert mm(lib, fn, gs=64, x=NUL) == NULL
     assert mm(lib, fn, K=129) == SHAPE
     assert mm(lib, fn, N=-4) == SHAPE
     assert mm(lib, fn, M=-1) == SHAPE

@@ -15,11 +15,11 @@ from gpu_util import TOL, announce, dev, guarded_empty, host, rel_err, sentinel_
 pytestmark = pytest.mark.gpu
 
 
-def packed(W, bits, s=None, chunk=2048):
+def packed(W, bits, s=None, chunk=2048, group_size=128):
     """Oracle quantize + pack, in row chunks to bound host memory."""
     parts = []
     for r in range(0, W.shape[0], chunk):
-        q, d, z = O.quantize(W[r:r + chunk], s, bits)
+        q, d, z = O.quantize(W[r:r + chunk], s, bits, group_size)
         parts.append((O.pack(q, bits), d, z))
     return tuple(np.concatenate([p[i] for p in parts]) for i in range(3))
 
@@ -37,22 +37,22 @@ def workload_layer(w, shape_index, bits=4):
     return _CACHE[key]
 
 
-def run(fn, x, qw, d, z, N, bits):
+def run(fn, x, qw, d, z, N, bits, group_size=128):
     import torch
     y = getattr(awq, fn)(dev(x), dev(qw.reshape(-1)), dev(O.tile_params(d)), dev(O.tile_params(z)),
-                         N=N, bits=bits)
+                         N=N, bits=bits, group_size=group_size)
     torch.cuda.synchronize()
     return host(y).astype(np.float64)
 
 
-def check(fn, M, N, K, bits, seed, sigma=1.0, rows=None, layer=None, x=None):
-    announce(fn, f"M={M} N={N} K={K} bits={bits} seed={seed}")
+def check(fn, M, N, K, bits, seed, sigma=1.0, rows=None, layer=None, x=None, group_size=128):
+    announce(fn, f"M={M} N={N} K={K} bits={bits} group_size={group_size} seed={seed}")
     if layer is None:
-        qw, d, z = packed(WL.random_weights(N, K, seed=seed), bits)
+        qw, d, z = packed(WL.random_weights(N, K, seed=seed), bits, group_size=group_size)
     else:
         _, qw, d, z = layer
     x = WL.random_activations(M, K, seed=seed + 1, sigma=sigma) if x is None else x
-    y = run(fn, x, qw, d, z, N, bits)
+    y = run(fn, x, qw, d, z, N, bits, group_size)
     if rows is None:
         y_ref = O.matmul(x, qw, d, z, bits, K)
         err = rel_err(y, y_ref)
@@ -100,6 +100,19 @@ def test_gemv_sliced_two_blocks_per_workgroup(gpu, M):
     rng = np.random.default_rng(M)
     rows = np.concatenate([[0, 15, 16, N - 1], rng.choice(N, 60, replace=False)])
     check("gemv", M, N, K, 4, seed=31 + M, rows=rows)
+
+
+# ----------------------------------------------------------------------------- 64-wide groups
+@pytest.mark.parametrize("bits", [4, 3])
+@pytest.mark.parametrize("fn,M,N,K", [
+    ("gemv", 1, 300, 4096),        # x staged once, short rows (ring of 2)
+    ("gemv", 4, 130, 11008),       # 4 x 11008 > 32K halves: K in slices, ragged last slice
+    ("gemv", 16, 1000, 2048),      # K slices, one 16-group slice
+    ("gemm", 5, 302, 2048),        # split K
+    ("gemm", 257, 200, 1152),      # several M tiles, no split
+])
+def test_group64_matmuls(gpu, fn, M, N, K, bits):
+    check(fn, M, N, K, bits, seed=400 + M + N, group_size=64)
 
 
 # ----------------------------------------------------------------------------- GEMM

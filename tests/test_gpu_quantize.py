@@ -11,29 +11,29 @@ from gpu_util import announce, dev, guarded_empty, host, sentinel_intact
 pytestmark = pytest.mark.gpu
 
 
-def _check_rows(W, s, bits, rows=None, zero_point=True):
+def _check_rows(W, s, bits, rows=None, zero_point=True, group_size=128):
     """GPU quantize_pack of the whole W; oracle on `rows` (all if None)."""
     import torch
     N, K = W.shape
     announce("quantize_pack", f"N={N} K={K} bits={bits} s={'yes' if s is not None else 'no'} "
-                              f"zero_point={zero_point}")
+                              f"zero_point={zero_point} group_size={group_size}")
     qw, sc, ze = awq.quantize_pack(dev(W), None if s is None else dev(s), bits=bits,
-                                   zero_point=zero_point)
+                                   group_size=group_size, zero_point=zero_point)
     torch.cuda.synchronize()
     words = host(qw).view(np.uint32)
     if rows is None:
-        q, d, z = O.quantize(W, s, bits, zero_point=zero_point)
+        q, d, z = O.quantize(W, s, bits, group_size, zero_point)
         assert np.array_equal(words, O.pack(q, bits).ravel()), "packed tiles differ"
         rows = np.arange(N)
     else:
         rows = np.asarray(rows)
-        q, d, z = O.quantize(W[rows], s, bits, zero_point=zero_point)
+        q, d, z = O.quantize(W[rows], s, bits, group_size, zero_point)
         assert words.size == O.packed_words(N, K, bits)
         got_rows = O.tiles_to_rows(words, bits, K)
         assert np.array_equal(got_rows[rows], O.pack_rows(q, bits)), "packed codes differ"
         assert not got_rows[N:].any(), "padding rows not zero"
     sc_h, ze_h = host(sc), host(ze)
-    assert sc_h.shape == ((N + 15) // 16, K // 128, 16)
+    assert sc_h.shape == ((N + 15) // 16, K // group_size, 16)
     assert not O.untile_params(sc_h, sc_h.shape[0] * 16)[N:].any(), "padding scales not zero"
     sc_rows, ze_rows = O.untile_params(sc_h, N)[rows], O.untile_params(ze_h, N)[rows]
     assert np.array_equal(sc_rows.view(np.uint16), d.view(np.uint16)), "scales differ"
@@ -56,6 +56,16 @@ def test_ragged_shapes(gpu, bits, N, K, zero_point):
     W = WL.random_weights(N, K, seed=N * 7 + K)
     s = np.random.default_rng(K).lognormal(0, 1.5, K).astype(np.float32)
     _check_rows(W, s, bits, zero_point=zero_point)
+
+
+@pytest.mark.parametrize("zero_point", [True, False])
+@pytest.mark.parametrize("bits", [4, 3])
+@pytest.mark.parametrize("N,K", [(1, 128), (37, 384), (129, 11008)])
+def test_group64(gpu, bits, N, K, zero_point):
+    W = WL.random_weights(N, K, seed=N * 5 + K)
+    W[:, 64:128] *= 8                                # the two groups of tile 0 on different scales
+    s = np.random.default_rng(K + 1).lognormal(0, 1.5, K).astype(np.float32)
+    _check_rows(W, s, bits, zero_point=zero_point, group_size=64)
 
 
 @pytest.mark.parametrize("zero_point", [True, False])

@@ -19,17 +19,19 @@ from gpu_util import TOL, announce, dev, host, rel_err
 pytestmark = pytest.mark.gpu
 
 
-def gpu_search(W, X, alphas, bits, zero_point=True):
+def gpu_search(W, X, alphas, bits, zero_point=True, group_size=128):
     import torch
-    s, loss, best = awq.search_scale(dev(W), dev(X), alphas, bits=bits, zero_point=zero_point)
+    s, loss, best = awq.search_scale(dev(W), dev(X), alphas, bits=bits, group_size=group_size,
+                                     zero_point=zero_point)
     torch.cuda.synchronize()
     return host(s), host(loss).astype(np.float64), int(host(best)[0])
 
 
-def check_search(W, X, alphas, bits, zero_point=True):
-    announce("search_scale", W.shape, X.shape, len(alphas), bits, f"zero_point={zero_point}")
-    s_g, loss_g, best_g = gpu_search(W, X, alphas, bits, zero_point)
-    s_r, loss_r, best_r = O.search_scale(W, X, alphas, bits, zero_point=zero_point)
+def check_search(W, X, alphas, bits, zero_point=True, group_size=128):
+    announce("search_scale", W.shape, X.shape, len(alphas), bits, f"zero_point={zero_point}",
+             f"group_size={group_size}")
+    s_g, loss_g, best_g = gpu_search(W, X, alphas, bits, zero_point, group_size)
+    s_r, loss_r, best_r = O.search_scale(W, X, alphas, bits, group_size, zero_point)
     assert np.allclose(loss_g, loss_r, rtol=1e-2, atol=0), (loss_g, loss_r)
     assert best_g == best_r or loss_r[best_g] <= (1 + 1e-3) * loss_r[best_r], (best_g, best_r)
     s_expect = O.candidate_scale(O.act_stat(X), alphas[best_g])
@@ -57,6 +59,13 @@ def test_ragged_search(gpu):
     W = WL.random_weights(77, 384, seed=4)
     X = WL.random_activations(100, 384, seed=5, sigma=1.5)
     check_search(W, X, [0.0, 0.3, 0.6, 0.9], 4)
+
+
+@pytest.mark.parametrize("zero_point", [True, False])
+def test_group64_search(gpu, zero_point):
+    W = WL.random_weights(77, 384, seed=14)
+    X = WL.random_activations(100, 384, seed=15, sigma=1.5)
+    check_search(W, X, [0.0, 0.25, 0.5, 0.75], 4, zero_point, group_size=64)
 
 
 @pytest.mark.parametrize("bits", [4, 3])

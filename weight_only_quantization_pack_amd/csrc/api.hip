@@ -25,7 +25,7 @@ int check_ptrs(std::initializer_list<const void*> ps) {
 
 int check_quant_params(int bits, int group_size, int zero_point) {
     if (bits != 3 && bits != 4) return AWQ_ERR_UNSUPPORTED;
-    if (group_size != awq::kGroup) return AWQ_ERR_UNSUPPORTED;
+    if (group_size != 128 && group_size != 64) return AWQ_ERR_UNSUPPORTED;
     if (zero_point != 0 && zero_point != 1) return AWQ_ERR_UNSUPPORTED;
     return AWQ_OK;
 }
@@ -77,7 +77,7 @@ int awq_quantize_pack(const void* W, const float* s, int N, int K, int bits, int
     if (N == 0) return AWQ_OK;
     if ((st = check_ptrs({W, qweight, scales, zeros}))) return st;
     if (s != nullptr && (st = check_ptr(s))) return st;
-    return hip_status(awq::launch_quantize_pack(W, s, N, K, bits, zero_point, qweight, scales, zeros,
+    return hip_status(awq::launch_quantize_pack(W, s, N, K, bits, group_size, zero_point, qweight, scales, zeros,
                                                 (hipStream_t)stream));
 }
 
@@ -109,7 +109,7 @@ int awq_search_scale(const void* W, const void* X_cal, int T, int N, int K, cons
     if (loss_out != nullptr && (st = check_ptr(loss_out))) return st;
     if (best_out != nullptr && (st = check_ptr(best_out))) return st;
     if (workspace_bytes < awq::search_workspace_bytes(T, N, K, n_alpha)) return AWQ_ERR_WORKSPACE;
-    return hip_status(awq::launch_search(W, X_cal, T, N, K, alphas, n_alpha, bits, zero_point, s_out,
+    return hip_status(awq::launch_search(W, X_cal, T, N, K, alphas, n_alpha, bits, group_size, zero_point, s_out,
                                          loss_out, best_out, workspace, (hipStream_t)stream));
 }
 
@@ -126,7 +126,7 @@ int awq_gemv(const void* x, const void* qweight, const void* scales, const void*
         return AWQ_ERR_SHAPE;
     if (M == 0 || N == 0) return AWQ_OK;
     if ((st = check_ptrs({x, qweight, scales, zeros, y}))) return st;
-    return hip_status(awq::launch_gemv(x, qweight, scales, zeros, y, M, N, K, bits,
+    return hip_status(awq::launch_gemv(x, qweight, scales, zeros, y, M, N, K, bits, group_size,
                                        (hipStream_t)stream));
 }
 
@@ -140,7 +140,7 @@ int awq_gemm(const void* x, const void* qweight, const void* scales, const void*
     if ((long long)M * K >= (1LL << 31) || (long long)N * K / 8 >= (1LL << 31)) return AWQ_ERR_SHAPE;
     if (M == 0 || N == 0) return AWQ_OK;
     if ((st = check_ptrs({x, qweight, scales, zeros, y}))) return st;
-    return hip_status(awq::launch_gemm(x, qweight, scales, zeros, y, M, N, K, bits,
+    return hip_status(awq::launch_gemm(x, qweight, scales, zeros, y, M, N, K, bits, group_size,
                                        (hipStream_t)stream));
 }
 
@@ -166,7 +166,7 @@ int awq_gemm_splitk(const void* x, const void* qweight, const void* scales, cons
         if (workspace_bytes < need) return AWQ_ERR_WORKSPACE;
     }
     return hip_status(awq::launch_gemm_splitk(x, qweight, scales, zeros, y, M, N, K, bits,
-                                              workspace, (hipStream_t)stream));
+                                              group_size, workspace, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -14,7 +14,7 @@
 
 namespace awq {
 
-constexpr int kGroup = 128;          // q_group_size
+constexpr int kGroup = 128;          // codes per packed tile, and the default q_group_size
 constexpr int kWave = 64;            // CDNA wavefront width
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -111,29 +111,30 @@ __device__ __forceinline__ uint32_t quant_code(float v, const GroupParams& p) {
 // host-side launchers (each .hip file owns its kernels); they return 0 or a
 // hipError_t value.  Arguments have been validated by the C ABI layer.
 // ---------------------------------------------------------------------------
-int launch_quantize_pack(const void* W, const float* s, int N, int K, int bits, int zero_point,
-                         void* qweight, void* scales, void* zeros, hipStream_t st);
+int launch_quantize_pack(const void* W, const float* s, int N, int K, int bits, int group_size,
+                         int zero_point, void* qweight, void* scales, void* zeros, hipStream_t st);
 int launch_scale_activations(const void* x, const float* s, void* x_out, int M, int K,
                              hipStream_t st);
 // compute units of the current device
 int device_cu_count();
 
 int launch_gemv(const void* x, const void* qweight, const void* scales, const void* zeros,
-                void* y, int M, int N, int K, int bits, hipStream_t st);
+                void* y, int M, int N, int K, int bits, int group_size, hipStream_t st);
 int launch_gemm(const void* x, const void* qweight, const void* scales, const void* zeros,
-                void* y, int M, int N, int K, int bits, hipStream_t st);
+                void* y, int M, int N, int K, int bits, int group_size, hipStream_t st);
 // split-K prefill: number of K splits for this shape on the current device
 // (1: no split, no workspace) and the fp32 partial workspace it needs
 int gemm_splits(int M, int N, int K);
 size_t gemm_splitk_workspace_bytes(int M, int N, int K);
 int launch_gemm_splitk(const void* x, const void* qweight, const void* scales, const void* zeros,
-                       void* y, int M, int N, int K, int bits, void* workspace, hipStream_t st);
+                       void* y, int M, int N, int K, int bits, int group_size, void* workspace,
+                       hipStream_t st);
 size_t search_workspace_bytes(int T, int N, int K, int n_alpha);
 size_t loss_gemm_tiles(int T, int N);
 int launch_loss_gemm(const void* X, const void* D, int T, int N, int K, int n_batch,
                      double* partials, hipStream_t st);
 int launch_search(const void* W, const void* X_cal, int T, int N, int K, const float* alphas,
-                  int n_alpha, int bits, int zero_point, float* s_out, float* loss_out,
-                  int* best_out, void* workspace, hipStream_t st);
+                  int n_alpha, int bits, int group_size, int zero_point, float* s_out,
+                  float* loss_out, int* best_out, void* workspace, hipStream_t st);
 
 }  // namespace awq

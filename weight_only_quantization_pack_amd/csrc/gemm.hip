@@ -410,7 +410,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(
 // Split K (part != nullptr): workgroup (tile, blockIdx.y) covers groups
 // [blockIdx.y * gsplit, +gsplit) and writes its fp32 partial tile to
 // part[blockIdx.y][M][N]; k_splitk_reduce adds the splits in order.
-template <int BITS, int S>
+template <int BITS, int GS, int S>
 __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
     const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
@@ -423,8 +423,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, hq = lane >> 4;
     const int G = K / kGroup;
-    const int g_begin = (int)blockIdx.y * gsplit;      // this workgroup's groups: [g_begin, g_begin + GS)
-    const int GS = min(G - g_begin, gsplit);
+    const int g_begin = (int)blockIdx.y * gsplit;      // this workgroup's groups: [g_begin, g_begin + NGS)
+    const int NGS = min(G - g_begin, gsplit);
     const int NB = (N + 15) / 16;
     const int nTn = (N + GN - 1) / GN, nTm = (M + GM - 1) / GM;
     const int nT = nTn * nTm;
@@ -448,13 +448,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
         tbase[c] = (uint32_t)blk * (uint32_t)G;
     }
     const uint32_t psh = 16u * (uint32_t)(j & 1);      // the lane's half of a parameter word
+    // scales / zeros [block][group][16]: kGroup / GS groups per tile; with
+    // 64-wide groups a lane's quarter hq selects the tile's first or second
+    const uint32_t pgrp = GS == 64 ? (uint32_t)(hq >> 1) : 0u;
 
     constexpr int WQ = BITS == 4 ? 4 : 3;              // words per lane slot
     struct BStage { uint32_t q[4][WQ]; uint32_t d[4], z[4]; };
     // part p (0..3) of step kt's loads: A rows groups 2p, 2p + 1 (direct to LDS
     // buffer `slot`), B tile p of this wave and its scale and zero words
     auto issue_part = [&](int kt, int slot, BStage& bs, int p) {
-        const uint32_t g = (uint32_t)(g_begin + min(kt, GS - 1));
+        const uint32_t g = (uint32_t)(g_begin + min(kt, NGS - 1));
 #pragma unroll
         for (int i = 2 * p; i < 2 * p + 2; ++i) {
             const int rg = wave * 8 + i;
@@ -470,8 +473,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
             const uint3 v = *reinterpret_cast<const uint3*>(qw + (size_t)(tt * 192u + 3u * lane));
             bs.q[p][0] = v.x; bs.q[p][1] = v.y; bs.q[p][2] = v.z;
         }
-        bs.d[p] = *reinterpret_cast<const uint32_t*>(scales + tt * 16u + (uint32_t)(j & ~1));
-        bs.z[p] = *reinterpret_cast<const uint32_t*>(zeros + tt * 16u + (uint32_t)(j & ~1));
+        const uint32_t pidx = (tt * (kGroup / GS) + pgrp) * 16u + (uint32_t)(j & ~1);
+        bs.d[p] = *reinterpret_cast<const uint32_t*>(scales + pidx);
+        bs.z[p] = *reinterpret_cast<const uint32_t*>(zeros + pidx);
     };
     auto issue = [&](int kt, int slot, BStage& bs) {
 #pragma unroll
@@ -557,7 +561,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
         issue(s, s, bs[s]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // GS >= 1; a loop without an entry test keeps the compiler from sinking the
+    // NGS >= 1; a loop without an entry test keeps the compiler from sinking the
     // prologue's register loads behind one (out of the order above)
     int kt0 = 0;
     do {
@@ -575,10 +579,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
             __builtin_amdgcn_sched_barrier(0);
             // the last round may run past G: those steps keep the load stream
             // (and so the compiler's wait counts) uniform but compute nothing
-            if (kt < GS) compute(bs[st], As + st * ABUF);
+            if (kt < NGS) compute(bs[st], As + st * ABUF);
         }
         kt0 += S;
-    } while (kt0 < GS);
+    } while (kt0 < NGS);
 
     if (part != nullptr) {
         float* prow0 = part + (size_t)blockIdx.y * M * N;
@@ -649,10 +653,13 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 constexpr int kGemmStages = 4;
 
 int launch_w4p(const void* x, const void* qweight, const void* scales, const void* zeros, void* y,
-               float* part, int M, int N, int K, int bits, int splits, int gsplit, hipStream_t st) {
+               float* part, int M, int N, int K, int bits, int group_size, int splits, int gsplit,
+               hipStream_t st) {
     const int nT = ((N + w4::GN - 1) / w4::GN) * ((M + w4::GM - 1) / w4::GM);
     const size_t lds = (size_t)kGemmStages * w4::ABUF;
-    auto kern = bits == 4 ? k_gemm_w4p<4, kGemmStages> : k_gemm_w4p<3, kGemmStages>;
+    auto kern = group_size == 64
+                    ? (bits == 4 ? k_gemm_w4p<4, 64, kGemmStages> : k_gemm_w4p<3, 64, kGemmStages>)
+                    : (bits == 4 ? k_gemm_w4p<4, 128, kGemmStages> : k_gemm_w4p<3, 128, kGemmStages>);
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return (int)e;
@@ -683,15 +690,16 @@ size_t gemm_splitk_workspace_bytes(int M, int N, int K) {
 }
 
 int launch_gemm_splitk(const void* x, const void* qweight, const void* scales, const void* zeros,
-                       void* y, int M, int N, int K, int bits, void* workspace, hipStream_t st) {
+                       void* y, int M, int N, int K, int bits, int group_size, void* workspace,
+                       hipStream_t st) {
     const int s = gemm_splits(M, N, K);
-    if (s <= 1) return launch_gemm(x, qweight, scales, zeros, y, M, N, K, bits, st);
+    if (s <= 1) return launch_gemm(x, qweight, scales, zeros, y, M, N, K, bits, group_size, st);
     if ((unsigned long long)M * K >= (1ull << 31) || (unsigned long long)N * K / 8 >= (1ull << 31))
         return (int)hipErrorInvalidValue;
     const int G = K / kGroup;
     const int gsplit = (G + s - 1) / s;
     float* part = static_cast<float*>(workspace);
-    int err = launch_w4p(x, qweight, scales, zeros, y, part, M, N, K, bits, s, gsplit, st);
+    int err = launch_w4p(x, qweight, scales, zeros, y, part, M, N, K, bits, group_size, s, gsplit, st);
     if (err) return err;
     const long long mn = (long long)M * N;
     const long long blocks = (mn / 4 + 1 + 255) / 256;
@@ -701,7 +709,7 @@ int launch_gemm_splitk(const void* x, const void* qweight, const void* scales, c
 }
 
 int launch_gemm(const void* x, const void* qweight, const void* scales, const void* zeros,
-                void* y, int M, int N, int K, int bits, hipStream_t st) {
+                void* y, int M, int N, int K, int bits, int group_size, hipStream_t st) {
     // the kernel uses 32-bit element offsets into x and into the packed tiles
     if ((unsigned long long)M * K >= (1ull << 31) || (unsigned long long)N * K / 8 >= (1ull << 31))
         return (int)hipErrorInvalidValue;
@@ -711,9 +719,10 @@ int launch_gemm(const void* x, const void* qweight, const void* scales, const vo
     // whose 2 x CUs slots round the tile count better (MI355X, M = 2048:
     // 14336x4096 (256 tiles) 974 vs 743 TFLOP/s; 4096x14336 (896 tiles) 764 vs
     // 816; 4096x6144 (384 tiles) 739 vs 849).
-    // int3 has the pipelined kernel only
-    if (bits == 3 || nT <= device_cu_count()) {
-        return launch_w4p(x, qweight, scales, zeros, y, nullptr, M, N, K, bits, 1, K / kGroup, st);
+    // int3 and 64-wide groups have the pipelined kernel only
+    if (bits == 3 || group_size == 64 || nT <= device_cu_count()) {
+        return launch_w4p(x, qweight, scales, zeros, y, nullptr, M, N, K, bits, group_size, 1,
+                          K / kGroup, st);
     } else {
         hipLaunchKernelGGL(k_gemm_w4, dim3(nT), dim3(256), 0, st, (const _Float16*)x,
                            (const uint32_t*)qweight, (const _Float16*)scales, (const _Float16*)zeros,

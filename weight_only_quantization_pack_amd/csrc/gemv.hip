@@ -154,7 +154,12 @@ __device__ __forceinline__ _Float16 low_half(uint32_t v) {
 // a group with x (rows j >= M read row 0) as the A operand from LDS at xa and
 // the slot's exact (q - z) as the B operand; the group scale multiplies the
 // accumulator lanes of the lane's row.
-template <int BITS, int WQ>
+//
+// With 64-wide groups (GS = 64) one MFMA mixes both groups of the tile (its
+// k32 slice takes 8 codes from each quarter), so the lane multiplies its
+// operand by its own group's scale first: (q - z) * D rounded once to fp16,
+// and the MFMA accumulates straight into acc.
+template <int BITS, int WQ, int GS>
 __device__ __forceinline__ void accumulate_tile(const Slot<WQ>& w, const RawParams& p, const _Float16* xa,
                                                 uint32_t psh, float4_t& acc) {
     const _Float16 zh = low_half(p.z >> psh);
@@ -173,17 +178,35 @@ __device__ __forceinline__ void accumulate_tile(const Slot<WQ>& w, const RawPara
         bop[2] = dequant_24_int3((w1 >> 16) | ((w2 & 0xFFu) << 16), zz);
         bop[3] = dequant_24_int3(w2 >> 8, zz);
     }
-    float4_t accg = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (GS == 64) {
+        const _Float16 dh = low_half(p.d >> psh);
+        const half2_t dd = {dh, dh};
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-        accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const half8_t*>(xa + 8 * q), bop[q],
-                                                      accg, 0, 0, 0);
-    const float d = (float)low_half(p.d >> psh);
+        for (int q = 0; q < 4; ++q) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(d, accg[r], acc[r]);
+            for (int t = 0; t < 4; ++t) {
+                const half2_t v = (half2_t){bop[q][2 * t], bop[q][2 * t + 1]} * dd;
+                bop[q][2 * t] = v[0];
+                bop[q][2 * t + 1] = v[1];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const half8_t*>(xa + 8 * q), bop[q],
+                                                         acc, 0, 0, 0);
+    } else {
+        float4_t accg = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const half8_t*>(xa + 8 * q), bop[q],
+                                                          accg, 0, 0, 0);
+        const float d = (float)low_half(p.d >> psh);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(d, accg[r], acc[r]);
+    }
 }
 
-template <int BITS, int WK, int U, int XL>
+template <int BITS, int GS, int WK, int U, int XL>
 __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qweight,
     const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
@@ -207,13 +230,17 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
     // the launcher guarantees every buffer is < 2^31 bytes
     const uint32_t tiles = (uint32_t)NB * (uint32_t)G;
     const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(qweight, tiles * 64u * WQ * 4u);
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scales, tiles * 32u);
-    const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(zeros, tiles * 32u);
+    // scales / zeros: [block][group][16], kGroup / GS groups per tile
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scales, tiles * (32u * kGroup / GS));
+    const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(zeros, tiles * (32u * kGroup / GS));
+    // this lane's parameter group within a tile: its quarter's (GS = 64)
+    const uint32_t pgrp = GS == 64 ? (uint32_t)(h >> 1) : 0u;
     auto load = [&](int b, int i, Slot<WQ>& w, RawParams& p) {
         const bool ok = b < NB && i < nw;
         const uint32_t t = (uint32_t)b * (uint32_t)G + (uint32_t)(wave + WK * i);
         const uint32_t oq = ok ? (t * 64u + (uint32_t)lane) * (WQ * 4u) : kBufferOutOfRange;
-        const uint32_t op = ok ? (t * 16u + (uint32_t)(j & ~1)) * 2u : kBufferOutOfRange;
+        const uint32_t op = ok ? ((t * (kGroup / GS) + pgrp) * 16u + (uint32_t)(j & ~1)) * 2u
+                               : kBufferOutOfRange;
         w = buffer_slot<WQ>(rq, oq);
         p.d = __builtin_amdgcn_raw_buffer_load_b32(rs, op, 0, 0);
         p.z = __builtin_amdgcn_raw_buffer_load_b32(rz, op, 0, 0);
@@ -268,7 +295,7 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
             for (int u = 0; u < U; ++u) {
                 const int i = i0 + u;
                 if (i < nw)                            // wave-uniform; loads stay outside
-                    accumulate_tile<BITS, WQ>(ring[u], pr[u], xa0 + (size_t)(wave + WK * i) * kGroup, psh, acc);
+                    accumulate_tile<BITS, WQ, GS>(ring[u], pr[u], xa0 + (size_t)(wave + WK * i) * kGroup, psh, acc);
                 // refill the slot with the item U places on (this block or the next)
                 const int k = i + U;
                 const bool here = k < nwp;
@@ -314,7 +341,7 @@ using GemvX1Fn = GemvX1FnT;
 // so the compiler's waits cover exactly one ring slot; the next slice's x is
 // loaded into registers during the current slice, ahead of its ring loads.
 // The waves' partial sums meet in LDS once per block at the end.
-template <int BITS, int WK, int U, int BMAX, int XL>
+template <int BITS, int GS, int WK, int U, int BMAX, int XL>
 __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_xs(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qweight,
     const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
@@ -337,8 +364,11 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_xs(
 
     const uint32_t tiles = (uint32_t)NB * (uint32_t)G;
     const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(qweight, tiles * 64u * WQ * 4u);
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scales, tiles * 32u);
-    const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(zeros, tiles * 32u);
+    // scales / zeros: [block][group][16], kGroup / GS groups per tile
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scales, tiles * (32u * kGroup / GS));
+    const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(zeros, tiles * (32u * kGroup / GS));
+    // this lane's parameter group within a tile: its quarter's (GS = 64)
+    const uint32_t pgrp = GS == 64 ? (uint32_t)(h >> 1) : 0u;
     const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
 
     // item (s, k, u): block blockIdx.x + k gridDim.x, group s SG + wave + WK u
@@ -348,7 +378,8 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_xs(
         const bool ok = b < NB && g < G;
         const uint32_t t = (uint32_t)b * (uint32_t)G + (uint32_t)g;
         const uint32_t oq = ok ? (t * 64u + (uint32_t)lane) * (WQ * 4u) : kBufferOutOfRange;
-        const uint32_t op = ok ? (t * 16u + (uint32_t)(j & ~1)) * 2u : kBufferOutOfRange;
+        const uint32_t op = ok ? ((t * (kGroup / GS) + pgrp) * 16u + (uint32_t)(j & ~1)) * 2u
+                               : kBufferOutOfRange;
         w = buffer_slot<WQ>(rq, oq);
         p.d = __builtin_amdgcn_raw_buffer_load_b32(rs, op, 0, 0);
         p.z = __builtin_amdgcn_raw_buffer_load_b32(rz, op, 0, 0);
@@ -404,7 +435,7 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_xs(
             for (int u = 0; u < U; ++u) {
                 const int g = s * SG + wave + WK * u;
                 if (blockIdx.x + k * gridDim.x < NB && g < G)    // wave-uniform
-                    accumulate_tile<BITS, WQ>(ring[u], pr[u], xa0 + (size_t)(wave + WK * u) * kGroup, psh, acc[k]);
+                    accumulate_tile<BITS, WQ, GS>(ring[u], pr[u], xa0 + (size_t)(wave + WK * u) * kGroup, psh, acc[k]);
                 // refill: the same group of the next block, or of the first block in the next slice
                 if (k + 1 < BMAX)
                     load(s, k + 1, u, ring[u], pr[u]);
@@ -444,34 +475,35 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_xs(
 constexpr int kGemvSliceRing = 2;                      // U of k_gemv_xs: slices of 16 groups
 
 using GemvXsFn = GemvX1FnT;
-template <int BITS, int BMAX>
+template <int BITS, int GS, int BMAX>
 GemvXsFn pick_xs_loads(int xl) {
-    if (xl <= 2) return k_gemv_xs<BITS, kGemvWaves, kGemvSliceRing, BMAX, 2>;
-    if (xl <= 4) return k_gemv_xs<BITS, kGemvWaves, kGemvSliceRing, BMAX, 4>;
-    return k_gemv_xs<BITS, kGemvWaves, kGemvSliceRing, BMAX, 8>;
+    if (xl <= 2) return k_gemv_xs<BITS, GS, kGemvWaves, kGemvSliceRing, BMAX, 2>;
+    if (xl <= 4) return k_gemv_xs<BITS, GS, kGemvWaves, kGemvSliceRing, BMAX, 4>;
+    return k_gemv_xs<BITS, GS, kGemvWaves, kGemvSliceRing, BMAX, 8>;
 }
-template <int BITS>
+template <int BITS, int GS>
 GemvXsFn pick_xs(int bmax, int xl) {
-    return bmax <= 1 ? pick_xs_loads<BITS, 1>(xl) : pick_xs_loads<BITS, 2>(xl);
+    return bmax <= 1 ? pick_xs_loads<BITS, GS, 1>(xl) : pick_xs_loads<BITS, GS, 2>(xl);
 }
 
 // k_gemv_x1 instance: ring depth (short rows: 2, else 4) and the number of
 // 16-byte x loads per lane that stage a wave's (group, row) pairs (<= 12:
 // M * K <= 32768 gives at most 48 pairs per wave)
-template <int BITS, int U>
+template <int BITS, int GS, int U>
 GemvX1Fn pick_x1_loads(int xl) {
-    if (xl <= 1) return k_gemv_x1<BITS, kGemvWaves, U, 1>;
-    if (xl <= 2) return k_gemv_x1<BITS, kGemvWaves, U, 2>;
-    if (xl <= 4) return k_gemv_x1<BITS, kGemvWaves, U, 4>;
-    if (xl <= 8) return k_gemv_x1<BITS, kGemvWaves, U, 8>;
-    return k_gemv_x1<BITS, kGemvWaves, U, 12>;
+    if (xl <= 1) return k_gemv_x1<BITS, GS, kGemvWaves, U, 1>;
+    if (xl <= 2) return k_gemv_x1<BITS, GS, kGemvWaves, U, 2>;
+    if (xl <= 4) return k_gemv_x1<BITS, GS, kGemvWaves, U, 4>;
+    if (xl <= 8) return k_gemv_x1<BITS, GS, kGemvWaves, U, 8>;
+    return k_gemv_x1<BITS, GS, kGemvWaves, U, 12>;
 }
-template <int BITS>
+template <int BITS, int GS>
 GemvX1Fn pick_x1(bool short_rows, int xl) {
-    return short_rows ? pick_x1_loads<BITS, kGemvRingShort>(xl) : pick_x1_loads<BITS, kGemvRingLong>(xl);
+    return short_rows ? pick_x1_loads<BITS, GS, kGemvRingShort>(xl)
+                      : pick_x1_loads<BITS, GS, kGemvRingLong>(xl);
 }
 
-template <int BITS>
+template <int BITS, int GS>
 int launch_bits(const void* x, const void* qweight, const void* scales, const void* zeros,
                 void* y, int M, int N, int K, hipStream_t st) {
     const int G = K / kGroup;
@@ -486,7 +518,7 @@ int launch_bits(const void* x, const void* qweight, const void* scales, const vo
     if ((size_t)M * (K + 8) * 2 <= (size_t)kGemvXBuf) {
         // x staged once; persistent workgroups (as many as fit on a CU by LDS,
         // at most kGemvCuWaves waves)
-        auto kern = pick_x1<BITS>(G <= 4 * kGemvWaves,
+        auto kern = pick_x1<BITS, GS>(G <= 4 * kGemvWaves,
                                   ((G + kGemvWaves - 1) / kGemvWaves * M + 3) / 4);   // x loads per lane
         if (x1_lds > 64 * 1024) {
             const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -507,7 +539,7 @@ int launch_bits(const void* x, const void* qweight, const void* scales, const vo
         const int per_cu = max(1, min(kGemvCuWaves / kGemvWaves, (int)((160 * 1024) / lds)));
         const int grid = max(min(NB, cus * per_cu), (NB + 1) / 2);
         const int bmax = (NB + grid - 1) / grid;
-        auto kern = pick_xs<BITS>(bmax, (kGemvSliceRing * M + 3) / 4);
+        auto kern = pick_xs<BITS, GS>(bmax, (kGemvSliceRing * M + 3) / 4);
         if (lds > 64 * 1024) {
             const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -532,9 +564,12 @@ int device_cu_count() {
 }
 
 int launch_gemv(const void* x, const void* qweight, const void* scales, const void* zeros,
-                void* y, int M, int N, int K, int bits, hipStream_t st) {
-    return bits == 4 ? launch_bits<4>(x, qweight, scales, zeros, y, M, N, K, st)
-                     : launch_bits<3>(x, qweight, scales, zeros, y, M, N, K, st);
+                void* y, int M, int N, int K, int bits, int group_size, hipStream_t st) {
+    if (group_size == 64)
+        return bits == 4 ? launch_bits<4, 64>(x, qweight, scales, zeros, y, M, N, K, st)
+                         : launch_bits<3, 64>(x, qweight, scales, zeros, y, M, N, K, st);
+    return bits == 4 ? launch_bits<4, 128>(x, qweight, scales, zeros, y, M, N, K, st)
+                     : launch_bits<3, 128>(x, qweight, scales, zeros, y, M, N, K, st);
 }
 
 }  // namespace awq

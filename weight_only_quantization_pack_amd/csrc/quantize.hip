@@ -1,9 +1,10 @@
 // Group quantization + packing (format 2) and the activation-side divide.
 //
-// What is computed: round-to-nearest asymmetric quantization of W*diag(s)
-// in groups of 128 input channels, with an fp16 scale and an integer zero
-// point per group ("Quantizing a model with AutoAWQ": w_bit, q_group_size,
-// zero_point; llm-awq README "Usage" step 3, real INT4 weights).
+// What is computed: round-to-nearest quantization of W*diag(s) in groups of
+// 128 (or 64) input channels, with an fp16 scale and an integer zero point
+// per group, asymmetric or symmetric ("Quantizing a model with AutoAWQ":
+// w_bit, q_group_size, zero_point; llm-awq README "Usage" step 3, real INT4
+// weights).
 //
 // Layout of the work: one wavefront per packed tile (16-row block b,
 // group g).  Lane slot s = 16h + j quantizes the 32 codes of row 16b + j in
@@ -26,7 +27,8 @@ __device__ __forceinline__ void unpack8(const uint4& raw, float* f) {
 }
 
 // One wave per tile; BITS selects 4 words (int4) or 3 words (int3) per slot.
-template <int BITS, bool ZP>
+// GS = 128: one group per tile; GS = 64: two (quarters 0-1 and 2-3 of a row).
+template <int BITS, bool ZP, int GS>
 __global__ __launch_bounds__(256) void k_quantize_pack(
     const _Float16* __restrict__ W, const float* __restrict__ s, int N, int K,
     long long n_tiles, uint32_t* __restrict__ qweight, uint16_t* __restrict__ scales,
@@ -61,9 +63,12 @@ __global__ __launch_bounds__(256) void k_quantize_pack(
     float mn = v[0], mx = v[0];
 #pragma unroll
     for (int i = 1; i < 32; ++i) { mn = fminf(mn, v[i]); mx = fmaxf(mx, v[i]); }
-    // the four quarters of row j sit in lanes j, j+16, j+32, j+48
+    // the four quarters of row j sit in lanes j, j+16, j+32, j+48; a 64-group
+    // is quarters {0,1} or {2,3}
     mn = fminf(mn, __shfl_xor(mn, 16)); mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mn = fminf(mn, __shfl_xor(mn, 32)); mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if constexpr (GS == 128) {
+        mn = fminf(mn, __shfl_xor(mn, 32)); mx = fmaxf(mx, __shfl_xor(mx, 32));
+    }
     const GroupParams p = group_params<Q, ZP>(mn, mx);
 
     uint32_t out[WQ];
@@ -106,8 +111,8 @@ __global__ __launch_bounds__(256) void k_quantize_pack(
 #pragma unroll
         for (int i = 0; i < 3; ++i) dst[i] = valid ? out[i] : 0u;
     }
-    if (h == 0) {                          // format 2: [block][g][row in block]
-        const size_t pidx = (size_t)tile * 16 + j;
+    if (GS == 128 ? h == 0 : (h & 1) == 0) {  // format 2: [block][group][row in block]
+        const size_t pidx = (GS == 128 ? (size_t)tile : 2 * (size_t)tile + (h >> 1)) * 16 + j;
         scales[pidx] = valid ? p.dbits : (uint16_t)0;
         zeros[pidx] = valid ? half_bits((_Float16)p.zero) : (uint16_t)0;
     }
@@ -131,12 +136,17 @@ __global__ __launch_bounds__(256) void k_scale_activations(
 
 }  // namespace
 
-int launch_quantize_pack(const void* W, const float* s, int N, int K, int bits, int zero_point,
-                         void* qweight, void* scales, void* zeros, hipStream_t st) {
+template <int GS>
+static auto pick_quantize(int bits, int zero_point) {
+    return bits == 4 ? (zero_point ? k_quantize_pack<4, true, GS> : k_quantize_pack<4, false, GS>)
+                     : (zero_point ? k_quantize_pack<3, true, GS> : k_quantize_pack<3, false, GS>);
+}
+
+int launch_quantize_pack(const void* W, const float* s, int N, int K, int bits, int group_size,
+                         int zero_point, void* qweight, void* scales, void* zeros, hipStream_t st) {
     const long long n_tiles = (long long)((N + 15) / 16) * (K / kGroup);
     const long long grid = (n_tiles + 3) / 4;
-    auto kern = bits == 4 ? (zero_point ? k_quantize_pack<4, true> : k_quantize_pack<4, false>)
-                          : (zero_point ? k_quantize_pack<3, true> : k_quantize_pack<3, false>);
+    auto kern = group_size == 64 ? pick_quantize<64>(bits, zero_point) : pick_quantize<128>(bits, zero_point);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const _Float16*)W, s, N, K,
                        n_tiles, (uint32_t*)qweight, (uint16_t*)scales, (uint16_t*)zeros);
     return (int)hipGetLastError();

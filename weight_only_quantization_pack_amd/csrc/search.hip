@@ -66,9 +66,9 @@ __global__ __launch_bounds__(256) void k_candidate_scales(const float* __restric
 }
 
 // Quantization error of every alpha: one lane = 8 consecutive weights of one
-// row, 16 lanes = one group (same lane layout as the int4 quantize kernel;
-// the error does not depend on the packed format).
-template <int Q, bool ZP>
+// row, GS / 8 lanes = one group (16 for 128-groups, 8 for 64-groups; the error
+// does not depend on the packed format).
+template <int Q, bool ZP, int GS>
 __global__ __launch_bounds__(256) void k_quant_err(const uint4* __restrict__ W,
                                                   const float* __restrict__ s_all, int K,
                                                   long long n_chunks, uint4* __restrict__ D) {
@@ -91,9 +91,9 @@ __global__ __launch_bounds__(256) void k_quant_err(const uint4* __restrict__ W,
 #pragma unroll
     for (int i = 1; i < 8; ++i) { mn = fminf(mn, v[i]); mx = fmaxf(mx, v[i]); }
 #pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-        mn = fminf(mn, __shfl_xor(mn, m, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, m, 16));
+    for (int m = 1; m < GS / 8; m <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, m, GS / 8));
+        mx = fmaxf(mx, __shfl_xor(mx, m, GS / 8));
     }
     const GroupParams p = group_params<Q, ZP>(mn, mx);
     uint4 out;
@@ -142,9 +142,15 @@ size_t search_workspace_bytes(int T, int N, int K, int n_alpha) {
     return layout(T, N, K, n_alpha).total;
 }
 
+template <int GS>
+static auto pick_quant_err(int bits, int zero_point) {
+    return bits == 4 ? (zero_point ? k_quant_err<15, true, GS> : k_quant_err<15, false, GS>)
+                     : (zero_point ? k_quant_err<7, true, GS> : k_quant_err<7, false, GS>);
+}
+
 int launch_search(const void* W, const void* X_cal, int T, int N, int K, const float* alphas,
-                  int n_alpha, int bits, int zero_point, float* s_out, float* loss_out,
-                  int* best_out, void* workspace, hipStream_t st) {
+                  int n_alpha, int bits, int group_size, int zero_point, float* s_out,
+                  float* loss_out, int* best_out, void* workspace, hipStream_t st) {
     const Layout L = layout(T, N, K, n_alpha);
     char* ws = static_cast<char*>(workspace);
     float* s_x = reinterpret_cast<float*>(ws + L.sx);
@@ -162,8 +168,8 @@ int launch_search(const void* W, const void* X_cal, int T, int N, int K, const f
                        s_x, K, grid, n_alpha, s_all);
     const long long n_chunks = (long long)N * K / 8;
     const dim3 qgrid((unsigned)((n_chunks + 255) / 256), n_alpha);
-    auto qerr = bits == 4 ? (zero_point ? k_quant_err<15, true> : k_quant_err<15, false>)
-                          : (zero_point ? k_quant_err<7, true> : k_quant_err<7, false>);
+    auto qerr = group_size == 64 ? pick_quant_err<64>(bits, zero_point)
+                                 : pick_quant_err<128>(bits, zero_point);
     hipLaunchKernelGGL(qerr, qgrid, dim3(256), 0, st, (const uint4*)W, s_all, K, n_chunks, (uint4*)D);
     int err = (int)hipGetLastError();
     if (err) return err;
