@@ -45,8 +45,8 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def gemv_bytes(M, N, K, bits=4):
-    return N * K * bits // 8 + 4 * N * (K // 128) + 2 * M * K + 2 * M * N
+def gemv_bytes(M, N, K, bits=4, group_size=128):
+    return N * K * bits // 8 + 4 * N * (K // group_size) + 2 * M * K + 2 * M * N
 
 
 def gemv_traffic_per_launch():
@@ -310,6 +310,74 @@ def main(argv=None):
     gemm_tflops = tot_flops / (tot_ms * 1e-3) / 1e12
 
     # ------------------------------------------------------------------ offline path
+    # ---------------------------------------- variants of the pages (context, not the metric)
+    # the Llama-7B decode step with int3 codes and with 64-wide groups (own
+    # algorithmic bytes), and the int3 prefill GEMM at M = 2048
+    variants = {}
+    for bits, gs in ((3, 128), (4, 64)):
+        vb = sum(N * K * bits // 8 + 4 * N * (K // gs) for K, N in layer)
+        Rv = max(2, math.ceil(COLD_BYTES / vb))
+        vpacked = {}
+        with torch.cuda.stream(stream):
+            for (K, N), i in shape_index.items():
+                W = torch.from_numpy(wl2.weights(i)).to(dev)
+                vpacked[(K, N)] = awq.quantize_pack(W, None, bits=bits, group_size=gs)
+                del W
+        vreps = [[tuple(t.clone() for t in vpacked[sh]) for sh in layer] for _ in range(Rv)]
+        del vpacked
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            for r in range(Rv):
+                for j, (K, N) in enumerate(layer):
+                    awq.gemv(xs[K], *vreps[r][j], N=N, bits=bits, group_size=gs, out=ys[j])
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for r in range(Rv):
+                for j, (K, N) in enumerate(layer):
+                    awq.gemv(xs[K], *vreps[r][j], N=N, bits=bits, group_size=gs, out=ys[j])
+        with torch.cuda.stream(stream):
+            for _ in range(2):
+                g.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n_rep = max(2, 200 // Rv)
+            a.record(stream)
+            for _ in range(n_rep):
+                g.replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / (n_rep * Rv)
+        sb = sum(gemv_bytes(1, N, K, bits, gs) for K, N in layer)
+        variants[f"decode_step_int{bits}_g{gs}"] = {
+            "us": round(us, 2), "GBps": round(sb / (us * 1e-6) / 1e9, 1),
+            "frac_hbm": round(sb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "step_bytes": sb}
+        log(f"  variant decode step int{bits} g{gs}: {us:.2f} us, {sb / (us * 1e-6) / 1e9:.1f} GB/s")
+        del vreps, g
+        torch.cuda.empty_cache()
+    tot3_flops, tot3_ms = 0.0, 0.0
+    for i, (K, N) in enumerate(wl4.shapes):
+        with torch.cuda.stream(stream):
+            W = torch.from_numpy(wl4.weights(i)).to(dev)
+            qw, sc, ze = awq.quantize_pack(W, None, bits=3)
+            del W
+            x = torch.from_numpy(wl4.activations(M, i)).to(dev)
+            y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            for _ in range(2):
+                awq.gemm(x, qw, sc, ze, N=N, bits=3, out=y)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(max(2, args.gemm_iters // 2)):
+                awq.gemm(x, qw, sc, ze, N=N, bits=3, out=y)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / max(2, args.gemm_iters // 2)
+        tot3_flops += 2.0 * M * N * K
+        tot3_ms += ms
+        del qw, sc, ze, x, y
+    variants["gemm_int3_M2048_TFLOPs"] = round(tot3_flops / (tot3_ms * 1e-3) / 1e12, 1)
+    log(f"  variant int3 GEMM M={M}: {variants['gemm_int3_M2048_TFLOPs']} TFLOP/s")
+
     offline = None
     if not args.no_offline:
         wl5 = WL.workload(5)
@@ -373,6 +441,7 @@ def main(argv=None):
                      "kernel": "k_gemv_x1<4,8,U> (ring U=2 for K=4096, U=4 for K=11008)", "avg_launch_us": round(avg_launch_us, 3)},
         "gemv_per_shape": per_shape,
         "batched_decode_llama70b_mlp": batched,
+        "variants": variants,
         "gemm": {"M": M, "TFLOPs": round(gemm_tflops, 1), "per_shape": gemm_res,
                  "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1),
                               "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
