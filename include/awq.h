@@ -151,8 +151,10 @@ size_t awq_search_workspace_bytes(int T, int N, int K, int n_alpha);
  *   best_out int32 [1] out (device), or NULL
  *   workspace / workspace_bytes: device scratch of at least
  *            awq_search_workspace_bytes(T, N, K, n_alpha) bytes.
- * The loss GEMM runs on fp16 MFMA with fp32 accumulation, so L_i carries a
- * relative error of order 1e-4 and near-ties may pick a neighbouring alpha.
+ * The loss GEMM runs on fp16 MFMA with fp32 accumulation over the fp16
+ * differences W - w_hat_i * (1/s_i) (the codes use the exact division of
+ * awq_quantize_pack), so L_i carries a relative error of order 1e-4 and
+ * near-ties may pick a neighbouring alpha.
  */
 int awq_search_scale(const void* W, const void* X_cal, int T, int N, int K,
                      const float* alphas, int n_alpha, int bits, int group_size,

@@ -4,12 +4,12 @@
 //
 //   1. s_x[k]   = mean_t |X_cal[t][k]|            exact fp64 sums
 //   2. s_i[k]   = fp32(pow(max(s_x[k], 1e-4), alpha_i))   fp64 pow
-//   3. D_i      = fp16(W - w_hat_i / s_i)         same quantizer as quantize_pack
+//   3. D_i      = fp16(W - w_hat_i * (1/s_i))     same quantizer (codes) as quantize_pack
 //   4. L_i      = sum over tiles of sum (X_cal . D_i^T)^2 / (T N)   MFMA GEMM
 //   5. best     = first i with the smallest L_i; s_out = s_best
 // All alphas are processed in one launch per stage (the D_i of every alpha
-// live side by side in the workspace), so the loss GEMM grid has
-// n_alpha x tiles workgroups.  The reductions run in a fixed order, so the
+// live side by side in the workspace; W is read once for all of them), so
+// the loss GEMM grid has n_alpha x tiles workgroups.  The reductions run in a fixed order, so the
 // result does not depend on scheduling.
 #include "awq_internal.h"
 
@@ -23,7 +23,7 @@ struct AlphaGrid { float a[kMaxAlpha]; };
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t sx, sall, D, part, total;
+    size_t sx, sall, sinv, D, part, total;
 };
 
 Layout layout(int T, int N, int K, int n_alpha) {
@@ -31,6 +31,7 @@ Layout layout(int T, int N, int K, int n_alpha) {
     size_t off = 0;
     L.sx = off;   off += align256((size_t)K * sizeof(float));
     L.sall = off; off += align256((size_t)n_alpha * K * sizeof(float));
+    L.sinv = off; off += align256((size_t)n_alpha * K * sizeof(float));
     L.D = off;    off += align256((size_t)n_alpha * N * K * sizeof(_Float16));
     L.part = off; off += align256((size_t)n_alpha * loss_gemm_tiles(T, N) * sizeof(double));
     L.total = off;
@@ -57,54 +58,74 @@ __global__ __launch_bounds__(256) void k_act_stat(const _Float16* __restrict__ X
 
 __global__ __launch_bounds__(256) void k_candidate_scales(const float* __restrict__ s_x, int K,
                                                          AlphaGrid grid, int n_alpha,
-                                                         float* __restrict__ s_all) {
+                                                         float* __restrict__ s_all,
+                                                         float* __restrict__ s_inv) {
     const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= (long long)n_alpha * K) return;
     const int i = (int)(t / K), k = (int)(t % K);
     const double base = fmax((double)s_x[k], 1e-4);
-    s_all[t] = (float)pow(base, (double)grid.a[i]);
+    const float sv = (float)pow(base, (double)grid.a[i]);
+    s_all[t] = sv;
+    s_inv[t] = 1.0f / sv;                         // for the loss only (D = W - w_hat * (1/s))
 }
 
 // Quantization error of every alpha: one lane = 8 consecutive weights of one
 // row, GS / 8 lanes = one group (16 for 128-groups, 8 for 64-groups; the error
-// does not depend on the packed format).
+// does not depend on the packed format).  W is read once: each lane keeps its
+// 8 weights and walks the alphas, writing D_alpha for each (s_alpha is small
+// and stays in L2), so the traffic is one read of W plus the D writes.  The
+// codes use the true fp32 division v / Delta, as awq_quantize_pack does; D
+// multiplies by the reciprocal of s (within 1.5 fp32 ulp of w_hat / s before
+// D's own fp16 rounding), which halves the divisions of this VALU-bound loop.
 template <int Q, bool ZP, int GS>
 __global__ __launch_bounds__(256) void k_quant_err(const uint4* __restrict__ W,
-                                                  const float* __restrict__ s_all, int K,
-                                                  long long n_chunks, uint4* __restrict__ D) {
+                                                  const float* __restrict__ s_all,
+                                                  const float* __restrict__ s_inv, int K,
+                                                  long long n_chunks, int n_alpha,
+                                                  uint4* __restrict__ D) {
     const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    const int alpha = blockIdx.y;
     const bool active = t < n_chunks;
-    const float* s = s_all + (size_t)alpha * K;
     const int k0 = active ? (int)(t % (K / 8)) * 8 : 0;
-    float w[8], v[8], sv[8];
-    if (active) {
-        const uint4 raw = W[t];
+    float w[8];
+    {
+        const uint4 raw = active ? W[t] : make_uint4(0, 0, 0, 0);
         const _Float16* h = reinterpret_cast<const _Float16*>(&raw);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) { w[i] = (float)h[i]; sv[i] = s[k0 + i]; v[i] = w[i] * sv[i]; }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) { w[i] = 0.f; sv[i] = 1.f; v[i] = 0.f; }
+        for (int i = 0; i < 8; ++i) w[i] = (float)h[i];
     }
-    float mn = v[0], mx = v[0];
+    for (int alpha = 0; alpha < n_alpha; ++alpha) {
+        const float* s = s_all + (size_t)alpha * K + k0;
+        const float* si = s_inv + (size_t)alpha * K + k0;
+        float v[8], sv[8], ri[8];
+        const float4 s0 = *reinterpret_cast<const float4*>(s);
+        const float4 s1 = *reinterpret_cast<const float4*>(s + 4);
+        const float4 r0 = *reinterpret_cast<const float4*>(si);
+        const float4 r1 = *reinterpret_cast<const float4*>(si + 4);
+        sv[0] = s0.x; sv[1] = s0.y; sv[2] = s0.z; sv[3] = s0.w;
+        sv[4] = s1.x; sv[5] = s1.y; sv[6] = s1.z; sv[7] = s1.w;
+        ri[0] = r0.x; ri[1] = r0.y; ri[2] = r0.z; ri[3] = r0.w;
+        ri[4] = r1.x; ri[5] = r1.y; ri[6] = r1.z; ri[7] = r1.w;
 #pragma unroll
-    for (int i = 1; i < 8; ++i) { mn = fminf(mn, v[i]); mx = fmaxf(mx, v[i]); }
+        for (int i = 0; i < 8; ++i) v[i] = w[i] * sv[i];
+        float mn = v[0], mx = v[0];
 #pragma unroll
-    for (int m = 1; m < GS / 8; m <<= 1) {
-        mn = fminf(mn, __shfl_xor(mn, m, GS / 8));
-        mx = fmaxf(mx, __shfl_xor(mx, m, GS / 8));
+        for (int i = 1; i < 8; ++i) { mn = fminf(mn, v[i]); mx = fmaxf(mx, v[i]); }
+#pragma unroll
+        for (int m = 1; m < GS / 8; m <<= 1) {
+            mn = fminf(mn, __shfl_xor(mn, m, GS / 8));
+            mx = fmaxf(mx, __shfl_xor(mx, m, GS / 8));
+        }
+        const GroupParams p = group_params<Q, ZP>(mn, mx);
+        uint4 out;
+        _Float16* o = reinterpret_cast<_Float16*>(&out);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float q = (float)quant_code<Q>(v[i], p);
+            const float w_hat = (q - p.zero) * p.delta;          // exact in fp32
+            o[i] = (_Float16)(w[i] - w_hat * ri[i]);
+        }
+        if (active) D[(size_t)alpha * n_chunks + t] = out;
     }
-    const GroupParams p = group_params<Q, ZP>(mn, mx);
-    uint4 out;
-    _Float16* o = reinterpret_cast<_Float16*>(&out);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float q = (float)quant_code<Q>(v[i], p);
-        const float w_hat = (q - p.zero) * p.delta;          // exact in fp32
-        o[i] = (_Float16)(w[i] - w_hat / sv[i]);
-    }
-    if (active) D[(size_t)alpha * (n_chunks) + t] = out;
 }
 
 // One workgroup: fixed-order fp64 sums of the loss partials, first argmin.
@@ -155,6 +176,7 @@ int launch_search(const void* W, const void* X_cal, int T, int N, int K, const f
     char* ws = static_cast<char*>(workspace);
     float* s_x = reinterpret_cast<float*>(ws + L.sx);
     float* s_all = reinterpret_cast<float*>(ws + L.sall);
+    float* s_inv = reinterpret_cast<float*>(ws + L.sinv);
     _Float16* D = reinterpret_cast<_Float16*>(ws + L.D);
     double* part = reinterpret_cast<double*>(ws + L.part);
 
@@ -165,12 +187,12 @@ int launch_search(const void* W, const void* X_cal, int T, int N, int K, const f
                        (const _Float16*)X_cal, T, K, s_x);
     const long long nsk = (long long)n_alpha * K;
     hipLaunchKernelGGL(k_candidate_scales, dim3((unsigned)((nsk + 255) / 256)), dim3(256), 0, st,
-                       s_x, K, grid, n_alpha, s_all);
+                       s_x, K, grid, n_alpha, s_all, s_inv);
     const long long n_chunks = (long long)N * K / 8;
-    const dim3 qgrid((unsigned)((n_chunks + 255) / 256), n_alpha);
     auto qerr = group_size == 64 ? pick_quant_err<64>(bits, zero_point)
                                  : pick_quant_err<128>(bits, zero_point);
-    hipLaunchKernelGGL(qerr, qgrid, dim3(256), 0, st, (const uint4*)W, s_all, K, n_chunks, (uint4*)D);
+    hipLaunchKernelGGL(qerr, dim3((unsigned)((n_chunks + 255) / 256)), dim3(256), 0, st, (const uint4*)W,
+                       s_all, s_inv, K, n_chunks, n_alpha, (uint4*)D);
     int err = (int)hipGetLastError();
     if (err) return err;
     err = launch_loss_gemm(X_cal, D, T, N, K, n_alpha, part, st);
