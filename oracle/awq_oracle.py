@@ -328,6 +328,22 @@ def scale_activations(x: np.ndarray, s: np.ndarray) -> np.ndarray:
     return (x32 / np.asarray(s, dtype=np.float32)[None, :]).astype(np.float16)
 
 
+def apply_inv_scale(x: np.ndarray, inv_s: np.ndarray) -> np.ndarray:
+    """x'[m, k] = fp16_rne(fp32(x[m, k]) * inv_s[k]).
+
+    The same activation side of the [P5] 02.02 transform as
+    ``scale_activations``, with the caller's reciprocal 1/s instead of s
+    (reading: the matmul entry points that fold the scale into their
+    activation load take inv_s, as the fused modules of "transformers - AWQ"
+    fold it into the layer before).  With inv_s = fp32(1/s) the result equals
+    fp16_rne(x / s) except where x/s lies within an fp32 ulp of an fp16
+    rounding boundary, and then differs by one fp16 ulp.
+    """
+    x32 = np.asarray(x, dtype=np.float16).astype(np.float32)
+    with np.errstate(over="ignore"):
+        return (x32 * np.asarray(inv_s, dtype=np.float32)[None, :]).astype(np.float16)
+
+
 # ---------------------------------------------------------------------------
 # a8 / a9 / a10: the W4A16 (W3A16) matmul
 # ---------------------------------------------------------------------------
@@ -391,6 +407,44 @@ def matmul_rows(x: np.ndarray, qweight: np.ndarray, scales: np.ndarray,
     q = q.reshape(len(rows), ROW_BLOCK, K)[:, 0, :]
     w_hat = dequantize(q, scales[rows], zeros[rows], K // np.asarray(scales).shape[1])
     return np.asarray(x, dtype=np.float16).astype(np.float64) @ w_hat.T
+
+
+# ---------------------------------------------------------------------------
+# f4: the gate/up half of the fused MLP ("transformers - AWQ", "Fused modules")
+# ---------------------------------------------------------------------------
+def silu(t) -> np.ndarray:
+    """SiLU(t) = t * sigmoid(t) = t / (1 + exp(-t)), fp64.
+
+    Reading: the pages fuse an MLP of gate, up and down layers for the Llama
+    and Mistral architectures without naming its activation; those
+    architectures use SiLU on the gate output, times the up output.
+    """
+    t = np.asarray(t, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return t / (1.0 + np.exp(-t))
+
+
+def gate_up(x: np.ndarray, inv_s, gate, up, bits: int, K: int) -> np.ndarray:
+    """h[m, n] = SiLU(g[m, n]) * u[m, n], fp64, with g = x' . w_hat_gate^T and
+    u = x' . w_hat_up^T from the packed layers gate = (qweight, scales, zeros)
+    and up likewise; x' = apply_inv_scale(x, inv_s), or x when inv_s is None
+    (gate and up read the same input, so they share one scale).
+
+    "transformers - AWQ", "Fused modules": the MLP's gate, up and down layers
+    fused into one module; this is the part ahead of the down projection.
+    """
+    xs = np.asarray(x, dtype=np.float16) if inv_s is None else apply_inv_scale(x, inv_s)
+    g = matmul(xs, *gate, bits, K)
+    u = matmul(xs, *up, bits, K)
+    return silu(g) * u
+
+
+def gate_up_rows(x: np.ndarray, inv_s, gate, up, bits: int, K: int, rows) -> np.ndarray:
+    """Output columns h[:, rows] of ``gate_up`` only (sampled checks at full size)."""
+    xs = np.asarray(x, dtype=np.float16) if inv_s is None else apply_inv_scale(x, inv_s)
+    g = matmul_rows(xs, *gate, bits, K, rows)
+    u = matmul_rows(xs, *up, bits, K, rows)
+    return silu(g) * u
 
 
 # ---------------------------------------------------------------------------
