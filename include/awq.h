@@ -179,6 +179,42 @@ int awq_gemv(const void* x, const void* qweight, const void* scales,
              int group_size, void* stream);
 
 /*
+ * awq_gemv_scaled -- awq_gemv with the activation side of the equivalent
+ * transform (section 02.02 "AWQ" of the VPTQ blog: x / s against weights
+ * quantized as W * s) folded into the activation load, so no separate pass
+ * over x is needed (the fused modules of "transformers - AWQ" fold it into
+ * the layer before):
+ *   x'[m][k] = fp16_rne(fp32(x[m][k]) * inv_s[k]);  y = awq_gemv(x', ...)
+ *   inv_s  fp32 [K] in, device, 16-byte aligned: the caller's 1 / s (NULL is
+ *          AWQ_ERR_NULL).  With inv_s = fp32(1 / s), x' equals
+ *          awq_scale_activations(x, s) except where x / s lies within one fp32
+ *          ulp of an fp16 rounding boundary (then one fp16 ulp apart).
+ *   Other arguments, limits and errors as awq_gemv.
+ */
+int awq_gemv_scaled(const void* x, const float* inv_s, const void* qweight,
+                    const void* scales, const void* zeros, void* y, int M, int N,
+                    int K, int bits, int group_size, void* stream);
+
+/*
+ * awq_gemv_gate_up -- the gate and up projections of a fused MLP ("transformers
+ * - AWQ", "Fused modules": the gate, up and down layers of the MLP fused into
+ * one module; Llama and Mistral use SiLU on the gate output) in one launch:
+ *   g = x' . w_hat_gate^T,  u = x' . w_hat_up^T   (fp32 sums, as awq_gemv)
+ *   h[m][n] = fp16_rne(SiLU(g[m][n]) * u[m][n]),  SiLU(t) = t / (1 + e^-t) in fp32
+ *   x' = x * inv_s as in awq_gemv_scaled, or x when inv_s is NULL (gate and up
+ *   read the same input, so they share one activation scale).
+ *   gate_* / up_*: two layers of the same N x K shape, bits and group_size,
+ *   packed by awq_quantize_pack.  h fp16 [M][N] out.  The down projection is
+ *   a plain awq_gemv / awq_gemv_scaled on h.
+ *   Limits and errors as awq_gemv; every pointer but inv_s is required.
+ */
+int awq_gemv_gate_up(const void* x, const float* inv_s, const void* gate_qweight,
+                     const void* gate_scales, const void* gate_zeros,
+                     const void* up_qweight, const void* up_scales,
+                     const void* up_zeros, void* h, int M, int N, int K, int bits,
+                     int group_size, void* stream);
+
+/*
  * awq_gemm -- context-stage (prefill) W4A16 product, same formula as
  * awq_gemv for any M >= 1 (the context kernel of the llm-awq README
  * feature list; version "gemm" in the transformers quantization_config).

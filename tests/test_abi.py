@@ -125,6 +125,45 @@ def test_gemv_and_gemm_specific_limits(lib):
     assert mm(lib, "awq_gemv", M=16, N=16, K=1 << 26) == SHAPE
 
 
+def _scaled(lib, x=P, inv_s=P5, qw=P2, sc=P3, ze=P4, y=P, M=1, N=64, K=256, bits=4, gs=128):
+    return lib.awq_gemv_scaled(x, inv_s, qw, sc, ze, y, M, N, K, bits, gs, NUL)
+
+
+def _gate_up(lib, x=P, inv_s=P5, g=(P2, P3, P4), u=(P2, P3, P4), h=P, M=1, N=64, K=256, bits=4,
+             gs=128):
+    return lib.awq_gemv_gate_up(x, inv_s, *g, *u, h, M, N, K, bits, gs, NUL)
+
+
+def test_gemv_scaled_validation(lib):
+    assert _scaled(lib, inv_s=NUL) == NULL            # the scaled entry point needs its scale
+    assert _scaled(lib, inv_s=MIS) == ALIGN
+    assert _scaled(lib, bits=5) == UNSUP
+    assert _scaled(lib, gs=32) == UNSUP
+    assert _scaled(lib, M=17) == UNSUP
+    assert _scaled(lib, K=129) == SHAPE
+    assert _scaled(lib, M=-1) == SHAPE
+    assert _scaled(lib, M=1, N=1 << 16, K=1 << 16) == SHAPE
+    assert _scaled(lib, y=NUL) == NULL
+    assert _scaled(lib, M=0, x=NUL) == OK
+    assert _scaled(lib, N=0, inv_s=NUL) == OK
+
+
+def test_gemv_gate_up_validation(lib):
+    assert _gate_up(lib, u=(NUL, P3, P4)) == NULL
+    assert _gate_up(lib, g=(P2, NUL, P4)) == NULL
+    assert _gate_up(lib, h=NUL) == NULL
+    assert _gate_up(lib, u=(P2, P3, MIS)) == ALIGN
+    assert _gate_up(lib, inv_s=MIS) == ALIGN
+    assert _gate_up(lib, inv_s=NUL, x=NUL) == NULL    # inv_s is optional, x is not
+    assert _gate_up(lib, bits=2) == UNSUP
+    assert _gate_up(lib, gs=256) == UNSUP
+    assert _gate_up(lib, M=17) == UNSUP
+    assert _gate_up(lib, K=200) == SHAPE
+    assert _gate_up(lib, N=-1) == SHAPE
+    assert _gate_up(lib, M=16, N=16, K=1 << 26) == SHAPE
+    assert _gate_up(lib, M=0, x=NUL, h=NUL) == OK
+
+
 def test_gemm_splitk_validation(lib):
     # without a GPU the library assumes 256 compute units: 32 tiles of a
     # 64 x 8192 output leave most idle, so K = 28672 (224 groups) is split 8 ways

@@ -6,10 +6,11 @@ seeded synthetic workloads.  The library is loaded on first use and a
 missing build raises immediately: there is no CPU fallback.
 """
 from .binding import (AwqError, quantize_pack, search_scale, search_workspace_bytes,  # noqa: F401
-                      gemv, gemm, gemm_splitk_workspace_bytes, scale_activations, library_path,
+                      gemv, gemv_gate_up, gemm, gemm_splitk_workspace_bytes, scale_activations,
+                      library_path,
                       load_library,
                       pack_format_version, packed_words_per_row, packed_words)
 
 __all__ = ["AwqError", "quantize_pack", "search_scale", "search_workspace_bytes",
-           "gemv", "gemm", "gemm_splitk_workspace_bytes", "scale_activations", "library_path", "load_library",
+           "gemv", "gemv_gate_up", "gemm", "gemm_splitk_workspace_bytes", "scale_activations", "library_path", "load_library",
            "pack_format_version", "packed_words_per_row", "packed_words"]

@@ -35,6 +35,11 @@ SIGNATURES = [
                           _c_int, _c_int, _c_int, _c_void_p]),
     ("awq_gemm", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                           _c_int, _c_int, _c_int, _c_void_p]),
+    ("awq_gemv_scaled", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                 _c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p]),
+    ("awq_gemv_gate_up", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                  _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int,
+                                  _c_int, _c_void_p]),
     ("awq_gemm_splitk_workspace_bytes", _c_size_t, [_c_int, _c_int, _c_int]),
     ("awq_gemm_splitk", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
                                  _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_size_t, _c_void_p]),
@@ -197,17 +202,22 @@ def search_scale(W, X_cal, alphas, bits: int = 4, group_size: int = GROUP_SIZE,
     return s_out, loss[:n_alpha], best
 
 
+def _need_layer(qweight, scales, zeros, N, K, bits, group_size, what=""):
+    torch = _torch()
+    words = int(load_library().awq_packed_words(N, K, bits))
+    _need(qweight, torch.int32, (words,), what + "qweight")
+    G = K // group_size if group_size > 0 else 0
+    NB = (N + 15) // 16
+    _need(scales, torch.float16, (NB, G, 16), what + "scales")
+    _need(zeros, torch.float16, (NB, G, 16), what + "zeros")
+
+
 def _matmul(fn_name, x, qweight, scales, zeros, N, bits, group_size, out, workspace=None):
     torch = _torch()
     lib = load_library()
     M, K = x.shape
     _need(x, torch.float16, (M, K), "x")
-    words = int(lib.awq_packed_words(N, K, bits))
-    _need(qweight, torch.int32, (words,), "qweight")
-    G = K // group_size if group_size > 0 else 0
-    NB = (N + 15) // 16
-    _need(scales, torch.float16, (NB, G, 16), "scales")
-    _need(zeros, torch.float16, (NB, G, 16), "zeros")
+    _need_layer(qweight, scales, zeros, N, K, bits, group_size)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=x.device)
     else:
@@ -224,9 +234,56 @@ def _matmul(fn_name, x, qweight, scales, zeros, N, bits, group_size, out, worksp
     return out
 
 
-def gemv(x, qweight, scales, zeros, N: int, bits: int = 4, group_size: int = GROUP_SIZE, out=None):
-    """Decode product y = x . w_hat^T for 1 <= M <= 16 rows of x; N output columns."""
-    return _matmul("awq_gemv", x, qweight, scales, zeros, N, bits, group_size, out)
+def gemv(x, qweight, scales, zeros, N: int, bits: int = 4, group_size: int = GROUP_SIZE, out=None,
+         inv_s=None):
+    """Decode product y = x . w_hat^T for 1 <= M <= 16 rows of x; N output columns.
+
+    inv_s (fp32 [K] device tensor, the reciprocal of the AWQ scale) folds the
+    activation scale into the load: y = fp16(x * inv_s) . w_hat^T through
+    awq_gemv_scaled."""
+    if inv_s is None:
+        return _matmul("awq_gemv", x, qweight, scales, zeros, N, bits, group_size, out)
+    torch = _torch()
+    lib = load_library()
+    M, K = x.shape
+    _need(x, torch.float16, (M, K), "x")
+    _need(inv_s, torch.float32, (K,), "inv_s")
+    _need_layer(qweight, scales, zeros, N, K, bits, group_size)
+    out = _out(out, M, N, x.device)
+    st = lib.awq_gemv_scaled(_ptr(x), _ptr(inv_s), _ptr(qweight), _ptr(scales), _ptr(zeros),
+                             _ptr(out), M, N, K, bits, group_size, _stream_ptr(x))
+    _check(st, "awq_gemv_scaled")
+    return out
+
+
+def gemv_gate_up(x, gate, up, N: int, bits: int = 4, group_size: int = GROUP_SIZE, inv_s=None,
+                 out=None):
+    """Gate/up half of a fused MLP in one launch: h = SiLU(x' . w_gate^T) * (x' . w_up^T).
+
+    gate, up: (qweight, scales, zeros) of two N x K layers; x' = fp16(x * inv_s)
+    when inv_s (fp32 [K]) is given, else x.  h fp16 [M][N] (awq_gemv_gate_up)."""
+    torch = _torch()
+    lib = load_library()
+    M, K = x.shape
+    _need(x, torch.float16, (M, K), "x")
+    if inv_s is not None:
+        _need(inv_s, torch.float32, (K,), "inv_s")
+    _need_layer(*gate, N, K, bits, group_size, "gate ")
+    _need_layer(*up, N, K, bits, group_size, "up ")
+    out = _out(out, M, N, x.device)
+    st = lib.awq_gemv_gate_up(_ptr(x), _ptr(inv_s), _ptr(gate[0]), _ptr(gate[1]), _ptr(gate[2]),
+                              _ptr(up[0]), _ptr(up[1]), _ptr(up[2]), _ptr(out), M, N, K, bits,
+                              group_size, _stream_ptr(x))
+    _check(st, "awq_gemv_gate_up")
+    return out
+
+
+def _out(out, M, N, device):
+    torch = _torch()
+    if out is None:
+        return torch.empty((M, N), dtype=torch.float16, device=device)
+    _need(out, torch.float16, (M, N), "out")
+    return out
 
 
 def gemm_splitk_workspace_bytes(M: int, N: int, K: int) -> int:

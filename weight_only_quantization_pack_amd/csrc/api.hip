@@ -113,8 +113,9 @@ int awq_search_scale(const void* W, const void* X_cal, int T, int N, int K, cons
                                          loss_out, best_out, workspace, (hipStream_t)stream));
 }
 
-int awq_gemv(const void* x, const void* qweight, const void* scales, const void* zeros, void* y,
-             int M, int N, int K, int bits, int group_size, void* stream) {
+namespace {
+// shared checks of the decode entry points; 1 = nothing to do (M or N is 0)
+int check_gemv(int M, int N, int K, int bits, int group_size) {
     int st = check_quant_params(bits, group_size, 1);
     if (st) return st;
     if (M > kMaxGemvM) return AWQ_ERR_UNSUPPORTED;
@@ -124,9 +125,40 @@ int awq_gemv(const void* x, const void* qweight, const void* scales, const void*
     if ((long long)M * K * 2 >= (1LL << 31) ||
         16LL * ((N + 15) / 16) * K / 8 * bits >= (1LL << 31))
         return AWQ_ERR_SHAPE;
-    if (M == 0 || N == 0) return AWQ_OK;
+    return (M == 0 || N == 0) ? -1 : AWQ_OK;
+}
+}  // namespace
+
+int awq_gemv(const void* x, const void* qweight, const void* scales, const void* zeros, void* y,
+             int M, int N, int K, int bits, int group_size, void* stream) {
+    int st = check_gemv(M, N, K, bits, group_size);
+    if (st) return st < 0 ? AWQ_OK : st;
     if ((st = check_ptrs({x, qweight, scales, zeros, y}))) return st;
-    return hip_status(awq::launch_gemv(x, qweight, scales, zeros, y, M, N, K, bits, group_size,
+    return hip_status(awq::launch_gemv(x, nullptr, qweight, scales, zeros, nullptr, nullptr, nullptr,
+                                       y, M, N, K, bits, group_size, (hipStream_t)stream));
+}
+
+int awq_gemv_scaled(const void* x, const float* inv_s, const void* qweight, const void* scales,
+                    const void* zeros, void* y, int M, int N, int K, int bits, int group_size,
+                    void* stream) {
+    int st = check_gemv(M, N, K, bits, group_size);
+    if (st) return st < 0 ? AWQ_OK : st;
+    if ((st = check_ptrs({x, inv_s, qweight, scales, zeros, y}))) return st;
+    return hip_status(awq::launch_gemv(x, inv_s, qweight, scales, zeros, nullptr, nullptr, nullptr,
+                                       y, M, N, K, bits, group_size, (hipStream_t)stream));
+}
+
+int awq_gemv_gate_up(const void* x, const float* inv_s, const void* gate_qweight,
+                     const void* gate_scales, const void* gate_zeros, const void* up_qweight,
+                     const void* up_scales, const void* up_zeros, void* h, int M, int N, int K,
+                     int bits, int group_size, void* stream) {
+    int st = check_gemv(M, N, K, bits, group_size);
+    if (st) return st < 0 ? AWQ_OK : st;
+    if ((st = check_ptrs({x, gate_qweight, gate_scales, gate_zeros, up_qweight, up_scales, up_zeros, h})))
+        return st;
+    if (inv_s && (st = check_ptr(inv_s))) return st;
+    return hip_status(awq::launch_gemv(x, inv_s, gate_qweight, gate_scales, gate_zeros, up_qweight,
+                                       up_scales, up_zeros, h, M, N, K, bits, group_size,
                                        (hipStream_t)stream));
 }
 

@@ -118,7 +118,11 @@ int launch_scale_activations(const void* x, const float* s, void* x_out, int M, 
 // compute units of the current device
 int device_cu_count();
 
-int launch_gemv(const void* x, const void* qweight, const void* scales, const void* zeros,
+// decode product; inv_s (or NULL) folds the activation scale into the x
+// load; qweight2 (or NULL) makes it the fused gate/up pair (gate = the first
+// layer, up = the second, y = SiLU(gate) * up)
+int launch_gemv(const void* x, const float* inv_s, const void* qweight, const void* scales,
+                const void* zeros, const void* qweight2, const void* scales2, const void* zeros2,
                 void* y, int M, int N, int K, int bits, int group_size, hipStream_t st);
 int launch_gemm(const void* x, const void* qweight, const void* scales, const void* zeros,
                 void* y, int M, int N, int K, int bits, int group_size, hipStream_t st);

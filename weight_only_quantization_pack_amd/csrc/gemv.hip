@@ -150,6 +150,43 @@ __device__ __forceinline__ _Float16 low_half(uint32_t v) {
     return __builtin_bit_cast(_Float16, (unsigned short)v);
 }
 
+// Kernel arguments.  Entry [1] of the weight arrays is the second layer of a
+// fused pair (FUSE: gate = [0], up = [1]); inv_s is read only with SCALE.
+struct GemvArgs {
+    const _Float16* x;
+    const float* inv_s;                      // fp32 [K]: x'[m][k] = fp16(x[m][k] * inv_s[k])
+    const uint32_t* qweight[2];
+    const _Float16* scales[2];
+    const _Float16* zeros[2];
+    _Float16* y;
+    int M, N, K;
+};
+
+// x' = fp16_rne(fp32(x) * inv_s) of one 16-byte chunk of 8 activations
+__device__ __forceinline__ uint4 scale_chunk(uint4 v, const float* s) {
+    const _Float16* h = reinterpret_cast<const _Float16*>(&v);
+    uint4 o;
+    _Float16* oh = reinterpret_cast<_Float16*>(&o);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        // the fp32 product is rounded before the fp16 conversion (the empty asm
+        // keeps the compiler from fusing both into one rounding of the exact
+        // product, which differs in the rare double-rounding cases)
+        float t = (float)h[e] * s[e];
+        asm volatile("" : "+v"(t));
+        oh[e] = (_Float16)t;
+    }
+    return o;
+}
+
+// output of a fused gate/up pair from the fp32 sums: SiLU(g) * u, rounded once
+__device__ __forceinline__ _Float16 silu_mul(float g, float u) {
+    return (_Float16)(g / (1.0f + expf(-g)) * u);
+}
+
+// the buffer descriptors of one layer's packed tiles and parameters
+struct LayerRsrc { __amdgpu_buffer_rsrc_t q, s, z; };
+
 // acc += D * sum_k x[j][k] * (q[k] - z) over one tile: the four k32 MFMAs of
 // a group with x (rows j >= M read row 0) as the A operand from LDS at xa and
 // the slot's exact (q - z) as the B operand; the group scale multiplies the
@@ -206,13 +243,19 @@ __device__ __forceinline__ void accumulate_tile(const Slot<WQ>& w, const RawPara
     }
 }
 
-template <int BITS, int GS, int WK, int U, int XL>
-__global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
-    const _Float16* __restrict__ x, const uint32_t* __restrict__ qweight,
-    const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
-    _Float16* __restrict__ y, int M, int N, int K) {
+// SCALE: x is multiplied by inv_s while it is staged (each lane loads the
+// scale of its own x chunks next to them, 32 bytes per chunk, so instances
+// with SCALE keep XL <= 4).  FUSE: the workgroup computes row block b of two
+// layers that read the same x (gate, then up): each wave's ring walks its
+// gate tiles of the block, then its up tiles, into two accumulators, and the
+// block's output is SiLU(gate) * up.
+template <int BITS, int GS, int WK, int U, int XL, bool SCALE, bool FUSE>
+__global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(GemvArgs a) {
+    static_assert(!SCALE || XL <= 4, "scaled staging keeps 8 fp32 per x chunk in registers");
     constexpr int WQ = BITS == 4 ? 4 : 3;
+    constexpr int NH = FUSE ? 2 : 1;                   // layers per row block
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int M = a.M, N = a.N, K = a.K;
     const int G = K / kGroup;
     const int NB = (N + 15) / 16;
     const int XS = K + 8;                              // halves per staged x row
@@ -220,30 +263,41 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
     float4_t* red = reinterpret_cast<float4_t*>(smem + (((size_t)M * XS * 2 + 15) & ~(size_t)15));
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    // FUSE picks a layer's buffer descriptors by the ring position, which
+    // depends on wave: stating that wave is uniform keeps them in SGPRs
+    const int lane = tid & 63, wave = FUSE ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
     const int j = lane & 15, h = lane >> 4;
     const int nw = wave < G ? (G - wave + WK - 1) / WK : 0;   // groups g = wave + WK i of a block
-    const int nwp = (nw + U - 1) / U * U;                       // ring items per block
+    const int nwp = (nw + U - 1) / U * U;                       // ring items per block and layer
+    const int IB = NH * nwp;                                    // ring items per block
     const _Float16* xa0 = xs + (size_t)(j < M ? j : 0) * XS + 32 * h;
     const uint32_t psh = 16u * (uint32_t)(j & 1);              // the lane's half of a param word
 
     // the launcher guarantees every buffer is < 2^31 bytes
     const uint32_t tiles = (uint32_t)NB * (uint32_t)G;
-    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(qweight, tiles * 64u * WQ * 4u);
     // scales / zeros: [block][group][16], kGroup / GS groups per tile
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scales, tiles * (32u * kGroup / GS));
-    const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(zeros, tiles * (32u * kGroup / GS));
+    LayerRsrc L[NH];
+#pragma unroll
+    for (int l = 0; l < NH; ++l) {
+        L[l].q = buffer_rsrc(a.qweight[l], tiles * 64u * WQ * 4u);
+        L[l].s = buffer_rsrc(a.scales[l], tiles * (32u * kGroup / GS));
+        L[l].z = buffer_rsrc(a.zeros[l], tiles * (32u * kGroup / GS));
+    }
     // this lane's parameter group within a tile: its quarter's (GS = 64)
     const uint32_t pgrp = GS == 64 ? (uint32_t)(h >> 1) : 0u;
-    auto load = [&](int b, int i, Slot<WQ>& w, RawParams& p) {
+    // ring item f of block b: layer f / nwp, group wave + WK (f % nwp)
+    auto load = [&](int b, int f, Slot<WQ>& w, RawParams& p) {
+        const bool up = FUSE && f >= nwp;              // wave-uniform
+        const int i = up ? f - nwp : f;
         const bool ok = b < NB && i < nw;
         const uint32_t t = (uint32_t)b * (uint32_t)G + (uint32_t)(wave + WK * i);
         const uint32_t oq = ok ? (t * 64u + (uint32_t)lane) * (WQ * 4u) : kBufferOutOfRange;
         const uint32_t op = ok ? ((t * (kGroup / GS) + pgrp) * 16u + (uint32_t)(j & ~1)) * 2u
                                : kBufferOutOfRange;
-        w = buffer_slot<WQ>(rq, oq);
-        p.d = __builtin_amdgcn_raw_buffer_load_b32(rs, op, 0, 0);
-        p.z = __builtin_amdgcn_raw_buffer_load_b32(rz, op, 0, 0);
+        const LayerRsrc& r = up ? L[NH - 1] : L[0];
+        w = buffer_slot<WQ>(r.q, oq);
+        p.d = __builtin_amdgcn_raw_buffer_load_b32(r.s, op, 0, 0);
+        p.z = __builtin_amdgcn_raw_buffer_load_b32(r.z, op, 0, 0);
     };
 
     // Each wave stages only the x columns of its own groups (the same groups in
@@ -256,9 +310,11 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
     // flight on entry to the sweep are ordered as in the sweep itself.
     const int pairs = nw * M;
     const uint32_t mdiv = 65536u / (uint32_t)M + 1u;   // q / M = (q * mdiv) >> 16 for q < 2048, M <= 16
-    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.x, (uint32_t)M * (uint32_t)K * 2u);
+    const __amdgpu_buffer_rsrc_t ri = buffer_rsrc(a.inv_s, SCALE ? (uint32_t)K * 4u : 0u);
     uint4 xv[XL];
     uint32_t xat[XL];
+    float sv[SCALE ? XL : 1][8];
 #pragma unroll
     for (int p = 0; p < XL; ++p) {
         const uint32_t q = (uint32_t)((lane >> 4) + 4 * p);
@@ -269,6 +325,20 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
             rx, ok ? (m * (uint32_t)K + col) * 2u : kBufferOutOfRange, 0, 0);
         xv[p] = make_uint4(v[0], v[1], v[2], v[3]);
         xat[p] = ok ? m * (uint32_t)XS + col : (uint32_t)K;
+        if constexpr (SCALE) {
+            const uint32_t so = ok ? col * 4u : kBufferOutOfRange;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const auto f = __builtin_amdgcn_raw_buffer_load_b128(ri, so + 16u * c, 0, 0);
+                // through a scalar: a bit_cast of the vector element itself
+                // keeps only element 0 of the load with this compiler
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t u = f[e];
+                    sv[p][4 * c + e] = __builtin_bit_cast(float, u);
+                }
+            }
+        }
     }
     Slot<WQ> ring[U];
     RawParams pr[U];
@@ -280,7 +350,11 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int p = 0; p < XL; ++p) *reinterpret_cast<uint4*>(xs + xat[p]) = xv[p];
+    for (int p = 0; p < XL; ++p) {
+        uint4 v = xv[p];
+        if constexpr (SCALE) v = scale_chunk(v, sv[p]);
+        *reinterpret_cast<uint4*>(xs + xat[p]) = v;
+    }
     // the wave's own LDS stores complete before its lanes read each other's chunks
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
@@ -289,34 +363,50 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
     int buf = 0;
     do {
         const int bn = b + gridDim.x;                  // next block of this workgroup
-        float4_t acc = {0.f, 0.f, 0.f, 0.f};
-        for (int i0 = 0; i0 < nwp; i0 += U) {
+        float4_t acc[NH];
+#pragma unroll
+        for (int l = 0; l < NH; ++l) acc[l] = (float4_t){0.f, 0.f, 0.f, 0.f};
+        for (int f0 = 0; f0 < IB; f0 += U) {
+            // nwp is a multiple of U: a ring round belongs to one layer
+            const bool upr = FUSE && f0 >= nwp;
+            const int i0 = upr ? f0 - nwp : f0;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int i = i0 + u;
-                if (i < nw)                            // wave-uniform; loads stay outside
-                    accumulate_tile<BITS, WQ, GS>(ring[u], pr[u], xa0 + (size_t)(wave + WK * i) * kGroup, psh, acc);
+                if (i < nw) {                          // wave-uniform; loads stay outside
+                    const _Float16* xa = xa0 + (size_t)(wave + WK * i) * kGroup;
+                    if (FUSE && upr)
+                        accumulate_tile<BITS, WQ, GS>(ring[u], pr[u], xa, psh, acc[NH - 1]);
+                    else
+                        accumulate_tile<BITS, WQ, GS>(ring[u], pr[u], xa, psh, acc[0]);
+                }
                 // refill the slot with the item U places on (this block or the next)
-                const int k = i + U;
-                const bool here = k < nwp;
-                load(here ? b : bn, here ? k : k - nwp, ring[u], pr[u]);
+                const int k = f0 + u + U;
+                const bool here = k < IB;
+                load(here ? b : bn, here ? k : k - IB, ring[u], pr[u]);
             }
         }
-        red[(buf * WK + wave) * 64 + lane] = acc;
+#pragma unroll
+        for (int l = 0; l < NH; ++l) red[((buf * NH + l) * WK + wave) * 64 + lane] = acc[l];
         __syncthreads();
         if (wave == 0) {
-            float4_t sum = red[(buf * WK) * 64 + lane];
+            float4_t sum[NH];
 #pragma unroll
-            for (int w = 1; w < WK; ++w) {
-                const float4_t o = red[(buf * WK + w) * 64 + lane];
-                sum[0] += o[0]; sum[1] += o[1]; sum[2] += o[2]; sum[3] += o[3];
+            for (int l = 0; l < NH; ++l) {
+                sum[l] = red[((buf * NH + l) * WK) * 64 + lane];
+#pragma unroll
+                for (int w = 1; w < WK; ++w) {
+                    const float4_t o = red[((buf * NH + l) * WK + w) * 64 + lane];
+                    sum[l][0] += o[0]; sum[l][1] += o[1]; sum[l][2] += o[2]; sum[l][3] += o[3];
+                }
             }
             const int n = 16 * b + j;
             if (n < N) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int m = 4 * h + r;
-                    if (m < M) y[(size_t)m * N + n] = (_Float16)sum[r];
+                    if (m < M)
+                        a.y[(size_t)m * N + n] = FUSE ? silu_mul(sum[0][r], sum[NH - 1][r]) : (_Float16)sum[0][r];
                 }
             }
         }
@@ -326,9 +416,7 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(
 }
 
 
-using GemvX1FnT = void (*)(const _Float16*, const uint32_t*, const _Float16*, const _Float16*,
-                           _Float16*, int, int, int);
-using GemvX1Fn = GemvX1FnT;
+using GemvFn = void (*)(GemvArgs);
 
 // x too large for LDS at once (M rows, M * K > 32K halves): K is swept in
 // slices of SG = WK * U groups, x staged one slice at a time, each wave
@@ -341,15 +429,23 @@ using GemvX1Fn = GemvX1FnT;
 // so the compiler's waits cover exactly one ring slot; the next slice's x is
 // loaded into registers during the current slice, ahead of its ring loads.
 // The waves' partial sums meet in LDS once per block at the end.
-template <int BITS, int GS, int WK, int U, int BMAX, int XL>
-__global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_xs(
-    const _Float16* __restrict__ x, const uint32_t* __restrict__ qweight,
-    const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
-    _Float16* __restrict__ y, int M, int N, int K) {
+//
+// SCALE: each wave also loads, one slice ahead, the inv_s of its U = 2 groups
+// of the next slice (one 16-byte load per lane), parks it in its own 1 KB of
+// LDS while staging, and multiplies every x chunk by the 8 values of the
+// chunk's columns on the way into the x slice.  FUSE: the workgroup owns one
+// row block of two layers reading the same x (gate, up; BMAX = 1) and keeps an
+// accumulator for each; the block's output is SiLU(gate) * up.
+template <int BITS, int GS, int WK, int U, int BMAX, int XL, bool SCALE, bool FUSE>
+__global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_xs(GemvArgs a) {
+    static_assert(!FUSE || BMAX == 1, "a fused pair takes the two accumulators");
+    static_assert(!SCALE || U == 2, "a wave's inv_s slice is 64 lanes x 4 floats = 2 groups");
     constexpr int WQ = BITS == 4 ? 4 : 3;
     constexpr int SG = WK * U;                         // groups per slice
     constexpr int XS = SG * kGroup + 8;                // halves per staged x row
+    constexpr int NA = FUSE ? 2 : BMAX;                // accumulators: (block, layer) items
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int M = a.M, N = a.N, K = a.K;
     _Float16* xs = reinterpret_cast<_Float16*>(smem);
     float4_t* red = reinterpret_cast<float4_t*>(smem);   // after the sweep, over x
     const int G = K / kGroup;
@@ -361,28 +457,39 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_xs(
     const int j = lane & 15, h = lane >> 4;
     const _Float16* xa0 = xs + (size_t)(j < M ? j : 0) * XS + 32 * h;
     const uint32_t psh = 16u * (uint32_t)(j & 1);
+    // SCALE: this wave's inv_s of the slice being staged, [U][kGroup] fp32
+    float* sw = reinterpret_cast<float*>(smem + (((size_t)M * XS * 2 + 15) & ~(size_t)15)) + wave * U * kGroup;
 
     const uint32_t tiles = (uint32_t)NB * (uint32_t)G;
-    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(qweight, tiles * 64u * WQ * 4u);
-    // scales / zeros: [block][group][16], kGroup / GS groups per tile
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scales, tiles * (32u * kGroup / GS));
-    const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(zeros, tiles * (32u * kGroup / GS));
+    constexpr int NH = FUSE ? 2 : 1;
+    LayerRsrc L[NH];
+#pragma unroll
+    for (int l = 0; l < NH; ++l) {
+        L[l].q = buffer_rsrc(a.qweight[l], tiles * 64u * WQ * 4u);
+        // scales / zeros: [block][group][16], kGroup / GS groups per tile
+        L[l].s = buffer_rsrc(a.scales[l], tiles * (32u * kGroup / GS));
+        L[l].z = buffer_rsrc(a.zeros[l], tiles * (32u * kGroup / GS));
+    }
     // this lane's parameter group within a tile: its quarter's (GS = 64)
     const uint32_t pgrp = GS == 64 ? (uint32_t)(h >> 1) : 0u;
-    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.x, (uint32_t)M * (uint32_t)K * 2u);
+    const __amdgpu_buffer_rsrc_t ri = buffer_rsrc(a.inv_s, SCALE ? (uint32_t)K * 4u : 0u);
 
-    // item (s, k, u): block blockIdx.x + k gridDim.x, group s SG + wave + WK u
+    // accumulator item k: block blockIdx.x + k gridDim.x, or (FUSE) layer k of block blockIdx.x
+    auto item_block = [&](int k) { return FUSE ? (int)blockIdx.x : (int)blockIdx.x + k * (int)gridDim.x; };
+    // item (s, k, u): item k's tile of group s SG + wave + WK u
     auto load = [&](int s, int k, int u, Slot<WQ>& w, RawParams& p) {
-        const int b = blockIdx.x + k * gridDim.x;
+        const int b = item_block(k);
         const int g = s * SG + wave + WK * u;
         const bool ok = b < NB && g < G;
         const uint32_t t = (uint32_t)b * (uint32_t)G + (uint32_t)g;
         const uint32_t oq = ok ? (t * 64u + (uint32_t)lane) * (WQ * 4u) : kBufferOutOfRange;
         const uint32_t op = ok ? ((t * (kGroup / GS) + pgrp) * 16u + (uint32_t)(j & ~1)) * 2u
                                : kBufferOutOfRange;
-        w = buffer_slot<WQ>(rq, oq);
-        p.d = __builtin_amdgcn_raw_buffer_load_b32(rs, op, 0, 0);
-        p.z = __builtin_amdgcn_raw_buffer_load_b32(rz, op, 0, 0);
+        const LayerRsrc& r = (FUSE && k == 1) ? L[NH - 1] : L[0];
+        w = buffer_slot<WQ>(r.q, oq);
+        p.d = __builtin_amdgcn_raw_buffer_load_b32(r.s, op, 0, 0);
+        p.z = __builtin_amdgcn_raw_buffer_load_b32(r.z, op, 0, 0);
     };
     // the wave's x of slice s: (group u, row m) pairs q = (lane >> 4) + 4p as
     // 16-byte chunks; pairs past U * M land in row 0's padding xs[SG*128 ..]
@@ -405,39 +512,63 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_xs(
             xv[p] = make_uint4(v[0], v[1], v[2], v[3]);
         }
     };
+    // SCALE: lane l carries inv_s of group l / 32 of the wave's pair, columns 4 (l % 32) ..
+    auto load_s = [&](int s) -> uint4 {
+        const int g = s * SG + wave + WK * (lane >> 5);
+        const uint32_t off = ((uint32_t)kGroup * (uint32_t)g + 4u * (uint32_t)(lane & 31)) * 4u;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(ri, g < G ? off : kBufferOutOfRange, 0, 0);
+        return make_uint4(v[0], v[1], v[2], v[3]);
+    };
 
     uint4 xv[XL];
+    uint4 sv = make_uint4(0, 0, 0, 0);
     Slot<WQ> ring[U];
     RawParams pr[U];
     load_x(0, xv);
+    if constexpr (SCALE) sv = load_s(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         __builtin_amdgcn_sched_barrier(0);
         load(0, 0, u, ring[u], pr[u]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    float4_t acc[BMAX];
+    float4_t acc[NA];
 #pragma unroll
-    for (int k = 0; k < BMAX; ++k) acc[k] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < NA; ++k) acc[k] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
     // NS >= 1: no entry test, so the loads above stay where they are
     int s = 0;
     do {
         // stage slice s (this wave's reads of slice s - 1 precede in program order)
+        if constexpr (SCALE) {
+            *reinterpret_cast<uint4*>(sw + 4 * lane) = sv;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-        for (int p = 0; p < XL; ++p) *reinterpret_cast<uint4*>(xs + x_at(p)) = xv[p];
+            for (int p = 0; p < XL; ++p) {
+                const uint32_t q = (uint32_t)((lane >> 4) + 4 * p);
+                const uint32_t u = min((q * mdiv) >> 16, (uint32_t)(U - 1));   // pairs past U * M: any
+                float f[8];
+                *reinterpret_cast<float4*>(f) = *reinterpret_cast<const float4*>(sw + u * kGroup + 8 * j);
+                *reinterpret_cast<float4*>(f + 4) = *reinterpret_cast<const float4*>(sw + u * kGroup + 8 * j + 4);
+                *reinterpret_cast<uint4*>(xs + x_at(p)) = scale_chunk(xv[p], f);
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < XL; ++p) *reinterpret_cast<uint4*>(xs + x_at(p)) = xv[p];
+        }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         load_x(s + 1, xv);
+        if constexpr (SCALE) sv = load_s(s + 1);
 #pragma unroll
-        for (int k = 0; k < BMAX; ++k) {
+        for (int k = 0; k < NA; ++k) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int g = s * SG + wave + WK * u;
-                if (blockIdx.x + k * gridDim.x < NB && g < G)    // wave-uniform
+                if (item_block(k) < NB && g < G)     // wave-uniform
                     accumulate_tile<BITS, WQ, GS>(ring[u], pr[u], xa0 + (size_t)(wave + WK * u) * kGroup, psh, acc[k]);
-                // refill: the same group of the next block, or of the first block in the next slice
-                if (k + 1 < BMAX)
+                // refill: the same group of the next item, or of the first item in the next slice
+                if (k + 1 < NA)
                     load(s, k + 1, u, ring[u], pr[u]);
                 else
                     load(s + 1, 0, u, ring[u], pr[u]);
@@ -447,25 +578,52 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_xs(
     } while (s < NS);
 
     __syncthreads();                                   // every wave is done with x
-#pragma unroll
-    for (int k = 0; k < BMAX; ++k) {
-        const int buf = k & 1;
-        red[(buf * WK + wave) * 64 + lane] = acc[k];
+    if constexpr (FUSE) {
+        red[(0 * WK + wave) * 64 + lane] = acc[0];
+        red[(1 * WK + wave) * 64 + lane] = acc[1];
         __syncthreads();
-        const int b = blockIdx.x + k * gridDim.x;
-        if (wave == 0 && b < NB) {
-            float4_t sum = red[(buf * WK) * 64 + lane];
+        const int b = blockIdx.x;
+        if (wave == 0) {
+            float4_t sum[2];
 #pragma unroll
-            for (int w = 1; w < WK; ++w) {
-                const float4_t o = red[(buf * WK + w) * 64 + lane];
-                sum[0] += o[0]; sum[1] += o[1]; sum[2] += o[2]; sum[3] += o[3];
+            for (int l = 0; l < 2; ++l) {
+                sum[l] = red[(l * WK) * 64 + lane];
+#pragma unroll
+                for (int w = 1; w < WK; ++w) {
+                    const float4_t o = red[(l * WK + w) * 64 + lane];
+                    sum[l][0] += o[0]; sum[l][1] += o[1]; sum[l][2] += o[2]; sum[l][3] += o[3];
+                }
             }
             const int n = 16 * b + j;
             if (n < N) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int m = 4 * h + r;
-                    if (m < M) y[(size_t)m * N + n] = (_Float16)sum[r];
+                    if (m < M) a.y[(size_t)m * N + n] = silu_mul(sum[0][r], sum[1][r]);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < BMAX; ++k) {
+            const int buf = k & 1;
+            red[(buf * WK + wave) * 64 + lane] = acc[k];
+            __syncthreads();
+            const int b = blockIdx.x + k * gridDim.x;
+            if (wave == 0 && b < NB) {
+                float4_t sum = red[(buf * WK) * 64 + lane];
+#pragma unroll
+                for (int w = 1; w < WK; ++w) {
+                    const float4_t o = red[(buf * WK + w) * 64 + lane];
+                    sum[0] += o[0]; sum[1] += o[1]; sum[2] += o[2]; sum[3] += o[3];
+                }
+                const int n = 16 * b + j;
+                if (n < N) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int m = 4 * h + r;
+                        if (m < M) a.y[(size_t)m * N + n] = (_Float16)sum[r];
+                    }
                 }
             }
         }
@@ -474,82 +632,92 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_xs(
 
 constexpr int kGemvSliceRing = 2;                      // U of k_gemv_xs: slices of 16 groups
 
-using GemvXsFn = GemvX1FnT;
-template <int BITS, int GS, int BMAX>
-GemvXsFn pick_xs_loads(int xl) {
-    if (xl <= 2) return k_gemv_xs<BITS, GS, kGemvWaves, kGemvSliceRing, BMAX, 2>;
-    if (xl <= 4) return k_gemv_xs<BITS, GS, kGemvWaves, kGemvSliceRing, BMAX, 4>;
-    return k_gemv_xs<BITS, GS, kGemvWaves, kGemvSliceRing, BMAX, 8>;
+template <int BITS, int GS, bool SC, bool FU, int BMAX>
+GemvFn pick_xs_loads(int xl) {
+    if (xl <= 2) return k_gemv_xs<BITS, GS, kGemvWaves, kGemvSliceRing, BMAX, 2, SC, FU>;
+    if (xl <= 4) return k_gemv_xs<BITS, GS, kGemvWaves, kGemvSliceRing, BMAX, 4, SC, FU>;
+    return k_gemv_xs<BITS, GS, kGemvWaves, kGemvSliceRing, BMAX, 8, SC, FU>;
 }
-template <int BITS, int GS>
-GemvXsFn pick_xs(int bmax, int xl) {
-    return bmax <= 1 ? pick_xs_loads<BITS, GS, 1>(xl) : pick_xs_loads<BITS, GS, 2>(xl);
+template <int BITS, int GS, bool SC, bool FU>
+GemvFn pick_xs(int bmax, int xl) {
+    if constexpr (FU) return pick_xs_loads<BITS, GS, SC, FU, 1>(xl);
+    else return bmax <= 1 ? pick_xs_loads<BITS, GS, SC, FU, 1>(xl) : pick_xs_loads<BITS, GS, SC, FU, 2>(xl);
 }
 
 // k_gemv_x1 instance: ring depth (short rows: 2, else 4) and the number of
 // 16-byte x loads per lane that stage a wave's (group, row) pairs (<= 12:
-// M * K <= 32768 gives at most 48 pairs per wave)
-template <int BITS, int GS, int U>
-GemvX1Fn pick_x1_loads(int xl) {
-    if (xl <= 1) return k_gemv_x1<BITS, GS, kGemvWaves, U, 1>;
-    if (xl <= 2) return k_gemv_x1<BITS, GS, kGemvWaves, U, 2>;
-    if (xl <= 4) return k_gemv_x1<BITS, GS, kGemvWaves, U, 4>;
-    if (xl <= 8) return k_gemv_x1<BITS, GS, kGemvWaves, U, 8>;
-    return k_gemv_x1<BITS, GS, kGemvWaves, U, 12>;
+// M * K <= 32768 gives at most 48 pairs per wave; <= 4 with SCALE)
+template <int BITS, int GS, bool SC, bool FU, int U>
+GemvFn pick_x1_loads(int xl) {
+    if (xl <= 1) return k_gemv_x1<BITS, GS, kGemvWaves, U, 1, SC, FU>;
+    if (xl <= 2) return k_gemv_x1<BITS, GS, kGemvWaves, U, 2, SC, FU>;
+    if (xl <= 4) return k_gemv_x1<BITS, GS, kGemvWaves, U, 4, SC, FU>;
+    if constexpr (!SC) {
+        if (xl <= 8) return k_gemv_x1<BITS, GS, kGemvWaves, U, 8, SC, FU>;
+        return k_gemv_x1<BITS, GS, kGemvWaves, U, 12, SC, FU>;
+    }
+    return nullptr;
 }
-template <int BITS, int GS>
-GemvX1Fn pick_x1(bool short_rows, int xl) {
-    return short_rows ? pick_x1_loads<BITS, GS, kGemvRingShort>(xl)
-                      : pick_x1_loads<BITS, GS, kGemvRingLong>(xl);
+template <int BITS, int GS, bool SC, bool FU>
+GemvFn pick_x1(bool short_rows, int xl) {
+    return short_rows ? pick_x1_loads<BITS, GS, SC, FU, kGemvRingShort>(xl)
+                      : pick_x1_loads<BITS, GS, SC, FU, kGemvRingLong>(xl);
 }
 
-template <int BITS, int GS>
-int launch_bits(const void* x, const void* qweight, const void* scales, const void* zeros,
-                void* y, int M, int N, int K, hipStream_t st) {
+int set_lds(GemvFn kern, size_t lds) {
+    if (lds <= 64 * 1024) return 0;
+    return (int)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
+// SC: inv_s folded into the x staging; FU: a gate/up pair with the SiLU * up output
+template <int BITS, int GS, bool SC, bool FU>
+int launch_bits(const GemvArgs& a, hipStream_t st) {
+    const int M = a.M, N = a.N, K = a.K;
     const int G = K / kGroup;
     const int NB = (N + 15) / 16;
     constexpr size_t WQ = BITS == 4 ? 4 : 3;
+    constexpr int NH = FU ? 2 : 1;
     // the kernels address their buffers with 32-bit offsets (the API rejects
     // larger matrices)
     if ((size_t)NB * G * 64 * WQ * 4 >= ((size_t)1 << 31)) return (int)hipErrorInvalidValue;
     const int cus = device_cu_count();
-    const size_t red = 2 * (size_t)kGemvWaves * 64 * 16;
-    const size_t x1_lds = (((size_t)M * (K + 8) * 2 + 15) & ~(size_t)15) + red;
-    if ((size_t)M * (K + 8) * 2 <= (size_t)kGemvXBuf) {
+    const int xl1 = ((G + kGemvWaves - 1) / kGemvWaves * M + 3) / 4;   // x1: x loads per lane
+    if ((size_t)M * (K + 8) * 2 <= (size_t)kGemvXBuf && (!SC || xl1 <= 4)) {
         // x staged once; persistent workgroups (as many as fit on a CU by LDS,
         // at most kGemvCuWaves waves)
-        auto kern = pick_x1<BITS, GS>(G <= 4 * kGemvWaves,
-                                  ((G + kGemvWaves - 1) / kGemvWaves * M + 3) / 4);   // x loads per lane
-        if (x1_lds > 64 * 1024) {
-            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)x1_lds);
-            if (e != hipSuccess) return (int)e;
-        }
-        const int per_cu = max(1, min(kGemvCuWaves / kGemvWaves, (int)((160 * 1024) / x1_lds)));
+        const size_t red = 2 * NH * (size_t)kGemvWaves * 64 * 16;
+        const size_t lds = (((size_t)M * (K + 8) * 2 + 15) & ~(size_t)15) + red;
+        auto kern = pick_x1<BITS, GS, SC, FU>(G <= 4 * kGemvWaves, xl1);
+        if (!kern) return (int)hipErrorInvalidValue;
+        if (int e = set_lds(kern, lds)) return e;
+        const int per_cu = max(1, min(kGemvCuWaves / kGemvWaves, (int)((160 * 1024) / lds)));
         const int grid = min(NB, cus * per_cu);
-        hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kGemvWaves), x1_lds, st,
-                           (const _Float16*)x, (const uint32_t*)qweight, (const _Float16*)scales,
-                           (const _Float16*)zeros, (_Float16*)y, M, N, K);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kGemvWaves), lds, st, a);
     } else {
         // K in slices of 16 groups; up to 2 row blocks per workgroup (4 per
         // workgroup reads x half as often but spills at M = 16; measured on
-        // MI355X, 8192x28672 at M = 16: 39.5 us with 2, 41.8 us with 4)
+        // MI355X, 8192x28672 at M = 16: 39.5 us with 2, 41.8 us with 4); a
+        // fused pair is one block of two layers, which reads x as often
         constexpr int SG = kGemvWaves * kGemvSliceRing;
-        const size_t lds = max(((size_t)M * (SG * kGroup + 8) * 2 + 15) & ~(size_t)15, red);
+        const size_t red = 2 * (size_t)kGemvWaves * 64 * 16;
+        const size_t xsl = ((size_t)M * (SG * kGroup + 8) * 2 + 15) & ~(size_t)15;
+        const size_t lds = max(xsl + (SC ? (size_t)SG * kGroup * 4 : 0), red);
         const int per_cu = max(1, min(kGemvCuWaves / kGemvWaves, (int)((160 * 1024) / lds)));
-        const int grid = max(min(NB, cus * per_cu), (NB + 1) / 2);
+        const int grid = FU ? NB : max(min(NB, cus * per_cu), (NB + 1) / 2);
         const int bmax = (NB + grid - 1) / grid;
-        auto kern = pick_xs<BITS, GS>(bmax, (kGemvSliceRing * M + 3) / 4);
-        if (lds > 64 * 1024) {
-            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            if (e != hipSuccess) return (int)e;
-        }
-        hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kGemvWaves), lds, st,
-                           (const _Float16*)x, (const uint32_t*)qweight, (const _Float16*)scales,
-                           (const _Float16*)zeros, (_Float16*)y, M, N, K);
+        auto kern = pick_xs<BITS, GS, SC, FU>(bmax, (kGemvSliceRing * M + 3) / 4);
+        if (int e = set_lds(kern, lds)) return e;
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kGemvWaves), lds, st, a);
     }
     return (int)hipGetLastError();
+}
+
+template <bool SC, bool FU>
+int launch_mode(const GemvArgs& a, int bits, int group_size, hipStream_t st) {
+    if (group_size == 64)
+        return bits == 4 ? launch_bits<4, 64, SC, FU>(a, st) : launch_bits<3, 64, SC, FU>(a, st);
+    return bits == 4 ? launch_bits<4, 128, SC, FU>(a, st) : launch_bits<3, 128, SC, FU>(a, st);
 }
 
 }  // namespace
@@ -563,13 +731,26 @@ int device_cu_count() {
     return 256;
 }
 
-int launch_gemv(const void* x, const void* qweight, const void* scales, const void* zeros,
+int launch_gemv(const void* x, const float* inv_s, const void* qweight, const void* scales,
+                const void* zeros, const void* qweight2, const void* scales2, const void* zeros2,
                 void* y, int M, int N, int K, int bits, int group_size, hipStream_t st) {
-    if (group_size == 64)
-        return bits == 4 ? launch_bits<4, 64>(x, qweight, scales, zeros, y, M, N, K, st)
-                         : launch_bits<3, 64>(x, qweight, scales, zeros, y, M, N, K, st);
-    return bits == 4 ? launch_bits<4, 128>(x, qweight, scales, zeros, y, M, N, K, st)
-                     : launch_bits<3, 128>(x, qweight, scales, zeros, y, M, N, K, st);
+    GemvArgs a{};
+    a.x = (const _Float16*)x;
+    a.inv_s = inv_s;
+    a.qweight[0] = (const uint32_t*)qweight;
+    a.scales[0] = (const _Float16*)scales;
+    a.zeros[0] = (const _Float16*)zeros;
+    a.qweight[1] = (const uint32_t*)qweight2;
+    a.scales[1] = (const _Float16*)scales2;
+    a.zeros[1] = (const _Float16*)zeros2;
+    a.y = (_Float16*)y;
+    a.M = M; a.N = N; a.K = K;
+    const bool fuse = qweight2 != nullptr;
+    if (inv_s)
+        return fuse ? launch_mode<true, true>(a, bits, group_size, st)
+                    : launch_mode<true, false>(a, bits, group_size, st);
+    return fuse ? launch_mode<false, true>(a, bits, group_size, st)
+                : launch_mode<false, false>(a, bits, group_size, st);
 }
 
 }  // namespace awq
