@@ -51,12 +51,14 @@ def gate_up(x, inv_s, g, u, N, bits, group_size):
     return host(h)
 
 
-# (M, N, K): x staged once with 1, 2 and 4 loads per lane, ragged N, one
-# group, and the sliced path (x too large for LDS, or more loads than the
-# scaled staging keeps in registers: M = 1 with K = 28672, M = 4 with K = 8192)
+# (M, N, K): x staged once with 1, 2, 4 and 8 loads per lane (8: M = 1 with
+# K = 28672, M = 13 with K = 2048, M = 16 with K = 1408; inv_s of chunks past
+# the fourth loaded behind the ring), ragged N, one group, and the sliced path
+# (x too large for LDS: M = 3 with K = 11008, M = 4 with K = 8192, M = 8 with
+# K = 4096; M = 16 with K = 4096 loads the next slice after the sweep)
 SHAPES = [(1, 512, 512), (1, 4096, 4096), (2, 37, 384), (4, 1000, 4096), (3, 130, 11008),
           (1, 64, 128), (1, 300, 28672), (4, 200, 8192), (8, 96, 4096), (13, 50, 2048),
-          (16, 600, 1408)]
+          (16, 600, 1408), (16, 200, 4096)]
 
 
 @pytest.mark.parametrize("group_size", [128, 64])
@@ -74,9 +76,9 @@ def test_gemv_scaled(gpu, M, N, K, bits, group_size):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (4, 1000, 4096), (1, 64, 128), (4, 200, 8192),
-                                   (3, 130, 11008)])
+                                   (3, 130, 11008), (1, 300, 28672), (16, 600, 1408), (16, 200, 4096)])
 def test_gemv_scaled_stages_x_prime_exactly(gpu, M, N, K):
-    """Same kernel as awq_gemv on the oracle's x' (x fits in LDS with <= 4
+    """Same kernel as awq_gemv on the oracle's x' (x fits in LDS with <= 8
     loads per lane, or takes the sliced path in both): identical bits."""
     import torch
     announce("gemv_scaled exact", f"M={M} N={N} K={K}")
@@ -93,7 +95,7 @@ def test_gemv_scaled_stages_x_prime_exactly(gpu, M, N, K):
 @pytest.mark.parametrize("bits", [4, 3])
 @pytest.mark.parametrize("M,N,K", [(1, 512, 512), (1, 1000, 4096), (2, 37, 384), (4, 700, 4096),
                                    (1, 64, 128), (3, 130, 11008), (1, 300, 28672), (5, 200, 8192),
-                                   (8, 96, 4096), (16, 600, 1408)])
+                                   (8, 96, 4096), (16, 600, 1408), (16, 200, 4096)])
 @pytest.mark.parametrize("scaled", [False, True])
 def test_gate_up(gpu, M, N, K, bits, group_size, scaled):
     announce("gate_up", f"M={M} N={N} K={K} bits={bits} gs={group_size} scaled={scaled}")

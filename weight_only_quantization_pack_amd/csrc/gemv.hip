@@ -244,14 +244,15 @@ __device__ __forceinline__ void accumulate_tile(const Slot<WQ>& w, const RawPara
 }
 
 // SCALE: x is multiplied by inv_s while it is staged (each lane loads the
-// scale of its own x chunks next to them, 32 bytes per chunk, so instances
-// with SCALE keep XL <= 4).  FUSE: the workgroup computes row block b of two
+// scale of its first 4 x chunks next to them, 32 bytes per chunk, and that of
+// further chunks after the ring's first loads; XL <= 8).  FUSE: the workgroup computes row block b of two
 // layers that read the same x (gate, then up): each wave's ring walks its
 // gate tiles of the block, then its up tiles, into two accumulators, and the
 // block's output is SiLU(gate) * up.
 template <int BITS, int GS, int WK, int U, int XL, bool SCALE, bool FUSE>
 __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(GemvArgs a) {
-    static_assert(!SCALE || XL <= 4, "scaled staging keeps 8 fp32 per x chunk in registers");
+    static_assert(!SCALE || XL <= 8, "scaled staging: at most 8 x loads per lane");
+    constexpr int SE = SCALE ? (XL < 4 ? XL : 4) : 0;  // chunks whose inv_s is loaded with x
     constexpr int WQ = BITS == 4 ? 4 : 3;
     constexpr int NH = FUSE ? 2 : 1;                   // layers per row block
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -314,7 +315,24 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(GemvArgs a
     const __amdgpu_buffer_rsrc_t ri = buffer_rsrc(a.inv_s, SCALE ? (uint32_t)K * 4u : 0u);
     uint4 xv[XL];
     uint32_t xat[XL];
-    float sv[SCALE ? XL : 1][8];
+    float sv[SE > 0 ? SE : 1][8];
+    auto load_inv_s = [&](int p, float* out) {
+        const uint32_t q = (uint32_t)((lane >> 4) + 4 * p);
+        const uint32_t i = (q * mdiv) >> 16;
+        const uint32_t col = (uint32_t)kGroup * (uint32_t)(wave + WK * (int)i) + 8u * (uint32_t)j;
+        const uint32_t so = (int)q < pairs ? col * 4u : kBufferOutOfRange;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const auto f = __builtin_amdgcn_raw_buffer_load_b128(ri, so + 16u * c, 0, 0);
+            // through a scalar: a bit_cast of the vector element itself
+            // keeps only element 0 of the load with this compiler
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t u = f[e];
+                out[4 * c + e] = __builtin_bit_cast(float, u);
+            }
+        }
+    };
 #pragma unroll
     for (int p = 0; p < XL; ++p) {
         const uint32_t q = (uint32_t)((lane >> 4) + 4 * p);
@@ -325,20 +343,7 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(GemvArgs a
             rx, ok ? (m * (uint32_t)K + col) * 2u : kBufferOutOfRange, 0, 0);
         xv[p] = make_uint4(v[0], v[1], v[2], v[3]);
         xat[p] = ok ? m * (uint32_t)XS + col : (uint32_t)K;
-        if constexpr (SCALE) {
-            const uint32_t so = ok ? col * 4u : kBufferOutOfRange;
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const auto f = __builtin_amdgcn_raw_buffer_load_b128(ri, so + 16u * c, 0, 0);
-                // through a scalar: a bit_cast of the vector element itself
-                // keeps only element 0 of the load with this compiler
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t u = f[e];
-                    sv[p][4 * c + e] = __builtin_bit_cast(float, u);
-                }
-            }
-        }
+        if (p < SE) load_inv_s(p, sv[p < SE ? p : 0]);
     }
     Slot<WQ> ring[U];
     RawParams pr[U];
@@ -352,7 +357,18 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_x1(GemvArgs a
 #pragma unroll
     for (int p = 0; p < XL; ++p) {
         uint4 v = xv[p];
-        if constexpr (SCALE) v = scale_chunk(v, sv[p]);
+        if constexpr (SCALE) {
+            if (p < SE) {
+                v = scale_chunk(v, sv[p < SE ? p : 0]);
+            } else {
+                // chunks past the first 4: inv_s loaded only now (behind the
+                // ring, once per workgroup), so it never shares registers with
+                // the first chunks' scales
+                float t[8];
+                load_inv_s(p, t);
+                v = scale_chunk(v, t);
+            }
+        }
         *reinterpret_cast<uint4*>(xs + xat[p]) = v;
     }
     // the wave's own LDS stores complete before its lanes read each other's chunks
@@ -430,10 +446,12 @@ using GemvFn = void (*)(GemvArgs);
 // loaded into registers during the current slice, ahead of its ring loads.
 // The waves' partial sums meet in LDS once per block at the end.
 //
-// SCALE: each wave also loads, one slice ahead, the inv_s of its U = 2 groups
-// of the next slice (one 16-byte load per lane), parks it in its own 1 KB of
-// LDS while staging, and multiplies every x chunk by the 8 values of the
-// chunk's columns on the way into the x slice.  FUSE: the workgroup owns one
+// SCALE: each wave also loads the inv_s of its U = 2 groups of the next slice
+// (one 16-byte load per lane), parks it in its own 1 KB of LDS while staging,
+// and multiplies every x chunk by the 8 values of the chunk's columns on the
+// way into the x slice; with 8 x loads per lane (M >= 13) the next slice's x
+// and inv_s are loaded at the end of the current slice rather than at its
+// start, which keeps them out of the registers live during the sweep.  FUSE: the workgroup owns one
 // row block of two layers reading the same x (gate, up; BMAX = 1) and keeps an
 // accumulator for each; the block's output is SiLU(gate) * up.
 template <int BITS, int GS, int WK, int U, int BMAX, int XL, bool SCALE, bool FUSE>
@@ -444,6 +462,7 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_xs(GemvArgs a
     constexpr int SG = WK * U;                         // groups per slice
     constexpr int XS = SG * kGroup + 8;                // halves per staged x row
     constexpr int NA = FUSE ? 2 : BMAX;                // accumulators: (block, layer) items
+    constexpr bool LATE = SCALE && XL > 4;             // next slice's x loaded after the sweep
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int M = a.M, N = a.N, K = a.K;
     _Float16* xs = reinterpret_cast<_Float16*>(smem);
@@ -558,8 +577,10 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_xs(GemvArgs a
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        load_x(s + 1, xv);
-        if constexpr (SCALE) sv = load_s(s + 1);
+        if constexpr (!LATE) {
+            load_x(s + 1, xv);
+            if constexpr (SCALE) sv = load_s(s + 1);
+        }
 #pragma unroll
         for (int k = 0; k < NA; ++k) {
 #pragma unroll
@@ -573,6 +594,14 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_xs(GemvArgs a
                 else
                     load(s + 1, 0, u, ring[u], pr[u]);
             }
+        }
+        if constexpr (LATE) {
+            // the next slice's x and inv_s only now, behind the ring refills of
+            // its first tiles (needed right after its staging anyway): they are
+            // not live during the sweep, which keeps M >= 13 within 128 VGPRs
+            __builtin_amdgcn_sched_barrier(0);
+            load_x(s + 1, xv);
+            sv = load_s(s + 1);
         }
         ++s;
     } while (s < NS);
@@ -646,16 +675,14 @@ GemvFn pick_xs(int bmax, int xl) {
 
 // k_gemv_x1 instance: ring depth (short rows: 2, else 4) and the number of
 // 16-byte x loads per lane that stage a wave's (group, row) pairs (<= 12:
-// M * K <= 32768 gives at most 48 pairs per wave; <= 4 with SCALE)
+// M * K <= 32768 gives at most 48 pairs per wave; <= 8 with SCALE)
 template <int BITS, int GS, bool SC, bool FU, int U>
 GemvFn pick_x1_loads(int xl) {
     if (xl <= 1) return k_gemv_x1<BITS, GS, kGemvWaves, U, 1, SC, FU>;
     if (xl <= 2) return k_gemv_x1<BITS, GS, kGemvWaves, U, 2, SC, FU>;
     if (xl <= 4) return k_gemv_x1<BITS, GS, kGemvWaves, U, 4, SC, FU>;
-    if constexpr (!SC) {
-        if (xl <= 8) return k_gemv_x1<BITS, GS, kGemvWaves, U, 8, SC, FU>;
-        return k_gemv_x1<BITS, GS, kGemvWaves, U, 12, SC, FU>;
-    }
+    if (xl <= 8) return k_gemv_x1<BITS, GS, kGemvWaves, U, 8, SC, FU>;
+    if constexpr (!SC) return k_gemv_x1<BITS, GS, kGemvWaves, U, 12, SC, FU>;
     return nullptr;
 }
 template <int BITS, int GS, bool SC, bool FU>
@@ -683,7 +710,7 @@ int launch_bits(const GemvArgs& a, hipStream_t st) {
     if ((size_t)NB * G * 64 * WQ * 4 >= ((size_t)1 << 31)) return (int)hipErrorInvalidValue;
     const int cus = device_cu_count();
     const int xl1 = ((G + kGemvWaves - 1) / kGemvWaves * M + 3) / 4;   // x1: x loads per lane
-    if ((size_t)M * (K + 8) * 2 <= (size_t)kGemvXBuf && (!SC || xl1 <= 4)) {
+    if ((size_t)M * (K + 8) * 2 <= (size_t)kGemvXBuf && (!SC || xl1 <= 8)) {
         // x staged once; persistent workgroups (as many as fit on a CU by LDS,
         // at most kGemvCuWaves waves)
         const size_t red = 2 * NH * (size_t)kGemvWaves * 64 * 16;
