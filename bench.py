@@ -354,6 +354,67 @@ def main(argv=None):
         log(f"  variant decode step int{bits} g{gs}: {us:.2f} us, {sb / (us * 1e-6) / 1e9:.1f} GB/s")
         del vreps, g
         torch.cuda.empty_cache()
+    # the same layer with the fused modules of "transformers - AWQ": q/k/v as
+    # one product over their concatenated rows (N = 3 x 4096), o, the gate/up
+    # pair in one launch with SiLU(g) * u (awq_gemv_gate_up), down on h --
+    # 4 launches instead of 7, the same weight bytes
+    with torch.cuda.stream(stream):
+        base = {}
+        for (K, N), i in shape_index.items():
+            W = torch.from_numpy(wl2.weights(i)).to(dev)
+            base[(K, N)] = awq.quantize_pack(W, None, bits=4)
+            del W
+        q4 = base[(4096, 4096)]
+        qkv = tuple(torch.cat([t, t, t]) for t in q4)      # 16-row blocks: rows concatenate
+    fused_bytes = (gemv_bytes(1, 3 * 4096, 4096) + gemv_bytes(1, 4096, 4096)
+                   + 2 * (11008 * 4096 // 2 + 4 * 11008 * 32) + 2 * 4096 + 2 * 11008
+                   + gemv_bytes(1, 4096, 11008))
+    Rf = max(2, math.ceil(COLD_BYTES / weight_bytes))
+    freps = [(tuple(t.clone() for t in qkv), tuple(t.clone() for t in q4),
+              tuple(t.clone() for t in base[(4096, 11008)]), tuple(t.clone() for t in base[(4096, 11008)]),
+              tuple(t.clone() for t in base[(11008, 4096)])) for _ in range(Rf)]
+    del base, qkv, q4
+    y_qkv = torch.empty((1, 3 * 4096), dtype=torch.float16, device=dev)
+    y_o = torch.empty((1, 4096), dtype=torch.float16, device=dev)
+    h = torch.empty((1, 11008), dtype=torch.float16, device=dev)
+    y_d = torch.empty((1, 4096), dtype=torch.float16, device=dev)
+
+    def fused_step(r):
+        qkv_w, o_w, g_w, u_w, d_w = freps[r]
+        awq.gemv(xs[4096], *qkv_w, N=3 * 4096, out=y_qkv)
+        awq.gemv(xs[4096], *o_w, N=4096, out=y_o)
+        awq.gemv_gate_up(xs[4096], g_w, u_w, N=11008, out=h)
+        awq.gemv(xs[11008], *d_w, N=4096, out=y_d)
+
+    with torch.cuda.stream(stream):
+        for r in range(Rf):
+            fused_step(r)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for r in range(Rf):
+            fused_step(r)
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_rep = max(2, 200 // Rf)
+        a.record(stream)
+        for _ in range(n_rep):
+            g.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / (n_rep * Rf)
+    variants["decode_step_fused_modules"] = {
+        "us": round(us, 2), "GBps": round(fused_bytes / (us * 1e-6) / 1e9, 1),
+        "frac_hbm": round(fused_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "step_bytes": fused_bytes,
+        "launches": ["gemv qkv 4096x12288", "gemv o 4096x4096", "gemv_gate_up 4096x11008",
+                     "gemv down 11008x4096"]}
+    log(f"  variant decode step fused modules: {us:.2f} us, {fused_bytes / (us * 1e-6) / 1e9:.1f} GB/s")
+    del freps, g
+    torch.cuda.empty_cache()
+
     tot3_flops, tot3_ms = 0.0, 0.0
     for i, (K, N) in enumerate(wl4.shapes):
         with torch.cuda.stream(stream):
@@ -438,7 +499,7 @@ def main(argv=None):
                      "unit": "GB/s", "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
                      "traffic": gemv_traffic_per_launch(), "traffic_unit": "HBM bytes per launch",
                      "algorithmic_bytes_per_launch": round(step_bytes / len(layer)),
-                     "kernel": "k_gemv_x1<4,8,U> (ring U=2 for K=4096, U=4 for K=11008)", "avg_launch_us": round(avg_launch_us, 3)},
+                     "kernel": "k_gemv_x1<4,128,8,U,XL,false,false> (ring U=2, XL=1 for K=4096; U=4, XL=4 for K=11008)", "avg_launch_us": round(avg_launch_us, 3)},
         "gemv_per_shape": per_shape,
         "batched_decode_llama70b_mlp": batched,
         "variants": variants,
