@@ -486,6 +486,22 @@ def search_scale(W: np.ndarray, X_cal: np.ndarray, alphas, bits: int = 4,
     return candidate_scale(s_x, alphas[best]), losses, best
 
 
+def search_scale_shared(Ws, X_cal: np.ndarray, alphas, bits: int = 4,
+                        group_size: int = GROUP_SIZE, zero_point: bool = True):
+    """One alpha (one s) for several layers that read the same input.
+
+    [P5] 02.02: the activations are divided by s once, before the layers that
+    read them, so every layer fed by that input must carry the same s
+    (reading: q/k/v after one norm, gate/up after another); [P1] "Usage"
+    step 1 searches per model.  Reading: the loss is the output MSE over all
+    the layers' outputs together, i.e. the search of the layer whose rows are
+    the layers' rows one after the other -- so it is that search, written out.
+    Returns (s_best fp32 [K], losses fp64 [n_alpha], best index).
+    """
+    W = np.concatenate([np.asarray(w, dtype=np.float16) for w in Ws], axis=0)
+    return search_scale(W, X_cal, alphas, bits, group_size, zero_point)
+
+
 def awq_quantize_layer(W: np.ndarray, X_cal: np.ndarray, alphas, bits: int = 4,
                        zero_point: bool = True, group_size: int = GROUP_SIZE):
     """Whole offline pass: search, then quantize and pack with the chosen s."""
