@@ -162,6 +162,27 @@ int awq_search_scale(const void* W, const void* X_cal, int T, int N, int K,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * awq_search_scale_shared -- one scale search for several layers that read
+ * the same input (q/k/v after one norm, gate/up after another): the
+ * activations are divided by s once (section 02.02 "AWQ" of the VPTQ blog), so
+ * every layer fed by that input carries the same s.
+ *   The layers' rows, in order, are searched as the rows of one layer of
+ *   N = sum Ns[l] rows: L_i is the mean over t and every row of every layer,
+ *   i.e. the row-weighted mean of the layers' own losses; everything else as
+ *   awq_search_scale.  Each layer is read in place (no copy).
+ *   Ws       HOST array of n_layers device pointers, layer l fp16 [Ns[l]][K]
+ *   Ns       HOST int array [n_layers], each >= 1;  1 <= n_layers <= 8
+ *   workspace: awq_search_workspace_bytes(T, sum Ns, K, n_alpha) bytes.
+ *   Errors as awq_search_scale; n_layers out of range is AWQ_ERR_UNSUPPORTED,
+ *   a NULL Ws / Ns / layer pointer AWQ_ERR_NULL, a row count <= 0 AWQ_ERR_SHAPE.
+ */
+int awq_search_scale_shared(const void* const* Ws, const int* Ns, int n_layers,
+                            const void* X_cal, int T, int K, const float* alphas,
+                            int n_alpha, int bits, int group_size, int zero_point,
+                            float* s_out, float* loss_out, int* best_out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * awq_gemv -- decode-stage W4A16 (or W3A16) product for small batches (the
  * decode kernel of the llm-awq README feature list):
  *   y[m][n] = sum_g D[n][g] * sum_{k in g} x[m][k] * (q[n][k] - z[n][g])

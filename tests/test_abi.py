@@ -214,6 +214,40 @@ def test_search_validation(lib):
     assert search(lib, ws_bytes=good - 1) == WS
 
 
+def shared(lib, Ws=(P, P2, P3), Ns=(64, 32, 32), n=None, X=P4, T=64, K=512, alphas=(0.0, 0.5),
+           bits=4, gs=128, zp=1, s_out=P5, loss=NUL, best=NUL, ws=P, ws_bytes=None):
+    n = (3 if Ws is None else len(Ws)) if n is None else n
+    if ws_bytes is None:
+        ws_bytes = lib.awq_search_workspace_bytes(T, max(1, sum(Ns or (1,))), K, max(1, len(alphas)))
+    wp = (ctypes.c_void_p * max(1, len(Ws)))(*[w.value for w in Ws]) if Ws is not None else None
+    npt = (ctypes.c_int * max(1, len(Ns)))(*Ns) if Ns is not None else None
+    a = (ctypes.c_float * max(1, len(alphas)))(*alphas)
+    return lib.awq_search_scale_shared(ctypes.cast(wp, ctypes.c_void_p) if wp is not None else NUL,
+                                       ctypes.cast(npt, ctypes.c_void_p) if npt is not None else NUL,
+                                       n, X, T, K, ctypes.cast(a, ctypes.c_void_p), len(alphas), bits,
+                                       gs, zp, s_out, loss, best, ws, ws_bytes, NUL)
+
+
+def test_search_shared_validation(lib):
+    assert shared(lib, n=0) == UNSUP
+    assert shared(lib, Ws=tuple([P] * 9), Ns=tuple([16] * 9)) == UNSUP
+    assert shared(lib, Ws=None) == NULL
+    assert shared(lib, Ns=None) == NULL
+    assert shared(lib, Ws=(P, NUL, P3)) == NULL
+    assert shared(lib, Ws=(P, MIS, P3)) == ALIGN
+    assert shared(lib, Ns=(64, 0, 32)) == SHAPE
+    assert shared(lib, Ns=(64, -5, 32)) == SHAPE
+    assert shared(lib, K=130) == SHAPE
+    assert shared(lib, T=0) == SHAPE
+    assert shared(lib, T=8193) == UNSUP
+    assert shared(lib, alphas=()) == UNSUP
+    assert shared(lib, bits=5) == UNSUP
+    assert shared(lib, X=NUL) == NULL
+    assert shared(lib, s_out=MIS) == ALIGN
+    good = lib.awq_search_workspace_bytes(64, 128, 512, 2)
+    assert shared(lib, ws_bytes=good - 1) == WS
+
+
 def test_binding_refuses_when_library_missing(monkeypatch, tmp_path):
     monkeypatch.setenv("AWQ_MI355X_LIB", str(tmp_path / "nope.so"))
     monkeypatch.setattr(B, "_lib", None)

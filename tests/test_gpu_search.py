@@ -138,3 +138,73 @@ def test_workload1_end_to_end(gpu):
             y = getattr(awq, fn)(xs, qw, sc, ze, N=W.shape[0], bits=4)
             torch.cuda.synchronize()
             assert rel_err(host(y), y_ref) <= TOL, fn
+
+
+# ----------------------------------------------------------------------------- shared input
+def check_shared(Ws, X, alphas, bits=4, zero_point=True, group_size=128):
+    import torch
+    announce("search_scale_shared", [w.shape for w in Ws], X.shape, len(alphas), bits)
+    s_g, loss_g, best_g = awq.search_scale_shared([dev(W) for W in Ws], dev(X), alphas, bits=bits,
+                                                  group_size=group_size, zero_point=zero_point)
+    torch.cuda.synchronize()
+    s_g, loss_g, best_g = host(s_g), host(loss_g).astype(np.float64), int(host(best_g)[0])
+    s_r, loss_r, best_r = O.search_scale_shared(Ws, X, alphas, bits, group_size, zero_point)
+    assert np.allclose(loss_g, loss_r, rtol=1e-2, atol=0), (loss_g, loss_r)
+    assert best_g == best_r or loss_r[best_g] <= (1 + 1e-3) * loss_r[best_r], (best_g, best_r)
+    s_expect = O.candidate_scale(O.act_stat(X), alphas[best_g])
+    ulp = np.abs(s_g.view(np.int32).astype(np.int64) - s_expect.view(np.int32).astype(np.int64))
+    assert ulp.max() <= 1, f"s differs by {ulp.max()} ulp"
+    return s_g, loss_g, best_g
+
+
+@pytest.mark.parametrize("bits", [4, 3])
+def test_shared_search_qkv_like(gpu, bits):
+    """q, k, v of a grouped-query layer (k, v narrower), ragged row counts."""
+    K = 1024
+    Ws = [WL.random_weights(n, K, seed=50 + i) for i, n in enumerate((512, 128, 128))]
+    Ws[0][:, :4] *= 20
+    X = WL.random_activations(256, K, seed=60, sigma=1.5)
+    check_shared(Ws, X, [i / 10 for i in range(10)], bits)
+
+
+def test_shared_search_equals_search_of_the_stacked_layer(gpu):
+    """In-place multi-layer reads give the same bits as one layer holding the
+    rows one after the other (same D layout, same fixed-order reductions)."""
+    import torch
+    K = 512
+    Ws = [WL.random_weights(n, K, seed=70 + i) for i, n in enumerate((77, 16, 200, 33))]
+    X = WL.random_activations(128, K, seed=71, sigma=1.5)
+    alphas = [0.0, 0.25, 0.5, 0.75]
+    s_a, loss_a, best_a = check_shared(Ws, X, alphas, 4)
+    s_b, loss_b, best_b = awq.search_scale(dev(np.concatenate(Ws)), dev(X), alphas, bits=4)
+    torch.cuda.synchronize()
+    assert np.array_equal(s_a, host(s_b)) and best_a == int(host(best_b)[0])
+    assert np.array_equal(loss_a.astype(np.float32), host(loss_b))
+
+
+@pytest.mark.parametrize("zero_point,group_size", [(False, 128), (True, 64)])
+def test_shared_search_variants(gpu, zero_point, group_size):
+    K = 384
+    Ws = [WL.random_weights(n, K, seed=80 + i) for i, n in enumerate((96, 48))]
+    X = WL.random_activations(100, K, seed=81, sigma=1.5)
+    check_shared(Ws, X, [0.0, 0.3, 0.6, 0.9], 4, zero_point, group_size)
+
+
+def test_shared_search_gate_up_then_fused_pass(gpu):
+    """gate/up share one s: search, pack both with it, run the fused
+    gate/up GEMV with inv_s = 1/s, compare with the oracle end to end."""
+    import torch
+    K, N = 512, 256
+    Wg = WL.random_weights(N, K, seed=90)
+    Wu = WL.random_weights(N, K, seed=91)
+    X = WL.random_activations(128, K, seed=92, sigma=1.5)
+    s_g, _, _ = check_shared([Wg, Wu], X, [i / 10 for i in range(10)], 4)
+    gate = awq.quantize_pack(dev(Wg), dev(s_g), bits=4)
+    up = awq.quantize_pack(dev(Wu), dev(s_g), bits=4)
+    inv_s = (np.float32(1) / s_g).astype(np.float32)
+    x = WL.random_activations(4, K, seed=93, sigma=1.5)
+    h = awq.gemv_gate_up(dev(x), gate, up, N=N, inv_s=dev(inv_s))
+    torch.cuda.synchronize()
+    pg, pu = O.quantize(Wg, s_g, 4), O.quantize(Wu, s_g, 4)
+    h_ref = O.gate_up(x, inv_s, (O.pack(pg[0], 4), pg[1], pg[2]), (O.pack(pu[0], 4), pu[1], pu[2]), 4, K)
+    assert rel_err(host(h), h_ref) <= TOL

@@ -31,6 +31,9 @@ SIGNATURES = [
     ("awq_search_scale", _c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_int,
                                   _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p,
                                   _c_void_p, _c_size_t, _c_void_p]),
+    ("awq_search_scale_shared", _c_int, [_c_void_p, _c_void_p, _c_int, _c_void_p, _c_int, _c_int,
+                                         _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p,
+                                         _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     ("awq_gemv", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                           _c_int, _c_int, _c_int, _c_void_p]),
     ("awq_gemm", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
@@ -210,6 +213,39 @@ def _need_layer(qweight, scales, zeros, N, K, bits, group_size, what=""):
     NB = (N + 15) // 16
     _need(scales, torch.float16, (NB, G, 16), what + "scales")
     _need(zeros, torch.float16, (NB, G, 16), what + "zeros")
+
+
+def search_scale_shared(Ws, X_cal, alphas, bits: int = 4, group_size: int = GROUP_SIZE,
+                        zero_point: bool = True, workspace=None):
+    """One s for several layers reading X_cal (awq_search_scale_shared): the
+    layers' rows together form the searched layer.  Returns (s fp32 [K],
+    losses fp32 [n_alpha], best int32 [1]) as search_scale."""
+    torch = _torch()
+    lib = load_library()
+    Ws = list(Ws)
+    if not Ws:
+        raise ValueError("Ws must hold at least one layer")
+    T, K = X_cal.shape
+    _need(X_cal, torch.float16, (T, K), "X_cal")
+    for i, W in enumerate(Ws):
+        _need(W, torch.float16, (W.shape[0], K), f"Ws[{i}]")
+    n = len(Ws)
+    ptrs = (_c_void_p * n)(*[W.data_ptr() for W in Ws])
+    Ns = (ctypes.c_int * n)(*[int(W.shape[0]) for W in Ws])
+    a = (ctypes.c_float * len(alphas))(*[float(v) for v in alphas])
+    n_alpha = len(alphas)
+    need = int(lib.awq_search_workspace_bytes(T, sum(Ns), K, n_alpha))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X_cal.device)
+    s_out = torch.empty(K, dtype=torch.float32, device=X_cal.device)
+    loss = torch.empty(max(n_alpha, 1), dtype=torch.float32, device=X_cal.device)
+    best = torch.empty(1, dtype=torch.int32, device=X_cal.device)
+    st = lib.awq_search_scale_shared(ctypes.cast(ptrs, _c_void_p), ctypes.cast(Ns, _c_void_p), n,
+                                     _ptr(X_cal), T, K, ctypes.cast(a, _c_void_p), n_alpha, bits,
+                                     group_size, int(zero_point), _ptr(s_out), _ptr(loss), _ptr(best),
+                                     _ptr(workspace), workspace.numel(), _stream_ptr(X_cal))
+    _check(st, "awq_search_scale_shared")
+    return s_out, loss[:n_alpha], best
 
 
 def _matmul(fn_name, x, qweight, scales, zeros, N, bits, group_size, out, workspace=None):

@@ -109,8 +109,39 @@ int awq_search_scale(const void* W, const void* X_cal, int T, int N, int K, cons
     if (loss_out != nullptr && (st = check_ptr(loss_out))) return st;
     if (best_out != nullptr && (st = check_ptr(best_out))) return st;
     if (workspace_bytes < awq::search_workspace_bytes(T, N, K, n_alpha)) return AWQ_ERR_WORKSPACE;
-    return hip_status(awq::launch_search(W, X_cal, T, N, K, alphas, n_alpha, bits, group_size, zero_point, s_out,
-                                         loss_out, best_out, workspace, (hipStream_t)stream));
+    return hip_status(awq::launch_search(&W, &N, 1, X_cal, T, K, alphas, n_alpha, bits, group_size,
+                                         zero_point, s_out, loss_out, best_out, workspace,
+                                         (hipStream_t)stream));
+}
+
+int awq_search_scale_shared(const void* const* Ws, const int* Ns, int n_layers, const void* X_cal,
+                            int T, int K, const float* alphas, int n_alpha, int bits, int group_size,
+                            int zero_point, float* s_out, float* loss_out, int* best_out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_quant_params(bits, group_size, zero_point);
+    if (st) return st;
+    if (n_alpha < 1 || n_alpha > kMaxAlpha) return AWQ_ERR_UNSUPPORTED;
+    if (n_layers < 1 || n_layers > awq::kMaxSearchLayers) return AWQ_ERR_UNSUPPORTED;
+    if (T > kMaxT) return AWQ_ERR_UNSUPPORTED;
+    if (Ws == nullptr || Ns == nullptr || alphas == nullptr) return AWQ_ERR_NULL;
+    long long N = 0;
+    for (int l = 0; l < n_layers; ++l) {
+        if (Ns[l] <= 0) return AWQ_ERR_SHAPE;
+        N += Ns[l];
+    }
+    if (T <= 0 || N > (1LL << 30)) return AWQ_ERR_SHAPE;
+    if ((st = check_nk((int)N, K))) return st;
+    for (int l = 0; l < n_layers; ++l)
+        if (Ws[l] == nullptr) return AWQ_ERR_NULL;
+    if ((st = check_ptrs({X_cal, s_out, workspace}))) return st;
+    for (int l = 0; l < n_layers; ++l)
+        if ((st = check_ptr(Ws[l]))) return st;
+    if (loss_out != nullptr && (st = check_ptr(loss_out))) return st;
+    if (best_out != nullptr && (st = check_ptr(best_out))) return st;
+    if (workspace_bytes < awq::search_workspace_bytes(T, (int)N, K, n_alpha)) return AWQ_ERR_WORKSPACE;
+    return hip_status(awq::launch_search(Ws, Ns, n_layers, X_cal, T, K, alphas, n_alpha, bits,
+                                         group_size, zero_point, s_out, loss_out, best_out,
+                                         workspace, (hipStream_t)stream));
 }
 
 namespace {

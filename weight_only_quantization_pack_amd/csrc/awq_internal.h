@@ -137,8 +137,12 @@ size_t search_workspace_bytes(int T, int N, int K, int n_alpha);
 size_t loss_gemm_tiles(int T, int N);
 int launch_loss_gemm(const void* X, const void* D, int T, int N, int K, int n_batch,
                      double* partials, hipStream_t st);
-int launch_search(const void* W, const void* X_cal, int T, int N, int K, const float* alphas,
-                  int n_alpha, int bits, int group_size, int zero_point, float* s_out,
-                  float* loss_out, int* best_out, void* workspace, hipStream_t st);
+// layers searched together (shared input): at most this many
+constexpr int kMaxSearchLayers = 8;
+// Ws / Ns: host arrays of n_layers device weight pointers and row counts;
+// the layers' rows in order form the N = sum Ns rows of the search
+int launch_search(const void* const* Ws, const int* Ns, int n_layers, const void* X_cal, int T, int K,
+                  const float* alphas, int n_alpha, int bits, int group_size, int zero_point,
+                  float* s_out, float* loss_out, int* best_out, void* workspace, hipStream_t st);
 
 }  // namespace awq

@@ -11,6 +11,10 @@
 // live side by side in the workspace; W is read once for all of them), so
 // the loss GEMM grid has n_alpha x tiles workgroups.  The reductions run in a fixed order, so the
 // result does not depend on scheduling.
+//
+// Several layers that read the same input (q/k/v, gate/up) take one search:
+// their rows are treated as the rows of one layer (read in place from each
+// layer's own buffer) and the loss averages over all their outputs.
 #include "awq_internal.h"
 
 namespace awq {
@@ -19,6 +23,14 @@ namespace {
 
 constexpr int kMaxAlpha = 64;
 struct AlphaGrid { float a[kMaxAlpha]; };
+
+// the layers searched together: their rows one after the other, layer l's
+// 16-byte chunks starting at chunk cstart[l] of the whole (cstart[0] = 0)
+struct LayerList {
+    const uint4* w[kMaxSearchLayers];
+    long long cstart[kMaxSearchLayers];
+    int n;
+};
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -78,7 +90,7 @@ __global__ __launch_bounds__(256) void k_candidate_scales(const float* __restric
 // multiplies by the reciprocal of s (within 1.5 fp32 ulp of w_hat / s before
 // D's own fp16 rounding), which halves the divisions of this VALU-bound loop.
 template <int Q, bool ZP, int GS>
-__global__ __launch_bounds__(256) void k_quant_err(const uint4* __restrict__ W,
+__global__ __launch_bounds__(256) void k_quant_err(LayerList layers,
                                                   const float* __restrict__ s_all,
                                                   const float* __restrict__ s_inv, int K,
                                                   long long n_chunks, int n_alpha,
@@ -86,9 +98,14 @@ __global__ __launch_bounds__(256) void k_quant_err(const uint4* __restrict__ W,
     const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     const bool active = t < n_chunks;
     const int k0 = active ? (int)(t % (K / 8)) * 8 : 0;
+    // this chunk's layer (rows never straddle layers: a layer holds whole rows)
+    const uint4* src = layers.w[0] + t;
+#pragma unroll
+    for (int l = 1; l < kMaxSearchLayers; ++l)
+        if (l < layers.n && t >= layers.cstart[l]) src = layers.w[l] + (t - layers.cstart[l]);
     float w[8];
     {
-        const uint4 raw = active ? W[t] : make_uint4(0, 0, 0, 0);
+        const uint4 raw = active ? *src : make_uint4(0, 0, 0, 0);
         const _Float16* h = reinterpret_cast<const _Float16*>(&raw);
 #pragma unroll
         for (int i = 0; i < 8; ++i) w[i] = (float)h[i];
@@ -169,9 +186,17 @@ static auto pick_quant_err(int bits, int zero_point) {
                      : (zero_point ? k_quant_err<7, true, GS> : k_quant_err<7, false, GS>);
 }
 
-int launch_search(const void* W, const void* X_cal, int T, int N, int K, const float* alphas,
-                  int n_alpha, int bits, int group_size, int zero_point, float* s_out,
-                  float* loss_out, int* best_out, void* workspace, hipStream_t st) {
+int launch_search(const void* const* Ws, const int* Ns, int n_layers, const void* X_cal, int T, int K,
+                  const float* alphas, int n_alpha, int bits, int group_size, int zero_point,
+                  float* s_out, float* loss_out, int* best_out, void* workspace, hipStream_t st) {
+    LayerList layers{};
+    int N = 0;
+    for (int l = 0; l < n_layers; ++l) {
+        layers.w[l] = static_cast<const uint4*>(Ws[l]);
+        layers.cstart[l] = (long long)N * (K / 8);
+        N += Ns[l];
+    }
+    layers.n = n_layers;
     const Layout L = layout(T, N, K, n_alpha);
     char* ws = static_cast<char*>(workspace);
     float* s_x = reinterpret_cast<float*>(ws + L.sx);
@@ -191,7 +216,7 @@ int launch_search(const void* W, const void* X_cal, int T, int N, int K, const f
     const long long n_chunks = (long long)N * K / 8;
     auto qerr = group_size == 64 ? pick_quant_err<64>(bits, zero_point)
                                  : pick_quant_err<128>(bits, zero_point);
-    hipLaunchKernelGGL(qerr, dim3((unsigned)((n_chunks + 255) / 256)), dim3(256), 0, st, (const uint4*)W,
+    hipLaunchKernelGGL(qerr, dim3((unsigned)((n_chunks + 255) / 256)), dim3(256), 0, st, layers,
                        s_all, s_inv, K, n_chunks, n_alpha, (uint4*)D);
     int err = (int)hipGetLastError();
     if (err) return err;
