@@ -182,34 +182,39 @@ def main(argv=None):
     log(f"decode step {ms_per_step * 1e3:.2f} us  ->  {gemv_gbs:.1f} GB/s "
         f"({100 * gemv_gbs / HBM_PEAK_GBS:.1f}% of HBM peak); avg launch {avg_launch_us:.2f} us")
 
-    # per-shape GEMV times (same graph technique, one shape per graph)
+    # per-shape GEMV times (same graph technique, one shape per graph, its own
+    # >= 768 MB of replicas so that the shape is as cold as in the step)
+    del reps
     per_shape = {}
     for (K, N) in wl2.shapes:
         j = layer.index((K, N))
+        Rs = max(2, math.ceil(COLD_BYTES / (N * K // 2 + 4 * N * (K // 128))))
+        sreps = [tuple(t.clone() for t in packed[(K, N)]) for _ in range(Rs)]
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            for r in range(R):
-                qw, sc, ze = reps[r][j]
+            for r in range(Rs):
+                qw, sc, ze = sreps[r]
                 awq.gemv(xs[K], qw, sc, ze, N=N, bits=4, out=ys[j])
         with torch.cuda.stream(stream):
             for _ in range(3):
                 g.replay()
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            n_rep = max(1, 200 // R)
+            n_rep = max(2, 400 // Rs)
             a.record(stream)
             for _ in range(n_rep):
                 g.replay()
             b.record(stream)
         torch.cuda.synchronize()
-        us = a.elapsed_time(b) * 1e3 / (n_rep * R)
+        us = a.elapsed_time(b) * 1e3 / (n_rep * Rs)
         gbs = gemv_bytes(1, N, K) / (us * 1e-6) / 1e9
         per_shape[f"{K}x{N}"] = {"us": round(us, 3), "GBps": round(gbs, 1),
-                                 "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+                                 "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "cold_replicas": Rs}
         log(f"  gemv K={K} N={N}: {us:.2f} us, {gbs:.1f} GB/s")
-        del g
+        del g, sreps
+        torch.cuda.empty_cache()
 
-    del reps, packed
+    del packed
     torch.cuda.empty_cache()
 
     # --------------------------------------------- batched decode (context, not the metric)

@@ -120,6 +120,15 @@ struct Params { _Float16 d, z; };
 #define AWQ_GEMV_MINBLK 4
 #endif
 
+// cache policy of the weight tile loads: nt (non-temporal; each byte is read
+// once per launch).  Measured on MI355X against the default policy: 4096x4096
+// 4.40 vs 4.69 us, 4096x11008 7.09 vs 7.55 us, 8192x28672 / 28672x8192 about
+// 3 % faster; sc1 alone changed nothing.  x keeps the default: every
+// workgroup reads it.
+#ifndef AWQ_GEMV_CPOL
+#define AWQ_GEMV_CPOL 2
+#endif
+
 constexpr uint32_t kBufferOutOfRange = 0x80000000u;   // > every buffer's size (< 2^31 bytes)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
@@ -131,10 +140,10 @@ template <int WQ>
 __device__ __forceinline__ Slot<WQ> buffer_slot(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     Slot<WQ> s;
     if constexpr (WQ == 4) {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AWQ_GEMV_CPOL);
         s.w[0] = v[0]; s.w[1] = v[1]; s.w[2] = v[2]; s.w[3] = v[3];
     } else {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, AWQ_GEMV_CPOL);
         s.w[0] = v[0]; s.w[1] = v[1]; s.w[2] = v[2];
     }
     return s;
