@@ -49,7 +49,7 @@ SUPPORTED_BITS = (3, 4)
 SPAN_FLOOR = np.float32(1e-5)      # reading: (hi - lo), or max |v|, floored before the divide
 STAT_FLOOR = 1e-4                  # reading: s_x floored before the power
 
-PACK_FORMAT_VERSION = 2
+PACK_FORMAT_VERSION = 3
 
 
 def levels(bits: int) -> int:
@@ -195,7 +195,7 @@ def dequantize(q: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
 
 
 # ---------------------------------------------------------------------------
-# a6: packing (format version 2, chosen for gfx950)
+# a6: packing (format version 3, chosen for gfx950)
 # ---------------------------------------------------------------------------
 ROW_BLOCK = 16          # rows of one packed tile
 QUARTER = 32            # codes of one lane slot in a tile
@@ -212,8 +212,12 @@ def pack_rows(q: np.ndarray, bits: int) -> np.ndarray:
     is at bits 4t..4t+3 and code 8j+2t+1 at bits 16+4t..19+4t (t = 0..3),
     so (word >> 4t) & 0x000F000F holds the pair (q[8j+2t], q[8j+2t+1]) in
     its two 16-bit halves.
-    bits=3 (W = 3K/32): each run of 32 codes k = 32c..32c+31 is a 96-bit
-    little-endian bit stream (code i at stream bits 3i..3i+2) in 3 words.
+    bits=3 (W = 3K/32): each run of 32 codes c_0..c_31 (k = 32r + i) fills 3
+    words.  Pair P = (c_2P, c_2P+1), P = 0..14, sits in word P // 5 with c_2P
+    at bits 3t..3t+2 and c_2P+1 at bits 16+3t..18+3t (t = P % 5), so that
+    (word >> 3t) & 0x00070007 holds the pair in its two 16-bit halves, like
+    the int4 nibble pairs; the last pair spreads over the spare bits: bit b of
+    c_30 is bit 15 of word b, bit b of c_31 is bit 31 of word b.
     """
     q = np.asarray(q, dtype=np.uint8)
     N, K = q.shape
@@ -229,17 +233,21 @@ def pack_rows(q: np.ndarray, bits: int) -> np.ndarray:
         return word
     c = q.reshape(N, K // 32, 32).astype(np.uint32)
     out = np.zeros((N, K // 32, 3), dtype=np.uint32)
-    for i in range(32):
-        for b in range(3):
-            pos = 3 * i + b
-            bit = (c[:, :, i] >> np.uint32(b)) & np.uint32(1)
-            out[:, :, pos // 32] |= bit << np.uint32(pos % 32)
+    for P in range(15):
+        w, t = divmod(P, 5)
+        out[:, :, w] |= c[:, :, 2 * P] << np.uint32(3 * t)
+        out[:, :, w] |= c[:, :, 2 * P + 1] << np.uint32(16 + 3 * t)
+    for b in range(3):
+        out[:, :, b] |= ((c[:, :, 30] >> np.uint32(b)) & np.uint32(1)) << np.uint32(15)
+        out[:, :, b] |= ((c[:, :, 31] >> np.uint32(b)) & np.uint32(1)) << np.uint32(31)
     return out.reshape(N, 3 * (K // 32))
 
 
 def pack(q: np.ndarray, bits: int) -> np.ndarray:
-    """Packed weights, format 2: tiles of 16 rows x 128 codes (one 128-group or
+    """Packed weights, format 3: tiles of 16 rows x 128 codes (one 128-group or
     two 64-groups; the codes' layout does not depend on the group size).
+    Format 3 is format 2 with the int3 pair layout of ``pack_rows`` (int4 as
+    before).
 
     The row words of ``pack_rows`` are regrouped so that the 16 rows of
     block b and the group g form one contiguous tile of 64 lane slots:
@@ -302,8 +310,12 @@ def unpack(words: np.ndarray, bits: int, K: int, N: int | None = None) -> np.nda
                 i, e = divmod(kk, 8)
                 pos = 4 * (e // 2) + 16 * (e % 2) + b
             else:
-                p = 3 * kk + b
-                i, pos = divmod(p, 32)
+                P, odd = divmod(kk, 2)
+                if P < 15:
+                    i, tp = divmod(P, 5)
+                    pos = 3 * tp + 16 * odd + b
+                else:
+                    i, pos = b, 15 + 16 * odd
             for n in range(N):
                 blk, j = divmod(n, ROW_BLOCK)
                 w = t[blk, g, 16 * h + j, i]
@@ -378,20 +390,15 @@ def unpack_fast(words: np.ndarray, bits: int, K: int, N: int | None = None) -> n
         r = np.arange(8, dtype=np.uint32)
         shift = 4 * (r // 2) + 16 * (r % 2)
         return ((w >> shift[None, None, :]) & np.uint32(15)).astype(np.uint8).reshape(N, K)
-    w = rows.reshape(N, K // 32, 3).astype(np.uint64)
-    stream_lo = w[:, :, 0] | (w[:, :, 1] << np.uint64(32))      # bits 0..63
-    stream_hi = w[:, :, 2]                                       # bits 64..95
+    w = rows.reshape(N, K // 32, 3)
     q = np.zeros((N, K // 32, 32), dtype=np.uint8)
-    for i in range(32):
-        p = 3 * i
-        if p + 3 <= 64:
-            val = (stream_lo >> np.uint64(p)) & np.uint64(7)
-        elif p >= 64:
-            val = (stream_hi >> np.uint64(p - 64)) & np.uint64(7)
-        else:   # code straddles bit 64
-            nlo = 64 - p
-            val = (stream_lo >> np.uint64(p)) | ((stream_hi << np.uint64(nlo)) & np.uint64(7))
-        q[:, :, i] = val.astype(np.uint8)
+    for P in range(15):
+        wi, t = divmod(P, 5)
+        q[:, :, 2 * P] = ((w[:, :, wi] >> np.uint32(3 * t)) & np.uint32(7)).astype(np.uint8)
+        q[:, :, 2 * P + 1] = ((w[:, :, wi] >> np.uint32(16 + 3 * t)) & np.uint32(7)).astype(np.uint8)
+    for b in range(3):
+        q[:, :, 30] |= (((w[:, :, b] >> np.uint32(15)) & np.uint32(1)) << np.uint32(b)).astype(np.uint8)
+        q[:, :, 31] |= (((w[:, :, b] >> np.uint32(31)) & np.uint32(1)) << np.uint32(b)).astype(np.uint8)
     return q.reshape(N, K)
 
 

@@ -1,4 +1,4 @@
-"""Pins for the oracle's packing (format v1), activation transform and matmul."""
+"""Pins for the oracle's packing (format 3), activation transform and matmul."""
 import numpy as np
 import pytest
 
@@ -26,8 +26,10 @@ def test_tile_slot_is_row_and_quarter(bits):
         if bits == 4:
             assert all(int(w) == v * rep for w in t[0, 1, s_])
         else:
-            stream = sum(v << (3 * i) for i in range(32))
-            assert [int(w) for w in t[0, 1, s_]] == [(stream >> (32 * d)) & 0xFFFFFFFF for d in range(3)]
+            # v in all 32 codes: pairs at bits 3t / 16 + 3t (t < 5) of every word,
+            # and bit b of codes 30 and 31 at bits 15 and 31 of word b
+            want = [v * 0x1249 * 0x10001 + ((v >> d) & 1) * 0x80008000 for d in range(3)]
+            assert [int(w) for w in t[0, 1, s_]] == want
     # codes equal to the quarter index: slot s encodes quarter s // 16
     q = ((np.arange(256) % 128) // 32 * np.ones((5, 1))).astype(np.uint8)
     t = O.pack(q, bits)
@@ -38,17 +40,47 @@ def test_tile_slot_is_row_and_quarter(bits):
             assert all(int(w) == (s_ // 16) * rep for w in t[0, 0, s_])
 
 
-def test_int3_stream_matches_big_integer():
+def test_int3_bits_land_where_the_layout_says():
+    """Each code's 3 bits placed one by one from the layout's statement (pair P
+    < 15: word P // 5, bit 3 (P % 5) + 16 (code odd) + b; codes 30 and 31: word
+    b, bit 15 or 31), summed as Python integers."""
     rng = np.random.default_rng(1)
     q = rng.integers(0, 8, (3, 256)).astype(np.uint8)
     words = O.pack_rows(q, 3)
     for n in range(3):
-        for c in range(256 // 32):
-            stream = 0
+        for r in range(256 // 32):
+            want = [0, 0, 0]
             for i in range(32):
-                stream |= int(q[n, 32 * c + i]) << (3 * i)
-            want = [(stream >> (32 * d)) & 0xFFFFFFFF for d in range(3)]
-            assert [int(w) for w in words[n, 3 * c:3 * c + 3]] == want
+                c = int(q[n, 32 * r + i])
+                for b in range(3):
+                    if i < 30:
+                        word, pos = i // 2 // 5, 3 * (i // 2 % 5) + 16 * (i % 2) + b
+                    else:
+                        word, pos = b, 15 + 16 * (i - 30)
+                    want[word] += ((c >> b) & 1) << pos
+            assert [int(w) for w in words[n, 3 * r:3 * r + 3]] == want
+
+
+def test_int3_pairs_are_fp16_magic_operands():
+    """(w >> 3t) & 0x00070007 | 0x64006400 is the fp16 pair (1024+c_2P, 1024+c_2P+1)
+    for pairs P = 5 word + t < 15; the last pair gathers bit 15 / 31 of the three
+    words: ((w0 >> 15) & 0x00010001) | ((w1 >> 14) & 0x00020002) | ((w2 >> 13) &
+    0x00040004) | 0x64006400."""
+    rng = np.random.default_rng(2)
+    q = rng.integers(0, 8, (4, 128)).astype(np.uint8)
+    words = O.pack_rows(q, 3).reshape(4, 4, 3)          # [row][32-code run][word]
+    runs = q.reshape(4, 4, 32).astype(np.float64)
+    for P in range(16):
+        if P < 15:
+            wd, t = divmod(P, 5)
+            pair = ((words[:, :, wd] >> np.uint32(3 * t)) & np.uint32(0x00070007)) | np.uint32(0x64006400)
+        else:
+            pair = (((words[:, :, 0] >> np.uint32(15)) & np.uint32(0x00010001))
+                    | ((words[:, :, 1] >> np.uint32(14)) & np.uint32(0x00020002))
+                    | ((words[:, :, 2] >> np.uint32(13)) & np.uint32(0x00040004)) | np.uint32(0x64006400))
+        h = np.ascontiguousarray(pair).view(np.float16).reshape(4, 4, 2).astype(np.float64) - 1024
+        assert np.array_equal(h[:, :, 0], runs[:, :, 2 * P])
+        assert np.array_equal(h[:, :, 1], runs[:, :, 2 * P + 1])
 
 
 def test_int4_pairs_are_fp16_magic_operands():
