@@ -38,13 +38,17 @@
  *   - M == 0 or N == 0 is a valid empty call: it returns AWQ_OK and
  *     launches nothing.
  *
- * Packed weight format, version 2 (chosen for gfx950 MFMA operand loads):
+ * Packed weight format, version 3 (chosen for gfx950 MFMA operand loads):
  *   Row words.  bits = 4: word j of row n holds the codes of k = 8j..8j+7;
  *     code 8j+2t is at bits 4t..4t+3 and code 8j+2t+1 at bits 16+4t..19+4t
  *     (t = 0..3), so ((w >> 4t) & 0x000F000F) | 0x64006400 is the fp16 pair
  *     (1024 + q[8j+2t], 1024 + q[8j+2t+1]).  bits = 3: each run of 32 codes
- *     k = 32c..32c+31 is a 96-bit little-endian bit stream (code i at stream
- *     bits 3i..3i+2) held in 3 words.
+ *     c[i] = q[32r + i] fills 3 words; pair P = (c[2P], c[2P+1]), P < 15, sits
+ *     in word P / 5 with c[2P] at bits 3t..3t+2 and c[2P+1] at bits
+ *     16+3t..18+3t (t = P % 5), so ((w >> 3t) & 0x00070007) | 0x64006400 is
+ *     its fp16 pair; bit b of c[30] and of c[31] is bit 15 and bit 31 of word
+ *     b.  (Version 2 held the int3 run as a 96-bit bit stream; int4 and the
+ *     tiling are unchanged.)
  *   Tiles.  Rows are taken 16 at a time (row block b = rows 16b..16b+15,
  *     padded with zero rows past N).  Tile (b, t) holds k = 128t .. 128t+127
  *     of the 16 rows of block b as 64 lane slots; slot s = 16h + j holds the

@@ -55,7 +55,7 @@ def test_status_strings(lib):
 
 
 def test_format_helpers(lib):
-    assert lib.awq_pack_format_version() == 2
+    assert lib.awq_pack_format_version() == 3
     assert lib.awq_packed_words(4096, 4096, 4) == 4096 * 512
     assert lib.awq_packed_words(37, 384, 4) == 48 * 48
     assert lib.awq_packed_words(37, 384, 3) == 48 * 36

@@ -55,7 +55,7 @@ const char* awq_status_str(int status) {
     }
 }
 
-int awq_pack_format_version(void) { return 2; }
+int awq_pack_format_version(void) { return 3; }
 
 size_t awq_packed_words_per_row(int K, int bits) {
     if (K <= 0) return 0;

@@ -50,6 +50,17 @@ __device__ __forceinline__ uint32_t int4_pair_bits(uint32_t w, int t) {
     return and_or(w >> (4 * t), 0x000F000Fu, 0x64006400u);
 }
 
+// The fp16 pair (1024 + c[2P], 1024 + c[2P+1]) of a packed int3 lane slot (3
+// words, codes c[0..31]): pairs P < 15 sit at bits 3t..3t+2 / 16+3t..18+3t of
+// word P / 5 (t = P % 5), so one shift and one AND-OR give them; bit b of
+// c[30] and c[31] is bit 15 / 31 of word b.  P is a compile-time constant.
+__device__ __forceinline__ uint32_t int3_pair_bits(const uint32_t* w, int P) {
+    if (P < 15) return and_or(w[P / 5] >> (3 * (P % 5)), 0x00070007u, 0x64006400u);
+    uint32_t r = and_or(w[0] >> 15, 0x00010001u, 0x64006400u);
+    r = and_or(w[1] >> 14, 0x00020002u, r);
+    return and_or(w[2] >> 13, 0x00040004u, r);
+}
+
 // The four fp16 pairs of a packed int4 word with one shift.  Pairs t = 0, 2
 // (code nibbles at bits 0..3 / 16..19 of w and of w >> 8) use exponent 2^10,
 // giving 1024 + q; pairs t = 1, 3 (nibbles at bits 4..7 / 20..23) are OR-ed

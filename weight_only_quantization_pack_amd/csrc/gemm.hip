@@ -5,7 +5,7 @@
 //
 // W4A16 (k_gemm_w4; context kernel of the llm-awq README feature list,
 // version "gemm" of the transformers quantization_config).  B is the packed
-// format-2 weight: tile (b, g) = 16 rows x group g, lane slot s = 16h + j
+// packed weight: tile (b, g) = 16 rows x group g, lane slot s = 16h + j
 // holding row j's codes 32h..32h+31, which is exactly the B-operand layout
 // of v_mfma_f32_16x16x32_f16 for the four k32 steps of the group (step i
 // uses word i of every slot, physical k = 128g + 32h + 8i + e).  So each
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void k_gemm_lds(
                           : make_uint4(0, 0, 0, 0);
         }
         if constexpr (B_INT4) {
-            // format 2: tile (block, kt) is 64 slots of 16 B; slot s = 16h + j
+            // packed tiles: tile (block, kt) is 64 slots of 16 B; slot s = 16h + j
             // is row 16*block + j, codes 32h..32h+31 of the group
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void k_gemm_lds(
                 } else {
                     rb[i] = make_uint4(0, 0, 0, 0);
                 }
-                // format-2 scales/zeros: [block][g][16], zero on padding rows
+                // tiled scales/zeros: [block][g][16], zero on padding rows
                 const size_t pidx = ((size_t)blk * G + kt) * 16 + (slot & 15);
                 rs[i] = 16 * blk < N ? scales[pidx] : (_Float16)0.0f;
                 rz[i] = 16 * blk < N ? zeros[pidx] : (_Float16)0.0f;
@@ -234,12 +234,11 @@ __device__ __forceinline__ half8_t dequant_scaled(uint32_t w, half2_t zz, half2_
 
 // fp16 B operand w_hat = (q - z) * D of 8 int3 codes held in the low 24 bits
 // of v (code e at bits 3e..3e+2); zz = 1024 + z
-__device__ __forceinline__ half8_t dequant_scaled_int3(uint32_t v, half2_t zz, half2_t dd) {
+__device__ __forceinline__ half8_t dequant_scaled_int3(const uint32_t* w, int s, half2_t zz, half2_t dd) {
     half8_t b;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        const uint32_t pair = ((v >> (6 * t)) & 7u) | (((v >> (6 * t + 3)) & 7u) << 16);
-        const half2_t p = (as_half2(pair | 0x64006400u) - zz) * dd;
+        const half2_t p = (as_half2(int3_pair_bits(w, 4 * s + t)) - zz) * dd;
         b[2 * t] = p[0];
         b[2 * t + 1] = p[1];
     }
@@ -517,13 +516,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
                 if constexpr (BITS == 4) {
                     b[c] = dequant_scaled(bs.q[c][s], zz[c], zz16[c], dd[c]);
                 } else {
-                    // 96-bit stream of 32 codes; substep s takes bits 24s..24s+23
-                    const uint32_t* w = bs.q[c];
-                    const uint32_t v = s == 0 ? (w[0] & 0xFFFFFFu)
-                                     : s == 1 ? ((w[0] >> 24) | ((w[1] & 0xFFFFu) << 8))
-                                     : s == 2 ? ((w[1] >> 16) | ((w[2] & 0xFFu) << 16))
-                                              : (w[2] >> 8);
-                    b[c] = dequant_scaled_int3(v, zz[c], dd[c]);
+                    // substep s takes the slot's code pairs 4s..4s+3
+                    b[c] = dequant_scaled_int3(bs.q[c], s, zz[c], dd[c]);
                 }
             }
         };

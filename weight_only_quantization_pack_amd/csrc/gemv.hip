@@ -7,7 +7,7 @@
 // zero-padded to 16) and the weights as the B operand, so the cost per
 // weight stays flat up to M = 16.
 //
-// Work split.  Packed format 2 stores tile (b, g) = 16 rows x group g as 64
+// Work split.  The packed format stores tile (b, g) = 16 rows x group g as 64
 // lane slots of 16 bytes (slot s = 16h + j: row j, quarter h), contiguous
 // along g, with the 16 scales and zeros of the tile in [b][g][16] order.
 // Persistent workgroups of WK waves own row blocks blockIdx.x, +gridDim.x,
@@ -71,13 +71,12 @@ __device__ __forceinline__ half8_t dequant_word_int4(uint32_t w, half2_t zz, hal
     return b;
 }
 
-// fp16 operand (q - z) of 8 int3 codes held in the low 24 bits of v.
-__device__ __forceinline__ half8_t dequant_24_int3(uint32_t v, half2_t zz) {
+// fp16 operand (q - z) of int3 codes 8s..8s+7 of a lane slot (pairs 4s..4s+3)
+__device__ __forceinline__ half8_t dequant_int3(const uint32_t* w, int s, half2_t zz) {
     half8_t b;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        const uint32_t pair = ((v >> (6 * t)) & 7u) | (((v >> (6 * t + 3)) & 7u) << 16);
-        const half2_t p = as_half2(and_or(pair, 0x00070007u, 0x64006400u)) - zz;
+        const half2_t p = as_half2(int3_pair_bits(w, 4 * s + t)) - zz;
         b[2 * t] = p[0];
         b[2 * t + 1] = p[1];
     }
@@ -217,12 +216,8 @@ __device__ __forceinline__ void accumulate_tile(const Slot<WQ>& w, const RawPara
 #pragma unroll
         for (int q = 0; q < 4; ++q) bop[q] = dequant_word_int4(w.w[q], zz, zz16);
     } else {
-        // 96-bit stream of 32 codes; operand q takes stream bits 24q..24q+23
-        const uint32_t w0 = w.w[0], w1 = w.w[1], w2 = w.w[2];
-        bop[0] = dequant_24_int3(w0 & 0xFFFFFFu, zz);
-        bop[1] = dequant_24_int3((w0 >> 24) | ((w1 & 0xFFFFu) << 8), zz);
-        bop[2] = dequant_24_int3((w1 >> 16) | ((w2 & 0xFFu) << 16), zz);
-        bop[3] = dequant_24_int3(w2 >> 8, zz);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bop[q] = dequant_int3(w.w, q, zz);
     }
     if constexpr (GS == 64) {
         const _Float16 dh = low_half(p.d >> psh);

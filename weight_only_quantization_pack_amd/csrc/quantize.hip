@@ -1,4 +1,4 @@
-// Group quantization + packing (format 2) and the activation-side divide.
+// Group quantization + packing (format 3) and the activation-side divide.
 //
 // What is computed: round-to-nearest quantization of W*diag(s) in groups of
 // 128 (or 64) input channels, with an fp16 scale and an integer zero point
@@ -11,7 +11,7 @@
 // quarter h of the group (four 16-byte loads of W), the group's min/max is
 // met across the four lanes of that row (xor-shuffles 16 and 32), and the
 // wave writes its tile as one contiguous 1 KB store (768 B for bits 3) in
-// the format-2 slot order, so the decode and prefill kernels can read a
+// the packed slot order, so the decode and prefill kernels can read a
 // tile with one contiguous wave load.  The group scales and zeros go to the
 // same tile order ([block][g][16]).  Rows past N are written as zeros.
 // The kernel is HBM-bound (offline).
@@ -84,24 +84,17 @@ __global__ __launch_bounds__(256) void k_quantize_pack(
             out[i] = word;
         }
     } else {
-        uint64_t lo = 0;
-        uint32_t hi = 0;
+        // pair P < 15 at bits 3t / 16 + 3t of word P / 5; bit b of codes 30 and
+        // 31 at bits 15 and 31 of word b
+        out[0] = out[1] = out[2] = 0;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const uint32_t q = quant_code<Q>(v[i], p);
-            const int pos = 3 * i;
-            if (pos + 3 <= 64) {
-                lo |= (uint64_t)q << pos;
-            } else if (pos >= 64) {
-                hi |= q << (pos - 64);
-            } else {                       // code straddles stream bit 64
-                lo |= (uint64_t)q << pos;
-                hi |= q >> (64 - pos);
-            }
+        for (int P = 0; P < 15; ++P) {
+            out[P / 5] |= quant_code<Q>(v[2 * P], p) << (3 * (P % 5));
+            out[P / 5] |= quant_code<Q>(v[2 * P + 1], p) << (16 + 3 * (P % 5));
         }
-        out[0] = (uint32_t)lo;
-        out[1] = (uint32_t)(lo >> 32);
-        out[2] = hi;
+        const uint32_t c30 = quant_code<Q>(v[30], p), c31 = quant_code<Q>(v[31], p);
+#pragma unroll
+        for (int b = 0; b < 3; ++b) out[b] |= (((c30 >> b) & 1u) << 15) | (((c31 >> b) & 1u) << 31);
     }
     uint32_t* dst = qweight + ((size_t)tile * 64 + lane) * WQ;
     if constexpr (BITS == 4) {
@@ -111,7 +104,7 @@ __global__ __launch_bounds__(256) void k_quantize_pack(
 #pragma unroll
         for (int i = 0; i < 3; ++i) dst[i] = valid ? out[i] : 0u;
     }
-    if (GS == 128 ? h == 0 : (h & 1) == 0) {  // format 2: [block][group][row in block]
+    if (GS == 128 ? h == 0 : (h & 1) == 0) {  // tiled: [block][group][row in block]
         const size_t pidx = (GS == 128 ? (size_t)tile : 2 * (size_t)tile + (h >> 1)) * 16 + j;
         scales[pidx] = valid ? p.dbits : (uint16_t)0;
         zeros[pidx] = valid ? half_bits((_Float16)p.zero) : (uint16_t)0;
