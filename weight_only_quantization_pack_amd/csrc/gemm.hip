@@ -409,13 +409,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(
 // Split K (part != nullptr): workgroup (tile, blockIdx.y) covers groups
 // [blockIdx.y * gsplit, +gsplit) and writes its fp32 partial tile to
 // part[blockIdx.y][M][N]; k_splitk_reduce adds the splits in order.
-template <int BITS, int GS, int S>
+template <int BITS, int GS, int S, int GMT>
 __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
     const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
     _Float16* __restrict__ Y, float* __restrict__ part, int M, int N, int K, int gsplit) {
     using namespace w4;
-    extern __shared__ __attribute__((aligned(16))) unsigned char As[];   // S x ABUF
+    static_assert(GMT == 128 || GMT == 64, "128- or 64-row tiles");
+    constexpr int FR = GMT / 16;                       // 16-row A fragments (and row groups per wave)
+    constexpr int ABUFT = GMT * ROW_BYTES;             // one A buffer
+    extern __shared__ __attribute__((aligned(16))) unsigned char As[];   // S x ABUFT
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -425,16 +428,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     const int g_begin = (int)blockIdx.y * gsplit;      // this workgroup's groups: [g_begin, g_begin + NGS)
     const int NGS = min(G - g_begin, gsplit);
     const int NB = (N + 15) / 16;
-    const int nTn = (N + GN - 1) / GN, nTm = (M + GM - 1) / GM;
+    const int nTn = (N + GN - 1) / GN, nTm = (M + GMT - 1) / GMT;
     const int nT = nTn * nTm;
     int t = blockIdx.x;
     if (nT % 8 == 0) t = (t % 8) * (nT / 8) + t / 8;
-    const int m0 = (t / nTn) * GM, n0 = (t % nTn) * GN;
+    const int m0 = (t / nTn) * GMT, n0 = (t % nTn) * GN;
 
-    uint32_t a_off[8];
+    uint32_t a_off[FR];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int rg = wave * 8 + i;
+    for (int i = 0; i < FR; ++i) {
+        const int rg = wave * FR + i;
         const int r = 4 * rg + (lane >> 4);
         const int kc = (lane & 15) ^ (r & 15);
         const int grow = min(m0 + r, M - 1);
@@ -452,16 +455,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     const uint32_t pgrp = GS == 64 ? (uint32_t)(hq >> 1) : 0u;
 
     constexpr int WQ = BITS == 4 ? 4 : 3;              // words per lane slot
+    constexpr int LPS = FR + 4 + 8;                    // loads per step and wave: A, B tiles, D and z words
     struct BStage { uint32_t q[4][WQ]; uint32_t d[4], z[4]; };
     // part p (0..3) of step kt's loads: A rows groups 2p, 2p + 1 (direct to LDS
     // buffer `slot`), B tile p of this wave and its scale and zero words
     auto issue_part = [&](int kt, int slot, BStage& bs, int p) {
         const uint32_t g = (uint32_t)(g_begin + min(kt, NGS - 1));
 #pragma unroll
-        for (int i = 2 * p; i < 2 * p + 2; ++i) {
-            const int rg = wave * 8 + i;
+        for (int i = p * FR / 4; i < (p + 1) * FR / 4; ++i) {
+            const int rg = wave * FR + i;
             __builtin_amdgcn_global_load_lds((global_void_t*)(x + a_off[i] + g * GK),
-                                             (lds_void_t*)(As + slot * ABUF + rg * 1024), 16, 0, 0);
+                                             (lds_void_t*)(As + slot * ABUFT + rg * 1024), 16, 0, 0);
         }
         const uint32_t tt = tbase[p] + g;
         // one dwordx4 (int4) or dwordx3 (int3) load: 20 loads per step either way
@@ -481,13 +485,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
         for (int p = 0; p < 4; ++p) issue_part(kt, slot, bs, p);
     };
 
-    float4_t acc[8][4];
+    float4_t acc[FR][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < FR; ++i)
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[i][c] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-    // One K-step: four k32 substeps of 32 MFMAs.  The A fragments (8 LDS reads)
+    // One K-step: four k32 substeps of 4 FR MFMAs.  The A fragments (FR LDS reads)
     // and B operands (4 dequantized words) of substep s + 1 are produced while
     // the MFMAs of substep s run, so that neither LDS latency nor the
     // dequantization sits between two MFMA groups.
@@ -505,7 +509,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
         auto read_a = [&](int s, half8_t* a) {
             const int kc = 4 * hq + s;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < FR; ++i) {
                 const int r = 16 * i + j;
                 a[i] = *reinterpret_cast<const half8_t*>(abuf + r * ROW_BYTES + ((kc ^ (r & 15)) << 4));
             }
@@ -521,24 +525,24 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
                 }
             }
         };
-        half8_t a_cur[8], b_cur[4];
+        half8_t a_cur[FR], b_cur[4];
         read_a(0, a_cur);
         dequant(0, b_cur);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            half8_t a_nxt[8], b_nxt[4];
+            half8_t a_nxt[FR], b_nxt[4];
             if (s < 3) {
                 read_a(s + 1, a_nxt);
                 dequant(s + 1, b_nxt);
             }
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < FR; ++i)
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
                     acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b_cur[c], a_cur[i], acc[i][c], 0, 0, 0);
             if (s < 3) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) a_cur[i] = a_nxt[i];
+                for (int i = 0; i < FR; ++i) a_cur[i] = a_nxt[i];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) b_cur[c] = b_nxt[c];
             }
@@ -563,7 +567,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
         for (int st = 0; st < S; ++st) {
             const int kt = kt0 + st;
             // step kt has landed once at most the S - 2 later steps' loads are outstanding
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(20 * (S - 2)));
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS * (S - 2)));
             // every wave's A(kt) is in LDS and its reads of A(kt-1) are done.  A
             // bare barrier: __syncthreads() is a release fence that would also
             // drain the later steps' direct-to-LDS loads (vmcnt(0))
@@ -573,7 +577,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
             __builtin_amdgcn_sched_barrier(0);
             // the last round may run past G: those steps keep the load stream
             // (and so the compiler's wait counts) uniform but compute nothing
-            if (kt < NGS) compute(bs[st], As + st * ABUF);
+            if (kt < NGS) compute(bs[st], As + st * ABUFT);
         }
         kt0 += S;
     } while (kt0 < NGS);
@@ -581,7 +585,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     if (part != nullptr) {
         float* prow0 = part + (size_t)blockIdx.y * M * N;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < FR; ++i) {
             const int m = m0 + 16 * i + j;
             if (m >= M) continue;
             float* prow = prow0 + (size_t)m * N;
@@ -600,7 +604,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
         return;
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < FR; ++i) {
         const int m = m0 + 16 * i + j;
         if (m >= M) continue;
         _Float16* yrow = Y + (size_t)m * N;
@@ -646,14 +650,24 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 
 constexpr int kGemmStages = 4;
 
-int launch_w4p(const void* x, const void* qweight, const void* scales, const void* zeros, void* y,
-               float* part, int M, int N, int K, int bits, int group_size, int splits, int gsplit,
-               hipStream_t st) {
-    const int nT = ((N + w4::GN - 1) / w4::GN) * ((M + w4::GM - 1) / w4::GM);
-    const size_t lds = (size_t)kGemmStages * w4::ABUF;
+// tile height of the pipelined kernel: 64 rows while M fits in one such tile
+// row (half of a 128-row tile would multiply padding rows), else 128
+int w4p_rows(int M) { return M <= 64 ? 64 : 128; }
+
+int w4p_tiles(int M, int N) {
+    const int rows = w4p_rows(M);
+    return ((N + w4::GN - 1) / w4::GN) * ((M + rows - 1) / rows);
+}
+
+template <int GMT>
+int launch_w4p_rows(const void* x, const void* qweight, const void* scales, const void* zeros,
+                    void* y, float* part, int M, int N, int K, int bits, int group_size, int splits,
+                    int gsplit, hipStream_t st) {
+    const int nT = ((N + w4::GN - 1) / w4::GN) * ((M + GMT - 1) / GMT);
+    const size_t lds = (size_t)kGemmStages * GMT * w4::ROW_BYTES;
     auto kern = group_size == 64
-                    ? (bits == 4 ? k_gemm_w4p<4, 64, kGemmStages> : k_gemm_w4p<3, 64, kGemmStages>)
-                    : (bits == 4 ? k_gemm_w4p<4, 128, kGemmStages> : k_gemm_w4p<3, 128, kGemmStages>);
+                    ? (bits == 4 ? k_gemm_w4p<4, 64, kGemmStages, GMT> : k_gemm_w4p<3, 64, kGemmStages, GMT>)
+                    : (bits == 4 ? k_gemm_w4p<4, 128, kGemmStages, GMT> : k_gemm_w4p<3, 128, kGemmStages, GMT>);
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return (int)e;
@@ -663,12 +677,22 @@ int launch_w4p(const void* x, const void* qweight, const void* scales, const voi
     return (int)hipGetLastError();
 }
 
+int launch_w4p(const void* x, const void* qweight, const void* scales, const void* zeros, void* y,
+               float* part, int M, int N, int K, int bits, int group_size, int splits, int gsplit,
+               hipStream_t st) {
+    if (w4p_rows(M) == 64)
+        return launch_w4p_rows<64>(x, qweight, scales, zeros, y, part, M, N, K, bits, group_size,
+                                   splits, gsplit, st);
+    return launch_w4p_rows<128>(x, qweight, scales, zeros, y, part, M, N, K, bits, group_size,
+                                splits, gsplit, st);
+}
+
 }  // namespace
 
 int gemm_splits(int M, int N, int K) {
     // split K only while the tiles leave at least half the CUs idle; each
     // split keeps >= 8 groups (two rounds of the 4-step pipeline), <= 16 splits
-    const int nT = ((N + w4::GN - 1) / w4::GN) * ((M + w4::GM - 1) / w4::GM);
+    const int nT = w4p_tiles(M, N);
     const int cus = device_cu_count();
     const int G = K / kGroup;
     if (2 * nT > cus) return 1;
@@ -713,8 +737,8 @@ int launch_gemm(const void* x, const void* qweight, const void* scales, const vo
     // whose 2 x CUs slots round the tile count better (MI355X, M = 2048:
     // 14336x4096 (256 tiles) 974 vs 743 TFLOP/s; 4096x14336 (896 tiles) 764 vs
     // 816; 4096x6144 (384 tiles) 739 vs 849).
-    // int3 and 64-wide groups have the pipelined kernel only
-    if (bits == 3 || group_size == 64 || nT <= device_cu_count()) {
+    // int3, 64-wide groups and M <= 64 (64-row tiles) take the pipelined kernel
+    if (bits == 3 || group_size == 64 || nT <= device_cu_count() || w4p_rows(M) == 64) {
         return launch_w4p(x, qweight, scales, zeros, y, nullptr, M, N, K, bits, group_size, 1,
                           K / kGroup, st);
     } else {
