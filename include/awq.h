@@ -124,6 +124,18 @@ int awq_quantize_pack(const void* W, const float* s, int N, int K, int bits,
                       void* scales, void* zeros, void* stream);
 
 /*
+ * awq_dequantize -- fake quantization ("Usage" step 2 of the llm-awq README,
+ * --q_backend fake: the quantized weights kept as dequantized fp16 values):
+ *   W_hat[n][k] = fp16_rne((q[n][k] - z[n][g]) * D[n][g])
+ *   (the product is exact in fp32; one rounding to fp16)
+ *   qweight, scales, zeros as produced by awq_quantize_pack (same bits and
+ *   group_size); W_hat fp16 [N][K] out.  Errors as awq_quantize_pack.
+ */
+int awq_dequantize(const void* qweight, const void* scales, const void* zeros,
+                   void* W_hat, int N, int K, int bits, int group_size,
+                   void* stream);
+
+/*
  * awq_scale_activations -- the activation side of the equivalent transform
  * (section 02.02 "AWQ" of the VPTQ blog): x_out[m][k] = fp16_rne(fp32(x[m][k]) / s[k]).
  *   x      fp16 [M][K] in;  s fp32 [K] in;  x_out fp16 [M][K] out (may equal x).

@@ -327,6 +327,20 @@ def packed_words_per_row(K: int, bits: int) -> int:
     return K // 8 if bits == 4 else 3 * (K // 32)
 
 
+def fake_quantize(qweight: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
+                  bits: int, K: int) -> np.ndarray:
+    """w_hat as fp16 [N][K] from the packed layer: fp16_rne((q - z) * D).
+
+    [P1] "Usage" step 2 (--q_backend fake): the quantized weights are kept as
+    dequantized fp16 values for evaluation.  (q - z) * D is exact in fp64 (a
+    small integer times an fp16 value), so this is its single rounding to fp16.
+    The group size comes from the [N][G] parameters.
+    """
+    N, G = np.asarray(scales).shape
+    q = unpack_fast(qweight, bits, K, N)
+    return dequantize(q, scales, zeros, K // G).astype(np.float16)
+
+
 # ---------------------------------------------------------------------------
 # a7: activation-side half of the equivalent transform
 # ---------------------------------------------------------------------------

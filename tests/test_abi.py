@@ -164,6 +164,18 @@ def test_gemv_gate_up_validation(lib):
     assert _gate_up(lib, M=0, x=NUL, h=NUL) == OK
 
 
+def test_dequantize_validation(lib):
+    f = lib.awq_dequantize
+    assert f(P, P2, P3, P4, 64, 256, 5, 128, NUL) == UNSUP
+    assert f(P, P2, P3, P4, 64, 256, 4, 32, NUL) == UNSUP
+    assert f(P, P2, P3, P4, 64, 200, 4, 128, NUL) == SHAPE
+    assert f(P, P2, P3, P4, -1, 256, 4, 128, NUL) == SHAPE
+    assert f(NUL, P2, P3, P4, 64, 256, 4, 128, NUL) == NULL
+    assert f(P, P2, P3, NUL, 64, 256, 3, 64, NUL) == NULL
+    assert f(P, P2, MIS, P4, 64, 256, 4, 128, NUL) == ALIGN
+    assert f(NUL, NUL, NUL, NUL, 0, 256, 4, 128, NUL) == OK
+
+
 def test_gemm_splitk_validation(lib):
     # without a GPU the library assumes 256 compute units: 32 tiles of a
     # 64 x 8192 output leave most idle, so K = 28672 (224 groups) is split 8 ways

@@ -130,3 +130,32 @@ def test_scale_activations_bit_exact(gpu, M, K):
     out = awq.scale_activations(dev(x), dev(s))
     torch.cuda.synchronize()
     assert np.array_equal(host(out).view(np.uint16), O.scale_activations(x, s).view(np.uint16))
+
+
+# ----------------------------------------------------------------------------- fake quantization
+@pytest.mark.parametrize("bits,group_size", [(4, 128), (3, 128), (4, 64), (3, 64)])
+@pytest.mark.parametrize("N,K", [(37, 384), (1, 128), (300, 1152)])
+def test_fake_quantize_bit_exact(gpu, bits, group_size, N, K):
+    """awq_dequantize (--q_backend fake) = the oracle's fp16_rne((q - z) D), bit for bit."""
+    import torch
+    announce("fake_quantize", N, K, bits, group_size)
+    q, d, z = O.quantize(WL.random_weights(N, K, seed=N + K + bits), None, bits, group_size)
+    qw = O.pack(q, bits)
+    got = awq.fake_quantize(dev(qw.reshape(-1)), dev(O.tile_params(d)), dev(O.tile_params(z)), N, K,
+                            bits=bits, group_size=group_size)
+    torch.cuda.synchronize()
+    want = O.fake_quantize(qw, d, z, bits, K)
+    assert np.array_equal(host(got).view(np.uint16), want.view(np.uint16))
+
+
+def test_fake_quantize_full_layer_chain(gpu):
+    """4096 x 4096 int4: awq_quantize_pack then awq_dequantize on the GPU against
+    the oracle's quantize, pack and fake quantization of the same W, bit for bit."""
+    import torch
+    W = WL.workload(2).weights(0)
+    qw, sc, ze = awq.quantize_pack(dev(W), None, bits=4)
+    got = awq.fake_quantize(qw, sc, ze, 4096, 4096, bits=4)
+    torch.cuda.synchronize()
+    q, d, z = O.quantize(W, None, 4)
+    want = O.fake_quantize(O.pack(q, 4), d, z, 4, 4096)
+    assert np.array_equal(host(got).view(np.uint16), want.view(np.uint16))

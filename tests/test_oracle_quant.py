@@ -221,3 +221,35 @@ def test_page_configs_are_the_defaults():
     assert cfg["transformers_quantization_config"]["zero_point"] is True
     for bits, gs in cfg["model_zoo_configs"]["configs"]:
         assert bits in O.SUPPORTED_BITS and gs == O.GROUP_SIZE
+
+
+# ----------------------------------------------------------------------------- fake quantization
+def test_fake_quantize_is_w_on_the_grid_and_requantizes_to_the_same_codes():
+    """"Usage" step 2 (--q_backend fake): w_hat kept as fp16.  Grid-valued
+    weights come back unchanged; a fake-quantized layer quantizes again to the
+    same codes and zeros (its scale at most one fp16 step lower); values agree
+    with the fp64 dequantize to fp16 rounding."""
+    rng = np.random.default_rng(31)
+    i = rng.integers(0, 16, (37, 256))
+    i[:, ::128] = 0
+    i[:, 1::128] = 15
+    e = rng.integers(5, 8, (37, 1))
+    W = ((i - 7) * np.ldexp(1.0, -e)).astype(np.float16)
+    for bits in (4, 3):
+        q, d, z = O.quantize(W, None, bits)
+        fq = O.fake_quantize(O.pack(q, bits), d, z, bits, 256)
+        assert fq.dtype == np.float16 and fq.shape == W.shape
+        if bits == 4:
+            assert np.array_equal(fq.view(np.uint16), W.view(np.uint16))
+    Wr = WL.random_weights(40, 384, seed=32)
+    for bits, gs in ((4, 128), (3, 128), (4, 64)):
+        q, d, z = O.quantize(Wr, None, bits, gs)
+        fq = O.fake_quantize(O.pack(q, bits), d, z, bits, 384)
+        w64 = O.dequantize(q, d, z, gs)
+        assert np.all(np.abs(fq.astype(np.float64) - w64) <= np.spacing(np.abs(fq)).astype(np.float64) / 2)
+        # the fp16 rounding of w_hat can narrow a group's span, which may move
+        # the rounded-down scale one fp16 step lower; the codes stay
+        q2, d2, z2 = O.quantize(fq, None, bits, gs)
+        assert np.array_equal(q2, q) and np.array_equal(z2, z)
+        step = d.view(np.uint16).astype(np.int64) - d2.view(np.uint16).astype(np.int64)
+        assert np.all((step == 0) | (step == 1))

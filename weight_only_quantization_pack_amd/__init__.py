@@ -8,10 +8,11 @@ missing build raises immediately: there is no CPU fallback.
 from .binding import (AwqError, quantize_pack, search_scale, search_scale_shared,  # noqa: F401
                       search_workspace_bytes,
                       gemv, gemv_gate_up, gemm, gemm_splitk_workspace_bytes, scale_activations,
+                      fake_quantize,
                       library_path,
                       load_library,
                       pack_format_version, packed_words_per_row, packed_words)
 
 __all__ = ["AwqError", "quantize_pack", "search_scale", "search_scale_shared", "search_workspace_bytes",
-           "gemv", "gemv_gate_up", "gemm", "gemm_splitk_workspace_bytes", "scale_activations", "library_path", "load_library",
+           "gemv", "gemv_gate_up", "gemm", "gemm_splitk_workspace_bytes", "scale_activations", "fake_quantize", "library_path", "load_library",
            "pack_format_version", "packed_words_per_row", "packed_words"]

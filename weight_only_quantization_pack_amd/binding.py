@@ -38,6 +38,8 @@ SIGNATURES = [
                           _c_int, _c_int, _c_int, _c_void_p]),
     ("awq_gemm", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                           _c_int, _c_int, _c_int, _c_void_p]),
+    ("awq_dequantize", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int,
+                                _c_int, _c_void_p]),
     ("awq_gemv_scaled", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                  _c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p]),
     ("awq_gemv_gate_up", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -161,6 +163,22 @@ def quantize_pack(W, s=None, bits: int = 4, group_size: int = GROUP_SIZE,
                                _ptr(qweight), _ptr(scales), _ptr(zeros), _stream_ptr(W))
     _check(st, "awq_quantize_pack")
     return qweight, scales, zeros
+
+
+def fake_quantize(qweight, scales, zeros, N: int, K: int, bits: int = 4, group_size: int = GROUP_SIZE,
+                  out=None):
+    """w_hat fp16 [N][K] = fp16((q - z) * D) from the packed layer (awq_dequantize)."""
+    torch = _torch()
+    lib = load_library()
+    _need_layer(qweight, scales, zeros, N, K, bits, group_size)
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.float16, device=qweight.device)
+    else:
+        _need(out, torch.float16, (N, K), "out")
+    st = lib.awq_dequantize(_ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(out), N, K, bits,
+                            group_size, _stream_ptr(qweight))
+    _check(st, "awq_dequantize")
+    return out
 
 
 def scale_activations(x, s, out=None):

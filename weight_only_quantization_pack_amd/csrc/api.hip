@@ -81,6 +81,18 @@ int awq_quantize_pack(const void* W, const float* s, int N, int K, int bits, int
                                                 (hipStream_t)stream));
 }
 
+int awq_dequantize(const void* qweight, const void* scales, const void* zeros, void* W_hat, int N,
+                   int K, int bits, int group_size, void* stream) {
+    int st = check_quant_params(bits, group_size, 1);
+    if (st) return st;
+    if ((st = check_nk(N, K))) return st;
+    if ((long long)N * K >= (1LL << 40)) return AWQ_ERR_SHAPE;
+    if (N == 0) return AWQ_OK;
+    if ((st = check_ptrs({qweight, scales, zeros, W_hat}))) return st;
+    return hip_status(awq::launch_dequantize(qweight, scales, zeros, W_hat, N, K, bits, group_size,
+                                             (hipStream_t)stream));
+}
+
 int awq_scale_activations(const void* x, const float* s, void* x_out, int M, int K, void* stream) {
     if (M < 0 || K <= 0 || K % awq::kGroup != 0) return AWQ_ERR_SHAPE;
     if (M == 0) return AWQ_OK;

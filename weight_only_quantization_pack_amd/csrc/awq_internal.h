@@ -126,6 +126,8 @@ int launch_quantize_pack(const void* W, const float* s, int N, int K, int bits, 
                          int zero_point, void* qweight, void* scales, void* zeros, hipStream_t st);
 int launch_scale_activations(const void* x, const float* s, void* x_out, int M, int K,
                              hipStream_t st);
+int launch_dequantize(const void* qweight, const void* scales, const void* zeros, void* W_hat, int N,
+                      int K, int bits, int group_size, hipStream_t st);
 // compute units of the current device
 int device_cu_count();
 

@@ -127,6 +127,53 @@ __global__ __launch_bounds__(256) void k_scale_activations(
     x_out[t] = out;
 }
 
+// Fake quantization (llm-awq README "Usage" step 2, --q_backend fake): the
+// packed layer back to fp16 w_hat = fp16_rne((q - z) * D), the exact product
+// of a small integer and an fp16 value rounded once.  One wave per tile, lane
+// (row j, quarter h) writes the 32 values of its slot with four 16-byte stores.
+template <int BITS, int GS>
+__global__ __launch_bounds__(256) void k_dequantize(const uint32_t* __restrict__ qweight,
+                                                   const _Float16* __restrict__ scales,
+                                                   const _Float16* __restrict__ zeros,
+                                                   _Float16* __restrict__ W_hat, int N, int K,
+                                                   long long n_tiles) {
+    constexpr int WQ = BITS == 4 ? 4 : 3;
+    const long long tile = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (tile >= n_tiles) return;
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 15, h = lane >> 4;
+    const int G = K / kGroup;
+    const int b = (int)(tile / G), g = (int)(tile % G);
+    const int n = 16 * b + j;
+    if (n >= N) return;                               // padding rows: nothing to write
+    const uint32_t* src = qweight + ((size_t)tile * 64 + lane) * WQ;
+    uint32_t w[WQ];
+#pragma unroll
+    for (int i = 0; i < WQ; ++i) w[i] = src[i];
+    const size_t pidx = (GS == 128 ? (size_t)tile : 2 * (size_t)tile + (h >> 1)) * 16 + j;
+    const float d = (float)scales[pidx], z = (float)zeros[pidx];
+    uint32_t c[32];
+    if constexpr (BITS == 4) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) c[i] = (w[i / 8] >> (4 * ((i % 8) / 2) + 16 * (i % 2))) & 15u;
+    } else {
+#pragma unroll
+        for (int P = 0; P < 15; ++P) {
+            c[2 * P] = (w[P / 5] >> (3 * (P % 5))) & 7u;
+            c[2 * P + 1] = (w[P / 5] >> (16 + 3 * (P % 5))) & 7u;
+        }
+        c[30] = ((w[0] >> 15) & 1u) | ((w[1] >> 14) & 2u) | ((w[2] >> 13) & 4u);
+        c[31] = ((w[0] >> 31) & 1u) | ((w[1] >> 30) & 2u) | ((w[2] >> 29) & 4u);
+    }
+    uint4 out[4];
+    _Float16* o = reinterpret_cast<_Float16*>(out);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) o[i] = (_Float16)(((float)c[i] - z) * d);
+    uint4* dst = reinterpret_cast<uint4*>(W_hat + (size_t)n * K + kGroup * g + 32 * h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = out[i];
+}
+
 }  // namespace
 
 template <int GS>
@@ -152,6 +199,17 @@ int launch_scale_activations(const void* x, const float* s, void* x_out, int M, 
     const long long grid = (n_chunks + block - 1) / block;
     hipLaunchKernelGGL(k_scale_activations, dim3((unsigned)grid), dim3(block), 0, st,
                        (const uint4*)x, s, (uint4*)x_out, K, n_chunks);
+    return (int)hipGetLastError();
+}
+
+int launch_dequantize(const void* qweight, const void* scales, const void* zeros, void* W_hat, int N,
+                      int K, int bits, int group_size, hipStream_t st) {
+    const long long n_tiles = (long long)((N + 15) / 16) * (K / kGroup);
+    const long long grid = (n_tiles + 3) / 4;
+    auto kern = group_size == 64 ? (bits == 4 ? k_dequantize<4, 64> : k_dequantize<3, 64>)
+                                 : (bits == 4 ? k_dequantize<4, 128> : k_dequantize<3, 128>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, (const uint32_t*)qweight,
+                       (const _Float16*)scales, (const _Float16*)zeros, (_Float16*)W_hat, N, K, n_tiles);
     return (int)hipGetLastError();
 }
 
