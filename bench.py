@@ -82,6 +82,9 @@ def main(argv=None):
     ap.add_argument("--pmc-probe", action="store_true",
                     help="short run for rocprofv3 --pmc: a 256 MiB device copy (known size, "
                          "calibrates FETCH_SIZE/WRITE_SIZE) then one cold pass of the decode step")
+    ap.add_argument("--pmc-gemm-probe", action="store_true",
+                    help="short run for rocprofv3 --pmc: the three M=2048 prefill GEMMs, three "
+                         "launches each after one warm-up launch")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -104,6 +107,23 @@ def main(argv=None):
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(0)
     stream = torch.cuda.Stream()          # default priority
+
+    if args.pmc_gemm_probe:
+        wl4 = WL.workload(4)
+        res = {}
+        with torch.cuda.stream(stream):
+            for i, (K, N) in enumerate(wl4.shapes):
+                W = torch.from_numpy(wl4.weights(i)).to(dev)
+                qw, sc, ze = awq.quantize_pack(W, None, bits=4)
+                x = torch.from_numpy(wl4.activations(2048, i)).to(dev)
+                y = torch.empty((2048, N), dtype=torch.float16, device=dev)
+                for _ in range(4):
+                    awq.gemm(x, qw, sc, ze, N=N, bits=4, out=y)
+                res[f"{K}x{N}"] = 2.0 * 2048 * N * K
+                del W, qw, sc, ze, x, y
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_gemm_probe": True, "M": 2048, "flops_per_launch": res}))
+        return 0
 
     # ------------------------------------------------------------------ decode GEMV
     wl2 = WL.workload(2)
