@@ -38,6 +38,14 @@
 namespace awq {
 namespace {
 
+// wave priority of k_gemm_w4 while it issues a K-step's MFMAs: its two
+// workgroups per CU put two waves on each SIMD, and the one in its MFMA phase
+// goes first while the other loads and dequantizes (MI355X, M = 2048:
+// 4096x6144 118-119 vs 123-124 us, 4096x14336 284-289 vs 291-292 us)
+#ifndef AWQ_GEMM_PRIO
+#define AWQ_GEMM_PRIO 1
+#endif
+
 constexpr int BM = 128, BN = 128, BK = 128;
 constexpr int LDS_STRIDE = BK + 8;          // halves; +16 B per row against bank conflicts
 
@@ -334,6 +342,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(
             dd[c] = (half2_t){bp[c][0], bp[c][0]};
         }
         const unsigned char* abuf = As + buf * ABUF;
+#if AWQ_GEMM_PRIO
+        __builtin_amdgcn_s_setprio(AWQ_GEMM_PRIO);
+#endif
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             half8_t b[4];
@@ -370,6 +381,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(
                 __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
             }
         }
+#if AWQ_GEMM_PRIO
+        __builtin_amdgcn_s_setprio(0);
+#endif
 #pragma unroll
         for (int c = 0; c < 4; ++c) { bq[c] = bq_next[c]; bp[c] = bp_next[c]; }
     }
