@@ -50,21 +50,30 @@ Layout layout(int T, int N, int K, int n_alpha) {
     return L;
 }
 
-// Block: 64 columns x 4 row phases.  Sums of |fp16| in fp64 are exact for
-// T < 2^13, so the partial order cannot change the result.
-__global__ __launch_bounds__(256) void k_act_stat(const _Float16* __restrict__ X, int T, int K,
-                                                 float* __restrict__ s_x) {
-    const int kk = threadIdx.x & 63, ph = threadIdx.x >> 6;
-    const int k = blockIdx.x * 64 + kk;
-    double sum = 0.0;
-    if (k < K)
-        for (int t = ph; t < T; t += 4) sum += fabs((double)X[(size_t)t * K + k]);
-    __shared__ double part[4][64];
-    part[ph][kk] = sum;
+// Block: 64 columns, 1024 threads.  Thread (chunk c = tid % 8, phase r = tid / 8)
+// adds |x| of columns 8c..8c+7 over rows r, r + 128, ... with one 16-byte load
+// per row (eight threads read a 128-byte row segment), then the 128 phases of
+// each column meet in LDS.  Sums of |fp16| in fp64 are exact for T < 2^13, so
+// the order of the additions cannot change the result.
+__global__ __launch_bounds__(1024) void k_act_stat(const _Float16* __restrict__ X, int T, int K,
+                                                  float* __restrict__ s_x) {
+    const int c = threadIdx.x & 7, r = threadIdx.x >> 3;
+    const int k0 = blockIdx.x * 64 + 8 * c;              // K is a multiple of 128
+    double sum[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int t = r; t < T; t += 128) {
+        const uint4 v = *reinterpret_cast<const uint4*>(X + (size_t)t * K + k0);
+        const _Float16* h = reinterpret_cast<const _Float16*>(&v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum[e] += fabs((double)h[e]);
+    }
+    __shared__ double part[128][64 + 1];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[r][8 * c + e] = sum[e];
     __syncthreads();
-    if (ph == 0 && k < K) {
-        const double tot = ((part[0][kk] + part[1][kk]) + part[2][kk]) + part[3][kk];
-        s_x[k] = (float)(tot / (double)T);
+    if (threadIdx.x < 64) {
+        double tot = 0.0;
+        for (int q = 0; q < 128; ++q) tot += part[q][threadIdx.x];
+        s_x[blockIdx.x * 64 + threadIdx.x] = (float)(tot / (double)T);
     }
 }
 
@@ -146,6 +155,9 @@ __global__ __launch_bounds__(256) void k_quant_err(LayerList layers,
 }
 
 // One workgroup: fixed-order fp64 sums of the loss partials, first argmin.
+// Wave w sums the partials of alphas w, w + 4, ...: lane l adds tiles l, l + 64,
+// ... and the 64 lane sums meet in a fixed butterfly, so the result does not
+// depend on scheduling.
 __global__ __launch_bounds__(256) void k_select(const double* __restrict__ partials, int n_tiles,
                                                int n_alpha, double inv_count,
                                                const float* __restrict__ s_all, int K,
@@ -154,11 +166,13 @@ __global__ __launch_bounds__(256) void k_select(const double* __restrict__ parti
                                                int* __restrict__ best_out) {
     __shared__ double loss[kMaxAlpha];
     __shared__ int best_s;
-    const int tid = threadIdx.x;
-    if (tid < n_alpha) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int a = wave; a < n_alpha; a += 4) {
         double s = 0.0;
-        for (int j = 0; j < n_tiles; ++j) s += partials[(size_t)tid * n_tiles + j];
-        loss[tid] = s * inv_count;
+        for (int j = lane; j < n_tiles; j += 64) s += partials[(size_t)a * n_tiles + j];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+        if (lane == 0) loss[a] = s * inv_count;
     }
     __syncthreads();
     if (tid == 0) {
@@ -208,8 +222,7 @@ int launch_search(const void* const* Ws, const int* Ns, int n_layers, const void
     AlphaGrid grid{};
     for (int i = 0; i < n_alpha; ++i) grid.a[i] = alphas[i];
 
-    hipLaunchKernelGGL(k_act_stat, dim3((K + 63) / 64), dim3(256), 0, st,
-                       (const _Float16*)X_cal, T, K, s_x);
+    hipLaunchKernelGGL(k_act_stat, dim3(K / 64), dim3(1024), 0, st, (const _Float16*)X_cal, T, K, s_x);
     const long long nsk = (long long)n_alpha * K;
     hipLaunchKernelGGL(k_candidate_scales, dim3((unsigned)((nsk + 255) / 256)), dim3(256), 0, st,
                        s_x, K, grid, n_alpha, s_all, s_inv);
