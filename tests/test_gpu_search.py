@@ -208,3 +208,28 @@ def test_shared_search_gate_up_then_fused_pass(gpu):
     pg, pu = O.quantize(Wg, s_g, 4), O.quantize(Wu, s_g, 4)
     h_ref = O.gate_up(x, inv_s, (O.pack(pg[0], 4), pg[1], pg[2]), (O.pack(pu[0], 4), pu[1], pu[2]), 4, K)
     assert rel_err(host(h), h_ref) <= TOL
+
+
+def test_error_kernel_decides_exact_ties_like_the_quantizer(gpu):
+    """The search decides each code from v * (1/D) unless that lands near a
+    half-integer, where it divides.  Here every quotient is an exact half-
+    integer with D = 3 * 2^-10 (1/D inexact): groups span [-7D, 8D] and hold
+    (m + 1/2) D otherwise, all exact fp16 values; alpha = 0 makes s = 1.  A
+    wrong tie rule moves half the weights by D, which the loss shows."""
+    import torch
+    D = 3.0 * 2.0 ** -10
+    rng = np.random.default_rng(12)
+    N, K = 64, 512
+    m = rng.integers(-7, 8, (N, K))
+    W = ((m + 0.5) * D).astype(np.float32)
+    W[:, ::128] = -7 * D
+    W[:, 1::128] = 8 * D
+    W = W.astype(np.float16)
+    assert np.array_equal(W.astype(np.float64)[:, 2::128], ((m + 0.5) * D)[:, 2::128])   # exact in fp16
+    X = WL.random_activations(128, K, seed=13, sigma=1.0)
+    s_g, loss_g, best_g = awq.search_scale(dev(W), dev(X), [0.0], bits=4)
+    torch.cuda.synchronize()
+    _, loss_r, _ = O.search_scale(W, X, [0.0], 4)
+    q, d, z = O.quantize(W, None, 4)
+    assert np.all(d.astype(np.float64) == D) and np.all(z == 7)   # the stated grid
+    assert abs(float(host(loss_g)[0]) - loss_r[0]) <= 1e-3 * loss_r[0], (host(loss_g), loss_r)
