@@ -86,6 +86,27 @@ def test_degenerate_groups(gpu, bits, zero_point):
                 zero_point=zero_point)
 
 
+@pytest.mark.parametrize("bits", [4, 3])
+def test_exact_half_integer_quotients(gpu, bits):
+    """The quantizer decides each code from v * (1/D) unless that lands near a
+    half-integer, where it divides.  Here 98 % of the quotients v / D are exact
+    half-integers with D = 3 * 2^-10 (1/D inexact): every group spans
+    [lo D, hi D] with hi - lo = Q and holds (m + 1/2) D otherwise, all exact
+    fp16 values, so a wrong tie rule changes the codes."""
+    Q = 2 ** bits - 1
+    lo, hi = -(Q // 2), Q - Q // 2
+    D = 3.0 * 2.0 ** -10
+    rng = np.random.default_rng(14)
+    m = rng.integers(lo, hi, (48, 384))
+    W = (m + 0.5) * D
+    W[:, ::128], W[:, 1::128] = lo * D, hi * D
+    W16 = W.astype(np.float16)
+    assert np.array_equal(W16.astype(np.float64), W)              # exact in fp16
+    _, d, z = O.quantize(W16, None, bits)
+    assert np.all(d.astype(np.float64) == D) and np.all(z == -lo)  # the stated grid
+    _check_rows(W16, None, bits)
+
+
 @pytest.mark.parametrize("shape_index", [0, 1, 2])
 def test_workload2_full_size(gpu, shape_index):
     W = WL.workload(2).weights(shape_index)

@@ -118,6 +118,32 @@ __device__ __forceinline__ uint32_t quant_code(float v, const GroupParams& p) {
     return (uint32_t)c;
 }
 
+// The codes of NV values of one group, equal to quant_code's, without a
+// division per value: 1/D is rounded once and v * (1/D) lies within
+// 1.5 * 2^-23 relative of the rounded quotient v / D (|v / D| <= 16.4 for
+// every group the quantizer forms), so unless it is within 2^-16 of a
+// half-integer both round to the same integer.  Values near a half-integer
+// (rare: one ballot for the NV values) take the division.
+template <int Q, int NV>
+__device__ __forceinline__ void quant_codes(const float* v, const GroupParams& p, float* q) {
+    const float rd = 1.0f / p.delta;
+    bool near = false;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const float t = v[i] * rd;
+        q[i] = __builtin_rintf(t);
+        near |= fabsf(t - __builtin_floorf(t) - 0.5f) <= 0x1p-16f;
+    }
+    if (__builtin_amdgcn_ballot_w64(near)) {
+        if (near) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i) q[i] = __builtin_rintf(v[i] / p.delta);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) q[i] = fminf(fmaxf(q[i] + p.zero, 0.0f), (float)Q);
+}
+
 // ---------------------------------------------------------------------------
 // host-side launchers (each .hip file owns its kernels); they return 0 or a
 // hipError_t value.  Arguments have been validated by the C ABI layer.

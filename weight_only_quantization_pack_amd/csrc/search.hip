@@ -142,32 +142,13 @@ __global__ __launch_bounds__(256) void k_quant_err(LayerList layers,
             mx = fmaxf(mx, __shfl_xor(mx, m, GS / 8));
         }
         const GroupParams p = group_params<Q, ZP>(mn, mx);
-        // The codes are rint(fp32(v / D)), decided without a division per
-        // weight: 1/D is rounded once, and v * (1/D) is within 1.5 * 2^-23
-        // relative of the rounded quotient (|v / D| <= 16), so unless it lies
-        // within 2^-16 of a half-integer both round to the same integer.  Near
-        // a half-integer (rare; one ballot per 8 weights) the division decides.
-        const float rd = 1.0f / p.delta;
         float qc[8];
-        bool near = false;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float t = v[i] * rd;
-            qc[i] = __builtin_rintf(t);
-            near |= fabsf(t - __builtin_floorf(t) - 0.5f) <= 0x1p-16f;
-        }
-        if (__builtin_amdgcn_ballot_w64(near)) {
-            if (near) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) qc[i] = __builtin_rintf(v[i] / p.delta);
-            }
-        }
+        quant_codes<Q, 8>(v, p, qc);                   // as quant_code, see there
         uint4 out;
         _Float16* o = reinterpret_cast<_Float16*>(&out);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float q = fminf(fmaxf(qc[i] + p.zero, 0.0f), (float)Q);   // as quant_code
-            const float w_hat = (q - p.zero) * p.delta;          // exact in fp32
+            const float w_hat = (qc[i] - p.zero) * p.delta;      // exact in fp32
             o[i] = (_Float16)(w[i] - w_hat * ri[i]);
         }
         if (active) D[(size_t)alpha * n_chunks + t] = out;
