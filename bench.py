@@ -533,7 +533,7 @@ def main(argv=None):
                               "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4),
                               "traffic": None,
-                              "kernel": "k_gemm_w4p<4> (<= 256 tiles: 14336x4096), k_gemm_w4 (more)"}},
+                              "kernel": "k_gemm_w4p, 128 x 64*NBW tiles: NBW 7 for 4096x14336 (512 tiles), 4 for 14336x4096 (256), 6 for 4096x6144 (256)"}},
         "offline": offline,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count,

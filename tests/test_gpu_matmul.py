@@ -131,6 +131,29 @@ def test_gemm_int3_many_tiles(gpu, M):
     check("gemm", M, N, K, 3, seed=7, rows=np.concatenate([[0, N - 1], rows]))
 
 
+@pytest.mark.parametrize("bits,group_size", [(4, 128), (3, 128), (4, 64)])
+@pytest.mark.parametrize("N,width", [(14296, 448), (6100, 384)])
+def test_gemm_wide_tiles(gpu, N, width, bits, group_size):
+    """M = 2048 on 256 CUs: N = 14296 takes 128 x 448 tiles (7 column blocks per
+    wave; 512 tiles, two rounds) and N = 6100 128 x 384 tiles (6 per wave; 256
+    tiles).  Both end in a ragged tile whose last waves' columns lie past N;
+    the compared columns include every side of the first and last tile edges."""
+    M, K = 2048, 1024
+    last = (N - 1) // width * width
+    edges = [0, width - 1, width, 2 * width - 1, last - 1, last, N - 1]
+    rows = np.random.default_rng(N + bits + group_size).choice(N, 33, replace=False)
+    check("gemm", M, N, K, bits, seed=31 + bits, rows=np.concatenate([edges, rows]),
+          group_size=group_size)
+
+
+def test_gemm_two_workgroups_per_cu(gpu):
+    """M = 2048, N = 8192 on 256 CUs: 512 tiles of 128 x 256 columns, run by the
+    double-buffered kernel at two workgroups per CU (one round of 512 slots)."""
+    M, N, K = 2048, 8192, 1024
+    rows = np.random.default_rng(3).choice(N, 40, replace=False)
+    check("gemm", M, N, K, 4, seed=41, rows=np.concatenate([[0, 255, 256, N - 257, N - 1], rows]))
+
+
 @pytest.mark.parametrize("bits", [4, 3])
 @pytest.mark.parametrize("M,N,K", [(5, 302, 2048), (130, 200, 4736), (64, 1000, 8192)])
 def test_gemm_split_k(gpu, M, N, K, bits):

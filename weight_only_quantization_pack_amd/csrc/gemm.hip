@@ -20,19 +20,24 @@
 // A workgroup (4 waves) owns a 128 x 256 output tile; each wave a 128 x 64
 // strip (8 x 4 MFMA blocks, 128 fp32 accumulators per lane), so per k32 step
 // a wave reads 8 A fragments from LDS and dequantizes 4 B fragments for 32
-// MFMAs.  Tiles are mapped so that each XCD (workgroup id mod 8) walks a
+// MFMAs.  The pipelined kernel also has 128 x 384 and 128 x 448 tiles (6 or
+// 7 blocks per wave, up to 224 accumulators per lane in AGPRs): the same A
+// fragments feed 48 or 56 MFMAs, and the tile count of N = 6144 or 14336
+// becomes a whole number of rounds on 256 CUs.  Tiles are mapped so that each XCD (workgroup id mod 8) walks a
 // contiguous run of row-major tiles and keeps its A rows in its L2.
 //
 // Two schedules of that tile: k_gemm_w4 double-buffers A and B (one K-step
 // ahead) at two workgroups per CU; k_gemm_w4p keeps three K-steps in flight
 // (four 32 KB A buffers, four B register slots) at one workgroup per CU, with
 // the next k32 substep's A fragments and B operands prepared under the
-// current substep's MFMAs.  The launcher takes k_gemm_w4p while the tiles fit
-// on the CUs in one round and k_gemm_w4 otherwise.
+// current substep's MFMAs.  gemm_tile_choice picks the kernel and tile width
+// from the rounds each option takes on the CUs.
 //
 // Loss GEMM (k_loss_gemm): B = D_alpha = W - w_hat_alpha / s_alpha (fp16,
 // row-major), 128 x 128 tiles through LDS, and the epilogue sums Y^2 per tile
 // instead of storing Y.
+#include <climits>
+
 #include "awq_internal.h"
 
 namespace awq {
@@ -44,6 +49,12 @@ namespace {
 // 4096x6144 118-119 vs 123-124 us, 4096x14336 284-289 vs 291-292 us)
 #ifndef AWQ_GEMM_PRIO
 #define AWQ_GEMM_PRIO 1
+#endif
+
+// the k_gemm_w4p tiles with at least this many 16-column blocks per wave
+// dequantize each B tile just before its MFMAs (fewer live registers)
+#ifndef AWQ_GEMM_ILV
+#define AWQ_GEMM_ILV 7
 #endif
 
 constexpr int BM = 128, BN = 128, BK = 128;
@@ -353,7 +364,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(
 // Split K (part != nullptr): workgroup (tile, blockIdx.y) covers groups
 // [blockIdx.y * gsplit, +gsplit) and writes its fp32 partial tile to
 // part[blockIdx.y][M][N]; k_splitk_reduce adds the splits in order.
-template <int BITS, int GS, int S, int GMT>
+template <int BITS, int GS, int S, int GMT, int NBW>
 __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
     const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
@@ -362,6 +373,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     static_assert(GMT == 128 || GMT == 64, "128- or 64-row tiles");
     constexpr int FR = GMT / 16;                       // 16-row A fragments (and row groups per wave)
     constexpr int ABUFT = GMT * ROW_BYTES;             // one A buffer
+    constexpr int TN = 64 * NBW;                       // tile columns: NBW 16-column blocks per wave
     extern __shared__ __attribute__((aligned(16))) unsigned char As[];   // S x ABUFT
 
     const int tid = threadIdx.x;
@@ -372,11 +384,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     const int g_begin = (int)blockIdx.y * gsplit;      // this workgroup's groups: [g_begin, g_begin + NGS)
     const int NGS = min(G - g_begin, gsplit);
     const int NB = (N + 15) / 16;
-    const int nTn = (N + GN - 1) / GN, nTm = (M + GMT - 1) / GMT;
+    const int nTn = (N + TN - 1) / TN, nTm = (M + GMT - 1) / GMT;
     const int nT = nTn * nTm;
     int t = blockIdx.x;
     if (nT % 8 == 0) t = (t % 8) * (nT / 8) + t / 8;
-    const int m0 = (t / nTn) * GMT, n0 = (t % nTn) * GN;
+    const int m0 = (t / nTn) * GMT, n0 = (t % nTn) * TN;
 
     uint32_t a_off[FR];
 #pragma unroll
@@ -387,10 +399,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
         const int grow = min(m0 + r, M - 1);
         a_off[i] = (uint32_t)grow * (uint32_t)K + 8u * kc;
     }
-    uint32_t tbase[4];
+    uint32_t tbase[NBW];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int blk = min(n0 / 16 + wave * 4 + c, NB - 1);
+    for (int c = 0; c < NBW; ++c) {
+        const int blk = min(n0 / 16 + wave * NBW + c, NB - 1);
         tbase[c] = (uint32_t)blk * (uint32_t)G;
     }
     const uint32_t psh = 16u * (uint32_t)(j & 1);      // the lane's half of a parameter word
@@ -399,14 +411,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     const uint32_t pgrp = GS == 64 ? (uint32_t)(hq >> 1) : 0u;
 
     constexpr int WQ = BITS == 4 ? 4 : 3;              // words per lane slot
-    constexpr int LPS = FR + 4 + 8;                    // loads per step and wave: A, B tiles, D and z words
-    struct BStage { uint32_t q[4][WQ]; uint32_t d[4], z[4]; };
-    // part p (0..3) of step kt's loads: A rows groups 2p, 2p + 1 (direct to LDS
-    // buffer `slot`), B tile p of this wave and its scale and zero words
+    constexpr int LPS = FR + 3 * NBW;                  // loads per step and wave: A, B tiles, D and z words
+    static_assert(LPS * (S - 2) <= 63, "vmcnt counts to 63");
+    struct BStage { uint32_t q[NBW][WQ]; uint32_t d[NBW], z[NBW]; };
+    // part p (0..NBW-1) of step kt's loads: the A row groups i with
+    // i * NBW / FR = p (direct to LDS buffer `slot`), B tile p of this wave and
+    // its scale and zero words
     auto issue_part = [&](int kt, int slot, BStage& bs, int p) {
         const uint32_t g = (uint32_t)(g_begin + min(kt, NGS - 1));
 #pragma unroll
-        for (int i = p * FR / 4; i < (p + 1) * FR / 4; ++i) {
+        for (int i = 0; i < FR; ++i) {
+            if (i * NBW / FR != p) continue;
             const int rg = wave * FR + i;
             __builtin_amdgcn_global_load_lds((global_void_t*)(x + a_off[i] + g * GK),
                                              (lds_void_t*)(As + slot * ABUFT + rg * 1024), 16, 0, 0);
@@ -426,23 +441,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     };
     auto issue = [&](int kt, int slot, BStage& bs) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) issue_part(kt, slot, bs, p);
+        for (int p = 0; p < NBW; ++p) issue_part(kt, slot, bs, p);
     };
 
-    float4_t acc[FR][4];
+    float4_t acc[FR][NBW];
 #pragma unroll
     for (int i = 0; i < FR; ++i)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[i][c] = (float4_t){0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < NBW; ++c) acc[i][c] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-    // One K-step: four k32 substeps of 4 FR MFMAs.  The A fragments (FR LDS reads)
-    // and B operands (4 dequantized words) of substep s + 1 are produced while
+    // One K-step: four k32 substeps of NBW FR MFMAs.  The A fragments (FR LDS
+    // reads) and B operands (NBW dequantized words) of substep s + 1 are produced while
     // the MFMAs of substep s run, so that neither LDS latency nor the
     // dequantization sits between two MFMA groups.
     auto compute = [&](const BStage& bs, const unsigned char* abuf) {
-        half2_t zz[4], zz16[4], dd[4];
+        half2_t zz[NBW], zz16[NBW], dd[NBW];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < NBW; ++c) {
             const _Float16 z = __builtin_bit_cast(_Float16, (unsigned short)(bs.z[c] >> psh));
             const _Float16 d = __builtin_bit_cast(_Float16, (unsigned short)(bs.d[c] >> psh));
             const _Float16 zb = (_Float16)1024.0f + z, zb16 = (_Float16)64.0f + z;
@@ -460,7 +475,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
         };
         auto dequant = [&](int s, half8_t* b) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
+            for (int c = 0; c < NBW; ++c) {
                 if constexpr (BITS == 4) {
                     b[c] = dequant_scaled(bs.q[c][s], zz[c], zz16[c], dd[c]);
                 } else {
@@ -469,12 +484,37 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
                 }
             }
         };
-        half8_t a_cur[FR], b_cur[4];
+        if constexpr (NBW >= AWQ_GEMM_ILV) {
+            // registers for one tile's B operand only: each tile is dequantized
+            // just before its FR MFMAs, under the previous tile's
+            half8_t a_cur[FR];
+            read_a(0, a_cur);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                half8_t a_nxt[FR];
+                if (s < 3) read_a(s + 1, a_nxt);
+#pragma unroll
+                for (int c = 0; c < NBW; ++c) {
+                    half8_t b;
+                    if constexpr (BITS == 4) b = dequant_scaled(bs.q[c][s], zz[c], zz16[c], dd[c]);
+                    else b = dequant_scaled_int3(bs.q[c], s, zz[c], dd[c]);
+#pragma unroll
+                    for (int i = 0; i < FR; ++i)
+                        acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a_cur[i], acc[i][c], 0, 0, 0);
+                }
+                if (s < 3) {
+#pragma unroll
+                    for (int i = 0; i < FR; ++i) a_cur[i] = a_nxt[i];
+                }
+            }
+            return;
+        }
+        half8_t a_cur[FR], b_cur[NBW];
         read_a(0, a_cur);
         dequant(0, b_cur);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            half8_t a_nxt[FR], b_nxt[4];
+            half8_t a_nxt[FR], b_nxt[NBW];
             if (s < 3) {
                 read_a(s + 1, a_nxt);
                 dequant(s + 1, b_nxt);
@@ -482,13 +522,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
 #pragma unroll
             for (int i = 0; i < FR; ++i)
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
+                for (int c = 0; c < NBW; ++c)
                     acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b_cur[c], a_cur[i], acc[i][c], 0, 0, 0);
             if (s < 3) {
 #pragma unroll
                 for (int i = 0; i < FR; ++i) a_cur[i] = a_nxt[i];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) b_cur[c] = b_nxt[c];
+                for (int c = 0; c < NBW; ++c) b_cur[c] = b_nxt[c];
             }
         }
     };
@@ -534,8 +574,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
             if (m >= M) continue;
             float* prow = prow0 + (size_t)m * N;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int n = n0 + wave * 64 + 16 * c + 4 * hq;
+            for (int c = 0; c < NBW; ++c) {
+                const int n = n0 + wave * 16 * NBW + 16 * c + 4 * hq;
                 if (n + 3 < N && ((N & 3) == 0)) {
                     *reinterpret_cast<float4_t*>(prow + n) = acc[i][c];
                 } else {
@@ -553,8 +593,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
         if (m >= M) continue;
         _Float16* yrow = Y + (size_t)m * N;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int n = n0 + wave * 64 + 16 * c + 4 * hq;
+        for (int c = 0; c < NBW; ++c) {
+            const int n = n0 + wave * 16 * NBW + 16 * c + 4 * hq;
             const half2_t lo = {(_Float16)acc[i][c][0], (_Float16)acc[i][c][1]};
             const half2_t hi = {(_Float16)acc[i][c][2], (_Float16)acc[i][c][3]};
             if (n + 3 < N && ((N & 3) == 0)) {
@@ -598,20 +638,24 @@ constexpr int kGemmStages = 4;
 // row (half of a 128-row tile would multiply padding rows), else 128
 int w4p_rows(int M) { return M <= 64 ? 64 : 128; }
 
-int w4p_tiles(int M, int N) {
+int w4p_tiles(int M, int N, int nbw = 4) {
     const int rows = w4p_rows(M);
-    return ((N + w4::GN - 1) / w4::GN) * ((M + rows - 1) / rows);
+    return ((N + 64 * nbw - 1) / (64 * nbw)) * ((M + rows - 1) / rows);
 }
 
-template <int GMT>
+template <int GMT, int NBW>
 int launch_w4p_rows(const void* x, const void* qweight, const void* scales, const void* zeros,
                     void* y, float* part, int M, int N, int K, int bits, int group_size, int splits,
                     int gsplit, hipStream_t st) {
-    const int nT = ((N + w4::GN - 1) / w4::GN) * ((M + GMT - 1) / GMT);
-    const size_t lds = (size_t)kGemmStages * GMT * w4::ROW_BYTES;
+#ifndef AWQ_GEMM_S7
+#define AWQ_GEMM_S7 3
+#endif
+    constexpr int S = NBW >= 7 ? AWQ_GEMM_S7 : kGemmStages;   // NBW = 7: four stages spill
+    const int nT = ((N + 64 * NBW - 1) / (64 * NBW)) * ((M + GMT - 1) / GMT);
+    const size_t lds = (size_t)S * GMT * w4::ROW_BYTES;
     auto kern = group_size == 64
-                    ? (bits == 4 ? k_gemm_w4p<4, 64, kGemmStages, GMT> : k_gemm_w4p<3, 64, kGemmStages, GMT>)
-                    : (bits == 4 ? k_gemm_w4p<4, 128, kGemmStages, GMT> : k_gemm_w4p<3, 128, kGemmStages, GMT>);
+                    ? (bits == 4 ? k_gemm_w4p<4, 64, S, GMT, NBW> : k_gemm_w4p<3, 64, S, GMT, NBW>)
+                    : (bits == 4 ? k_gemm_w4p<4, 128, S, GMT, NBW> : k_gemm_w4p<3, 128, S, GMT, NBW>);
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return (int)e;
@@ -621,14 +665,49 @@ int launch_w4p_rows(const void* x, const void* qweight, const void* scales, cons
     return (int)hipGetLastError();
 }
 
+// nbw: 16-column blocks per wave of the 128-row tiles (4, 6 or 7; see
+// gemm_tile_choice); 64-row tiles always take 4
 int launch_w4p(const void* x, const void* qweight, const void* scales, const void* zeros, void* y,
                float* part, int M, int N, int K, int bits, int group_size, int splits, int gsplit,
-               hipStream_t st) {
+               hipStream_t st, int nbw = 4) {
     if (w4p_rows(M) == 64)
-        return launch_w4p_rows<64>(x, qweight, scales, zeros, y, part, M, N, K, bits, group_size,
+        return launch_w4p_rows<64, 4>(x, qweight, scales, zeros, y, part, M, N, K, bits, group_size,
+                                      splits, gsplit, st);
+    if (nbw == 6)
+        return launch_w4p_rows<128, 6>(x, qweight, scales, zeros, y, part, M, N, K, bits, group_size,
+                                       splits, gsplit, st);
+    if (nbw == 7)
+        return launch_w4p_rows<128, 7>(x, qweight, scales, zeros, y, part, M, N, K, bits, group_size,
+                                       splits, gsplit, st);
+    return launch_w4p_rows<128, 4>(x, qweight, scales, zeros, y, part, M, N, K, bits, group_size,
                                    splits, gsplit, st);
-    return launch_w4p_rows<128>(x, qweight, scales, zeros, y, part, M, N, K, bits, group_size,
-                                splits, gsplit, st);
+}
+
+// The GEMM's kernel and tile for M > 64: 16-column blocks per wave (4, 6 or
+// 7) of the pipelined one-workgroup-per-CU kernel, or 0 for the
+// double-buffered kernel at two workgroups per CU (int4, 128-wide groups
+// only).  A CU's time is taken as proportional to the tiles it runs times
+// their width, so each candidate costs ceil(tiles / slots) * NBW; a round of
+// the two-per-CU kernel (two 4-block tiles per CU, one's loads under the
+// other's MFMAs) is priced at 7, below the 8 of two pipelined rounds.  The
+// cheapest wins, ties going to the wider tile (fewer A reads from LDS per
+// MFMA).  MI355X, M = 2048: 4096x14336 NBW 7 (512 tiles, two rounds) 881-892
+// vs 828-839 TFLOP/s for the two-per-CU kernel (896 tiles) and 732-739 for
+// NBW 4 (four rounds); 4096x6144 NBW 6 (256 tiles) 989-1015 vs 862 and 717;
+// 14336x4096 NBW 4 (256 tiles) 943 vs NBW 6 775, NBW 7 670.  M <= 64
+// (64-row tiles) always takes NBW 4.
+int gemm_tile_choice(int M, int N, int bits, int group_size, int cus) {
+    if (w4p_rows(M) == 64) return 4;
+    int best = 4, best_cost = INT_MAX;
+    for (const int nbw : {7, 6, 4}) {
+        const int rounds = (w4p_tiles(M, N, nbw) + cus - 1) / cus;
+        if (rounds * nbw < best_cost) { best = nbw; best_cost = rounds * nbw; }
+    }
+    if (bits == 4 && group_size == 128) {
+        const int rounds2 = (w4p_tiles(M, N) + 2 * cus - 1) / (2 * cus);
+        if (rounds2 * 7 < best_cost) best = 0;
+    }
+    return best;
 }
 
 }  // namespace
@@ -676,15 +755,10 @@ int launch_gemm(const void* x, const void* qweight, const void* scales, const vo
     if ((unsigned long long)M * K >= (1ull << 31) || (unsigned long long)N * K / 8 >= (1ull << 31))
         return (int)hipErrorInvalidValue;
     const int nT = ((N + w4::GN - 1) / w4::GN) * ((M + w4::GM - 1) / w4::GM);
-    // Up to one tile per CU: the 4-stage pipelined kernel (one workgroup per
-    // CU).  More tiles: the double-buffered kernel at two workgroups per CU,
-    // whose 2 x CUs slots round the tile count better (MI355X, M = 2048:
-    // 14336x4096 (256 tiles) 974 vs 743 TFLOP/s; 4096x14336 (896 tiles) 764 vs
-    // 816; 4096x6144 (384 tiles) 739 vs 849).
-    // int3, 64-wide groups and M <= 64 (64-row tiles) take the pipelined kernel
-    if (bits == 3 || group_size == 64 || nT <= device_cu_count() || w4p_rows(M) == 64) {
+    const int nbw = gemm_tile_choice(M, N, bits, group_size, device_cu_count());
+    if (nbw > 0) {
         return launch_w4p(x, qweight, scales, zeros, y, nullptr, M, N, K, bits, group_size, 1,
-                          K / kGroup, st);
+                          K / kGroup, st, nbw);
     } else {
         hipLaunchKernelGGL(k_gemm_w4, dim3(nT), dim3(256), 0, st, (const _Float16*)x,
                            (const uint32_t*)qweight, (const _Float16*)scales, (const _Float16*)zeros,
