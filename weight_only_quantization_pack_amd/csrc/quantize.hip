@@ -26,45 +26,6 @@ __device__ __forceinline__ void unpack8(const uint4& raw, float* f) {
     for (int i = 0; i < 8; ++i) f[i] = (float)h[i];
 }
 
-// The codes of the 32 values of one lane, each equal to quant_code's, in
-// bits 16..19 of T[i] (bits 20..23 zero), decided without a division or a
-// rounding instruction.  One fma forms t = v * (1/D) + (z + 128.5 + 3 * 2^-16),
-// clamped to [128.25, 128.5 + Q]; there fp32 values are multiples of 2^-16,
-// so the float's bits 16..22 hold the integer part of t - 128 and bits 0..15
-// its fraction F.  t is within 2^-17 (the fma's rounding) + 16.4 * 2^-24 (that
-// of 1/D, |v / D| <= 16.4) < 0.64 * 2^-16 of v / D + z + 1/2 + 3 * 2^-16, so
-// F >= 6 * 2^-16 puts v / D + z more than 2.3 * 2^-16 above and 1/2 - 6 * 2^-16
-// below a half-integer: its integer part is then rint(v / D) + z for the
-// exact quotient and for its rounding to fp32 (within 2^-20) alike, with no
-// tie.  The clamp bounds give F = 1/4 and 1/2 for codes 0 and Q, which
-// clamping the rounded quotient also gives.  Lanes with some F <= 5 * 2^-16
-// (rare: one ballot) take quant_code's division for all their values.
-template <int Q, int NV>
-__device__ __forceinline__ void quant_codes_b2(const float* v, const GroupParams& p, uint32_t* T) {
-    const float rd = 1.0f / p.delta;
-    const float zb = p.zero + (128.5f + 0x3p-16f);   // exact: z <= 15
-    uint32_t fmin = 0xFFFFu;                          // least fraction F, in units of 2^-16
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const float t = __builtin_amdgcn_fmed3f(__builtin_fmaf(v[i], rd, zb), 128.25f, 128.5f + Q);
-        T[i] = __builtin_bit_cast(uint32_t, t);
-        fmin = min(fmin, T[i] & 0xFFFFu);
-    }
-    const bool near = fmin <= 5u;
-    if (__builtin_amdgcn_ballot_w64(near)) {
-        if (near) {
-#pragma unroll
-            for (int i = 0; i < NV; ++i) T[i] = quant_code<Q>(v[i], p) << 16;
-        }
-    }
-}
-
-// Codes 2i and 2i + 1 (bits 16..19 of T[2i], T[2i + 1]) as one magic pair:
-// bits 0..3 and 16..19.
-__device__ __forceinline__ uint32_t code_pair(const uint32_t* T, int i) {
-    return ((T[2 * i] >> 16) & 0xFFu) | (T[2 * i + 1] & 0x00FF0000u);
-}
-
 // One wave per tile; BITS selects 4 words (int4) or 3 words (int3) per slot.
 // GS = 128: one group per tile; GS = 64: two (quarters 0-1 and 2-3 of a row).
 template <int BITS, bool ZP, int GS>

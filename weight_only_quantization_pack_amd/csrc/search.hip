@@ -95,9 +95,11 @@ __global__ __launch_bounds__(256) void k_candidate_scales(const float* __restric
 // does not depend on the packed format).  W is read once: each lane keeps its
 // 8 weights and walks the alphas, writing D_alpha for each (s_alpha is small
 // and stays in L2), so the traffic is one read of W plus the D writes.  The
-// codes use the true fp32 division v / Delta, as awq_quantize_pack does; D
-// multiplies by the reciprocal of s (within 1.5 fp32 ulp of w_hat / s before
-// D's own fp16 rounding), which halves the divisions of this VALU-bound loop.
+// codes are rint(fp32(v / Delta)) as in awq_quantize_pack, decided in fixed
+// point (quant_codes_b2); w_hat = fma(q, Delta, -z * Delta) is the exact
+// (q - z) * Delta.  D multiplies by the reciprocal of s (within 1.5 fp32 ulp
+// of w_hat / s before D's own fp16 rounding), which spares this VALU-bound
+// loop a division per weight.
 template <int Q, bool ZP, int GS>
 __global__ __launch_bounds__(256) void k_quant_err(LayerList layers,
                                                   const float* __restrict__ s_all,
@@ -142,13 +144,15 @@ __global__ __launch_bounds__(256) void k_quant_err(LayerList layers,
             mx = fmaxf(mx, __shfl_xor(mx, m, GS / 8));
         }
         const GroupParams p = group_params<Q, ZP>(mn, mx);
-        float qc[8];
-        quant_codes<Q, 8>(v, p, qc);                   // as quant_code, see there
+        uint32_t T[8];
+        quant_codes_b2<Q, 8>(v, p, T);                 // = quant_code of each value, << 16
+        const float zd = -(p.zero * p.delta);          // exact: z <= 16, Delta an fp16 value
         uint4 out;
         _Float16* o = reinterpret_cast<_Float16*>(&out);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float w_hat = (qc[i] - p.zero) * p.delta;      // exact in fp32
+            const float q = (float)((T[i] >> 16) & 0xFFu);
+            const float w_hat = __builtin_fmaf(q, p.delta, zd);  // (q - z) * Delta, exact
             o[i] = (_Float16)(w[i] - w_hat * ri[i]);
         }
         if (active) D[(size_t)alpha * n_chunks + t] = out;
