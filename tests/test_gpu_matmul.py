@@ -133,12 +133,14 @@ def test_gemm_int3_many_tiles(gpu, M):
 
 @pytest.mark.parametrize("bits,group_size", [(4, 128), (3, 128), (4, 64)])
 @pytest.mark.parametrize("N,width", [(14296, 448), (6100, 384)])
-def test_gemm_wide_tiles(gpu, N, width, bits, group_size):
-    """M = 2048 on 256 CUs: N = 14296 takes 128 x 448 tiles (7 column blocks per
-    wave; 512 tiles, two rounds) and N = 6100 128 x 384 tiles (6 per wave; 256
-    tiles).  Both end in a ragged tile whose last waves' columns lie past N;
-    the compared columns include every side of the first and last tile edges."""
-    M, K = 2048, 1024
+@pytest.mark.parametrize("M", [2048, 1999])
+def test_gemm_wide_tiles(gpu, M, N, width, bits, group_size):
+    """M = 2048 or 1999 (16 row tiles, the last one ragged) on 256 CUs: N =
+    14296 takes 128 x 448 tiles (7 column blocks per wave; 512 tiles, two
+    rounds) and N = 6100 128 x 384 tiles (6 per wave; 256 tiles).  Both end in
+    a ragged tile whose last waves' columns lie past N; the compared columns
+    include every side of the first and last tile edges."""
+    K = 1024
     last = (N - 1) // width * width
     edges = [0, width - 1, width, 2 * width - 1, last - 1, last, N - 1]
     rows = np.random.default_rng(N + bits + group_size).choice(N, 33, replace=False)
