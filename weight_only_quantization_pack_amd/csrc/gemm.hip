@@ -160,6 +160,16 @@ typedef __attribute__((address_space(1))) const void global_void_t;
 // outstanding, no wait on lgkm/exp counters
 constexpr unsigned vmcnt_imm(unsigned n) { return (n & 15u) | ((n >> 4) << 14) | (7u << 4) | (15u << 8); }
 
+// The 16-byte chunk position that holds global chunk kc of A row r in LDS is
+// kc ^ a_swz(r).  An A-fragment read has lane (j, hq) fetch chunk 4 hq + s of
+// row 16 i + j; measured on MI355X (SQ_LDS_BANK_CONFLICT), XOR-ing with r & 15
+// costs 4 conflict cycles per 8-cycle ds_read_b128, while any bit permutation
+// of r & 15 that puts bit 0 or 1 of the row into bit 2 of the XOR is free of
+// conflicts.  a_swz swaps bits 0 and 2.
+__device__ __forceinline__ int a_swz(int r) {
+    return (r & 0xA) | ((r & 1) << 2) | ((r >> 2) & 1);
+}
+
 namespace w4 {
 constexpr int GM = 128, GN = 256, GK = 128;    // workgroup tile; GK = one group
 constexpr int ROW_BYTES = GK * 2;              // one A row of a K-step in LDS
@@ -217,15 +227,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(
 
     // A: 32 direct-to-LDS instructions per K-step (1 KB = 4 rows each), 8 per
     // wave.  Lane l of instruction rg writes LDS chunk p = l & 15 of row
-    // r = 4 rg + (l >> 4), which holds the row's global chunk p ^ (r & 15):
-    // the 16 rows read by one LDS phase then sit on 16 different bank quads.
+    // r = 4 rg + (l >> 4), which holds the row's global chunk p ^ a_swz(r), so
+    // that the A-fragment reads are free of bank conflicts.
     // 32-bit element offsets into A (the launcher guarantees M * K < 2^31)
     uint32_t a_off[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int rg = wave * 8 + i;
         const int r = 4 * rg + (lane >> 4);
-        const int kc = (lane & 15) ^ (r & 15);
+        const int kc = (lane & 15) ^ a_swz(r);
         const int grow = min(m0 + r, M - 1);          // rows past M: any valid row (never stored)
         a_off[i] = (uint32_t)grow * (uint32_t)K + 8u * kc;
     }
@@ -299,7 +309,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(
             for (int i = 0; i < 8; ++i) {
                 const int r = 16 * i + j;
                 const half8_t a = *reinterpret_cast<const half8_t*>(
-                    abuf + r * ROW_BYTES + ((kc ^ (r & 15)) << 4));
+                    abuf + r * ROW_BYTES + ((kc ^ a_swz(r)) << 4));
                 // weights as the A operand, activations as B: the accumulator of
                 // lane 16 hq + j then holds output row m = 16 i + j and the four
                 // consecutive columns 16 c + 4 hq + r
@@ -395,7 +405,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     for (int i = 0; i < FR; ++i) {
         const int rg = wave * FR + i;
         const int r = 4 * rg + (lane >> 4);
-        const int kc = (lane & 15) ^ (r & 15);
+        const int kc = (lane & 15) ^ a_swz(r);
         const int grow = min(m0 + r, M - 1);
         a_off[i] = (uint32_t)grow * (uint32_t)K + 8u * kc;
     }
@@ -470,7 +480,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
 #pragma unroll
             for (int i = 0; i < FR; ++i) {
                 const int r = 16 * i + j;
-                a[i] = *reinterpret_cast<const half8_t*>(abuf + r * ROW_BYTES + ((kc ^ (r & 15)) << 4));
+                a[i] = *reinterpret_cast<const half8_t*>(abuf + r * ROW_BYTES + ((kc ^ a_swz(r)) << 4));
             }
         };
         auto dequant = [&](int s, half8_t* b) {
