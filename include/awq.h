@@ -144,10 +144,24 @@ int awq_scale_activations(const void* x, const float* s, void* x_out, int M,
                           int K, void* stream);
 
 /*
- * awq_search_workspace_bytes -- device workspace needed by awq_search_scale
- * for T calibration tokens, an N x K layer and n_alpha grid points.
+ * awq_search_workspace_bytes -- device workspace of awq_search_scale's
+ * default path for T calibration tokens, an N x K layer and n_alpha grid
+ * points: it holds W - w_hat_i / s_i for every alpha (n_alpha * N * K fp16)
+ * for the loss GEMM.  0 when an argument is <= 0.
  */
 size_t awq_search_workspace_bytes(int T, int N, int K, int n_alpha);
+
+/*
+ * awq_search_workspace_bytes_fused -- the smaller workspace (scales and loss
+ * partials only, under a megabyte for a 4096 x 4096 layer) with which
+ * awq_search_scale and awq_search_scale_shared take their fused path: one
+ * loss kernel forms W - w_hat_i / s_i in registers instead of writing it out
+ * (same codes and the same fp16 differences; MI355X, 4096 x 4096, T = 512, 20
+ * alphas: 0.85 ms against 0.81 ms).  A workspace of at least
+ * awq_search_workspace_bytes selects the default path, one of at least this
+ * size the fused one, anything smaller is AWQ_ERR_WORKSPACE.
+ */
+size_t awq_search_workspace_bytes_fused(int T, int N, int K, int n_alpha);
 
 /*
  * awq_search_scale -- the AWQ scale search ("Usage" step 1, --run_awq, of
@@ -166,9 +180,10 @@ size_t awq_search_workspace_bytes(int T, int N, int K, int n_alpha);
  *   loss_out fp32 [n_alpha] out, or NULL
  *   best_out int32 [1] out (device), or NULL
  *   workspace / workspace_bytes: device scratch of at least
- *            awq_search_workspace_bytes(T, N, K, n_alpha) bytes.
- * The loss GEMM runs on fp16 MFMA with fp32 accumulation over the fp16
- * differences W - w_hat_i * (1/s_i) (the codes use the exact division of
+ *            awq_search_workspace_bytes(T, N, K, n_alpha) bytes (default
+ *            path), or of awq_search_workspace_bytes_fused bytes (fused path).
+ * The loss is one fp16 MFMA kernel with fp32 accumulation that forms the fp16
+ * differences W - w_hat_i * (1/s_i) in registers (the codes are those of
  * awq_quantize_pack), so L_i carries a relative error of order 1e-4 and
  * near-ties may pick a neighbouring alpha.
  */
@@ -188,7 +203,8 @@ int awq_search_scale(const void* W, const void* X_cal, int T, int N, int K,
  *   awq_search_scale.  Each layer is read in place (no copy).
  *   Ws       HOST array of n_layers device pointers, layer l fp16 [Ns[l]][K]
  *   Ns       HOST int array [n_layers], each >= 1;  1 <= n_layers <= 8
- *   workspace: awq_search_workspace_bytes(T, sum Ns, K, n_alpha) bytes.
+ *   workspace: awq_search_workspace_bytes(T, sum Ns, K, n_alpha) bytes, or
+ *            the _fused size for the fused path.
  *   Errors as awq_search_scale; n_layers out of range is AWQ_ERR_UNSUPPORTED,
  *   a NULL Ws / Ns / layer pointer AWQ_ERR_NULL, a row count <= 0 AWQ_ERR_SHAPE.
  */

@@ -38,6 +38,7 @@ def header_functions():
 def test_header_declares_the_boundary():
     names = header_functions()
     for must in ["awq_quantize_pack", "awq_search_scale", "awq_search_workspace_bytes",
+                 "awq_search_workspace_bytes_fused",
                  "awq_gemv", "awq_gemm", "awq_scale_activations", "awq_status_str"]:
         assert must in names
 
@@ -69,7 +70,13 @@ def test_format_helpers(lib):
 def test_search_workspace_size(lib):
     T, N, K, A = 512, 4096, 4096, 20
     need = lib.awq_search_workspace_bytes(T, N, K, A)
-    assert need >= A * N * K * 2 + (A + 1) * K * 4
+    assert need >= A * N * K * 2 + (2 * A + 1) * K * 4       # D for every alpha + scales
+    # fused path: s_x, s_alpha and 1/s_alpha, and one fp64 loss partial per
+    # alpha and 256 x 128 output block; W - w_hat / s stays in registers
+    fused = lib.awq_search_workspace_bytes_fused(T, N, K, A)
+    partials = A * ((N + 127) // 128) * ((T + 255) // 256) * 8
+    assert (2 * A + 1) * K * 4 + partials <= fused < A * N * K * 2 // 100
+    assert lib.awq_search_workspace_bytes_fused(0, N, K, A) == 0
     assert lib.awq_search_workspace_bytes(0, N, K, A) == 0
     assert lib.awq_search_workspace_bytes(T, N, K, 0) == 0
 
@@ -222,8 +229,11 @@ def test_search_validation(lib):
     assert search(lib, W=NUL) == NULL
     assert search(lib, s_out=MIS) == ALIGN
     assert search(lib, loss=MIS) == ALIGN
-    good = lib.awq_search_workspace_bytes(64, 256, 512, 2)
-    assert search(lib, ws_bytes=good - 1) == WS
+    # below the fused path's size: no path fits (between it and the default
+    # size the fused path runs, which needs a GPU)
+    least = lib.awq_search_workspace_bytes_fused(64, 256, 512, 2)
+    assert 0 < least < lib.awq_search_workspace_bytes(64, 256, 512, 2)
+    assert search(lib, ws_bytes=least - 1) == WS
 
 
 def shared(lib, Ws=(P, P2, P3), Ns=(64, 32, 32), n=None, X=P4, T=64, K=512, alphas=(0.0, 0.5),
@@ -256,8 +266,8 @@ def test_search_shared_validation(lib):
     assert shared(lib, bits=5) == UNSUP
     assert shared(lib, X=NUL) == NULL
     assert shared(lib, s_out=MIS) == ALIGN
-    good = lib.awq_search_workspace_bytes(64, 128, 512, 2)
-    assert shared(lib, ws_bytes=good - 1) == WS
+    least = lib.awq_search_workspace_bytes_fused(64, 128, 512, 2)
+    assert shared(lib, ws_bytes=least - 1) == WS
 
 
 def test_binding_refuses_when_library_missing(monkeypatch, tmp_path):

@@ -18,11 +18,23 @@ from gpu_util import TOL, announce, dev, host, rel_err
 
 pytestmark = pytest.mark.gpu
 
+FUSED = False
+
+
+@pytest.fixture(autouse=True, params=[False, True], ids=["buffered", "fused"])
+def search_path(request):
+    """Every search test runs on both paths: the default one (error kernel
+    writing D, loss GEMM) and the fused loss kernel (small workspace)."""
+    global FUSED
+    FUSED = request.param
+    yield
+    FUSED = False
+
 
 def gpu_search(W, X, alphas, bits, zero_point=True, group_size=128):
     import torch
     s, loss, best = awq.search_scale(dev(W), dev(X), alphas, bits=bits, group_size=group_size,
-                                     zero_point=zero_point)
+                                     zero_point=zero_point, fused=FUSED)
     torch.cuda.synchronize()
     return host(s), host(loss).astype(np.float64), int(host(best)[0])
 
@@ -121,7 +133,7 @@ def test_workload1_end_to_end(gpu):
     W, X = wl.weights(), wl.calibration()
     announce("workload1 end to end")
     Wd = dev(W)
-    s, _, _ = awq.search_scale(Wd, dev(X), wl.alphas, bits=4)
+    s, _, _ = awq.search_scale(Wd, dev(X), wl.alphas, bits=4, fused=FUSED)
     qw, sc, ze = awq.quantize_pack(Wd, s, bits=4)
     torch.cuda.synchronize()
     s_g = host(s)
@@ -145,7 +157,8 @@ def check_shared(Ws, X, alphas, bits=4, zero_point=True, group_size=128):
     import torch
     announce("search_scale_shared", [w.shape for w in Ws], X.shape, len(alphas), bits)
     s_g, loss_g, best_g = awq.search_scale_shared([dev(W) for W in Ws], dev(X), alphas, bits=bits,
-                                                  group_size=group_size, zero_point=zero_point)
+                                                  group_size=group_size, zero_point=zero_point,
+                                                  fused=FUSED)
     torch.cuda.synchronize()
     s_g, loss_g, best_g = host(s_g), host(loss_g).astype(np.float64), int(host(best_g)[0])
     s_r, loss_r, best_r = O.search_scale_shared(Ws, X, alphas, bits, group_size, zero_point)
@@ -176,7 +189,8 @@ def test_shared_search_equals_search_of_the_stacked_layer(gpu):
     X = WL.random_activations(128, K, seed=71, sigma=1.5)
     alphas = [0.0, 0.25, 0.5, 0.75]
     s_a, loss_a, best_a = check_shared(Ws, X, alphas, 4)
-    s_b, loss_b, best_b = awq.search_scale(dev(np.concatenate(Ws)), dev(X), alphas, bits=4)
+    s_b, loss_b, best_b = awq.search_scale(dev(np.concatenate(Ws)), dev(X), alphas, bits=4,
+                                           fused=FUSED)
     torch.cuda.synchronize()
     assert np.array_equal(s_a, host(s_b)) and best_a == int(host(best_b)[0])
     assert np.array_equal(loss_a.astype(np.float32), host(loss_b))
@@ -227,9 +241,34 @@ def test_error_kernel_decides_exact_ties_like_the_quantizer(gpu):
     W = W.astype(np.float16)
     assert np.array_equal(W.astype(np.float64)[:, 2::128], ((m + 0.5) * D)[:, 2::128])   # exact in fp16
     X = WL.random_activations(128, K, seed=13, sigma=1.0)
-    s_g, loss_g, best_g = awq.search_scale(dev(W), dev(X), [0.0], bits=4)
+    s_g, loss_g, best_g = awq.search_scale(dev(W), dev(X), [0.0], bits=4, fused=FUSED)
     torch.cuda.synchronize()
     _, loss_r, _ = O.search_scale(W, X, [0.0], 4)
     q, d, z = O.quantize(W, None, 4)
     assert np.all(d.astype(np.float64) == D) and np.all(z == 7)   # the stated grid
     assert abs(float(host(loss_g)[0]) - loss_r[0]) <= 1e-3 * loss_r[0], (host(loss_g), loss_r)
+
+
+@pytest.mark.parametrize("bits,zero_point,group_size", [(4, True, 128), (3, False, 64)])
+def test_fused_and_buffered_paths_agree(gpu, bits, zero_point, group_size):
+    """The two loss paths form the same fp16 differences and sum the same
+    products in different blocks: equal choice, losses within fp64 summation
+    order.  T = 300 spans two 256-row blocks of the fused kernel, the last one
+    ragged; N = 200 leaves a partial 128-row block."""
+    import torch
+    if FUSED:
+        pytest.skip("compares the two paths itself")
+    W = WL.random_weights(200, 768, seed=101)
+    W[:, :3] *= 15
+    X = WL.random_activations(300, 768, seed=102, sigma=1.5)
+    alphas = [i / 8 for i in range(8)]
+    out = []
+    for fused in (False, True):
+        s, loss, best = awq.search_scale(dev(W), dev(X), alphas, bits=bits, group_size=group_size,
+                                         zero_point=zero_point, fused=fused)
+        torch.cuda.synchronize()
+        out.append((host(s), host(loss).astype(np.float64), int(host(best)[0])))
+    (s0, l0, b0), (s1, l1, b1) = out
+    assert b0 == b1 and np.array_equal(s0, s1)
+    assert np.allclose(l0, l1, rtol=1e-6, atol=0), (l0, l1)
+    check_search(W, X, alphas, bits, zero_point, group_size)

@@ -28,6 +28,7 @@ SIGNATURES = [
                                    _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     ("awq_scale_activations", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_void_p]),
     ("awq_search_workspace_bytes", _c_size_t, [_c_int, _c_int, _c_int, _c_int]),
+    ("awq_search_workspace_bytes_fused", _c_size_t, [_c_int, _c_int, _c_int, _c_int]),
     ("awq_search_scale", _c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_int,
                                   _c_int, _c_int, _c_int, _c_void_p, _c_void_p, _c_void_p,
                                   _c_void_p, _c_size_t, _c_void_p]),
@@ -195,13 +196,19 @@ def scale_activations(x, s, out=None):
     return out
 
 
-def search_workspace_bytes(T: int, N: int, K: int, n_alpha: int) -> int:
-    return int(load_library().awq_search_workspace_bytes(T, N, K, n_alpha))
+def search_workspace_bytes(T: int, N: int, K: int, n_alpha: int, fused: bool = False) -> int:
+    """Workspace of the default search path, or (fused=True) the far smaller
+    one with which the search takes its fused loss kernel."""
+    lib = load_library()
+    f = lib.awq_search_workspace_bytes_fused if fused else lib.awq_search_workspace_bytes
+    return int(f(T, N, K, n_alpha))
 
 
 def search_scale(W, X_cal, alphas, bits: int = 4, group_size: int = GROUP_SIZE,
-                 zero_point: bool = True, workspace=None):
-    """AWQ alpha-grid search.  Returns (s fp32 [K], loss fp32 [n_alpha], best int32 [1])."""
+                 zero_point: bool = True, workspace=None, fused: bool = False):
+    """AWQ alpha-grid search.  Returns (s fp32 [K], loss fp32 [n_alpha], best int32 [1]).
+    The path follows the workspace size (awq_search_workspace_bytes[_fused]);
+    without a workspace, fused=True allocates the small one of the fused path."""
     torch = _torch()
     lib = load_library()
     N, K = W.shape
@@ -210,7 +217,7 @@ def search_scale(W, X_cal, alphas, bits: int = 4, group_size: int = GROUP_SIZE,
     _need(X_cal, torch.float16, (T, K), "X_cal")
     a = (ctypes.c_float * len(alphas))(*[float(v) for v in alphas])
     n_alpha = len(alphas)
-    need = int(lib.awq_search_workspace_bytes(T, N, K, n_alpha))
+    need = search_workspace_bytes(T, N, K, n_alpha, fused)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=W.device)
     s_out = torch.empty(K, dtype=torch.float32, device=W.device)
@@ -234,10 +241,11 @@ def _need_layer(qweight, scales, zeros, N, K, bits, group_size, what=""):
 
 
 def search_scale_shared(Ws, X_cal, alphas, bits: int = 4, group_size: int = GROUP_SIZE,
-                        zero_point: bool = True, workspace=None):
+                        zero_point: bool = True, workspace=None, fused: bool = False):
     """One s for several layers reading X_cal (awq_search_scale_shared): the
     layers' rows together form the searched layer.  Returns (s fp32 [K],
-    losses fp32 [n_alpha], best int32 [1]) as search_scale."""
+    losses fp32 [n_alpha], best int32 [1]) as search_scale (workspace and
+    fused as there)."""
     torch = _torch()
     lib = load_library()
     Ws = list(Ws)
@@ -252,7 +260,7 @@ def search_scale_shared(Ws, X_cal, alphas, bits: int = 4, group_size: int = GROU
     Ns = (ctypes.c_int * n)(*[int(W.shape[0]) for W in Ws])
     a = (ctypes.c_float * len(alphas))(*[float(v) for v in alphas])
     n_alpha = len(alphas)
-    need = int(lib.awq_search_workspace_bytes(T, sum(Ns), K, n_alpha))
+    need = search_workspace_bytes(T, sum(Ns), K, n_alpha, fused)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=X_cal.device)
     s_out = torch.empty(K, dtype=torch.float32, device=X_cal.device)

@@ -103,8 +103,23 @@ int awq_scale_activations(const void* x, const float* s, void* x_out, int M, int
 
 size_t awq_search_workspace_bytes(int T, int N, int K, int n_alpha) {
     if (T <= 0 || N <= 0 || K <= 0 || n_alpha <= 0) return 0;
-    return awq::search_workspace_bytes(T, N, K, n_alpha);
+    return awq::search_workspace_bytes(T, N, K, n_alpha, false);
 }
+
+size_t awq_search_workspace_bytes_fused(int T, int N, int K, int n_alpha) {
+    if (T <= 0 || N <= 0 || K <= 0 || n_alpha <= 0) return 0;
+    return awq::search_workspace_bytes(T, N, K, n_alpha, true);
+}
+
+namespace {
+// the search path a workspace of this size takes: 0 = D buffered (the
+// default), 1 = fused loss, -1 = too small for either
+int search_path(int T, int N, int K, int n_alpha, size_t workspace_bytes) {
+    if (workspace_bytes >= awq::search_workspace_bytes(T, N, K, n_alpha, false)) return 0;
+    if (workspace_bytes >= awq::search_workspace_bytes(T, N, K, n_alpha, true)) return 1;
+    return -1;
+}
+}  // namespace
 
 int awq_search_scale(const void* W, const void* X_cal, int T, int N, int K, const float* alphas,
                      int n_alpha, int bits, int group_size, int zero_point, float* s_out,
@@ -120,10 +135,11 @@ int awq_search_scale(const void* W, const void* X_cal, int T, int N, int K, cons
     if ((st = check_ptrs({W, X_cal, s_out, workspace}))) return st;
     if (loss_out != nullptr && (st = check_ptr(loss_out))) return st;
     if (best_out != nullptr && (st = check_ptr(best_out))) return st;
-    if (workspace_bytes < awq::search_workspace_bytes(T, N, K, n_alpha)) return AWQ_ERR_WORKSPACE;
+    const int path = search_path(T, N, K, n_alpha, workspace_bytes);
+    if (path < 0) return AWQ_ERR_WORKSPACE;
     return hip_status(awq::launch_search(&W, &N, 1, X_cal, T, K, alphas, n_alpha, bits, group_size,
                                          zero_point, s_out, loss_out, best_out, workspace,
-                                         (hipStream_t)stream));
+                                         path == 1, (hipStream_t)stream));
 }
 
 int awq_search_scale_shared(const void* const* Ws, const int* Ns, int n_layers, const void* X_cal,
@@ -150,10 +166,11 @@ int awq_search_scale_shared(const void* const* Ws, const int* Ns, int n_layers, 
         if ((st = check_ptr(Ws[l]))) return st;
     if (loss_out != nullptr && (st = check_ptr(loss_out))) return st;
     if (best_out != nullptr && (st = check_ptr(best_out))) return st;
-    if (workspace_bytes < awq::search_workspace_bytes(T, (int)N, K, n_alpha)) return AWQ_ERR_WORKSPACE;
+    const int path = search_path(T, (int)N, K, n_alpha, workspace_bytes);
+    if (path < 0) return AWQ_ERR_WORKSPACE;
     return hip_status(awq::launch_search(Ws, Ns, n_layers, X_cal, T, K, alphas, n_alpha, bits,
                                          group_size, zero_point, s_out, loss_out, best_out,
-                                         workspace, (hipStream_t)stream));
+                                         workspace, path == 1, (hipStream_t)stream));
 }
 
 namespace {

@@ -118,6 +118,13 @@ __device__ __forceinline__ uint32_t quant_code(float v, const GroupParams& p) {
     return (uint32_t)c;
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void global_void_t;
+
+// s_waitcnt immediate (gfx9): wait until at most n vector-memory ops are
+// outstanding, no wait on lgkm/exp counters
+constexpr unsigned vmcnt_imm(unsigned n) { return (n & 15u) | ((n >> 4) << 14) | (7u << 4) | (15u << 8); }
+
 // The codes of NV values of one group, each equal to quant_code's, in
 // bits 16..19 of T[i] (bits 20..23 zero), decided without a division or a
 // rounding instruction.  One fma forms t = v * (1/D) + (z + 128.5 + 3 * 2^-16),
@@ -185,7 +192,8 @@ size_t gemm_splitk_workspace_bytes(int M, int N, int K);
 int launch_gemm_splitk(const void* x, const void* qweight, const void* scales, const void* zeros,
                        void* y, int M, int N, int K, int bits, int group_size, void* workspace,
                        hipStream_t st);
-size_t search_workspace_bytes(int T, int N, int K, int n_alpha);
+// fused: the workspace of the fused loss kernel (no D buffer), else the default
+size_t search_workspace_bytes(int T, int N, int K, int n_alpha, bool fused);
 size_t loss_gemm_tiles(int T, int N);
 int launch_loss_gemm(const void* X, const void* D, int T, int N, int K, int n_batch,
                      double* partials, hipStream_t st);
@@ -195,6 +203,7 @@ constexpr int kMaxSearchLayers = 8;
 // the layers' rows in order form the N = sum Ns rows of the search
 int launch_search(const void* const* Ws, const int* Ns, int n_layers, const void* X_cal, int T, int K,
                   const float* alphas, int n_alpha, int bits, int group_size, int zero_point,
-                  float* s_out, float* loss_out, int* best_out, void* workspace, hipStream_t st);
+                  float* s_out, float* loss_out, int* best_out, void* workspace, bool fused,
+                  hipStream_t st);
 
 }  // namespace awq

@@ -153,12 +153,6 @@ __global__ __launch_bounds__(256) void k_loss_gemm(
     }
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void global_void_t;
-
-// s_waitcnt immediate (gfx9): wait until at most n vector-memory ops are
-// outstanding, no wait on lgkm/exp counters
-constexpr unsigned vmcnt_imm(unsigned n) { return (n & 15u) | ((n >> 4) << 14) | (7u << 4) | (15u << 8); }
 
 // The 16-byte chunk position that holds global chunk kc of A row r in LDS is
 // kc ^ a_swz(r).  An A-fragment read has lane (j, hq) fetch chunk 4 hq + s of

@@ -34,18 +34,28 @@ struct LayerList {
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// The loss runs one of two ways: a separate error kernel writing D for every
+// alpha into the workspace plus a dense loss GEMM (the default: fastest, needs
+// n_alpha * N * K * 2 bytes), or one fused kernel forming D in registers (a
+// workspace of under a megabyte; MI355X, 4096 x 4096, T = 512, 20 alphas:
+// 0.85 ms against 0.81 ms, since forming D there does not overlap its MFMAs).
+constexpr int kFusedT = 256;            // calibration rows per workgroup of the fused loss
+size_t fused_tiles(int T, int N) {
+    return (size_t)((N + 127) / 128) * (size_t)((T + kFusedT - 1) / kFusedT);
+}
+
 struct Layout {
     size_t sx, sall, sinv, D, part, total;
 };
 
-Layout layout(int T, int N, int K, int n_alpha) {
+Layout layout(int T, int N, int K, int n_alpha, bool fused) {
     Layout L;
     size_t off = 0;
     L.sx = off;   off += align256((size_t)K * sizeof(float));
     L.sall = off; off += align256((size_t)n_alpha * K * sizeof(float));
     L.sinv = off; off += align256((size_t)n_alpha * K * sizeof(float));
-    L.D = off;    off += align256((size_t)n_alpha * N * K * sizeof(_Float16));
-    L.part = off; off += align256((size_t)n_alpha * loss_gemm_tiles(T, N) * sizeof(double));
+    L.D = off;    off += fused ? 0 : align256((size_t)n_alpha * N * K * sizeof(_Float16));
+    L.part = off; off += align256((size_t)n_alpha * (fused ? fused_tiles(T, N) : loss_gemm_tiles(T, N)) * sizeof(double));
     L.total = off;
     return L;
 }
@@ -159,6 +169,240 @@ __global__ __launch_bounds__(256) void k_quant_err(LayerList layers,
     }
 }
 
+// Fused loss (the error matrix D_alpha = W - w_hat_alpha / s_alpha never goes
+// to memory): L_alpha * T * N = sum over (t, n) of (X D_alpha^T)[t][n]^2.  A
+// workgroup owns 128 rows of W (32 per wave, two 16-row MFMA B tiles) and up
+// to 512 calibration rows for one alpha, so every D value is formed once per
+// alpha: each wave builds its D fragments in registers in the B-operand layout
+// of v_mfma_f32_16x16x32_f16 (lane (j, q) holds row j's k = 32 s + 8 q + e of
+// substep s), quantizing the group from W, s and 1/s with the codes of
+// quant_codes_b2, exactly as the separate error kernel does.  X streams
+// through LDS in 64-k steps (256 rows x 128 B, two buffers, direct-to-LDS
+// loads, chunk p of row r holding global chunk p ^ (r & 7), which the
+// A-fragment reads see free of bank conflicts on MI355X); W, s and 1/s of the
+// next group are loaded into registers one group ahead.  The 64 x 2 MFMA
+// accumulators of a lane (128 fp32) live in AGPRs.  The epilogue squares and
+// sums the outputs of rows < T and columns < N in fp32 per lane, then in fp64
+// in a fixed order, into one partial per workgroup.
+namespace lf {
+constexpr int kT = kFusedT;             // calibration rows per workgroup
+constexpr int kFR = kT / 16;            // X fragments per substep
+constexpr int kStepK = 64;              // k per LDS step (half a group)
+constexpr int kRow = kStepK * 2;        // bytes of one X row in LDS
+constexpr int kBuf = kT * kRow;         // 32 KB per buffer
+constexpr int kXLoads = kBuf / 1024 / 4;   // direct-to-LDS loads per wave and step (8)
+constexpr int kWLoads = 2 * 4;             // W loads per wave and group
+}
+
+struct RowList {                        // rows of the layers searched together
+    const _Float16* w[kMaxSearchLayers];
+    int nstart[kMaxSearchLayers];
+    int n;
+};
+
+template <int Q, bool ZP, int GS>
+__global__ __launch_bounds__(256, 1) void k_loss_fused(RowList layers, const _Float16* __restrict__ X,
+                                                       int T, int N, int K,
+                                                       const float* __restrict__ s_all,
+                                                       const float* __restrict__ s_inv,
+                                                       double* __restrict__ partials) {
+    static_assert(GS == 128 || GS == 64, "128- or 64-wide groups");
+    extern __shared__ __attribute__((aligned(16))) unsigned char Xs[];   // 2 x lf::kBuf
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15, hq = lane >> 4;
+    const int alpha = blockIdx.z;
+    const int t0 = blockIdx.y * lf::kT;
+    const int G = K / kGroup;
+    const int n_base = blockIdx.x * 128 + wave * 32;
+
+    // this lane's W row in each of its two tiles (rows past N: row N - 1, never summed)
+    const _Float16* wrow[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int n = min(n_base + 16 * c + j, N - 1);
+        int l = 0;
+#pragma unroll
+        for (int m = 1; m < kMaxSearchLayers; ++m)
+            if (m < layers.n && n >= layers.nstart[m]) l = m;
+        wrow[c] = layers.w[l] + (size_t)(n - layers.nstart[l]) * K;
+    }
+    const float* s_a = s_all + (size_t)alpha * K + 8 * hq;
+    const float* r_a = s_inv + (size_t)alpha * K + 8 * hq;
+
+    // X: load q (0..kXLoads-1) of this wave writes rows 8 (kXLoads wave + q) .. + 7
+    // of the tile, lane l row + (l >> 3), LDS chunk l & 7; rows past T read row T - 1
+    uint32_t x_off[lf::kXLoads];
+#pragma unroll
+    for (int q = 0; q < lf::kXLoads; ++q) {
+        const int rr = 8 * (lf::kXLoads * wave + q) + (lane >> 3);
+        const int row = min(t0 + rr, T - 1);
+        const int kc = (lane & 7) ^ (rr & 7);
+        x_off[q] = (uint32_t)row * (uint32_t)K + 8u * (uint32_t)kc;
+    }
+    auto issue_x = [&](int step, int buf) {
+        const uint32_t k0 = (uint32_t)min(step, 2 * G - 1) * lf::kStepK;
+#pragma unroll
+        for (int q = 0; q < lf::kXLoads; ++q)
+            __builtin_amdgcn_global_load_lds((global_void_t*)(X + x_off[q] + k0),
+                                             (lds_void_t*)(Xs + buf * lf::kBuf + (lf::kXLoads * wave + q) * 1024),
+                                             16, 0, 0);
+    };
+
+    // the next group's W rows (loaded one group ahead) and its s and 1/s
+    // (loaded during the second half of the group before): value i = 8 sub + e
+    // of a lane is k = 32 sub + 8 q + e of the group
+    struct PreW { uint4 w[2][4]; };
+    struct PreS { float4 s[8], r[8]; };
+    auto issue_w = [&](int g, PreW& p) {
+        const int k0 = kGroup * min(g, G - 1);
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int sub = 0; sub < 4; ++sub)
+                p.w[c][sub] = *reinterpret_cast<const uint4*>(wrow[c] + k0 + 32 * sub + 8 * hq);
+    };
+    auto issue_s = [&](int g, PreS& p) {
+        const int k0 = kGroup * min(g, G - 1);
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) {
+            p.s[2 * sub] = *reinterpret_cast<const float4*>(s_a + k0 + 32 * sub);
+            p.s[2 * sub + 1] = *reinterpret_cast<const float4*>(s_a + k0 + 32 * sub + 4);
+        }
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub) {
+            p.r[2 * sub] = *reinterpret_cast<const float4*>(r_a + k0 + 32 * sub);
+            p.r[2 * sub + 1] = *reinterpret_cast<const float4*>(r_a + k0 + 32 * sub + 4);
+        }
+    };
+    auto f4 = [](const float4& q, int e) { return e == 0 ? q.x : e == 1 ? q.y : e == 2 ? q.z : q.w; };
+    auto wval = [](const uint4& raw, int e) {
+        return (float)reinterpret_cast<const _Float16*>(&raw)[e];
+    };
+
+    half8_t dfr[2][4];                   // D fragments of the current group: [tile][substep]
+    auto make_d = [&](const PreW& pw, const PreS& ps) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            float v[32];
+#pragma unroll
+            for (int i = 0; i < 32; ++i) v[i] = wval(pw.w[c][i / 8], i % 8) * f4(ps.s[i / 4], i % 4);
+            constexpr int NV = GS / 4;       // values of one group in a lane
+#pragma unroll
+            for (int gg = 0; gg < 32 / NV; ++gg) {
+                float mn = v[NV * gg], mx = v[NV * gg];
+#pragma unroll
+                for (int i = 1; i < NV; ++i) { mn = fminf(mn, v[NV * gg + i]); mx = fmaxf(mx, v[NV * gg + i]); }
+                // the group's other values sit in the lanes of the same row j
+                mn = fminf(mn, __shfl_xor(mn, 16)); mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mn = fminf(mn, __shfl_xor(mn, 32)); mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const GroupParams gp = group_params<Q, ZP>(mn, mx);
+                uint32_t Tc[NV];
+                quant_codes_b2<Q, NV>(v + NV * gg, gp, Tc);
+                const float zd = -(gp.zero * gp.delta);     // exact: z <= 16, Delta an fp16 value
+#pragma unroll
+                for (int i = 0; i < NV; ++i) {
+                    const int idx = NV * gg + i;
+                    const float q = (float)((Tc[i] >> 16) & 0xFFu);
+                    const float w_hat = __builtin_fmaf(q, gp.delta, zd);   // (q - z) * Delta, exact
+                    const float w = wval(pw.w[c][idx / 8], idx % 8);
+                    dfr[c][idx / 8][idx % 8] = (_Float16)(w - w_hat * f4(ps.r[idx / 4], idx % 4));
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);   // one tile's temporaries at a time
+        }
+    };
+
+    float4_t acc[lf::kFR][2];          // [X fragment][tile]
+#pragma unroll
+    for (int i = 0; i < lf::kFR; ++i) acc[i][0] = acc[i][1] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+    // the two substeps of one LDS step (half h of the group): X fragments in
+    // batches of 8, batch b + 1 read under batch b's 16 MFMAs (a scheduling
+    // barrier per batch keeps the compiler from hoisting every read)
+    constexpr int kB = 8, kNB = 2 * lf::kFR / kB;          // batches per LDS step
+    auto read_batch = [&](const unsigned char* buf, int b, half8_t* xf) {
+        const int sub = b / (lf::kFR / kB), i0 = (b % (lf::kFR / kB)) * kB;
+        const int kc = 4 * sub + hq;
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
+            const int r = 16 * (i0 + u) + j;
+            xf[u] = *reinterpret_cast<const half8_t*>(buf + r * lf::kRow + ((kc ^ (r & 7)) << 4));
+        }
+    };
+    auto compute_half = [&](int h, const unsigned char* buf) {
+        half8_t xa[kB], xb[kB];
+        read_batch(buf, 0, xa);
+#pragma unroll
+        for (int b = 0; b < kNB; ++b) {
+            half8_t* cur = (b & 1) ? xb : xa;
+            half8_t* nxt = (b & 1) ? xa : xb;
+            if (b + 1 < kNB) read_batch(buf, b + 1, nxt);
+            const int sub = b / (lf::kFR / kB), i0 = (b % (lf::kFR / kB)) * kB;
+#pragma unroll
+            for (int u = 0; u < kB; ++u) {
+                acc[i0 + u][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dfr[0][2 * h + sub], cur[u], acc[i0 + u][0], 0, 0, 0);
+                acc[i0 + u][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dfr[1][2 * h + sub], cur[u], acc[i0 + u][1], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    PreW pw;
+    PreS ps;
+    issue_x(0, 0);
+    issue_w(0, pw);
+    issue_s(0, ps);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    for (int g = 0; g < G; ++g) {
+        // step 2g, buffer 0: X(2g) and the group's W, s, 1/s have landed
+        __builtin_amdgcn_sched_barrier(0);
+        issue_x(2 * g + 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        make_d(pw, ps);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_w(g + 1, pw);                  // clamped past the last group: a uniform load stream
+        __builtin_amdgcn_sched_barrier(0);
+        compute_half(0, Xs);
+        // step 2g + 1, buffer 1: X(2g + 1) has landed once at most the next
+        // group's W loads are outstanding; every wave is done with buffer 0
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(lf::kWLoads));
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        issue_x(2 * g + 2, 0);
+        issue_s(g + 1, ps);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_half(1, Xs + lf::kBuf);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+
+    float sq = 0.0f;
+#pragma unroll
+    for (int i = 0; i < lf::kFR; ++i) {
+        const bool t_ok = t0 + 16 * i + j < T;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool ok = t_ok && n_base + 16 * c + 4 * hq + r < N;
+                sq = __builtin_fmaf(ok ? acc[i][c][r] : 0.0f, ok ? acc[i][c][r] : 0.0f, sq);
+            }
+    }
+    double dsq = (double)sq;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) dsq += __shfl_xor(dsq, off);
+    __shared__ double wsum[4];
+    if (lane == 0) wsum[wave] = dsq;
+    __syncthreads();
+    if (tid == 0) {
+        const size_t tile = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
+        const size_t n_tiles = (size_t)gridDim.x * gridDim.y;
+        partials[(size_t)alpha * n_tiles + tile] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+    }
+}
+
 // One workgroup: fixed-order fp64 sums of the loss partials, first argmin.
 // Wave w sums the partials of alphas w, w + 4, ...: lane l adds tiles l, l + 64,
 // ... and the 64 lane sums meet in a fixed butterfly, so the result does not
@@ -195,8 +439,14 @@ __global__ __launch_bounds__(256) void k_select(const double* __restrict__ parti
 
 }  // namespace
 
-size_t search_workspace_bytes(int T, int N, int K, int n_alpha) {
-    return layout(T, N, K, n_alpha).total;
+size_t search_workspace_bytes(int T, int N, int K, int n_alpha, bool fused) {
+    return layout(T, N, K, n_alpha, fused).total;
+}
+
+template <int GS>
+static auto pick_loss_fused(int bits, int zero_point) {
+    return bits == 4 ? (zero_point ? k_loss_fused<15, true, GS> : k_loss_fused<15, false, GS>)
+                     : (zero_point ? k_loss_fused<7, true, GS> : k_loss_fused<7, false, GS>);
 }
 
 template <int GS>
@@ -207,7 +457,8 @@ static auto pick_quant_err(int bits, int zero_point) {
 
 int launch_search(const void* const* Ws, const int* Ns, int n_layers, const void* X_cal, int T, int K,
                   const float* alphas, int n_alpha, int bits, int group_size, int zero_point,
-                  float* s_out, float* loss_out, int* best_out, void* workspace, hipStream_t st) {
+                  float* s_out, float* loss_out, int* best_out, void* workspace, bool fused,
+                  hipStream_t st) {
     LayerList layers{};
     int N = 0;
     for (int l = 0; l < n_layers; ++l) {
@@ -216,7 +467,7 @@ int launch_search(const void* const* Ws, const int* Ns, int n_layers, const void
         N += Ns[l];
     }
     layers.n = n_layers;
-    const Layout L = layout(T, N, K, n_alpha);
+    const Layout L = layout(T, N, K, n_alpha, fused);
     char* ws = static_cast<char*>(workspace);
     float* s_x = reinterpret_cast<float*>(ws + L.sx);
     float* s_all = reinterpret_cast<float*>(ws + L.sall);
@@ -231,16 +482,40 @@ int launch_search(const void* const* Ws, const int* Ns, int n_layers, const void
     const long long nsk = (long long)n_alpha * K;
     hipLaunchKernelGGL(k_candidate_scales, dim3((unsigned)((nsk + 255) / 256)), dim3(256), 0, st,
                        s_x, K, grid, n_alpha, s_all, s_inv);
-    const long long n_chunks = (long long)N * K / 8;
-    auto qerr = group_size == 64 ? pick_quant_err<64>(bits, zero_point)
-                                 : pick_quant_err<128>(bits, zero_point);
-    hipLaunchKernelGGL(qerr, dim3((unsigned)((n_chunks + 255) / 256)), dim3(256), 0, st, layers,
-                       s_all, s_inv, K, n_chunks, n_alpha, (uint4*)D);
-    int err = (int)hipGetLastError();
-    if (err) return err;
-    err = launch_loss_gemm(X_cal, D, T, N, K, n_alpha, part, st);
-    if (err) return err;
-    const int n_tiles = (int)loss_gemm_tiles(T, N);
+    int n_tiles;
+    if (fused) {
+        RowList rows{};
+        int n0 = 0;
+        for (int l = 0; l < n_layers; ++l) {
+            rows.w[l] = static_cast<const _Float16*>(Ws[l]);
+            rows.nstart[l] = n0;
+            n0 += Ns[l];
+        }
+        rows.n = n_layers;
+        auto kern = group_size == 64 ? pick_loss_fused<64>(bits, zero_point)
+                                     : pick_loss_fused<128>(bits, zero_point);
+        const int lds = 2 * lf::kBuf;
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return (int)e;
+        const dim3 grid_f((N + 127) / 128, (T + lf::kT - 1) / lf::kT, n_alpha);
+        hipLaunchKernelGGL(kern, grid_f, dim3(256), lds, st, rows, (const _Float16*)X_cal, T, N, K,
+                           (const float*)s_all, (const float*)s_inv, part);
+        const int err = (int)hipGetLastError();
+        if (err) return err;
+        n_tiles = (int)fused_tiles(T, N);
+    } else {
+        const long long n_chunks = (long long)N * K / 8;
+        auto qerr = group_size == 64 ? pick_quant_err<64>(bits, zero_point)
+                                     : pick_quant_err<128>(bits, zero_point);
+        hipLaunchKernelGGL(qerr, dim3((unsigned)((n_chunks + 255) / 256)), dim3(256), 0, st, layers,
+                           s_all, s_inv, K, n_chunks, n_alpha, (uint4*)D);
+        int err = (int)hipGetLastError();
+        if (err) return err;
+        err = launch_loss_gemm(X_cal, D, T, N, K, n_alpha, part, st);
+        if (err) return err;
+        n_tiles = (int)loss_gemm_tiles(T, N);
+    }
     hipLaunchKernelGGL(k_select, dim3(1), dim3(256), 0, st, part, n_tiles, n_alpha,
                        1.0 / ((double)T * (double)N), s_all, K, s_out, loss_out, best_out);
     return (int)hipGetLastError();
