@@ -482,6 +482,22 @@ def main(argv=None):
             b.record(stream)
             torch.cuda.synchronize()
             search_ms = a.elapsed_time(b) / 5
+            # the fused path (the loss kernel forms W - w_hat / s in registers),
+            # which a workspace of awq_search_workspace_bytes_fused selects
+            wsf = torch.empty(awq.search_workspace_bytes(X.shape[0], W.shape[0], W.shape[1],
+                                                         len(wl5.alphas), fused=True),
+                              dtype=torch.uint8, device=dev)
+            for _ in range(2):
+                awq.search_scale(W, X, wl5.alphas, bits=4, workspace=wsf)
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(5):
+                awq.search_scale(W, X, wl5.alphas, bits=4, workspace=wsf)
+            b.record(stream)
+            torch.cuda.synchronize()
+            search_fused_ms = a.elapsed_time(b) / 5
+            search_ws = (ws.numel(), wsf.numel())
+            del wsf
             a.record(stream)
             for _ in range(20):
                 qp = awq.quantize_pack(W, s, bits=4)
@@ -490,6 +506,8 @@ def main(argv=None):
             qp_us = a.elapsed_time(b) * 1e3 / 20
         qp_bytes = W.numel() * 2 + W.shape[1] * 4 + W.numel() // 2 + 4 * W.numel() // 128
         offline = {"search_4096x4096_T512_20alpha_ms": round(search_ms, 3),
+                   "search_fused_path_ms": round(search_fused_ms, 3),
+                   "search_workspace_bytes": {"default": search_ws[0], "fused": search_ws[1]},
                    "search_loss_gemm_TFLOPs_incl_quant": round(
                        20 * 2.0 * 512 * 4096 * 4096 / (search_ms * 1e-3) / 1e12, 1),
                    "quantize_pack_4096x4096_us": round(qp_us, 2),
