@@ -174,7 +174,7 @@ size_t awq_search_workspace_bytes_fused(int T, int N, int K, int n_alpha);
  *              with w_hat_i the dequantized weights of awq_quantize_pack(W, s_i)
  *              (same bits and zero_point)
  *   best     = smallest i with L_i == min L
- *   W        fp16 [N][K] in;  X_cal fp16 [T][K] in, 1 <= T <= 8192
+ *   W        fp16 [N][K] in;  X_cal fp16 [T][K] in, 1 <= T <= 8192, T * K < 2^31
  *   alphas   HOST fp32 [n_alpha], 1 <= n_alpha <= 64
  *   s_out    fp32 [K] out: s_best
  *   loss_out fp32 [n_alpha] out, or NULL

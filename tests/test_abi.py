@@ -226,6 +226,7 @@ def test_search_validation(lib):
     assert search(lib, T=8193) == UNSUP
     assert search(lib, T=0) == SHAPE
     assert search(lib, K=130) == SHAPE
+    assert search(lib, T=8192, K=262144) == SHAPE      # T * K reaches 2^31
     assert search(lib, W=NUL) == NULL
     assert search(lib, s_out=MIS) == ALIGN
     assert search(lib, loss=MIS) == ALIGN
@@ -260,6 +261,7 @@ def test_search_shared_validation(lib):
     assert shared(lib, Ns=(64, 0, 32)) == SHAPE
     assert shared(lib, Ns=(64, -5, 32)) == SHAPE
     assert shared(lib, K=130) == SHAPE
+    assert shared(lib, T=8192, K=262144) == SHAPE
     assert shared(lib, T=0) == SHAPE
     assert shared(lib, T=8193) == UNSUP
     assert shared(lib, alphas=()) == UNSUP

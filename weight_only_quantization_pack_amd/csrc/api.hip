@@ -131,6 +131,7 @@ int awq_search_scale(const void* W, const void* X_cal, int T, int N, int K, cons
     if (T > kMaxT) return AWQ_ERR_UNSUPPORTED;
     if (T <= 0 || N <= 0) return AWQ_ERR_SHAPE;
     if ((st = check_nk(N, K))) return st;
+    if ((long long)T * K >= (1LL << 31)) return AWQ_ERR_SHAPE;   // 32-bit offsets into X_cal
     if (alphas == nullptr) return AWQ_ERR_NULL;
     if ((st = check_ptrs({W, X_cal, s_out, workspace}))) return st;
     if (loss_out != nullptr && (st = check_ptr(loss_out))) return st;
@@ -159,6 +160,7 @@ int awq_search_scale_shared(const void* const* Ws, const int* Ns, int n_layers, 
     }
     if (T <= 0 || N > (1LL << 30)) return AWQ_ERR_SHAPE;
     if ((st = check_nk((int)N, K))) return st;
+    if ((long long)T * K >= (1LL << 31)) return AWQ_ERR_SHAPE;   // 32-bit offsets into X_cal
     for (int l = 0; l < n_layers; ++l)
         if (Ws[l] == nullptr) return AWQ_ERR_NULL;
     if ((st = check_ptrs({X_cal, s_out, workspace}))) return st;
