@@ -20,10 +20,11 @@
 // A workgroup (4 waves) owns a 128 x 256 output tile; each wave a 128 x 64
 // strip (8 x 4 MFMA blocks, 128 fp32 accumulators per lane), so per k32 step
 // a wave reads 8 A fragments from LDS and dequantizes 4 B fragments for 32
-// MFMAs.  The pipelined kernel also has 128 x 384 and 128 x 448 tiles (6 or
-// 7 blocks per wave, up to 224 accumulators per lane in AGPRs): the same A
-// fragments feed 48 or 56 MFMAs, and the tile count of N = 6144 or 14336
-// becomes a whole number of rounds on 256 CUs.  Tiles are mapped so that each XCD (workgroup id mod 8) walks a
+// MFMAs.  The pipelined kernel also has 128 x 384 and 128 x 448 tiles, and
+// takes a template wave count: 128 x 256 and 128 x 384 run as 8 waves of 2 or
+// 3 column blocks (two waves per SIMD), 128 x 448 as 4 waves of 7 (224
+// accumulators per lane in AGPRs, the same A fragments feeding 56 MFMAs); the
+// tile count of N = 6144 or 14336 becomes a whole number of rounds on 256 CUs.  Tiles are mapped so that each XCD (workgroup id mod 8) walks a
 // contiguous run of row-major tiles and keeps its A rows in its L2.
 //
 // Two schedules of that tile: k_gemm_w4 double-buffers A and B (one K-step
@@ -368,8 +369,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(
 // Split K (part != nullptr): workgroup (tile, blockIdx.y) covers groups
 // [blockIdx.y * gsplit, +gsplit) and writes its fp32 partial tile to
 // part[blockIdx.y][M][N]; k_splitk_reduce adds the splits in order.
-template <int BITS, int GS, int S, int GMT, int NBW>
-__global__ __launch_bounds__(256, 1) void k_gemm_w4p(
+template <int BITS, int GS, int S, int GMT, int NBW, int WV = 4>
+__global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
     const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
     _Float16* __restrict__ Y, float* __restrict__ part, int M, int N, int K, int gsplit) {
@@ -377,7 +378,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     static_assert(GMT == 128 || GMT == 64, "128- or 64-row tiles");
     constexpr int FR = GMT / 16;                       // 16-row A fragments (and row groups per wave)
     constexpr int ABUFT = GMT * ROW_BYTES;             // one A buffer
-    constexpr int TN = 64 * NBW;                       // tile columns: NBW 16-column blocks per wave
+    constexpr int TN = 16 * NBW * WV;                  // tile columns: NBW 16-column blocks per wave
+    constexpr int FRL = 4 * FR / WV;                   // A row groups (4 rows) each wave loads
     extern __shared__ __attribute__((aligned(16))) unsigned char As[];   // S x ABUFT
 
     const int tid = threadIdx.x;
@@ -394,10 +396,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     if (nT % 8 == 0) t = (t % 8) * (nT / 8) + t / 8;
     const int m0 = (t / nTn) * GMT, n0 = (t % nTn) * TN;
 
-    uint32_t a_off[FR];
+    uint32_t a_off[FRL];
 #pragma unroll
-    for (int i = 0; i < FR; ++i) {
-        const int rg = wave * FR + i;
+    for (int i = 0; i < FRL; ++i) {
+        const int rg = wave * FRL + i;
         const int r = 4 * rg + (lane >> 4);
         const int kc = (lane & 15) ^ a_swz(r);
         const int grow = min(m0 + r, M - 1);
@@ -415,7 +417,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     const uint32_t pgrp = GS == 64 ? (uint32_t)(hq >> 1) : 0u;
 
     constexpr int WQ = BITS == 4 ? 4 : 3;              // words per lane slot
-    constexpr int LPS = FR + 3 * NBW;                  // loads per step and wave: A, B tiles, D and z words
+    constexpr int LPS = FRL + 3 * NBW;                 // loads per step and wave: A, B tiles, D and z words
     static_assert(LPS * (S - 2) <= 63, "vmcnt counts to 63");
     struct BStage { uint32_t q[NBW][WQ]; uint32_t d[NBW], z[NBW]; };
     // part p (0..NBW-1) of step kt's loads: the A row groups i with
@@ -424,9 +426,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_w4p(
     auto issue_part = [&](int kt, int slot, BStage& bs, int p) {
         const uint32_t g = (uint32_t)(g_begin + min(kt, NGS - 1));
 #pragma unroll
-        for (int i = 0; i < FR; ++i) {
-            if (i * NBW / FR != p) continue;
-            const int rg = wave * FR + i;
+        for (int i = 0; i < FRL; ++i) {
+            if (i * NBW / FRL != p) continue;
+            const int rg = wave * FRL + i;
             __builtin_amdgcn_global_load_lds((global_void_t*)(x + a_off[i] + g * GK),
                                              (lds_void_t*)(As + slot * ABUFT + rg * 1024), 16, 0, 0);
         }
@@ -647,7 +649,7 @@ int w4p_tiles(int M, int N, int nbw = 4) {
     return ((N + 64 * nbw - 1) / (64 * nbw)) * ((M + rows - 1) / rows);
 }
 
-template <int GMT, int NBW>
+template <int GMT, int NBW, int WV = 4>
 int launch_w4p_rows(const void* x, const void* qweight, const void* scales, const void* zeros,
                     void* y, float* part, int M, int N, int K, int bits, int group_size, int splits,
                     int gsplit, hipStream_t st) {
@@ -655,22 +657,26 @@ int launch_w4p_rows(const void* x, const void* qweight, const void* scales, cons
 #define AWQ_GEMM_S7 3
 #endif
     constexpr int S = NBW >= 7 ? AWQ_GEMM_S7 : kGemmStages;   // NBW = 7: four stages spill
-    const int nT = ((N + 64 * NBW - 1) / (64 * NBW)) * ((M + GMT - 1) / GMT);
+    const int nT = ((N + 16 * NBW * WV - 1) / (16 * NBW * WV)) * ((M + GMT - 1) / GMT);
     const size_t lds = (size_t)S * GMT * w4::ROW_BYTES;
     auto kern = group_size == 64
-                    ? (bits == 4 ? k_gemm_w4p<4, 64, S, GMT, NBW> : k_gemm_w4p<3, 64, S, GMT, NBW>)
-                    : (bits == 4 ? k_gemm_w4p<4, 128, S, GMT, NBW> : k_gemm_w4p<3, 128, S, GMT, NBW>);
+                    ? (bits == 4 ? k_gemm_w4p<4, 64, S, GMT, NBW, WV> : k_gemm_w4p<3, 64, S, GMT, NBW, WV>)
+                    : (bits == 4 ? k_gemm_w4p<4, 128, S, GMT, NBW, WV> : k_gemm_w4p<3, 128, S, GMT, NBW, WV>);
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return (int)e;
-    hipLaunchKernelGGL(kern, dim3(nT, splits), dim3(256), lds, st, (const _Float16*)x,
+    hipLaunchKernelGGL(kern, dim3(nT, splits), dim3(64 * WV), lds, st, (const _Float16*)x,
                        (const uint32_t*)qweight, (const _Float16*)scales, (const _Float16*)zeros,
                        (_Float16*)y, part, M, N, K, gsplit);
     return (int)hipGetLastError();
 }
 
-// nbw: 16-column blocks per wave of the 128-row tiles (4, 6 or 7; see
-// gemm_tile_choice); 64-row tiles always take 4
+// nbw: the 128-row tile's width in 64-column units (4, 6 or 7; see
+// gemm_tile_choice).  256 and 384 columns run as 8 waves of 2 or 3 16-column
+// blocks (two waves per SIMD hide each other's waits: MI355X, M = 2048,
+// 14336x4096 877-886 -> 890-919 TFLOP/s, 4096x6144 919-942 -> 960-986),
+// 448 columns as 4 waves of 7 (8 waves cannot split it).  64-row tiles take
+// 4 waves of 4 blocks.
 int launch_w4p(const void* x, const void* qweight, const void* scales, const void* zeros, void* y,
                float* part, int M, int N, int K, int bits, int group_size, int splits, int gsplit,
                hipStream_t st, int nbw = 4) {
@@ -678,13 +684,13 @@ int launch_w4p(const void* x, const void* qweight, const void* scales, const voi
         return launch_w4p_rows<64, 4>(x, qweight, scales, zeros, y, part, M, N, K, bits, group_size,
                                       splits, gsplit, st);
     if (nbw == 6)
-        return launch_w4p_rows<128, 6>(x, qweight, scales, zeros, y, part, M, N, K, bits, group_size,
-                                       splits, gsplit, st);
+        return launch_w4p_rows<128, 3, 8>(x, qweight, scales, zeros, y, part, M, N, K, bits,
+                                          group_size, splits, gsplit, st);
     if (nbw == 7)
         return launch_w4p_rows<128, 7>(x, qweight, scales, zeros, y, part, M, N, K, bits, group_size,
                                        splits, gsplit, st);
-    return launch_w4p_rows<128, 4>(x, qweight, scales, zeros, y, part, M, N, K, bits, group_size,
-                                   splits, gsplit, st);
+    return launch_w4p_rows<128, 2, 8>(x, qweight, scales, zeros, y, part, M, N, K, bits, group_size,
+                                      splits, gsplit, st);
 }
 
 // The GEMM's kernel and tile for M > 64: 16-column blocks per wave (4, 6 or
