@@ -551,7 +551,7 @@ def main(argv=None):
                               "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4),
                               "traffic": None,
-                              "kernel": "k_gemm_w4p, 128 x 64*NBW tiles: NBW 7 for 4096x14336 (512 tiles), 4 for 14336x4096 (256), 6 for 4096x6144 (256)"}},
+                              "kernel": "k_gemm_w4p: 128 x 448 tiles (4 waves x 7 column blocks) for 4096x14336 (512 tiles), 128 x 256 (8 waves x 2) for 14336x4096 (256), 128 x 384 (8 waves x 3) for 4096x6144 (256)"}},
         "offline": offline,
         "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count,
