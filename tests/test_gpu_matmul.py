@@ -102,6 +102,17 @@ def test_gemv_sliced_two_blocks_per_workgroup(gpu, M):
     check("gemv", M, N, K, 4, seed=31 + M, rows=rows)
 
 
+@pytest.mark.parametrize("M,bits,group_size", [(5, 4, 128), (16, 3, 128), (8, 4, 64)])
+def test_gemv_sliced_wide_layer(gpu, M, bits, group_size):
+    """K sliced on a layer of 1025 row blocks (the 4-wave workgroup form, slices
+    of 8 groups): K = 4736 leaves a ragged last slice of 5 groups, and N = 16393
+    a last block with one valid row."""
+    N, K = 16393, 4736
+    rng = np.random.default_rng(M + bits)
+    rows = np.concatenate([[0, 15, 16, N - 2, N - 1], rng.choice(N, 60, replace=False)])
+    check("gemv", M, N, K, bits, seed=37 + M, rows=rows, group_size=group_size)
+
+
 # ----------------------------------------------------------------------------- 64-wide groups
 @pytest.mark.parametrize("bits", [4, 3])
 @pytest.mark.parametrize("fn,M,N,K", [

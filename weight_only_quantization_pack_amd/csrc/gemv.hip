@@ -665,16 +665,17 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_xs(GemvArgs a
 
 constexpr int kGemvSliceRing = 2;                      // U of k_gemv_xs: slices of 16 groups
 
-template <int BITS, int GS, bool SC, bool FU, int BMAX>
+template <int BITS, int GS, bool SC, bool FU, int WK, int BMAX>
 GemvFn pick_xs_loads(int xl) {
-    if (xl <= 2) return k_gemv_xs<BITS, GS, kGemvWaves, kGemvSliceRing, BMAX, 2, SC, FU>;
-    if (xl <= 4) return k_gemv_xs<BITS, GS, kGemvWaves, kGemvSliceRing, BMAX, 4, SC, FU>;
-    return k_gemv_xs<BITS, GS, kGemvWaves, kGemvSliceRing, BMAX, 8, SC, FU>;
+    if (xl <= 2) return k_gemv_xs<BITS, GS, WK, kGemvSliceRing, BMAX, 2, SC, FU>;
+    if (xl <= 4) return k_gemv_xs<BITS, GS, WK, kGemvSliceRing, BMAX, 4, SC, FU>;
+    return k_gemv_xs<BITS, GS, WK, kGemvSliceRing, BMAX, 8, SC, FU>;
 }
-template <int BITS, int GS, bool SC, bool FU>
+template <int BITS, int GS, bool SC, bool FU, int WK>
 GemvFn pick_xs(int bmax, int xl) {
-    if constexpr (FU) return pick_xs_loads<BITS, GS, SC, FU, 1>(xl);
-    else return bmax <= 1 ? pick_xs_loads<BITS, GS, SC, FU, 1>(xl) : pick_xs_loads<BITS, GS, SC, FU, 2>(xl);
+    if constexpr (FU) return pick_xs_loads<BITS, GS, SC, FU, WK, 1>(xl);
+    else return bmax <= 1 ? pick_xs_loads<BITS, GS, SC, FU, WK, 1>(xl)
+                          : pick_xs_loads<BITS, GS, SC, FU, WK, 2>(xl);
 }
 
 // k_gemv_x1 instance: ring depth (short rows: 2, else 4) and the number of
@@ -699,6 +700,24 @@ int set_lds(GemvFn kern, size_t lds) {
     if (lds <= 64 * 1024) return 0;
     return (int)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
+// the K-sliced kernel with WK waves per workgroup
+template <int BITS, int GS, bool SC, bool FU, int WK>
+int launch_xs(const GemvArgs& a, int cus, hipStream_t st) {
+    const int M = a.M, N = a.N;
+    const int NB = (N + 15) / 16;
+    constexpr int SG = WK * kGemvSliceRing;
+    const size_t red = 2 * (size_t)WK * 64 * 16;
+    const size_t xsl = ((size_t)M * (SG * kGroup + 8) * 2 + 15) & ~(size_t)15;
+    const size_t lds = max(xsl + (SC ? (size_t)SG * kGroup * 4 : 0), red);
+    const int per_cu = max(1, min(kGemvCuWaves / WK, (int)((160 * 1024) / lds)));
+    const int grid = FU ? NB : max(min(NB, cus * per_cu), (NB + 1) / 2);
+    const int bmax = (NB + grid - 1) / grid;
+    auto kern = pick_xs<BITS, GS, SC, FU, WK>(bmax, (kGemvSliceRing * M + 3) / 4);
+    if (int e = set_lds(kern, lds)) return e;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * WK), lds, st, a);
+    return 0;
 }
 
 // SC: inv_s folded into the x staging; FU: a gate/up pair with the SiLU * up output
@@ -726,20 +745,17 @@ int launch_bits(const GemvArgs& a, hipStream_t st) {
         const int grid = min(NB, cus * per_cu);
         hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kGemvWaves), lds, st, a);
     } else {
-        // K in slices of 16 groups; up to 2 row blocks per workgroup (4 per
-        // workgroup reads x half as often but spills at M = 16; measured on
-        // MI355X, 8192x28672 at M = 16: 39.5 us with 2, 41.8 us with 4); a
-        // fused pair is one block of two layers, which reads x as often
-        constexpr int SG = kGemvWaves * kGemvSliceRing;
-        const size_t red = 2 * (size_t)kGemvWaves * 64 * 16;
-        const size_t xsl = ((size_t)M * (SG * kGroup + 8) * 2 + 15) & ~(size_t)15;
-        const size_t lds = max(xsl + (SC ? (size_t)SG * kGroup * 4 : 0), red);
-        const int per_cu = max(1, min(kGemvCuWaves / kGemvWaves, (int)((160 * 1024) / lds)));
-        const int grid = FU ? NB : max(min(NB, cus * per_cu), (NB + 1) / 2);
-        const int bmax = (NB + grid - 1) / grid;
-        auto kern = pick_xs<BITS, GS, SC, FU>(bmax, (kGemvSliceRing * M + 3) / 4);
-        if (int e = set_lds(kern, lds)) return e;
-        hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kGemvWaves), lds, st, a);
+        // K in slices; up to 2 row blocks per workgroup (4 per workgroup reads
+        // x half as often but spills at M = 16; measured on MI355X, 8192x28672
+        // at M = 16: 39.5 us with 2, 41.8 us with 4); a fused pair is one block
+        // of two layers, which reads x as often.  Wide layers (>= 1024 row
+        // blocks) take 4-wave workgroups (slices of 8 groups, twice as many
+        // workgroups per CU): 8192x28672 at M = 4 27.4 -> 24.9 us, M = 16 37.8
+        // -> 36.7 us; narrower ones keep 8 waves (4096x4096 at M = 16: 5.9 vs
+        // 6.0 us)
+        const int e = NB >= 1024 ? launch_xs<BITS, GS, SC, FU, kGemvWaves / 2>(a, cus, st)
+                                 : launch_xs<BITS, GS, SC, FU, kGemvWaves>(a, cus, st);
+        if (e) return e;
     }
     return (int)hipGetLastError();
 }
