@@ -663,7 +663,7 @@ __global__ __launch_bounds__(64 * WK, AWQ_GEMV_MINBLK) void k_gemv_xs(GemvArgs a
     }
 }
 
-constexpr int kGemvSliceRing = 2;                      // U of k_gemv_xs: slices of 16 groups
+constexpr int kGemvSliceRing = 2;                      // U of k_gemv_xs: slices of 2 * WK groups
 
 template <int BITS, int GS, bool SC, bool FU, int WK, int BMAX>
 GemvFn pick_xs_loads(int xl) {
@@ -753,7 +753,7 @@ int launch_bits(const GemvArgs& a, hipStream_t st) {
         // workgroups per CU): 8192x28672 at M = 4 27.4 -> 24.9 us, M = 16 37.8
         // -> 36.7 us; narrower ones keep 8 waves (4096x4096 at M = 16: 5.9 vs
         // 6.0 us)
-        const int e = NB >= 1024 ? launch_xs<BITS, GS, SC, FU, kGemvWaves / 2>(a, cus, st)
+        const int e = NB >= 1024 ? launch_xs<BITS, GS, SC, FU, 4>(a, cus, st)
                                  : launch_xs<BITS, GS, SC, FU, kGemvWaves>(a, cus, st);
         if (e) return e;
     }
