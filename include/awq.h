@@ -146,8 +146,8 @@ int awq_scale_activations(const void* x, const float* s, void* x_out, int M,
 /*
  * awq_search_workspace_bytes -- device workspace of awq_search_scale's
  * default path for T calibration tokens, an N x K layer and n_alpha grid
- * points: it holds W - w_hat_i / s_i for every alpha (n_alpha * N * K fp16)
- * for the loss GEMM.  0 when an argument is <= 0.
+ * points: it holds W - w_hat_i / s_i for every alpha (n_alpha x N rounded up
+ * to a multiple of 16 x K fp16, in the loss GEMM's tiled layout).  0 when an argument is <= 0.
  */
 size_t awq_search_workspace_bytes(int T, int N, int K, int n_alpha);
 

@@ -195,6 +195,10 @@ int launch_gemm_splitk(const void* x, const void* qweight, const void* scales, c
 // fused: the workspace of the fused loss kernel (no D buffer), else the default
 size_t search_workspace_bytes(int T, int N, int K, int n_alpha, bool fused);
 size_t loss_gemm_tiles(int T, int N);
+// rows of one alpha's D in the loss GEMM's tiled layout (N rounded up to 16)
+inline size_t loss_rows(int N) { return (size_t)(N + 15) / 16 * 16; }
+// D: n_batch entries of loss_rows(N) x K fp16 in that layout (written by the
+// search's error kernel)
 int launch_loss_gemm(const void* X, const void* D, int T, int N, int K, int n_batch,
                      double* partials, hipStream_t st);
 // layers searched together (shared input): at most this many

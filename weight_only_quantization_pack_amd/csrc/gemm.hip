@@ -34,8 +34,9 @@
 // current substep's MFMAs.  gemm_tile_choice picks the kernel and tile width
 // from the rounds each option takes on the CUs.
 //
-// Loss GEMM (k_loss_gemm): B = D_alpha = W - w_hat_alpha / s_alpha (fp16,
-// row-major), 128 x 128 tiles through LDS, and the epilogue sums Y^2 per tile
+// Loss GEMM (k_loss_gemm_p): B = D_alpha = W - w_hat_alpha / s_alpha (fp16,
+// in a tiled layout the search's error kernel writes), the pipelined kernel's
+// schedule with fp16 B operands, and an epilogue that sums Y^2 per tile
 // instead of storing Y.
 #include <climits>
 
@@ -58,102 +59,8 @@ namespace {
 #define AWQ_GEMM_ILV 7
 #endif
 
-constexpr int BM = 128, BN = 128, BK = 128;
-constexpr int LDS_STRIDE = BK + 8;          // halves; +16 B per row against bank conflicts
-
 __device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 __device__ __forceinline__ uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
-
-// Loss GEMM of the scale search: partials[z][tile] = sum over the tile of
-// (A . B_z^T)^2, A = X_cal fp16 [M][K], B_z = D_alpha fp16 [N][K] (one batch
-// entry per alpha, b_batch_stride apart).  128 x 128 tiles through LDS, the next
-// K-step's global data loaded during the current step's MFMAs; rows past M or
-// N load as zeros and add nothing.  The tile's sum of squares is reduced in a
-// fixed order (lanes, then the 4 waves in fp64), so it is deterministic.
-__global__ __launch_bounds__(256) void k_loss_gemm(
-    const _Float16* __restrict__ A, const _Float16* __restrict__ B, double* __restrict__ partials,
-    int M, int N, int K, long long b_batch_stride) {
-    __shared__ __attribute__((aligned(16))) _Float16 As[BM * LDS_STRIDE];
-    __shared__ __attribute__((aligned(16))) _Float16 Bs[BN * LDS_STRIDE];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-    const int KT = K / BK;
-    const _Float16* Bh = B + (size_t)blockIdx.z * b_batch_stride;
-
-    // registers for one K-step of global data
-    uint4 ra[8], rb[8];
-    auto load_step = [&](int kt) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int id = tid + 256 * i, r = id >> 4, c = id & 15, m = m0 + r, n = n0 + r;
-            ra[i] = m < M ? *reinterpret_cast<const uint4*>(A + (size_t)m * K + kt * BK + c * 8)
-                          : make_uint4(0, 0, 0, 0);
-            rb[i] = n < N ? *reinterpret_cast<const uint4*>(Bh + (size_t)n * K + kt * BK + c * 8)
-                          : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto store_step = [&]() {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int id = tid + 256 * i, r = id >> 4, c = id & 15;
-            *reinterpret_cast<uint4*>(&As[r * LDS_STRIDE + c * 8]) = ra[i];
-            *reinterpret_cast<uint4*>(&Bs[r * LDS_STRIDE + c * 8]) = rb[i];
-        }
-    };
-
-    float4_t acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = (float4_t){0.f, 0.f, 0.f, 0.f};
-
-    load_step(0);
-    for (int kt = 0; kt < KT; ++kt) {
-        __syncthreads();                       // previous step's reads are done
-        store_step();
-        __syncthreads();
-        if (kt + 1 < KT) load_step(kt + 1);    // in flight during the MFMAs
-#pragma unroll
-        for (int ks = 0; ks < BK / 32; ++ks) {
-            half8_t a[4], b[4];
-            const int kk = ks * 32 + (lane >> 4) * 8;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a[i] = *reinterpret_cast<const half8_t*>(&As[(wm * 64 + i * 16 + (lane & 15)) * LDS_STRIDE + kk]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                b[j] = *reinterpret_cast<const half8_t*>(&Bs[(wn * 64 + j * 16 + (lane & 15)) * LDS_STRIDE + kk]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
-    }
-
-    float sq = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sq = __builtin_fmaf(acc[i][j][r], acc[i][j][r], sq);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
-    __shared__ double wsum[4];
-    if (lane == 0) wsum[wave] = (double)sq;
-    __syncthreads();
-    if (tid == 0) {
-        const size_t tile = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
-        const size_t n_tiles = (size_t)gridDim.x * gridDim.y;
-        partials[(size_t)blockIdx.z * n_tiles + tile] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
-    }
-}
-
 
 // The 16-byte chunk position that holds global chunk kc of A row r in LDS is
 // kc ^ a_swz(r).  An A-fragment read has lane (j, hq) fetch chunk 4 hq + s of
@@ -614,6 +521,162 @@ __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
     }
 }
 
+// Loss GEMM of the scale search: partials[z][tile] = sum over the tile's
+// valid entries of (X . D_z^T)^2, X = X_cal fp16 [M][K], D_z = W - w_hat_z / s_z
+// (one batch entry per alpha, b_batch_stride halves apart) in the tiled layout
+// the search's error kernel writes: 16-row x 128-column tiles, each k32 step
+// of a tile one contiguous 1 KB run in MFMA operand order (lane 16 hq + j:
+// row j, columns 32 q + 8 hq .. + 7).  The prefill kernel's schedule with an
+// fp16 B: X goes to LDS by direct-to-LDS loads (the swizzled 128-row buffers,
+// S stages of one 128-wide K-step) and each wave streams its NBW D blocks
+// straight into registers, four 1 KB wave loads per block and K-step (read
+// row-major, D's 256-byte row pieces 8 KB apart cost ~13 % more time).  Rows
+// past M or N load clamped rows (or the padding rows of the last block) and
+// are left out of the sum, which is formed in a fixed order (lanes in fp32,
+// then the waves in fp64).  Tiles are numbered column-major, so the XCD that
+// runs eight consecutive tiles shares each D tile between the row tiles in
+// its L2.
+template <int S, int NBW, int WV>
+__global__ __launch_bounds__(64 * WV, 1) void k_loss_gemm_p(
+    const _Float16* __restrict__ x, const _Float16* __restrict__ D, double* __restrict__ partials,
+    int M, int N, int K, long long b_batch_stride) {
+    using namespace w4;
+    constexpr int GMT = 128, FR = GMT / 16;
+    constexpr int ABUFT = GMT * ROW_BYTES;             // one X buffer (32 KB)
+    constexpr int TN = 16 * NBW * WV;
+    constexpr int FRL = 4 * FR / WV;                   // X row groups (4 rows) each wave loads
+    constexpr int LPS = FRL + 4 * NBW;                 // loads per step and wave
+    static_assert(LPS * (S - 2) <= 63, "vmcnt counts to 63");
+    extern __shared__ __attribute__((aligned(16))) unsigned char As[];   // S x ABUFT
+    __shared__ double wsum[WV];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15, hq = lane >> 4;
+    const int G = K / kGroup;
+    const int nTn = (N + TN - 1) / TN, nTm = (M + GMT - 1) / GMT;
+    const int nT = nTn * nTm;
+    int t = blockIdx.x;
+    if (nT % 8 == 0) t = (t % 8) * (nT / 8) + t / 8;
+    const int m0 = (t % nTm) * GMT, n0 = (t / nTm) * TN;
+    const _Float16* Dz = D + (size_t)blockIdx.y * (size_t)b_batch_stride;
+
+    uint32_t a_off[FRL];
+#pragma unroll
+    for (int i = 0; i < FRL; ++i) {
+        const int rg = wave * FRL + i;
+        const int r = 4 * rg + (lane >> 4);
+        const int kc = (lane & 15) ^ a_swz(r);
+        a_off[i] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + 8u * kc;
+    }
+    // D block blk, group g: the tile at (blk G + g) 2048 halves, k32 step q at
+    // + 512 q, lane 16 hq + j at + 8 lane (row j, columns 32 q + 8 hq ..)
+    const _Float16* brow[NBW];
+    const int NB16 = (N + 15) / 16;
+#pragma unroll
+    for (int c = 0; c < NBW; ++c) {
+        const int blk = min(n0 / 16 + wave * NBW + c, NB16 - 1);
+        brow[c] = Dz + (size_t)blk * G * 2048 + lane * 8;
+    }
+
+    struct BStage { half8_t b[NBW][4]; };
+    auto issue = [&](int kt, int slot, BStage& bs) {
+        const uint32_t g = (uint32_t)min(kt, G - 1);
+#pragma unroll
+        for (int i = 0; i < FRL; ++i) {
+            const int rg = wave * FRL + i;
+            __builtin_amdgcn_global_load_lds((global_void_t*)(x + a_off[i] + g * GK),
+                                             (lds_void_t*)(As + slot * ABUFT + rg * 1024), 16, 0, 0);
+        }
+#pragma unroll
+        for (int c = 0; c < NBW; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                bs.b[c][q] = *reinterpret_cast<const half8_t*>(brow[c] + g * 2048 + 512 * q);
+    };
+
+    float4_t acc[FR][NBW];
+#pragma unroll
+    for (int i = 0; i < FR; ++i)
+#pragma unroll
+        for (int c = 0; c < NBW; ++c) acc[i][c] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const BStage& bs, const unsigned char* abuf) {
+        auto read_a = [&](int q, half8_t* a) {
+            const int kc = 4 * q + hq;
+#pragma unroll
+            for (int i = 0; i < FR; ++i) {
+                const int r = 16 * i + j;
+                a[i] = *reinterpret_cast<const half8_t*>(abuf + r * ROW_BYTES + ((kc ^ a_swz(r)) << 4));
+            }
+        };
+        half8_t a_cur[FR];
+        read_a(0, a_cur);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            half8_t a_nxt[FR];
+            if (q < 3) read_a(q + 1, a_nxt);
+#pragma unroll
+            for (int i = 0; i < FR; ++i)
+#pragma unroll
+                for (int c = 0; c < NBW; ++c)
+                    acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bs.b[c][q], a_cur[i], acc[i][c], 0, 0, 0);
+            if (q < 3) {
+#pragma unroll
+                for (int i = 0; i < FR; ++i) a_cur[i] = a_nxt[i];
+            }
+        }
+    };
+
+    BStage bs[S];
+#pragma unroll
+    for (int st = 0; st < S - 1; ++st) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(st, st, bs[st]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    int kt0 = 0;
+    do {
+#pragma unroll
+        for (int st = 0; st < S; ++st) {
+            const int kt = kt0 + st;
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS * (S - 2)));
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            issue(kt + S - 1, (st + S - 1) % S, bs[(st + S - 1) % S]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt < G) compute(bs[st], As + st * ABUFT);
+        }
+        kt0 += S;
+    } while (kt0 < G);
+
+    // accumulator of lane 16 hq + j, block (i, c): X row m0 + 16 i + j, D row
+    // n0 + 16 (wave NBW + c) + 4 hq + r
+    float sq = 0.0f;
+#pragma unroll
+    for (int i = 0; i < FR; ++i) {
+        const bool mv = m0 + 16 * i + j < M;
+#pragma unroll
+        for (int c = 0; c < NBW; ++c) {
+            const int n = n0 + wave * 16 * NBW + 16 * c + 4 * hq;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (mv && n + r < N) sq = __builtin_fmaf(acc[i][c][r], acc[i][c][r], sq);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
+    if (lane == 0) wsum[wave] = (double)sq;
+    __syncthreads();
+    if (tid == 0) {
+        double tot = wsum[0];
+#pragma unroll
+        for (int w = 1; w < WV; ++w) tot += wsum[w];
+        partials[(size_t)blockIdx.y * nT + blockIdx.x] = tot;
+    }
+}
+
 // y[i] = fp16(sum over s = 0 .. splits-1 of part[s][i]), in that order.
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part,
                                                        _Float16* __restrict__ y, long long mn,
@@ -777,15 +840,27 @@ int launch_gemm(const void* x, const void* qweight, const void* scales, const vo
     return (int)hipGetLastError();
 }
 
+// the loss GEMM's form: 3 stages, 8 waves of 2 D blocks (128 x 256 tiles);
+// MI355X, 4096 x 4096, T = 512, 20 alphas, whole search: 0.73-0.74 ms, 4 waves
+// of 4 blocks 0.74-0.76 ms, the 128 x 128 register-staged kernel it replaced
+// (row-major D) 0.79-0.81 ms
+constexpr int kLossS = 3, kLossNBW = 2, kLossWV = 8;
+constexpr int kLossTN = 16 * kLossNBW * kLossWV;     // D rows per tile
+
 size_t loss_gemm_tiles(int T, int N) {
-    return (size_t)((N + BN - 1) / BN) * (size_t)((T + BM - 1) / BM);
+    return (size_t)((N + kLossTN - 1) / kLossTN) * (size_t)((T + 127) / 128);
 }
 
 int launch_loss_gemm(const void* X, const void* D, int T, int N, int K, int n_batch,
                      double* partials, hipStream_t st) {
-    const dim3 grid((N + BN - 1) / BN, (T + BM - 1) / BM, n_batch), block(256);
-    hipLaunchKernelGGL(k_loss_gemm, grid, block, 0, st, (const _Float16*)X, (const _Float16*)D,
-                       partials, T, N, K, (long long)N * K);
+    auto kern = k_loss_gemm_p<kLossS, kLossNBW, kLossWV>;
+    const size_t lds = (size_t)kLossS * 128 * w4::ROW_BYTES;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return (int)e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)loss_gemm_tiles(T, N), n_batch), dim3(64 * kLossWV), lds, st,
+                       (const _Float16*)X, (const _Float16*)D, partials, T, N, K,
+                       (long long)loss_rows(N) * K);
     return (int)hipGetLastError();
 }
 

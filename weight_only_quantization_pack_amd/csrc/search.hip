@@ -36,9 +36,10 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // The loss runs one of two ways: a separate error kernel writing D for every
 // alpha into the workspace plus a dense loss GEMM (the default: fastest, needs
-// n_alpha * N * K * 2 bytes), or one fused kernel forming D in registers (a
-// workspace of under a megabyte; MI355X, 4096 x 4096, T = 512, 20 alphas:
-// 0.85 ms against 0.81 ms, since forming D there does not overlap its MFMAs).
+// n_alpha * N * K * 2 bytes, N rounded up to 16), or one fused kernel forming D
+// in registers (a workspace of under a megabyte; MI355X, 4096 x 4096, T = 512,
+// 20 alphas: 0.85-0.88 ms against 0.70-0.71 ms, since forming D there does not
+// overlap its MFMAs).
 constexpr int kFusedT = 256;            // calibration rows per workgroup of the fused loss
 size_t fused_tiles(int T, int N) {
     return (size_t)((N + 127) / 128) * (size_t)((T + kFusedT - 1) / kFusedT);
@@ -54,7 +55,7 @@ Layout layout(int T, int N, int K, int n_alpha, bool fused) {
     L.sx = off;   off += align256((size_t)K * sizeof(float));
     L.sall = off; off += align256((size_t)n_alpha * K * sizeof(float));
     L.sinv = off; off += align256((size_t)n_alpha * K * sizeof(float));
-    L.D = off;    off += fused ? 0 : align256((size_t)n_alpha * N * K * sizeof(_Float16));
+    L.D = off;    off += fused ? 0 : align256((size_t)n_alpha * loss_rows(N) * K * sizeof(_Float16));
     L.part = off; off += align256((size_t)n_alpha * (fused ? fused_tiles(T, N) : loss_gemm_tiles(T, N)) * sizeof(double));
     L.total = off;
     return L;
@@ -100,30 +101,42 @@ __global__ __launch_bounds__(256) void k_candidate_scales(const float* __restric
     s_inv[t] = 1.0f / sv;                         // for the loss only (D = W - w_hat * (1/s))
 }
 
-// Quantization error of every alpha: one lane = 8 consecutive weights of one
-// row, GS / 8 lanes = one group (16 for 128-groups, 8 for 64-groups; the error
-// does not depend on the packed format).  W is read once: each lane keeps its
-// 8 weights and walks the alphas, writing D_alpha for each (s_alpha is small
-// and stays in L2), so the traffic is one read of W plus the D writes.  The
-// codes are rint(fp32(v / Delta)) as in awq_quantize_pack, decided in fixed
-// point (quant_codes_b2); w_hat = fma(q, Delta, -z * Delta) is the exact
-// (q - z) * Delta.  D multiplies by the reciprocal of s (within 1.5 fp32 ulp
-// of w_hat / s before D's own fp16 rounding), which spares this VALU-bound
-// loop a division per weight.
+// Quantization error of every alpha.  One workgroup per 16-row x 128-column
+// tile of W (block b, group g of 128 columns), written as one tile of D in
+// the loss GEMM's layout: wave q takes the tile's k32 step q, lane 16 hq + j
+// the 8 weights of row 16 b + j at columns 128 g + 32 q + 8 hq .. + 7, so each
+// wave stores its D step as one contiguous 1 KB run per alpha.  A group's
+// min/max is met over the 4 lanes of a row (hq) and then over the waves
+// holding the group's other steps (all 4 for 128-groups, steps q and q ^ 1 for
+// 64-groups) through LDS, one barrier per alpha.  W is read once: each lane
+// keeps its 8 weights and walks the alphas, writing D_alpha for each (s_alpha
+// is small and stays in L2).  The codes are rint(fp32(v / Delta)) as in
+// awq_quantize_pack, decided in fixed point (quant_codes_b2); w_hat =
+// fma(q, Delta, -z * Delta) is the exact (q - z) * Delta.  D multiplies by
+// the reciprocal of s (within 1.5 fp32 ulp of w_hat / s before D's own fp16
+// rounding), which spares this VALU-bound loop a division per weight.  Rows
+// past N (the last block's padding) load nothing and store nothing.
 template <int Q, bool ZP, int GS>
 __global__ __launch_bounds__(256) void k_quant_err(LayerList layers,
                                                   const float* __restrict__ s_all,
-                                                  const float* __restrict__ s_inv, int K,
-                                                  long long n_chunks, int n_alpha,
+                                                  const float* __restrict__ s_inv, int N, int K,
+                                                  int n_alpha, long long d_stride,
                                                   uint4* __restrict__ D) {
-    const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    const bool active = t < n_chunks;
-    const int k0 = active ? (int)(t % (K / 8)) * 8 : 0;
+    __shared__ float red[2][2][4][16];                 // [alpha parity][min, max][step q][row j]
+    const int G = K / kGroup;
+    const int b = (int)(blockIdx.x / (unsigned)G), g = (int)(blockIdx.x % (unsigned)G);
+    const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int j = lane & 15, hq = lane >> 4;
+    const int n = 16 * b + j;
+    const bool active = n < N;
+    const int k0 = kGroup * g + 32 * q + 8 * hq;
     // this chunk's layer (rows never straddle layers: a layer holds whole rows)
+    const long long t = (long long)n * (K / 8) + k0 / 8;
     const uint4* src = layers.w[0] + t;
 #pragma unroll
     for (int l = 1; l < kMaxSearchLayers; ++l)
         if (l < layers.n && t >= layers.cstart[l]) src = layers.w[l] + (t - layers.cstart[l]);
+    const size_t dpos = ((size_t)blockIdx.x * 4 + q) * 64 + lane;
     float w[8];
     {
         const uint4 raw = active ? *src : make_uint4(0, 0, 0, 0);
@@ -148,10 +161,18 @@ __global__ __launch_bounds__(256) void k_quant_err(LayerList layers,
         float mn = v[0], mx = v[0];
 #pragma unroll
         for (int i = 1; i < 8; ++i) { mn = fminf(mn, v[i]); mx = fmaxf(mx, v[i]); }
+        // the row's 4 lanes of this step (lanes j, j + 16, j + 32, j + 48)
+        mn = fminf(mn, __shfl_xor(mn, 16)); mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mn = fminf(mn, __shfl_xor(mn, 32)); mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // the group's other steps: min and max are exact, so the order is free
+        const int par = alpha & 1;
+        if (hq == 0) { red[par][0][q][j] = mn; red[par][1][q][j] = mx; }
+        __syncthreads();
+        if constexpr (GS == 128) {
 #pragma unroll
-        for (int m = 1; m < GS / 8; m <<= 1) {
-            mn = fminf(mn, __shfl_xor(mn, m, GS / 8));
-            mx = fmaxf(mx, __shfl_xor(mx, m, GS / 8));
+            for (int o = 0; o < 4; ++o) { mn = fminf(mn, red[par][0][o][j]); mx = fmaxf(mx, red[par][1][o][j]); }
+        } else {
+            mn = fminf(mn, red[par][0][q ^ 1][j]); mx = fmaxf(mx, red[par][1][q ^ 1][j]);
         }
         const GroupParams p = group_params<Q, ZP>(mn, mx);
         uint32_t T[8];
@@ -161,11 +182,11 @@ __global__ __launch_bounds__(256) void k_quant_err(LayerList layers,
         _Float16* o = reinterpret_cast<_Float16*>(&out);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float q = (float)((T[i] >> 16) & 0xFFu);
-            const float w_hat = __builtin_fmaf(q, p.delta, zd);  // (q - z) * Delta, exact
+            const float qf = (float)((T[i] >> 16) & 0xFFu);
+            const float w_hat = __builtin_fmaf(qf, p.delta, zd);  // (q - z) * Delta, exact
             o[i] = (_Float16)(w[i] - w_hat * ri[i]);
         }
-        if (active) D[(size_t)alpha * n_chunks + t] = out;
+        if (active) D[(size_t)alpha * d_stride + dpos] = out;
     }
 }
 
@@ -505,11 +526,11 @@ int launch_search(const void* const* Ws, const int* Ns, int n_layers, const void
         if (err) return err;
         n_tiles = (int)fused_tiles(T, N);
     } else {
-        const long long n_chunks = (long long)N * K / 8;
         auto qerr = group_size == 64 ? pick_quant_err<64>(bits, zero_point)
                                      : pick_quant_err<128>(bits, zero_point);
-        hipLaunchKernelGGL(qerr, dim3((unsigned)((n_chunks + 255) / 256)), dim3(256), 0, st, layers,
-                           s_all, s_inv, K, n_chunks, n_alpha, (uint4*)D);
+        const size_t n_tiles16 = loss_rows(N) / 16 * (size_t)(K / kGroup);
+        hipLaunchKernelGGL(qerr, dim3((unsigned)n_tiles16), dim3(256), 0, st, layers, s_all, s_inv, N, K,
+                           n_alpha, (long long)loss_rows(N) * K / 8, (uint4*)D);
         int err = (int)hipGetLastError();
         if (err) return err;
         err = launch_loss_gemm(X_cal, D, T, N, K, n_alpha, part, st);
