@@ -841,9 +841,9 @@ int launch_gemm(const void* x, const void* qweight, const void* scales, const vo
 }
 
 // the loss GEMM's form: 3 stages, 8 waves of 2 D blocks (128 x 256 tiles);
-// MI355X, 4096 x 4096, T = 512, 20 alphas, whole search: 0.73-0.74 ms, 4 waves
-// of 4 blocks 0.74-0.76 ms, the 128 x 128 register-staged kernel it replaced
-// (row-major D) 0.79-0.81 ms
+// MI355X, 4096 x 4096, T = 512, 20 alphas, whole search over three runs: 0.71 ms,
+// 4 stages 0.72 ms, 4 waves of 4 blocks 0.73-0.74 ms (2 or 3 stages); the
+// 128 x 128 register-staged kernel it replaced (row-major D) 0.79-0.81 ms
 constexpr int kLossS = 3, kLossNBW = 2, kLossWV = 8;
 constexpr int kLossTN = 16 * kLossNBW * kLossWV;     // D rows per tile
 
