@@ -113,6 +113,22 @@ def test_gemv_sliced_wide_layer(gpu, M, bits, group_size):
     check("gemv", M, N, K, bits, seed=37 + M, rows=rows, group_size=group_size)
 
 
+@pytest.mark.parametrize("M", [8, 13])
+def test_gemv_sliced_long_rows_two_blocks(gpu, M):
+    """K >= 16384 at M >= 8 with at least two blocks per CU: two row blocks per
+    workgroup.  N = 8200 gives 513 blocks (the last workgroup holds one valid
+    block) and K = 16512 a ragged last slice of one group."""
+    N, K = 8200, 16512
+    key = ("long_rows", N, K)
+    if key not in _CACHE:
+        _CACHE.clear()
+        W = WL.random_weights(N, K, seed=91)
+        _CACHE[key] = (W,) + packed(W, 4)
+    rng = np.random.default_rng(M)
+    rows = np.concatenate([[0, 15, 16, 8191, 8192, N - 1], rng.choice(N, 58, replace=False)])
+    check("gemv", M, N, K, 4, seed=92 + M, rows=rows, layer=_CACHE[key])
+
+
 # ----------------------------------------------------------------------------- 64-wide groups
 @pytest.mark.parametrize("bits", [4, 3])
 @pytest.mark.parametrize("fn,M,N,K", [

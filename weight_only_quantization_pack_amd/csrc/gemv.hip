@@ -712,7 +712,12 @@ int launch_xs(const GemvArgs& a, int cus, hipStream_t st) {
     const size_t xsl = ((size_t)M * (SG * kGroup + 8) * 2 + 15) & ~(size_t)15;
     const size_t lds = max(xsl + (SC ? (size_t)SG * kGroup * 4 : 0), red);
     const int per_cu = max(1, min(kGemvCuWaves / WK, (int)((160 * 1024) / lds)));
-    const int grid = FU ? NB : max(min(NB, cus * per_cu), (NB + 1) / 2);
+    int grid = FU ? NB : max(min(NB, cus * per_cu), (NB + 1) / 2);
+    // long rows at M >= 8: two blocks per workgroup stage x half as often, which
+    // pays once the halved grid still covers every CU (MI355X, 28672x8192 at
+    // M = 8 / 16: 35.4 -> 32.7 / 46.0 -> 38.5 us; K = 4096 or 11008, or fewer
+    // blocks, measured slower)
+    if (!FU && WK == kGemvWaves && M >= 8 && a.K >= 16384 && (NB + 1) / 2 >= cus) grid = (NB + 1) / 2;
     const int bmax = (NB + grid - 1) / grid;
     auto kern = pick_xs<BITS, GS, SC, FU, WK>(bmax, (kGemvSliceRing * M + 3) / 4);
     if (int e = set_lds(kern, lds)) return e;
