@@ -85,6 +85,9 @@ def main(argv=None):
     ap.add_argument("--pmc-gemm-probe", action="store_true",
                     help="short run for rocprofv3 --pmc: the three M=2048 prefill GEMMs, three "
                          "launches each after one warm-up launch")
+    ap.add_argument("--pmc-search-probe", action="store_true",
+                    help="only run the 20-alpha search of the 4096x4096 layer on 512 calibration "
+                         "tokens three times (default path; for rocprofv3 --pmc counter runs)")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -123,6 +126,33 @@ def main(argv=None):
                 del W, qw, sc, ze, x, y
         torch.cuda.synchronize()
         print(json.dumps({"pmc_gemm_probe": True, "M": 2048, "flops_per_launch": res}))
+        return 0
+
+    if args.pmc_search_probe:
+        # calibration copy of known size, then the search three times
+        src = torch.empty(256 * 2**20, dtype=torch.uint8, device=dev).random_(0, 255)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        wl5 = WL.workload(5)
+        with torch.cuda.stream(stream):
+            W = torch.from_numpy(wl5.weights()).to(dev)
+            X = torch.from_numpy(wl5.calibration()).to(dev)
+            T, (N, K), A = X.shape[0], W.shape, len(wl5.alphas)
+            ws = torch.empty(awq.search_workspace_bytes(T, N, K, A), dtype=torch.uint8, device=dev)
+            for _ in range(3):
+                awq.search_scale(W, X, wl5.alphas, bits=4, workspace=ws)
+        torch.cuda.synchronize()
+        # loss GEMM: 2 T N K flops per alpha; error kernel: W read once, D written
+        # once per alpha (N rounded up to 16 rows)
+        print(json.dumps({"pmc_search_probe": True, "copy_bytes": 256 * 2**20, "T": T, "N": N,
+                          "K": K, "n_alpha": A,
+                          "loss_gemm_flops": 2.0 * T * N * K * A,
+                          "quant_err_bytes": 2 * N * K + A * 2 * ((N + 15) // 16 * 16) * K,
+                          "loss_gemm_d_bytes": A * 2 * ((N + 15) // 16 * 16) * K}))
         return 0
 
     # ------------------------------------------------------------------ decode GEMV

@@ -526,7 +526,9 @@ __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
 // (one batch entry per alpha, b_batch_stride halves apart) in the tiled layout
 // the search's error kernel writes: 16-row x 128-column tiles, each k32 step
 // of a tile one contiguous 1 KB run in MFMA operand order (lane 16 hq + j:
-// row j, columns 32 q + 8 hq .. + 7).  The prefill kernel's schedule with an
+// row j, columns 32 hq + 8 q .. + 7, the packed weights' order, which with
+// a_swz reads X conflict-free; columns 32 q + 8 hq had half the LDS cycles in
+// bank conflicts).  The prefill kernel's schedule with an
 // fp16 B: X goes to LDS by direct-to-LDS loads (the swizzled 128-row buffers,
 // S stages of one 128-wide K-step) and each wave streams its NBW D blocks
 // straight into registers, four 1 KB wave loads per block and K-step (read
@@ -571,7 +573,7 @@ __global__ __launch_bounds__(64 * WV, 1) void k_loss_gemm_p(
         a_off[i] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + 8u * kc;
     }
     // D block blk, group g: the tile at (blk G + g) 2048 halves, k32 step q at
-    // + 512 q, lane 16 hq + j at + 8 lane (row j, columns 32 q + 8 hq ..)
+    // + 512 q, lane 16 hq + j at + 8 lane (row j, columns 32 hq + 8 q ..)
     const _Float16* brow[NBW];
     const int NB16 = (N + 15) / 16;
 #pragma unroll
@@ -604,7 +606,7 @@ __global__ __launch_bounds__(64 * WV, 1) void k_loss_gemm_p(
 
     auto compute = [&](const BStage& bs, const unsigned char* abuf) {
         auto read_a = [&](int q, half8_t* a) {
-            const int kc = 4 * q + hq;
+            const int kc = 4 * hq + q;
 #pragma unroll
             for (int i = 0; i < FR; ++i) {
                 const int r = 16 * i + j;

@@ -104,11 +104,11 @@ __global__ __launch_bounds__(256) void k_candidate_scales(const float* __restric
 // Quantization error of every alpha.  One workgroup per 16-row x 128-column
 // tile of W (block b, group g of 128 columns), written as one tile of D in
 // the loss GEMM's layout: wave q takes the tile's k32 step q, lane 16 hq + j
-// the 8 weights of row 16 b + j at columns 128 g + 32 q + 8 hq .. + 7, so each
+// the 8 weights of row 16 b + j at columns 128 g + 32 hq + 8 q .. + 7, so each
 // wave stores its D step as one contiguous 1 KB run per alpha.  A group's
-// min/max is met over the 4 lanes of a row (hq) and then over the waves
-// holding the group's other steps (all 4 for 128-groups, steps q and q ^ 1 for
-// 64-groups) through LDS, one barrier per alpha.  W is read once: each lane
+// min/max is met over the lanes of a row that hold it (all 4 quarters hq for
+// 128-groups, hq and hq ^ 1 for 64-groups) and then over the 4 waves through
+// LDS, one barrier per alpha.  W is read once: each lane
 // keeps its 8 weights and walks the alphas, writing D_alpha for each (s_alpha
 // is small and stays in L2).  The codes are rint(fp32(v / Delta)) as in
 // awq_quantize_pack, decided in fixed point (quant_codes_b2); w_hat =
@@ -122,14 +122,14 @@ __global__ __launch_bounds__(256) void k_quant_err(LayerList layers,
                                                   const float* __restrict__ s_inv, int N, int K,
                                                   int n_alpha, long long d_stride,
                                                   uint4* __restrict__ D) {
-    __shared__ float red[2][2][4][16];                 // [alpha parity][min, max][step q][row j]
+    __shared__ float red[2][2][4][4][16];              // [alpha parity][min, max][step q][quarter hq][row j]
     const int G = K / kGroup;
     const int b = (int)(blockIdx.x / (unsigned)G), g = (int)(blockIdx.x % (unsigned)G);
     const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int j = lane & 15, hq = lane >> 4;
     const int n = 16 * b + j;
     const bool active = n < N;
-    const int k0 = kGroup * g + 32 * q + 8 * hq;
+    const int k0 = kGroup * g + 32 * hq + 8 * q;
     // this chunk's layer (rows never straddle layers: a layer holds whole rows)
     const long long t = (long long)n * (K / 8) + k0 / 8;
     const uint4* src = layers.w[0] + t;
@@ -161,18 +161,20 @@ __global__ __launch_bounds__(256) void k_quant_err(LayerList layers,
         float mn = v[0], mx = v[0];
 #pragma unroll
         for (int i = 1; i < 8; ++i) { mn = fminf(mn, v[i]); mx = fmaxf(mx, v[i]); }
-        // the row's 4 lanes of this step (lanes j, j + 16, j + 32, j + 48)
+        // the row's lanes of this step in the group (lanes j + 16 hq: hq ^ 1 for
+        // 64-groups, all four for 128-groups)
         mn = fminf(mn, __shfl_xor(mn, 16)); mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mn = fminf(mn, __shfl_xor(mn, 32)); mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // the group's other steps: min and max are exact, so the order is free
-        const int par = alpha & 1;
-        if (hq == 0) { red[par][0][q][j] = mn; red[par][1][q][j] = mx; }
-        __syncthreads();
         if constexpr (GS == 128) {
+            mn = fminf(mn, __shfl_xor(mn, 32)); mx = fmaxf(mx, __shfl_xor(mx, 32));
+        }
+        // the group's other steps (the 4 waves): min and max are exact, so the
+        // order is free
+        const int par = alpha & 1;
+        red[par][0][q][hq][j] = mn; red[par][1][q][hq][j] = mx;
+        __syncthreads();
 #pragma unroll
-            for (int o = 0; o < 4; ++o) { mn = fminf(mn, red[par][0][o][j]); mx = fmaxf(mx, red[par][1][o][j]); }
-        } else {
-            mn = fminf(mn, red[par][0][q ^ 1][j]); mx = fmaxf(mx, red[par][1][q ^ 1][j]);
+        for (int o = 0; o < 4; ++o) {
+            mn = fminf(mn, red[par][0][o][hq][j]); mx = fmaxf(mx, red[par][1][o][hq][j]);
         }
         const GroupParams p = group_params<Q, ZP>(mn, mx);
         uint32_t T[8];
