@@ -74,6 +74,12 @@
 extern "C" {
 #endif
 
+/* The HIP stream handle, declared as HIP declares it so that this header
+ * needs no HIP include (the same type as hip_runtime_api.h's hipStream_t).
+ * Every call is asynchronous on the stream it is given; NULL is the default
+ * stream. */
+typedef struct ihipStream_t* hipStream_t;
+
 typedef enum {
     AWQ_OK = 0,
     AWQ_ERR_NULL = 1,         /* a required pointer is NULL                 */
@@ -85,9 +91,9 @@ typedef enum {
 } awq_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
-const char* awq_status_str(int status);
+const char* awq_status_str(awq_status status);
 
-/* Version of the packed weight format described above (2). */
+/* Version of the packed weight format described above (3). */
 int awq_pack_format_version(void);
 
 /* uint32 words per packed row: K/8 for bits 4, 3K/32 for bits 3
@@ -119,9 +125,9 @@ size_t awq_packed_words(int N, int K, int bits);
  * w_hat = (q - z) * D, so awq_gemv and awq_gemm serve both.
  * bits in {3, 4}; group_size 128 or 64; zero_point 0 or 1.
  */
-int awq_quantize_pack(const void* W, const float* s, int N, int K, int bits,
+awq_status awq_quantize_pack(const void* W, const float* s, int N, int K, int bits,
                       int group_size, int zero_point, void* qweight,
-                      void* scales, void* zeros, void* stream);
+                      void* scales, void* zeros, hipStream_t stream);
 
 /*
  * awq_dequantize -- fake quantization ("Usage" step 2 of the llm-awq README,
@@ -131,17 +137,17 @@ int awq_quantize_pack(const void* W, const float* s, int N, int K, int bits,
  *   qweight, scales, zeros as produced by awq_quantize_pack (same bits and
  *   group_size); W_hat fp16 [N][K] out.  Errors as awq_quantize_pack.
  */
-int awq_dequantize(const void* qweight, const void* scales, const void* zeros,
+awq_status awq_dequantize(const void* qweight, const void* scales, const void* zeros,
                    void* W_hat, int N, int K, int bits, int group_size,
-                   void* stream);
+                   hipStream_t stream);
 
 /*
  * awq_scale_activations -- the activation side of the equivalent transform
  * (section 02.02 "AWQ" of the VPTQ blog): x_out[m][k] = fp16_rne(fp32(x[m][k]) / s[k]).
  *   x      fp16 [M][K] in;  s fp32 [K] in;  x_out fp16 [M][K] out (may equal x).
  */
-int awq_scale_activations(const void* x, const float* s, void* x_out, int M,
-                          int K, void* stream);
+awq_status awq_scale_activations(const void* x, const float* s, void* x_out, int M,
+                          int K, hipStream_t stream);
 
 /*
  * awq_search_workspace_bytes -- device workspace of awq_search_scale's
@@ -187,10 +193,10 @@ size_t awq_search_workspace_bytes_fused(int T, int N, int K, int n_alpha);
  * awq_quantize_pack), so L_i carries a relative error of order 1e-4 and
  * near-ties may pick a neighbouring alpha.
  */
-int awq_search_scale(const void* W, const void* X_cal, int T, int N, int K,
+awq_status awq_search_scale(const void* W, const void* X_cal, int T, int N, int K,
                      const float* alphas, int n_alpha, int bits, int group_size,
                      int zero_point, float* s_out, float* loss_out, int* best_out,
-                     void* workspace, size_t workspace_bytes, void* stream);
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * awq_search_scale_shared -- one scale search for several layers that read
@@ -208,11 +214,11 @@ int awq_search_scale(const void* W, const void* X_cal, int T, int N, int K,
  *   Errors as awq_search_scale; n_layers out of range is AWQ_ERR_UNSUPPORTED,
  *   a NULL Ws / Ns / layer pointer AWQ_ERR_NULL, a row count <= 0 AWQ_ERR_SHAPE.
  */
-int awq_search_scale_shared(const void* const* Ws, const int* Ns, int n_layers,
+awq_status awq_search_scale_shared(const void* const* Ws, const int* Ns, int n_layers,
                             const void* X_cal, int T, int K, const float* alphas,
                             int n_alpha, int bits, int group_size, int zero_point,
                             float* s_out, float* loss_out, int* best_out,
-                            void* workspace, size_t workspace_bytes, void* stream);
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * awq_gemv -- decode-stage W4A16 (or W3A16) product for small batches (the
@@ -227,9 +233,9 @@ int awq_search_scale_shared(const void* const* Ws, const int* Ns, int n_layers,
  *   be < 2^31 bytes (16 * ceil(N/16) * K * bits / 8) and x < 2^31 bytes
  *   (M * K * 2), else AWQ_ERR_SHAPE.
  */
-int awq_gemv(const void* x, const void* qweight, const void* scales,
+awq_status awq_gemv(const void* x, const void* qweight, const void* scales,
              const void* zeros, void* y, int M, int N, int K, int bits,
-             int group_size, void* stream);
+             int group_size, hipStream_t stream);
 
 /*
  * awq_gemv_scaled -- awq_gemv with the activation side of the equivalent
@@ -244,9 +250,9 @@ int awq_gemv(const void* x, const void* qweight, const void* scales,
  *          ulp of an fp16 rounding boundary (then one fp16 ulp apart).
  *   Other arguments, limits and errors as awq_gemv.
  */
-int awq_gemv_scaled(const void* x, const float* inv_s, const void* qweight,
+awq_status awq_gemv_scaled(const void* x, const float* inv_s, const void* qweight,
                     const void* scales, const void* zeros, void* y, int M, int N,
-                    int K, int bits, int group_size, void* stream);
+                    int K, int bits, int group_size, hipStream_t stream);
 
 /*
  * awq_gemv_gate_up -- the gate and up projections of a fused MLP ("transformers
@@ -261,11 +267,11 @@ int awq_gemv_scaled(const void* x, const float* inv_s, const void* qweight,
  *   a plain awq_gemv / awq_gemv_scaled on h.
  *   Limits and errors as awq_gemv; every pointer but inv_s is required.
  */
-int awq_gemv_gate_up(const void* x, const float* inv_s, const void* gate_qweight,
+awq_status awq_gemv_gate_up(const void* x, const float* inv_s, const void* gate_qweight,
                      const void* gate_scales, const void* gate_zeros,
                      const void* up_qweight, const void* up_scales,
                      const void* up_zeros, void* h, int M, int N, int K, int bits,
-                     int group_size, void* stream);
+                     int group_size, hipStream_t stream);
 
 /*
  * awq_gemm -- context-stage (prefill) W4A16 product, same formula as
@@ -275,9 +281,9 @@ int awq_gemv_gate_up(const void* x, const float* inv_s, const void* gate_qweight
  *   bits in {3, 4}; group_size 128 or 64; M*K < 2^31 and N*K/8 < 2^31 (else
  *   AWQ_ERR_SHAPE).
  */
-int awq_gemm(const void* x, const void* qweight, const void* scales,
+awq_status awq_gemm(const void* x, const void* qweight, const void* scales,
              const void* zeros, void* y, int M, int N, int K, int bits,
-             int group_size, void* stream);
+             int group_size, hipStream_t stream);
 
 /*
  * awq_gemm_splitk_workspace_bytes -- device workspace awq_gemm_splitk needs
@@ -300,10 +306,10 @@ size_t awq_gemm_splitk_workspace_bytes(int M, int N, int K);
  * Callers that need no workspace use awq_gemm.  (The split-K / stream-K
  * prefill item of the decode/prefill split in "transformers - AWQ".)
  */
-int awq_gemm_splitk(const void* x, const void* qweight, const void* scales,
+awq_status awq_gemm_splitk(const void* x, const void* qweight, const void* scales,
                     const void* zeros, void* y, int M, int N, int K, int bits,
                     int group_size, void* workspace, size_t workspace_bytes,
-                    void* stream);
+                    hipStream_t stream);
 
 #ifdef __cplusplus
 }

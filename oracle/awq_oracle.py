@@ -521,12 +521,3 @@ def search_scale_shared(Ws, X_cal: np.ndarray, alphas, bits: int = 4,
     """
     W = np.concatenate([np.asarray(w, dtype=np.float16) for w in Ws], axis=0)
     return search_scale(W, X_cal, alphas, bits, group_size, zero_point)
-
-
-def awq_quantize_layer(W: np.ndarray, X_cal: np.ndarray, alphas, bits: int = 4,
-                       zero_point: bool = True, group_size: int = GROUP_SIZE):
-    """Whole offline pass: search, then quantize and pack with the chosen s."""
-    s, losses, best = search_scale(W, X_cal, alphas, bits, group_size, zero_point)
-    q, d, z = quantize(W, s, bits, group_size, zero_point)
-    return {"s": s, "losses": losses, "best": best,
-            "qweight": pack(q, bits), "scales": d, "zeros": z, "q": q}

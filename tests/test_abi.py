@@ -43,6 +43,27 @@ def test_header_declares_the_boundary():
         assert must in names
 
 
+def test_header_compiles_as_c_and_beside_hip():
+    """The header is plain C (C11) and agrees with HIP's own hipStream_t when
+    both are included (a conflicting typedef would not compile)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no host C compiler")
+    r = subprocess.run([gcc, "-std=c11", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HEADER],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    hip_inc = "/opt/rocm/include"
+    if not os.path.exists(os.path.join(hip_inc, "hip", "hip_runtime_api.h")):
+        pytest.skip("no HIP headers")
+    src = '#include <hip/hip_runtime_api.h>\n#include "awq.h"\nint main(void) { hipStream_t s = 0; return (int)awq_status_str(AWQ_OK)[0] + (s != 0); }\n'
+    r = subprocess.run([shutil.which("g++") or "g++", "-std=c++17", "-fsyntax-only", "-D__HIP_PLATFORM_AMD__",
+                        f"-I{hip_inc}", f"-I{os.path.dirname(HEADER)}", "-x", "c++", "-"],
+                       input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
 def test_every_declared_symbol_is_exported(lib):
     for name in header_functions():
         assert hasattr(lib, name), name

@@ -110,8 +110,10 @@ def test_gate_up(gpu, M, N, K, bits, group_size, scaled):
 
 
 @pytest.mark.parametrize("M", [1, 4, 16])
-def test_gate_up_llama70b_sampled(gpu, M):
-    """Config-3 gate/up shape (K = 8192, N = 28672) at full size, sampled columns."""
+def test_gate_up_llama70b_full(gpu, M):
+    """Config-3 gate/up shape (K = 8192, N = 28672) at full size with the folded
+    scale, whole output tensor (M = 1: x staged once; 4, 16: K sliced, one row
+    block of both layers per workgroup)."""
     wl = WL.workload(3)
     K, N = wl.shapes[0]
     announce("gate_up 70b", f"M={M} N={N} K={K}")
@@ -120,9 +122,23 @@ def test_gate_up_llama70b_sampled(gpu, M):
     x = wl.activations(M, 0)
     inv_s = inv_scale(K, 33)
     h = gate_up(x, inv_s, g, u, N, 4, 128).astype(np.float64)
-    rows = np.concatenate([[0, 15, 16, N - 1], np.random.default_rng(3).choice(N, 60, replace=False)])
-    h_ref = O.gate_up_rows(x, inv_s, g, u, 4, K, rows)
-    err = rel_err(h[:, rows], h_ref)
+    h_ref = O.gate_up(x, inv_s, g, u, 4, K)
+    err = rel_err(h, h_ref)
+    assert err <= TOL, f"rel err {err:.3e}"
+
+
+# x staged once with 12 x loads per lane (unscaled: the scaled form takes the
+# sliced kernel past 8 loads), for the fused pair
+@pytest.mark.parametrize("group_size", [128, 64])
+@pytest.mark.parametrize("bits", [4, 3])
+@pytest.mark.parametrize("M,N,K", [(3, 1000, 10368), (5, 300, 6400), (7, 130, 4480), (15, 600, 2176)])
+def test_gate_up_x1_twelve_loads(gpu, M, N, K, bits, group_size):
+    announce("gate_up xl12", f"M={M} N={N} K={K} bits={bits} gs={group_size}")
+    g = layer(N, K, bits, seed=41 + N, group_size=group_size)
+    u = layer(N, K, bits, seed=42 + N, group_size=group_size)
+    x = WL.random_activations(M, K, seed=43 + M, sigma=1.0)
+    h = gate_up(x, None, g, u, N, bits, group_size).astype(np.float64)
+    err = rel_err(h, O.gate_up(x, None, g, u, bits, K))
     assert err <= TOL, f"rel err {err:.3e}"
 
 

@@ -134,7 +134,7 @@ def packed_words_per_row(K: int, bits: int) -> int:
 
 
 def packed_words(N: int, K: int, bits: int) -> int:
-    """uint32 words of a packed N x K matrix (format 2: rows padded to 16)."""
+    """uint32 words of a packed N x K matrix (format 3: rows padded to 16)."""
     return int(load_library().awq_packed_words(N, K, bits))
 
 
@@ -143,7 +143,7 @@ def quantize_pack(W, s=None, bits: int = 4, group_size: int = GROUP_SIZE,
     """Quantize fp16 W [N][K] (times s [K] if given) and pack.
 
     Returns (qweight int32 [packed_words(N, K, bits)], scales fp16
-    [ceil(N/16)][G][16], zeros fp16 [ceil(N/16)][G][16]) in packed format 2.
+    [ceil(N/16)][G][16], zeros fp16 [ceil(N/16)][G][16]) in packed format 3.
     """
     torch = _torch()
     lib = load_library()

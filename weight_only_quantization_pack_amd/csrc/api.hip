@@ -36,13 +36,17 @@ int check_nk(int N, int K) {
     return AWQ_OK;
 }
 
-int hip_status(int err) { return err == 0 ? AWQ_OK : AWQ_ERR_HIP; }
+awq_status hip_status(int err) { return err == 0 ? AWQ_OK : AWQ_ERR_HIP; }
+
+// the checks above return awq_status values as int
+awq_status as_status(int st) { return static_cast<awq_status>(st); }
+static_assert(sizeof(awq_status) == sizeof(int), "awq_status is passed as a C int");
 
 }  // namespace
 
 extern "C" {
 
-const char* awq_status_str(int status) {
+const char* awq_status_str(awq_status status) {
     switch (status) {
         case AWQ_OK: return "AWQ_OK";
         case AWQ_ERR_NULL: return "AWQ_ERR_NULL";
@@ -69,36 +73,36 @@ size_t awq_packed_words(int N, int K, int bits) {
     return 16 * (((size_t)N + 15) / 16) * awq_packed_words_per_row(K, bits);
 }
 
-int awq_quantize_pack(const void* W, const float* s, int N, int K, int bits, int group_size,
-                      int zero_point, void* qweight, void* scales, void* zeros, void* stream) {
+awq_status awq_quantize_pack(const void* W, const float* s, int N, int K, int bits, int group_size,
+                      int zero_point, void* qweight, void* scales, void* zeros, hipStream_t stream) {
     int st = check_quant_params(bits, group_size, zero_point);
-    if (st) return st;
-    if ((st = check_nk(N, K))) return st;
+    if (st) return as_status(st);
+    if ((st = check_nk(N, K))) return as_status(st);
     if (N == 0) return AWQ_OK;
-    if ((st = check_ptrs({W, qweight, scales, zeros}))) return st;
-    if (s != nullptr && (st = check_ptr(s))) return st;
+    if ((st = check_ptrs({W, qweight, scales, zeros}))) return as_status(st);
+    if (s != nullptr && (st = check_ptr(s))) return as_status(st);
     return hip_status(awq::launch_quantize_pack(W, s, N, K, bits, group_size, zero_point, qweight, scales, zeros,
-                                                (hipStream_t)stream));
+                                                stream));
 }
 
-int awq_dequantize(const void* qweight, const void* scales, const void* zeros, void* W_hat, int N,
-                   int K, int bits, int group_size, void* stream) {
+awq_status awq_dequantize(const void* qweight, const void* scales, const void* zeros, void* W_hat, int N,
+                   int K, int bits, int group_size, hipStream_t stream) {
     int st = check_quant_params(bits, group_size, 1);
-    if (st) return st;
-    if ((st = check_nk(N, K))) return st;
+    if (st) return as_status(st);
+    if ((st = check_nk(N, K))) return as_status(st);
     if ((long long)N * K >= (1LL << 40)) return AWQ_ERR_SHAPE;
     if (N == 0) return AWQ_OK;
-    if ((st = check_ptrs({qweight, scales, zeros, W_hat}))) return st;
+    if ((st = check_ptrs({qweight, scales, zeros, W_hat}))) return as_status(st);
     return hip_status(awq::launch_dequantize(qweight, scales, zeros, W_hat, N, K, bits, group_size,
-                                             (hipStream_t)stream));
+                                             stream));
 }
 
-int awq_scale_activations(const void* x, const float* s, void* x_out, int M, int K, void* stream) {
+awq_status awq_scale_activations(const void* x, const float* s, void* x_out, int M, int K, hipStream_t stream) {
     if (M < 0 || K <= 0 || K % awq::kGroup != 0) return AWQ_ERR_SHAPE;
     if (M == 0) return AWQ_OK;
     int st = check_ptrs({x, s, x_out});
-    if (st) return st;
-    return hip_status(awq::launch_scale_activations(x, s, x_out, M, K, (hipStream_t)stream));
+    if (st) return as_status(st);
+    return hip_status(awq::launch_scale_activations(x, s, x_out, M, K, stream));
 }
 
 size_t awq_search_workspace_bytes(int T, int N, int K, int n_alpha) {
@@ -121,34 +125,34 @@ int search_path(int T, int N, int K, int n_alpha, size_t workspace_bytes) {
 }
 }  // namespace
 
-int awq_search_scale(const void* W, const void* X_cal, int T, int N, int K, const float* alphas,
+awq_status awq_search_scale(const void* W, const void* X_cal, int T, int N, int K, const float* alphas,
                      int n_alpha, int bits, int group_size, int zero_point, float* s_out,
                      float* loss_out, int* best_out, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+                     hipStream_t stream) {
     int st = check_quant_params(bits, group_size, zero_point);
-    if (st) return st;
+    if (st) return as_status(st);
     if (n_alpha < 1 || n_alpha > kMaxAlpha) return AWQ_ERR_UNSUPPORTED;
     if (T > kMaxT) return AWQ_ERR_UNSUPPORTED;
     if (T <= 0 || N <= 0) return AWQ_ERR_SHAPE;
-    if ((st = check_nk(N, K))) return st;
+    if ((st = check_nk(N, K))) return as_status(st);
     if ((long long)T * K >= (1LL << 31)) return AWQ_ERR_SHAPE;   // 32-bit offsets into X_cal
     if (alphas == nullptr) return AWQ_ERR_NULL;
-    if ((st = check_ptrs({W, X_cal, s_out, workspace}))) return st;
-    if (loss_out != nullptr && (st = check_ptr(loss_out))) return st;
-    if (best_out != nullptr && (st = check_ptr(best_out))) return st;
+    if ((st = check_ptrs({W, X_cal, s_out, workspace}))) return as_status(st);
+    if (loss_out != nullptr && (st = check_ptr(loss_out))) return as_status(st);
+    if (best_out != nullptr && (st = check_ptr(best_out))) return as_status(st);
     const int path = search_path(T, N, K, n_alpha, workspace_bytes);
     if (path < 0) return AWQ_ERR_WORKSPACE;
     return hip_status(awq::launch_search(&W, &N, 1, X_cal, T, K, alphas, n_alpha, bits, group_size,
                                          zero_point, s_out, loss_out, best_out, workspace,
-                                         path == 1, (hipStream_t)stream));
+                                         path == 1, stream));
 }
 
-int awq_search_scale_shared(const void* const* Ws, const int* Ns, int n_layers, const void* X_cal,
+awq_status awq_search_scale_shared(const void* const* Ws, const int* Ns, int n_layers, const void* X_cal,
                             int T, int K, const float* alphas, int n_alpha, int bits, int group_size,
                             int zero_point, float* s_out, float* loss_out, int* best_out,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
     int st = check_quant_params(bits, group_size, zero_point);
-    if (st) return st;
+    if (st) return as_status(st);
     if (n_alpha < 1 || n_alpha > kMaxAlpha) return AWQ_ERR_UNSUPPORTED;
     if (n_layers < 1 || n_layers > awq::kMaxSearchLayers) return AWQ_ERR_UNSUPPORTED;
     if (T > kMaxT) return AWQ_ERR_UNSUPPORTED;
@@ -159,30 +163,30 @@ int awq_search_scale_shared(const void* const* Ws, const int* Ns, int n_layers, 
         N += Ns[l];
     }
     if (T <= 0 || N > (1LL << 30)) return AWQ_ERR_SHAPE;
-    if ((st = check_nk((int)N, K))) return st;
+    if ((st = check_nk((int)N, K))) return as_status(st);
     if ((long long)T * K >= (1LL << 31)) return AWQ_ERR_SHAPE;   // 32-bit offsets into X_cal
     for (int l = 0; l < n_layers; ++l)
         if (Ws[l] == nullptr) return AWQ_ERR_NULL;
-    if ((st = check_ptrs({X_cal, s_out, workspace}))) return st;
+    if ((st = check_ptrs({X_cal, s_out, workspace}))) return as_status(st);
     for (int l = 0; l < n_layers; ++l)
-        if ((st = check_ptr(Ws[l]))) return st;
-    if (loss_out != nullptr && (st = check_ptr(loss_out))) return st;
-    if (best_out != nullptr && (st = check_ptr(best_out))) return st;
+        if ((st = check_ptr(Ws[l]))) return as_status(st);
+    if (loss_out != nullptr && (st = check_ptr(loss_out))) return as_status(st);
+    if (best_out != nullptr && (st = check_ptr(best_out))) return as_status(st);
     const int path = search_path(T, (int)N, K, n_alpha, workspace_bytes);
     if (path < 0) return AWQ_ERR_WORKSPACE;
     return hip_status(awq::launch_search(Ws, Ns, n_layers, X_cal, T, K, alphas, n_alpha, bits,
                                          group_size, zero_point, s_out, loss_out, best_out,
-                                         workspace, path == 1, (hipStream_t)stream));
+                                         workspace, path == 1, stream));
 }
 
 namespace {
 // shared checks of the decode entry points; 1 = nothing to do (M or N is 0)
 int check_gemv(int M, int N, int K, int bits, int group_size) {
     int st = check_quant_params(bits, group_size, 1);
-    if (st) return st;
+    if (st) return as_status(st);
     if (M > kMaxGemvM) return AWQ_ERR_UNSUPPORTED;
     if (M < 0) return AWQ_ERR_SHAPE;
-    if ((st = check_nk(N, K))) return st;
+    if ((st = check_nk(N, K))) return as_status(st);
     // the decode kernels address x and the packed tiles with 32-bit offsets
     if ((long long)M * K * 2 >= (1LL << 31) ||
         16LL * ((N + 15) / 16) * K / 8 * bits >= (1LL << 31))
@@ -191,51 +195,51 @@ int check_gemv(int M, int N, int K, int bits, int group_size) {
 }
 }  // namespace
 
-int awq_gemv(const void* x, const void* qweight, const void* scales, const void* zeros, void* y,
-             int M, int N, int K, int bits, int group_size, void* stream) {
+awq_status awq_gemv(const void* x, const void* qweight, const void* scales, const void* zeros, void* y,
+             int M, int N, int K, int bits, int group_size, hipStream_t stream) {
     int st = check_gemv(M, N, K, bits, group_size);
-    if (st) return st < 0 ? AWQ_OK : st;
-    if ((st = check_ptrs({x, qweight, scales, zeros, y}))) return st;
+    if (st) return st < 0 ? AWQ_OK : as_status(st);
+    if ((st = check_ptrs({x, qweight, scales, zeros, y}))) return as_status(st);
     return hip_status(awq::launch_gemv(x, nullptr, qweight, scales, zeros, nullptr, nullptr, nullptr,
-                                       y, M, N, K, bits, group_size, (hipStream_t)stream));
+                                       y, M, N, K, bits, group_size, stream));
 }
 
-int awq_gemv_scaled(const void* x, const float* inv_s, const void* qweight, const void* scales,
+awq_status awq_gemv_scaled(const void* x, const float* inv_s, const void* qweight, const void* scales,
                     const void* zeros, void* y, int M, int N, int K, int bits, int group_size,
-                    void* stream) {
+                    hipStream_t stream) {
     int st = check_gemv(M, N, K, bits, group_size);
-    if (st) return st < 0 ? AWQ_OK : st;
-    if ((st = check_ptrs({x, inv_s, qweight, scales, zeros, y}))) return st;
+    if (st) return st < 0 ? AWQ_OK : as_status(st);
+    if ((st = check_ptrs({x, inv_s, qweight, scales, zeros, y}))) return as_status(st);
     return hip_status(awq::launch_gemv(x, inv_s, qweight, scales, zeros, nullptr, nullptr, nullptr,
-                                       y, M, N, K, bits, group_size, (hipStream_t)stream));
+                                       y, M, N, K, bits, group_size, stream));
 }
 
-int awq_gemv_gate_up(const void* x, const float* inv_s, const void* gate_qweight,
+awq_status awq_gemv_gate_up(const void* x, const float* inv_s, const void* gate_qweight,
                      const void* gate_scales, const void* gate_zeros, const void* up_qweight,
                      const void* up_scales, const void* up_zeros, void* h, int M, int N, int K,
-                     int bits, int group_size, void* stream) {
+                     int bits, int group_size, hipStream_t stream) {
     int st = check_gemv(M, N, K, bits, group_size);
-    if (st) return st < 0 ? AWQ_OK : st;
+    if (st) return st < 0 ? AWQ_OK : as_status(st);
     if ((st = check_ptrs({x, gate_qweight, gate_scales, gate_zeros, up_qweight, up_scales, up_zeros, h})))
-        return st;
-    if (inv_s && (st = check_ptr(inv_s))) return st;
+        return as_status(st);
+    if (inv_s && (st = check_ptr(inv_s))) return as_status(st);
     return hip_status(awq::launch_gemv(x, inv_s, gate_qweight, gate_scales, gate_zeros, up_qweight,
                                        up_scales, up_zeros, h, M, N, K, bits, group_size,
-                                       (hipStream_t)stream));
+                                       stream));
 }
 
-int awq_gemm(const void* x, const void* qweight, const void* scales, const void* zeros, void* y,
-             int M, int N, int K, int bits, int group_size, void* stream) {
+awq_status awq_gemm(const void* x, const void* qweight, const void* scales, const void* zeros, void* y,
+             int M, int N, int K, int bits, int group_size, hipStream_t stream) {
     int st = check_quant_params(bits, group_size, 1);
-    if (st) return st;
+    if (st) return as_status(st);
     if (M < 0) return AWQ_ERR_SHAPE;
-    if ((st = check_nk(N, K))) return st;
+    if ((st = check_nk(N, K))) return as_status(st);
     // the prefill kernel addresses x and the packed tiles with 32-bit offsets
     if ((long long)M * K >= (1LL << 31) || (long long)N * K / 8 >= (1LL << 31)) return AWQ_ERR_SHAPE;
     if (M == 0 || N == 0) return AWQ_OK;
-    if ((st = check_ptrs({x, qweight, scales, zeros, y}))) return st;
+    if ((st = check_ptrs({x, qweight, scales, zeros, y}))) return as_status(st);
     return hip_status(awq::launch_gemm(x, qweight, scales, zeros, y, M, N, K, bits, group_size,
-                                       (hipStream_t)stream));
+                                       stream));
 }
 
 size_t awq_gemm_splitk_workspace_bytes(int M, int N, int K) {
@@ -243,24 +247,24 @@ size_t awq_gemm_splitk_workspace_bytes(int M, int N, int K) {
     return awq::gemm_splitk_workspace_bytes(M, N, K);
 }
 
-int awq_gemm_splitk(const void* x, const void* qweight, const void* scales, const void* zeros,
+awq_status awq_gemm_splitk(const void* x, const void* qweight, const void* scales, const void* zeros,
                     void* y, int M, int N, int K, int bits, int group_size, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    size_t workspace_bytes, hipStream_t stream) {
     int st = check_quant_params(bits, group_size, 1);
-    if (st) return st;
+    if (st) return as_status(st);
     if (M < 0) return AWQ_ERR_SHAPE;
-    if ((st = check_nk(N, K))) return st;
+    if ((st = check_nk(N, K))) return as_status(st);
     if ((long long)M * K >= (1LL << 31) || (long long)N * K / 8 >= (1LL << 31)) return AWQ_ERR_SHAPE;
     if (M == 0 || N == 0) return AWQ_OK;
-    if ((st = check_ptrs({x, qweight, scales, zeros, y}))) return st;
+    if ((st = check_ptrs({x, qweight, scales, zeros, y}))) return as_status(st);
     const size_t need = awq::gemm_splitk_workspace_bytes(M, N, K);
     if (need > 0) {
         if (workspace == nullptr) return AWQ_ERR_NULL;
-        if ((st = check_ptr(workspace))) return st;
+        if ((st = check_ptr(workspace))) return as_status(st);
         if (workspace_bytes < need) return AWQ_ERR_WORKSPACE;
     }
     return hip_status(awq::launch_gemm_splitk(x, qweight, scales, zeros, y, M, N, K, bits,
-                                              group_size, workspace, (hipStream_t)stream));
+                                              group_size, workspace, stream));
 }
 
 }  // extern "C"
