@@ -6,16 +6,20 @@ shapes, in algorithmic GB/s.  One step = the seven linears of one Llama-7B
 decoder layer at decode (q, k, v, o: 4096x4096; gate, up: 4096->11008;
 down: 11008->4096), each one awq_gemv launch on packed int4 g128 weights.
 Weights rotate over enough replicas (>= 768 MB, three times the 256 MB
-Infinity Cache) that every step reads them from HBM.  The step's launches
-are captured once in a HIP graph and replayed, so host launch overhead is
-not timed.  Timing: HIP events on the launch stream around exactly --steps
-steps, after --warmup untimed steps.
+Infinity Cache) that every step reads them from HBM (step i reads replica
+i % R).  Exactly --warmup untimed steps, then exactly --steps timed steps,
+each run as one captured HIP graph of that many steps (one eager step before
+the captures loads the code objects), so host launch overhead is not timed.
+Timing: HIP events on the launch stream around the timed graph.  Beside it,
+the achievable read rate at each launch's byte count: a plain streaming-read
+kernel (libawq_probe, best of a sweep of launch shapes), timed the same way.
 
 Second half of the metric (gemm): prefill GEMM TFLOP/s at M = 2048 on the
-Mistral-7B shapes (4096x14336, 14336x4096, 4096x6144).  Also reported:
-the offline path (alpha search on the 4096x4096 layer with 512 calibration
-tokens and 20 grid points; quantize+pack) and the CPU oracle timed on a
-bounded sample of the same decode step.
+Mistral-7B shapes (4096x14336, 14336x4096, 4096x6144), and the same shapes
+at M = 512.  Also reported: the offline path (alpha search on the 4096x4096
+layer with 512 calibration tokens and 20 grid points; quantize+pack) and the
+CPU oracle on the host cores: the decode step (the headline leg), the M =
+2048 products, quantize+pack and the 20-alpha search.
 
 Algorithmic bytes per GEMV launch: N*K/2 (int4 codes) + 4*N*K/128 (fp16
 scale and zero per group) + 2*M*K (x) + 2*M*N (y).  Flops per GEMM launch:
@@ -197,32 +201,34 @@ def main(argv=None):
                           "gemv_launch_bytes": {f"{K}x{N}": gemv_bytes(1, N, K) for K, N in layer}}))
         return 0
 
-    # one graph = R consecutive steps, each on its own replica
+    # Exactly --warmup untimed and --steps timed steps: each is one graph of that
+    # many consecutive steps, step i reading replica i % R.  One eager step
+    # before the captures loads the code objects.
     with torch.cuda.stream(stream):
-        for r in range(R):          # eager warm-up (also loads the code object)
-            step(r)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        for r in range(R):
-            step(r)
+        step(0)
     torch.cuda.synchronize()
 
-    def replay(n_steps):
-        assert n_steps % R == 0
-        for _ in range(n_steps // R):
-            graph.replay()
+    def capture(n_steps, first):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n_steps):
+                step((first + i) % R)
+        return g
 
-    warm = R * max(1, math.ceil(args.warmup / R))
-    steps = R * max(1, math.ceil(args.steps / R))
+    warm = max(0, args.warmup)
+    steps = max(1, args.steps)
+    warm_graph = capture(warm, 0) if warm > 0 else None
+    timed_graph = capture(steps, warm)
+    torch.cuda.synchronize()
     with torch.cuda.stream(stream):
-        replay(warm)
+        if warm_graph is not None:
+            warm_graph.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         torch.cuda.synchronize()
         e0.record(stream)
-        replay(steps)
+        timed_graph.replay()
         e1.record(stream)
     torch.cuda.synchronize()
     ms_total = e0.elapsed_time(e1)
@@ -230,7 +236,16 @@ def main(argv=None):
     gemv_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     avg_launch_us = ms_per_step * 1e3 / len(layer)
     log(f"decode step {ms_per_step * 1e3:.2f} us  ->  {gemv_gbs:.1f} GB/s "
-        f"({100 * gemv_gbs / HBM_PEAK_GBS:.1f}% of HBM peak); avg launch {avg_launch_us:.2f} us")
+        f"({100 * gemv_gbs / HBM_PEAK_GBS:.1f}% of HBM peak); avg launch {avg_launch_us:.2f} us "
+        f"({steps} timed steps after {warm} warm-up steps)")
+    del warm_graph, timed_graph
+
+    # the plain-read ceiling at each launch's byte count (cold, graph replay)
+    ceiling = read_ceiling(torch, dev, stream, props.multi_processor_count,
+                           sorted({gemv_bytes(1, N, K) for K, N in layer}
+                                  | {gemv_bytes(1, N, K) for K, N in WL.workload(3).shapes}))
+    step_ceiling_us = sum(ceiling[gemv_bytes(1, N, K)]["us"] for K, N in layer)
+    ceiling_gbs = step_bytes / (step_ceiling_us * 1e-6) / 1e9
 
     # per-shape GEMV times (same graph technique, one shape per graph, its own
     # >= 768 MB of replicas so that the shape is as cold as in the step)
@@ -258,8 +273,11 @@ def main(argv=None):
         torch.cuda.synchronize()
         us = a.elapsed_time(b) * 1e3 / (n_rep * Rs)
         gbs = gemv_bytes(1, N, K) / (us * 1e-6) / 1e9
+        cl = ceiling[gemv_bytes(1, N, K)]
         per_shape[f"{K}x{N}"] = {"us": round(us, 3), "GBps": round(gbs, 1),
-                                 "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "cold_replicas": Rs}
+                                 "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "cold_replicas": Rs,
+                                 "read_ceiling_us": cl["us"],
+                                 "frac_of_read_ceiling": round(cl["us"] / us, 4)}
         log(f"  gemv K={K} N={N}: {us:.2f} us, {gbs:.1f} GB/s")
         del g, sreps
         torch.cuda.empty_cache()
@@ -309,6 +327,7 @@ def main(argv=None):
             gbs = gemv_bytes(M, N, K) / (us * 1e-6) / 1e9
             res[f"M{M}"] = {"us": round(us, 2), "GBps": round(gbs, 1),
                             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                            "frac_of_read_ceiling_M1": round(ceiling[gemv_bytes(1, N, K)]["us"] / us, 4),
                             "TFLOPs": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 1),
                             "entry": "awq_gemv" if M <= 16 else "awq_gemm"}
             log(f"  batched decode K={K} N={N} M={M}: {us:.2f} us, {gbs:.1f} GB/s")
@@ -320,49 +339,61 @@ def main(argv=None):
     # ------------------------------------------------------------------ prefill GEMM
     wl4 = WL.workload(4)
     M = 2048
-    gemm_res = {}
+    gemm_res, gemm_m512 = {}, {}
     tot_flops, tot_ms = 0.0, 0.0
+    tot512_flops, tot512_ms = 0.0, 0.0
     for i, (K, N) in enumerate(wl4.shapes):
         with torch.cuda.stream(stream):
             W = torch.from_numpy(wl4.weights(i)).to(dev)
             qw, sc, ze = awq.quantize_pack(W, None, bits=4)
             Wt = W.t().contiguous()                    # [K][N]: dense fp16 reference operand
             del W
-            x = torch.from_numpy(wl4.activations(M, i)).to(dev)
-            y = torch.empty((M, N), dtype=torch.float16, device=dev)
-            for _ in range(3):
-                awq.gemm(x, qw, sc, ze, N=N, bits=4, out=y)
+        for Mi in (2048, 512):
+            with torch.cuda.stream(stream):
+                x = torch.from_numpy(wl4.activations(Mi, i)).to(dev)
+                y = torch.empty((Mi, N), dtype=torch.float16, device=dev)
+                for _ in range(3):
+                    awq.gemm(x, qw, sc, ze, N=N, bits=4, out=y)
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(args.gemm_iters):
+                    awq.gemm(x, qw, sc, ze, N=N, bits=4, out=y)
+                b.record(stream)
             torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(args.gemm_iters):
-                awq.gemm(x, qw, sc, ze, N=N, bits=4, out=y)
-            b.record(stream)
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / args.gemm_iters
-        flops = 2.0 * M * N * K
-        tf = flops / (ms * 1e-3) / 1e12
-        # context, not the metric: the same product with dense fp16 weights
-        # through torch.matmul (hipBLASLt), i.e. what the vendor library reaches
-        # on this GPU for this shape without any dequantization
-        with torch.cuda.stream(stream):
-            for _ in range(3):
-                ref = torch.matmul(x, Wt)
-            a.record(stream)
-            for _ in range(args.gemm_iters):
-                ref = torch.matmul(x, Wt)
-            b.record(stream)
-        torch.cuda.synchronize()
-        ref_tf = flops / (a.elapsed_time(b) / args.gemm_iters * 1e-3) / 1e12
-        gemm_res[f"{K}x{N}"] = {"us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
-                                "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
-                                "dense_fp16_hipblaslt_TFLOPs": round(ref_tf, 1)}
-        tot_flops += flops
-        tot_ms += ms
-        log(f"  gemm M={M} K={K} N={N}: {ms * 1e3:.1f} us, {tf:.1f} TFLOP/s "
-            f"(dense fp16 torch.matmul {ref_tf:.1f})")
-        del qw, sc, ze, x, y, Wt, ref
+            ms = a.elapsed_time(b) / args.gemm_iters
+            flops = 2.0 * Mi * N * K
+            tf = flops / (ms * 1e-3) / 1e12
+            # context, not the metric: the same product with dense fp16 weights
+            # through torch.matmul (hipBLASLt), i.e. what the vendor library reaches
+            # on this GPU for this shape without any dequantization
+            with torch.cuda.stream(stream):
+                for _ in range(3):
+                    ref = torch.matmul(x, Wt)
+                a.record(stream)
+                for _ in range(args.gemm_iters):
+                    ref = torch.matmul(x, Wt)
+                b.record(stream)
+            torch.cuda.synchronize()
+            ref_tf = flops / (a.elapsed_time(b) / args.gemm_iters * 1e-3) / 1e12
+            rec = {"us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
+                   "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                   "dense_fp16_hipblaslt_TFLOPs": round(ref_tf, 1)}
+            if Mi == 2048:
+                gemm_res[f"{K}x{N}"] = rec
+                tot_flops += flops
+                tot_ms += ms
+            else:
+                rec["split_k_workspace_bytes"] = awq.gemm_splitk_workspace_bytes(Mi, N, K)
+                gemm_m512[f"{K}x{N}"] = rec
+                tot512_flops += flops
+                tot512_ms += ms
+            log(f"  gemm M={Mi} K={K} N={N}: {ms * 1e3:.1f} us, {tf:.1f} TFLOP/s "
+                f"(dense fp16 torch.matmul {ref_tf:.1f})")
+            del x, y, ref
+        del qw, sc, ze, Wt
     gemm_tflops = tot_flops / (tot_ms * 1e-3) / 1e12
+    gemm512_tflops = tot512_flops / (tot512_ms * 1e-3) / 1e12
 
     # ------------------------------------------------------------------ offline path
     # ---------------------------------------- variants of the pages (context, not the metric)
@@ -549,7 +580,7 @@ def main(argv=None):
     # ------------------------------------------------------------------ CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(layer, wl2, shape_index, step_bytes)
+        cpu = cpu_baseline(layer, wl2, shape_index, step_bytes, wl4, WL.workload(5))
 
     out = {
         "metric": METRIC,
@@ -572,11 +603,18 @@ def main(argv=None):
                      "unit": "GB/s", "frac": round(gemv_gbs / HBM_PEAK_GBS, 4),
                      "traffic": gemv_traffic_per_launch(), "traffic_unit": "HBM bytes per launch",
                      "algorithmic_bytes_per_launch": round(step_bytes / len(layer)),
-                     "kernel": "k_gemv_x1<4,128,8,U,XL,false,false> (ring U=2, XL=1 for K=4096; U=4, XL=4 for K=11008)", "avg_launch_us": round(avg_launch_us, 3)},
+                     "kernel": "k_gemv_x1<4,128,8,U,XL,false,false> (ring U=2, XL=1 for K=4096; U=4, XL=4 for K=11008)", "avg_launch_us": round(avg_launch_us, 3),
+                     "read_ceiling": {"GBps": round(ceiling_gbs, 1), "step_us": round(step_ceiling_us, 3),
+                                      "frac": round(gemv_gbs / ceiling_gbs, 4),
+                                      "what": "a plain streaming-read kernel (libawq_probe) reading each "
+                                              "launch's byte count once, cold, in graph replay; best of a "
+                                              "sweep of launch shapes",
+                                      "per_launch_bytes": {str(k): v for k, v in ceiling.items()}}},
         "gemv_per_shape": per_shape,
         "batched_decode_llama70b_mlp": batched,
         "variants": variants,
         "gemm": {"M": M, "TFLOPs": round(gemm_tflops, 1), "per_shape": gemm_res,
+                 "M512": {"TFLOPs": round(gemm512_tflops, 1), "per_shape": gemm_m512},
                  "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1),
                               "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4),
@@ -591,8 +629,75 @@ def main(argv=None):
     return 0
 
 
-def cpu_baseline(layer, wl2, shape_index, step_bytes):
-    """The oracle (not tuned) on one decode step of the layer, on the host cores."""
+def read_ceiling(torch, dev, stream, cus, sizes):
+    """Time of a plain streaming read of each byte count: the achievable HBM
+    read rate at that size, to set each GEMV launch against.
+
+    libawq_probe's read kernel (16-byte non-temporal buffer loads, several in
+    flight per lane, one XOR word per workgroup) over a sweep of launch shapes
+    (lanes per workgroup, loads in flight per lane, workgroups per CU); the
+    fastest is kept.  Each size reads consecutive disjoint slices of a 1 GiB
+    buffer (four times the 256 MB Infinity Cache), one launch per slice,
+    captured in one graph and replayed: the same cold-cache technique and
+    launch path as the GEMV timings.  Returns {bytes: {"us", "GBps", "config"}}.
+    """
+    import ctypes
+    path = os.path.join(ROOT, "weight_only_quantization_pack_amd", "lib", "libawq_probe.so")
+    probe = ctypes.CDLL(path)
+    probe.awq_probe_read.restype = ctypes.c_int
+    probe.awq_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    span = 1 << 30
+    buf = torch.zeros(span, dtype=torch.uint8, device=dev)
+    out = torch.zeros(8 * cus, dtype=torch.int32, device=dev)
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    res = {}
+    for B in sizes:
+        stride = (B + 4095) // 4096 * 4096
+        n = span // stride
+        best = None
+        for threads, unroll in ((256, 8), (512, 4), (512, 8), (256, 16)):
+            for per_cu in (1, 2, 4):
+                groups = per_cu * cus
+
+                def sweep():
+                    for r in range(n):
+                        rc = probe.awq_probe_read(ctypes.c_void_p(buf.data_ptr() + r * stride), B, threads,
+                                                  unroll, groups, ctypes.c_void_p(out.data_ptr()), sptr)
+                        if rc != 0:
+                            raise RuntimeError(f"read probe failed: hip error {rc}")
+                with torch.cuda.stream(stream):
+                    sweep()
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    sweep()
+                with torch.cuda.stream(stream):
+                    g.replay()
+                    torch.cuda.synchronize()
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    n_rep = max(2, 200 // n)
+                    a.record(stream)
+                    for _ in range(n_rep):
+                        g.replay()
+                    b.record(stream)
+                torch.cuda.synchronize()
+                us = a.elapsed_time(b) * 1e3 / (n_rep * n)
+                if best is None or us < best["us"]:
+                    best = {"us": round(us, 3), "GBps": round(B / (us * 1e-6) / 1e9, 1),
+                            "config": f"{threads} lanes x {unroll} loads, {per_cu} workgroups per CU"}
+                del g
+        res[B] = best
+        log(f"  read ceiling {B / 1e6:.2f} MB: {best['us']:.2f} us = {best['GBps']:.1f} GB/s ({best['config']})")
+    del buf, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(layer, wl2, shape_index, step_bytes, wl4, wl5):
+    """The oracle (not tuned) on the host cores: one decode step of the layer
+    (the headline leg), the three M = 2048 prefill products, quantize+pack of
+    the 4096 x 4096 layer and its 20-alpha search."""
     import numpy as np
     import oracle as O
     try:
@@ -617,12 +722,55 @@ def cpu_baseline(layer, wl2, shape_index, step_bytes):
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
     log(f"cpu baseline: {t:.3f} s per decode step ({len(times)} reps)")
+    del packs
+
+    # prefill: the three Mistral-7B products at M = 2048, once each
+    flops, secs = 0.0, 0.0
+    for i, (K, N) in enumerate(wl4.shapes):
+        q, d, z = O.quantize(wl4.weights(i), None, 4)
+        qw = O.pack(q, 4)
+        x = wl4.activations(2048, i)
+        t0 = time.perf_counter()
+        O.matmul(x, qw, d, z, 4, K)
+        secs += time.perf_counter() - t0
+        flops += 2.0 * 2048 * N * K
+    log(f"cpu baseline: M = 2048 prefill, three shapes in {secs:.2f} s")
+
+    # quantize + pack of the 4096 x 4096 layer with an activation scale, and
+    # the whole 20-alpha search of it on 512 calibration tokens
+    W, X = wl5.weights(), wl5.calibration()
+    s = O.candidate_scale(O.act_stat(X), 0.5)
+    qp = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        q, d, z = O.quantize(W, s, 4)
+        O.pack(q, 4)
+        qp.append(time.perf_counter() - t0)
+    qp_t = float(np.median(qp))
+    qp_bytes = W.size * 2 + W.shape[1] * 4 + W.size // 2 + 4 * W.size // 128
+    t0 = time.perf_counter()
+    O.search_scale(W, X, wl5.alphas, 4)
+    search_t = time.perf_counter() - t0
+    log(f"cpu baseline: quantize+pack {qp_t * 1e3:.0f} ms, 20-alpha search {search_t:.2f} s")
+
     return {"value": round(step_bytes / t / 1e9, 3), "unit": "GB/s", "cores": blas_threads,
             "kind": "oracle",
             "sample": f"{len(times)} full decode steps of the Llama-7B layer (7 GEMVs, M=1) through "
                       f"oracle.matmul: numpy unpack + fp64 dequantize (single-threaded) and fp64 "
                       f"product (OpenBLAS, {blas_threads} threads); median {t:.3f} s per step; "
-                      f"host has {os.cpu_count()} logical CPUs"}
+                      f"host has {os.cpu_count()} logical CPUs",
+            "legs": {
+                "gemm_m2048": {"value": round(flops / secs / 1e12, 4), "unit": "TFLOP/s",
+                               "sample": "the three Mistral-7B prefill products at M = 2048 through "
+                                         "oracle.matmul (fp64 BLAS product), once each, "
+                                         f"{secs:.2f} s in total"},
+                "quantize_pack_4096x4096": {"value": round(qp_bytes / qp_t / 1e9, 4), "unit": "GB/s",
+                                            "ms": round(qp_t * 1e3, 1),
+                                            "sample": "oracle.quantize (fp32 numpy) + oracle.pack "
+                                                      "of the whole layer with s = s_x^0.5, median of 3"},
+                "search_4096x4096_T512_20alpha": {"value": round(search_t * 1e3, 1), "unit": "ms",
+                                                  "sample": "the whole 20-alpha oracle.search_scale "
+                                                            "(fp64 loss per alpha), once"}}}
 
 
 if __name__ == "__main__":

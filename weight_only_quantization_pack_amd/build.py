@@ -4,6 +4,8 @@
 
 Every .hip source under csrc/ is compiled to an object in _build/ (in
 parallel), then linked into weight_only_quantization_pack_amd/lib/libawq.so.
+The measuring kernels under probe/ (a plain streaming read, the benchmark's
+bandwidth reference; not part of the library) go into lib/libawq_probe.so.
 --asm also keeps the gfx950 assembly of each source in _build/asm/.
 """
 from __future__ import annotations
@@ -72,11 +74,19 @@ def build(asm: bool = False, verbose: bool = False) -> str:
             objs.append(obj)
             if verbose and out.strip():
                 print(out)
-    lib = os.path.join(LIBDIR, "libawq.so")
+    lib = _link(objs, "libawq.so")
+    probe_srcs = sorted(glob.glob(os.path.join(HERE, "probe", "*.hip")))
+    if probe_srcs:
+        _link([compile_one(s, asm)[0] for s in probe_srcs], "libawq_probe.so")
+    return lib
+
+
+def _link(objs, name):
+    lib = os.path.join(LIBDIR, name)
     tmp = lib + ".tmp"
     rc, out = _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     if rc != 0:
-        raise RuntimeError(f"link failed:\n{out}")
+        raise RuntimeError(f"link of {name} failed:\n{out}")
     os.replace(tmp, lib)
     return lib
 
