@@ -311,6 +311,29 @@ awq_status awq_gemm_splitk(const void* x, const void* qweight, const void* scale
                     int group_size, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
 
+/*
+ * awq_gemm_splitk_noalloc -- awq_gemm_splitk for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels, split count and
+ * results (bit for bit), with the fp32 partial sums in a fixed device array
+ * of awq_gemm_splitk_noalloc_max_bytes() bytes (32 MiB) that the library
+ * holds on each GPU it runs on until the process ends.  The call allocates
+ * nothing and frees nothing.
+ *   Arguments, limits and errors as awq_gemm_splitk without the workspace;
+ *   a shape whose split needs more than the array holds
+ *   (awq_gemm_splitk_workspace_bytes(M, N, K) > the maximum) is
+ *   AWQ_ERR_WORKSPACE, and AWQ_ERR_HIP if the runtime cannot give the
+ *   array's address on the current device.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (other streams or host threads) race and must be serialized by the
+ *   caller.  Each call writes every partial it reads, so nothing carries over
+ *   from a previous call.
+ */
+size_t awq_gemm_splitk_noalloc_max_bytes(void);
+awq_status awq_gemm_splitk_noalloc(const void* x, const void* qweight, const void* scales,
+                                   const void* zeros, void* y, int M, int N, int K, int bits,
+                                   int group_size, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

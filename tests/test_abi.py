@@ -220,6 +220,18 @@ def test_gemm_splitk_validation(lib):
     assert f(NUL, NUL, NUL, NUL, NUL, 0, 8192, 28672, 4, 128, NUL, 0, NUL) == OK   # empty
 
 
+def test_gemm_splitk_noalloc_validation(lib):
+    f = lib.awq_gemm_splitk_noalloc
+    assert lib.awq_gemm_splitk_noalloc_max_bytes() == 32 << 20
+    assert f(P, P2, P3, P4, P5, 64, 4096, 4096, 5, 128, NUL) == UNSUP
+    assert f(P, P2, P3, P4, P5, 64, 4096, 4096, 4, 96, NUL) == UNSUP
+    assert f(P, P2, P3, P4, P5, -1, 4096, 4096, 4, 128, NUL) == SHAPE
+    assert f(P, P2, P3, P4, P5, 64, 4096, 4000, 4, 128, NUL) == SHAPE
+    assert f(NUL, P2, P3, P4, P5, 64, 4096, 4096, 4, 128, NUL) == NULL
+    assert f(P, P2, P3, P4, MIS, 64, 4096, 4096, 4, 128, NUL) == ALIGN
+    assert f(NUL, NUL, NUL, NUL, NUL, 0, 4096, 4096, 4, 128, NUL) == OK     # empty: nothing launched
+
+
 def test_scale_activations_validation(lib):
     assert lib.awq_scale_activations(P, P2, P3, 4, 100, NUL) == SHAPE
     assert lib.awq_scale_activations(P, P2, P3, -1, 128, NUL) == SHAPE

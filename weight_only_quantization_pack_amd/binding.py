@@ -49,6 +49,9 @@ SIGNATURES = [
     ("awq_gemm_splitk_workspace_bytes", _c_size_t, [_c_int, _c_int, _c_int]),
     ("awq_gemm_splitk", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
                                  _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_size_t, _c_void_p]),
+    ("awq_gemm_splitk_noalloc_max_bytes", _c_size_t, []),
+    ("awq_gemm_splitk_noalloc", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                         _c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p]),
 ]
 
 STATUS = {0: "AWQ_OK", 1: "AWQ_ERR_NULL", 2: "AWQ_ERR_SHAPE", 3: "AWQ_ERR_UNSUPPORTED",
@@ -294,6 +297,20 @@ def _matmul(fn_name, x, qweight, scales, zeros, N, bits, group_size, out, worksp
                                    M, N, K, bits, group_size, _stream_ptr(x))
     _check(st, fn_name)
     return out
+
+
+def gemm_splitk_noalloc(x, qweight, scales, zeros, N: int, bits: int = 4,
+                        group_size: int = GROUP_SIZE, out=None):
+    """awq_gemm_splitk_noalloc: the split-K prefill product with its fp32
+    partials in the library's fixed per-GPU array (the call allocates no device
+    memory; `out` is allocated here only when not given).  Calls overlapping on
+    one GPU race on that array."""
+    return _matmul("awq_gemm_splitk_noalloc", x, qweight, scales, zeros, N, bits, group_size, out)
+
+
+def gemm_splitk_noalloc_max_bytes() -> int:
+    """Size of the fixed partial-sum array of awq_gemm_splitk_noalloc."""
+    return int(load_library().awq_gemm_splitk_noalloc_max_bytes())
 
 
 def gemv(x, qweight, scales, zeros, N: int, bits: int = 4, group_size: int = GROUP_SIZE, out=None,

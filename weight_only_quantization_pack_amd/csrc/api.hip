@@ -3,6 +3,8 @@
 // been checked, so invalid calls never launch and never write an output.
 #include "awq_internal.h"
 
+#include <mutex>
+
 namespace {
 
 constexpr int kMaxGemvM = 16;
@@ -265,6 +267,67 @@ awq_status awq_gemm_splitk(const void* x, const void* qweight, const void* scale
     }
     return hip_status(awq::launch_gemm_splitk(x, qweight, scales, zeros, y, M, N, K, bits,
                                               group_size, workspace, stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// awq_gemm_splitk_noalloc: awq_gemm_splitk with the fp32 partial sums in a
+// fixed device array instead of a caller workspace.  Split K runs only while
+// the output tiles (at most 128 x 256) occupy at most half the CUs, so the
+// partials take at most CUs x 128 x 256 x 4 bytes: 32 MiB on a 256-CU MI355X.
+// Each GPU the library runs on holds its own copy of the array until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): the device address of each
+// GPU's copy is asked of the runtime once, with that device current, and kept.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// the current device's copy of `scratch` (nullptr if the runtime cannot say)
+void* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+size_t awq_gemm_splitk_noalloc_max_bytes(void) { return kScratchBytes; }
+
+awq_status awq_gemm_splitk_noalloc(const void* x, const void* qweight, const void* scales,
+                                   const void* zeros, void* y, int M, int N, int K, int bits,
+                                   int group_size, hipStream_t stream) {
+    int st = check_quant_params(bits, group_size, 1);
+    if (st) return as_status(st);
+    if (M < 0) return AWQ_ERR_SHAPE;
+    if ((st = check_nk(N, K))) return as_status(st);
+    if ((long long)M * K >= (1LL << 31) || (long long)N * K / 8 >= (1LL << 31)) return AWQ_ERR_SHAPE;
+    if (M == 0 || N == 0) return AWQ_OK;
+    if ((st = check_ptrs({x, qweight, scales, zeros, y}))) return as_status(st);
+    const size_t need = awq::gemm_splitk_workspace_bytes(M, N, K);
+    if (need > kScratchBytes) return AWQ_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (need > 0 && (ws = device_scratch()) == nullptr) return AWQ_ERR_HIP;
+    // every split writes all M x N entries of its partial tile, so nothing in
+    // the array needs clearing between calls
+    return hip_status(awq::launch_gemm_splitk(x, qweight, scales, zeros, y, M, N, K, bits,
+                                              group_size, ws, stream));
 }
 
 }  // extern "C"
