@@ -379,6 +379,26 @@ def main(argv=None):
             rec = {"us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1),
                    "frac_mfma": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                    "dense_fp16_hipblaslt_TFLOPs": round(ref_tf, 1)}
+            # the activation scale folded into the product (awq_gemm_scaled),
+            # and the same product as two launches (awq_scale_activations into
+            # a buffer, then awq_gemm), on the same inputs
+            inv = torch.from_numpy((1.0 / np.random.default_rng(K).lognormal(0, 0.5, K)).astype(np.float32)).to(dev)
+            svec = (1.0 / inv).contiguous()
+            xs_buf = torch.empty_like(x)
+            with torch.cuda.stream(stream):
+                for mode in ("folded", "two_pass"):
+                    for it in range(3 + args.gemm_iters):
+                        if it == 3:
+                            a.record(stream)
+                        if mode == "folded":
+                            awq.gemm(x, qw, sc, ze, N=N, bits=4, out=y, inv_s=inv)
+                        else:
+                            awq.scale_activations(x, svec, out=xs_buf)
+                            awq.gemm(xs_buf, qw, sc, ze, N=N, bits=4, out=y)
+                    b.record(stream)
+                    torch.cuda.synchronize()
+                    rec[f"scaled_{mode}_us"] = round(a.elapsed_time(b) / args.gemm_iters * 1e3, 2)
+            del xs_buf
             if Mi == 2048:
                 gemm_res[f"{K}x{N}"] = rec
                 tot_flops += flops

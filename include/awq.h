@@ -312,6 +312,26 @@ awq_status awq_gemm_splitk(const void* x, const void* qweight, const void* scale
                     hipStream_t stream);
 
 /*
+ * awq_gemm_scaled -- awq_gemm (and, given a workspace, awq_gemm_splitk) with
+ * the activation side of the equivalent transform (section 02.02 "AWQ" of the
+ * VPTQ blog: x / s against weights quantized as W * s) folded into the
+ * activation tiles, so a prefill needs no separate pass over x (the fused
+ * modules of "transformers - AWQ" fold it into the layer before):
+ *   x'[m][k] = fp16_rne(fp32(x[m][k]) * inv_s[k]);  y = awq_gemm(x', ...)
+ *   the same x' as awq_gemv_scaled, bit for bit.
+ *   inv_s    fp32 [K] in, device, 16-byte aligned: the caller's 1 / s.
+ *   workspace / workspace_bytes: NULL or 0 runs without a K split (as
+ *            awq_gemm); otherwise at least awq_gemm_splitk_workspace_bytes(M,
+ *            N, K) bytes (else AWQ_ERR_WORKSPACE), and the shape splits K as
+ *            awq_gemm_splitk does.
+ *   Other arguments, limits and errors as awq_gemm.
+ */
+awq_status awq_gemm_scaled(const void* x, const float* inv_s, const void* qweight,
+                           const void* scales, const void* zeros, void* y, int M, int N, int K,
+                           int bits, int group_size, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
  * awq_gemm_splitk_noalloc -- awq_gemm_splitk for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc): the same kernels, split count and

@@ -220,6 +220,21 @@ def test_gemm_splitk_validation(lib):
     assert f(NUL, NUL, NUL, NUL, NUL, 0, 8192, 28672, 4, 128, NUL, 0, NUL) == OK   # empty
 
 
+def test_gemm_scaled_validation(lib):
+    f = lib.awq_gemm_scaled
+    W = ctypes.c_void_p(0x60000)
+    assert f(P, NUL, P2, P3, P4, P5, 64, 512, 512, 4, 128, NUL, 0, NUL) == NULL     # inv_s required
+    assert f(P, MIS, P2, P3, P4, P5, 64, 512, 512, 4, 128, NUL, 0, NUL) == ALIGN
+    assert f(P, P, P2, P3, P4, P5, 64, 512, 500, 4, 128, NUL, 0, NUL) == SHAPE
+    assert f(P, P, P2, P3, P4, P5, 64, 512, 512, 5, 128, NUL, 0, NUL) == UNSUP
+    # a workspace that is given must hold the split's partials
+    need = lib.awq_gemm_splitk_workspace_bytes(64, 512, 8192)
+    assert need > 0
+    assert f(P, P, P2, P3, P4, P5, 64, 512, 8192, 4, 128, W, need - 16, NUL) == WS
+    assert f(P, P, P2, P3, P4, P5, 64, 512, 8192, 4, 128, MIS, need, NUL) == ALIGN
+    assert f(NUL, NUL, NUL, NUL, NUL, NUL, 0, 512, 512, 4, 128, NUL, 0, NUL) == OK
+
+
 def test_gemm_splitk_noalloc_validation(lib):
     f = lib.awq_gemm_splitk_noalloc
     assert lib.awq_gemm_splitk_noalloc_max_bytes() == 32 << 20

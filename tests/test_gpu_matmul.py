@@ -288,3 +288,75 @@ def test_empty_calls(gpu, fn):
     y = getattr(awq, fn)(x, dev(qw.reshape(-1)), dev(O.tile_params(d)), dev(O.tile_params(z)),
                          N=8, bits=4)
     assert tuple(y.shape) == (0, 8)
+
+
+# ----------------------------------------------------------------------------- folded scale (prefill)
+# (M, N, K): every tile form of the pipelined kernel with the scale folded into
+# its activation tiles -- 64-row tiles with split K (M = 5, 64), 128-row 8 x 2
+# tiles with a ragged split (130 x 200 x 4736: 37 groups in splits of 10, 10,
+# 10, 7), several row tiles, 4 x 7 (N = 14296) and 8 x 3 (N = 6100) wide tiles
+# with ragged edges, and N = 8192 at M = 2048, where awq_gemm takes the
+# two-workgroups-per-CU kernel but the scaled product the 8 x 2 tiles
+SCALED_GEMM = [(5, 302, 2048), (64, 1000, 8192), (130, 200, 4736), (257, 600, 1152),
+               (2048, 14296, 1024), (1999, 6100, 1024), (2048, 8192, 1024)]
+
+
+def _inv_scale(K, seed):
+    s = np.random.default_rng(seed).lognormal(0, 1, K).astype(np.float32)
+    return (np.float32(1) / s).astype(np.float32)
+
+
+@pytest.mark.parametrize("bits,group_size", [(4, 128), (3, 128), (4, 64)])
+@pytest.mark.parametrize("M,N,K", SCALED_GEMM)
+def test_gemm_scaled(gpu, M, N, K, bits, group_size):
+    """awq_gemm_scaled within the matmul bar of the oracle's product of
+    x' = fp16(fp32(x) * inv_s), and bit-identical to awq_gemm on the oracle's
+    x' wherever both take the same kernel (the scale is applied exactly in LDS
+    before any MFMA reads the tile)."""
+    import torch
+    announce("gemm_scaled", f"M={M} N={N} K={K} bits={bits} gs={group_size}")
+    qw, d, z = packed(WL.random_weights(N, K, seed=N + K), bits, group_size=group_size)
+    x = WL.random_activations(M, K, seed=M + 3, sigma=1.5)
+    inv_s = _inv_scale(K, K + 5)
+    xs = O.apply_inv_scale(x, inv_s)
+    args = (dev(qw.reshape(-1)), dev(O.tile_params(d)), dev(O.tile_params(z)))
+    y = awq.gemm(dev(x), *args, N=N, bits=bits, group_size=group_size, inv_s=dev(inv_s))
+    y_plain = awq.gemm(dev(xs), *args, N=N, bits=bits, group_size=group_size)
+    torch.cuda.synchronize()
+    err = rel_err(host(y).astype(np.float64), O.matmul(xs, qw, d, z, bits, K))
+    assert err <= TOL, f"rel err {err:.3e}"
+    if not (M, N, K) == (2048, 8192, 1024) or (bits, group_size) != (4, 128):
+        assert np.array_equal(host(y).view(np.uint16), host(y_plain).view(np.uint16))
+
+
+@pytest.mark.parametrize("M", [5, 130])
+def test_gemm_scaled_without_split(gpu, M):
+    """No workspace: the scaled product runs without a K split (one launch)."""
+    import torch
+    N, K = 302, 4736
+    qw, d, z = packed(WL.random_weights(N, K, seed=3), 4)
+    x = WL.random_activations(M, K, seed=4, sigma=1.5)
+    inv_s = _inv_scale(K, 6)
+    announce("gemm_scaled no split", M, N, K)
+    y = awq.gemm(dev(x), dev(qw.reshape(-1)), dev(O.tile_params(d)), dev(O.tile_params(z)), N=N,
+                 bits=4, inv_s=dev(inv_s), split_k=False)
+    torch.cuda.synchronize()
+    err = rel_err(host(y).astype(np.float64), O.matmul(O.apply_inv_scale(x, inv_s), qw, d, z, 4, K))
+    assert err <= TOL, f"rel err {err:.3e}"
+
+
+@pytest.mark.parametrize("shape_index", [0, 1, 2])
+def test_gemm_scaled_workload4_full(gpu, shape_index):
+    """Mistral-7B prefill shapes at M = 2048 with the folded scale, whole tensor."""
+    import torch
+    wl = WL.workload(4)
+    K, N = wl.shapes[shape_index]
+    _, qw, d, z = workload_layer(4, shape_index)
+    x = wl.activations(2048, shape_index)
+    inv_s = _inv_scale(K, 11)
+    announce("gemm_scaled workload 4", K, N)
+    y = awq.gemm(dev(x), dev(qw.reshape(-1)), dev(O.tile_params(d)), dev(O.tile_params(z)), N=N,
+                 bits=4, inv_s=dev(inv_s))
+    torch.cuda.synchronize()
+    err = rel_err(host(y).astype(np.float64), O.matmul(O.apply_inv_scale(x, inv_s), qw, d, z, 4, K))
+    assert err <= TOL, f"rel err {err:.3e}"

@@ -49,6 +49,9 @@ SIGNATURES = [
     ("awq_gemm_splitk_workspace_bytes", _c_size_t, [_c_int, _c_int, _c_int]),
     ("awq_gemm_splitk", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
                                  _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_size_t, _c_void_p]),
+    ("awq_gemm_scaled", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                 _c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p, _c_size_t,
+                                 _c_void_p]),
     ("awq_gemm_splitk_noalloc_max_bytes", _c_size_t, []),
     ("awq_gemm_splitk_noalloc", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                          _c_int, _c_int, _c_int, _c_int, _c_int, _c_void_p]),
@@ -299,6 +302,27 @@ def _matmul(fn_name, x, qweight, scales, zeros, N, bits, group_size, out, worksp
     return out
 
 
+def _gemm_scaled(x, inv_s, qweight, scales, zeros, N, bits, group_size, out, split_k, workspace):
+    torch = _torch()
+    lib = load_library()
+    M, K = x.shape
+    _need(x, torch.float16, (M, K), "x")
+    _need(inv_s, torch.float32, (K,), "inv_s")
+    _need_layer(qweight, scales, zeros, N, K, bits, group_size)
+    out = _out(out, M, N, x.device)
+    need = gemm_splitk_workspace_bytes(M, N, K) if split_k else 0
+    if need == 0:
+        workspace = None
+    elif workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    st = lib.awq_gemm_scaled(_ptr(x), _ptr(inv_s), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(out),
+                             M, N, K, bits, group_size, _ptr(workspace),
+                             0 if workspace is None else workspace.numel() * workspace.element_size(),
+                             _stream_ptr(x))
+    _check(st, "awq_gemm_scaled")
+    return out
+
+
 def gemm_splitk_noalloc(x, qweight, scales, zeros, N: int, bits: int = 4,
                         group_size: int = GROUP_SIZE, out=None):
     """awq_gemm_splitk_noalloc: the split-K prefill product with its fp32
@@ -371,14 +395,19 @@ def gemm_splitk_workspace_bytes(M: int, N: int, K: int) -> int:
 
 
 def gemm(x, qweight, scales, zeros, N: int, bits: int = 4, group_size: int = GROUP_SIZE, out=None,
-         split_k: bool = True, workspace=None):
+         split_k: bool = True, workspace=None, inv_s=None):
     """Prefill product y = x . w_hat^T for any M >= 1 rows of x (bits 4 or 3); N output columns.
 
     With split_k (default) shapes with few output tiles run through
     awq_gemm_splitk; its fp32 workspace is `workspace` (a device tensor of at
     least gemm_splitk_workspace_bytes bytes) or allocated here.  split_k=False
-    always calls awq_gemm.
+    always calls awq_gemm.  inv_s (fp32 [K] device tensor, the reciprocal of
+    the AWQ scale) folds the activation scale into the product through
+    awq_gemm_scaled: y = fp16(x * inv_s) . w_hat^T.
     """
+    if inv_s is not None:
+        return _gemm_scaled(x, inv_s, qweight, scales, zeros, N, bits, group_size, out, split_k,
+                            workspace)
     if split_k and x.dim() == 2:
         need = gemm_splitk_workspace_bytes(x.shape[0], N, x.shape[1])
         if need > 0:

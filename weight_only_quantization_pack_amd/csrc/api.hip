@@ -240,7 +240,7 @@ awq_status awq_gemm(const void* x, const void* qweight, const void* scales, cons
     if ((long long)M * K >= (1LL << 31) || (long long)N * K / 8 >= (1LL << 31)) return AWQ_ERR_SHAPE;
     if (M == 0 || N == 0) return AWQ_OK;
     if ((st = check_ptrs({x, qweight, scales, zeros, y}))) return as_status(st);
-    return hip_status(awq::launch_gemm(x, qweight, scales, zeros, y, M, N, K, bits, group_size,
+    return hip_status(awq::launch_gemm(x, nullptr, qweight, scales, zeros, y, M, N, K, bits, group_size,
                                        stream));
 }
 
@@ -265,7 +265,27 @@ awq_status awq_gemm_splitk(const void* x, const void* qweight, const void* scale
         if ((st = check_ptr(workspace))) return as_status(st);
         if (workspace_bytes < need) return AWQ_ERR_WORKSPACE;
     }
-    return hip_status(awq::launch_gemm_splitk(x, qweight, scales, zeros, y, M, N, K, bits,
+    return hip_status(awq::launch_gemm_splitk(x, nullptr, qweight, scales, zeros, y, M, N, K, bits,
+                                              group_size, workspace, stream));
+}
+
+awq_status awq_gemm_scaled(const void* x, const float* inv_s, const void* qweight,
+                           const void* scales, const void* zeros, void* y, int M, int N, int K,
+                           int bits, int group_size, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+    int st = check_quant_params(bits, group_size, 1);
+    if (st) return as_status(st);
+    if (M < 0) return AWQ_ERR_SHAPE;
+    if ((st = check_nk(N, K))) return as_status(st);
+    if ((long long)M * K >= (1LL << 31) || (long long)N * K / 8 >= (1LL << 31)) return AWQ_ERR_SHAPE;
+    if (M == 0 || N == 0) return AWQ_OK;
+    if ((st = check_ptrs({x, inv_s, qweight, scales, zeros, y}))) return as_status(st);
+    if (workspace == nullptr || workspace_bytes == 0)
+        return hip_status(awq::launch_gemm(x, inv_s, qweight, scales, zeros, y, M, N, K, bits,
+                                           group_size, stream));
+    if ((st = check_ptr(workspace))) return as_status(st);
+    if (workspace_bytes < awq::gemm_splitk_workspace_bytes(M, N, K)) return AWQ_ERR_WORKSPACE;
+    return hip_status(awq::launch_gemm_splitk(x, inv_s, qweight, scales, zeros, y, M, N, K, bits,
                                               group_size, workspace, stream));
 }
 
@@ -326,7 +346,7 @@ awq_status awq_gemm_splitk_noalloc(const void* x, const void* qweight, const voi
     if (need > 0 && (ws = device_scratch()) == nullptr) return AWQ_ERR_HIP;
     // every split writes all M x N entries of its partial tile, so nothing in
     // the array needs clearing between calls
-    return hip_status(awq::launch_gemm_splitk(x, qweight, scales, zeros, y, M, N, K, bits,
+    return hip_status(awq::launch_gemm_splitk(x, nullptr, qweight, scales, zeros, y, M, N, K, bits,
                                               group_size, ws, stream));
 }
 

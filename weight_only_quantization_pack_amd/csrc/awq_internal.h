@@ -183,15 +183,17 @@ int device_cu_count();
 int launch_gemv(const void* x, const float* inv_s, const void* qweight, const void* scales,
                 const void* zeros, const void* qweight2, const void* scales2, const void* zeros2,
                 void* y, int M, int N, int K, int bits, int group_size, hipStream_t st);
-int launch_gemm(const void* x, const void* qweight, const void* scales, const void* zeros,
-                void* y, int M, int N, int K, int bits, int group_size, hipStream_t st);
+// prefill product; inv_s (or NULL) folds the activation scale into the A tiles
+int launch_gemm(const void* x, const float* inv_s, const void* qweight, const void* scales,
+                const void* zeros, void* y, int M, int N, int K, int bits, int group_size,
+                hipStream_t st);
 // split-K prefill: number of K splits for this shape on the current device
 // (1: no split, no workspace) and the fp32 partial workspace it needs
 int gemm_splits(int M, int N, int K);
 size_t gemm_splitk_workspace_bytes(int M, int N, int K);
-int launch_gemm_splitk(const void* x, const void* qweight, const void* scales, const void* zeros,
-                       void* y, int M, int N, int K, int bits, int group_size, void* workspace,
-                       hipStream_t st);
+int launch_gemm_splitk(const void* x, const float* inv_s, const void* qweight, const void* scales,
+                       const void* zeros, void* y, int M, int N, int K, int bits, int group_size,
+                       void* workspace, hipStream_t st);
 // fused: the workspace of the fused loss kernel (no D buffer), else the default
 size_t search_workspace_bytes(int T, int N, int K, int n_alpha, bool fused);
 size_t loss_gemm_tiles(int T, int N);

@@ -39,6 +39,7 @@
 // schedule with fp16 B operands, and an epilogue that sums Y^2 per tile
 // instead of storing Y.
 #include <climits>
+#include <type_traits>
 
 #include "awq_internal.h"
 
@@ -276,18 +277,22 @@ __global__ __launch_bounds__(256, 2) void k_gemm_w4(
 // Split K (part != nullptr): workgroup (tile, blockIdx.y) covers groups
 // [blockIdx.y * gsplit, +gsplit) and writes its fp32 partial tile to
 // part[blockIdx.y][M][N]; k_splitk_reduce adds the splits in order.
-template <int BITS, int GS, int S, int GMT, int NBW, int WV = 4>
+template <int BITS, int GS, int S, int GMT, int NBW, int WV = 4, bool SC = false>
 __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
     const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
-    _Float16* __restrict__ Y, float* __restrict__ part, int M, int N, int K, int gsplit) {
+    _Float16* __restrict__ Y, float* __restrict__ part, const float* __restrict__ inv_s,
+    int M, int N, int K, int gsplit) {
     using namespace w4;
     static_assert(GMT == 128 || GMT == 64, "128- or 64-row tiles");
     constexpr int FR = GMT / 16;                       // 16-row A fragments (and row groups per wave)
     constexpr int ABUFT = GMT * ROW_BYTES;             // one A buffer
     constexpr int TN = 16 * NBW * WV;                  // tile columns: NBW 16-column blocks per wave
     constexpr int FRL = 4 * FR / WV;                   // A row groups (4 rows) each wave loads
-    extern __shared__ __attribute__((aligned(16))) unsigned char As[];   // S x ABUFT
+    // S x ABUFT of A buffers; with SC each wave's own copy of the K-step's 128
+    // inv_s values follows, S x WV x 512 bytes
+    extern __shared__ __attribute__((aligned(16))) unsigned char As[];
+    unsigned char* const isb_base = As + S * ABUFT;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -324,7 +329,8 @@ __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
     const uint32_t pgrp = GS == 64 ? (uint32_t)(hq >> 1) : 0u;
 
     constexpr int WQ = BITS == 4 ? 4 : 3;              // words per lane slot
-    constexpr int LPS = FRL + 3 * NBW;                 // loads per step and wave: A, B tiles, D and z words
+    // loads per step and wave: A, B tiles, D and z words (and with SC the inv_s copy)
+    constexpr int LPS = FRL + 3 * NBW + (SC ? 1 : 0);
     static_assert(LPS * (S - 2) <= 63, "vmcnt counts to 63");
     struct BStage { uint32_t q[NBW][WQ]; uint32_t d[NBW], z[NBW]; };
     // part p (0..NBW-1) of step kt's loads: the A row groups i with
@@ -332,6 +338,12 @@ __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
     // its scale and zero words
     auto issue_part = [&](int kt, int slot, BStage& bs, int p) {
         const uint32_t g = (uint32_t)(g_begin + min(kt, NGS - 1));
+        if constexpr (SC) {
+            // the step's 128 inv_s values into this wave's own copy (32 lanes x 16 B)
+            if (p == 0 && lane < 32)
+                __builtin_amdgcn_global_load_lds((global_void_t*)(inv_s + g * GK + 4u * lane),
+                                                 (lds_void_t*)(isb_base + (slot * WV + wave) * 512), 16, 0, 0);
+        }
 #pragma unroll
         for (int i = 0; i < FRL; ++i) {
             if (i * NBW / FRL != p) continue;
@@ -367,7 +379,8 @@ __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
     // reads) and B operands (NBW dequantized words) of substep s + 1 are produced while
     // the MFMAs of substep s run, so that neither LDS latency nor the
     // dequantization sits between two MFMA groups.
-    auto compute = [&](const BStage& bs, const unsigned char* abuf) {
+    // mid(s) runs after substep s's MFMAs have issued (they execute while it runs)
+    auto compute = [&](const BStage& bs, const unsigned char* abuf, auto&& mid) {
         half2_t zz[NBW], zz16[NBW], dd[NBW];
 #pragma unroll
         for (int c = 0; c < NBW; ++c) {
@@ -415,6 +428,7 @@ __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
                     for (int i = 0; i < FR; ++i)
                         acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a_cur[i], acc[i][c], 0, 0, 0);
                 }
+                mid(s);
                 if (s < 3) {
 #pragma unroll
                     for (int i = 0; i < FR; ++i) a_cur[i] = a_nxt[i];
@@ -437,6 +451,7 @@ __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
 #pragma unroll
                 for (int c = 0; c < NBW; ++c)
                     acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(b_cur[c], a_cur[i], acc[i][c], 0, 0, 0);
+            mid(s);
             if (s < 3) {
 #pragma unroll
                 for (int i = 0; i < FR; ++i) a_cur[i] = a_nxt[i];
@@ -444,6 +459,59 @@ __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
                 for (int c = 0; c < NBW; ++c) b_cur[c] = b_nxt[c];
             }
         }
+    };
+
+    // SC: x' = fp16(fp32(x) * inv_s) in place, over the A chunks this wave
+    // loaded itself into buffer `slot` (lane l of row group rg wrote the 16
+    // bytes at rg * 1024 + 16 l: row 4 rg + l / 16, global chunk
+    // (l % 16) ^ a_swz(row)), once its loads of that step have landed; the other
+    // waves see the scaled rows after the next barrier.  Each fp32 product is
+    // rounded once (v_fma_mix_f32 of the fp16 value, inv_s and -0, which keeps
+    // the sign of a zero product), then the pair to fp16 (v_cvt_pk_f16_f32,
+    // round to nearest even).
+    // chunks [i0, i0 + NC) of this wave's rows in buffer `slot`: every LDS read
+    // first, then the products, then the writes, so the reads' latencies overlap
+    auto scale_chunks = [&](int slot, int i0, auto nc) {
+        constexpr int NC = decltype(nc)::value;
+        const unsigned char* isb = isb_base + (slot * WV + wave) * 512;
+        uint4 v[NC];
+        float4 s0[NC], s1[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int rg = wave * FRL + i0 + c;
+            const int kc = (lane & 15) ^ a_swz(4 * rg + (lane >> 4));
+            v[c] = *reinterpret_cast<const uint4*>(As + slot * ABUFT + rg * 1024 + 16 * lane);
+            s0[c] = *reinterpret_cast<const float4*>(isb + 32 * kc);
+            s1[c] = *reinterpret_cast<const float4*>(isb + 32 * kc + 16);
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const float sv[8] = {s0[c].x, s0[c].y, s0[c].z, s0[c].w, s1[c].x, s1[c].y, s1[c].z, s1[c].w};
+            const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float t0, t1;
+                asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]"
+                    : "=v"(t0) : "v"(w[e]), "v"(sv[2 * e]), "s"(0x80000000u));
+                asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+                    : "=v"(t1) : "v"(w[e]), "v"(sv[2 * e + 1]), "s"(0x80000000u));
+                asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(o[e]) : "v"(t0), "v"(t1));
+            }
+            v[c] = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            *reinterpret_cast<uint4*>(As + slot * ABUFT + (wave * FRL + i0 + c) * 1024 + 16 * lane) = v[c];
+    };
+    // all FRL chunks of a step, in groups of SCG (the registers of SCG chunks live at once)
+    constexpr int SCG = (GMT == 64 || NBW >= 7) ? 4 : (NBW <= 2 ? 1 : 2);
+    auto scale_group = [&](int slot, int q) {
+        // the wide 128-row tiles keep the scaling apart from the MFMA code
+        // around it (interleaved, the registers of both spill); the others
+        // leave it to the scheduler to interleave
+        if constexpr (GMT == 128 && NBW >= 3) __builtin_amdgcn_sched_barrier(0);
+        scale_chunks(slot, q * SCG, std::integral_constant<int, SCG>{});
     };
 
     // the loads of every step are issued as one unit in the same order, in the
@@ -456,6 +524,13 @@ __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
         issue(s, s, bs[s]);
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (SC) {
+        // step 0 is scaled here; step kt + 1 under the MFMAs of step kt
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS * (S - 2)));
+#pragma unroll
+        for (int q = 0; q < FRL / SCG; ++q) scale_group(0, q);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     // NGS >= 1; a loop without an entry test keeps the compiler from sinking the
     // prologue's register loads behind one (out of the order above)
     int kt0 = 0;
@@ -474,7 +549,28 @@ __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
             __builtin_amdgcn_sched_barrier(0);
             // the last round may run past G: those steps keep the load stream
             // (and so the compiler's wait counts) uniform but compute nothing
-            if (kt < NGS) compute(bs[st], As + st * ABUFT);
+            auto mid = [&](int s) {
+                if constexpr (SC) {
+                    // step kt + 1 has landed once at most the S - 2 steps after it
+                    // are in flight.  8 x 2 tiles scale one chunk after each
+                    // substep (their next-substep operands leave few registers);
+                    // the others scale all of them after substep 1 (64-row
+                    // tiles) or, where the next substep's operands fill the
+                    // registers (8 x 3, 4 x 7), after the last substep
+                    constexpr int NG = FRL / SCG;            // chunk groups per step
+                    constexpr int S0 = NBW <= 2 ? 0 : (GMT == 64 ? 1 : 3);
+                    if (s == S0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS * (S - 2)));
+                    if constexpr (NG == 4) {
+                        scale_group((st + 1) % S, s);
+                    } else {
+                        if (s == S0) {
+#pragma unroll
+                            for (int q = 0; q < NG; ++q) scale_group((st + 1) % S, q);
+                        }
+                    }
+                }
+            };
+            if (kt < NGS) compute(bs[st], As + st * ABUFT, mid);
         }
         kt0 += S;
     } while (kt0 < NGS);
@@ -714,26 +810,40 @@ int w4p_tiles(int M, int N, int nbw = 4) {
     return ((N + 64 * nbw - 1) / (64 * nbw)) * ((M + rows - 1) / rows);
 }
 
-template <int GMT, int NBW, int WV = 4>
-int launch_w4p_rows(const void* x, const void* qweight, const void* scales, const void* zeros,
-                    void* y, float* part, int M, int N, int K, int bits, int group_size, int splits,
-                    int gsplit, hipStream_t st) {
+template <int GMT, int NBW, int WV, bool SC>
+int launch_w4p_rows_sc(const void* x, const void* qweight, const void* scales, const void* zeros,
+                       void* y, float* part, const float* inv_s, int M, int N, int K, int bits,
+                       int group_size, int splits, int gsplit, hipStream_t st) {
 #ifndef AWQ_GEMM_S7
 #define AWQ_GEMM_S7 3
 #endif
-    constexpr int S = NBW >= 7 ? AWQ_GEMM_S7 : kGemmStages;   // NBW = 7: four stages spill
+    // NBW = 7: four stages spill; 64-row tiles with the folded scale keep a
+    // fifth, since each step must land one step earlier to be scaled
+    constexpr int S = NBW >= 7 ? AWQ_GEMM_S7 : (SC && GMT == 64) ? kGemmStages + 1 : kGemmStages;
+    static_assert(!SC || (4 * GMT / 16 / WV) % (GMT == 64 || NBW >= 7 ? 4 : (NBW <= 2 ? 1 : 2)) == 0, "chunk groups");
     const int nT = ((N + 16 * NBW * WV - 1) / (16 * NBW * WV)) * ((M + GMT - 1) / GMT);
-    const size_t lds = (size_t)S * GMT * w4::ROW_BYTES;
+    const size_t lds = (size_t)S * GMT * w4::ROW_BYTES + (SC ? (size_t)S * WV * 512 : 0);
     auto kern = group_size == 64
-                    ? (bits == 4 ? k_gemm_w4p<4, 64, S, GMT, NBW, WV> : k_gemm_w4p<3, 64, S, GMT, NBW, WV>)
-                    : (bits == 4 ? k_gemm_w4p<4, 128, S, GMT, NBW, WV> : k_gemm_w4p<3, 128, S, GMT, NBW, WV>);
+                    ? (bits == 4 ? k_gemm_w4p<4, 64, S, GMT, NBW, WV, SC> : k_gemm_w4p<3, 64, S, GMT, NBW, WV, SC>)
+                    : (bits == 4 ? k_gemm_w4p<4, 128, S, GMT, NBW, WV, SC> : k_gemm_w4p<3, 128, S, GMT, NBW, WV, SC>);
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return (int)e;
     hipLaunchKernelGGL(kern, dim3(nT, splits), dim3(64 * WV), lds, st, (const _Float16*)x,
                        (const uint32_t*)qweight, (const _Float16*)scales, (const _Float16*)zeros,
-                       (_Float16*)y, part, M, N, K, gsplit);
+                       (_Float16*)y, part, inv_s, M, N, K, gsplit);
     return (int)hipGetLastError();
+}
+
+// inv_s (or NULL): the activation scale folded into the A tiles
+template <int GMT, int NBW, int WV = 4>
+int launch_w4p_rows(const void* x, const void* qweight, const void* scales, const void* zeros,
+                    void* y, float* part, const float* inv_s, int M, int N, int K, int bits,
+                    int group_size, int splits, int gsplit, hipStream_t st) {
+    return inv_s ? launch_w4p_rows_sc<GMT, NBW, WV, true>(x, qweight, scales, zeros, y, part, inv_s, M, N,
+                                                          K, bits, group_size, splits, gsplit, st)
+                 : launch_w4p_rows_sc<GMT, NBW, WV, false>(x, qweight, scales, zeros, y, part, nullptr, M,
+                                                           N, K, bits, group_size, splits, gsplit, st);
 }
 
 // nbw: the 128-row tile's width in 64-column units (4, 6 or 7; see
@@ -743,19 +853,19 @@ int launch_w4p_rows(const void* x, const void* qweight, const void* scales, cons
 // 448 columns as 4 waves of 7 (8 waves cannot split it).  64-row tiles take
 // 4 waves of 4 blocks.
 int launch_w4p(const void* x, const void* qweight, const void* scales, const void* zeros, void* y,
-               float* part, int M, int N, int K, int bits, int group_size, int splits, int gsplit,
-               hipStream_t st, int nbw = 4) {
+               float* part, const float* inv_s, int M, int N, int K, int bits, int group_size,
+               int splits, int gsplit, hipStream_t st, int nbw = 4) {
     if (w4p_rows(M) == 64)
-        return launch_w4p_rows<64, 4>(x, qweight, scales, zeros, y, part, M, N, K, bits, group_size,
-                                      splits, gsplit, st);
+        return launch_w4p_rows<64, 4>(x, qweight, scales, zeros, y, part, inv_s, M, N, K, bits,
+                                      group_size, splits, gsplit, st);
     if (nbw == 6)
-        return launch_w4p_rows<128, 3, 8>(x, qweight, scales, zeros, y, part, M, N, K, bits,
+        return launch_w4p_rows<128, 3, 8>(x, qweight, scales, zeros, y, part, inv_s, M, N, K, bits,
                                           group_size, splits, gsplit, st);
     if (nbw == 7)
-        return launch_w4p_rows<128, 7>(x, qweight, scales, zeros, y, part, M, N, K, bits, group_size,
-                                       splits, gsplit, st);
-    return launch_w4p_rows<128, 2, 8>(x, qweight, scales, zeros, y, part, M, N, K, bits, group_size,
-                                      splits, gsplit, st);
+        return launch_w4p_rows<128, 7>(x, qweight, scales, zeros, y, part, inv_s, M, N, K, bits,
+                                       group_size, splits, gsplit, st);
+    return launch_w4p_rows<128, 2, 8>(x, qweight, scales, zeros, y, part, inv_s, M, N, K, bits,
+                                      group_size, splits, gsplit, st);
 }
 
 // The GEMM's kernel and tile for M > 64: 16-column blocks per wave (4, 6 or
@@ -805,17 +915,18 @@ size_t gemm_splitk_workspace_bytes(int M, int N, int K) {
     return s > 1 ? (size_t)s * M * N * sizeof(float) : 0;
 }
 
-int launch_gemm_splitk(const void* x, const void* qweight, const void* scales, const void* zeros,
-                       void* y, int M, int N, int K, int bits, int group_size, void* workspace,
-                       hipStream_t st) {
+int launch_gemm_splitk(const void* x, const float* inv_s, const void* qweight, const void* scales,
+                       const void* zeros, void* y, int M, int N, int K, int bits, int group_size,
+                       void* workspace, hipStream_t st) {
     const int s = gemm_splits(M, N, K);
-    if (s <= 1) return launch_gemm(x, qweight, scales, zeros, y, M, N, K, bits, group_size, st);
+    if (s <= 1) return launch_gemm(x, inv_s, qweight, scales, zeros, y, M, N, K, bits, group_size, st);
     if ((unsigned long long)M * K >= (1ull << 31) || (unsigned long long)N * K / 8 >= (1ull << 31))
         return (int)hipErrorInvalidValue;
     const int G = K / kGroup;
     const int gsplit = (G + s - 1) / s;
     float* part = static_cast<float*>(workspace);
-    int err = launch_w4p(x, qweight, scales, zeros, y, part, M, N, K, bits, group_size, s, gsplit, st);
+    int err = launch_w4p(x, qweight, scales, zeros, y, part, inv_s, M, N, K, bits, group_size, s, gsplit,
+                         st);
     if (err) return err;
     const long long mn = (long long)M * N;
     const long long blocks = (mn / 4 + 1 + 255) / 256;
@@ -824,15 +935,18 @@ int launch_gemm_splitk(const void* x, const void* qweight, const void* scales, c
     return (int)hipGetLastError();
 }
 
-int launch_gemm(const void* x, const void* qweight, const void* scales, const void* zeros,
-                void* y, int M, int N, int K, int bits, int group_size, hipStream_t st) {
+int launch_gemm(const void* x, const float* inv_s, const void* qweight, const void* scales,
+                const void* zeros, void* y, int M, int N, int K, int bits, int group_size,
+                hipStream_t st) {
     // the kernel uses 32-bit element offsets into x and into the packed tiles
     if ((unsigned long long)M * K >= (1ull << 31) || (unsigned long long)N * K / 8 >= (1ull << 31))
         return (int)hipErrorInvalidValue;
     const int nT = ((N + w4::GN - 1) / w4::GN) * ((M + w4::GM - 1) / w4::GM);
-    const int nbw = gemm_tile_choice(M, N, bits, group_size, device_cu_count());
+    int nbw = gemm_tile_choice(M, N, bits, group_size, device_cu_count());
+    // the folded activation scale lives in the pipelined kernel only
+    if (nbw == 0 && inv_s != nullptr) nbw = 4;
     if (nbw > 0) {
-        return launch_w4p(x, qweight, scales, zeros, y, nullptr, M, N, K, bits, group_size, 1,
+        return launch_w4p(x, qweight, scales, zeros, y, nullptr, inv_s, M, N, K, bits, group_size, 1,
                           K / kGroup, st, nbw);
     } else {
         hipLaunchKernelGGL(k_gemm_w4, dim3(nT), dim3(256), 0, st, (const _Float16*)x,
