@@ -10,5 +10,5 @@ from .awq_oracle import (act_stat, candidate_scale, quantize, quantize_values, d
                          levels, packed_words_per_row, pack_rows,
                          packed_words, words_per_quarter, tiles_to_rows,
                          tile_params, untile_params, apply_inv_scale, silu, gate_up,
-                         gate_up_rows, search_scale_shared,
+                         gate_up_rows, search_scale_shared, mlp_block_loss, search_scale_mlp,
                          fake_quantize)

@@ -521,3 +521,49 @@ def search_scale_shared(Ws, X_cal: np.ndarray, alphas, bits: int = 4,
     """
     W = np.concatenate([np.asarray(w, dtype=np.float16) for w in Ws], axis=0)
     return search_scale(W, X_cal, alphas, bits, group_size, zero_point)
+
+
+# ---------------------------------------------------------------------------
+# f2: the gate/up scale searched on the MLP block's output
+# ---------------------------------------------------------------------------
+def mlp_block_loss(X_cal: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray,
+                   s: np.ndarray, bits: int = 4, group_size: int = GROUP_SIZE,
+                   zero_point: bool = True) -> float:
+    """L = mean over tokens t and block outputs o of (y_q[t, o] - y[t, o])^2 for
+    the MLP block y = (SiLU(X Wg^T) * (X Wu^T)) Wd^T, where y_q has the gate and
+    up weights quantized with the activation scale s (the deployed pair
+    (X / s).w_hat^T, i.e. X.(w_hat / s)^T) and the down projection Wd kept as it
+    is; fp64 throughout.
+
+    Reading: "Usage" step 1 of the llm-awq README searches the scales per
+    model; gate and up read one input, so they share one s (section 02.02 of
+    the VPTQ blog: the activations are divided by s once), and the error that
+    matters is that of the block those two layers feed -- the MLP's output
+    after SiLU(gate) * up and the down projection ("transformers - AWQ", "Fused
+    modules": the MLP as gate, up and down).  Wg, Wu fp16 [I][K]; Wd fp16
+    [K_out][I]; X_cal fp16 [T][K].
+    """
+    X = np.asarray(X_cal, dtype=np.float16).astype(np.float64)
+    s64 = np.asarray(s, np.float32).astype(np.float64)
+    hats = []
+    for W in (Wg, Wu):
+        q, d, z = quantize(W, s, bits, group_size, zero_point)
+        hats.append(dequantize(q, d, z, group_size) / s64[None, :])
+    Wg64, Wu64 = (np.asarray(w, np.float16).astype(np.float64) for w in (Wg, Wu))
+    h_q = silu(X @ hats[0].T) * (X @ hats[1].T)
+    h = silu(X @ Wg64.T) * (X @ Wu64.T)
+    E = (h_q - h) @ np.asarray(Wd, np.float16).astype(np.float64).T
+    return float(np.mean(E * E))
+
+
+def search_scale_mlp(X_cal: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray, alphas,
+                     bits: int = 4, group_size: int = GROUP_SIZE, zero_point: bool = True):
+    """The alpha grid search of the gate/up pair's shared scale on the MLP
+    block's output error (``mlp_block_loss``): s_i = candidate_scale(s_x,
+    alpha_i), the first index of the smallest loss is chosen.  Returns
+    (s_best fp32 [K], losses fp64 [n_alpha], best index)."""
+    s_x = act_stat(X_cal)
+    losses = np.asarray([mlp_block_loss(X_cal, Wg, Wu, Wd, candidate_scale(s_x, a), bits, group_size,
+                                        zero_point) for a in alphas], dtype=np.float64)
+    best = int(np.argmin(losses))
+    return candidate_scale(s_x, alphas[best]), losses, best
