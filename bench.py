@@ -579,6 +579,24 @@ def main(argv=None):
             search_fused_ms = a.elapsed_time(b) / 5
             search_ws = (ws.numel(), wsf.numel())
             del wsf
+            # the gate/up pair of the Llama-7B MLP (4096 -> 11008 -> 4096) searched
+            # on the block's output (awq_search_scale_mlp), same tokens and grid
+            Wg = torch.from_numpy(wl2.weights(1)).to(dev)          # 4096 x 11008 layer: [11008][4096]
+            Wu = torch.from_numpy(WL.random_weights(11008, 4096, seed=7)).to(dev)
+            Wd = torch.from_numpy(wl2.weights(2)).to(dev)          # 11008 x 4096 layer: [4096][11008]
+            wsm = torch.empty(awq.search_mlp_workspace_bytes(X.shape[0], 4096, 11008, 4096, len(wl5.alphas)),
+                              dtype=torch.uint8, device=dev)
+            for _ in range(2):
+                awq.search_scale_mlp(Wg, Wu, Wd, X, wl5.alphas, workspace=wsm)
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(3):
+                awq.search_scale_mlp(Wg, Wu, Wd, X, wl5.alphas, workspace=wsm)
+            b.record(stream)
+            torch.cuda.synchronize()
+            search_mlp_ms = a.elapsed_time(b) / 3
+            search_mlp_ws = wsm.numel()
+            del Wg, Wu, Wd, wsm
             a.record(stream)
             for _ in range(20):
                 qp = awq.quantize_pack(W, s, bits=4)
@@ -589,6 +607,8 @@ def main(argv=None):
         offline = {"search_4096x4096_T512_20alpha_ms": round(search_ms, 3),
                    "search_fused_path_ms": round(search_fused_ms, 3),
                    "search_workspace_bytes": {"default": search_ws[0], "fused": search_ws[1]},
+                   "search_mlp_block_llama7b_T512_20alpha_ms": round(search_mlp_ms, 3),
+                   "search_mlp_block_workspace_bytes": search_mlp_ws,
                    "search_loss_gemm_TFLOPs_incl_quant": round(
                        20 * 2.0 * 512 * 4096 * 4096 / (search_ms * 1e-3) / 1e12, 1),
                    "quantize_pack_4096x4096_us": round(qp_us, 2),

@@ -221,6 +221,45 @@ awq_status awq_search_scale_shared(const void* const* Ws, const int* Ns, int n_l
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * awq_search_mlp_workspace_bytes -- device workspace of awq_search_scale_mlp:
+ * the quantization errors of both layers for every alpha (n_alpha x 2I x K
+ * fp16), the tiled weights, the reference activations (3 x T x I fp32), the
+ * change of the intermediate activation per alpha (n_alpha x T x I fp16) and
+ * the loss partials.  0 for invalid sizes (K or I not a multiple of 128).
+ */
+size_t awq_search_mlp_workspace_bytes(int T, int K, int I, int K_out, int n_alpha);
+
+/*
+ * awq_search_scale_mlp -- the AWQ scale search ("Usage" step 1 of the llm-awq
+ * README) of the gate and up projections of an MLP block, which read one
+ * input and so share one s (section 02.02 "AWQ" of the VPTQ blog), with the
+ * error measured on the block's output ("transformers - AWQ", "Fused
+ * modules": the MLP as gate, up and down):
+ *   y      = (SiLU(X W_gate^T) * (X W_up^T)) W_down^T
+ *   y_i    = the same with gate and up replaced by their fake-quantized
+ *            weights w_hat_i / s_i (awq_quantize_pack with s_i), W_down kept
+ *   L_i    = mean over t and the K_out outputs of (y_i - y)^2
+ *   best   = smallest i with L_i == min L;  s_i as in awq_search_scale
+ *   W_gate, W_up  fp16 [I][K];  W_down fp16 [K_out][I];  X_cal fp16 [T][K]
+ *   K and I multiples of 128; 1 <= T <= 8192, T * K and T * I < 2^31
+ *   alphas HOST fp32 [n_alpha], 1 <= n_alpha <= 64
+ *   s_out fp32 [K] out; loss_out fp32 [n_alpha] out or NULL; best_out int32
+ *   [1] out (device) or NULL; workspace of at least
+ *   awq_search_mlp_workspace_bytes(T, K, I, K_out, n_alpha) bytes.
+ * The change of the intermediate activation SiLU(g) u is formed in fp32 from
+ * the fp16-MFMA products of X with the weights and with their quantization
+ * errors, rounded to fp16 and multiplied by W_down on fp16 MFMA with fp32
+ * accumulation, so L_i carries a relative error of order 1e-3 and near-ties
+ * may pick a neighbouring alpha.  Errors as awq_search_scale (an I or K that
+ * is not a multiple of 128 is AWQ_ERR_SHAPE).
+ */
+awq_status awq_search_scale_mlp(const void* W_gate, const void* W_up, const void* W_down,
+                                const void* X_cal, int T, int K, int I, int K_out,
+                                const float* alphas, int n_alpha, int bits, int group_size,
+                                int zero_point, float* s_out, float* loss_out, int* best_out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * awq_gemv -- decode-stage W4A16 (or W3A16) product for small batches (the
  * decode kernel of the llm-awq README feature list):
  *   y[m][n] = sum_g D[n][g] * sum_{k in g} x[m][k] * (q[n][k] - z[n][g])

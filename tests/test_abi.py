@@ -220,6 +220,30 @@ def test_gemm_splitk_validation(lib):
     assert f(NUL, NUL, NUL, NUL, NUL, 0, 8192, 28672, 4, 128, NUL, 0, NUL) == OK   # empty
 
 
+def test_search_mlp_validation(lib):
+    f = lib.awq_search_scale_mlp
+    a = (ctypes.c_float * 2)(0.0, 0.5)
+    A = ctypes.cast(a, ctypes.c_void_p)
+    W = ctypes.c_void_p(0x60000)
+    need = lib.awq_search_mlp_workspace_bytes(64, 256, 384, 200, 2)
+    assert need > 0
+    assert lib.awq_search_mlp_workspace_bytes(64, 256, 300, 200, 2) == 0     # I % 128 != 0
+    args = lambda **kw: [kw.get("wg", P), kw.get("wu", P2), kw.get("wd", P3), kw.get("x", P4),
+                         kw.get("T", 64), kw.get("K", 256), kw.get("I", 384), kw.get("K_out", 200),
+                         kw.get("al", A), kw.get("na", 2), kw.get("bits", 4), 128, 1, P5, NUL, NUL,
+                         kw.get("ws", W), kw.get("wsb", need), NUL]
+    assert f(*args(bits=5)) == UNSUP
+    assert f(*args(na=0)) == UNSUP
+    assert f(*args(T=9000)) == UNSUP
+    assert f(*args(I=300)) == SHAPE
+    assert f(*args(K=200)) == SHAPE
+    assert f(*args(K_out=0)) == SHAPE
+    assert f(*args(al=NUL)) == NULL
+    assert f(*args(wd=NUL)) == NULL
+    assert f(*args(x=MIS)) == ALIGN
+    assert f(*args(wsb=need - 1)) == WS
+
+
 def test_gemm_scaled_validation(lib):
     f = lib.awq_gemm_scaled
     W = ctypes.c_void_p(0x60000)

@@ -35,6 +35,10 @@ SIGNATURES = [
     ("awq_search_scale_shared", _c_int, [_c_void_p, _c_void_p, _c_int, _c_void_p, _c_int, _c_int,
                                          _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p,
                                          _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
+    ("awq_search_mlp_workspace_bytes", _c_size_t, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    ("awq_search_scale_mlp", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int, _c_int,
+                                      _c_int, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p,
+                                      _c_void_p, _c_void_p, _c_void_p, _c_size_t, _c_void_p]),
     ("awq_gemv", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                           _c_int, _c_int, _c_int, _c_void_p]),
     ("awq_gemm", _c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
@@ -233,6 +237,40 @@ def search_scale(W, X_cal, alphas, bits: int = 4, group_size: int = GROUP_SIZE,
                               bits, group_size, int(zero_point), _ptr(s_out), _ptr(loss),
                               _ptr(best), _ptr(workspace), workspace.numel(), _stream_ptr(W))
     _check(st, "awq_search_scale")
+    return s_out, loss[:n_alpha], best
+
+
+def search_mlp_workspace_bytes(T: int, K: int, I: int, K_out: int, n_alpha: int) -> int:
+    return int(load_library().awq_search_mlp_workspace_bytes(T, K, I, K_out, n_alpha))
+
+
+def search_scale_mlp(W_gate, W_up, W_down, X_cal, alphas, bits: int = 4, group_size: int = GROUP_SIZE,
+                     zero_point: bool = True, workspace=None):
+    """The gate/up pair's shared scale searched on the MLP block's output
+    (awq_search_scale_mlp).  W_gate, W_up fp16 [I][K], W_down fp16 [K_out][I],
+    X_cal fp16 [T][K].  Returns (s fp32 [K], loss fp32 [n_alpha], best int32 [1])."""
+    torch = _torch()
+    lib = load_library()
+    I, K = W_gate.shape
+    K_out = W_down.shape[0]
+    T = X_cal.shape[0]
+    _need(W_gate, torch.float16, (I, K), "W_gate")
+    _need(W_up, torch.float16, (I, K), "W_up")
+    _need(W_down, torch.float16, (K_out, I), "W_down")
+    _need(X_cal, torch.float16, (T, K), "X_cal")
+    n_alpha = len(alphas)
+    a = (ctypes.c_float * n_alpha)(*[float(v) for v in alphas])
+    need = search_mlp_workspace_bytes(T, K, I, K_out, n_alpha)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=W_gate.device)
+    s_out = torch.empty(K, dtype=torch.float32, device=W_gate.device)
+    loss = torch.empty(max(n_alpha, 1), dtype=torch.float32, device=W_gate.device)
+    best = torch.empty(1, dtype=torch.int32, device=W_gate.device)
+    st = lib.awq_search_scale_mlp(_ptr(W_gate), _ptr(W_up), _ptr(W_down), _ptr(X_cal), T, K, I, K_out,
+                                  ctypes.cast(a, _c_void_p), n_alpha, bits, group_size, int(zero_point),
+                                  _ptr(s_out), _ptr(loss), _ptr(best), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream_ptr(W_gate))
+    _check(st, "awq_search_scale_mlp")
     return s_out, loss[:n_alpha], best
 
 

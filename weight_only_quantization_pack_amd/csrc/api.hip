@@ -181,6 +181,37 @@ awq_status awq_search_scale_shared(const void* const* Ws, const int* Ns, int n_l
                                          workspace, path == 1, stream));
 }
 
+size_t awq_search_mlp_workspace_bytes(int T, int K, int I, int K_out, int n_alpha) {
+    if (T <= 0 || K <= 0 || I <= 0 || K_out <= 0 || n_alpha <= 0) return 0;
+    if (K % awq::kGroup != 0 || I % awq::kGroup != 0) return 0;
+    return awq::search_mlp_workspace_bytes(T, K, I, K_out, n_alpha);
+}
+
+awq_status awq_search_scale_mlp(const void* W_gate, const void* W_up, const void* W_down,
+                                const void* X_cal, int T, int K, int I, int K_out,
+                                const float* alphas, int n_alpha, int bits, int group_size,
+                                int zero_point, float* s_out, float* loss_out, int* best_out,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int st = check_quant_params(bits, group_size, zero_point);
+    if (st) return as_status(st);
+    if (n_alpha < 1 || n_alpha > kMaxAlpha) return AWQ_ERR_UNSUPPORTED;
+    if (T > kMaxT) return AWQ_ERR_UNSUPPORTED;
+    if (T <= 0 || I <= 0 || K_out <= 0) return AWQ_ERR_SHAPE;
+    if ((st = check_nk(I, K))) return as_status(st);
+    if (I % awq::kGroup != 0) return AWQ_ERR_SHAPE;            // I is the down projection's K
+    // 32-bit offsets into X_cal and into the intermediate activations
+    if ((long long)T * K >= (1LL << 31) || (long long)T * I >= (1LL << 31)) return AWQ_ERR_SHAPE;
+    if ((long long)K_out * I >= (1LL << 40) || (long long)I * K >= (1LL << 40)) return AWQ_ERR_SHAPE;
+    if (alphas == nullptr) return AWQ_ERR_NULL;
+    if ((st = check_ptrs({W_gate, W_up, W_down, X_cal, s_out, workspace}))) return as_status(st);
+    if (loss_out != nullptr && (st = check_ptr(loss_out))) return as_status(st);
+    if (best_out != nullptr && (st = check_ptr(best_out))) return as_status(st);
+    if (workspace_bytes < awq::search_mlp_workspace_bytes(T, K, I, K_out, n_alpha)) return AWQ_ERR_WORKSPACE;
+    return hip_status(awq::launch_search_mlp(W_gate, W_up, W_down, K_out, X_cal, T, K, I, alphas, n_alpha,
+                                             bits, group_size, zero_point, s_out, loss_out, best_out,
+                                             workspace, stream));
+}
+
 namespace {
 // shared checks of the decode entry points; 1 = nothing to do (M or N is 0)
 int check_gemv(int M, int N, int K, int bits, int group_size) {

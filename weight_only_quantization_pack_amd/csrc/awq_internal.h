@@ -201,12 +201,26 @@ size_t loss_gemm_tiles(int T, int N);
 inline size_t loss_rows(int N) { return (size_t)(N + 15) / 16 * 16; }
 // D: n_batch entries of loss_rows(N) x K fp16 in that layout (written by the
 // search's error kernel)
-int launch_loss_gemm(const void* X, const void* D, int T, int N, int K, int n_batch,
-                     double* partials, hipStream_t st);
+// X batched by a_stride halves and D by d_stride halves per batch entry
+int launch_loss_gemm(const void* X, long long a_stride, const void* D, long long d_stride, int T,
+                     int N, int K, int n_batch, double* partials, hipStream_t st);
+// the block-output search of a gate/up pair: D = [gate; up] rows (I each, I a
+// multiple of 128) in the loss GEMM's tiled layout, d_stride halves per batch
+// entry.  ref: D holds the weights themselves; writes g, u, h = SiLU(g) u
+// (fp32 [3][T][I]) to gu_ref.  Otherwise D holds their quantization errors and
+// the change of h, fp16 [n_batch][T][I], goes to dh.
+int launch_mlp_gemm(const void* X, const void* D, long long d_stride, int T, int I, int K,
+                    int n_batch, bool ref, float* gu_ref, _Float16* dh, hipStream_t st);
 // layers searched together (shared input): at most this many
 constexpr int kMaxSearchLayers = 8;
 // Ws / Ns: host arrays of n_layers device weight pointers and row counts;
 // the layers' rows in order form the N = sum Ns rows of the search
+// the gate/up scale searched on the MLP block's output (Wd [K_out][I] kept)
+size_t search_mlp_workspace_bytes(int T, int K, int I, int K_out, int n_alpha);
+int launch_search_mlp(const void* Wg, const void* Wu, const void* Wd, int K_out, const void* X_cal, int T,
+                      int K, int I, const float* alphas, int n_alpha, int bits, int group_size,
+                      int zero_point, float* s_out, float* loss_out, int* best_out, void* workspace,
+                      hipStream_t st);
 int launch_search(const void* const* Ws, const int* Ns, int n_layers, const void* X_cal, int T, int K,
                   const float* alphas, int n_alpha, int bits, int group_size, int zero_point,
                   float* s_out, float* loss_out, int* best_out, void* workspace, bool fused,

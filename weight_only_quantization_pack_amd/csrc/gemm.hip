@@ -633,15 +633,39 @@ __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
 // are left out of the sum, which is formed in a fixed order (lanes in fp32,
 // then the waves in fp64).  Tiles are numbered column-major, so the XCD that
 // runs eight consecutive tiles shares each D tile between the row tiles in
-// its L2.
-template <int S, int NBW, int WV>
+// its L2.  X may be batched too (a_batch_stride halves per batch entry).
+//
+// The block-output search of a gate/up pair (EPI_MLP_*) runs the same
+// schedule with NBW = 2 over D rows [gate; up] (I rows each, I a multiple of
+// 128): wave w takes gate block i0 / 16 + w and the up block of the same
+// rows, so each lane holds g and u (or their quantization errors) for the
+// same (token, channel) pairs, and the epilogue forms the block's
+// intermediate activation there instead of summing squares:
+//   EPI_MLP_REF: D = [Wg; Wu] itself: g, u and h = SiLU(g) u (fp32) to ref[3][M][I]
+//   EPI_MLP_DH:  D = errors W - w_hat / s of the pair (dg = X Dg^T = g - g_q):
+//                dh = fp16(SiLU(g - dg)(u - du) - h) to dh[z][M][I] (the change
+//                of the intermediate activation)
+enum { EPI_SQ = 0, EPI_MLP_REF = 1, EPI_MLP_DH = 2 };
+
+struct LossOut {
+    double* partials;          // EPI_SQ: [n_batch][tiles]
+    float* ref;                // EPI_MLP_*: g, u, h fp32 [3][M][I]
+    _Float16* dh;              // EPI_MLP_DH: [n_batch][M][I]
+    int I;                     // EPI_MLP_*: intermediate channels (gate rows)
+};
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
+
+template <int S, int NBW, int WV, int EPI = EPI_SQ>
 __global__ __launch_bounds__(64 * WV, 1) void k_loss_gemm_p(
-    const _Float16* __restrict__ x, const _Float16* __restrict__ D, double* __restrict__ partials,
-    int M, int N, int K, long long b_batch_stride) {
+    const _Float16* __restrict__ x, const _Float16* __restrict__ D, LossOut out,
+    int M, int N, int K, long long a_batch_stride, long long b_batch_stride) {
     using namespace w4;
+    static_assert(EPI == EPI_SQ || NBW == 2, "the MLP epilogues pair one gate and one up block");
     constexpr int GMT = 128, FR = GMT / 16;
     constexpr int ABUFT = GMT * ROW_BYTES;             // one X buffer (32 KB)
-    constexpr int TN = 16 * NBW * WV;
+    // tile columns: D rows, or (MLP) intermediate channels (one gate and one up block per wave)
+    constexpr int TN = EPI == EPI_SQ ? 16 * NBW * WV : 16 * WV;
     constexpr int FRL = 4 * FR / WV;                   // X row groups (4 rows) each wave loads
     constexpr int LPS = FRL + 4 * NBW;                 // loads per step and wave
     static_assert(LPS * (S - 2) <= 63, "vmcnt counts to 63");
@@ -653,12 +677,14 @@ __global__ __launch_bounds__(64 * WV, 1) void k_loss_gemm_p(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, hq = lane >> 4;
     const int G = K / kGroup;
-    const int nTn = (N + TN - 1) / TN, nTm = (M + GMT - 1) / GMT;
+    const int NC = EPI == EPI_SQ ? N : out.I;          // tile columns span
+    const int nTn = (NC + TN - 1) / TN, nTm = (M + GMT - 1) / GMT;
     const int nT = nTn * nTm;
     int t = blockIdx.x;
     if (nT % 8 == 0) t = (t % 8) * (nT / 8) + t / 8;
     const int m0 = (t % nTm) * GMT, n0 = (t / nTm) * TN;
     const _Float16* Dz = D + (size_t)blockIdx.y * (size_t)b_batch_stride;
+    x += (size_t)blockIdx.y * (size_t)a_batch_stride;
 
     uint32_t a_off[FRL];
 #pragma unroll
@@ -674,10 +700,11 @@ __global__ __launch_bounds__(64 * WV, 1) void k_loss_gemm_p(
     const int NB16 = (N + 15) / 16;
 #pragma unroll
     for (int c = 0; c < NBW; ++c) {
-        const int blk = min(n0 / 16 + wave * NBW + c, NB16 - 1);
+        int blk;
+        if constexpr (EPI == EPI_SQ) blk = min(n0 / 16 + wave * NBW + c, NB16 - 1);
+        else blk = (c == 0 ? 0 : out.I / 16) + n0 / 16 + wave;   // gate block, then the same rows of up
         brow[c] = Dz + (size_t)blk * G * 2048 + lane * 8;
     }
-
     struct BStage { half8_t b[NBW][4]; };
     auto issue = [&](int kt, int slot, BStage& bs) {
         const uint32_t g = (uint32_t)min(kt, G - 1);
@@ -749,6 +776,40 @@ __global__ __launch_bounds__(64 * WV, 1) void k_loss_gemm_p(
         kt0 += S;
     } while (kt0 < G);
 
+    if constexpr (EPI != EPI_SQ) {
+        // lane 16 hq + j, fragment i: token m0 + 16 i + j, channels
+        // n0 + 16 wave + 4 hq + r (r = 0..3); acc[i][0] is the gate's, acc[i][1] the up's
+        const int I = out.I;
+        const int col = n0 + 16 * wave + 4 * hq;
+#pragma unroll
+        for (int i = 0; i < FR; ++i) {
+            const int m = m0 + 16 * i + j;
+            if (m >= M) continue;
+            const size_t e = (size_t)m * I + col;
+            if constexpr (EPI == EPI_MLP_REF) {
+                float4_t h;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) h[r] = silu_f(acc[i][0][r]) * acc[i][1][r];
+                *reinterpret_cast<float4_t*>(out.ref + e) = acc[i][0];
+                *reinterpret_cast<float4_t*>(out.ref + (size_t)M * I + e) = acc[i][1];
+                *reinterpret_cast<float4_t*>(out.ref + 2 * (size_t)M * I + e) = h;
+            } else {
+                const float4_t g0 = *reinterpret_cast<const float4_t*>(out.ref + e);
+                const float4_t u0 = *reinterpret_cast<const float4_t*>(out.ref + (size_t)M * I + e);
+                const float4_t h0 = *reinterpret_cast<const float4_t*>(out.ref + 2 * (size_t)M * I + e);
+                half2_t dv[2];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    // D = W - w_hat / s, so the quantized pair's outputs are g - dg and u - du
+                    const float d = silu_f(g0[r] - acc[i][0][r]) * (u0[r] - acc[i][1][r]) - h0[r];
+                    dv[r >> 1][r & 1] = (_Float16)d;
+                }
+                *reinterpret_cast<uint2*>(out.dh + (size_t)blockIdx.y * M * I + e) =
+                    make_uint2(as_u32(dv[0]), as_u32(dv[1]));
+            }
+        }
+        return;
+    }
     // accumulator of lane 16 hq + j, block (i, c): X row m0 + 16 i + j, D row
     // n0 + 16 (wave NBW + c) + 4 hq + r
     float sq = 0.0f;
@@ -771,7 +832,7 @@ __global__ __launch_bounds__(64 * WV, 1) void k_loss_gemm_p(
         double tot = wsum[0];
 #pragma unroll
         for (int w = 1; w < WV; ++w) tot += wsum[w];
-        partials[(size_t)blockIdx.y * nT + blockIdx.x] = tot;
+        out.partials[(size_t)blockIdx.y * nT + blockIdx.x] = tot;
     }
 }
 
@@ -967,17 +1028,38 @@ size_t loss_gemm_tiles(int T, int N) {
     return (size_t)((N + kLossTN - 1) / kLossTN) * (size_t)((T + 127) / 128);
 }
 
-int launch_loss_gemm(const void* X, const void* D, int T, int N, int K, int n_batch,
-                     double* partials, hipStream_t st) {
-    auto kern = k_loss_gemm_p<kLossS, kLossNBW, kLossWV>;
+namespace {
+template <int EPI>
+int launch_loss_kernel(const void* X, long long a_stride, const void* D, long long d_stride, int T,
+                       int N, int K, int n_batch, const LossOut& out, hipStream_t st) {
+    auto kern = k_loss_gemm_p<kLossS, kLossNBW, kLossWV, EPI>;
     const size_t lds = (size_t)kLossS * 128 * w4::ROW_BYTES;
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return (int)e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)loss_gemm_tiles(T, N), n_batch), dim3(64 * kLossWV), lds, st,
-                       (const _Float16*)X, (const _Float16*)D, partials, T, N, K,
-                       (long long)loss_rows(N) * K);
+    const size_t tiles = EPI == EPI_SQ ? loss_gemm_tiles(T, N)
+                                       : (size_t)(out.I / (16 * kLossWV)) * (size_t)((T + 127) / 128);
+    hipLaunchKernelGGL(kern, dim3((unsigned)tiles, n_batch), dim3(64 * kLossWV), lds, st,
+                       (const _Float16*)X, (const _Float16*)D, out, T, N, K, a_stride, d_stride);
     return (int)hipGetLastError();
+}
+}  // namespace
+
+int launch_loss_gemm(const void* X, long long a_stride, const void* D, long long d_stride, int T,
+                     int N, int K, int n_batch, double* partials, hipStream_t st) {
+    LossOut out{};
+    out.partials = partials;
+    return launch_loss_kernel<EPI_SQ>(X, a_stride, D, d_stride, T, N, K, n_batch, out, st);
+}
+
+int launch_mlp_gemm(const void* X, const void* D, long long d_stride, int T, int I, int K,
+                    int n_batch, bool ref, float* gu_ref, _Float16* dh, hipStream_t st) {
+    LossOut out{};
+    out.ref = gu_ref;
+    out.dh = dh;
+    out.I = I;
+    return ref ? launch_loss_kernel<EPI_MLP_REF>(X, 0, D, d_stride, T, 2 * I, K, n_batch, out, st)
+               : launch_loss_kernel<EPI_MLP_DH>(X, 0, D, d_stride, T, 2 * I, K, n_batch, out, st);
 }
 
 }  // namespace awq

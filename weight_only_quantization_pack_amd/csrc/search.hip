@@ -460,6 +460,26 @@ __global__ __launch_bounds__(256) void k_select(const double* __restrict__ parti
     for (int k = tid; k < K; k += blockDim.x) s_out[k] = sb[k];
 }
 
+// Rows of the layers in `layers` (fp16, row-major, the N rows one layer after
+// the other) rewritten in the loss GEMM's tiled layout, as k_quant_err writes
+// D: one workgroup per 16-row x 128-column tile, wave q its k32 step, lane
+// 16 hq + j the 8 values of row 16 b + j at columns 128 g + 32 hq + 8 q.
+// Padding rows of the last block are written as zeros.
+__global__ __launch_bounds__(256) void k_tile_rows(LayerList layers, int N, int K, uint4* __restrict__ out) {
+    const int G = K / kGroup;
+    const int b = (int)(blockIdx.x / (unsigned)G), g = (int)(blockIdx.x % (unsigned)G);
+    const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int j = lane & 15, hq = lane >> 4;
+    const int n = 16 * b + j;
+    const int k0 = kGroup * g + 32 * hq + 8 * q;
+    const long long t = (long long)n * (K / 8) + k0 / 8;
+    const uint4* src = layers.w[0] + t;
+#pragma unroll
+    for (int l = 1; l < kMaxSearchLayers; ++l)
+        if (l < layers.n && t >= layers.cstart[l]) src = layers.w[l] + (t - layers.cstart[l]);
+    out[((size_t)blockIdx.x * 4 + q) * 64 + lane] = n < N ? *src : make_uint4(0, 0, 0, 0);
+}
+
 }  // namespace
 
 size_t search_workspace_bytes(int T, int N, int K, int n_alpha, bool fused) {
@@ -535,12 +555,96 @@ int launch_search(const void* const* Ws, const int* Ns, int n_layers, const void
                            n_alpha, (long long)loss_rows(N) * K / 8, (uint4*)D);
         int err = (int)hipGetLastError();
         if (err) return err;
-        err = launch_loss_gemm(X_cal, D, T, N, K, n_alpha, part, st);
+        err = launch_loss_gemm(X_cal, 0, D, (long long)loss_rows(N) * K, T, N, K, n_alpha, part, st);
         if (err) return err;
         n_tiles = (int)loss_gemm_tiles(T, N);
     }
     hipLaunchKernelGGL(k_select, dim3(1), dim3(256), 0, st, part, n_tiles, n_alpha,
                        1.0 / ((double)T * (double)N), s_all, K, s_out, loss_out, best_out);
+    return (int)hipGetLastError();
+}
+
+namespace {
+// workspace of the block-output search
+struct MlpLayout {
+    size_t sx, sall, sinv, D, wt, wdt, ref, dh, part, total;
+};
+
+MlpLayout mlp_layout(int T, int K, int I, int K_out, int n_alpha) {
+    MlpLayout L;
+    size_t off = 0;
+    L.sx = off;   off += align256((size_t)K * sizeof(float));
+    L.sall = off; off += align256((size_t)n_alpha * K * sizeof(float));
+    L.sinv = off; off += align256((size_t)n_alpha * K * sizeof(float));
+    L.D = off;    off += align256((size_t)n_alpha * 2 * I * K * sizeof(_Float16));
+    L.wt = off;   off += align256((size_t)2 * I * K * sizeof(_Float16));
+    L.wdt = off;  off += align256(loss_rows(K_out) * (size_t)I * sizeof(_Float16));
+    L.ref = off;  off += align256((size_t)3 * T * I * sizeof(float));
+    L.dh = off;   off += align256((size_t)n_alpha * T * I * sizeof(_Float16));
+    L.part = off; off += align256((size_t)n_alpha * loss_gemm_tiles(T, K_out) * sizeof(double));
+    L.total = off;
+    return L;
+}
+}  // namespace
+
+size_t search_mlp_workspace_bytes(int T, int K, int I, int K_out, int n_alpha) {
+    return mlp_layout(T, K, I, K_out, n_alpha).total;
+}
+
+// The gate/up pair's shared scale searched on the MLP block's output:
+//   D_a      = [Wg; Wu] - w_hat_a / s_a            (k_quant_err, both layers)
+//   g, u, h  = X Wg^T, X Wu^T, SiLU(g) u            (once, fp32)
+//   dh_a     = fp16(SiLU(g - X Dg_a^T) (u - X Du_a^T) - h)
+//   L_a      = sum (dh_a Wd^T)^2 / (T K_out)          (the loss GEMM on dh_a, Wd)
+// The change of the block's output is formed from the fp32 quantization error
+// of g and u (a difference of fp16-rounded block outputs would lose it).
+int launch_search_mlp(const void* Wg, const void* Wu, const void* Wd, int K_out, const void* X_cal, int T,
+                      int K, int I, const float* alphas, int n_alpha, int bits, int group_size,
+                      int zero_point, float* s_out, float* loss_out, int* best_out, void* workspace,
+                      hipStream_t st) {
+    const MlpLayout L = mlp_layout(T, K, I, K_out, n_alpha);
+    char* ws = static_cast<char*>(workspace);
+    float* s_x = reinterpret_cast<float*>(ws + L.sx);
+    float* s_all = reinterpret_cast<float*>(ws + L.sall);
+    float* s_inv = reinterpret_cast<float*>(ws + L.sinv);
+    _Float16* D = reinterpret_cast<_Float16*>(ws + L.D);
+    _Float16* wt = reinterpret_cast<_Float16*>(ws + L.wt);
+    _Float16* wdt = reinterpret_cast<_Float16*>(ws + L.wdt);
+    float* ref = reinterpret_cast<float*>(ws + L.ref);
+    _Float16* dh = reinterpret_cast<_Float16*>(ws + L.dh);
+    double* part = reinterpret_cast<double*>(ws + L.part);
+    const int N = 2 * I;
+
+    AlphaGrid grid{};
+    for (int i = 0; i < n_alpha; ++i) grid.a[i] = alphas[i];
+    hipLaunchKernelGGL(k_act_stat, dim3(K / 64), dim3(1024), 0, st, (const _Float16*)X_cal, T, K, s_x);
+    const long long nsk = (long long)n_alpha * K;
+    hipLaunchKernelGGL(k_candidate_scales, dim3((unsigned)((nsk + 255) / 256)), dim3(256), 0, st,
+                       s_x, K, grid, n_alpha, s_all, s_inv);
+
+    LayerList pair{};
+    pair.w[0] = static_cast<const uint4*>(Wg);
+    pair.w[1] = static_cast<const uint4*>(Wu);
+    pair.cstart[0] = 0;
+    pair.cstart[1] = (long long)I * (K / 8);
+    pair.n = 2;
+    auto qerr = group_size == 64 ? pick_quant_err<64>(bits, zero_point) : pick_quant_err<128>(bits, zero_point);
+    hipLaunchKernelGGL(qerr, dim3((unsigned)((size_t)N / 16 * (K / kGroup))), dim3(256), 0, st, pair, s_all,
+                       s_inv, N, K, n_alpha, (long long)N * K / 8, (uint4*)D);
+    hipLaunchKernelGGL(k_tile_rows, dim3((unsigned)((size_t)N / 16 * (K / kGroup))), dim3(256), 0, st, pair, N,
+                       K, (uint4*)wt);
+    LayerList down{};
+    down.w[0] = static_cast<const uint4*>(Wd);
+    down.n = 1;
+    hipLaunchKernelGGL(k_tile_rows, dim3((unsigned)(loss_rows(K_out) / 16 * (I / kGroup))), dim3(256), 0, st,
+                       down, K_out, I, (uint4*)wdt);
+    int err = (int)hipGetLastError();
+    if (err) return err;
+    if ((err = launch_mlp_gemm(X_cal, wt, 0, T, I, K, 1, true, ref, nullptr, st))) return err;
+    if ((err = launch_mlp_gemm(X_cal, D, (long long)N * K, T, I, K, n_alpha, false, ref, dh, st))) return err;
+    if ((err = launch_loss_gemm(dh, (long long)T * I, wdt, 0, T, K_out, I, n_alpha, part, st))) return err;
+    hipLaunchKernelGGL(k_select, dim3(1), dim3(256), 0, st, part, (int)loss_gemm_tiles(T, K_out), n_alpha,
+                       1.0 / ((double)T * (double)K_out), s_all, K, s_out, loss_out, best_out);
     return (int)hipGetLastError();
 }
 
