@@ -152,8 +152,10 @@ awq_status awq_scale_activations(const void* x, const float* s, void* x_out, int
 /*
  * awq_search_workspace_bytes -- device workspace of awq_search_scale's
  * default path for T calibration tokens, an N x K layer and n_alpha grid
- * points: it holds W - w_hat_i / s_i for every alpha (n_alpha x N rounded up
- * to a multiple of 16 x K fp16, in the loss GEMM's tiled layout).  0 when an argument is <= 0.
+ * points: it holds W - w_hat_i / s_i for one chunk of alphas (as many as fit
+ * in 128 MB, at least one: N rounded up to a multiple of 16 x K fp16 each, in
+ * the loss GEMM's tiled layout; the grid is run chunk by chunk).  0 when an
+ * argument is <= 0.
  */
 size_t awq_search_workspace_bytes(int T, int N, int K, int n_alpha);
 
@@ -222,10 +224,12 @@ awq_status awq_search_scale_shared(const void* const* Ws, const int* Ns, int n_l
 
 /*
  * awq_search_mlp_workspace_bytes -- device workspace of awq_search_scale_mlp:
- * the quantization errors of both layers for every alpha (n_alpha x 2I x K
- * fp16), the tiled weights, the reference activations (3 x T x I fp32), the
- * change of the intermediate activation per alpha (n_alpha x T x I fp16) and
- * the loss partials.  0 for invalid sizes (K or I not a multiple of 128).
+ * the quantization errors of both layers for one chunk of alphas (chunk x 2I
+ * x K fp16; the chunk is as many alphas as fit in 128 MB, but at least enough
+ * to fill the GPU), the tiled weights, the reference activations (3 x T x I
+ * fp32), the change of the intermediate activation per alpha of the chunk
+ * (chunk x T x I fp16) and the loss partials.  0 for invalid sizes (K or I
+ * not a multiple of 128).
  */
 size_t awq_search_mlp_workspace_bytes(int T, int K, int I, int K_out, int n_alpha);
 

@@ -91,7 +91,12 @@ def test_format_helpers(lib):
 def test_search_workspace_size(lib):
     T, N, K, A = 512, 4096, 4096, 20
     need = lib.awq_search_workspace_bytes(T, N, K, A)
-    assert need >= A * N * K * 2 + (2 * A + 1) * K * 4       # D for every alpha + scales
+    # D of one chunk of alphas (4 x 33.5 MB fit the 128 MB chunk budget) + scales
+    assert need >= 4 * N * K * 2 + (2 * A + 1) * K * 4
+    assert need < 5 * N * K * 2
+    # a D larger than the budget runs one alpha at a time
+    big = lib.awq_search_workspace_bytes(T, 28672, 8192, A)
+    assert 28672 * 8192 * 2 <= big < 2 * 28672 * 8192 * 2
     # fused path: s_x, s_alpha and 1/s_alpha, and one fp64 loss partial per
     # alpha and 256 x 128 output block; W - w_hat / s stays in registers
     fused = lib.awq_search_workspace_bytes_fused(T, N, K, A)

@@ -45,17 +45,32 @@ size_t fused_tiles(int T, int N) {
     return (size_t)((N + 127) / 128) * (size_t)((T + kFusedT - 1) / kFusedT);
 }
 
+// The default path runs the alpha grid in chunks whose error matrices D fit
+// in half of the 256 MB Infinity Cache, so the loss GEMM reads D back from the
+// cache rather than from HBM, and the workspace holds one chunk (W is read
+// once per chunk).  A D of more than that is one alpha per chunk.
+#ifndef AWQ_SEARCH_CHUNK_BYTES
+#define AWQ_SEARCH_CHUNK_BYTES ((size_t)128 << 20)
+#endif
+int alpha_chunk(size_t d_bytes_per_alpha, int n_alpha) {
+    const size_t c = AWQ_SEARCH_CHUNK_BYTES / (d_bytes_per_alpha > 0 ? d_bytes_per_alpha : 1);
+    return (int)(c < 1 ? 1 : (c > (size_t)n_alpha ? (size_t)n_alpha : c));
+}
+
 struct Layout {
     size_t sx, sall, sinv, D, part, total;
+    int chunk;                          // alphas per error-kernel + loss-GEMM pass
 };
 
 Layout layout(int T, int N, int K, int n_alpha, bool fused) {
     Layout L;
+    const size_t d_alpha = loss_rows(N) * K * sizeof(_Float16);
+    L.chunk = fused ? n_alpha : alpha_chunk(d_alpha, n_alpha);
     size_t off = 0;
     L.sx = off;   off += align256((size_t)K * sizeof(float));
     L.sall = off; off += align256((size_t)n_alpha * K * sizeof(float));
     L.sinv = off; off += align256((size_t)n_alpha * K * sizeof(float));
-    L.D = off;    off += fused ? 0 : align256((size_t)n_alpha * loss_rows(N) * K * sizeof(_Float16));
+    L.D = off;    off += fused ? 0 : align256((size_t)L.chunk * d_alpha);
     L.part = off; off += align256((size_t)n_alpha * (fused ? fused_tiles(T, N) : loss_gemm_tiles(T, N)) * sizeof(double));
     L.total = off;
     return L;
@@ -551,13 +566,18 @@ int launch_search(const void* const* Ws, const int* Ns, int n_layers, const void
         auto qerr = group_size == 64 ? pick_quant_err<64>(bits, zero_point)
                                      : pick_quant_err<128>(bits, zero_point);
         const size_t n_tiles16 = loss_rows(N) / 16 * (size_t)(K / kGroup);
-        hipLaunchKernelGGL(qerr, dim3((unsigned)n_tiles16), dim3(256), 0, st, layers, s_all, s_inv, N, K,
-                           n_alpha, (long long)loss_rows(N) * K / 8, (uint4*)D);
-        int err = (int)hipGetLastError();
-        if (err) return err;
-        err = launch_loss_gemm(X_cal, 0, D, (long long)loss_rows(N) * K, T, N, K, n_alpha, part, st);
-        if (err) return err;
         n_tiles = (int)loss_gemm_tiles(T, N);
+        for (int a0 = 0; a0 < n_alpha; a0 += L.chunk) {
+            const int na = min(L.chunk, n_alpha - a0);
+            hipLaunchKernelGGL(qerr, dim3((unsigned)n_tiles16), dim3(256), 0, st, layers,
+                               (const float*)s_all + (size_t)a0 * K, (const float*)s_inv + (size_t)a0 * K,
+                               N, K, na, (long long)loss_rows(N) * K / 8, (uint4*)D);
+            int err = (int)hipGetLastError();
+            if (err) return err;
+            err = launch_loss_gemm(X_cal, 0, D, (long long)loss_rows(N) * K, T, N, K, na,
+                                   part + (size_t)a0 * n_tiles, st);
+            if (err) return err;
+        }
     }
     hipLaunchKernelGGL(k_select, dim3(1), dim3(256), 0, st, part, n_tiles, n_alpha,
                        1.0 / ((double)T * (double)N), s_all, K, s_out, loss_out, best_out);
@@ -568,19 +588,36 @@ namespace {
 // workspace of the block-output search
 struct MlpLayout {
     size_t sx, sall, sinv, D, wt, wdt, ref, dh, part, total;
+    int chunk;                          // alphas per pass, as in the single-layer search
 };
+
+// alphas per pass of the block search: the cache budget's count, but at
+// least enough that the down projection's loss GEMM (its tiles times the
+// pass's alphas) gives every CU two workgroups
+#ifndef AWQ_MLP_MIN_CHUNK
+#define AWQ_MLP_MIN_CHUNK 0
+#endif
+int mlp_chunk(int T, int K, int I, int K_out, int n_alpha) {
+    const int budget = alpha_chunk((size_t)2 * I * K * sizeof(_Float16), n_alpha);
+    const int tiles = (int)loss_gemm_tiles(T, K_out);
+    int fill = (2 * device_cu_count() + tiles - 1) / tiles;
+    if (AWQ_MLP_MIN_CHUNK > 0) fill = AWQ_MLP_MIN_CHUNK;
+    return min(n_alpha, max(budget, fill));
+}
 
 MlpLayout mlp_layout(int T, int K, int I, int K_out, int n_alpha) {
     MlpLayout L;
+    const size_t d_alpha = (size_t)2 * I * K * sizeof(_Float16);
+    L.chunk = mlp_chunk(T, K, I, K_out, n_alpha);
     size_t off = 0;
     L.sx = off;   off += align256((size_t)K * sizeof(float));
     L.sall = off; off += align256((size_t)n_alpha * K * sizeof(float));
     L.sinv = off; off += align256((size_t)n_alpha * K * sizeof(float));
-    L.D = off;    off += align256((size_t)n_alpha * 2 * I * K * sizeof(_Float16));
+    L.D = off;    off += align256((size_t)L.chunk * d_alpha);
     L.wt = off;   off += align256((size_t)2 * I * K * sizeof(_Float16));
     L.wdt = off;  off += align256(loss_rows(K_out) * (size_t)I * sizeof(_Float16));
     L.ref = off;  off += align256((size_t)3 * T * I * sizeof(float));
-    L.dh = off;   off += align256((size_t)n_alpha * T * I * sizeof(_Float16));
+    L.dh = off;   off += align256((size_t)L.chunk * T * I * sizeof(_Float16));
     L.part = off; off += align256((size_t)n_alpha * loss_gemm_tiles(T, K_out) * sizeof(double));
     L.total = off;
     return L;
@@ -629,8 +666,6 @@ int launch_search_mlp(const void* Wg, const void* Wu, const void* Wd, int K_out,
     pair.cstart[1] = (long long)I * (K / 8);
     pair.n = 2;
     auto qerr = group_size == 64 ? pick_quant_err<64>(bits, zero_point) : pick_quant_err<128>(bits, zero_point);
-    hipLaunchKernelGGL(qerr, dim3((unsigned)((size_t)N / 16 * (K / kGroup))), dim3(256), 0, st, pair, s_all,
-                       s_inv, N, K, n_alpha, (long long)N * K / 8, (uint4*)D);
     hipLaunchKernelGGL(k_tile_rows, dim3((unsigned)((size_t)N / 16 * (K / kGroup))), dim3(256), 0, st, pair, N,
                        K, (uint4*)wt);
     LayerList down{};
@@ -641,8 +676,18 @@ int launch_search_mlp(const void* Wg, const void* Wu, const void* Wd, int K_out,
     int err = (int)hipGetLastError();
     if (err) return err;
     if ((err = launch_mlp_gemm(X_cal, wt, 0, T, I, K, 1, true, ref, nullptr, st))) return err;
-    if ((err = launch_mlp_gemm(X_cal, D, (long long)N * K, T, I, K, n_alpha, false, ref, dh, st))) return err;
-    if ((err = launch_loss_gemm(dh, (long long)T * I, wdt, 0, T, K_out, I, n_alpha, part, st))) return err;
+    const size_t n_tiles = loss_gemm_tiles(T, K_out);
+    for (int a0 = 0; a0 < n_alpha; a0 += L.chunk) {
+        const int na = min(L.chunk, n_alpha - a0);
+        hipLaunchKernelGGL(qerr, dim3((unsigned)((size_t)N / 16 * (K / kGroup))), dim3(256), 0, st, pair,
+                           (const float*)s_all + (size_t)a0 * K, (const float*)s_inv + (size_t)a0 * K, N, K, na,
+                           (long long)N * K / 8, (uint4*)D);
+        if ((err = (int)hipGetLastError())) return err;
+        if ((err = launch_mlp_gemm(X_cal, D, (long long)N * K, T, I, K, na, false, ref, dh, st))) return err;
+        if ((err = launch_loss_gemm(dh, (long long)T * I, wdt, 0, T, K_out, I, na, part + (size_t)a0 * n_tiles,
+                                    st)))
+            return err;
+    }
     hipLaunchKernelGGL(k_select, dim3(1), dim3(256), 0, st, part, (int)loss_gemm_tiles(T, K_out), n_alpha,
                        1.0 / ((double)T * (double)K_out), s_all, K, s_out, loss_out, best_out);
     return (int)hipGetLastError();
