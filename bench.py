@@ -89,6 +89,9 @@ def main(argv=None):
     ap.add_argument("--pmc-gemm-probe", action="store_true",
                     help="short run for rocprofv3 --pmc: the three M=2048 prefill GEMMs, three "
                          "launches each after one warm-up launch")
+    ap.add_argument("--pmc-batched-probe", action="store_true",
+                    help="short run for rocprofv3 --pmc: a 256 MiB device copy, then the Llama-70B MLP "
+                         "shapes at M = 64 (awq_gemm, split K) and M = 16 (awq_gemv), three launches each")
     ap.add_argument("--pmc-search-probe", action="store_true",
                     help="only run the 20-alpha search of the 4096x4096 layer on 512 calibration "
                          "tokens three times (default path; for rocprofv3 --pmc counter runs)")
@@ -130,6 +133,33 @@ def main(argv=None):
                 del W, qw, sc, ze, x, y
         torch.cuda.synchronize()
         print(json.dumps({"pmc_gemm_probe": True, "M": 2048, "flops_per_launch": res}))
+        return 0
+
+    if args.pmc_batched_probe:
+        src = torch.empty(256 * 2**20, dtype=torch.uint8, device=dev).random_(0, 255)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        wl3 = WL.workload(3)
+        order = []
+        with torch.cuda.stream(stream):
+            for i, (K, N) in enumerate(wl3.shapes):
+                W = torch.from_numpy(wl3.weights(i)).to(dev)
+                qw, sc, ze = awq.quantize_pack(W, None, bits=4)
+                del W
+                for M in (64, 16):
+                    x = torch.from_numpy(wl3.activations(M, i)).to(dev)
+                    y = torch.empty((M, N), dtype=torch.float16, device=dev)
+                    fn = awq.gemm if M > 16 else awq.gemv
+                    for _ in range(3):
+                        fn(x, qw, sc, ze, N=N, bits=4, out=y)
+                        order.append(f"{K}x{N} M={M}")
+                del qw, sc, ze
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_batched_probe": True, "copy_bytes": 256 * 2**20, "launches": order}))
         return 0
 
     if args.pmc_search_probe:
