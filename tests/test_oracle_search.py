@@ -121,3 +121,25 @@ def test_oracle_digests_unchanged():
         for key in ("qweight", "scales", "zeros", "search_best"):
             assert now[bits][key] == stored[bits][key]
         assert np.allclose(now[bits]["search_losses"], stored[bits]["search_losses"], rtol=1e-12)
+
+
+@pytest.mark.parametrize("w", [1, 5])
+def test_scaled_activations_stay_finite(w):
+    """x' = fp16(x / s) must not overflow fp16.  s is not normalised (the scale
+    search is equivariant only under power-of-two factors of s, where the fp32
+    product W s and the rounded-down fp16 group scale are exact), so |x / s| is
+    bounded only by the data: max |x_k| / max(s_x[k], 1e-4)^alpha.  On the
+    workloads' calibration activations and fresh activations of the same law it
+    stays far below 65504 at alpha = 1 (the largest grid point's direction) and at
+    the search's own choice."""
+    import numpy as np
+    wl = WL.workload(w)
+    X = wl.calibration()
+    s_x = O.act_stat(X)
+    alphas = wl.alphas if len(wl.alphas) > 1 else [0.0, wl.alphas[0]]
+    _, _, best = O.search_scale(wl.weights(), X, alphas, 4)
+    x = wl.activations(64)
+    for a in (alphas[best], 1.0):
+        xs = O.scale_activations(x, O.candidate_scale(s_x, a)).astype(np.float64)
+        assert np.all(np.isfinite(xs))
+        assert np.abs(xs).max() < 65504 / 16
