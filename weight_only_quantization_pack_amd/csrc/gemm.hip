@@ -505,7 +505,9 @@ __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
             *reinterpret_cast<uint4*>(As + slot * ABUFT + (wave * FRL + i0 + c) * 1024 + 16 * lane) = v[c];
     };
     // all FRL chunks of a step, in groups of SCG (the registers of SCG chunks live at once)
-    constexpr int SCG = (GMT == 64 || NBW >= 7) ? 4 : (NBW <= 2 ? 1 : 2);
+    constexpr int SCG0 = (GMT == 64 || NBW >= 7) ? 4 : (NBW <= 2 ? 1 : 2);
+    constexpr int SCG = SCG0 < FRL ? SCG0 : FRL;
+    static_assert(!SC || FRL % SCG == 0, "the chunk groups cover a step's chunks");
     auto scale_group = [&](int slot, int q) {
         // the wide 128-row tiles keep the scaling apart from the MFMA code
         // around it (interleaved, the registers of both spill); the others
@@ -881,7 +883,6 @@ int launch_w4p_rows_sc(const void* x, const void* qweight, const void* scales, c
     // NBW = 7: four stages spill; 64-row tiles with the folded scale keep a
     // fifth, since each step must land one step earlier to be scaled
     constexpr int S = NBW >= 7 ? AWQ_GEMM_S7 : (SC && GMT == 64) ? kGemmStages + 1 : kGemmStages;
-    static_assert(!SC || (4 * GMT / 16 / WV) % (GMT == 64 || NBW >= 7 ? 4 : (NBW <= 2 ? 1 : 2)) == 0, "chunk groups");
     const int nT = ((N + 16 * NBW * WV - 1) / (16 * NBW * WV)) * ((M + GMT - 1) / GMT);
     const size_t lds = (size_t)S * GMT * w4::ROW_BYTES + (SC ? (size_t)S * WV * 512 : 0);
     auto kern = group_size == 64
