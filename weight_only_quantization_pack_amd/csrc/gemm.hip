@@ -331,6 +331,13 @@ __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
     constexpr int WQ = BITS == 4 ? 4 : 3;              // words per lane slot
     // loads per step and wave: A, B tiles, D and z words (and with SC the inv_s copy)
     constexpr int LPS = FRL + 3 * NBW + (SC ? 1 : 0);
+    // 8 x 2 tiles spread the next step's loads over the substeps, the
+    // others issue them as one unit before the compute: the folded-scale
+    // form waits for step kt + 1 inside the substeps; 8 x 3 spills when
+    // spread; 4 x 7 measured no faster and 64-row tiles slower (one wave per
+    // SIMD: a wave stalled on the memory pipeline leaves its SIMD's MFMA
+    // unit idle whichever substep it stalls in)
+    constexpr bool SPREAD = !SC && GMT == 128 && NBW == 2 && WV == 8;
     static_assert(LPS * (S - 2) <= 63, "vmcnt counts to 63");
     struct BStage { uint32_t q[NBW][WQ]; uint32_t d[NBW], z[NBW]; };
     // part p (0..NBW-1) of step kt's loads: the A row groups i with
@@ -547,11 +554,22 @@ __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
             // drain the later steps' direct-to-LDS loads (vmcnt(0))
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
-            issue(kt + S - 1, (st + S - 1) % S, bs[(st + S - 1) % S]);
+            const int ls = (st + S - 1) % S;       // the slot step kt + S - 1 loads into
+            if constexpr (!SPREAD) issue(kt + S - 1, ls, bs[ls]);
             __builtin_amdgcn_sched_barrier(0);
             // the last round may run past G: those steps keep the load stream
             // (and so the compiler's wait counts) uniform but compute nothing
             auto mid = [&](int s) {
+                if constexpr (SPREAD) {
+                    // part p of step kt + S - 1's loads right behind substep
+                    // 4 p / NBW's MFMAs: the wave's wait for the shared memory
+                    // pipeline then passes while those MFMAs execute
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int p = 0; p < NBW; ++p)
+                        if (p * 4 / NBW == s) issue_part(kt + S - 1, ls, bs[ls], p);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 if constexpr (SC) {
                     // step kt + 1 has landed once at most the S - 2 steps after it
                     // are in flight.  8 x 2 tiles scale one chunk after each
@@ -572,7 +590,11 @@ __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
                     }
                 }
             };
-            if (kt < NGS) compute(bs[st], As + st * ABUFT, mid);
+            if (kt < NGS) {
+                compute(bs[st], As + st * ABUFT, mid);
+            } else if constexpr (SPREAD) {
+                issue(kt + S - 1, ls, bs[ls]);
+            }
         }
         kt0 += S;
     } while (kt0 < NGS);
@@ -708,19 +730,24 @@ __global__ __launch_bounds__(64 * WV, 1) void k_loss_gemm_p(
         brow[c] = Dz + (size_t)blk * G * 2048 + lane * 8;
     }
     struct BStage { half8_t b[NBW][4]; };
-    auto issue = [&](int kt, int slot, BStage& bs) {
+    // part p (0..3) of step kt's loads: the X row groups i with i * 4 / FRL == p
+    // (direct to LDS buffer `slot`) and the k32 step p of every D block
+    auto issue_part = [&](int kt, int slot, BStage& bs, int p) {
         const uint32_t g = (uint32_t)min(kt, G - 1);
 #pragma unroll
         for (int i = 0; i < FRL; ++i) {
+            if (i * 4 / FRL != p) continue;
             const int rg = wave * FRL + i;
             __builtin_amdgcn_global_load_lds((global_void_t*)(x + a_off[i] + g * GK),
                                              (lds_void_t*)(As + slot * ABUFT + rg * 1024), 16, 0, 0);
         }
 #pragma unroll
         for (int c = 0; c < NBW; ++c)
+            bs.b[c][p] = *reinterpret_cast<const half8_t*>(brow[c] + g * 2048 + 512 * p);
+    };
+    auto issue = [&](int kt, int slot, BStage& bs) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                bs.b[c][q] = *reinterpret_cast<const half8_t*>(brow[c] + g * 2048 + 512 * q);
+        for (int p = 0; p < 4; ++p) issue_part(kt, slot, bs, p);
     };
 
     float4_t acc[FR][NBW];
@@ -729,7 +756,8 @@ __global__ __launch_bounds__(64 * WV, 1) void k_loss_gemm_p(
 #pragma unroll
         for (int c = 0; c < NBW; ++c) acc[i][c] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const BStage& bs, const unsigned char* abuf) {
+    // mid(q) runs after substep q's MFMAs have issued
+    auto compute = [&](const BStage& bs, const unsigned char* abuf, auto&& mid) {
         auto read_a = [&](int q, half8_t* a) {
             const int kc = 4 * hq + q;
 #pragma unroll
@@ -749,6 +777,7 @@ __global__ __launch_bounds__(64 * WV, 1) void k_loss_gemm_p(
 #pragma unroll
                 for (int c = 0; c < NBW; ++c)
                     acc[i][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bs.b[c][q], a_cur[i], acc[i][c], 0, 0, 0);
+            mid(q);
             if (q < 3) {
 #pragma unroll
                 for (int i = 0; i < FR; ++i) a_cur[i] = a_nxt[i];
@@ -771,9 +800,17 @@ __global__ __launch_bounds__(64 * WV, 1) void k_loss_gemm_p(
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS * (S - 2)));
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             __builtin_amdgcn_sched_barrier(0);
-            issue(kt + S - 1, (st + S - 1) % S, bs[(st + S - 1) % S]);
-            __builtin_amdgcn_sched_barrier(0);
-            if (kt < G) compute(bs[st], As + st * ABUFT);
+            // step kt + S - 1's loads, part q right behind substep q's MFMAs:
+            // a wave's wait for the shared memory pipeline then passes while
+            // those MFMAs execute (steps past G keep the load stream uniform)
+            const int ls = (st + S - 1) % S;
+            auto mid = [&](int q) {
+                __builtin_amdgcn_sched_barrier(0);
+                issue_part(kt + S - 1, ls, bs[ls], q);
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            if (kt < G) compute(bs[st], As + st * ABUFT, mid);
+            else issue(kt + S - 1, ls, bs[ls]);
         }
         kt0 += S;
     } while (kt0 < G);
