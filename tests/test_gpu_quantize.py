@@ -107,6 +107,45 @@ def test_exact_half_integer_quotients(gpu, bits):
     _check_rows(W16, None, bits)
 
 
+def boundary_groups(bits, zero_point, group_size, n_rows=96, seed=21):
+    """Rows whose first group puts the scale quotient (hi - lo) / Q (or
+    max |v| / (2^(b-1) - 1)) within -64 .. +63 fp32 ulps of an fp16 value, and
+    (zero point) -lo / D near a half-integer: the activation scale of column
+    c of that group is 1 + (c - 64) 2^-23, and each row's extreme weights
+    (exact fp16 multiples of an fp16 value g) sit in random columns.  The
+    quantizer decides these from a reciprocal and falls back to a division
+    only near such boundaries, so the fallback windows are crossed here."""
+    Q = 2 ** bits - 1
+    den = Q if zero_point else (Q - 1) // 2
+    K = 2 * 128
+    rng = np.random.default_rng(seed)
+    W = WL.random_weights(n_rows, K, seed=seed).astype(np.float64)
+    W[:, :group_size] = 0.0
+    s = np.ones(K, np.float32)
+    s[:group_size] = (1.0 + (np.arange(group_size) - group_size // 2) * 2.0 ** -23).astype(np.float32)
+    for n in range(n_rows):
+        # g: 6 significant bits, in [2^-11, 2^3), so den g and (k + 1/2) g are exact fp16
+        g = (32 + int(rng.integers(0, 32))) * 2.0 ** int(rng.integers(-16, -2))
+        c1, c2 = rng.choice(group_size, 2, replace=False)
+        if zero_point and n % 2:
+            k = int(rng.integers(0, Q))
+            W[n, c2] = -(k + 0.5) * g
+            W[n, c1] = (Q - k - 0.5) * g
+        else:
+            W[n, c1] = den * g
+    W16 = W.astype(np.float16)
+    assert np.array_equal(W16[:, :group_size].astype(np.float64), W[:, :group_size])
+    return W16, s
+
+
+@pytest.mark.parametrize("group_size", [128, 64])
+@pytest.mark.parametrize("zero_point", [True, False])
+@pytest.mark.parametrize("bits", [4, 3])
+def test_scale_and_zero_near_rounding_boundaries(gpu, bits, zero_point, group_size):
+    W, s = boundary_groups(bits, zero_point, group_size)
+    _check_rows(W, s, bits, zero_point=zero_point, group_size=group_size)
+
+
 @pytest.mark.parametrize("shape_index", [0, 1, 2])
 def test_workload2_full_size(gpu, shape_index):
     W = WL.workload(2).weights(shape_index)

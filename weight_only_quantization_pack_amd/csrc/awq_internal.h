@@ -75,13 +75,41 @@ __device__ __forceinline__ void int4_word_pairs(uint32_t w, uint32_t p[4]) {
 }
 
 // Group parameters of one quantization group from its (already reduced)
-// minimum and maximum of v = w * s.  All IEEE fp32, correctly rounded
-// division, round-half-even rint.
+// minimum and maximum of v = w * s.  Every result is the one IEEE fp32
+// arithmetic gives (correctly rounded division, round-half-even rint); the
+// divisions are replaced by multiplications where the result provably
+// cannot differ, with the division kept for the rare lanes near a rounding
+// boundary.
 struct GroupParams {
     float delta;       // D as fp32 (exactly the stored fp16 value)
     float zero;        // integer zero point z, as fp32
+    float rd;          // 1 / D within 1 fp32 ulp (v_rcp_f32)
     uint16_t dbits;    // the stored fp16 scale
 };
+
+// f16_bits_round_down(fp32(num / DEN)) for positive finite num.  m = num *
+// fp32(1 / DEN) is within 2^-23 relative (under 2 ulp) of the exact quotient
+// and its fp32 rounding within 2.5 ulp, so when m is in fp16's normal range
+// and more than 8 fp32 ulps from every fp16 value (the 13 bits below fp16's
+// precision not within 8 of 0 or 2^13; a binade edge at most doubles the
+// distance in m's ulps) both round down to the same fp16.  Lanes outside that
+// (rare: one ballot) divide.
+template <int DEN>
+__device__ __forceinline__ uint16_t f16_down_quotient(float num) {
+    float m = num * (1.0f / (float)DEN);
+    const uint32_t low = __builtin_bit_cast(uint32_t, m) & 0x1FFFu;
+    const bool slow = !(m >= 0x1p-14f && m < 0x1p15f) || low < 8u || low > 0x1FF8u;
+    if (__builtin_amdgcn_ballot_w64(slow)) {
+        if (slow) {
+            // an opaque copy keeps the division inside this branch (the
+            // compiler otherwise computes it on every lane and selects)
+            float n = num;
+            asm volatile("" : "+v"(n));
+            m = n / (float)DEN;
+        }
+    }
+    return f16_bits_round_down(m);
+}
 
 // Scale and zero point of a group from its min and max (fp32, IEEE).
 // zero_point (asymmetric): range widened to contain 0, D = largest fp16 <=
@@ -89,23 +117,32 @@ struct GroupParams {
 // (zero_point false, "Quantizing a model with AutoAWQ"): D = largest fp16 <=
 // max(max |v|, 1e-5) / (2^(b-1) - 1) and the fixed z = 2^(b-1), so codes
 // rint(v / D) + z keep the same unsigned storage and (q - z) * D dequant.
+// z is decided in fixed point as the codes are (quant_codes_b2): 0 <= -lo / D
+// <= Q / (1 - 2^-10) < 16.4, so t = -lo * (1/D) + 128.5 + 3 * 2^-16 lies in
+// [128, 256) with its integer part minus 128 in bits 16..22; a fraction of at
+// least 6 * 2^-16 decides rint(-lo / D) (the argument of quant_codes_b2).
 template <int Q, bool ZP>
 __device__ __forceinline__ GroupParams group_params(float vmin, float vmax) {
     GroupParams p;
     if constexpr (ZP) {
-        float lo = fminf(vmin, 0.0f);
-        float hi = fmaxf(vmax, 0.0f);
-        float span = fmaxf(hi - lo, 1e-5f);
-        float d32 = span / (float)Q;
-        p.dbits = f16_bits_round_down(d32);
+        const float lo = fminf(vmin, 0.0f);
+        const float hi = fmaxf(vmax, 0.0f);
+        const float span = fmaxf(hi - lo, 1e-5f);
+        p.dbits = f16_down_quotient<Q>(span);
         p.delta = (float)bits_half(p.dbits);
-        float z = __builtin_rintf(-lo / p.delta);
+        p.rd = __builtin_amdgcn_rcpf(p.delta);
+        const uint32_t T = __builtin_bit_cast(uint32_t, __builtin_fmaf(-lo, p.rd, 128.5f + 0x3p-16f));
+        const bool near = (T & 0xFFFFu) <= 5u;
+        float z = (float)((T >> 16) & 0xFFu);
+        if (__builtin_amdgcn_ballot_w64(near)) {
+            if (near) z = __builtin_rintf(-lo / p.delta);
+        }
         p.zero = fminf(fmaxf(z, 0.0f), (float)Q);
     } else {
         const float amax = fmaxf(fmaxf(-vmin, vmax), 1e-5f);   // max |v|: negation is exact
-        const float d32 = amax / (float)((Q - 1) / 2);
-        p.dbits = f16_bits_round_down(d32);
+        p.dbits = f16_down_quotient<(Q - 1) / 2>(amax);
         p.delta = (float)bits_half(p.dbits);
+        p.rd = __builtin_amdgcn_rcpf(p.delta);
         p.zero = (float)((Q + 1) / 2);
     }
     return p;
@@ -130,8 +167,9 @@ constexpr unsigned vmcnt_imm(unsigned n) { return (n & 15u) | ((n >> 4) << 14) |
 // rounding instruction.  One fma forms t = v * (1/D) + (z + 128.5 + 3 * 2^-16),
 // clamped to [128.25, 128.5 + Q]; there fp32 values are multiples of 2^-16,
 // so the float's bits 16..22 hold the integer part of t - 128 and bits 0..15
-// its fraction F.  t is within 2^-17 (the fma's rounding) + 16.4 * 2^-24 (that
-// of 1/D, |v / D| <= 16.4) < 0.64 * 2^-16 of v / D + z + 1/2 + 3 * 2^-16, so
+// its fraction F.  t is within 2^-17 (the fma's rounding) + 16.4 * 2^-23 (1/D
+// from v_rcp_f32, within 1 ulp; |v / D| <= 16.4) < 0.63 * 2^-16 of
+// v / D + z + 1/2 + 3 * 2^-16, so
 // F >= 6 * 2^-16 puts v / D + z more than 2.3 * 2^-16 above and 1/2 - 6 * 2^-16
 // below a half-integer: its integer part is then rint(v / D) + z for the
 // exact quotient and for its rounding to fp32 (within 2^-20) alike, with no
@@ -140,7 +178,7 @@ constexpr unsigned vmcnt_imm(unsigned n) { return (n & 15u) | ((n >> 4) << 14) |
 // (rare: one ballot) take quant_code's division for all their values.
 template <int Q, int NV>
 __device__ __forceinline__ void quant_codes_b2(const float* v, const GroupParams& p, uint32_t* T) {
-    const float rd = 1.0f / p.delta;
+    const float rd = p.rd;
     const float zb = p.zero + (128.5f + 0x3p-16f);   // exact: z <= 15
     uint32_t fmin = 0xFFFFu;                          // least fraction F, in units of 2^-16
 #pragma unroll
