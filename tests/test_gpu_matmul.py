@@ -145,7 +145,8 @@ def test_gemv_x1_twelve_loads(gpu, M, N, K, bits, group_size):
     ("gemv", 1, 300, 4096),        # x staged once, short rows (ring of 2)
     ("gemv", 4, 130, 11008),       # 4 x 11008 > 32K halves: K in slices, ragged last slice
     ("gemv", 16, 1000, 2048),      # K slices, one 16-group slice
-    ("gemm", 5, 302, 2048),        # split K
+    ("gemm", 5, 302, 2048),        # split K, 16-row tiles
+    ("gemm", 20, 302, 2048),       # split K, 32-row tiles
     ("gemm", 257, 200, 1152),      # several M tiles, no split
 ])
 def test_group64_matmuls(gpu, fn, M, N, K, bits):
@@ -207,6 +208,26 @@ def test_gemm_split_k(gpu, M, N, K, bits):
         assert err <= TOL, f"split_k={split}: rel err {err:.3e}"
 
 
+@pytest.mark.parametrize("bits", [4, 3])
+@pytest.mark.parametrize("M", [16, 17, 24, 32, 33])
+@pytest.mark.parametrize("N,K", [(302, 2048), (1000, 1152)])
+def test_gemm_row_tile_heights(gpu, M, N, K, bits):
+    """The pipelined kernel's 16-, 32- and 64-row tiles around their limits
+    (M = 16 | 17, 32 | 33; M = 24 leaves 8 padding rows in a 32-row tile),
+    with and without the K split, whole output."""
+    import torch
+    qw, d, z = packed(WL.random_weights(N, K, seed=N + K + M), bits)
+    x = WL.random_activations(M, K, seed=M + 11, sigma=1.0)
+    announce("gemm row tiles", f"M={M} N={N} K={K} bits={bits}")
+    y_ref = O.matmul(x, qw, d, z, bits, K)
+    args = (dev(x), dev(qw.reshape(-1)), dev(O.tile_params(d)), dev(O.tile_params(z)))
+    for split in (True, False):
+        y = awq.gemm(*args, N=N, bits=bits, split_k=split)
+        torch.cuda.synchronize()
+        err = rel_err(host(y).astype(np.float64), y_ref)
+        assert err <= TOL, f"split_k={split}: rel err {err:.3e}"
+
+
 @pytest.mark.parametrize("shape_index", [0, 1, 2])
 @pytest.mark.parametrize("M", [512, 2048])
 def test_gemm_workload4_full(gpu, M, shape_index):
@@ -219,12 +240,14 @@ def test_gemm_workload4_full(gpu, M, shape_index):
 
 
 @pytest.mark.parametrize("shape_index", [0, 1])
-def test_gemm_workload3_m64_full(gpu, shape_index):
-    """Llama-70B MLP shapes at M = 64 (64-row tiles, split K), whole tensor."""
+@pytest.mark.parametrize("M", [64, 16])
+def test_gemm_workload3_full(gpu, M, shape_index):
+    """Llama-70B MLP shapes at M = 64 and 16 (64- and 16-row tiles, split
+    K), whole tensor."""
     wl = WL.workload(3)
     K, N = wl.shapes[shape_index]
-    check("gemm", 64, N, K, 4, seed=0, layer=workload_layer(3, shape_index),
-          x=wl.activations(64, shape_index))
+    check("gemm", M, N, K, 4, seed=0, layer=workload_layer(3, shape_index),
+          x=wl.activations(M, shape_index))
 
 
 # ----------------------------------------------------------------------------- exact cases
@@ -292,12 +315,14 @@ def test_empty_calls(gpu, fn):
 
 # ----------------------------------------------------------------------------- folded scale (prefill)
 # (M, N, K): every tile form of the pipelined kernel with the scale folded into
-# its activation tiles -- 64-row tiles with split K (M = 5, 64), 128-row 8 x 2
+# its activation tiles -- 16-, 32- and 64-row tiles with split K (M = 5, 17,
+# 32, 64), 128-row 8 x 2
 # tiles with a ragged split (130 x 200 x 4736: 37 groups in splits of 10, 10,
 # 10, 7), several row tiles, 4 x 7 (N = 14296) and 8 x 3 (N = 6100) wide tiles
 # with ragged edges, and N = 8192 at M = 2048, where awq_gemm takes the
 # two-workgroups-per-CU kernel but the scaled product the 8 x 2 tiles
-SCALED_GEMM = [(5, 302, 2048), (64, 1000, 8192), (130, 200, 4736), (257, 600, 1152),
+SCALED_GEMM = [(5, 302, 2048), (17, 302, 2048), (32, 1000, 4736), (64, 1000, 8192), (130, 200, 4736),
+               (257, 600, 1152),
                (2048, 14296, 1024), (1999, 6100, 1024), (2048, 8192, 1024)]
 
 

@@ -60,6 +60,18 @@ namespace {
 #define AWQ_GEMM_ILV 7
 #endif
 
+// raw buffer resource over `bytes` bytes (byte offsets, range-checked)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from buffer byte offset voff + soff straight into LDS at
+// lds + 16 * lane (a direct-to-LDS buffer load)
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, uint32_t voff,
+                                                  uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 __device__ __forceinline__ uint32_t as_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
 
@@ -284,7 +296,7 @@ __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
     _Float16* __restrict__ Y, float* __restrict__ part, const float* __restrict__ inv_s,
     int M, int N, int K, int gsplit) {
     using namespace w4;
-    static_assert(GMT == 128 || GMT == 64, "128- or 64-row tiles");
+    static_assert(GMT == 128 || GMT == 64 || GMT == 32 || GMT == 16, "16- to 128-row tiles");
     constexpr int FR = GMT / 16;                       // 16-row A fragments (and row groups per wave)
     constexpr int ABUFT = GMT * ROW_BYTES;             // one A buffer
     constexpr int TN = 16 * NBW * WV;                  // tile columns: NBW 16-column blocks per wave
@@ -329,6 +341,18 @@ __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
     const uint32_t pgrp = GS == 64 ? (uint32_t)(hq >> 1) : 0u;
 
     constexpr int WQ = BITS == 4 ? 4 : 3;              // words per lane slot
+    // Every load is a buffer load whose per-lane byte offset is fixed for the
+    // whole K loop and whose step-dependent part (group, tile) is wave-uniform
+    // and goes in the scalar offset: no per-step vector address arithmetic.
+    const uint32_t tiles_all = (uint32_t)NB * (uint32_t)G;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qw, tiles_all * 256u * WQ);
+    // scales / zeros: kGroup / GS groups of 16 fp16 values per tile
+    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(scales, tiles_all * (32u * kGroup / GS));
+    const __amdgpu_buffer_rsrc_t rze = make_rsrc(zeros, tiles_all * (32u * kGroup / GS));
+    const __amdgpu_buffer_rsrc_t ris = make_rsrc(inv_s, SC ? (uint32_t)K * 4u : 0u);
+    const uint32_t q_voff = 4u * WQ * (uint32_t)lane;
+    const uint32_t p_voff = 2u * (pgrp * 16u + (uint32_t)(j & ~1));
     // loads per step and wave: A, B tiles, D and z words (and with SC the inv_s copy)
     constexpr int LPS = FRL + 3 * NBW + (SC ? 1 : 0);
     // 8 x 2 tiles spread the next step's loads over the substeps, the
@@ -346,30 +370,25 @@ __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
     auto issue_part = [&](int kt, int slot, BStage& bs, int p) {
         const uint32_t g = (uint32_t)(g_begin + min(kt, NGS - 1));
         if constexpr (SC) {
-            // the step's 128 inv_s values into this wave's own copy (32 lanes x 16 B)
             if (p == 0 && lane < 32)
-                __builtin_amdgcn_global_load_lds((global_void_t*)(inv_s + g * GK + 4u * lane),
-                                                 (lds_void_t*)(isb_base + (slot * WV + wave) * 512), 16, 0, 0);
+                buffer_load_lds16(ris, isb_base + (slot * WV + wave) * 512, 16u * (uint32_t)lane, g * GK * 4u);
         }
 #pragma unroll
         for (int i = 0; i < FRL; ++i) {
             if (i * NBW / FRL != p) continue;
             const int rg = wave * FRL + i;
-            __builtin_amdgcn_global_load_lds((global_void_t*)(x + a_off[i] + g * GK),
-                                             (lds_void_t*)(As + slot * ABUFT + rg * 1024), 16, 0, 0);
+            buffer_load_lds16(rx, As + slot * ABUFT + rg * 1024, 2u * a_off[i], g * GK * 2u);
         }
         const uint32_t tt = tbase[p] + g;
-        // one dwordx4 (int4) or dwordx3 (int3) load: 20 loads per step either way
         if constexpr (BITS == 4) {
-            const uint4 v = *reinterpret_cast<const uint4*>(qw + (size_t)(tt * 256u + 4u * lane));
-            bs.q[p][0] = v.x; bs.q[p][1] = v.y; bs.q[p][2] = v.z; bs.q[p][3] = v.w;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rq, q_voff, tt * 1024u, 0);
+            bs.q[p][0] = v[0]; bs.q[p][1] = v[1]; bs.q[p][2] = v[2]; bs.q[p][3] = v[3];
         } else {
-            const uint3 v = *reinterpret_cast<const uint3*>(qw + (size_t)(tt * 192u + 3u * lane));
-            bs.q[p][0] = v.x; bs.q[p][1] = v.y; bs.q[p][2] = v.z;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b96(rq, q_voff, tt * 768u, 0);
+            bs.q[p][0] = v[0]; bs.q[p][1] = v[1]; bs.q[p][2] = v[2];
         }
-        const uint32_t pidx = (tt * (kGroup / GS) + pgrp) * 16u + (uint32_t)(j & ~1);
-        bs.d[p] = *reinterpret_cast<const uint32_t*>(scales + pidx);
-        bs.z[p] = *reinterpret_cast<const uint32_t*>(zeros + pidx);
+        bs.d[p] = __builtin_amdgcn_raw_buffer_load_b32(rsc, p_voff, tt * (kGroup / GS) * 32u, 0);
+        bs.z[p] = __builtin_amdgcn_raw_buffer_load_b32(rze, p_voff, tt * (kGroup / GS) * 32u, 0);
     };
     auto issue = [&](int kt, int slot, BStage& bs) {
 #pragma unroll
@@ -901,9 +920,11 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
 
 constexpr int kGemmStages = 4;
 
-// tile height of the pipelined kernel: 64 rows while M fits in one such tile
-// row (half of a 128-row tile would multiply padding rows), else 128
-int w4p_rows(int M) { return M <= 64 ? 64 : 128; }
+// tile height of the pipelined kernel: the smallest of 16, 32 and 64 rows
+// that holds M (a taller tile would spend its MFMAs and A reads on padding
+// rows; MI355X, Llama-70B MLP shapes with split K, cold: M = 16 52-56 ->
+// 34-35 us, M = 32 54 -> 43-44 us against 64-row tiles), else 128
+int w4p_rows(int M) { return M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128; }
 
 int w4p_tiles(int M, int N, int nbw = 4) {
     const int rows = w4p_rows(M);
@@ -949,14 +970,24 @@ int launch_w4p_rows(const void* x, const void* qweight, const void* scales, cons
 // gemm_tile_choice).  256 and 384 columns run as 8 waves of 2 or 3 16-column
 // blocks (two waves per SIMD hide each other's waits: MI355X, M = 2048,
 // 14336x4096 877-886 -> 890-919 TFLOP/s, 4096x6144 919-942 -> 960-986),
-// 448 columns as 4 waves of 7 (8 waves cannot split it).  64-row tiles take
-// 4 waves of 4 blocks.
+// 448 columns as 4 waves of 7 (8 waves cannot split it).  16-, 32- and
+// 64-row tiles take 4 waves of 4 blocks.
 int launch_w4p(const void* x, const void* qweight, const void* scales, const void* zeros, void* y,
                float* part, const float* inv_s, int M, int N, int K, int bits, int group_size,
                int splits, int gsplit, hipStream_t st, int nbw = 4) {
-    if (w4p_rows(M) == 64)
-        return launch_w4p_rows<64, 4>(x, qweight, scales, zeros, y, part, inv_s, M, N, K, bits,
-                                      group_size, splits, gsplit, st);
+    switch (w4p_rows(M)) {
+    case 16:
+        return launch_w4p_rows<16, 4>(x, qweight, scales, zeros, y, part, inv_s, M, N, K, bits, group_size,
+                                      splits, gsplit, st);
+    case 32:
+        return launch_w4p_rows<32, 4>(x, qweight, scales, zeros, y, part, inv_s, M, N, K, bits, group_size,
+                                      splits, gsplit, st);
+    case 64:
+        return launch_w4p_rows<64, 4>(x, qweight, scales, zeros, y, part, inv_s, M, N, K, bits, group_size,
+                                      splits, gsplit, st);
+    default:
+        break;
+    }
     if (nbw == 6)
         return launch_w4p_rows<128, 3, 8>(x, qweight, scales, zeros, y, part, inv_s, M, N, K, bits,
                                           group_size, splits, gsplit, st);
@@ -979,9 +1010,9 @@ int launch_w4p(const void* x, const void* qweight, const void* scales, const voi
 // vs 828-839 TFLOP/s for the two-per-CU kernel (896 tiles) and 732-739 for
 // NBW 4 (four rounds); 4096x6144 NBW 6 (256 tiles) 989-1015 vs 862 and 717;
 // 14336x4096 NBW 4 (256 tiles) 943 vs NBW 6 775, NBW 7 670.  M <= 64
-// (64-row tiles) always takes NBW 4.
+// (16- to 64-row tiles) always takes NBW 4.
 int gemm_tile_choice(int M, int N, int bits, int group_size, int cus) {
-    if (w4p_rows(M) == 64) return 4;
+    if (w4p_rows(M) <= 64) return 4;
     int best = 4, best_cost = INT_MAX;
     for (const int nbw : {7, 6, 4}) {
         const int rounds = (w4p_tiles(M, N, nbw) + cus - 1) / cus;
