@@ -739,15 +739,22 @@ __global__ __launch_bounds__(64 * WV, 1) void k_loss_gemm_p(
     }
     // D block blk, group g: the tile at (blk G + g) 2048 halves, k32 step q at
     // + 512 q, lane 16 hq + j at + 8 lane (row j, columns 32 hq + 8 q ..)
-    const _Float16* brow[NBW];
+    // buffer loads: per-lane byte offsets fixed for the K loop, the group's
+    // offset (wave-uniform) in the scalar operand; D blocks past the rows the
+    // layer has are clamped to its last block (read, never summed)
     const int NB16 = (N + 15) / 16;
+    const int nbk = EPI == EPI_SQ ? NB16 : 2 * (out.I / 16);   // D blocks of one batch entry
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(Dz, (uint32_t)nbk * (uint32_t)G * 4096u);
+    uint32_t bblk[NBW];                                // block offset of each D block, in tiles
 #pragma unroll
     for (int c = 0; c < NBW; ++c) {
         int blk;
         if constexpr (EPI == EPI_SQ) blk = min(n0 / 16 + wave * NBW + c, NB16 - 1);
         else blk = (c == 0 ? 0 : out.I / 16) + n0 / 16 + wave;   // gate block, then the same rows of up
-        brow[c] = Dz + (size_t)blk * G * 2048 + lane * 8;
+        bblk[c] = (uint32_t)blk * (uint32_t)G;
     }
+    const uint32_t d_voff = 16u * (uint32_t)lane;
     struct BStage { half8_t b[NBW][4]; };
     // part p (0..3) of step kt's loads: the X row groups i with i * 4 / FRL == p
     // (direct to LDS buffer `slot`) and the k32 step p of every D block
@@ -757,12 +764,13 @@ __global__ __launch_bounds__(64 * WV, 1) void k_loss_gemm_p(
         for (int i = 0; i < FRL; ++i) {
             if (i * 4 / FRL != p) continue;
             const int rg = wave * FRL + i;
-            __builtin_amdgcn_global_load_lds((global_void_t*)(x + a_off[i] + g * GK),
-                                             (lds_void_t*)(As + slot * ABUFT + rg * 1024), 16, 0, 0);
+            buffer_load_lds16(rx, As + slot * ABUFT + rg * 1024, 2u * a_off[i], g * GK * 2u);
         }
 #pragma unroll
-        for (int c = 0; c < NBW; ++c)
-            bs.b[c][p] = *reinterpret_cast<const half8_t*>(brow[c] + g * 2048 + 512 * p);
+        for (int c = 0; c < NBW; ++c) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rd, d_voff, (bblk[c] + g) * 4096u + 1024u * p, 0);
+            bs.b[c][p] = __builtin_bit_cast(half8_t, v);
+        }
     };
     auto issue = [&](int kt, int slot, BStage& bs) {
 #pragma unroll
@@ -1101,6 +1109,10 @@ namespace {
 template <int EPI>
 int launch_loss_kernel(const void* X, long long a_stride, const void* D, long long d_stride, int T,
                        int N, int K, int n_batch, const LossOut& out, hipStream_t st) {
+    // the kernel addresses one batch entry of D and of X with 32-bit byte offsets
+    const size_t d_rows = EPI == EPI_SQ ? (size_t)(N + 15) / 16 * 16 : 2 * (size_t)out.I;
+    if (d_rows * (size_t)K * 2 >= (1ull << 32) || (size_t)T * (size_t)K * 2 >= (1ull << 32))
+        return (int)hipErrorInvalidValue;
     auto kern = k_loss_gemm_p<kLossS, kLossNBW, kLossWV, EPI>;
     const size_t lds = (size_t)kLossS * 128 * w4::ROW_BYTES;
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
