@@ -355,13 +355,16 @@ __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
     const uint32_t p_voff = 2u * (pgrp * 16u + (uint32_t)(j & ~1));
     // loads per step and wave: A, B tiles, D and z words (and with SC the inv_s copy)
     constexpr int LPS = FRL + 3 * NBW + (SC ? 1 : 0);
-    // 8 x 2 tiles spread the next step's loads over the substeps, the
-    // others issue them as one unit before the compute: the folded-scale
-    // form waits for step kt + 1 inside the substeps; 8 x 3 spills when
-    // spread; 4 x 7 measured no faster and 64-row tiles slower (one wave per
-    // SIMD: a wave stalled on the memory pipeline leaves its SIMD's MFMA
-    // unit idle whichever substep it stalls in)
-    constexpr bool SPREAD = !SC && GMT == 128 && NBW == 2 && WV == 8;
+    // the 128-row tiles spread the next step's loads over the substeps
+    // (part p behind substep 4 p / NBW), the others issue them as one unit
+    // before the compute: the folded-scale form waits for step kt + 1 inside
+    // the substeps, and 64-row tiles measured 5 % slower spread (one wave per
+    // SIMD: a wave stalled on the memory pipeline leaves its SIMD's MFMA unit
+    // idle whichever substep it stalls in).  MI355X, M = 2048: 8 x 2 (14336 x
+    // 4096) 231-236 -> 221-228 us; with the buffer loads' freed registers
+    // also 4 x 7 (4096 x 14336, 1023 -> 1073-1079 TFLOP/s) and 8 x 3 at three
+    // stages (4096 x 6144, 991 -> 1025-1031; four stages spill when spread)
+    constexpr bool SPREAD = !SC && GMT == 128;
     static_assert(LPS * (S - 2) <= 63, "vmcnt counts to 63");
     struct BStage { uint32_t q[NBW][WQ]; uint32_t d[NBW], z[NBW]; };
     // part p (0..NBW-1) of step kt's loads: the A row groups i with
@@ -948,7 +951,10 @@ int launch_w4p_rows_sc(const void* x, const void* qweight, const void* scales, c
 #endif
     // NBW = 7: four stages spill; 64-row tiles with the folded scale keep a
     // fifth, since each step must land one step earlier to be scaled
-    constexpr int S = NBW >= 7 ? AWQ_GEMM_S7 : (SC && GMT == 64) ? kGemmStages + 1 : kGemmStages;
+    // 8 x 3 tiles with their loads spread over the substeps: three stages
+    // (four spill)
+    constexpr int S = NBW >= 7 ? AWQ_GEMM_S7 : (SC && GMT == 64) ? kGemmStages + 1
+                    : (NBW == 3 && !SC) ? kGemmStages - 1 : kGemmStages;
     const int nT = ((N + 16 * NBW * WV - 1) / (16 * NBW * WV)) * ((M + GMT - 1) / GMT);
     const size_t lds = (size_t)S * GMT * w4::ROW_BYTES + (SC ? (size_t)S * WV * 512 : 0);
     auto kern = group_size == 64
