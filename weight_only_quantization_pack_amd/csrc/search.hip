@@ -36,13 +36,18 @@ size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // The loss runs one of two ways: a separate error kernel writing D for every
 // alpha into the workspace plus a dense loss GEMM (the default: fastest, needs
-// n_alpha * N * K * 2 bytes, N rounded up to 16), or one fused kernel forming D
+// one chunk of alphas' D, N rounded up to 16), or one fused kernel forming D
 // in registers (a workspace of under a megabyte; MI355X, 4096 x 4096, T = 512,
-// 20 alphas: 0.85-0.88 ms against 0.70-0.71 ms, since forming D there does not
-// overlap its MFMAs).
-constexpr int kFusedT = 256;            // calibration rows per workgroup of the fused loss
+// 20 alphas: 0.73 ms against 0.65-0.68 ms median, since forming D there does
+// not overlap its MFMAs).  The fused kernel's workgroup takes 512 calibration
+// rows and one 16-row tile of W per wave, so every D value is formed once per
+// alpha (256 rows and two tiles per wave, which forms each D twice at T = 512:
+// 0.82 ms; 256 rows and one tile: 0.98 ms)
+constexpr int kFusedT = 512;            // calibration rows per workgroup of the fused loss
+constexpr int kFusedNT = 1;             // 16-row tiles of W per wave (4 waves)
+constexpr int kFusedRows = 64 * kFusedNT;
 size_t fused_tiles(int T, int N) {
-    return (size_t)((N + 127) / 128) * (size_t)((T + kFusedT - 1) / kFusedT);
+    return (size_t)((N + kFusedRows - 1) / kFusedRows) * (size_t)((T + kFusedT - 1) / kFusedT);
 }
 
 // The default path runs the alpha grid in chunks whose error matrices D fit
@@ -209,19 +214,19 @@ __global__ __launch_bounds__(256) void k_quant_err(LayerList layers,
 
 // Fused loss (the error matrix D_alpha = W - w_hat_alpha / s_alpha never goes
 // to memory): L_alpha * T * N = sum over (t, n) of (X D_alpha^T)[t][n]^2.  A
-// workgroup owns 128 rows of W (32 per wave, two 16-row MFMA B tiles) and up
-// to 512 calibration rows for one alpha, so every D value is formed once per
-// alpha: each wave builds its D fragments in registers in the B-operand layout
-// of v_mfma_f32_16x16x32_f16 (lane (j, q) holds row j's k = 32 s + 8 q + e of
+// workgroup owns 64 rows of W (one 16-row MFMA B tile per wave) and up to 512
+// calibration rows for one alpha, so every D value is formed once per alpha:
+// each wave builds its D fragments in registers in the B-operand layout of
+// v_mfma_f32_16x16x32_f16 (lane (j, q) holds row j's k = 32 s + 8 q + e of
 // substep s), quantizing the group from W, s and 1/s with the codes of
 // quant_codes_b2, exactly as the separate error kernel does.  X streams
-// through LDS in 64-k steps (256 rows x 128 B, two buffers, direct-to-LDS
+// through LDS in 64-k steps (512 rows x 128 B, two buffers, direct-to-LDS
 // loads, chunk p of row r holding global chunk p ^ (r & 7), which the
-// A-fragment reads see free of bank conflicts on MI355X); W, s and 1/s of the
-// next group are loaded into registers one group ahead.  The 64 x 2 MFMA
-// accumulators of a lane (128 fp32) live in AGPRs.  The epilogue squares and
-// sums the outputs of rows < T and columns < N in fp32 per lane, then in fp64
-// in a fixed order, into one partial per workgroup.
+// A-fragment reads see free of bank conflicts on MI355X); W of the next group
+// is loaded into registers one group ahead, its s and 1/s into LDS.  The 32
+// MFMA accumulators of a lane (128 fp32) live in AGPRs.  The epilogue squares
+// and sums the outputs of rows < T and columns < N in fp32 per lane, then in
+// fp64 in a fixed order, into one partial per workgroup.
 namespace lf {
 constexpr int kT = kFusedT;             // calibration rows per workgroup
 constexpr int kFR = kT / 16;            // X fragments per substep
@@ -229,7 +234,7 @@ constexpr int kStepK = 64;              // k per LDS step (half a group)
 constexpr int kRow = kStepK * 2;        // bytes of one X row in LDS
 constexpr int kBuf = kT * kRow;         // 32 KB per buffer
 constexpr int kXLoads = kBuf / 1024 / 4;   // direct-to-LDS loads per wave and step (8)
-constexpr int kWLoads = 2 * 4;             // W loads per wave and group
+constexpr int kWLoads = kFusedNT * 4;      // W loads per wave and group
 }
 
 struct RowList {                        // rows of the layers searched together
@@ -245,19 +250,20 @@ __global__ __launch_bounds__(256, 1) void k_loss_fused(RowList layers, const _Fl
                                                        const float* __restrict__ s_inv,
                                                        double* __restrict__ partials) {
     static_assert(GS == 128 || GS == 64, "128- or 64-wide groups");
-    extern __shared__ __attribute__((aligned(16))) unsigned char Xs[];   // 2 x lf::kBuf
+    extern __shared__ __attribute__((aligned(16))) unsigned char Xs[];   // 2 x lf::kBuf, then the s slots
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, hq = lane >> 4;
     const int alpha = blockIdx.z;
     const int t0 = blockIdx.y * lf::kT;
     const int G = K / kGroup;
-    const int n_base = blockIdx.x * 128 + wave * 32;
+    constexpr int NT = kFusedNT;
+    const int n_base = blockIdx.x * kFusedRows + wave * 16 * NT;
 
     // this lane's W row in each of its two tiles (rows past N: row N - 1, never summed)
-    const _Float16* wrow[2];
+    const _Float16* wrow[NT];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < NT; ++c) {
         const int n = min(n_base + 16 * c + j, N - 1);
         int l = 0;
 #pragma unroll
@@ -265,8 +271,6 @@ __global__ __launch_bounds__(256, 1) void k_loss_fused(RowList layers, const _Fl
             if (m < layers.n && n >= layers.nstart[m]) l = m;
         wrow[c] = layers.w[l] + (size_t)(n - layers.nstart[l]) * K;
     }
-    const float* s_a = s_all + (size_t)alpha * K + 8 * hq;
-    const float* r_a = s_inv + (size_t)alpha * K + 8 * hq;
 
     // X: load q (0..kXLoads-1) of this wave writes rows 8 (kXLoads wave + q) .. + 7
     // of the tile, lane l row + (l >> 3), LDS chunk l & 7; rows past T read row T - 1
@@ -287,41 +291,48 @@ __global__ __launch_bounds__(256, 1) void k_loss_fused(RowList layers, const _Fl
                                              16, 0, 0);
     };
 
-    // the next group's W rows (loaded one group ahead) and its s and 1/s
-    // (loaded during the second half of the group before): value i = 8 sub + e
+    // the next group's W rows, loaded one group ahead (its s and 1/s go to
+    // LDS during the second half of the group before): value i = 8 sub + e
     // of a lane is k = 32 sub + 8 q + e of the group
-    struct PreW { uint4 w[2][4]; };
-    struct PreS { float4 s[8], r[8]; };
+    struct PreW { uint4 w[NT][4]; };
+    // s and 1/s of a group go to LDS (two slots: the group being quantized and
+    // the next), written by wave 0 with one direct-to-LDS load (lanes 0..31
+    // the 128 s values, lanes 32..63 the 128 reciprocals) and read by every
+    // wave while it forms D; registers would hold them for a whole group
+    float* const Ss = reinterpret_cast<float*>(Xs + 2 * lf::kBuf);   // [2 slots][s 128, 1/s 128]
     auto issue_w = [&](int g, PreW& p) {
         const int k0 = kGroup * min(g, G - 1);
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < NT; ++c)
 #pragma unroll
             for (int sub = 0; sub < 4; ++sub)
                 p.w[c][sub] = *reinterpret_cast<const uint4*>(wrow[c] + k0 + 32 * sub + 8 * hq);
     };
-    auto issue_s = [&](int g, PreS& p) {
+    auto issue_s = [&](int g, int slot) {
+        if (wave != 0) return;                       // wave-uniform
         const int k0 = kGroup * min(g, G - 1);
-#pragma unroll
-        for (int sub = 0; sub < 4; ++sub) {
-            p.s[2 * sub] = *reinterpret_cast<const float4*>(s_a + k0 + 32 * sub);
-            p.s[2 * sub + 1] = *reinterpret_cast<const float4*>(s_a + k0 + 32 * sub + 4);
-        }
-#pragma unroll
-        for (int sub = 0; sub < 4; ++sub) {
-            p.r[2 * sub] = *reinterpret_cast<const float4*>(r_a + k0 + 32 * sub);
-            p.r[2 * sub + 1] = *reinterpret_cast<const float4*>(r_a + k0 + 32 * sub + 4);
-        }
+        const float* src = (lane < 32 ? s_all : s_inv) + (size_t)alpha * K + k0 + 4 * (lane & 31);
+        __builtin_amdgcn_global_load_lds((global_void_t*)src, (lds_void_t*)(Ss + slot * 256), 16, 0, 0);
     };
     auto f4 = [](const float4& q, int e) { return e == 0 ? q.x : e == 1 ? q.y : e == 2 ? q.z : q.w; };
     auto wval = [](const uint4& raw, int e) {
         return (float)reinterpret_cast<const _Float16*>(&raw)[e];
     };
 
-    half8_t dfr[2][4];                   // D fragments of the current group: [tile][substep]
-    auto make_d = [&](const PreW& pw, const PreS& ps) {
+    half8_t dfr[NT][4];                  // D fragments of the current group: [tile][substep]
+    auto make_d = [&](const PreW& pw, int slot) {
+        // value i = 8 sub + e of this lane is column 32 sub + 8 hq + e of the group
+        struct { float4 s[8], r[8]; } ps;
+        const float* sl = Ss + slot * 256 + 8 * hq;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int sub = 0; sub < 4; ++sub) {
+            ps.s[2 * sub] = *reinterpret_cast<const float4*>(sl + 32 * sub);
+            ps.s[2 * sub + 1] = *reinterpret_cast<const float4*>(sl + 32 * sub + 4);
+            ps.r[2 * sub] = *reinterpret_cast<const float4*>(sl + 128 + 32 * sub);
+            ps.r[2 * sub + 1] = *reinterpret_cast<const float4*>(sl + 128 + 32 * sub + 4);
+        }
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
             float v[32];
 #pragma unroll
             for (int i = 0; i < 32; ++i) v[i] = wval(pw.w[c][i / 8], i % 8) * f4(ps.s[i / 4], i % 4);
@@ -351,9 +362,11 @@ __global__ __launch_bounds__(256, 1) void k_loss_fused(RowList layers, const _Fl
         }
     };
 
-    float4_t acc[lf::kFR][2];          // [X fragment][tile]
+    float4_t acc[lf::kFR][NT];         // [X fragment][tile]
 #pragma unroll
-    for (int i = 0; i < lf::kFR; ++i) acc[i][0] = acc[i][1] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < lf::kFR; ++i)
+#pragma unroll
+        for (int c = 0; c < NT; ++c) acc[i][c] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
     // the two substeps of one LDS step (half h of the group): X fragments in
     // batches of 8, batch b + 1 read under batch b's 16 MFMAs (a scheduling
@@ -378,19 +391,18 @@ __global__ __launch_bounds__(256, 1) void k_loss_fused(RowList layers, const _Fl
             if (b + 1 < kNB) read_batch(buf, b + 1, nxt);
             const int sub = b / (lf::kFR / kB), i0 = (b % (lf::kFR / kB)) * kB;
 #pragma unroll
-            for (int u = 0; u < kB; ++u) {
-                acc[i0 + u][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dfr[0][2 * h + sub], cur[u], acc[i0 + u][0], 0, 0, 0);
-                acc[i0 + u][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dfr[1][2 * h + sub], cur[u], acc[i0 + u][1], 0, 0, 0);
-            }
+            for (int u = 0; u < kB; ++u)
+#pragma unroll
+                for (int c = 0; c < NT; ++c)
+                    acc[i0 + u][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dfr[c][2 * h + sub], cur[u], acc[i0 + u][c], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
     PreW pw;
-    PreS ps;
     issue_x(0, 0);
     issue_w(0, pw);
-    issue_s(0, ps);
+    issue_s(0, 0);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     for (int g = 0; g < G; ++g) {
@@ -398,7 +410,7 @@ __global__ __launch_bounds__(256, 1) void k_loss_fused(RowList layers, const _Fl
         __builtin_amdgcn_sched_barrier(0);
         issue_x(2 * g + 1, 1);
         __builtin_amdgcn_sched_barrier(0);
-        make_d(pw, ps);
+        make_d(pw, g & 1);
         __builtin_amdgcn_sched_barrier(0);
         issue_w(g + 1, pw);                  // clamped past the last group: a uniform load stream
         __builtin_amdgcn_sched_barrier(0);
@@ -409,7 +421,7 @@ __global__ __launch_bounds__(256, 1) void k_loss_fused(RowList layers, const _Fl
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
         issue_x(2 * g + 2, 0);
-        issue_s(g + 1, ps);
+        issue_s(g + 1, (g + 1) & 1);
         __builtin_amdgcn_sched_barrier(0);
         compute_half(1, Xs + lf::kBuf);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -421,7 +433,7 @@ __global__ __launch_bounds__(256, 1) void k_loss_fused(RowList layers, const _Fl
     for (int i = 0; i < lf::kFR; ++i) {
         const bool t_ok = t0 + 16 * i + j < T;
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < NT; ++c)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const bool ok = t_ok && n_base + 16 * c + 4 * hq + r < N;
@@ -552,11 +564,11 @@ int launch_search(const void* const* Ws, const int* Ns, int n_layers, const void
         rows.n = n_layers;
         auto kern = group_size == 64 ? pick_loss_fused<64>(bits, zero_point)
                                      : pick_loss_fused<128>(bits, zero_point);
-        const int lds = 2 * lf::kBuf;
+        const int lds = 2 * lf::kBuf + 2 * 256 * (int)sizeof(float);
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return (int)e;
-        const dim3 grid_f((N + 127) / 128, (T + lf::kT - 1) / lf::kT, n_alpha);
+        const dim3 grid_f((N + kFusedRows - 1) / kFusedRows, (T + lf::kT - 1) / lf::kT, n_alpha);
         hipLaunchKernelGGL(kern, grid_f, dim3(256), lds, st, rows, (const _Float16*)X_cal, T, N, K,
                            (const float*)s_all, (const float*)s_inv, part);
         const int err = (int)hipGetLastError();
