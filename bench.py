@@ -54,6 +54,28 @@ def gemv_bytes(M, N, K, bits=4, group_size=128):
     return N * K * bits // 8 + 4 * N * (K // group_size) + 2 * M * K + 2 * M * N
 
 
+def gemm_traffic():
+    """HBM bytes of the three M = 2048 prefill launches (one per shape, summed)
+    from the committed rocprofv3 PMC runs, and their algorithmic bytes.
+
+    profiles/gemm_mistral7b_m2048_traffic.json holds FETCH_SIZE + WRITE_SIZE
+    of `bench.py --pmc-gemm-probe`, scaled by a copy of known size; it is used
+    only while its recorded hash matches the current GEMM source, else None.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemm_mistral7b_m2048_traffic.json")
+    csrc = os.path.join(ROOT, "weight_only_quantization_pack_amd", "csrc")
+    try:
+        rec = json.load(open(path))
+        src = open(os.path.join(csrc, "gemm.hip"), "rb").read() + \
+            open(os.path.join(csrc, "awq_internal.h"), "rb").read()
+    except (OSError, ValueError):
+        return None, None
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None, None
+    return int(rec["traffic_bytes_three_launches"]), int(rec["algorithmic_bytes_three_launches"])
+
+
 def gemv_traffic_per_launch():
     """HBM bytes per decode GEMV launch from the committed rocprofv3 PMC runs.
 
@@ -88,8 +110,9 @@ def main(argv=None):
                     help="short run for rocprofv3 --pmc: a 256 MiB device copy (known size, "
                          "calibrates FETCH_SIZE/WRITE_SIZE) then one cold pass of the decode step")
     ap.add_argument("--pmc-gemm-probe", action="store_true",
-                    help="short run for rocprofv3 --pmc: the three M=2048 prefill GEMMs, three "
-                         "launches each after one warm-up launch")
+                    help="short run for rocprofv3 --pmc: a 256 MiB device copy (known size, "
+                         "calibrates FETCH_SIZE/WRITE_SIZE), then the three M=2048 prefill GEMMs, "
+                         "three launches each after one warm-up launch")
     ap.add_argument("--pmc-batched-probe", action="store_true",
                     help="short run for rocprofv3 --pmc: a 256 MiB device copy, then the Llama-70B MLP "
                          "shapes at M = 64 (awq_gemm, split K) and M = 16 (awq_gemv), three launches each")
@@ -120,6 +143,14 @@ def main(argv=None):
     stream = torch.cuda.Stream()          # default priority
 
     if args.pmc_gemm_probe:
+        # calibration copy of known size, then the three shapes
+        src = torch.empty(256 * 2**20, dtype=torch.uint8, device=dev).random_(0, 255)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
         wl4 = WL.workload(4)
         res = {}
         with torch.cuda.stream(stream):
@@ -133,7 +164,11 @@ def main(argv=None):
                 res[f"{K}x{N}"] = 2.0 * 2048 * N * K
                 del W, qw, sc, ze, x, y
         torch.cuda.synchronize()
-        print(json.dumps({"pmc_gemm_probe": True, "M": 2048, "flops_per_launch": res}))
+        # algorithmic bytes per launch: packed weights, scales and zeros, x, y
+        alg = {f"{K}x{N}": N * K // 2 + 4 * N * (K // 128) + 2 * 2048 * K + 2 * 2048 * N
+               for K, N in wl4.shapes}
+        print(json.dumps({"pmc_gemm_probe": True, "M": 2048, "copy_bytes": 256 * 2**20,
+                          "flops_per_launch": res, "algorithmic_bytes_per_launch": alg}))
         return 0
 
     if args.pmc_batched_probe:
@@ -696,7 +731,9 @@ def main(argv=None):
                  "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 1),
                               "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                               "frac": round(gemm_tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                              "traffic": None,
+                              "traffic": gemm_traffic()[0],
+                              "traffic_unit": "HBM bytes of one launch of each of the three shapes (sum)",
+                              "algorithmic_bytes": gemm_traffic()[1],
                               "kernel": "k_gemm_w4p: 128 x 448 tiles (4 waves x 7 column blocks) for 4096x14336 (512 tiles), 128 x 256 (8 waves x 2) for 14336x4096 (256), 128 x 384 (8 waves x 3) for 4096x6144 (256)"}},
         "offline": offline,
         "cpu_baseline": cpu,

@@ -294,7 +294,7 @@ __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
     const _Float16* __restrict__ x, const uint32_t* __restrict__ qw,
     const _Float16* __restrict__ scales, const _Float16* __restrict__ zeros,
     _Float16* __restrict__ Y, float* __restrict__ part, const float* __restrict__ inv_s,
-    int M, int N, int K, int gsplit) {
+    int M, int N, int K, int gsplit, int xcd_rows) {
     using namespace w4;
     static_assert(GMT == 128 || GMT == 64 || GMT == 32 || GMT == 16, "16- to 128-row tiles");
     constexpr int FR = GMT / 16;                       // 16-row A fragments (and row groups per wave)
@@ -316,9 +316,22 @@ __global__ __launch_bounds__(64 * WV, 1) void k_gemm_w4p(
     const int NB = (N + 15) / 16;
     const int nTn = (N + TN - 1) / TN, nTm = (M + GMT - 1) / GMT;
     const int nT = nTn * nTm;
-    int t = blockIdx.x;
-    if (nT % 8 == 0) t = (t % 8) * (nT / 8) + t / 8;
-    const int m0 = (t / nTn) * GMT, n0 = (t % nTn) * TN;
+    // XCD-aware tile order: workgroup ids go round-robin over the 8 XCDs, so
+    // XCD x runs ids x, x + 8, ...  The tile grid is cut into xcd_rows row
+    // blocks times 8 / xcd_rows column blocks, one per XCD, walked row-major,
+    // so that an XCD's L2 serves the activation rows and weight columns its
+    // tiles share (the host picks the cut; 0: tiles in id order)
+    int tm, tn;
+    if (xcd_rows > 0) {
+        const int xcd = (int)blockIdx.x & 7, u = (int)blockIdx.x >> 3;
+        const int R = nTm / xcd_rows, C = nTn / (8 / xcd_rows);      // tiles of one XCD's block
+        tm = (xcd / (8 / xcd_rows)) * R + u / C;
+        tn = (xcd % (8 / xcd_rows)) * C + u % C;
+    } else {
+        tm = (int)blockIdx.x / nTn;
+        tn = (int)blockIdx.x % nTn;
+    }
+    const int m0 = tm * GMT, n0 = tn * TN;
 
     uint32_t a_off[FRL];
 #pragma unroll
@@ -942,6 +955,27 @@ int w4p_tiles(int M, int N, int nbw = 4) {
     return ((N + 64 * nbw - 1) / (64 * nbw)) * ((M + rows - 1) / rows);
 }
 
+// The XCD cut of the pipelined kernel's tile grid (see k_gemm_w4p): with a
+// row blocks and 8 / a column blocks, each XCD reads its activation rows once
+// and its weight columns once, so the L2 misses are about (8 / a) x the
+// activation bytes + a x the weight bytes; the a in {1, 2, 4, 8} that
+// divides the grid and minimises that is taken (0 when the grid does not
+// split into 8 equal blocks).  Example, M = 2048 (16 row tiles): 4096 x 14336
+// (16.8 MB of activations, 29 MB of weights, 32 column tiles) a = 2,
+// 14336 x 4096 (58.7 MB, 29 MB) a = 4.
+int xcd_rows_for(int M, int N, int K, int bits, int gmt, int tn) {
+    const int nTm = (M + gmt - 1) / gmt, nTn = (N + tn - 1) / tn;
+    const double xb = 2.0 * M * K, wb = (double)N * K * bits / 8 + 4.0 * N * (K / kGroup);
+    int best = 0;
+    double best_cost = 0;
+    for (const int a : {8, 4, 2, 1}) {
+        if (nTm % a != 0 || nTn % (8 / a) != 0) continue;
+        const double cost = (8 / a) * xb + a * wb;
+        if (best == 0 || cost < best_cost) { best = a; best_cost = cost; }
+    }
+    return best;
+}
+
 template <int GMT, int NBW, int WV, bool SC>
 int launch_w4p_rows_sc(const void* x, const void* qweight, const void* scales, const void* zeros,
                        void* y, float* part, const float* inv_s, int M, int N, int K, int bits,
@@ -964,7 +998,8 @@ int launch_w4p_rows_sc(const void* x, const void* qweight, const void* scales, c
     if (e != hipSuccess) return (int)e;
     hipLaunchKernelGGL(kern, dim3(nT, splits), dim3(64 * WV), lds, st, (const _Float16*)x,
                        (const uint32_t*)qweight, (const _Float16*)scales, (const _Float16*)zeros,
-                       (_Float16*)y, part, inv_s, M, N, K, gsplit);
+                       (_Float16*)y, part, inv_s, M, N, K, gsplit,
+                       xcd_rows_for(M, N, K, bits, GMT, 16 * NBW * WV));
     return (int)hipGetLastError();
 }
 
