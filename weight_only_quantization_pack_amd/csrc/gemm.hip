@@ -24,8 +24,10 @@
 // takes a template wave count: 128 x 256 and 128 x 384 run as 8 waves of 2 or
 // 3 column blocks (two waves per SIMD), 128 x 448 as 4 waves of 7 (224
 // accumulators per lane in AGPRs, the same A fragments feeding 56 MFMAs); the
-// tile count of N = 6144 or 14336 becomes a whole number of rounds on 256 CUs.  Tiles are mapped so that each XCD (workgroup id mod 8) walks a
-// contiguous run of row-major tiles and keeps its A rows in its L2.
+// tile count of N = 6144 or 14336 becomes a whole number of rounds on 256 CUs.
+// Each XCD (workgroup id mod 8) takes one block of the tile grid, cut per
+// shape so that its L2 serves the activation rows and weight columns its
+// tiles share (xcd_rows_for).
 //
 // Two schedules of that tile: k_gemm_w4 double-buffers A and B (one K-step
 // ahead) at two workgroups per CU; k_gemm_w4p keeps three K-steps in flight
