@@ -232,8 +232,8 @@ constexpr int kT = kFusedT;             // calibration rows per workgroup
 constexpr int kFR = kT / 16;            // X fragments per substep
 constexpr int kStepK = 64;              // k per LDS step (half a group)
 constexpr int kRow = kStepK * 2;        // bytes of one X row in LDS
-constexpr int kBuf = kT * kRow;         // 32 KB per buffer
-constexpr int kXLoads = kBuf / 1024 / 4;   // direct-to-LDS loads per wave and step (8)
+constexpr int kBuf = kT * kRow;         // 64 KB per buffer
+constexpr int kXLoads = kBuf / 1024 / 4;   // direct-to-LDS loads per wave and step (16)
 constexpr int kWLoads = kFusedNT * 4;      // W loads per wave and group
 }
 
