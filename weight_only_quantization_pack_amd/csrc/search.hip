@@ -15,6 +15,8 @@
 // Several layers that read the same input (q/k/v, gate/up) take one search:
 // their rows are treated as the rows of one layer (read in place from each
 // layer's own buffer) and the loss averages over all their outputs.
+#include <type_traits>
+
 #include "awq_internal.h"
 
 namespace awq {
@@ -35,16 +37,15 @@ struct LayerList {
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // The loss runs one of two ways: a separate error kernel writing D for every
-// alpha into the workspace plus a dense loss GEMM (the default: fastest, needs
-// one chunk of alphas' D, N rounded up to 16), or one fused kernel forming D
-// in registers (a workspace of under a megabyte; MI355X, 4096 x 4096, T = 512,
-// 20 alphas: 0.73 ms against 0.65-0.68 ms median, since forming D there does
-// not overlap its MFMAs).  The fused kernel's workgroup takes 512 calibration
-// rows and one 16-row tile of W per wave, so every D value is formed once per
-// alpha (256 rows and two tiles per wave, which forms each D twice at T = 512:
-// 0.82 ms; 256 rows and one tile: 0.98 ms)
+// alpha into the workspace plus a dense loss GEMM (needs one chunk of alphas'
+// D, N rounded up to 16), or one fused kernel forming D in registers (a
+// workspace of under a megabyte).  MI355X, 4096 x 4096, T = 512, 20 alphas:
+// 0.52-0.54 ms and 0.65-0.66 ms.  The fused kernel's workgroup takes 512
+// calibration rows and 64 rows of W, so every D value is formed once per
+// alpha, by two waves of one SIMD that each form half of it while the other's
+// MFMAs run.
 constexpr int kFusedT = 512;            // calibration rows per workgroup of the fused loss
-constexpr int kFusedNT = 1;             // 16-row tiles of W per wave (4 waves)
+constexpr int kFusedNT = 1;             // 16-row tiles of W per wave
 constexpr int kFusedRows = 64 * kFusedNT;
 size_t fused_tiles(int T, int N) {
     return (size_t)((N + kFusedRows - 1) / kFusedRows) * (size_t)((T + kFusedT - 1) / kFusedT);
@@ -214,27 +215,41 @@ __global__ __launch_bounds__(256) void k_quant_err(LayerList layers,
 
 // Fused loss (the error matrix D_alpha = W - w_hat_alpha / s_alpha never goes
 // to memory): L_alpha * T * N = sum over (t, n) of (X D_alpha^T)[t][n]^2.  A
-// workgroup owns 64 rows of W (one 16-row MFMA B tile per wave) and up to 512
-// calibration rows for one alpha, so every D value is formed once per alpha:
-// each wave builds its D fragments in registers in the B-operand layout of
-// v_mfma_f32_16x16x32_f16 (lane (j, q) holds row j's k = 32 s + 8 q + e of
-// substep s), quantizing the group from W, s and 1/s with the codes of
-// quant_codes_b2, exactly as the separate error kernel does.  X streams
+// workgroup of 8 waves owns 64 rows of W (four 16-row MFMA B tiles) and up to
+// 512 calibration rows for one alpha.  Wave w takes tile w & 3 against
+// calibration rows 256 (w >> 2) .. + 255, so the two waves of a tile share a
+// SIMD: each forms the D fragments of half the group's columns (k 64 (w >> 2)
+// .. + 63) in registers in the B-operand layout of v_mfma_f32_16x16x32_f16
+// (lane (j, q) holds row j's k = 32 s + 8 q + e of substep s), meeting its
+// partner through LDS for the group's min and max (128-wide groups) and for the
+// other half of the fragments.  The codes are those of quant_codes_b2, exactly
+// as the separate error kernel forms them.  The kernel is software-pipelined
+// by one group: while a wave runs the 64 MFMAs of group g it forms its half of
+// D for group g + 1, in slices of VALU work placed behind each 4 MFMAs, and the
+// other wave of the SIMD fills the issue slots that one wave leaves.  X streams
 // through LDS in 64-k steps (512 rows x 128 B, two buffers, direct-to-LDS
-// loads, chunk p of row r holding global chunk p ^ (r & 7), which the
-// A-fragment reads see free of bank conflicts on MI355X); W of the next group
-// is loaded into registers one group ahead, its s and 1/s into LDS.  The 32
-// MFMA accumulators of a lane (128 fp32) live in AGPRs.  The epilogue squares
-// and sums the outputs of rows < T and columns < N in fp32 per lane, then in
-// fp64 in a fixed order, into one partial per workgroup.
+// buffer loads with the step's offset in the scalar operand, chunk p of row r
+// holding global chunk p ^ (r & 7), which the A-fragment reads see free of bank
+// conflicts on MI355X); W rows are loaded two groups ahead into registers, s
+// and 1/s one group ahead into an LDS slot.  The epilogue squares and sums the
+// outputs of rows < T and columns < N in fp32 per lane, then in fp64 in a
+// fixed order, into one partial per workgroup.
 namespace lf {
 constexpr int kT = kFusedT;             // calibration rows per workgroup
-constexpr int kFR = kT / 16;            // X fragments per substep
+constexpr int kWaves = 8;
+constexpr int kFR = kT / 2 / 16;        // X fragments per wave and substep (16)
 constexpr int kStepK = 64;              // k per LDS step (half a group)
 constexpr int kRow = kStepK * 2;        // bytes of one X row in LDS
 constexpr int kBuf = kT * kRow;         // 64 KB per buffer
-constexpr int kXLoads = kBuf / 1024 / 4;   // direct-to-LDS loads per wave and step (16)
-constexpr int kWLoads = kFusedNT * 4;      // W loads per wave and group
+constexpr int kNBuf = 2;
+constexpr int kXLoads = kBuf / 1024 / kWaves;   // direct-to-LDS loads per wave and step (8)
+constexpr int kWLoads = 2;              // W loads per wave and group
+constexpr int kUnits = 2 * kFR / 4;     // units of 4 MFMAs per LDS step (8)
+constexpr int kSBytes = 2 * 256 * 4;    // two slots of s and 1/s
+constexpr int kRedBytes = kWaves * 16 * 2 * 4;      // [wave][row][min, max]
+constexpr int kDxBytes = kWaves * 2 * 64 * 16;      // [wave][substep][lane] half8
+constexpr int kLds = kSBytes + kRedBytes + kDxBytes + kNBuf * kBuf;
+static_assert(kFusedNT == 1 && kFusedRows == 64, "four 16-row tiles per workgroup");
 }
 
 struct RowList {                        // rows of the layers searched together
@@ -244,212 +259,336 @@ struct RowList {                        // rows of the layers searched together
 };
 
 template <int Q, bool ZP, int GS>
-__global__ __launch_bounds__(256, 1) void k_loss_fused(RowList layers, const _Float16* __restrict__ X,
+__global__ __launch_bounds__(512, 1) void k_loss_fused(RowList layers, const _Float16* __restrict__ X,
                                                        int T, int N, int K,
                                                        const float* __restrict__ s_all,
                                                        const float* __restrict__ s_inv,
                                                        double* __restrict__ partials) {
     static_assert(GS == 128 || GS == 64, "128- or 64-wide groups");
-    extern __shared__ __attribute__((aligned(16))) unsigned char Xs[];   // 2 x lf::kBuf, then the s slots
+    // the small arrays first (within reach of a DS instruction's 16-bit offset
+    // from one base), then the X buffers
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    float* const Ss = reinterpret_cast<float*>(lds);                               // [2 slots][s 128, 1/s 128]
+    float* const Red = reinterpret_cast<float*>(lds + lf::kSBytes);                 // [wave][row][2]
+    unsigned char* const Dx = lds + lf::kSBytes + lf::kRedBytes;                    // [wave][substep][lane]
+    unsigned char* const Xs = lds + lf::kSBytes + lf::kRedBytes + lf::kDxBytes;     // kNBuf x lf::kBuf
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tile = wave & 3;                      // W tile
     const int j = lane & 15, hq = lane >> 4;
     const int alpha = blockIdx.z;
     const int t0 = blockIdx.y * lf::kT;
     const int G = K / kGroup;
-    constexpr int NT = kFusedNT;
-    const int n_base = blockIdx.x * kFusedRows + wave * 16 * NT;
-
-    // this lane's W row in each of its two tiles (rows past N: row N - 1, never summed)
-    const _Float16* wrow[NT];
-#pragma unroll
-    for (int c = 0; c < NT; ++c) {
-        const int n = min(n_base + 16 * c + j, N - 1);
-        int l = 0;
-#pragma unroll
-        for (int m = 1; m < kMaxSearchLayers; ++m)
-            if (m < layers.n && n >= layers.nstart[m]) l = m;
-        wrow[c] = layers.w[l] + (size_t)(n - layers.nstart[l]) * K;
-    }
-
-    // X: load q (0..kXLoads-1) of this wave writes rows 8 (kXLoads wave + q) .. + 7
-    // of the tile, lane l row + (l >> 3), LDS chunk l & 7; rows past T read row T - 1
-    uint32_t x_off[lf::kXLoads];
-#pragma unroll
-    for (int q = 0; q < lf::kXLoads; ++q) {
-        const int rr = 8 * (lf::kXLoads * wave + q) + (lane >> 3);
-        const int row = min(t0 + rr, T - 1);
-        const int kc = (lane & 7) ^ (rr & 7);
-        x_off[q] = (uint32_t)row * (uint32_t)K + 8u * (uint32_t)kc;
-    }
-    auto issue_x = [&](int step, int buf) {
-        const uint32_t k0 = (uint32_t)min(step, 2 * G - 1) * lf::kStepK;
+    const int n_base = blockIdx.x * kFusedRows + tile * 16;
+    // X: load q (0..kXLoads-1) of wave w fills rows 8 (kXLoads w + q) .. + 7 of
+    // the buffer, lane l row + (l >> 3) at position l & 7, which holds chunk
+    // (l & 7) ^ (l >> 3) of the row (chunk p of row r at position p ^ (r & 7),
+    // which the A-fragment reads see free of bank conflicts).  Byte offsets
+    // within X (T K < 2^31 halves, checked by the caller): the lane's part in
+    // the vector operand, the load's rows and the step's k in the scalar one.
+    // Rows past T fall outside the buffer (zero, no memory access) and their
+    // outputs are never summed.
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(X), (short)0, (int)((uint32_t)T * (uint32_t)K * 2u), 0x00020000);
+    const uint32_t x_voff = 2u * (uint32_t)K * (uint32_t)(t0 + 8 * lf::kXLoads * wave + (lane >> 3))
+                          + 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
+    // (past the last step it loads the last step again into the buffer the
+    // step would take, which nothing reads: a uniform load stream)
+    auto issue_x = [&](int step) __attribute__((always_inline)) {
+        const uint32_t soff = (uint32_t)min(step, 2 * G - 1) * (uint32_t)lf::kRow;
+        unsigned char* const buf = Xs + (step & (lf::kNBuf - 1)) * lf::kBuf;
 #pragma unroll
         for (int q = 0; q < lf::kXLoads; ++q)
-            __builtin_amdgcn_global_load_lds((global_void_t*)(X + x_off[q] + k0),
-                                             (lds_void_t*)(Xs + buf * lf::kBuf + (lf::kXLoads * wave + q) * 1024),
-                                             16, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(buf + (lf::kXLoads * wave + q) * 1024),
+                                                     16, x_voff, soff + (uint32_t)q * 16u * (uint32_t)K, 0, 0);
     };
-
-    // the next group's W rows, loaded one group ahead (its s and 1/s go to
-    // LDS during the second half of the group before): value i = 8 sub + e
-    // of a lane is k = 32 sub + 8 q + e of the group
-    struct PreW { uint4 w[NT][4]; };
-    // s and 1/s of a group go to LDS (two slots: the group being quantized and
-    // the next), written by wave 0 with one direct-to-LDS load (lanes 0..31
-    // the 128 s values, lanes 32..63 the 128 reciprocals) and read by every
-    // wave while it forms D; registers would hold them for a whole group
-    float* const Ss = reinterpret_cast<float*>(Xs + 2 * lf::kBuf);   // [2 slots][s 128, 1/s 128]
-    auto issue_w = [&](int g, PreW& p) {
-        const int k0 = kGroup * min(g, G - 1);
-#pragma unroll
-        for (int c = 0; c < NT; ++c)
-#pragma unroll
-            for (int sub = 0; sub < 4; ++sub)
-                p.w[c][sub] = *reinterpret_cast<const uint4*>(wrow[c] + k0 + 32 * sub + 8 * hq);
-    };
-    auto issue_s = [&](int g, int slot) {
+    // s and 1/s of a group go to LDS (two slots), written by wave 0 with one
+    // direct-to-LDS load (lanes 0..31 the 128 s values, lanes 32..63 the 128
+    // reciprocals) and read by every wave while it forms D
+    auto issue_s = [&](int g, int slot) __attribute__((always_inline)) {
         if (wave != 0) return;                       // wave-uniform
         const int k0 = kGroup * min(g, G - 1);
         const float* src = (lane < 32 ? s_all : s_inv) + (size_t)alpha * K + k0 + 4 * (lane & 31);
         __builtin_amdgcn_global_load_lds((global_void_t*)src, (lds_void_t*)(Ss + slot * 256), 16, 0, 0);
     };
-    auto f4 = [](const float4& q, int e) { return e == 0 ? q.x : e == 1 ? q.y : e == 2 ? q.z : q.w; };
-    auto wval = [](const uint4& raw, int e) {
-        return (float)reinterpret_cast<const _Float16*>(&raw)[e];
+    // weight e of a lane's 8 (the packed words stay 32-bit registers)
+    auto wword = [](const uint4& raw, int e) __attribute__((always_inline)) {
+        return e / 2 == 0 ? raw.x : e / 2 == 1 ? raw.y : e / 2 == 2 ? raw.z : raw.w;
     };
+    auto whalf = [](uint32_t word, int e) __attribute__((always_inline)) {
+        return (float)__builtin_bit_cast(_Float16, (unsigned short)((e & 1) ? (word >> 16) : (word & 0xFFFFu)));
+    };
+    auto wval = [&](const uint4& raw, int e) __attribute__((always_inline)) { return whalf(wword(raw, e), e); };
 
-    half8_t dfr[NT][4];                  // D fragments of the current group: [tile][substep]
-    auto make_d = [&](const PreW& pw, int slot) {
-        // value i = 8 sub + e of this lane is column 32 sub + 8 hq + e of the group
-        struct { float4 s[8], r[8]; } ps;
-        const float* sl = Ss + slot * 256 + 8 * hq;
+    // this wave's half of W of a group in registers: value i = 8 ls + e of a
+    // lane is k = 64 th + 32 ls + 8 q + e
+    struct PreW { uint4 w[2]; };
+    // This wave's half of one group's D, formed in slices: 16 values per lane,
+    // value i = 8 ls + e (one 64-group for 64-wide groups; half of one
+    // 128-group, whose min and max meet the partner wave's through LDS).
+    struct MakeD {
+        float v[16];
+        float mn, mx;
+        GroupParams gp;
+        uint32_t Tc[16];
+        uint32_t fmin;
+        float4 r0, r1;
+        half8_t d[2];
+    };
+    float4_t acc[lf::kFR];
 #pragma unroll
-        for (int sub = 0; sub < 4; ++sub) {
-            ps.s[2 * sub] = *reinterpret_cast<const float4*>(sl + 32 * sub);
-            ps.s[2 * sub + 1] = *reinterpret_cast<const float4*>(sl + 32 * sub + 4);
-            ps.r[2 * sub] = *reinterpret_cast<const float4*>(sl + 128 + 32 * sub);
-            ps.r[2 * sub + 1] = *reinterpret_cast<const float4*>(sl + 128 + 32 * sub + 4);
+    for (int i = 0; i < lf::kFR; ++i) acc[i] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+    // The rest depends on the wave's calibration half th = wave >> 2 (also the
+    // half of D's columns it forms), a compile-time constant in each copy.
+    auto run = [&](auto th_c) __attribute__((always_inline)) {
+        constexpr int TH = decltype(th_c)::value;
+        // this lane's W row (rows past N: row N - 1, never summed), from its half of the group
+        const _Float16* wrow;
+        {
+            const int n = min(n_base + j, N - 1);
+            int l = 0;
+#pragma unroll
+            for (int m = 1; m < kMaxSearchLayers; ++m)
+                if (m < layers.n && n >= layers.nstart[m]) l = m;
+            wrow = layers.w[l] + (size_t)(n - layers.nstart[l]) * K + 64 * TH + 8 * hq;
         }
+        auto issue_w = [&](int g, PreW& p) __attribute__((always_inline)) {
+            const int k0 = kGroup * min(g, G - 1);
 #pragma unroll
-        for (int c = 0; c < NT; ++c) {
-            float v[32];
+            for (int ls = 0; ls < 2; ++ls)
+                p.w[ls] = *reinterpret_cast<const uint4*>(wrow + k0 + 32 * ls);
+        };
+        // s (or 1/s, at +128) of value i of this lane in slot `slot`
+        const float* const s_lane = Ss + 64 * TH + 8 * hq;
+        auto s_at = [&](int slot, int i) __attribute__((always_inline)) {
+            return s_lane + slot * 256 + 32 * (i / 8) + (i % 8);
+        };
+        // v = w * s for the 8 values of local substep ls; running min and max
+        auto slice_scale = [&](MakeD& st, const PreW& pw, int slot, int ls) __attribute__((always_inline)) {
+            const float4 s0 = *reinterpret_cast<const float4*>(s_at(slot, 8 * ls));
+            const float4 s1 = *reinterpret_cast<const float4*>(s_at(slot, 8 * ls + 4));
+            const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+            float mn = 0.0f, mx = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 32; ++i) v[i] = wval(pw.w[c][i / 8], i % 8) * f4(ps.s[i / 4], i % 4);
-            constexpr int NV = GS / 4;       // values of one group in a lane
+            for (int e = 0; e < 8; ++e) {
+                const float v = wval(pw.w[ls], e) * sv[e];
+                st.v[8 * ls + e] = v;
+                mn = e == 0 ? v : fminf(mn, v);
+                mx = e == 0 ? v : fmaxf(mx, v);
+            }
+            if (ls == 0) { st.mn = mn; st.mx = mx; }
+            else { st.mn = fminf(st.mn, mn); st.mx = fmaxf(st.mx, mx); }
+        };
+        // the row's other values of this half sit in the lanes of the same row j
+        auto slice_rowminmax = [&](MakeD& st) __attribute__((always_inline)) {
+            st.mn = fminf(st.mn, __shfl_xor(st.mn, 16)); st.mx = fmaxf(st.mx, __shfl_xor(st.mx, 16));
+            st.mn = fminf(st.mn, __shfl_xor(st.mn, 32)); st.mx = fmaxf(st.mx, __shfl_xor(st.mx, 32));
+        };
+        auto slice_params = [&](MakeD& st) __attribute__((always_inline)) {
+            st.gp = group_params<Q, ZP>(st.mn, st.mx);
+            st.fmin = 0xFFFFu;
+        };
+        // fixed-point codes of values 4c .. 4c + 3 (quant_codes_b2's fast path)
+        auto slice_codes = [&](MakeD& st, int c) __attribute__((always_inline)) {
+            const float zb = st.gp.zero + (128.5f + 0x3p-16f);   // exact: z <= 15
 #pragma unroll
-            for (int gg = 0; gg < 32 / NV; ++gg) {
-                float mn = v[NV * gg], mx = v[NV * gg];
+            for (int i = 4 * c; i < 4 * c + 4; ++i) {
+                const float t = __builtin_amdgcn_fmed3f(__builtin_fmaf(st.v[i], st.gp.rd, zb), 128.25f, 128.5f + Q);
+                st.Tc[i] = __builtin_bit_cast(uint32_t, t);
+                st.fmin = min(st.fmin, st.Tc[i] & 0xFFFFu);
+            }
+        };
+        // a group whose fraction came too close to a rounding boundary takes
+        // quant_code's division (quant_codes_b2's fallback), on v = w * s formed
+        // again exactly as slice_scale formed it
+        auto slice_fallback = [&](MakeD& st, const PreW& pw, int slot) __attribute__((always_inline)) {
+            const bool near = st.fmin <= 5u;
+            if (__builtin_amdgcn_ballot_w64(near)) {
+                if (near) {
 #pragma unroll
-                for (int i = 1; i < NV; ++i) { mn = fminf(mn, v[NV * gg + i]); mx = fmaxf(mx, v[NV * gg + i]); }
-                // the group's other values sit in the lanes of the same row j
-                mn = fminf(mn, __shfl_xor(mn, 16)); mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mn = fminf(mn, __shfl_xor(mn, 32)); mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const GroupParams gp = group_params<Q, ZP>(mn, mx);
-                uint32_t Tc[NV];
-                quant_codes_b2<Q, NV>(v + NV * gg, gp, Tc);
-                const float zd = -(gp.zero * gp.delta);     // exact: z <= 16, Delta an fp16 value
-#pragma unroll
-                for (int i = 0; i < NV; ++i) {
-                    const int idx = NV * gg + i;
-                    const float q = (float)((Tc[i] >> 16) & 0xFFu);
-                    const float w_hat = __builtin_fmaf(q, gp.delta, zd);   // (q - z) * Delta, exact
-                    const float w = wval(pw.w[c][idx / 8], idx % 8);
-                    dfr[c][idx / 8][idx % 8] = (_Float16)(w - w_hat * f4(ps.r[idx / 4], idx % 4));
+                    for (int i = 0; i < 16; ++i)
+                        st.Tc[i] = quant_code<Q>(wval(pw.w[i / 8], i % 8) * *s_at(slot, i), st.gp) << 16;
                 }
             }
-            __builtin_amdgcn_sched_barrier(0);   // one tile's temporaries at a time
-        }
-    };
+        };
+        // D of values 4c .. 4c + 3: w - w_hat * (1/s)
+        auto slice_d = [&](MakeD& st, const PreW& pw, int slot, int c) __attribute__((always_inline)) {
+            const int ls = c / 2;
+            if (c % 2 == 0) {
+                st.r0 = *reinterpret_cast<const float4*>(s_at(slot, 8 * ls) + 128);
+                st.r1 = *reinterpret_cast<const float4*>(s_at(slot, 8 * ls + 4) + 128);
+            }
+            const float zd = -(st.gp.zero * st.gp.delta);   // exact: z <= 16, Delta an fp16 value
+#pragma unroll
+            for (int i = 4 * c; i < 4 * c + 4; ++i) {
+                const int e = i % 8;
+                const float qf = (float)((st.Tc[i] >> 16) & 0xFFu);
+                const float w_hat = __builtin_fmaf(qf, st.gp.delta, zd);   // (q - z) * Delta, exact
+                const float r = e == 0 ? st.r0.x : e == 1 ? st.r0.y : e == 2 ? st.r0.z : e == 3 ? st.r0.w
+                              : e == 4 ? st.r1.x : e == 5 ? st.r1.y : e == 6 ? st.r1.z : st.r1.w;
+                // w converted again here (an opaque copy of its packed pair keeps
+                // the compiler from holding the fp32 weights across the group)
+                uint32_t pair = wword(pw.w[ls], e);
+                asm volatile("" : "+v"(pair));
+                st.d[ls][e] = (_Float16)(whalf(pair, e) - w_hat * r);
+            }
+        };
+        // the partner wave's half of the min and max (128-wide groups)
+        auto put_red = [&](const MakeD& st) __attribute__((always_inline)) {
+            if (hq == 0) {
+                Red[(wave * 16 + j) * 2] = st.mn;
+                Red[(wave * 16 + j) * 2 + 1] = st.mx;
+            }
+        };
+        auto get_red = [&](MakeD& st) __attribute__((always_inline)) {
+            const float2 o = *reinterpret_cast<const float2*>(Red + ((wave ^ 4) * 16 + j) * 2);
+            st.mn = fminf(st.mn, o.x);
+            st.mx = fmaxf(st.mx, o.y);
+        };
+        auto put_d = [&](const MakeD& st) __attribute__((always_inline)) {
+#pragma unroll
+            for (int ls = 0; ls < 2; ++ls)
+                *reinterpret_cast<half8_t*>(Dx + ((wave * 2 + ls) * 64 + lane) * 16) = st.d[ls];
+        };
+        // slice u (0..15) of one group's D, behind unit u of the group; the
+        // group's middle barrier separates units 7 and 8
+        auto slice = [&](MakeD& st, const PreW& pw, int slot, int u) __attribute__((always_inline)) {
+            if constexpr (GS == 128) {
+                if (u < 2) slice_scale(st, pw, slot, u);
+                else if (u == 2) { slice_rowminmax(st); put_red(st); }
+                else if (u == 8) { get_red(st); slice_params(st); }
+                else if (u >= 9 && u < 13) slice_codes(st, u - 9);
+                else if (u == 13) { slice_fallback(st, pw, slot); slice_d(st, pw, slot, 0); }
+                else if (u == 14) { slice_d(st, pw, slot, 1); slice_d(st, pw, slot, 2); }
+                else if (u == 15) { slice_d(st, pw, slot, 3); put_d(st); }
+            } else {
+                if (u < 2) slice_scale(st, pw, slot, u);
+                else if (u == 2) { slice_rowminmax(st); slice_params(st); }
+                else if (u >= 3 && u < 7) slice_codes(st, u - 3);
+                else if (u == 7) slice_fallback(st, pw, slot);
+                else if (u >= 8 && u < 12) slice_d(st, pw, slot, u - 8);
+                else if (u == 15) put_d(st);
+            }
+        };
+        // the complete D fragments of a group: this wave's half from its own
+        // registers, the partner's from LDS
+        auto take_d = [&](const MakeD& st, half8_t* dcur) __attribute__((always_inline)) {
+#pragma unroll
+            for (int ls = 0; ls < 2; ++ls) {
+                dcur[2 * TH + ls] = st.d[ls];
+                dcur[2 * (TH ^ 1) + ls] = *reinterpret_cast<const half8_t*>(Dx + (((wave ^ 4) * 2 + ls) * 64 + lane) * 16);
+            }
+        };
 
-    float4_t acc[lf::kFR][NT];         // [X fragment][tile]
+        // A-fragment reads: lane (j, q) takes chunk 4 sub + q of row 256 TH + 16 i + j
+        // (substep sub of the LDS step), at position (4 sub + q) ^ (j & 7)
+        const uint32_t x_lane0 = (uint32_t)(256 * TH + j) * lf::kRow + 16u * (uint32_t)(hq ^ (j & 7));
+        const uint32_t x_lane1 = (uint32_t)(256 * TH + j) * lf::kRow + 16u * (uint32_t)((4 + hq) ^ (j & 7));
+        auto read_unit = [&](const unsigned char* buf, int u, half8_t* xf) __attribute__((always_inline)) {
+            const int sub = u / (lf::kFR / 4), i0 = 4 * (u % (lf::kFR / 4));
+            const unsigned char* const b = buf + (sub ? x_lane1 : x_lane0);
 #pragma unroll
-    for (int i = 0; i < lf::kFR; ++i)
+            for (int v = 0; v < 4; ++v)
+                xf[v] = *reinterpret_cast<const half8_t*>(b + (i0 + v) * 16 * lf::kRow);
+        };
+        // one LDS step (half h of a group): 8 units of 4 X fragments and 4
+        // MFMAs, the fragments of unit u + 1 read under unit u's MFMAs, one
+        // slice of the next group's D behind each unit
+        auto step = [&](int h, const half8_t* dcur, MakeD& st, const PreW& pwn, int slot_n) __attribute__((always_inline)) {
+            const unsigned char* const buf = Xs + h * lf::kBuf;      // step 2 g + h uses buffer h
+            half8_t xa[4], xb[4];
+            read_unit(buf, 0, xa);
 #pragma unroll
-        for (int c = 0; c < NT; ++c) acc[i][c] = (float4_t){0.f, 0.f, 0.f, 0.f};
+            for (int u = 0; u < lf::kUnits; ++u) {
+                half8_t* cur = (u & 1) ? xb : xa;
+                half8_t* nxt = (u & 1) ? xa : xb;
+                if (u + 1 < lf::kUnits) read_unit(buf, u + 1, nxt);
+                const int sub = u / (lf::kFR / 4), i0 = 4 * (u % (lf::kFR / 4));
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    acc[i0 + v] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dcur[2 * h + sub], cur[v], acc[i0 + v], 0, 0, 0);
+                slice(st, pwn, slot_n, lf::kUnits * h + u);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
 
-    // the two substeps of one LDS step (half h of the group): X fragments in
-    // batches of 8, batch b + 1 read under batch b's 16 MFMAs (a scheduling
-    // barrier per batch keeps the compiler from hoisting every read)
-    constexpr int kB = 8, kNB = 2 * lf::kFR / kB;          // batches per LDS step
-    auto read_batch = [&](const unsigned char* buf, int b, half8_t* xf) {
-        const int sub = b / (lf::kFR / kB), i0 = (b % (lf::kFR / kB)) * kB;
-        const int kc = 4 * sub + hq;
-#pragma unroll
-        for (int u = 0; u < kB; ++u) {
-            const int r = 16 * (i0 + u) + j;
-            xf[u] = *reinterpret_cast<const half8_t*>(buf + r * lf::kRow + ((kc ^ (r & 7)) << 4));
-        }
-    };
-    auto compute_half = [&](int h, const unsigned char* buf) {
-        half8_t xa[kB], xb[kB];
-        read_batch(buf, 0, xa);
-#pragma unroll
-        for (int b = 0; b < kNB; ++b) {
-            half8_t* cur = (b & 1) ? xb : xa;
-            half8_t* nxt = (b & 1) ? xa : xb;
-            if (b + 1 < kNB) read_batch(buf, b + 1, nxt);
-            const int sub = b / (lf::kFR / kB), i0 = (b % (lf::kFR / kB)) * kB;
-#pragma unroll
-            for (int u = 0; u < kB; ++u)
-#pragma unroll
-                for (int c = 0; c < NT; ++c)
-                    acc[i0 + u][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dfr[c][2 * h + sub], cur[u], acc[i0 + u][c], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
+        PreW pw[2];
+        half8_t dcur[4];                // D fragments of the group whose MFMAs run: [substep]
+        MakeD st;
 
-    PreW pw;
-    issue_x(0, 0);
-    issue_w(0, pw);
-    issue_s(0, 0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    for (int g = 0; g < G; ++g) {
-        // step 2g, buffer 0: X(2g) and the group's W, s, 1/s have landed
-        __builtin_amdgcn_sched_barrier(0);
-        issue_x(2 * g + 1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        make_d(pw, g & 1);
-        __builtin_amdgcn_sched_barrier(0);
-        issue_w(g + 1, pw);                  // clamped past the last group: a uniform load stream
-        __builtin_amdgcn_sched_barrier(0);
-        compute_half(0, Xs);
-        // step 2g + 1, buffer 1: X(2g + 1) has landed once at most the next
-        // group's W loads are outstanding; every wave is done with buffer 0
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(lf::kWLoads));
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        issue_x(2 * g + 2, 0);
-        issue_s(g + 1, (g + 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_half(1, Xs + lf::kBuf);
+        // prologue: X(0), W(0), W(1), s(0), s(1) land; D(0) formed in full
+        issue_x(0);
+        issue_w(0, pw[0]);
+        issue_w(1, pw[1]);
+        issue_s(0, 0);
+        issue_s(1, 1);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+            for (int u = 8 * m; u < 8 * m + 8; ++u) slice(st, pw[0], 0, u);
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+        take_d(st, dcur);
+        __builtin_amdgcn_sched_barrier(0);
 
-    float sq = 0.0f;
+        // group g: MFMAs on D(g) (dcur) while this wave's half of D(g + 1) is
+        // formed from W(g + 1) (pw[1]) and s(g + 1) (slot (g + 1) & 1); W(g + 2)
+        // loads into pw[0], s(g + 2) into slot g & 1
+        for (int g = 0; g < G; ++g) {
+            const int slot_n = (g + 1) & 1;
+            // step 2g, buffer 0: X(2g) has landed, as have W(g + 1) and s(g + 1)
+            issue_x(2 * g + 1);
+            issue_w(g + 2, pw[0]);               // clamped past the last group: a uniform load stream
+            __builtin_amdgcn_sched_barrier(0);
+            step(0, dcur, st, pw[1], slot_n);
+            // step 2g + 1, buffer 1: X(2g + 1) has landed once at most the W
+            // loads are outstanding; every wave is done with buffer 0 and slot
+            // g & 1, and the min and max of the partner's half are in LDS
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(lf::kWLoads));
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            issue_x(2 * g + 2);
+            issue_s(g + 2, g & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            step(1, dcur, st, pw[1], slot_n);
+            // every wave's half of D(g + 1) is in LDS, X(2g + 2) has landed
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            take_d(st, dcur);
+            pw[1] = pw[0];
+        }
+
+        float sq = 0.0f;
 #pragma unroll
-    for (int i = 0; i < lf::kFR; ++i) {
-        const bool t_ok = t0 + 16 * i + j < T;
-#pragma unroll
-        for (int c = 0; c < NT; ++c)
+        for (int i = 0; i < lf::kFR; ++i) {
+            const bool t_ok = t0 + 256 * TH + 16 * i + j < T;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const bool ok = t_ok && n_base + 16 * c + 4 * hq + r < N;
-                sq = __builtin_fmaf(ok ? acc[i][c][r] : 0.0f, ok ? acc[i][c][r] : 0.0f, sq);
+                const bool ok = t_ok && n_base + 4 * hq + r < N;
+                sq = __builtin_fmaf(ok ? acc[i][r] : 0.0f, ok ? acc[i][r] : 0.0f, sq);
             }
-    }
+        }
+        return sq;
+    };
+    const float sq = (wave >> 2) == 0 ? run(std::integral_constant<int, 0>{}) : run(std::integral_constant<int, 1>{});
+
     double dsq = (double)sq;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) dsq += __shfl_xor(dsq, off);
-    __shared__ double wsum[4];
+    __shared__ double wsum[lf::kWaves];
     if (lane == 0) wsum[wave] = dsq;
     __syncthreads();
     if (tid == 0) {
-        const size_t tile = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
+        double tot = wsum[0];
+#pragma unroll
+        for (int w = 1; w < lf::kWaves; ++w) tot += wsum[w];
+        const size_t tile_id = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
         const size_t n_tiles = (size_t)gridDim.x * gridDim.y;
-        partials[(size_t)alpha * n_tiles + tile] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+        partials[(size_t)alpha * n_tiles + tile_id] = tot;
     }
 }
 
@@ -564,12 +703,12 @@ int launch_search(const void* const* Ws, const int* Ns, int n_layers, const void
         rows.n = n_layers;
         auto kern = group_size == 64 ? pick_loss_fused<64>(bits, zero_point)
                                      : pick_loss_fused<128>(bits, zero_point);
-        const int lds = 2 * lf::kBuf + 2 * 256 * (int)sizeof(float);
+        const int lds = lf::kLds;
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return (int)e;
         const dim3 grid_f((N + kFusedRows - 1) / kFusedRows, (T + lf::kT - 1) / lf::kT, n_alpha);
-        hipLaunchKernelGGL(kern, grid_f, dim3(256), lds, st, rows, (const _Float16*)X_cal, T, N, K,
+        hipLaunchKernelGGL(kern, grid_f, dim3(64 * lf::kWaves), lds, st, rows, (const _Float16*)X_cal, T, N, K,
                            (const float*)s_all, (const float*)s_inv, part);
         const int err = (int)hipGetLastError();
         if (err) return err;
