@@ -118,7 +118,8 @@ def main(argv=None):
                          "shapes at M = 64 (awq_gemm, split K) and M = 16 (awq_gemv), three launches each")
     ap.add_argument("--pmc-search-probe", action="store_true",
                     help="only run the 20-alpha search of the 4096x4096 layer on 512 calibration "
-                         "tokens three times (default path; for rocprofv3 --pmc counter runs)")
+                         "tokens three times on each path (buffered, then fused; for rocprofv3 "
+                         "--pmc counter runs)")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -212,9 +213,12 @@ def main(argv=None):
             W = torch.from_numpy(wl5.weights()).to(dev)
             X = torch.from_numpy(wl5.calibration()).to(dev)
             T, (N, K), A = X.shape[0], W.shape, len(wl5.alphas)
-            ws = torch.empty(awq.search_workspace_bytes(T, N, K, A), dtype=torch.uint8, device=dev)
-            for _ in range(3):
-                awq.search_scale(W, X, wl5.alphas, bits=4, workspace=ws)
+            for fused in (False, True):
+                ws = torch.empty(awq.search_workspace_bytes(T, N, K, A, fused=fused), dtype=torch.uint8,
+                                 device=dev)
+                for _ in range(3):
+                    awq.search_scale(W, X, wl5.alphas, bits=4, workspace=ws)
+                del ws
         torch.cuda.synchronize()
         # loss GEMM: 2 T N K flops per alpha; error kernel: W read once, D written
         # once per alpha (N rounded up to 16 rows)
@@ -222,7 +226,8 @@ def main(argv=None):
                           "K": K, "n_alpha": A,
                           "loss_gemm_flops": 2.0 * T * N * K * A,
                           "quant_err_bytes": 2 * N * K + A * 2 * ((N + 15) // 16 * 16) * K,
-                          "loss_gemm_d_bytes": A * 2 * ((N + 15) // 16 * 16) * K}))
+                          "loss_gemm_d_bytes": A * 2 * ((N + 15) // 16 * 16) * K,
+                          "fused_loss_bytes": A * (2 * N * K + 2 * T * K)}))
         return 0
 
     # ------------------------------------------------------------------ decode GEMV
@@ -624,34 +629,39 @@ def main(argv=None):
         with torch.cuda.stream(stream):
             W = torch.from_numpy(wl5.weights()).to(dev)
             X = torch.from_numpy(wl5.calibration()).to(dev)
-            ws = torch.empty(awq.search_workspace_bytes(X.shape[0], W.shape[0], W.shape[1],
-                                                        len(wl5.alphas)), dtype=torch.uint8, device=dev)
-            for _ in range(2):
-                s, loss, best = awq.search_scale(W, X, wl5.alphas, bits=4, workspace=ws)
-            torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(5):
-                s, loss, best = awq.search_scale(W, X, wl5.alphas, bits=4, workspace=ws)
-            b.record(stream)
-            torch.cuda.synchronize()
-            search_ms = a.elapsed_time(b) / 5
-            # the fused path (the loss kernel forms W - w_hat / s in registers),
-            # which a workspace of awq_search_workspace_bytes_fused selects
-            wsf = torch.empty(awq.search_workspace_bytes(X.shape[0], W.shape[0], W.shape[1],
-                                                         len(wl5.alphas), fused=True),
-                              dtype=torch.uint8, device=dev)
-            for _ in range(2):
-                awq.search_scale(W, X, wl5.alphas, bits=4, workspace=wsf)
-            torch.cuda.synchronize()
-            a.record(stream)
-            for _ in range(5):
-                awq.search_scale(W, X, wl5.alphas, bits=4, workspace=wsf)
-            b.record(stream)
-            torch.cuda.synchronize()
-            search_fused_ms = a.elapsed_time(b) / 5
-            search_ws = (ws.numel(), wsf.numel())
-            del wsf
+
+            def time_search(Wt, Xt, fused, reps):
+                """Mean ms of awq_search_scale on the path a workspace of each size selects."""
+                wst = torch.empty(awq.search_workspace_bytes(Xt.shape[0], Wt.shape[0], Wt.shape[1],
+                                                             len(wl5.alphas), fused=fused),
+                                  dtype=torch.uint8, device=dev)
+                for _ in range(2):
+                    res = awq.search_scale(Wt, Xt, wl5.alphas, bits=4, workspace=wst)
+                torch.cuda.synchronize()
+                a.record(stream)
+                for _ in range(reps):
+                    res = awq.search_scale(Wt, Xt, wl5.alphas, bits=4, workspace=wst)
+                b.record(stream)
+                torch.cuda.synchronize()
+                return a.elapsed_time(b) / reps, wst.numel(), res
+
+            # the default path (the fused loss kernel forms W - w_hat / s in
+            # registers) and the buffered one (D written per chunk of alphas,
+            # then the loss GEMM), each selected by its workspace size
+            search_ms, ws_fused, (s, loss, best) = time_search(W, X, True, 5)
+            search_buf_ms, ws_buf, _ = time_search(W, X, False, 5)
+            search_ws = (ws_fused, ws_buf)
+            # both paths on the Llama-70B MLP shapes (same tokens and grid)
+            search_70b = {}
+            for (N70, K70) in ((28672, 8192), (8192, 28672)):
+                W70 = torch.from_numpy(WL.random_weights(N70, K70, seed=3)).to(dev)
+                X70 = torch.from_numpy(WL.random_activations(X.shape[0], K70, seed=4)).to(dev)
+                f_ms, f_ws, _ = time_search(W70, X70, True, 3)
+                b_ms, b_ws, _ = time_search(W70, X70, False, 3)
+                search_70b[f"{K70}x{N70}"] = {"fused_ms": round(f_ms, 3), "buffered_ms": round(b_ms, 3),
+                                              "fused_workspace_bytes": f_ws, "buffered_workspace_bytes": b_ws}
+                del W70, X70
             # the gate/up pair of the Llama-7B MLP (4096 -> 11008 -> 4096) searched
             # on the block's output (awq_search_scale_mlp), same tokens and grid
             Wg = torch.from_numpy(wl2.weights(1)).to(dev)          # 4096 x 11008 layer: [11008][4096]
@@ -678,8 +688,10 @@ def main(argv=None):
             qp_us = a.elapsed_time(b) * 1e3 / 20
         qp_bytes = W.numel() * 2 + W.shape[1] * 4 + W.numel() // 2 + 4 * W.numel() // 128
         offline = {"search_4096x4096_T512_20alpha_ms": round(search_ms, 3),
-                   "search_fused_path_ms": round(search_fused_ms, 3),
-                   "search_workspace_bytes": {"default": search_ws[0], "fused": search_ws[1]},
+                   "search_path": "fused loss kernel (the default: a workspace of awq_search_workspace_bytes_fused)",
+                   "search_buffered_path_ms": round(search_buf_ms, 3),
+                   "search_workspace_bytes": {"fused": search_ws[0], "buffered": search_ws[1]},
+                   "search_llama70b_mlp_T512_20alpha": search_70b,
                    "search_mlp_block_llama7b_T512_20alpha_ms": round(search_mlp_ms, 3),
                    "search_mlp_block_workspace_bytes": search_mlp_ws,
                    "search_loss_gemm_TFLOPs_incl_quant": round(
@@ -688,7 +700,7 @@ def main(argv=None):
                    "quantize_pack_GBps": round(qp_bytes / (qp_us * 1e-6) / 1e9, 1),
                    "best_alpha": float(wl5.alphas[int(best.item())])}
         log(f"offline: search {search_ms:.3f} ms, quantize_pack {qp_us:.1f} us")
-        del W, X, ws
+        del W, X
 
     # ------------------------------------------------------------------ CPU oracle baseline
     cpu = None

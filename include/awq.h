@@ -151,7 +151,7 @@ awq_status awq_scale_activations(const void* x, const float* s, void* x_out, int
 
 /*
  * awq_search_workspace_bytes -- device workspace of awq_search_scale's
- * default path for T calibration tokens, an N x K layer and n_alpha grid
+ * buffered path for T calibration tokens, an N x K layer and n_alpha grid
  * points: it holds W - w_hat_i / s_i for one chunk of alphas (as many as fit
  * in 128 MB, at least one: N rounded up to a multiple of 16 x K fp16 each, in
  * the loss GEMM's tiled layout; the grid is run chunk by chunk).  0 when an
@@ -160,14 +160,17 @@ awq_status awq_scale_activations(const void* x, const float* s, void* x_out, int
 size_t awq_search_workspace_bytes(int T, int N, int K, int n_alpha);
 
 /*
- * awq_search_workspace_bytes_fused -- the smaller workspace (scales and loss
- * partials only, under a megabyte for a 4096 x 4096 layer) with which
- * awq_search_scale and awq_search_scale_shared take their fused path: one
- * loss kernel forms W - w_hat_i / s_i in registers instead of writing it out
- * (same codes and the same fp16 differences; MI355X, 4096 x 4096, T = 512, 20
- * alphas: 0.85 ms against 0.81 ms).  A workspace of at least
- * awq_search_workspace_bytes selects the default path, one of at least this
- * size the fused one, anything smaller is AWQ_ERR_WORKSPACE.
+ * awq_search_workspace_bytes_fused -- the smaller workspace (the scales and
+ * one loss partial per tile and alpha: 0.7 MB for a 4096 x 4096 layer, T =
+ * 512, 20 alphas) with which awq_search_scale and awq_search_scale_shared take
+ * their fused path: one loss kernel forms W - w_hat_i / s_i in registers
+ * instead of writing it out (the same codes and the same fp16 differences).
+ * MI355X, T = 512, 20 alphas: 0.63-0.68 ms against 0.52-0.54 ms buffered on
+ * 4096 x 4096, where four alphas' differences fit the cache; 8.6 against 9.1
+ * ms and 9.7 against 11.6 ms on the Llama-70B MLP layers, where one alpha's
+ * do not.  A workspace of at least awq_search_workspace_bytes selects the
+ * buffered path, one of at least this size the fused one, anything smaller is
+ * AWQ_ERR_WORKSPACE.
  */
 size_t awq_search_workspace_bytes_fused(int T, int N, int K, int n_alpha);
 

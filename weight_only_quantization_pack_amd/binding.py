@@ -206,19 +206,20 @@ def scale_activations(x, s, out=None):
     return out
 
 
-def search_workspace_bytes(T: int, N: int, K: int, n_alpha: int, fused: bool = False) -> int:
-    """Workspace of the default search path, or (fused=True) the far smaller
-    one with which the search takes its fused loss kernel."""
+def search_workspace_bytes(T: int, N: int, K: int, n_alpha: int, fused: bool = True) -> int:
+    """Workspace of the search's fused path (the default: the loss kernel forms
+    W - w_hat / s in registers), or (fused=False) the larger one with which the
+    search writes those differences out per chunk of alphas and runs a loss GEMM."""
     lib = load_library()
     f = lib.awq_search_workspace_bytes_fused if fused else lib.awq_search_workspace_bytes
     return int(f(T, N, K, n_alpha))
 
 
 def search_scale(W, X_cal, alphas, bits: int = 4, group_size: int = GROUP_SIZE,
-                 zero_point: bool = True, workspace=None, fused: bool = False):
+                 zero_point: bool = True, workspace=None, fused: bool = True):
     """AWQ alpha-grid search.  Returns (s fp32 [K], loss fp32 [n_alpha], best int32 [1]).
     The path follows the workspace size (awq_search_workspace_bytes[_fused]);
-    without a workspace, fused=True allocates the small one of the fused path."""
+    without a workspace, the one of the path `fused` names is allocated."""
     torch = _torch()
     lib = load_library()
     N, K = W.shape
@@ -285,7 +286,7 @@ def _need_layer(qweight, scales, zeros, N, K, bits, group_size, what=""):
 
 
 def search_scale_shared(Ws, X_cal, alphas, bits: int = 4, group_size: int = GROUP_SIZE,
-                        zero_point: bool = True, workspace=None, fused: bool = False):
+                        zero_point: bool = True, workspace=None, fused: bool = True):
     """One s for several layers reading X_cal (awq_search_scale_shared): the
     layers' rows together form the searched layer.  Returns (s fp32 [K],
     losses fp32 [n_alpha], best int32 [1]) as search_scale (workspace and
