@@ -165,9 +165,9 @@ size_t awq_search_workspace_bytes(int T, int N, int K, int n_alpha);
  * 512, 20 alphas) with which awq_search_scale and awq_search_scale_shared take
  * their fused path: one loss kernel forms W - w_hat_i / s_i in registers
  * instead of writing it out (the same codes and the same fp16 differences).
- * MI355X, T = 512, 20 alphas: 0.63-0.68 ms against 0.52-0.54 ms buffered on
- * 4096 x 4096, where four alphas' differences fit the cache; 8.6 against 9.1
- * ms and 9.7 against 11.6 ms on the Llama-70B MLP layers, where one alpha's
+ * MI355X, T = 512, 20 alphas: 0.63-0.68 ms against 0.51-0.54 ms buffered on
+ * 4096 x 4096, where four alphas' differences fit the cache; 8.0 against 9.0
+ * ms and 8.0 against 11.6 ms on the Llama-70B MLP layers, where one alpha's
  * do not.  A workspace of at least awq_search_workspace_bytes selects the
  * buffered path, one of at least this size the fused one, anything smaller is
  * AWQ_ERR_WORKSPACE.

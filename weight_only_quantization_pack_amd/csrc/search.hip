@@ -276,10 +276,29 @@ __global__ __launch_bounds__(512, 1) void k_loss_fused(RowList layers, const _Fl
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tile = wave & 3;                      // W tile
     const int j = lane & 15, hq = lane >> 4;
-    const int alpha = blockIdx.z;
-    const int t0 = blockIdx.y * lf::kT;
+    // Workgroup L -> (unit, alpha), unit = calibration block * row blocks + row
+    // block.  Workgroups go to the XCDs round-robin (L mod 8), so each run of
+    // 8 A consecutive workgroups gives XCD x all A alphas of unit 8 c + x: the
+    // workgroups that run together on one XCD share their W rows in its L2.
+    // Units past the last whole run of 8 take the alphas in the plain order.
+    const int nblk = (N + kFusedRows - 1) / kFusedRows;
+    const int U = nblk * ((T + lf::kT - 1) / lf::kT);
+    const int A = (int)gridDim.x / U;
+    const int full = U / 8 * 8;
+    const int L = blockIdx.x;
+    int unit, alpha;
+    if (L < full * A) {
+        const int r = L % (8 * A);
+        unit = L / (8 * A) * 8 + r % 8;
+        alpha = r / 8;
+    } else {
+        const int Lt = L - full * A, rem = U - full;
+        unit = full + Lt % rem;
+        alpha = Lt / rem;
+    }
+    const int t0 = unit / nblk * lf::kT;
     const int G = K / kGroup;
-    const int n_base = blockIdx.x * kFusedRows + tile * 16;
+    const int n_base = unit % nblk * kFusedRows + tile * 16;
     // X: load q (0..kXLoads-1) of wave w fills rows 8 (kXLoads w + q) .. + 7 of
     // the buffer, lane l row + (l >> 3) at position l & 7, which holds chunk
     // (l & 7) ^ (l >> 3) of the row (chunk p of row r at position p ^ (r & 7),
@@ -586,9 +605,7 @@ __global__ __launch_bounds__(512, 1) void k_loss_fused(RowList layers, const _Fl
         double tot = wsum[0];
 #pragma unroll
         for (int w = 1; w < lf::kWaves; ++w) tot += wsum[w];
-        const size_t tile_id = (size_t)blockIdx.y * gridDim.x + blockIdx.x;
-        const size_t n_tiles = (size_t)gridDim.x * gridDim.y;
-        partials[(size_t)alpha * n_tiles + tile_id] = tot;
+        partials[(size_t)alpha * U + unit] = tot;
     }
 }
 
@@ -707,7 +724,7 @@ int launch_search(const void* const* Ws, const int* Ns, int n_layers, const void
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return (int)e;
-        const dim3 grid_f((N + kFusedRows - 1) / kFusedRows, (T + lf::kT - 1) / lf::kT, n_alpha);
+        const dim3 grid_f((unsigned)(fused_tiles(T, N) * (size_t)n_alpha));
         hipLaunchKernelGGL(kern, grid_f, dim3(64 * lf::kWaves), lds, st, rows, (const _Float16*)X_cal, T, N, K,
                            (const float*)s_all, (const float*)s_inv, part);
         const int err = (int)hipGetLastError();
