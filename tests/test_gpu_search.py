@@ -249,19 +249,24 @@ def test_error_kernel_decides_exact_ties_like_the_quantizer(gpu):
     assert abs(float(host(loss_g)[0]) - loss_r[0]) <= 1e-3 * loss_r[0], (host(loss_g), loss_r)
 
 
-@pytest.mark.parametrize("bits,zero_point,group_size", [(4, True, 128), (3, False, 64)])
-def test_fused_and_buffered_paths_agree(gpu, bits, zero_point, group_size):
+@pytest.mark.parametrize("bits,zero_point,group_size,N,T,n_alpha", [
+    (4, True, 128, 200, 300, 8), (3, False, 64, 200, 300, 8),
+    (4, True, 128, 300, 1100, 5), (4, False, 64, 300, 1100, 5)])
+def test_fused_and_buffered_paths_agree(gpu, bits, zero_point, group_size, N, T, n_alpha):
     """The two loss paths form the same fp16 differences and sum the same
     products in different blocks: equal choice, losses within fp64 summation
-    order.  T = 300 spans two 256-row blocks of the fused kernel, the last one
-    ragged; N = 200 leaves a partial 128-row block."""
+    order.  N = 200, T = 300: four 64-row units of the fused kernel (fewer
+    than one XCD's run of 8; the last unit and the calibration block ragged).
+    N = 300, T = 1100: 5 row units x 3 calibration blocks of 512 = 15 units,
+    one whole run of 8 units spread over the XCDs and 7 past it, the last row
+    unit and calibration block ragged."""
     import torch
     if FUSED:
         pytest.skip("compares the two paths itself")
-    W = WL.random_weights(200, 768, seed=101)
+    W = WL.random_weights(N, 768, seed=101)
     W[:, :3] *= 15
-    X = WL.random_activations(300, 768, seed=102, sigma=1.5)
-    alphas = [i / 8 for i in range(8)]
+    X = WL.random_activations(T, 768, seed=102, sigma=1.5)
+    alphas = [i / n_alpha for i in range(n_alpha)]
     out = []
     for fused in (False, True):
         s, loss, best = awq.search_scale(dev(W), dev(X), alphas, bits=bits, group_size=group_size,
