@@ -954,6 +954,7 @@ int w4p_rows(int M) { return M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128; }
 
 int w4p_tiles(int M, int N, int nbw = 4) {
     const int rows = w4p_rows(M);
+    if (rows <= 64) nbw = 2;                           // 128-column tiles (launch_w4p)
     return ((N + 64 * nbw - 1) / (64 * nbw)) * ((M + rows - 1) / rows);
 }
 
@@ -1021,20 +1022,29 @@ int launch_w4p_rows(const void* x, const void* qweight, const void* scales, cons
 // blocks (two waves per SIMD hide each other's waits: MI355X, M = 2048,
 // 14336x4096 877-886 -> 890-919 TFLOP/s, 4096x6144 919-942 -> 960-986),
 // 448 columns as 4 waves of 7 (8 waves cannot split it).  16-, 32- and
-// 64-row tiles take 4 waves of 4 blocks.
+// 64-row tiles (batched decode) are 128 columns wide: 4 waves of 2 blocks at
+// 16 rows, 8 waves of 1 block at 32 and 64 rows (two waves per SIMD), so a
+// layer gives twice the tiles of 256-column ones and split K takes fewer
+// splits.  MI355X, cold weights, medians of runs alternated with 4 waves of
+// 4 blocks (256 columns): Llama-70B MLP 8192x28672 / 28672x8192 at M = 16
+// 33.1 / 32.7 -> 32.6 / 32.3 us, M = 32 40.1 / 39.0 -> 36.2 / 36.9, M = 64
+// 52.3 / 50.6 -> 49.2 / 49.4; Llama-7B 4096x4096, 11008x4096, 4096x11008 at
+// M = 64 18.9, 23.9, 20.9 -> 13.2, 17.5, 17.7 us (M = 16: 12.6, 16.8, 13.9 ->
+// 9.6, 13.3, 12.3).  64-column tiles (1 block of 4 waves) were faster on some
+// of these shapes and slower on others (28672x8192 at M = 16: 39.0 us).
 int launch_w4p(const void* x, const void* qweight, const void* scales, const void* zeros, void* y,
                float* part, const float* inv_s, int M, int N, int K, int bits, int group_size,
                int splits, int gsplit, hipStream_t st, int nbw = 4) {
     switch (w4p_rows(M)) {
     case 16:
-        return launch_w4p_rows<16, 4>(x, qweight, scales, zeros, y, part, inv_s, M, N, K, bits, group_size,
-                                      splits, gsplit, st);
+        return launch_w4p_rows<16, 2, 4>(x, qweight, scales, zeros, y, part, inv_s, M, N, K, bits, group_size,
+                                         splits, gsplit, st);
     case 32:
-        return launch_w4p_rows<32, 4>(x, qweight, scales, zeros, y, part, inv_s, M, N, K, bits, group_size,
-                                      splits, gsplit, st);
+        return launch_w4p_rows<32, 1, 8>(x, qweight, scales, zeros, y, part, inv_s, M, N, K, bits, group_size,
+                                         splits, gsplit, st);
     case 64:
-        return launch_w4p_rows<64, 4>(x, qweight, scales, zeros, y, part, inv_s, M, N, K, bits, group_size,
-                                      splits, gsplit, st);
+        return launch_w4p_rows<64, 1, 8>(x, qweight, scales, zeros, y, part, inv_s, M, N, K, bits, group_size,
+                                         splits, gsplit, st);
     default:
         break;
     }
@@ -1060,7 +1070,7 @@ int launch_w4p(const void* x, const void* qweight, const void* scales, const voi
 // vs 828-839 TFLOP/s for the two-per-CU kernel (896 tiles) and 732-739 for
 // NBW 4 (four rounds); 4096x6144 NBW 6 (256 tiles) 989-1015 vs 862 and 717;
 // 14336x4096 NBW 4 (256 tiles) 943 vs NBW 6 775, NBW 7 670.  M <= 64
-// (16- to 64-row tiles) always takes NBW 4.
+// (16- to 64-row tiles) takes the 128-column tiles of launch_w4p.
 int gemm_tile_choice(int M, int N, int bits, int group_size, int cus) {
     if (w4p_rows(M) <= 64) return 4;
     int best = 4, best_cost = INT_MAX;
