@@ -210,10 +210,11 @@ def test_dequantize_validation(lib):
 
 
 def test_gemm_splitk_validation(lib):
-    # without a GPU the library assumes 256 compute units: 32 tiles of a
-    # 64 x 8192 output leave most idle, so K = 28672 (224 groups) is split 8 ways
+    # without a GPU the library assumes 256 compute units: the 64 tiles (64 rows
+    # x 128 columns) of a 64 x 8192 output leave most idle, so K = 28672 (224
+    # groups) is split 256 / 64 = 4 ways
     need = lib.awq_gemm_splitk_workspace_bytes(64, 8192, 28672)
-    assert need == 8 * 64 * 8192 * 4
+    assert need == 4 * 64 * 8192 * 4
     assert lib.awq_gemm_splitk_workspace_bytes(2048, 14336, 4096) == 0      # enough tiles
     assert lib.awq_gemm_splitk_workspace_bytes(64, 8192, 1000) == 0         # invalid K
     f = lib.awq_gemm_splitk

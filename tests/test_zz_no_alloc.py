@@ -27,7 +27,7 @@ def test_noalloc_matches_workspace_entry_twice(gpu):
     import torch
     cap = awq.gemm_splitk_noalloc_max_bytes()
     assert cap == 32 << 20
-    # 64 x 4096 x 14336: 16 tiles, 14 splits (14.7 MB of partials); then
+    # 64 x 4096 x 14336: 32 tiles of 128 columns, 8 splits (8.4 MB of partials); then
     # 5 x 302 x 2048: 2 splits over a few kB of the same array
     for M, N, K, bits in [(64, 4096, 14336, 4), (5, 302, 2048, 3)]:
         need = awq.gemm_splitk_workspace_bytes(M, N, K)
