@@ -217,8 +217,10 @@ __global__ __launch_bounds__(256) void k_quant_err(LayerList layers,
 // to memory): L_alpha * T * N = sum over (t, n) of (X D_alpha^T)[t][n]^2.  A
 // workgroup of 8 waves owns 64 rows of W (four 16-row MFMA B tiles) and up to
 // 512 calibration rows for one alpha.  Wave w takes tile w & 3 against
-// calibration rows 256 (w >> 2) .. + 255, so the two waves of a tile share a
-// SIMD: each forms the D fragments of half the group's columns (k 64 (w >> 2)
+// calibration rows 256 (w >> 2) .. + 255; the two waves of a tile (w and
+// w + 4, on one SIMD when the CU deals a workgroup's waves to its SIMDs
+// round-robin; correctness does not depend on it) each form the D fragments
+// of half the group's columns (k 64 (w >> 2)
 // .. + 63) in registers in the B-operand layout of v_mfma_f32_16x16x32_f16
 // (lane (j, q) holds row j's k = 32 s + 8 q + e of substep s), meeting its
 // partner through LDS for the group's min and max (128-wide groups) and for the
