@@ -383,11 +383,12 @@ def main(argv=None):
             with torch.cuda.graph(g, stream=stream):
                 for r in range(R3):
                     fn(x, *reps3[r], N=N, bits=4, out=y)
-            # warm-up as long as one timed loop, then the median of three loops
+            # warm-up as long as eight timed loops (20-50 ms: the first shape
+            # read slow after a shorter one), then the median of three loops
             n_rep = max(2, 100 // R3)
             loops = []
             with torch.cuda.stream(stream):
-                for _ in range(n_rep):
+                for _ in range(8 * n_rep):
                     g.replay()
                 torch.cuda.synchronize()
                 for _ in range(3):

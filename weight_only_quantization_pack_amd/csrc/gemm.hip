@@ -954,7 +954,8 @@ int w4p_rows(int M) { return M <= 16 ? 16 : M <= 32 ? 32 : M <= 64 ? 64 : 128; }
 
 int w4p_tiles(int M, int N, int nbw = 4) {
     const int rows = w4p_rows(M);
-    if (rows <= 64) nbw = 2;                           // 128-column tiles (launch_w4p)
+    if (rows == 16) nbw = 1;                           // 64-column tiles (launch_w4p)
+    else if (rows <= 64) nbw = 2;                      // 128-column tiles
     return ((N + 64 * nbw - 1) / (64 * nbw)) * ((M + rows - 1) / rows);
 }
 
@@ -1022,22 +1023,26 @@ int launch_w4p_rows(const void* x, const void* qweight, const void* scales, cons
 // blocks (two waves per SIMD hide each other's waits: MI355X, M = 2048,
 // 14336x4096 877-886 -> 890-919 TFLOP/s, 4096x6144 919-942 -> 960-986),
 // 448 columns as 4 waves of 7 (8 waves cannot split it).  16-, 32- and
-// 64-row tiles (batched decode) are 128 columns wide: 4 waves of 2 blocks at
-// 16 rows, 8 waves of 1 block at 32 and 64 rows (two waves per SIMD), so a
-// layer gives twice the tiles of 256-column ones and split K takes fewer
-// splits.  MI355X, cold weights, medians of runs alternated with 4 waves of
-// 4 blocks (256 columns): Llama-70B MLP 8192x28672 / 28672x8192 at M = 16
-// 33.1 / 32.7 -> 32.6 / 32.3 us, M = 32 40.1 / 39.0 -> 36.2 / 36.9, M = 64
-// 52.3 / 50.6 -> 49.2 / 49.4; Llama-7B 4096x4096, 11008x4096, 4096x11008 at
-// M = 64 18.9, 23.9, 20.9 -> 13.2, 17.5, 17.7 us (M = 16: 12.6, 16.8, 13.9 ->
-// 9.6, 13.3, 12.3).  64-column tiles (1 block of 4 waves) were faster on some
-// of these shapes and slower on others (28672x8192 at M = 16: 39.0 us).
+// 64-row tiles (batched decode) are narrower: 8 waves of 1 block (128
+// columns, two waves per SIMD) at 32 and 64 rows, 4 waves of 1 block (64
+// columns) at 16 rows, whose split K aims at two workgroups per CU
+// (gemm_splits).  More tiles than 256-column ones means fewer splits.
+// MI355X, cold weights, medians of runs alternated with 4 waves of 4 blocks
+// (256 columns): Llama-70B MLP 8192x28672 / 28672x8192 at M = 32 40.1 / 39.0
+// -> 36.2 / 36.9 us, M = 64 52.3 / 50.6 -> 49.2 / 49.4; Llama-7B 4096x4096,
+// 11008x4096, 4096x11008 at M = 64 18.9, 23.9, 20.9 -> 13.2, 17.5, 17.7 us.
+// At 16 rows, against 128-column tiles split for one workgroup per CU (which
+// themselves took the 70B shapes from 33.1 / 32.7 to 32.6 / 32.3 us and the
+// 7B ones from 12.6, 16.8, 13.9 to 9.6, 13.3, 12.3): 70B 33.0 / 32.8 -> 32.8
+// / 31.3, 7B 9.5, 13.4, 12.3 -> 8.4, 13.3, 11.5 us.  Two workgroups per CU at
+// 32 and 64 rows made the 7B shapes slower (11008x4096 at M = 32 14.6 ->
+// 18.0 us).
 int launch_w4p(const void* x, const void* qweight, const void* scales, const void* zeros, void* y,
                float* part, const float* inv_s, int M, int N, int K, int bits, int group_size,
                int splits, int gsplit, hipStream_t st, int nbw = 4) {
     switch (w4p_rows(M)) {
     case 16:
-        return launch_w4p_rows<16, 2, 4>(x, qweight, scales, zeros, y, part, inv_s, M, N, K, bits, group_size,
+        return launch_w4p_rows<16, 1, 4>(x, qweight, scales, zeros, y, part, inv_s, M, N, K, bits, group_size,
                                          splits, gsplit, st);
     case 32:
         return launch_w4p_rows<32, 1, 8>(x, qweight, scales, zeros, y, part, inv_s, M, N, K, bits, group_size,
@@ -1088,13 +1093,14 @@ int gemm_tile_choice(int M, int N, int bits, int group_size, int cus) {
 }  // namespace
 
 int gemm_splits(int M, int N, int K) {
-    // split K only while the tiles leave at least half the CUs idle; each
+    // split K only while the tiles leave at least half the workgroup slots
+    // idle: one slot per CU, two for the 16-row tiles (4 waves of 64 columns
+    // with a small footprint: two workgroups put two waves on each SIMD); each
     // split keeps >= 8 groups (two rounds of the 4-step pipeline), <= 16 splits
     const int nT = w4p_tiles(M, N);
-    const int cus = device_cu_count();
+    const int slots = device_cu_count() * (w4p_rows(M) == 16 ? 2 : 1);
     const int G = K / kGroup;
-    if (2 * nT > cus) return 1;
-    int s = min(min(cus / nT, G / 8), 16);
+    int s = min(min(slots / nT, G / 8), 16);
     if (s < 2) return 1;
     const int gsplit = (G + s - 1) / s;
     return (G + gsplit - 1) / gsplit;                  // no empty split
