@@ -115,7 +115,7 @@ def main(argv=None):
                          "three launches each after one warm-up launch")
     ap.add_argument("--pmc-batched-probe", action="store_true",
                     help="short run for rocprofv3 --pmc: a 256 MiB device copy, then the Llama-70B MLP "
-                         "shapes at M = 64 (awq_gemm, split K) and M = 16 (awq_gemv), three launches each")
+                         "shapes at M = 64 (awq_gemm) and M = 16 (awq_gemm, then awq_gemv), three launches each")
     ap.add_argument("--pmc-search-probe", action="store_true",
                     help="only run the 20-alpha search of the 4096x4096 layer on 512 calibration "
                          "tokens three times on each path (buffered, then fused; for rocprofv3 "
@@ -187,13 +187,12 @@ def main(argv=None):
                 W = torch.from_numpy(wl3.weights(i)).to(dev)
                 qw, sc, ze = awq.quantize_pack(W, None, bits=4)
                 del W
-                for M in (64, 16):
+                for M, fn in ((64, awq.gemm), (16, awq.gemm), (16, awq.gemv)):
                     x = torch.from_numpy(wl3.activations(M, i)).to(dev)
                     y = torch.empty((M, N), dtype=torch.float16, device=dev)
-                    fn = awq.gemm if M > 16 else awq.gemv
                     for _ in range(3):
                         fn(x, qw, sc, ze, N=N, bits=4, out=y)
-                        order.append(f"{K}x{N} M={M}")
+                        order.append(f"{K}x{N} M={M} {fn.__name__}")
                 del qw, sc, ze
         torch.cuda.synchronize()
         print(json.dumps({"pmc_batched_probe": True, "copy_bytes": 256 * 2**20, "launches": order}))
