@@ -92,11 +92,20 @@ __global__ __launch_bounds__(1024) void k_act_stat(const _Float16* __restrict__ 
     const int c = threadIdx.x & 7, r = threadIdx.x >> 3;
     const int k0 = blockIdx.x * 64 + 8 * c;              // K is a multiple of 128
     double sum[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int t = r; t < T; t += 128) {
-        const uint4 v = *reinterpret_cast<const uint4*>(X + (size_t)t * K + k0);
-        const _Float16* h = reinterpret_cast<const _Float16*>(&v);
+    // four rows' loads in flight before their sums (rows past T load nothing)
+    for (int t0 = r; t0 < T; t0 += 4 * 128) {
+        uint4 v[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sum[e] += fabs((double)h[e]);
+        for (int u = 0; u < 4; ++u) {
+            const int t = t0 + 128 * u;
+            v[u] = t < T ? *reinterpret_cast<const uint4*>(X + (size_t)t * K + k0) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const _Float16* h = reinterpret_cast<const _Float16*>(&v[u]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sum[e] += fabs((double)h[e]);
+        }
     }
     __shared__ double part[128][64 + 1];
 #pragma unroll
@@ -624,12 +633,23 @@ __global__ __launch_bounds__(256) void k_select(const double* __restrict__ parti
     __shared__ double loss[kMaxAlpha];
     __shared__ int best_s;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int a = wave; a < n_alpha; a += 4) {
-        double s = 0.0;
-        for (int j = lane; j < n_tiles; j += 64) s += partials[(size_t)a * n_tiles + j];
+    // wave w sums alphas w, w + 4, ..., four of them at a time so that their
+    // loads are in flight together (each alpha's order as one at a time)
+    for (int a0 = wave; a0 < n_alpha; a0 += 16) {
+        double s[4] = {0.0, 0.0, 0.0, 0.0};
+        for (int j = lane; j < n_tiles; j += 64) {
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-        if (lane == 0) loss[a] = s * inv_count;
+            for (int u = 0; u < 4; ++u) {
+                const int a = a0 + 4 * u;
+                if (a < n_alpha) s[u] += partials[(size_t)a * n_tiles + j];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) s[u] += __shfl_xor(s[u], off);
+            if (lane == 0 && a0 + 4 * u < n_alpha) loss[a0 + 4 * u] = s[u] * inv_count;
+        }
     }
     __syncthreads();
     if (tid == 0) {
@@ -642,7 +662,19 @@ __global__ __launch_bounds__(256) void k_select(const double* __restrict__ parti
     __syncthreads();
     if (loss_out && tid < n_alpha) loss_out[tid] = (float)loss[tid];
     const float* sb = s_all + (size_t)best_s * K;
-    for (int k = tid; k < K; k += blockDim.x) s_out[k] = sb[k];
+    for (int k0 = tid; k0 < K; k0 += 8 * (int)blockDim.x) {     // eight loads in flight
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int k = k0 + u * (int)blockDim.x;
+            v[u] = k < K ? sb[k] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int k = k0 + u * (int)blockDim.x;
+            if (k < K) s_out[k] = v[u];
+        }
+    }
 }
 
 // Rows of the layers in `layers` (fp16, row-major, the N rows one layer after
