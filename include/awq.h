@@ -334,8 +334,9 @@ awq_status awq_gemm(const void* x, const void* qweight, const void* scales,
 /*
  * awq_gemm_splitk_workspace_bytes -- device workspace awq_gemm_splitk needs
  * for an M x N x K product on the current device: 0 when the output tiles
- * already occupy at least half the compute units (no split), else
- * splits * M * N * 4 bytes of fp32 partial sums.  0 for invalid shapes.
+ * already occupy at least half the workgroup slots (one per compute unit,
+ * two for M <= 16; no split), else splits * M * N * 4 bytes of fp32 partial
+ * sums.  0 for invalid shapes.
  */
 size_t awq_gemm_splitk_workspace_bytes(int M, int N, int K);
 
