@@ -209,12 +209,14 @@ def test_gemm_split_k(gpu, M, N, K, bits):
 
 
 @pytest.mark.parametrize("bits", [4, 3])
-@pytest.mark.parametrize("M", [16, 17, 24, 32, 33])
+@pytest.mark.parametrize("M", [16, 17, 24, 32, 33, 48, 64])
 @pytest.mark.parametrize("N,K", [(302, 2048), (1000, 1152)])
 def test_gemm_row_tile_heights(gpu, M, N, K, bits):
     """The pipelined kernel's 16-, 32- and 64-row tiles around their limits
-    (M = 16 | 17, 32 | 33; M = 24 leaves 8 padding rows in a 32-row tile),
-    with and without the K split, whole output."""
+    (M = 16 | 17, 32 | 33; M = 24 and 48 leave padding rows in a 32- and a
+    64-row tile; 16-row tiles are 64 columns wide, 32- and 64-row ones 128, so
+    N = 302 and 1000 end in a partial column tile), with and without the K
+    split, whole output."""
     import torch
     qw, d, z = packed(WL.random_weights(N, K, seed=N + K + M), bits)
     x = WL.random_activations(M, K, seed=M + 11, sigma=1.0)
